@@ -1,0 +1,73 @@
+// ring_kernels.h -- launch interface between the host runtime and the HIP
+// kernels of the draft-KV ring (internal to the library).
+#pragma once
+
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ring_layout.h"
+
+#define RING_MAX_SEQ_INTERNAL 64
+
+namespace ringkv {
+
+// One begin_step launch: appends rows [row0, row0 + n_rows) of the step's new
+// rows (bulk chunk or fold-in) plus, for a fold-in, n_pad pad rows to the
+// trash slot; when do_mask != 0 it also rebuilds slot_pos, the mask and the
+// noise RoPE table of the sequence.
+struct StepArgs {
+  const uint16_t* k_new;     // [n_layer][n_new][kv_row] F16, K not rotated
+  const uint16_t* v_new;     // same shape
+  uint16_t* kring;           // this sequence's K tiles [n_layer][n_head_kv][n_tiles][4096]
+  uint16_t* vring;
+  int32_t* slot_pos;         // [cap]
+  uint16_t* mask;            // [q_len][kv_total]
+  double* rope_noise;        // [q_len][64][2] (cos, sin) at committed + i
+  const double* inv_freq;    // [64] theta_i
+  int64_t start;             // first new position
+  int64_t committed;
+  int64_t lo;
+  int32_t n_new;             // rows per layer in k_new / v_new
+  int32_t row0;              // first new row this launch appends
+  int32_t n_rows;            // real rows this launch appends
+  int32_t n_pad;             // pad rows (fold-in only)
+  int32_t cap, q_len, kv_total, n_head_kv, n_layer, trash_slot, n_tiles;
+  int32_t do_mask;
+};
+
+// One ring_attn launch over every sequence of the ring for one layer.
+struct AttnArgs {
+  uint16_t* kring;           // ring base (all sequences and layers)
+  uint16_t* vring;
+  const uint16_t* mask;      // [n_seq][q_len][kv_total]
+  const double* rope_noise;  // [n_seq][q_len][64][2]
+  const uint16_t* q;         // [n_seq][q_len][n_head][128]
+  const uint16_t* k_noise;   // [n_seq][q_len][kv_row]
+  const uint16_t* v_noise;
+  float* out;                // [n_seq][q_len][n_head][128]
+  float* part_acc;           // [n_seq * n_head_kv][n_split][mpad][128]
+  float* part_ml;            // [n_seq * n_head_kv][n_split][mpad][2]
+  int64_t seq_stride;        // halves between sequences in kring / vring
+  int64_t layer_offset;      // halves from a sequence's base to this layer
+  int64_t head_stride;       // halves between KV heads (n_tiles * 4096)
+  int32_t n_seq, n_head, n_head_kv, group, q_len, m, cap, kv_total, n_tiles;
+  int32_t n_split;
+  int32_t win[RING_MAX_SEQ_INTERNAL];
+};
+
+struct MergeArgs {
+  const float* part_acc;
+  const float* part_ml;
+  float* out;
+  int32_t n_units, n_split, n_head, n_head_kv, group, q_len, m, mpad;
+};
+
+// t0 / t1: optional events bound to the dispatch (start and end of the
+// kernel itself), or nullptr.
+hipError_t launch_step(const StepArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
+hipError_t launch_attn(const AttnArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
+hipError_t launch_fill_u16(uint16_t* p, uint16_t value, int64_t n, hipStream_t s);
+
+}  // namespace ringkv

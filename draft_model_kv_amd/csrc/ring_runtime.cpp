@@ -1,0 +1,592 @@
+// ring_runtime.cpp -- host side of the draft-KV ring C ABI (include/ring_kv.h).
+//
+// Owns the per-sequence step state (next_pos, held_lo, committed), plans each
+// begin_step (page "DFLASH2_RING_PORT.md", section 1.3), carves the device
+// workspace and enqueues the kernels of ring_kernels.hip on the caller's
+// stream.  Arguments are validated before any device work.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "ring_kernels.h"
+#include "ring_kv.h"
+
+using namespace ringkv;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return RING_OK;
+}
+
+int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+struct Layout {
+  int32_t n_tiles = 0, m = 0, mpad = 0, group = 0, n_split = 1;
+  int64_t seq_stride = 0;  // halves per sequence in the K (or V) ring
+  size_t off_k = 0, off_v = 0, off_slot = 0, off_mask = 0, off_rope = 0, off_freq = 0;
+  size_t off_pacc = 0, off_pml = 0, total = 0;
+};
+
+// Splits of the ring tiles per (sequence, KV head): enough work-groups to
+// cover the 256 compute units, and at least one 32-slot tile per wave.
+int32_t choose_splits(const ring_config& c) {
+  const int n_units = c.n_seq * c.n_head_kv;
+  const int ring_tiles = (c.cap + kTile - 1) / kTile;
+  int s = std::max(1, (256 + n_units - 1) / n_units);
+  s = std::min(s, std::max(1, (ring_tiles + 3) / 4));
+  if (const char* env = std::getenv("RING_ATTN_SPLITS")) {
+    const int v = std::atoi(env);
+    if (v >= 1 && v <= 1024) s = v;
+  }
+  return s;
+}
+
+int validate(const ring_config* c) {
+  if (!c) return fail(RING_EINVAL, "config is NULL");
+  if (c->cap < 1 || c->cap > (1 << 26)) return fail(RING_EINVAL, "cap %d out of [1, 2^26]", c->cap);
+  if (c->q_len < 1 || c->q_len > 32) return fail(RING_EINVAL, "q_len %d out of [1, 32]", c->q_len);
+  if (c->head_dim != kHeadDim)
+    return fail(RING_EINVAL, "head_dim %d unsupported (must be %d)", c->head_dim, kHeadDim);
+  if (c->n_head_kv < 1 || c->n_head < 1 || c->n_head % c->n_head_kv != 0)
+    return fail(RING_EINVAL, "n_head %d must be a positive multiple of n_head_kv %d", c->n_head,
+                c->n_head_kv);
+  if (c->n_head_kv > 64) return fail(RING_EINVAL, "n_head_kv %d > 64", c->n_head_kv);
+  if (c->q_len * (c->n_head / c->n_head_kv) > kMaxM)
+    return fail(RING_EINVAL, "q_len * n_head / n_head_kv = %d exceeds %d",
+                c->q_len * (c->n_head / c->n_head_kv), kMaxM);
+  if (c->n_layer < 1 || c->n_layer > 1024) return fail(RING_EINVAL, "n_layer %d out of [1, 1024]", c->n_layer);
+  if (c->n_seq < 1 || c->n_seq > RING_MAX_SEQ)
+    return fail(RING_EINVAL, "n_seq %d out of [1, %d]", c->n_seq, RING_MAX_SEQ);
+  if (!(c->rope_base > 1.0f) || !std::isfinite(c->rope_base))
+    return fail(RING_EINVAL, "rope_base must be finite and > 1");
+  return RING_OK;
+}
+
+void geometry_of(const ring_config& c, ring_geometry* g, Layout* L) {
+  g->a_step = 2 * c.q_len + 2;
+  g->trash_slot = c.cap + c.q_len;
+  g->kv_total = (int32_t)align_up((int64_t)c.cap + c.q_len + 1, 32);
+  g->kv_row = c.head_dim * c.n_head_kv;
+  g->kv_bytes_per_layer = 2ll * g->kv_row * g->kv_total * 2;
+
+  L->n_tiles = g->kv_total / kTile;
+  L->group = c.n_head / c.n_head_kv;
+  L->m = c.q_len * L->group;
+  L->mpad = L->m <= 32 ? 32 : 64;
+  L->n_split = choose_splits(c);
+  L->seq_stride = (int64_t)c.n_layer * c.n_head_kv * L->n_tiles * kTileHalves;
+  size_t off = 0;
+  auto take = [&off](size_t bytes) {
+    const size_t o = off;
+    off = (size_t)align_up((int64_t)(off + bytes), 256);
+    return o;
+  };
+  const size_t ring_bytes = (size_t)c.n_seq * L->seq_stride * 2;
+  L->off_k = take(ring_bytes);
+  L->off_v = take(ring_bytes);
+  L->off_slot = take((size_t)c.n_seq * c.cap * 4);
+  L->off_mask = take((size_t)c.n_seq * c.q_len * g->kv_total * 2);
+  L->off_rope = take((size_t)c.n_seq * c.q_len * 64 * 2 * 8);
+  L->off_freq = take(64 * 8);
+  const size_t n_part = L->n_split > 1 ? (size_t)c.n_seq * c.n_head_kv * L->n_split * L->mpad : 0;
+  L->off_pacc = take(n_part * kHeadDim * 4);
+  L->off_pml = take(n_part * 2 * 4);
+  L->total = off;
+  g->workspace_bytes = (int64_t)L->total;
+}
+
+struct Plan {
+  int64_t win, lo, start, n_new;
+  bool bulk;
+};
+
+// Section 1.3: win = min(committed, cap), lo = committed - win,
+// start = max(next_pos, lo); after a rewind that lost window rows the whole
+// window is appended again (start = lo).
+Plan plan_of(int64_t cap, int64_t a_step, int64_t committed, int64_t next_pos, int64_t held_lo) {
+  Plan p;
+  p.win = std::min(committed, cap);
+  p.lo = committed - p.win;
+  if (p.lo < held_lo) p.start = p.lo;
+  else p.start = std::max(std::min(next_pos, committed), p.lo);
+  p.n_new = committed - p.start;
+  p.bulk = p.n_new > a_step;
+  return p;
+}
+
+}  // namespace
+
+struct ring {
+  ring_config cfg{};
+  ring_geometry geo{};
+  Layout L;
+  int device = 0;
+  bool owns_ws = false;
+  uint8_t* ws = nullptr;
+  uint16_t* kring = nullptr;
+  uint16_t* vring = nullptr;
+  int32_t* slot_pos = nullptr;
+  uint16_t* mask = nullptr;
+  double* rope_noise = nullptr;
+  double* inv_freq = nullptr;
+  float* part_acc = nullptr;
+  float* part_ml = nullptr;
+  std::vector<int64_t> next_pos, held_lo, committed;
+  std::vector<double> inv_freq_host;
+  hipStream_t last_stream = nullptr;
+  // profiling: per kernel kind, event pairs (start, end) and how many are used
+  int32_t prof_max = 0;
+  std::vector<hipEvent_t> prof_ev[3];
+  int32_t prof_used[3] = {0, 0, 0};
+};
+
+namespace {
+
+int use_device(const ring* r) {
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return fail(RING_EDEVICE, "hipGetDevice failed");
+  if (cur != r->device && hipSetDevice(r->device) != hipSuccess)
+    return fail(RING_EDEVICE, "hipSetDevice(%d) failed", r->device);
+  return RING_OK;
+}
+
+StepArgs step_args(ring* r, int32_t seq) {
+  StepArgs a{};
+  a.kring = r->kring + seq * r->L.seq_stride;
+  a.vring = r->vring + seq * r->L.seq_stride;
+  a.slot_pos = r->slot_pos + (int64_t)seq * r->cfg.cap;
+  a.mask = r->mask + (int64_t)seq * r->cfg.q_len * r->geo.kv_total;
+  a.rope_noise = r->rope_noise + (int64_t)seq * r->cfg.q_len * 128;
+  a.inv_freq = r->inv_freq;
+  a.cap = r->cfg.cap;
+  a.q_len = r->cfg.q_len;
+  a.kv_total = r->geo.kv_total;
+  a.n_head_kv = r->cfg.n_head_kv;
+  a.n_layer = r->cfg.n_layer;
+  a.trash_slot = r->geo.trash_slot;
+  a.n_tiles = r->L.n_tiles;
+  return a;
+}
+
+// Next free (start, end) event pair for a launch of `kind`, or nullptrs.
+void next_events(ring* r, int kind, hipEvent_t* t0, hipEvent_t* t1) {
+  *t0 = *t1 = nullptr;
+  if (r->prof_used[kind] < r->prof_max) {
+    *t0 = r->prof_ev[kind][2 * r->prof_used[kind]];
+    *t1 = r->prof_ev[kind][2 * r->prof_used[kind] + 1];
+    ++r->prof_used[kind];
+  }
+}
+
+void destroy_events(ring* r) {
+  for (auto& v : r->prof_ev) {
+    for (hipEvent_t e : v) (void)hipEventDestroy(e);
+    v.clear();
+  }
+  r->prof_max = 0;
+  r->prof_used[0] = r->prof_used[1] = r->prof_used[2] = 0;
+}
+
+int check_launch(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(RING_EDEVICE, "%s: %s", what, hipGetErrorString(e));
+  return RING_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ring_query_geometry(const ring_config* cfg, ring_geometry* out) {
+  if (int e = validate(cfg)) return e;
+  if (!out) return fail(RING_EINVAL, "out is NULL");
+  Layout L;
+  geometry_of(*cfg, out, &L);
+  return ok();
+}
+
+int ring_init(const ring_config* cfg, void* workspace, size_t workspace_bytes, void* stream,
+              ring_t** out) {
+  if (!out) return fail(RING_EINVAL, "out is NULL");
+  *out = nullptr;
+  if (int e = validate(cfg)) return e;
+  ring* r = new (std::nothrow) ring();
+  if (!r) return fail(RING_ENOMEM, "host allocation failed");
+  r->cfg = *cfg;
+  geometry_of(*cfg, &r->geo, &r->L);
+  if (workspace) {
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) {
+      delete r;
+      return fail(RING_EINVAL, "workspace must be 256-byte aligned");
+    }
+    if (workspace_bytes < r->L.total) {
+      delete r;
+      return fail(RING_ENOMEM, "workspace of %zu bytes < %zu needed", workspace_bytes, r->L.total);
+    }
+  }
+  if (hipGetDevice(&r->device) != hipSuccess) {
+    delete r;
+    return fail(RING_EDEVICE, "no HIP device");
+  }
+  if (workspace) {
+    r->ws = static_cast<uint8_t*>(workspace);
+  } else {
+    void* p = nullptr;
+    if (hipMalloc(&p, r->L.total) != hipSuccess) {
+      (void)hipGetLastError();
+      delete r;
+      return fail(RING_ENOMEM, "hipMalloc of %zu bytes failed", r->L.total);
+    }
+    r->ws = static_cast<uint8_t*>(p);
+    r->owns_ws = true;
+  }
+  r->kring = reinterpret_cast<uint16_t*>(r->ws + r->L.off_k);
+  r->vring = reinterpret_cast<uint16_t*>(r->ws + r->L.off_v);
+  r->slot_pos = reinterpret_cast<int32_t*>(r->ws + r->L.off_slot);
+  r->mask = reinterpret_cast<uint16_t*>(r->ws + r->L.off_mask);
+  r->rope_noise = reinterpret_cast<double*>(r->ws + r->L.off_rope);
+  r->inv_freq = reinterpret_cast<double*>(r->ws + r->L.off_freq);
+  r->part_acc = reinterpret_cast<float*>(r->ws + r->L.off_pacc);
+  r->part_ml = reinterpret_cast<float*>(r->ws + r->L.off_pml);
+  r->next_pos.assign(cfg->n_seq, 0);
+  r->held_lo.assign(cfg->n_seq, 0);
+  r->committed.assign(cfg->n_seq, 0);
+  r->inv_freq_host.resize(64);
+  for (int i = 0; i < 64; ++i)
+    r->inv_freq_host[i] = std::pow((double)cfg->rope_base, -2.0 * i / (double)kHeadDim);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  r->last_stream = s;
+  const size_t ring_bytes = (size_t)cfg->n_seq * r->L.seq_stride * 2;
+  hipError_t e = hipMemsetAsync(r->kring, 0, ring_bytes, s);
+  if (e == hipSuccess) e = hipMemsetAsync(r->vring, 0, ring_bytes, s);
+  if (e == hipSuccess) e = hipMemsetAsync(r->slot_pos, 0xFF, (size_t)cfg->n_seq * cfg->cap * 4, s);
+  if (e == hipSuccess)
+    e = launch_fill_u16(r->mask, 0xFC00u, (int64_t)cfg->n_seq * cfg->q_len * r->geo.kv_total, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(r->inv_freq, r->inv_freq_host.data(), 64 * sizeof(double),
+                       hipMemcpyHostToDevice, s);
+  // Index state of committed = 0: nothing visible but the noise block.
+  for (int32_t seq = 0; seq < cfg->n_seq && e == hipSuccess; ++seq) {
+    StepArgs a = step_args(r, seq);
+    a.do_mask = 1;
+    e = launch_step(a, s, nullptr, nullptr);
+  }
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) {
+    const int code = fail(RING_EDEVICE, "ring_init device work failed: %s", hipGetErrorString(e));
+    if (r->owns_ws) (void)hipFree(r->ws);
+    delete r;
+    return code;
+  }
+  *out = r;
+  return ok();
+}
+
+namespace {
+void fill_plan(const ring_config& c, int32_t a_step, int32_t trash_slot, int64_t committed,
+               int64_t next_pos, int64_t held_lo, ring_plan* out, int32_t* ap_rows) {
+  const Plan p = plan_of(c.cap, a_step, committed, next_pos, held_lo);
+  out->committed = committed;
+  out->win = p.win;
+  out->lo = p.lo;
+  out->start = p.start;
+  out->n_new = p.n_new;
+  out->bulk = p.bulk ? 1 : 0;
+  out->n_chunks = p.bulk ? (int32_t)((p.n_new + kBulkChunk - 1) / kBulkChunk) : 0;
+  if (ap_rows && !p.bulk) {
+    for (int i = 0; i < a_step; ++i)
+      ap_rows[i] = i < p.n_new ? (int32_t)((p.start + i) % c.cap) : trash_slot;
+  }
+}
+}  // namespace
+
+int ring_plan_from_state(const ring_config* cfg, int64_t next_pos, int64_t held_lo,
+                         int64_t committed, ring_plan* out, int32_t* ap_rows) {
+  if (int e = validate(cfg)) return e;
+  if (!out) return fail(RING_EINVAL, "out is NULL");
+  if (next_pos < 0 || held_lo < 0 || held_lo > next_pos || next_pos - held_lo > cfg->cap)
+    return fail(RING_EINVAL, "state next_pos %lld / held_lo %lld is not one a ring can be in",
+                (long long)next_pos, (long long)held_lo);
+  if (committed < 0 || committed + cfg->q_len > INT32_MAX)
+    return fail(RING_ERANGE, "committed %lld out of range", (long long)committed);
+  fill_plan(*cfg, 2 * cfg->q_len + 2, cfg->cap + cfg->q_len, committed, next_pos, held_lo, out,
+            ap_rows);
+  return ok();
+}
+
+int ring_plan_step(const ring_t* r, int32_t seq, int64_t committed, ring_plan* out,
+                   int32_t* ap_rows) {
+  if (!r || !out) return fail(RING_EINVAL, "NULL argument");
+  if (seq < 0 || seq >= r->cfg.n_seq) return fail(RING_ERANGE, "seq %d out of range", seq);
+  if (committed < 0 || committed + r->cfg.q_len > INT32_MAX)
+    return fail(RING_ERANGE, "committed %lld out of range", (long long)committed);
+  fill_plan(r->cfg, r->geo.a_step, r->geo.trash_slot, committed, r->next_pos[seq],
+            r->held_lo[seq], out, ap_rows);
+  return ok();
+}
+
+int ring_begin_step(ring_t* r, int32_t seq, int64_t committed, const void* k_new,
+                    const void* v_new, int64_t n_rows, void* stream) {
+  if (!r) return fail(RING_EINVAL, "ring is NULL");
+  if (seq < 0 || seq >= r->cfg.n_seq) return fail(RING_ERANGE, "seq %d out of range", seq);
+  if (committed < 0 || committed + r->cfg.q_len > INT32_MAX)
+    return fail(RING_ERANGE, "committed %lld out of range", (long long)committed);
+  const Plan p = plan_of(r->cfg.cap, r->geo.a_step, committed, r->next_pos[seq], r->held_lo[seq]);
+  if (n_rows != p.n_new)
+    return fail(RING_ESTATE, "n_rows %lld != planned n_new %lld (start %lld)", (long long)n_rows,
+                (long long)p.n_new, (long long)p.start);
+  if (p.n_new > 0 && (!k_new || !v_new)) return fail(RING_EINVAL, "k_new / v_new is NULL");
+  if (int e = use_device(r)) return e;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  r->last_stream = s;
+
+  StepArgs a = step_args(r, seq);
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(v_new);
+  a.start = p.start;
+  a.committed = committed;
+  a.lo = p.lo;
+  a.n_new = (int32_t)p.n_new;
+  if (p.bulk) {
+    for (int64_t row0 = 0; row0 < p.n_new; row0 += kBulkChunk) {
+      a.row0 = (int32_t)row0;
+      a.n_rows = (int32_t)std::min<int64_t>(kBulkChunk, p.n_new - row0);
+      a.n_pad = 0;
+      a.do_mask = row0 + kBulkChunk >= p.n_new;
+      hipEvent_t t0, t1;
+      next_events(r, RING_KERNEL_STEP, &t0, &t1);
+      if (int e = check_launch(launch_step(a, s, t0, t1), "bulk append")) return e;
+    }
+  } else {
+    a.row0 = 0;
+    a.n_rows = (int32_t)p.n_new;
+    a.n_pad = r->geo.a_step - (int32_t)p.n_new;
+    a.do_mask = 1;
+    hipEvent_t t0, t1;
+    next_events(r, RING_KERNEL_STEP, &t0, &t1);
+    if (int e = check_launch(launch_step(a, s, t0, t1), "fold-in append")) return e;
+  }
+  r->next_pos[seq] = committed;
+  r->held_lo[seq] = p.lo;
+  r->committed[seq] = committed;
+  return ok();
+}
+
+int ring_attn(ring_t* r, int32_t layer, const void* q, const void* k_noise, const void* v_noise,
+              float* out, void* stream) {
+  if (!r) return fail(RING_EINVAL, "ring is NULL");
+  if (layer < 0 || layer >= r->cfg.n_layer) return fail(RING_ERANGE, "layer %d out of range", layer);
+  if (!q || !k_noise || !v_noise || !out) return fail(RING_EINVAL, "NULL tensor pointer");
+  const uintptr_t al = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_noise) |
+                       reinterpret_cast<uintptr_t>(v_noise) | reinterpret_cast<uintptr_t>(out);
+  if (al & 15) return fail(RING_EINVAL, "q, k_noise, v_noise and out must be 16-byte aligned");
+  if (int e = use_device(r)) return e;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  r->last_stream = s;
+
+  AttnArgs a{};
+  a.kring = r->kring;
+  a.vring = r->vring;
+  a.mask = r->mask;
+  a.rope_noise = r->rope_noise;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_noise = static_cast<const uint16_t*>(k_noise);
+  a.v_noise = static_cast<const uint16_t*>(v_noise);
+  a.out = out;
+  a.part_acc = r->part_acc;
+  a.part_ml = r->part_ml;
+  a.seq_stride = r->L.seq_stride;
+  a.head_stride = (int64_t)r->L.n_tiles * kTileHalves;
+  a.layer_offset = (int64_t)layer * r->cfg.n_head_kv * a.head_stride;
+  a.n_seq = r->cfg.n_seq;
+  a.n_head = r->cfg.n_head;
+  a.n_head_kv = r->cfg.n_head_kv;
+  a.group = r->L.group;
+  a.q_len = r->cfg.q_len;
+  a.m = r->L.m;
+  a.cap = r->cfg.cap;
+  a.kv_total = r->geo.kv_total;
+  a.n_tiles = r->L.n_tiles;
+  a.n_split = r->L.n_split;
+  for (int i = 0; i < r->cfg.n_seq; ++i)
+    a.win[i] = (int32_t)std::min<int64_t>(r->committed[i], r->cfg.cap);
+  hipEvent_t t0, t1;
+  next_events(r, RING_KERNEL_ATTN, &t0, &t1);
+  if (int e = check_launch(launch_attn(a, s, t0, t1), "ring_attn")) return e;
+  if (r->L.n_split > 1) {
+    MergeArgs m{};
+    m.part_acc = r->part_acc;
+    m.part_ml = r->part_ml;
+    m.out = out;
+    m.n_units = r->cfg.n_seq * r->cfg.n_head_kv;
+    m.n_split = r->L.n_split;
+    m.n_head = r->cfg.n_head;
+    m.n_head_kv = r->cfg.n_head_kv;
+    m.group = r->L.group;
+    m.q_len = r->cfg.q_len;
+    m.m = r->L.m;
+    m.mpad = r->L.mpad;
+    next_events(r, RING_KERNEL_MERGE, &t0, &t1);
+    if (int e = check_launch(launch_merge(m, s, t0, t1), "ring_attn merge")) return e;
+  }
+  return ok();
+}
+
+int ring_free(ring_t* r) {
+  if (!r) return ok();
+  int code = RING_OK;
+  if (use_device(r) == RING_OK) {
+    if (hipStreamSynchronize(r->last_stream) != hipSuccess)
+      code = fail(RING_EDEVICE, "stream synchronisation failed in ring_free");
+    if (r->owns_ws && hipFree(r->ws) != hipSuccess)
+      code = fail(RING_EDEVICE, "hipFree failed");
+    destroy_events(r);
+  } else {
+    code = RING_EDEVICE;
+  }
+  delete r;
+  if (code == RING_OK) return ok();
+  return code;
+}
+
+const char* ring_last_error(void) { return g_err.c_str(); }
+
+int ring_describe(const ring_t* r, char* buf, size_t len) {
+  if (!r || !buf || len == 0) return fail(RING_EINVAL, "NULL argument");
+  const double mib = (double)r->cfg.n_layer * r->geo.kv_bytes_per_layer / (1024.0 * 1024.0);
+  snprintf(buf, len,
+           "[draft-kv] ring: cap=%d kv_total=%d a_step=%d layers=%d seqs=%d f16 cache %.1f MiB "
+           "per seq, splits=%d",
+           r->cfg.cap, r->geo.kv_total, r->geo.a_step, r->cfg.n_layer, r->cfg.n_seq, mib,
+           r->L.n_split);
+  return ok();
+}
+
+int ring_read_slot_pos(const ring_t* r, int32_t seq, int32_t* host_out) {
+  if (!r || !host_out) return fail(RING_EINVAL, "NULL argument");
+  if (seq < 0 || seq >= r->cfg.n_seq) return fail(RING_ERANGE, "seq %d out of range", seq);
+  if (int e = use_device(r)) return e;
+  if (hipDeviceSynchronize() != hipSuccess) return fail(RING_EDEVICE, "device synchronisation failed");
+  if (hipMemcpy(host_out, r->slot_pos + (int64_t)seq * r->cfg.cap, (size_t)r->cfg.cap * 4,
+                hipMemcpyDeviceToHost) != hipSuccess)
+    return fail(RING_EDEVICE, "hipMemcpy failed");
+  return ok();
+}
+
+int ring_read_mask(const ring_t* r, int32_t seq, uint16_t* host_out) {
+  if (!r || !host_out) return fail(RING_EINVAL, "NULL argument");
+  if (seq < 0 || seq >= r->cfg.n_seq) return fail(RING_ERANGE, "seq %d out of range", seq);
+  if (int e = use_device(r)) return e;
+  if (hipDeviceSynchronize() != hipSuccess) return fail(RING_EDEVICE, "device synchronisation failed");
+  const size_t n = (size_t)r->cfg.q_len * r->geo.kv_total;
+  if (hipMemcpy(host_out, r->mask + (int64_t)seq * n, n * 2, hipMemcpyDeviceToHost) != hipSuccess)
+    return fail(RING_EDEVICE, "hipMemcpy failed");
+  return ok();
+}
+
+int ring_read_rows(const ring_t* r, int32_t seq, int32_t layer, int32_t slot0, int32_t n,
+                   uint16_t* k_out, uint16_t* v_out) {
+  if (!r) return fail(RING_EINVAL, "ring is NULL");
+  if (seq < 0 || seq >= r->cfg.n_seq) return fail(RING_ERANGE, "seq %d out of range", seq);
+  if (layer < 0 || layer >= r->cfg.n_layer) return fail(RING_ERANGE, "layer %d out of range", layer);
+  if (n < 0 || slot0 < 0 || (int64_t)slot0 + n > r->geo.kv_total)
+    return fail(RING_ERANGE, "slots [%d, %d) out of [0, %d)", slot0, slot0 + n, r->geo.kv_total);
+  if (n == 0) return ok();
+  if (int e = use_device(r)) return e;
+  if (hipDeviceSynchronize() != hipSuccess) return fail(RING_EDEVICE, "device synchronisation failed");
+  const int t0 = slot0 / kTile, t1 = (slot0 + n - 1) / kTile + 1;
+  const int64_t head_stride = (int64_t)r->L.n_tiles * kTileHalves;
+  const int kv_row = r->geo.kv_row;
+  std::vector<uint16_t> buf((size_t)(t1 - t0) * kTileHalves);
+  for (int which = 0; which < 2; ++which) {
+    uint16_t* dst = which == 0 ? k_out : v_out;
+    if (!dst) continue;
+    const uint16_t* base = (which == 0 ? r->kring : r->vring) + seq * r->L.seq_stride +
+                           (int64_t)layer * r->cfg.n_head_kv * head_stride;
+    for (int h = 0; h < r->cfg.n_head_kv; ++h) {
+      if (hipMemcpy(buf.data(), base + h * head_stride + (int64_t)t0 * kTileHalves,
+                    buf.size() * 2, hipMemcpyDeviceToHost) != hipSuccess)
+        return fail(RING_EDEVICE, "hipMemcpy failed");
+      for (int i = 0; i < n; ++i) {
+        const int slot = slot0 + i;
+        const uint16_t* tile = buf.data() + (int64_t)(slot / kTile - t0) * kTileHalves;
+        for (int d = 0; d < kHeadDim; ++d) {
+          const int off = which == 0 ? k_frag_index(slot % kTile, d) : v_frag_index(slot % kTile, d);
+          dst[(int64_t)i * kv_row + h * kHeadDim + d] = tile[off];
+        }
+      }
+    }
+  }
+  return ok();
+}
+
+int ring_read_state(const ring_t* r, int32_t seq, int64_t* next_pos, int64_t* held_lo) {
+  if (!r || !next_pos || !held_lo) return fail(RING_EINVAL, "NULL argument");
+  if (seq < 0 || seq >= r->cfg.n_seq) return fail(RING_ERANGE, "seq %d out of range", seq);
+  *next_pos = r->next_pos[seq];
+  *held_lo = r->held_lo[seq];
+  return ok();
+}
+
+int ring_profile_enable(ring_t* r, int32_t max_launches) {
+  if (!r || max_launches < 0 || max_launches > (1 << 20))
+    return fail(RING_EINVAL, "bad ring or max_launches");
+  if (int e = use_device(r)) return e;
+  if (hipStreamSynchronize(r->last_stream) != hipSuccess)
+    return fail(RING_EDEVICE, "stream synchronisation failed");
+  destroy_events(r);
+  for (auto& v : r->prof_ev) {
+    v.resize(2 * (size_t)max_launches, nullptr);
+    for (auto& e : v) {
+      if (hipEventCreate(&e) != hipSuccess) {
+        e = nullptr;
+        destroy_events(r);
+        return fail(RING_EDEVICE, "hipEventCreate failed");
+      }
+    }
+  }
+  r->prof_max = max_launches;
+  return ok();
+}
+
+int ring_profile_read(ring_t* r, int32_t kernel, int32_t* n_launches, double* total_ms) {
+  if (!r || !n_launches || !total_ms || kernel < 0 || kernel > 2)
+    return fail(RING_EINVAL, "bad argument");
+  if (int e = use_device(r)) return e;
+  double total = 0.0;
+  const int n = r->prof_used[kernel];
+  for (int i = 0; i < n; ++i) {
+    float ms = 0.0f;
+    hipEvent_t t0 = r->prof_ev[kernel][2 * i], t1 = r->prof_ev[kernel][2 * i + 1];
+    if (hipEventSynchronize(t1) != hipSuccess || hipEventElapsedTime(&ms, t0, t1) != hipSuccess)
+      return fail(RING_EDEVICE, "event timing failed");
+    total += ms;
+  }
+  r->prof_used[kernel] = 0;
+  *n_launches = n;
+  *total_ms = total;
+  return ok();
+}
+
+}  // extern "C"

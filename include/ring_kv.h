@@ -1,0 +1,222 @@
+/*
+ * ring_kv.h -- C ABI of the DFlash2 draft-KV ring for AMD Instinct MI355X (gfx950).
+ *
+ * The draft model's K/V cache is a fixed-size circular buffer: the row of
+ * absolute position p lives in slot p % cap, K is rotated (RoPE) at its
+ * absolute position, and explicit 0 / -inf masks select the window of the last
+ * `cap` committed positions.  Attention over the ring is then equal to
+ * attention over a full cache restricted to that window.
+ *   Source: page "DFLASH2_RING_PORT.md" (DFlash2 draft KV-ring port to
+ *   llama.cpp), TL;DR and section 1 ("what the ring does in Luce"): 1.1
+ *   geometry, 1.2 mod-cap slot map, 1.3 window and step start, 1.4 attention
+ *   masks, 1.5 fixed-topology step, 1.6 driver, 1.7 equivalence and memory.
+ *
+ * Conventions
+ *   - Every call returns RING_OK (0) or a negative RING_E* code and never
+ *     aborts; ring_last_error() gives a message for the calling thread.
+ *   - Arguments are validated before any device work: a failed call leaves
+ *     the ring unchanged.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Device work is enqueued asynchronously on it; device pointers passed in
+ *     must stay valid until the stream has passed that work.
+ *   - A ring_t may be used by one host thread at a time.
+ *   - F16 means IEEE binary16; every device buffer is in the ring's device
+ *     memory (the device that was current at ring_init).
+ */
+#ifndef RING_KV_H
+#define RING_KV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RING_OK       0
+#define RING_EINVAL  (-1)  /* bad argument or unsupported shape               */
+#define RING_ERANGE  (-2)  /* sequence, layer or position out of range        */
+#define RING_ENOMEM  (-3)  /* allocation failed or workspace too small        */
+#define RING_EDEVICE (-4)  /* HIP runtime error                               */
+#define RING_ESTATE  (-5)  /* call does not match the ring's state            */
+
+/* Largest number of sequences one ring may hold (their windows travel as
+ * kernel arguments). */
+#define RING_MAX_SEQ 64
+
+/* Shapes of one ring (all sequences and layers share them).
+ *   cap        ring capacity in context slots (last `cap` positions), >= 1
+ *   q_len      noise-block length, the draft's block size (8 on the page), 1..32
+ *   n_head     query heads; n_head_kv KV heads; n_head % n_head_kv == 0 and
+ *              q_len * n_head / n_head_kv <= 64
+ *   head_dim   must be 128
+ *   n_layer    draft layers, each with its own K and V ring (>= 1)
+ *   n_seq      independent sequences, 1..RING_MAX_SEQ
+ *   rope_base  RoPE base (theta_i = rope_base^(-2i/head_dim)), > 1          */
+typedef struct ring_config {
+  int32_t cap;
+  int32_t q_len;
+  int32_t n_head;
+  int32_t n_head_kv;
+  int32_t head_dim;
+  int32_t n_layer;
+  int32_t n_seq;
+  float rope_base;
+} ring_config;
+
+/* Derived geometry (section 1.1 of the page):
+ *   a_step     = 2 * q_len + 2, rows one fold-in step appends (real + pad)
+ *   trash_slot = cap + q_len, destination of pad rows
+ *   kv_total   = align_up(cap + q_len + 1, 32), rows per ring
+ *   kv_row     = head_dim * n_head_kv, F16 values per row
+ *   kv_bytes_per_layer  K plus V bytes of one (sequence, layer) ring
+ *   workspace_bytes     device bytes ring_init needs when the caller
+ *                       provides the workspace                              */
+typedef struct ring_geometry {
+  int32_t a_step;
+  int32_t trash_slot;
+  int32_t kv_total;
+  int32_t kv_row;
+  int64_t kv_bytes_per_layer;
+  int64_t workspace_bytes;
+} ring_geometry;
+
+/* Plan of one begin_step (section 1.3 of the page):
+ *   win = min(committed, cap), lo = committed - win,
+ *   start = max(next_pos, lo), n_new = committed - start; rows for positions
+ *   [start, committed) are appended.  bulk != 0 when n_new > a_step: the rows
+ *   go in n_chunks chunks of at most 1024 rows in ascending position;
+ *   otherwise they are folded into one fixed a_step-row append whose pad rows
+ *   target trash_slot.  After a rewind that dropped window rows the ring no
+ *   longer holds, start = lo (the whole window is appended again).          */
+typedef struct ring_plan {
+  int64_t committed;
+  int64_t win;
+  int64_t lo;
+  int64_t start;
+  int64_t n_new;
+  int32_t bulk;
+  int32_t n_chunks;
+} ring_plan;
+
+typedef struct ring ring_t;
+
+/* Pure host: validate `cfg` and fill `out`.  Errors: RING_EINVAL. */
+int ring_query_geometry(const ring_config* cfg, ring_geometry* out);
+
+/* Create a ring on the current HIP device.
+ *   workspace        device buffer of at least workspace_bytes, 256-byte
+ *                    aligned, owned by the caller (must outlive ring_free); or
+ *                    NULL to let the library allocate (and free) it.
+ *   workspace_bytes  size of `workspace` (ignored when it is NULL)
+ * Enqueues on `stream`: zeroing of every K/V ring row (empty slots are read
+ * by the attention and must be finite, section 1.1), slot_pos = -1 for every
+ * slot, and the index state of committed = 0 for every sequence.
+ * Errors: RING_EINVAL (cfg, alignment), RING_ENOMEM (too small / allocation),
+ * RING_EDEVICE.  On error *out is left NULL and nothing stays allocated.     */
+int ring_init(const ring_config* cfg, void* workspace, size_t workspace_bytes,
+              void* stream, ring_t** out);
+
+/* Pure host: the plan the next ring_begin_step(seq, committed) would run.
+ * `ap_rows` (nullable) receives, for a fold-in plan, the a_step destination
+ * rows: (start + i) % cap for i < n_new, then trash_slot.  For a bulk plan it
+ * receives nothing.  Errors: RING_ERANGE (seq, committed).                  */
+int ring_plan_step(const ring_t* r, int32_t seq, int64_t committed,
+                   ring_plan* out, int32_t* ap_rows);
+
+/* Pure host, no ring needed: the same plan from an explicit state.
+ *   next_pos  committed count of the sequence's previous step (0 at first)
+ *   held_lo   lo of the previous step (0 at first): the ring then holds
+ *             exactly positions [held_lo, next_pos)
+ * Errors: RING_EINVAL (cfg, state), RING_ERANGE (committed).                */
+int ring_plan_from_state(const ring_config* cfg, int64_t next_pos, int64_t held_lo,
+                         int64_t committed, ring_plan* out, int32_t* ap_rows);
+
+/* Append the newly committed rows of sequence `seq` and rebuild its mask.
+ *   committed  committed positions after this step (0 <= committed and
+ *              committed + q_len <= 2^31 - 1)
+ *   k_new      device F16 [n_layer][n_rows][kv_row]: K rows of positions
+ *              [start, committed) in ascending order, NOT yet rotated
+ *   v_new      device F16, same shape: V rows
+ *   n_rows     must equal the plan's n_new (may be 0; then k_new/v_new may
+ *              be NULL)
+ * Device work (section 1.2-1.4): K rotated at its absolute position p and
+ * written with V to slot p % cap of every layer's ring; pad rows of a fold-in
+ * write zeros to trash_slot; slot_pos[p % cap] = p; the F16 mask
+ * [q_len][kv_total] of the sequence becomes 0 (0x0000) for ring slots with
+ * lo <= slot_pos < committed and for the q_len noise slots, -inf (0xFC00)
+ * elsewhere; the RoPE table of the noise positions committed + i is rebuilt.
+ * Errors: RING_ERANGE, RING_ESTATE (n_rows != n_new), RING_EINVAL (NULL),
+ * RING_EDEVICE.                                                             */
+int ring_begin_step(ring_t* r, int32_t seq, int64_t committed,
+                    const void* k_new, const void* v_new, int64_t n_rows,
+                    void* stream);
+
+/* Masked GQA attention of the noise block of every sequence over its ring
+ * (one draft layer), section 1.4 masks, noise block visible both ways.
+ *   q        device F16 [n_seq][q_len][n_head][head_dim], not yet rotated;
+ *            query row i sits at absolute position committed + i
+ *   k_noise  device F16 [n_seq][q_len][kv_row], noise K, not yet rotated
+ *   v_noise  device F16 [n_seq][q_len][kv_row]
+ *   out      device F32 [n_seq][q_len][n_head][head_dim]
+ * Query head h reads KV head h / (n_head / n_head_kv); scores are scaled by
+ * 1/sqrt(head_dim).  The rotated noise K and V are also written to ring rows
+ * cap + j of this layer.  Uses each sequence's state from its last
+ * begin_step.  Errors: RING_ERANGE (layer), RING_EINVAL (NULL), RING_EDEVICE.*/
+int ring_attn(ring_t* r, int32_t layer, const void* q, const void* k_noise,
+              const void* v_noise, float* out, void* stream);
+
+/* Synchronise the ring's last stream and release what the library
+ * allocated.  A caller-owned workspace is not freed.  NULL is accepted.    */
+int ring_free(ring_t* r);
+
+/* Message of the calling thread's last failed call ("" if none).  The
+ * pointer stays valid until the thread's next ring_* call.                  */
+const char* ring_last_error(void);
+
+/* One-line summary in the style of the Luce log line (cap, kv_total, a_step,
+ * layers, F16 cache MiB) written to buf (always NUL-terminated).           */
+int ring_describe(const ring_t* r, char* buf, size_t len);
+
+/* ---- Inspection (synchronous: waits for the device; for tests/tools) ---- */
+
+/* slot_pos of sequence `seq`, int32 [cap], -1 for never-written slots.     */
+int ring_read_slot_pos(const ring_t* r, int32_t seq, int32_t* host_out);
+
+/* Mask of sequence `seq`, F16 bit patterns uint16 [q_len][kv_total].        */
+int ring_read_mask(const ring_t* r, int32_t seq, uint16_t* host_out);
+
+/* Rows [slot0, slot0 + n) of the (seq, layer) ring, converted from the
+ * device layout to plain rows: F16 bit patterns [n][kv_row] for K (rotated)
+ * and for V.  Either output may be NULL.                                    */
+int ring_read_rows(const ring_t* r, int32_t seq, int32_t layer, int32_t slot0,
+                   int32_t n, uint16_t* k_out, uint16_t* v_out);
+
+/* Host-side state of sequence `seq`: next_pos (= committed of its last step)
+ * and held_lo (= that step's lo).                                           */
+int ring_read_state(const ring_t* r, int32_t seq, int64_t* next_pos,
+                    int64_t* held_lo);
+
+/* ---- Profiling ----
+ * Kernel kinds: RING_KERNEL_STEP (append + mask launches of ring_begin_step),
+ * RING_KERNEL_ATTN (attention launch of ring_attn), RING_KERNEL_MERGE
+ * (cross-split merge launch of ring_attn, absent when one split suffices). */
+#define RING_KERNEL_STEP  0
+#define RING_KERNEL_ATTN  1
+#define RING_KERNEL_MERGE 2
+
+/* Time the next `max_launches` launches of each kernel kind with HIP events
+ * bound to the dispatch itself (kernel start to kernel end, no launch gaps).
+ * 0 turns profiling off.  Errors: RING_EINVAL, RING_EDEVICE.               */
+int ring_profile_enable(ring_t* r, int32_t max_launches);
+
+/* Wait for the timed launches of `kernel` to finish, report how many there
+ * were and their summed duration in milliseconds, and start counting anew.
+ * Errors: RING_EINVAL, RING_EDEVICE.                                        */
+int ring_profile_read(ring_t* r, int32_t kernel, int32_t* n_launches, double* total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RING_KV_H */

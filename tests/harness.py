@@ -1,0 +1,235 @@
+"""Drive the HIP ring and the CPU oracle through the same seeded step stream.
+
+Test infrastructure: imports both the binding and the oracle, feeds them the
+same ``workload`` inputs and compares them.  Neither side sees the other's
+results; only the inputs are shared.
+"""
+
+from __future__ import annotations
+
+import bisect
+import os
+from typing import Dict, List, Optional
+
+import numpy as np
+
+import oracle.ring_oracle as ro
+import workload as W
+from workload.configs import T_K, T_V
+
+ATOL = 2e-3   # attention output tolerance (absolute part)
+RTOL = 1e-2   # attention output tolerance (relative part)
+
+
+def f16_ulp_diff(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """Distance in units in the last place between two F16 arrays (finite)."""
+    ia = a.view(np.uint16).astype(np.int32)
+    ib = b.view(np.uint16).astype(np.int32)
+    # map sign-magnitude to a monotone integer line
+    ia = np.where(ia & 0x8000, -(ia & 0x7FFF), ia)
+    ib = np.where(ib & 0x8000, -(ib & 0x7FFF), ib)
+    return np.abs(ia - ib)
+
+
+def check_close(got: np.ndarray, ref: np.ndarray, what: str = "") -> Dict[str, float]:
+    """|got - ref| <= ATOL + RTOL |ref| element by element; returns error stats."""
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    err = np.abs(got.astype(np.float64) - ref.astype(np.float64))
+    tol = ATOL + RTOL * np.abs(ref.astype(np.float64))
+    bad = err > tol
+    stats = {"max_abs": float(err.max()) if err.size else 0.0,
+             "max_rel": float((err / np.maximum(np.abs(ref), 1e-30)).max()) if err.size else 0.0,
+             "max_ratio": float((err / tol).max()) if err.size else 0.0}
+    if bad.any():
+        idx = np.argwhere(bad)[0]
+        raise AssertionError(
+            f"{what}: {int(bad.sum())} of {bad.size} elements out of tolerance; first at "
+            f"{tuple(idx)} got {got[tuple(idx)]} ref {ref[tuple(idx)]}; stats {stats}")
+    return stats
+
+
+class Epochs:
+    """Which generation of row content each position has (rewinds start a new one)."""
+
+    def __init__(self):
+        self.starts = [0]
+        self.ids = [0]
+        self.next_id = 1
+
+    def rewind(self, committed: int) -> None:
+        k = bisect.bisect_left(self.starts, committed)
+        self.starts, self.ids = self.starts[:k], self.ids[:k]
+        if not self.starts or self.starts[-1] != committed:
+            self.starts.append(committed)
+            self.ids.append(self.next_id)
+        else:
+            self.ids[-1] = self.next_id
+        self.next_id += 1
+
+    def of(self, positions: np.ndarray) -> np.ndarray:
+        k = np.searchsorted(np.asarray(self.starts), positions, side="right") - 1
+        return np.asarray(self.ids)[k]
+
+
+class Driver:
+    """One ring (all sequences, all layers) and its oracle twin."""
+
+    def __init__(self, w: W.Workload, n_split: Optional[int] = None, device: str = "cuda:0"):
+        import torch
+        from draft_model_kv_amd import Ring
+        self.torch = torch
+        self.w = w
+        self.dev = torch.device(device)
+        old = os.environ.get("RING_ATTN_SPLITS")
+        if n_split is not None:
+            os.environ["RING_ATTN_SPLITS"] = str(n_split)
+        try:
+            self.ring = Ring(cap=w.cap, q_len=w.q_len, n_head=w.n_head, n_head_kv=w.n_head_kv,
+                             head_dim=w.head_dim, n_layer=w.n_layer, n_seq=w.n_seq,
+                             rope_base=w.rope_base, device=self.dev)
+        finally:
+            if n_split is not None:
+                if old is None:
+                    del os.environ["RING_ATTN_SPLITS"]
+                else:
+                    os.environ["RING_ATTN_SPLITS"] = old
+        self.geo = ro.geometry(w.cap, w.q_len, w.head_dim, w.n_head_kv)
+        self.orc = [ro.RingStep(self.geo, w.n_layer, w.n_head_kv, w.head_dim, w.rope_base)
+                    for _ in range(w.n_seq)]
+        self.epochs = [Epochs() for _ in range(w.n_seq)]
+        self.committed = [0] * w.n_seq
+        self.n_attn = 0
+
+    # ------------------------------------------------------------------ steps
+    def rows(self, seq: int, positions: np.ndarray):
+        """Raw K and V rows [n_layer, n, kv_row] for positions (their epochs)."""
+        w = self.w
+        n = len(positions)
+        k = np.empty((w.n_layer, n, w.kv_row), np.float16)
+        v = np.empty((w.n_layer, n, w.kv_row), np.float16)
+        if n == 0:
+            return k, v
+        ep = self.epochs[seq].of(positions)
+        for e in np.unique(ep):
+            sel = ep == e
+            for layer in range(w.n_layer):
+                k[layer, sel] = W.context_rows(w, seq, layer, T_K, positions[sel], int(e))
+                v[layer, sel] = W.context_rows(w, seq, layer, T_V, positions[sel], int(e))
+        return k, v
+
+    def step(self, seq: int, committed: int):
+        """begin_step on both sides; the plans must agree exactly."""
+        torch = self.torch
+        if committed < self.committed[seq]:
+            self.epochs[seq].rewind(committed)
+        lib_plan, lib_ap = self.ring.plan(seq, committed)
+        op = self.orc[seq].plan(committed)
+        got = (lib_plan.win, lib_plan.lo, lib_plan.start, lib_plan.n_new, bool(lib_plan.bulk))
+        want = (op.win, op.lo, op.start, op.n_new, op.bulk)
+        assert got == want, f"plan mismatch seq {seq} committed {committed}: {got} != {want}"
+        if op.bulk:
+            assert lib_plan.n_chunks == len(op.chunks)
+        else:
+            assert list(lib_ap[: self.geo.a_step]) == op.ap_rows
+        pos = np.arange(op.start, committed, dtype=np.int64)
+        k, v = self.rows(seq, pos)
+        if len(pos):
+            kt = torch.from_numpy(k).to(self.dev)
+            vt = torch.from_numpy(v).to(self.dev)
+            self.ring.begin_step(seq, committed, kt, vt)
+        else:
+            self.ring.begin_step(seq, committed, None, None)
+        self.orc[seq].commit(op, list(k), list(v))
+        self.committed[seq] = committed
+        return op
+
+    def noise(self, layer: int, step: int):
+        w = self.w
+        qs, ks, vs = [], [], []
+        for seq in range(w.n_seq):
+            q, kn, vn = W.noise_inputs(w, seq, layer, step)
+            qs.append(q); ks.append(kn); vs.append(vn)
+        return np.stack(qs), np.stack(ks), np.stack(vs)
+
+    def attn(self, layer: int, step: int):
+        """ring_attn on the device; returns (out, q, k_noise, v_noise) as numpy."""
+        torch = self.torch
+        q, kn, vn = self.noise(layer, step)
+        out = self.ring.attn(layer, torch.from_numpy(q).to(self.dev),
+                             torch.from_numpy(kn).to(self.dev),
+                             torch.from_numpy(vn).to(self.dev))
+        torch.cuda.synchronize(self.dev)
+        self.n_attn += 1
+        return out.cpu().numpy(), q, kn, vn
+
+    def oracle_attn(self, seq: int, layer: int, q, kn, vn, dtype=np.float32):
+        w = self.w
+        return ro.attend(self.orc[seq].caches[layer], self.committed[seq], w.cap,
+                         q[seq], kn[seq], vn[seq], w.n_head, dtype=dtype)
+
+    # ------------------------------------------------------------ comparisons
+    def check_index(self, seq: int):
+        """slot_pos and mask bit-exact against the oracle."""
+        sp = self.ring.slot_pos(seq)
+        want_sp = self.orc[seq].slots.slot_pos
+        if not np.array_equal(sp, want_sp):
+            bad = np.flatnonzero(sp != want_sp)
+            raise AssertionError(f"slot_pos mismatch seq {seq} at slots {bad[:8]}: "
+                                 f"{sp[bad[:8]]} != {want_sp[bad[:8]]}")
+        m = self.ring.mask(seq)
+        want_m = self.orc[seq].mask().view(np.uint16)
+        if not np.array_equal(m, want_m):
+            bad = np.argwhere(m != want_m)
+            raise AssertionError(f"mask mismatch seq {seq} at {bad[:4].tolist()}")
+
+    def check_rows(self, seq: int, layer: int, max_ulp: int = 1) -> int:
+        """Ring rows against the full cache; returns the count of 1-ulp K rows."""
+        g = self.geo
+        k, v = self.ring.rows(seq, layer, 0, g.kv_total)
+        sp = self.orc[seq].slots.slot_pos
+        cache = self.orc[seq].caches[layer]
+        filled = np.flatnonzero(sp >= 0)
+        empty = np.flatnonzero(sp < 0)
+        n_ulp = 0
+        if len(filled):
+            # rows of positions still held (stale ones after a rewind included)
+            want_k = np.empty((len(filled), g.kv_row), np.float16)
+            want_v = np.empty((len(filled), g.kv_row), np.float16)
+            for j, s in enumerate(filled):
+                want_k[j], want_v[j] = cache.row(int(sp[s]))
+            d = f16_ulp_diff(k[filled], want_k)
+            assert d.max() <= max_ulp, f"K rows differ by {d.max()} ulp (seq {seq} layer {layer})"
+            n_ulp = int((d > 0).sum())
+            assert np.array_equal(v[filled].view(np.uint16), want_v.view(np.uint16)), \
+                f"V rows differ (seq {seq} layer {layer})"
+        assert not k[empty].view(np.uint16).any() and not v[empty].view(np.uint16).any(), \
+            "empty ring slots must stay zero"
+        tr = g.trash_slot
+        assert np.isfinite(k[tr:].astype(np.float32)).all() and np.isfinite(v[tr:].astype(np.float32)).all()
+        assert not k[tr].view(np.uint16).any() and not v[tr].view(np.uint16).any(), \
+            "trash slot must hold zeros"
+        return n_ulp
+
+    def check_noise_rows(self, seq: int, layer: int, kn: np.ndarray, vn: np.ndarray):
+        g, w = self.geo, self.w
+        k, v = self.ring.rows(seq, layer, g.cap, w.q_len)
+        pq = ro.noise_positions(self.committed[seq], w.q_len)
+        want = ro.rope_rows_f16(kn[seq], pq, w.n_head_kv, w.head_dim, w.rope_base)
+        assert f16_ulp_diff(k, want).max() <= 1
+        assert np.array_equal(v.view(np.uint16), vn[seq].view(np.uint16))
+
+    def check_attn(self, layer: int, step: int, seqs=None, noise_rows: bool = True) -> Dict[str, float]:
+        out, q, kn, vn = self.attn(layer, step)
+        worst = {"max_abs": 0.0, "max_rel": 0.0, "max_ratio": 0.0}
+        for seq in (range(self.w.n_seq) if seqs is None else seqs):
+            ref = self.oracle_attn(seq, layer, q, kn, vn)
+            st = check_close(out[seq], ref, f"attn seq {seq} layer {layer} step {step}")
+            if noise_rows:
+                self.check_noise_rows(seq, layer, kn, vn)
+            for k_ in worst:
+                worst[k_] = max(worst[k_], st[k_])
+        return worst
+
+    def close(self):
+        self.ring.close()

@@ -1,0 +1,129 @@
+"""The C ABI library on the CPU: it loads, exports the header's functions, and
+its pure-host calls (geometry, step planner, validation) match the oracle.
+No kernel is launched here."""
+
+import os
+import random
+import re
+
+import numpy as np
+import pytest
+
+import oracle.ring_oracle as ro
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ring_kv.h")
+
+rk = pytest.importorskip("draft_model_kv_amd.ring",
+                         reason="libringkv.so not built (python draft_model_kv_amd/build.py)")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(ring_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_binding_exports():
+    assert header_functions() == sorted(rk.EXPORTS)
+
+
+def test_library_exports_every_header_function():
+    import ctypes
+    lib = ctypes.CDLL(rk.LIB_PATH)
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+@pytest.mark.parametrize("cap,q_len,n_head,n_head_kv,n_layer",
+                         [(4096, 8, 32, 8, 5), (64, 8, 32, 8, 1), (32768, 8, 64, 8, 1),
+                          (1, 1, 8, 8, 1), (100, 3, 16, 4, 2), (23, 8, 32, 8, 1)])
+def test_geometry_matches_oracle(cap, q_len, n_head, n_head_kv, n_layer):
+    g = rk.ring_query_geometry(rk.make_config(cap, q_len, n_head, n_head_kv, 128, n_layer))
+    o = ro.geometry(cap, q_len, 128, n_head_kv)
+    assert (g.a_step, g.trash_slot, g.kv_total, g.kv_row) == (o.a_step, o.trash_slot, o.kv_total, o.kv_row)
+    assert g.kv_bytes_per_layer * n_layer == ro.ring_bytes(n_layer, o.kv_row, o.kv_total)
+    assert g.workspace_bytes >= 2 * g.kv_bytes_per_layer * 0 + g.kv_bytes_per_layer * n_layer
+
+
+def test_describe_format_has_the_log_fields():
+    # the geometry behind the Luce log line of the ring notes (section 11, Test 4)
+    g = rk.ring_query_geometry(rk.make_config(4096, 8, 32, 8, 128, 5))
+    assert (g.kv_total, g.a_step) == (4128, 18)
+    assert round(5 * g.kv_bytes_per_layer / 2**20, 1) == 80.6
+
+
+@pytest.mark.parametrize("bad", [
+    dict(cap=0), dict(q_len=0), dict(q_len=33), dict(head_dim=64), dict(n_head=30),
+    dict(n_head_kv=0), dict(n_head=128, n_head_kv=8), dict(n_layer=0), dict(n_seq=0),
+    dict(n_seq=65), dict(rope_base=1.0), dict(rope_base=float("inf")),
+])
+def test_invalid_config_rejected(bad):
+    kw = dict(cap=64, q_len=8, n_head=32, n_head_kv=8, head_dim=128, n_layer=1, n_seq=1,
+              rope_base=1e6)
+    kw.update(bad)
+    with pytest.raises(rk.RingError) as e:
+        rk.ring_query_geometry(rk.make_config(**kw))
+    assert e.value.code == rk.RING_EINVAL
+    assert rk.ring_last_error()
+
+
+def test_planner_state_validation():
+    cfg = rk.make_config(64)
+    for state in [(-1, 0), (10, 11), (200, 100)]:
+        with pytest.raises(rk.RingError) as e:
+            rk.ring_plan_from_state(cfg, state[0], state[1], 100)
+        assert e.value.code == rk.RING_EINVAL
+    with pytest.raises(rk.RingError) as e:
+        rk.ring_plan_from_state(cfg, 0, 0, -1)
+    assert e.value.code == rk.RING_ERANGE
+    with pytest.raises(rk.RingError) as e:
+        rk.ring_plan_from_state(cfg, 0, 0, 2**31 - 8)
+    assert e.value.code == rk.RING_ERANGE
+
+
+def _compare_stream(cap, q_len, commits):
+    cfg = rk.make_config(cap, q_len)
+    g = ro.geometry(cap, q_len, 128, 8)
+    next_pos, held_lo = 0, 0
+    for c in commits:
+        lp, ap = rk.ring_plan_from_state(cfg, next_pos, held_lo, c)
+        op = ro.plan_step(g, c, next_pos, held_lo)
+        assert (lp.win, lp.lo, lp.start, lp.n_new, bool(lp.bulk)) == \
+            (op.win, op.lo, op.start, op.n_new, op.bulk), (cap, q_len, c)
+        if op.bulk:
+            assert ap is None and lp.n_chunks == len(op.chunks)
+        else:
+            assert list(ap) == op.ap_rows
+        next_pos, held_lo = c, op.lo
+
+
+def test_planner_matches_oracle_random_streams():
+    rnd = random.Random(1)
+    for cap in list(range(1, 12)) + [64, 100, 4096]:
+        for q_len in (1, 2, 8, 16):
+            c, commits = 0, []
+            for _ in range(80):
+                c = max(0, c + rnd.choice([-2 * cap, -3, -1, 0, 1, 2, 3, 5, 8, 9, 19, cap, 3 * cap + 1]))
+                commits.append(c)
+            _compare_stream(cap, q_len, commits)
+
+
+def test_planner_on_workload_streams():
+    import workload as W
+    for name in ("tiny_ring", "decode_stream", "long_prompt_wrap", "batched_seqs"):
+        w = W.WORKLOADS[name]
+        for seq in range(min(w.n_seq, 4)):
+            _compare_stream(w.cap, w.q_len, W.commit_stream(w, seq))
+
+
+def test_ring_init_without_device_fails_cleanly():
+    try:
+        import torch
+        if torch.cuda.is_available():
+            pytest.skip("a GPU is present")
+    except ImportError:
+        pass
+    with pytest.raises(rk.RingError) as e:
+        rk.ring_init(rk.make_config(64))
+    assert e.value.code == rk.RING_EDEVICE

@@ -1,0 +1,242 @@
+"""HIP ring path against the CPU oracle, element by element (needs the GPU).
+
+Index work (append plan, slot_pos, mask) must be bit-exact; ring K rows within
+one F16 ulp of the oracle's rounded RoPE (V exact, empty slots zero);
+attention outputs within |gpu - ref| <= 2e-3 + 1e-2 |ref| of the
+fp32-accumulated oracle.
+"""
+
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+
+import workload as W
+from tests.harness import Driver, check_close
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def small(name="edge", **kw):
+    base = dict(name=name, seed=100, cap=64, q_len=8, n_head=32, n_head_kv=8)
+    base.update(kw)
+    return W.Workload(**base)
+
+
+def run_steps(d, commits, layers=None, check_rows=True, seq=0):
+    layers = range(d.w.n_layer) if layers is None else layers
+    stats = []
+    for t, c in enumerate(commits):
+        d.step(seq, c)
+        d.check_index(seq)
+        if check_rows:
+            for layer in layers:
+                d.check_rows(seq, layer)
+        for layer in layers:
+            stats.append(d.check_attn(layer, d.n_attn))
+    return stats
+
+
+def test_init_state_and_committed_zero():
+    d = Driver(small(cap=64))
+    d.check_index(0)                 # slot_pos = -1, only the noise visible
+    d.check_rows(0, 0)               # every ring row zero
+    d.check_attn(0, 0)               # attention with no context at all
+    d.close()
+
+
+def test_single_key_closed_form():
+    """q_len = 1, committed = 0: the only visible key is the noise row, out = its V."""
+    w = small(cap=40, q_len=1)
+    d = Driver(w)
+    out, q, kn, vn = d.attn(0, 0)
+    for h in range(w.n_head):
+        g = h // w.group
+        assert np.array_equal(out[0, 0, h], vn[0, 0, g * 128:(g + 1) * 128].astype(np.float32))
+    d.close()
+
+
+def test_tiny_ring_every_step():
+    w = W.WORKLOADS["tiny_ring"]
+    d = Driver(w)
+    stream = W.commit_stream(w, 0)
+    say("tiny_ring", len(stream), "steps, cap", w.cap)
+    stats = run_steps(d, stream)
+    say("tiny_ring worst", max(s["max_ratio"] for s in stats))
+    d.close()
+
+
+@pytest.mark.parametrize("commits", [
+    [61, 69, 70, 77],                  # wrap inside one fold-in (slots 61..63, 0..4)
+    [128, 129, 136, 192, 200],         # prefill ending at 2 cap, then exact multiples
+    [60, 66, 70],                      # committed crosses cap
+    [100, 118, 137, 138],              # n_new == a_step (fold-in, no pad), then a_step + 1 (bulk)
+    [5, 5, 6, 6],                      # zero-row steps (all pads)
+    [200, 150, 151, 300, 290, 291],    # rewinds past what the ring holds
+    [50, 40, 45, 20, 64, 70],          # rewinds inside the window
+], ids=["wrap_in_fold", "multiple_of_cap", "cross_cap", "a_step_threshold", "zero_rows",
+        "rewind_far", "rewind_near"])
+def test_edge_streams(commits):
+    d = Driver(small(cap=64))
+    run_steps(d, commits)
+    d.close()
+
+
+def test_ragged_cap_and_short_block():
+    """cap not a multiple of 32, q_len 3 (noise block inside a partial tile)."""
+    d = Driver(small(cap=100, q_len=3, n_head=16, n_head_kv=4))
+    run_steps(d, [7, 57, 99, 100, 101, 130, 205, 206, 240])
+    d.close()
+
+
+def test_gqa8_outliers_two_query_blocks():
+    """64 query heads over 8 KV heads: 64 queries per KV head, +-30 outliers."""
+    w = small(cap=256, n_head=64, sigma=1.0, outlier_p=0.01, seed=104)
+    d = Driver(w)
+    run_steps(d, [300, 301, 305, 313, 330])
+    d.close()
+
+
+def test_multi_seq_multi_layer():
+    w = small(cap=128, n_layer=2, n_seq=3, seed=105)
+    d = Driver(w)
+    plan = {0: [10, 11, 19, 140], 1: [500, 501, 509, 510], 2: [127, 128, 129, 136]}
+    for t in range(4):
+        for seq in range(3):
+            d.step(seq, plan[seq][t])
+            d.check_index(seq)
+            for layer in range(2):
+                d.check_rows(seq, layer)
+        for layer in range(2):
+            d.check_attn(layer, t)
+    d.close()
+
+
+@pytest.mark.parametrize("n_split", [1, 2, 3, 7])
+def test_split_counts_agree(n_split):
+    w = small(cap=512, seed=106)
+    d = Driver(w, n_split=n_split)
+    run_steps(d, [700, 703, 708], check_rows=False)
+    d.close()
+
+
+def test_bulk_chunked_foldin_identical():
+    """One bulk step, 1024-row steps and fold-in steps end in the same ring."""
+    w = small(cap=1000, seed=107)
+    final = 2500
+    ways = {"bulk": [final],
+            "chunked": list(range(1024, final, 1024)) + [final],
+            "fold": list(range(18, final, 18)) + [final]}
+    got = {}
+    for name, commits in ways.items():
+        d = Driver(w)
+        for c in commits:
+            d.step(0, c)
+        d.check_index(0)
+        d.check_rows(0, 0)
+        k, v = d.ring.rows(0, 0, 0, d.geo.cap)
+        got[name] = (d.ring.slot_pos(0), d.ring.mask(0), k.view(np.uint16).copy(),
+                     v.view(np.uint16).copy())
+        d.close()
+    for name in ("chunked", "fold"):
+        for a, b in zip(got["bulk"], got[name]):
+            assert np.array_equal(a, b), name
+
+
+def test_error_paths_leave_state_unchanged():
+    from draft_model_kv_amd import RingError
+    from draft_model_kv_amd.ring import RING_ERANGE, RING_ESTATE, RING_EINVAL
+    import torch
+    d = Driver(small(cap=64))
+    d.step(0, 10)
+    before = (d.ring.state(0), d.ring.slot_pos(0).copy(), d.ring.mask(0).copy())
+    k = torch.zeros((1, 3, 1024), dtype=torch.float16, device="cuda")
+    with pytest.raises(RingError) as e:
+        d.ring.begin_step(0, 12, k, k)          # plan says 2 rows
+    assert e.value.code == RING_ESTATE
+    with pytest.raises(RingError) as e:
+        d.ring.begin_step(1, 12, k, k)          # no sequence 1
+    assert e.value.code == RING_ERANGE
+    q = torch.zeros((1, 8, 32, 128), dtype=torch.float16, device="cuda")
+    kn = torch.zeros((1, 8, 1024), dtype=torch.float16, device="cuda")
+    with pytest.raises(RingError) as e:
+        d.ring.attn(1, q, kn, kn)                # no layer 1
+    assert e.value.code == RING_ERANGE
+    from draft_model_kv_amd import ring_attn
+    out = torch.zeros((1, 8, 32, 128), dtype=torch.float32, device="cuda")
+    with pytest.raises(RingError) as e:
+        ring_attn(d.ring.handle, 0, q.data_ptr() + 2, kn.data_ptr(), kn.data_ptr(), out.data_ptr())
+    assert e.value.code == RING_EINVAL
+    after = (d.ring.state(0), d.ring.slot_pos(0), d.ring.mask(0))
+    assert before[0] == after[0] and np.array_equal(before[1], after[1]) and np.array_equal(before[2], after[2])
+    d.step(0, 12)
+    d.check_index(0)
+    d.check_attn(0, 0)
+    d.close()
+
+
+# ---------------------------------------------------------------------------
+# Full workload sizes, sampled checkpoints (every step runs on the device).
+# ---------------------------------------------------------------------------
+def _checkpoints(n, every, extra=()):
+    pts = set(range(0, n, every)) | {0, 1, n - 1} | set(extra)
+    return {p for p in pts if 0 <= p < n}
+
+
+def _run_workload(name, every, rows_at=(0,), max_steps=None):
+    w = W.WORKLOADS[name]
+    d = Driver(w)
+    streams = [W.commit_stream(w, s) for s in range(w.n_seq)]
+    n_warm = W.n_warmup_steps(w)
+    say(name, "warm-up", n_warm, "steps")
+    for t in range(n_warm):
+        for seq in range(w.n_seq):
+            d.step(seq, streams[seq][t])
+    for seq in range(w.n_seq):
+        d.check_index(seq)
+        for layer in range(w.n_layer):
+            d.check_rows(seq, layer)
+    n = len(streams[0]) - n_warm if max_steps is None else min(max_steps, len(streams[0]) - n_warm)
+    crossings = [t for t in range(n) for seq in range(w.n_seq)
+                 if streams[seq][n_warm + t - 1] < w.cap <= streams[seq][n_warm + t]]
+    pts = _checkpoints(n, every, crossings)
+    worst = 0.0
+    for t in range(n):
+        for seq in range(w.n_seq):
+            d.step(seq, streams[seq][n_warm + t])
+        for layer in range(w.n_layer):
+            if t in pts:
+                st = d.check_attn(layer, t, noise_rows=(layer == 0))
+                worst = max(worst, st["max_ratio"])
+            else:
+                d.attn(layer, t)
+        if t in pts:
+            for seq in range(w.n_seq):
+                d.check_index(seq)
+        if t in rows_at:
+            for seq in range(min(w.n_seq, 2)):
+                d.check_rows(seq, 0)
+    say(name, "steps", n, "checked", len(pts), "worst err/tol", round(worst, 4))
+    d.close()
+
+
+def test_decode_stream_full():
+    _run_workload("decode_stream", every=50, rows_at=(0, 1999))
+
+
+def test_long_prompt_wrap_full():
+    _run_workload("long_prompt_wrap", every=32, rows_at=(511,))
+
+
+def test_batched_seqs_full():
+    _run_workload("batched_seqs", every=16, rows_at=(255,))
+
+
+def test_large_window_full():
+    _run_workload("large_window", every=32, rows_at=(255,))
