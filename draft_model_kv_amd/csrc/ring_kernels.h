@@ -26,6 +26,7 @@ struct StepArgs {
   double* rope_noise;        // [q_len][64][2] (cos, sin) at committed + i
   const double* inv_freq;    // [64] theta_i
   int64_t start;             // first new position
+  int32_t start_mod;         // start % cap
   int64_t committed;
   int64_t lo;
   int32_t n_new;             // rows per layer in k_new / v_new

@@ -22,6 +22,7 @@ constexpr float kNegInf = -__builtin_inff();
 // log2(e) / sqrt(128): folds the 1/sqrt(head_dim) score scale and the
 // change of base for exp2 into the query.
 constexpr double kQScale = 1.4426950408889634074 / 11.313708498984760390;
+constexpr int kNoiseStride = 136;  // LDS row stride (halves) of staged noise rows
 
 // ---------------------------------------------------------------------------
 // F16 helpers
@@ -30,31 +31,31 @@ __device__ inline double f16_to_f64(uint16_t b) {
   return (double)__builtin_bit_cast(_Float16, b);
 }
 
-// binary64 -> binary16, one rounding, round to nearest even (subnormals and
-// overflow to infinity included).
+// binary64 -> binary16 with a single rounding to nearest even.  Rounds to
+// binary32 with round-to-odd first, then to binary16 with the hardware's
+// round-to-nearest-even: binary32 carries 24 >= 11 + 2 significand bits, so
+// the two roundings equal one (Boldo and Melquiond, "Emulation of FMA and
+// correctly rounded sums: proved algorithms using rounding to odd", IEEE
+// Trans. Computers 57(4), 2008).
 __device__ inline uint16_t f64_to_f16_rne(double x) {
-  const uint64_t b = __builtin_bit_cast(uint64_t, x);
-  const uint16_t sign = (uint16_t)((b >> 48) & 0x8000u);
-  const int exp = (int)((b >> 52) & 0x7FF);
-  const uint64_t man = b & ((1ull << 52) - 1);
-  if (exp == 0x7FF) return sign | 0x7C00u | (man ? 0x200u : 0u);
-  if (exp == 0) return sign;  // binary64 subnormal: far below binary16 range
-  const int e = exp - 1023;
-  if (e > 15) return sign | 0x7C00u;
-  const uint64_t full = man | (1ull << 52);
-  const int shift = (e >= -14) ? 42 : 28 - e;
-  if (shift > 62) return sign;
-  uint64_t q = full >> shift;
-  const uint64_t rem = full & ((1ull << shift) - 1);
-  const uint64_t halfway = 1ull << (shift - 1);
-  if (rem > halfway || (rem == halfway && (q & 1))) ++q;
-  if (e >= -14) {
-    int he = e + 15;
-    if (q == 2048) { q = 1024; ++he; }
-    if (he >= 31) return sign | 0x7C00u;
-    return sign | (uint16_t)(he << 10) | (uint16_t)(q & 0x3FF);
+  float f = (float)x;
+  const double back = (double)f;
+  if (back != x) {
+    uint32_t b = __builtin_bit_cast(uint32_t, f);
+    if (fabs(back) > fabs(x)) b -= 1;  // round-to-nearest went away from zero
+    b |= 1u;                           // truncation with the sticky bit set
+    f = __builtin_bit_cast(float, b);
   }
-  return sign | (uint16_t)q;  // subnormal; q == 1024 is the smallest normal
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// Work-group barrier that orders LDS only: global loads and stores issued
+// before it stay in flight (a full __syncthreads() would first wait for all of
+// them).  No kernel here passes data between waves through global memory.
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // Rotate the pair (x, y) by the angle whose cosine and sine are (c, s); no
@@ -79,6 +80,8 @@ __global__ __launch_bounds__(256) void k_ring_step(StepArgs a) {
   const int64_t layer_stride = head_stride * a.n_head_kv;
 
   if (blk < n_row_blocks) {
+    // One row (one position, all KV heads of one layer) per work-group.
+    __shared__ double2 cs_row[64];  // (cos, sin) of p * theta_f
     const int layer = blk / rows_per_layer;
     const int i = blk - layer * rows_per_layer;
     const bool pad = i >= a.n_rows;
@@ -92,39 +95,38 @@ __global__ __launch_bounds__(256) void k_ring_step(StepArgs a) {
       slot = (int)(p % a.cap);
       ksrc = a.k_new + ((int64_t)layer * a.n_new + idx) * kv_row;
       vsrc = a.v_new + ((int64_t)layer * a.n_new + idx) * kv_row;
+      if (t < 64) {
+        double sn, cs;
+        sincos((double)p * a.inv_freq[t], &sn, &cs);
+        cs_row[t] = make_double2(cs, sn);
+      }
     } else {
       slot = a.trash_slot;
     }
+    lds_barrier();
     const int s_t = slot & (kTile - 1);
     const int64_t tile_off = (int64_t)(slot >> 5) * kTileHalves;
     uint16_t* kl = a.kring + layer * layer_stride + tile_off;
     uint16_t* vl = a.vring + layer * layer_stride + tile_off;
-    // item = (head, two neighbouring rotation pairs)
-    for (int item = t; item < a.n_head_kv * 32; item += 256) {
-      const int h = item >> 5;
-      const int f0 = (item & 31) * 2;
+    for (int item = t; item < a.n_head_kv * 64; item += 256) {
+      const int h = item >> 6, f = item & 63;
       uint16_t* kd = kl + h * head_stride;
       uint16_t* vd = vl + h * head_stride;
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int f = f0 + u;
-        if (pad) {
-          kd[k_frag_index(s_t, f)] = 0;
-          kd[k_frag_index(s_t, f + 64)] = 0;
-          vd[v_frag_index(s_t, f)] = 0;
-          vd[v_frag_index(s_t, f + 64)] = 0;
-        } else {
-          const double x = f16_to_f64(ksrc[h * kHeadDim + f]);
-          const double y = f16_to_f64(ksrc[h * kHeadDim + f + 64]);
-          double sn, cs;
-          sincos((double)p * a.inv_freq[f], &sn, &cs);
-          double xr, yr;
-          rot_pair(x, y, cs, sn, xr, yr);
-          kd[k_frag_index(s_t, f)] = f64_to_f16_rne(xr);
-          kd[k_frag_index(s_t, f + 64)] = f64_to_f16_rne(yr);
-          vd[v_frag_index(s_t, f)] = vsrc[h * kHeadDim + f];
-          vd[v_frag_index(s_t, f + 64)] = vsrc[h * kHeadDim + f + 64];
-        }
+      if (pad) {
+        kd[k_frag_index(s_t, f)] = 0;
+        kd[k_frag_index(s_t, f + 64)] = 0;
+        vd[v_frag_index(s_t, f)] = 0;
+        vd[v_frag_index(s_t, f + 64)] = 0;
+      } else {
+        const double x = f16_to_f64(ksrc[h * kHeadDim + f]);
+        const double y = f16_to_f64(ksrc[h * kHeadDim + f + 64]);
+        const double2 cs = cs_row[f];
+        double xr, yr;
+        rot_pair(x, y, cs.x, cs.y, xr, yr);
+        kd[k_frag_index(s_t, f)] = f64_to_f16_rne(xr);
+        kd[k_frag_index(s_t, f + 64)] = f64_to_f16_rne(yr);
+        vd[v_frag_index(s_t, f)] = vsrc[h * kHeadDim + f];
+        vd[v_frag_index(s_t, f + 64)] = vsrc[h * kHeadDim + f + 64];
       }
     }
     return;
@@ -147,7 +149,8 @@ __global__ __launch_bounds__(256) void k_ring_step(StepArgs a) {
   bool vis;
   if (s < a.cap) {
     int64_t sp = a.slot_pos[s];
-    const int64_t d = ((int64_t)s - a.start % a.cap + a.cap) % a.cap;
+    int d = s - a.start_mod;  // offset of slot s from the first new slot, mod cap
+    if (d < 0) d += a.cap;
     if (d < a.n_new) {
       sp = a.start + d;
       a.slot_pos[s] = (int32_t)sp;
@@ -254,10 +257,25 @@ __device__ inline void attend_tile(const half8 (&kc)[8], const half8 (&vc)[8],
   }
 }
 
-template <int MB, int NW>
+// Work-group: NW waves for one (sequence, KV head, split).  The split-0
+// work-group of each (sequence, head) also owns the noise block.
+//
+// Order of work (memory latency is the cost on a 4096-slot ring, so every
+// load is issued as early as its inputs allow):
+//   1. loads for the query build, for the noise rows (split 0) and for the
+//      wave's first ring tile;
+//   2. the work-group rotates/scales/splits the queries into LDS and, in
+//      split 0, rotates the noise K rows, stages noise K/V in LDS and stores
+//      them to ring rows cap + r; one barrier;
+//   3. split 0's noise wave attends the noise block from LDS while the ring
+//      tiles are still in flight;
+//   4. each wave streams its ring tiles;
+//   5. waves merge through LDS; the work-group writes its output or partial.
+template <int MB, int NW, int NR>
 __global__ __launch_bounds__(NW * 64) void k_ring_attn(AttnArgs a) {
   constexpr int MP = MB * 32;
   constexpr int OS = 132;  // LDS row stride (floats) of the merged output
+  constexpr int NT = NW * 64;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int hl = lane >> 5;
@@ -281,15 +299,16 @@ __global__ __launch_bounds__(NW * 64) void k_ring_attn(AttnArgs a) {
   const double* rope = a.rope_noise + (int64_t)seq * a.q_len * 128;
   const uint16_t* mask_seq = a.mask + (int64_t)seq * a.q_len * a.kv_total;
 
-  // ---- ring tiles of this split (visible ring slots are [0, win)); start
-  //      their loads before anything else.
+  // Ring tiles of this split: the visible ring slots are [0, win).
   const int win = a.win[seq];
   const int nvt = (win + kTile - 1) / kTile;
   const int per = (nvt + a.n_split - 1) / a.n_split;
   const int t0 = min(nvt, split * per);
   const int t1 = min(nvt, t0 + per);
-  const uint16_t* kh = a.kring + seq * a.seq_stride + a.layer_offset + g * a.head_stride;
-  const uint16_t* vh = a.vring + seq * a.seq_stride + a.layer_offset + g * a.head_stride;
+  uint16_t* kh = a.kring + seq * a.seq_stride + a.layer_offset + g * a.head_stride;
+  uint16_t* vh = a.vring + seq * a.seq_stride + a.layer_offset + g * a.head_stride;
+  const bool noise_wg = split == 0;
+  const bool noise_wave = noise_wg && wave == (t1 - t0) % NW;
 
   // Query row (noise position index) of this lane's query in block mb.
   int qrow[MB];
@@ -299,6 +318,68 @@ __global__ __launch_bounds__(NW * 64) void k_ring_attn(AttnArgs a) {
     qrow[mb] = n < a.m ? n / a.group : 0;
   }
 
+  // Every global load below is issued unconditionally from an in-bounds
+  // (clamped) address, in the order its data is needed, and selected
+  // afterwards: the compiler can then wait for each group alone instead of
+  // draining every outstanding load at a control-flow join.
+
+  // ---- 1a. noise rows (used by split 0): thread item = (row r, freq f),
+  //      NR rounds of two items per thread (NR * 2 * NT >= q_len * 64).
+  const int n_noise_items = noise_wg ? a.q_len * 64 : 0;
+  constexpr int NI = 2 * NR;
+  uint16_t nkx[NI], nky[NI], nvx[NI], nvy[NI];
+  double2 ncs[NI];
+  const uint16_t* knb = a.k_noise + (int64_t)seq * a.q_len * kv_row + g * kHeadDim;
+  const uint16_t* vnb = a.v_noise + (int64_t)seq * a.q_len * kv_row + g * kHeadDim;
+  auto load_noise = [&]() {
+#pragma unroll
+    for (int u = 0; u < NI; ++u) {
+      const int item = min((int)threadIdx.x + u * NT, a.q_len * 64 - 1);
+      const int r = item >> 6, f = item & 63;
+      nkx[u] = knb[(int64_t)r * kv_row + f];
+      nky[u] = knb[(int64_t)r * kv_row + f + 64];
+      nvx[u] = vnb[(int64_t)r * kv_row + f];
+      nvy[u] = vnb[(int64_t)r * kv_row + f + 64];
+      ncs[u] = *(const double2*)(rope + (r * 64 + f) * 2);
+    }
+  };
+  // Mask of the noise block for accumulator row j (slot cap + row(j)); only
+  // loaded here, used by the noise wave after the barrier.
+  // Every work-group issues these few L2-resident loads, so the prologue
+  // stays one basic block (only split 0 uses them).
+  uint16_t nmraw[MB][16];
+  load_noise();
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const uint16_t* mr = mask_seq + (int64_t)qrow[mb] * a.kv_total;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int r = 8 * (j >> 2) + 4 * hl + (j & 3);
+      nmraw[mb][j] = mr[min(a.cap + r, a.kv_total - 1)];
+    }
+  }
+
+  // ---- 1b. loads for the query build: thread item = (mb, chunk pair c,
+  //      lane ln); x = dims 16c + 8h + e, y = the same dims + 64.
+  half8 qx[MB], qy[MB];
+  double2 qcs[MB][8];
+#pragma unroll
+  for (int k = 0; k < MB; ++k) {
+    const int item = threadIdx.x + k * NT;
+    const int c = (item >> 6) & 3, ln = item & 63;
+    const int n = min((item >> 8) * 32 + (ln & 31), a.m - 1), h2 = ln >> 5;
+    const int i = n / a.group, hh = n - i * a.group;
+    const uint16_t* qp =
+        a.q + (((int64_t)seq * a.q_len + i) * a.n_head + g * a.group + hh) * kHeadDim;
+    qx[k] = *(const half8*)(qp + 16 * c + 8 * h2);
+    qy[k] = *(const half8*)(qp + 16 * (c + 4) + 8 * h2);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      qcs[k][e] = *(const double2*)(rope + (i * 64 + 16 * c + 8 * h2 + e) * 2);
+  }
+
+  // ---- 1c. the wave's first ring tile (a wave without tiles loads its
+  //      split's first tile again and ignores it).
   auto load_tile = [&](int tile, half8 (&kc)[8], half8 (&vc)[8], uint32_t (&mw)[MB][8]) {
     const half8* kt = (const half8*)(kh + (int64_t)tile * kTileHalves);
     const half8* vt = (const half8*)(vh + (int64_t)tile * kTileHalves);
@@ -317,49 +398,70 @@ __global__ __launch_bounds__(NW * 64) void k_ring_attn(AttnArgs a) {
       }
     }
   };
-
   int tile = t0 + wave;
+  const int tile_last = max(t1 - 1, 0);
   half8 kc[8], vc[8];
   uint32_t mw[MB][8];
-  if (tile < t1) load_tile(tile, kc, vc, mw);
+  load_tile(min(tile, tile_last), kc, vc, mw);
 
-  // ---- queries of this KV head's group, rotated at committed + i, scaled by
-  //      log2(e)/sqrt(head_dim), split into hi + lo F16; built once per
-  //      work-group in LDS (fragment order: [mb][hi/lo][chunk][lane]).
+  // ---- 2a. queries: rotate at committed + i, scale by log2(e)/sqrt(d),
+  //      split into hi + lo F16 (fragment order [mb][hi/lo][chunk][lane]);
+  //      queries past q_len * group are zero.
   __shared__ half8 q_lds[MB * 2 * 8 * 64];
-  for (int item = threadIdx.x; item < MB * 4 * 64; item += NW * 64) {
-    const int mb = item / 256, c = (item >> 6) & 3, ln = item & 63;
-    const int n = mb * 32 + (ln & 31), h2 = ln >> 5;
-    const bool valid = n < a.m;
-    const int i = valid ? n / a.group : 0;
-    const int hh = valid ? n - i * a.group : 0;
-    const uint16_t* qp =
-        a.q + (((int64_t)seq * a.q_len + i) * a.n_head + g * a.group + hh) * kHeadDim;
-    half8 x = half8{}, y = half8{};
-    if (valid) {
-      x = *(const half8*)(qp + 16 * c + 8 * h2);
-      y = *(const half8*)(qp + 16 * (c + 4) + 8 * h2);
-    }
+#pragma unroll
+  for (int k = 0; k < MB; ++k) {
+    const int item = threadIdx.x + k * NT;
+    const int mb = item >> 8, c = (item >> 6) & 3, ln = item & 63;
+    const bool valid = mb * 32 + (ln & 31) < a.m;
     half8 xh, xl, yh, yl;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int f = 16 * c + 8 * h2 + e;
-      const double cs = rope[(i * 64 + f) * 2], sn = rope[(i * 64 + f) * 2 + 1];
-      double xr, yr;
-      rot_pair((double)x[e], (double)y[e], cs, sn, xr, yr);
-      xr *= kQScale;
-      yr *= kQScale;
-      xh[e] = (_Float16)(float)xr;
-      yh[e] = (_Float16)(float)yr;
-      xl[e] = (_Float16)(float)(xr - (double)xh[e]);
-      yl[e] = (_Float16)(float)(yr - (double)yh[e]);
+    for (int e = 0; e < 8; e += 2) {
+      float xr[2], yr[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const float cs = (float)qcs[k][e + u].x, sn = (float)qcs[k][e + u].y;
+        const float x = valid ? (float)qx[k][e + u] : 0.0f;
+        const float y = valid ? (float)qy[k][e + u] : 0.0f;
+        xr[u] = (x * cs - y * sn) * (float)kQScale;
+        yr[u] = (y * cs + x * sn) * (float)kQScale;
+      }
+      // hi = x rounded toward zero to F16, lo = the rest rounded likewise:
+      // hi + lo carries about 22 significant bits of x.
+      const auto xhp = __builtin_amdgcn_cvt_pkrtz(xr[0], xr[1]);
+      const auto yhp = __builtin_amdgcn_cvt_pkrtz(yr[0], yr[1]);
+      const auto xlp = __builtin_amdgcn_cvt_pkrtz(xr[0] - (float)xhp[0], xr[1] - (float)xhp[1]);
+      const auto ylp = __builtin_amdgcn_cvt_pkrtz(yr[0] - (float)yhp[0], yr[1] - (float)yhp[1]);
+      xh[e] = xhp[0]; xh[e + 1] = xhp[1];
+      yh[e] = yhp[0]; yh[e + 1] = yhp[1];
+      xl[e] = xlp[0]; xl[e + 1] = xlp[1];
+      yl[e] = ylp[0]; yl[e + 1] = ylp[1];
     }
     q_lds[((mb * 2 + 0) * 8 + c) * 64 + ln] = xh;
     q_lds[((mb * 2 + 0) * 8 + c + 4) * 64 + ln] = yh;
     q_lds[((mb * 2 + 1) * 8 + c) * 64 + ln] = xl;
     q_lds[((mb * 2 + 1) * 8 + c + 4) * 64 + ln] = yl;
   }
-  __syncthreads();
+
+  // ---- 2b. noise rows (split 0): rotate K at committed + r (fp64, one
+  //      rounding to F16), stage K and V in LDS as plain rows.
+  __shared__ uint16_t nk_lds[32 * kNoiseStride];
+  __shared__ uint16_t nv_lds[32 * kNoiseStride];
+  //      Every work-group runs this (a few instructions) so that no branch
+  //      holds the loads of 1a; items past q_len * 64 repeat the last item
+  //      and store the same values again.
+#pragma unroll
+  for (int u = 0; u < NI; ++u) {
+    const int item = min((int)threadIdx.x + u * NT, a.q_len * 64 - 1);
+    const int r = item >> 6, f = item & 63;
+    double xr, yr;
+    rot_pair(f16_to_f64(nkx[u]), f16_to_f64(nky[u]), ncs[u].x, ncs[u].y, xr, yr);
+    nk_lds[r * kNoiseStride + f] = f64_to_f16_rne(xr);
+    nk_lds[r * kNoiseStride + f + 64] = f64_to_f16_rne(yr);
+    nv_lds[r * kNoiseStride + f] = nvx[u];
+    nv_lds[r * kNoiseStride + f + 64] = nvy[u];
+  }
+  lds_barrier();
+
   QFrag<MB> qf;
   if constexpr (!QFrag<MB>::kLds) {
 #pragma unroll
@@ -381,55 +483,22 @@ __global__ __launch_bounds__(NW * 64) void k_ring_attn(AttnArgs a) {
     for (int b = 0; b < 4; ++b) o[mb][b] = f32x16{};
   }
 
-  // One query block: the next tile's loads are issued before the current
-  // tile is processed (two tiles in registers).  Two query blocks have no
-  // room for that; their next load follows the current tile.
-  constexpr bool kPrefetch = MB == 1;
-  while (tile < t1) {
-    const int next = tile + NW;
-    if constexpr (kPrefetch) {
-      half8 kn[8], vn[8];
-      uint32_t mn[MB][8];
-      if (next < t1) load_tile(next, kn, vn, mn);
-      attend_tile<MB>(kc, vc, mw, a.cap - tile * kTile, hl, qf, q_lds, lane, m_run, l_run, o);
-      if (next < t1) {
+  // ---- 3. noise block, visible to every query.
+  uint32_t nmw[MB][8];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) { kc[c] = kn[c]; vc[c] = vn[c]; }
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) mw[mb][j] = mn[mb][j];
-      }
-    } else {
-      attend_tile<MB>(kc, vc, mw, a.cap - tile * kTile, hl, qf, q_lds, lane, m_run, l_run, o);
-      if (next < t1) load_tile(next, kc, vc, mw);
-    }
-    tile = next;
-  }
-
-  // ---- noise block: rows r < q_len of k_noise / v_noise at committed + r,
-  //      visible to every query (split 0, the wave with the fewest tiles).
-  if (split == 0 && wave == (t1 - t0) % NW) {
-    const uint16_t* knb = a.k_noise + (int64_t)seq * a.q_len * kv_row + g * kHeadDim;
-    const uint16_t* vnb = a.v_noise + (int64_t)seq * a.q_len * kv_row + g * kHeadDim;
+    for (int w2 = 0; w2 < 8; ++w2)
+      nmw[mb][w2] = (uint32_t)nmraw[mb][2 * w2] | ((uint32_t)nmraw[mb][2 * w2 + 1] << 16);
+  if (noise_wave) {
+    // Rows r >= q_len of the 32-row noise tile are zero (their LDS rows are
+    // read but not used).
+    half8 nkc[8], nvc[8];
     const bool rv = col < a.q_len;
-    const int r = rv ? col : 0;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      half8 x = half8{}, y = half8{};
-      if (rv) {
-        x = *(const half8*)(knb + (int64_t)r * kv_row + 16 * c + 8 * hl);
-        y = *(const half8*)(knb + (int64_t)r * kv_row + 16 * (c + 4) + 8 * hl);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int f = 16 * c + 8 * hl + e;
-        const double cs = rope[(r * 64 + f) * 2], sn = rope[(r * 64 + f) * 2 + 1];
-        double xr, yr;
-        rot_pair((double)x[e], (double)y[e], cs, sn, xr, yr);
-        kc[c][e] = __builtin_bit_cast(_Float16, f64_to_f16_rne(xr));
-        kc[c + 4][e] = __builtin_bit_cast(_Float16, f64_to_f16_rne(yr));
-      }
+    for (int c = 0; c < 8; ++c) {
+      const half8 kk = *(const half8*)(nk_lds + col * kNoiseStride + 16 * c + 8 * hl);
+      nkc[c] = rv ? kk : half8{};
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -437,43 +506,54 @@ __global__ __launch_bounds__(NW * 64) void k_ring_attn(AttnArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int slot = 16 * ks + 8 * (e >> 2) + 4 * hl + (e & 3);
-        vc[j][e] = slot < a.q_len
-                       ? __builtin_bit_cast(_Float16, vnb[(int64_t)slot * kv_row + 32 * b + col])
-                       : (_Float16)0.0f;
+        const uint16_t vv = nv_lds[slot * kNoiseStride + 32 * b + col];
+        nvc[j][e] = __builtin_bit_cast(_Float16, (uint16_t)(slot < a.q_len ? vv : 0));
       }
     }
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const uint16_t* mr = mask_seq + (int64_t)qrow[mb] * a.kv_total + a.cap;
-#pragma unroll
-      for (int w2 = 0; w2 < 8; ++w2) {
-        const int r0 = 8 * (w2 >> 1) + 4 * hl + 2 * (w2 & 1);
-        const uint32_t lo = r0 < a.q_len ? mr[r0] : 0xFC00u;
-        const uint32_t hi = r0 + 1 < a.q_len ? mr[r0 + 1] : 0xFC00u;
-        mw[mb][w2] = lo | (hi << 16);
-      }
-    }
-    attend_tile<MB>(kc, vc, mw, a.q_len, hl, qf, q_lds, lane, m_run, l_run, o);
+    attend_tile<MB>(nkc, nvc, nmw, a.q_len, hl, qf, q_lds, lane, m_run, l_run, o);
+  }
 
-    // Rotated noise rows into ring rows cap + r of this layer.
-    uint16_t* khw = a.kring + seq * a.seq_stride + a.layer_offset + g * a.head_stride;
-    uint16_t* vhw = a.vring + seq * a.seq_stride + a.layer_offset + g * a.head_stride;
-    if (rv) {
-      const int slot = a.cap + col;
-      uint16_t* kt = khw + (int64_t)(slot >> 5) * kTileHalves;
+  // ---- 4. ring tiles.  One query block: the next tile's loads are issued
+  //      before the current tile is processed (two tiles in registers); two
+  //      query blocks have no room for that.
+  constexpr bool kPrefetch = MB == 1;
+  while (tile < t1) {
+    const int next = tile + NW;
+    if constexpr (kPrefetch) {
+      // The last prefetch re-reads the current tile (already in cache).
+      half8 kn[8], vn[8];
+      uint32_t mn[MB][8];
+      load_tile(next < t1 ? next : tile, kn, vn, mn);
+      attend_tile<MB>(kc, vc, mw, a.cap - tile * kTile, hl, qf, q_lds, lane, m_run, l_run, o);
 #pragma unroll
-      for (int c = 0; c < 8; ++c)
-        *(half8*)(kt + k_frag_index(slot & 31, 16 * c + 8 * hl)) = kc[c];
+      for (int c = 0; c < 8; ++c) { kc[c] = kn[c]; vc[c] = vn[c]; }
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) mw[mb][j] = mn[mb][j];
+    } else {
+      attend_tile<MB>(kc, vc, mw, a.cap - tile * kTile, hl, qf, q_lds, lane, m_run, l_run, o);
+      if (next < t1) load_tile(next, kc, vc, mw);
     }
-    for (int rr = 0; rr < a.q_len; ++rr) {
-      const int slot = a.cap + rr;
-      uint16_t* vt = vhw + (int64_t)(slot >> 5) * kTileHalves;
-      vt[v_frag_index(slot & 31, lane)] = vnb[(int64_t)rr * kv_row + lane];
-      vt[v_frag_index(slot & 31, lane + 64)] = vnb[(int64_t)rr * kv_row + lane + 64];
+    tile = next;
+  }
+
+  // Rotated noise rows into ring rows cap + r of this layer (from LDS, after
+  // the ring loads so these stores delay no wait).
+  if (noise_wg) {
+    for (int item = threadIdx.x; item < n_noise_items; item += NT) {
+      const int r = item >> 6, f = item & 63;
+      const int slot = a.cap + r;
+      uint16_t* kt = kh + (int64_t)(slot >> 5) * kTileHalves;
+      uint16_t* vt = vh + (int64_t)(slot >> 5) * kTileHalves;
+      kt[k_frag_index(slot & 31, f)] = nk_lds[r * kNoiseStride + f];
+      kt[k_frag_index(slot & 31, f + 64)] = nk_lds[r * kNoiseStride + f + 64];
+      vt[v_frag_index(slot & 31, f)] = nv_lds[r * kNoiseStride + f];
+      vt[v_frag_index(slot & 31, f + 64)] = nv_lds[r * kNoiseStride + f + 64];
     }
   }
 
-  // ---- merge the waves of this work-group through LDS (fixed wave order).
+  // ---- 5. merge the waves of this work-group through LDS (fixed wave order).
   __shared__ float sm_m[NW][MP];
   __shared__ float sm_l[NW][MP];
   __shared__ float sm_ml[MP][2];
@@ -485,7 +565,7 @@ __global__ __launch_bounds__(NW * 64) void k_ring_attn(AttnArgs a) {
       sm_l[wave][mb * 32 + col] = l_run[mb];
     }
   }
-  __syncthreads();
+  lds_barrier();
   float scale[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
@@ -525,11 +605,11 @@ __global__ __launch_bounds__(NW * 64) void k_ring_attn(AttnArgs a) {
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
 
   // ---- write the final output (one split) or this split's partial.
-  for (int item = threadIdx.x; item < a.m * 32; item += NW * 64) {
+  for (int item = threadIdx.x; item < a.m * 32; item += NT) {
     const int n = item >> 5, d4 = item & 31;
     float4 v = *(const float4*)&sm_o[n * OS + 4 * d4];
     if (a.n_split == 1) {
@@ -548,37 +628,60 @@ __global__ __launch_bounds__(NW * 64) void k_ring_attn(AttnArgs a) {
     }
   }
 }
+
 // ---------------------------------------------------------------------------
-// Cross-split merge: out = sum_t acc_t 2^(m_t - M) / sum_t l_t 2^(m_t - M).
+// Cross-split merge: out = sum_t acc_t 2^(m_t - M) / sum_t l_t 2^(m_t - M),
+// M = max_t m_t.  One wave per (sequence, KV head, query): lane t holds split
+// t's (m, l); lane (h, d4) sums splits h, h + 2, ... of dims 4 d4 .. 4 d4 + 3.
+// Every load is issued before the first use (2 KMAX >= n_split, n_split <= 64).
 // ---------------------------------------------------------------------------
+template <int KMAX>
 __global__ __launch_bounds__(256) void k_ring_merge(MergeArgs a) {
-  const int64_t item = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t total = (int64_t)a.n_units * a.m * 32;
-  if (item >= total) return;
-  const int d4 = (int)(item & 31);
-  const int64_t un = item >> 5;
-  const int n = (int)(un % a.m);
-  const int unit = (int)(un / a.m);
-  const float* ml = a.part_ml + ((int64_t)unit * a.n_split * a.mpad + n) * 2;
-  const float* acc = a.part_acc + ((int64_t)unit * a.n_split * a.mpad + n) * kHeadDim + 4 * d4;
-  float mx = kNegInf;
-  for (int t = 0; t < a.n_split; ++t) mx = fmaxf(mx, ml[(int64_t)t * a.mpad * 2]);
-  float lt = 0.0f;
-  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int t = 0; t < a.n_split; ++t) {
-    const float mt = ml[(int64_t)t * a.mpad * 2];
-    if (mt == kNegInf) continue;
-    const float w = exp2f(mt - mx);
-    lt += ml[(int64_t)t * a.mpad * 2 + 1] * w;
-    const float4 u = *(const float4*)(acc + (int64_t)t * a.mpad * kHeadDim);
-    v.x += w * u.x; v.y += w * u.y; v.z += w * u.z; v.w += w * u.w;
+  const int lane = threadIdx.x & 63;
+  const int wv = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (wv >= a.n_units * a.m) return;
+  const int n = wv % a.m, unit = wv / a.m;
+  const int hl = lane >> 5, d4 = lane & 31;
+  const int64_t base = (int64_t)unit * a.n_split * a.mpad + n;
+  const float* ml = a.part_ml + base * 2;
+  const float* acc = a.part_acc + base * kHeadDim + 4 * d4;
+  const int64_t ml_step = (int64_t)a.mpad * 2, acc_step = (int64_t)a.mpad * kHeadDim;
+
+  const float2 my = lane < a.n_split ? *(const float2*)(ml + lane * ml_step)
+                                     : make_float2(kNegInf, 0.0f);
+  float4 u[KMAX];
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) {
+    const int t = hl + 2 * k;
+    u[k] = *(const float4*)(acc + (t < a.n_split ? t : 0) * acc_step);
   }
-  const float inv = 1.0f / lt;
-  v.x *= inv; v.y *= inv; v.z *= inv; v.w *= inv;
-  const int seq = unit / a.n_head_kv, g = unit - seq * a.n_head_kv;
-  const int i = n / a.group, hh = n - i * a.group;
-  float* dst = a.out + (((int64_t)seq * a.q_len + i) * a.n_head + g * a.group + hh) * kHeadDim;
-  *(float4*)(dst + 4 * d4) = v;
+  float mx = my.x;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  const float w = my.x == kNegInf ? 0.0f : exp2f(my.x - mx);
+  float lt = my.y * w;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) lt += __shfl_xor(lt, o);
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) {
+    const int t = hl + 2 * k;
+    const float wt = __shfl(w, t);
+    const float ws = t < a.n_split ? wt : 0.0f;
+    v.x += ws * u[k].x; v.y += ws * u[k].y; v.z += ws * u[k].z; v.w += ws * u[k].w;
+  }
+  v.x += __shfl_xor(v.x, 32);
+  v.y += __shfl_xor(v.y, 32);
+  v.z += __shfl_xor(v.z, 32);
+  v.w += __shfl_xor(v.w, 32);
+  if (hl == 0) {
+    const float inv = 1.0f / lt;
+    v.x *= inv; v.y *= inv; v.z *= inv; v.w *= inv;
+    const int seq = unit / a.n_head_kv, g = unit - seq * a.n_head_kv;
+    const int i = n / a.group, hh = n - i * a.group;
+    float* dst = a.out + (((int64_t)seq * a.q_len + i) * a.n_head + g * a.group + hh) * kHeadDim;
+    *(float4*)(dst + 4 * d4) = v;
+  }
 }
 
 __global__ void k_fill_u16(uint16_t* p, uint16_t value, int64_t n) {
@@ -600,18 +703,41 @@ hipError_t launch_step(const StepArgs& a, hipStream_t s, hipEvent_t t0, hipEvent
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
   const int grid = a.n_seq * a.n_head_kv * a.n_split;
+  // noise rounds: two (row, frequency) items per thread per round
+  const int nr = (a.q_len * 64 + 511) / 512;
+#define RING_ATTN_LAUNCH(MB_, NR_) \
+  hipExtLaunchKernelGGL((k_ring_attn<MB_, 4, NR_>), dim3(grid), dim3(256), 0, s, t0, t1, 0, a)
   if (a.m <= 32) {
-    hipExtLaunchKernelGGL((k_ring_attn<1, 4>), dim3(grid), dim3(256), 0, s, t0, t1, 0, a);
+    switch (nr) {
+      case 1: RING_ATTN_LAUNCH(1, 1); break;
+      case 2: RING_ATTN_LAUNCH(1, 2); break;
+      case 3: RING_ATTN_LAUNCH(1, 3); break;
+      default: RING_ATTN_LAUNCH(1, 4); break;
+    }
   } else {
-    hipExtLaunchKernelGGL((k_ring_attn<2, 4>), dim3(grid), dim3(256), 0, s, t0, t1, 0, a);
+    switch (nr) {
+      case 1: RING_ATTN_LAUNCH(2, 1); break;
+      case 2: RING_ATTN_LAUNCH(2, 2); break;
+      case 3: RING_ATTN_LAUNCH(2, 3); break;
+      default: RING_ATTN_LAUNCH(2, 4); break;
+    }
   }
+#undef RING_ATTN_LAUNCH
   return hipGetLastError();
 }
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
-  const int64_t total = (int64_t)a.n_units * a.m * 32;
-  const int grid = (int)((total + 255) / 256);
-  hipExtLaunchKernelGGL(k_ring_merge, dim3(grid), dim3(256), 0, s, t0, t1, 0, a);
+  const int waves = a.n_units * a.m;
+  const dim3 grid((waves + 3) / 4), block(256);
+  if (a.n_split <= 2) {
+    hipExtLaunchKernelGGL(k_ring_merge<1>, grid, block, 0, s, t0, t1, 0, a);
+  } else if (a.n_split <= 8) {
+    hipExtLaunchKernelGGL(k_ring_merge<4>, grid, block, 0, s, t0, t1, 0, a);
+  } else if (a.n_split <= 32) {
+    hipExtLaunchKernelGGL(k_ring_merge<16>, grid, block, 0, s, t0, t1, 0, a);
+  } else {
+    hipExtLaunchKernelGGL(k_ring_merge<32>, grid, block, 0, s, t0, t1, 0, a);
+  }
   return hipGetLastError();
 }
 

@@ -48,8 +48,11 @@ struct Layout {
   size_t off_pacc = 0, off_pml = 0, total = 0;
 };
 
+constexpr int kMaxSplits = 64;  // the merge kernel holds one split per lane
+
 // Splits of the ring tiles per (sequence, KV head): enough work-groups to
 // cover the 256 compute units, and at least one 32-slot tile per wave.
+// RING_ATTN_SPLITS (1..64) overrides the choice, for tuning.
 int32_t choose_splits(const ring_config& c) {
   const int n_units = c.n_seq * c.n_head_kv;
   const int ring_tiles = (c.cap + kTile - 1) / kTile;
@@ -57,9 +60,9 @@ int32_t choose_splits(const ring_config& c) {
   s = std::min(s, std::max(1, (ring_tiles + 3) / 4));
   if (const char* env = std::getenv("RING_ATTN_SPLITS")) {
     const int v = std::atoi(env);
-    if (v >= 1 && v <= 1024) s = v;
+    if (v >= 1) s = v;
   }
-  return s;
+  return std::min(s, kMaxSplits);
 }
 
 int validate(const ring_config* c) {
@@ -365,6 +368,7 @@ int ring_begin_step(ring_t* r, int32_t seq, int64_t committed, const void* k_new
   a.k_new = static_cast<const uint16_t*>(k_new);
   a.v_new = static_cast<const uint16_t*>(v_new);
   a.start = p.start;
+  a.start_mod = (int32_t)(p.start % r->cfg.cap);
   a.committed = committed;
   a.lo = p.lo;
   a.n_new = (int32_t)p.n_new;

@@ -69,6 +69,14 @@ def _load() -> ctypes.CDLL:
         raise ImportError(
             f"{LIB_PATH} is missing: build the HIP library first "
             "(python draft_model_kv_amd/build.py); there is no CPU fallback")
+    # torch's HIP libraries load their own bundled libamdhip64.so by file name.
+    # Loading torch first makes that runtime satisfy this library's
+    # libamdhip64.so.7 dependency, so the process has one HIP runtime (two
+    # runtimes in one process do not share the device or its memory).
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     sig = {
