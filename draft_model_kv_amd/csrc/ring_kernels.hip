@@ -218,14 +218,20 @@ __device__ inline void attend_tile(const half8 (&kc)[8], const half8 (&vc)[8],
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const uint32_t w = mw[mb][2 * (j >> 2) + ((j & 3) >> 1)];
-      float b = (j & 1) ? f16_hi(w) : f16_lo(w);
-      const int r = 8 * (j >> 2) + 4 * hl + (j & 3);
-      if (r >= limit) b = kNegInf;
-      s[j] += b;
-      mx = fmaxf(mx, s[j]);
+      s[j] += (j & 1) ? f16_hi(w) : f16_lo(w);
     }
+    if (limit < kTile) {  // ragged tile: rows r >= limit are not ring slots
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int r = 8 * (j >> 2) + 4 * hl + (j & 3);
+        if (r >= limit) s[j] = kNegInf;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[j]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mnew = fmaxf(m_run[mb], mx);
+    const float m_old = m_run[mb];
+    const float mnew = fmaxf(m_old, mx);
     float alpha = 1.0f;
     float ls = 0.0f;
     if (mnew == kNegInf) {
@@ -248,9 +254,14 @@ __device__ inline void attend_tile(const half8 (&kc)[8], const half8 (&vc)[8],
       pb0[e] = (_Float16)s[e];
       pb1[e] = (_Float16)s[8 + e];
     }
+    // Rescale the accumulators only when some query's running max moved
+    // (never on a wave's first tile, whose accumulators are still zero).
+    if (__any(alpha != 1.0f && m_old != kNegInf)) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) o[mb][b] *= alpha;
+    }
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      o[mb][b] *= alpha;
       o[mb][b] = mfma32(vc[2 * b], pb0, o[mb][b]);
       o[mb][b] = mfma32(vc[2 * b + 1], pb1, o[mb][b]);
     }
@@ -258,41 +269,49 @@ __device__ inline void attend_tile(const half8 (&kc)[8], const half8 (&vc)[8],
 }
 
 // Work-group: NW waves for one (sequence, KV head, split).  The split-0
-// work-group of each (sequence, head) also owns the noise block.
+// work-group of each (sequence, head) also owns the noise block; it runs the
+// NOISE instance of the body, chosen by one uniform branch at the top.
 //
 // Order of work (memory latency is the cost on a 4096-slot ring, so every
 // load is issued as early as its inputs allow):
-//   1. loads for the query build, for the noise rows (split 0) and for the
+//   1. loads for the noise rows (NOISE), for the query build and for the
 //      wave's first ring tile;
-//   2. the work-group rotates/scales/splits the queries into LDS and, in
-//      split 0, rotates the noise K rows, stages noise K/V in LDS and stores
-//      them to ring rows cap + r; one barrier;
-//   3. split 0's noise wave attends the noise block from LDS while the ring
-//      tiles are still in flight;
+//   2. the work-group rotates/scales/splits the queries into LDS and (NOISE)
+//      rotates the noise K rows and stages noise K/V in LDS; one barrier;
+//   3. (NOISE) one wave attends the noise block from LDS while the ring tiles
+//      are still in flight;
 //   4. each wave streams its ring tiles;
-//   5. waves merge through LDS; the work-group writes its output or partial.
+//   5. (NOISE) rotated noise rows are stored to ring rows cap + r;
+//   6. waves merge through LDS; the work-group writes its output or partial.
+// Every global load is issued unconditionally from an in-bounds (clamped)
+// address and selected afterwards: the compiler can then wait for each group
+// of loads alone instead of draining all of them at a control-flow join.
 template <int MB, int NW, int NR>
-__global__ __launch_bounds__(NW * 64) void k_ring_attn(AttnArgs a) {
-  constexpr int MP = MB * 32;
-  constexpr int OS = 132;  // LDS row stride (floats) of the merged output
-  constexpr int NT = NW * 64;
+struct AttnShape {
+  static constexpr int MP = MB * 32;               // padded queries
+  static constexpr int OS = 132;                   // LDS row stride of a merge region (floats)
+  static constexpr int NT = NW * 64;               // threads
+  static constexpr int NI = 2 * NR;                // noise items per thread
+  static constexpr int kQBytes = MB * 2 * 8 * 64 * 16;
+  static constexpr int kNoiseBytes = 2 * 32 * kNoiseStride * 2;
+  static constexpr int kMergeBytes = NW * MP * OS * 4;
+  // The query fragments and the staged noise rows live until the end of the
+  // tile loop; the per-wave merge regions reuse the same bytes after it.
+  static constexpr int kLdsBytes =
+      kQBytes + kNoiseBytes > kMergeBytes ? kQBytes + kNoiseBytes : kMergeBytes;
+};
+
+template <int MB, int NW, int NR, bool NOISE>
+__device__ __forceinline__ void attn_body(const AttnArgs& a, int unit, int split,
+                                          unsigned char* lds, float (*sm_m)[MB * 32],
+                                          float (*sm_l)[MB * 32]) {
+  using S = AttnShape<MB, NW, NR>;
+  constexpr int MP = S::MP, OS = S::OS, NT = S::NT, NI = S::NI;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hl = lane >> 5;
   const int col = lane & 31;
 
-  // Work-group -> (sequence, KV head, split).  Work-groups are handed to the
-  // eight XCDs round-robin; keep every split of one (sequence, head) on one XCD.
-  const int n_units = a.n_seq * a.n_head_kv;
-  int unit, split;
-  if ((n_units & 7) == 0) {
-    const int xcd = blockIdx.x & 7, k = blockIdx.x >> 3;
-    unit = ((k / a.n_split) << 3) + xcd;
-    split = k % a.n_split;
-  } else {
-    unit = blockIdx.x / a.n_split;
-    split = blockIdx.x % a.n_split;
-  }
   const int seq = unit / a.n_head_kv;
   const int g = unit - seq * a.n_head_kv;
   const int kv_row = a.n_head_kv * kHeadDim;
@@ -307,55 +326,42 @@ __global__ __launch_bounds__(NW * 64) void k_ring_attn(AttnArgs a) {
   const int t1 = min(nvt, t0 + per);
   uint16_t* kh = a.kring + seq * a.seq_stride + a.layer_offset + g * a.head_stride;
   uint16_t* vh = a.vring + seq * a.seq_stride + a.layer_offset + g * a.head_stride;
-  const bool noise_wg = split == 0;
-  const bool noise_wave = noise_wg && wave == (t1 - t0) % NW;
+  const bool noise_wave = NOISE && wave == (t1 - t0) % NW;
 
   // Query row (noise position index) of this lane's query in block mb.
-  int qrow[MB];
+  unsigned qrow[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     const int n = mb * 32 + col;
     qrow[mb] = n < a.m ? n / a.group : 0;
   }
 
-  // Every global load below is issued unconditionally from an in-bounds
-  // (clamped) address, in the order its data is needed, and selected
-  // afterwards: the compiler can then wait for each group alone instead of
-  // draining every outstanding load at a control-flow join.
-
-  // ---- 1a. noise rows (used by split 0): thread item = (row r, freq f),
-  //      NR rounds of two items per thread (NR * 2 * NT >= q_len * 64).
-  const int n_noise_items = noise_wg ? a.q_len * 64 : 0;
-  constexpr int NI = 2 * NR;
+  // ---- 1a. noise rows: thread item = (row r, freq f), NR rounds of two
+  //      items per thread (NR * 2 * NT >= q_len * 64); items past the last
+  //      repeat it.  Mask words of the noise block for accumulator row j.
   uint16_t nkx[NI], nky[NI], nvx[NI], nvy[NI];
   double2 ncs[NI];
+  uint16_t nmraw[MB][16];
   const uint16_t* knb = a.k_noise + (int64_t)seq * a.q_len * kv_row + g * kHeadDim;
   const uint16_t* vnb = a.v_noise + (int64_t)seq * a.q_len * kv_row + g * kHeadDim;
-  auto load_noise = [&]() {
+  if constexpr (NOISE) {
 #pragma unroll
     for (int u = 0; u < NI; ++u) {
-      const int item = min((int)threadIdx.x + u * NT, a.q_len * 64 - 1);
-      const int r = item >> 6, f = item & 63;
-      nkx[u] = knb[(int64_t)r * kv_row + f];
-      nky[u] = knb[(int64_t)r * kv_row + f + 64];
-      nvx[u] = vnb[(int64_t)r * kv_row + f];
-      nvy[u] = vnb[(int64_t)r * kv_row + f + 64];
+      const unsigned item = min((int)threadIdx.x + u * NT, a.q_len * 64 - 1);
+      const unsigned r = item >> 6, f = item & 63;
+      nkx[u] = knb[r * kv_row + f];
+      nky[u] = knb[r * kv_row + f + 64];
+      nvx[u] = vnb[r * kv_row + f];
+      nvy[u] = vnb[r * kv_row + f + 64];
       ncs[u] = *(const double2*)(rope + (r * 64 + f) * 2);
     }
-  };
-  // Mask of the noise block for accumulator row j (slot cap + row(j)); only
-  // loaded here, used by the noise wave after the barrier.
-  // Every work-group issues these few L2-resident loads, so the prologue
-  // stays one basic block (only split 0 uses them).
-  uint16_t nmraw[MB][16];
-  load_noise();
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const uint16_t* mr = mask_seq + (int64_t)qrow[mb] * a.kv_total;
+    for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int r = 8 * (j >> 2) + 4 * hl + (j & 3);
-      nmraw[mb][j] = mr[min(a.cap + r, a.kv_total - 1)];
+      for (int j = 0; j < 16; ++j) {
+        const int r = 8 * (j >> 2) + 4 * hl + (j & 3);
+        nmraw[mb][j] = mask_seq[qrow[mb] * a.kv_total + min(a.cap + r, a.kv_total - 1)];
+      }
     }
   }
 
@@ -363,23 +369,23 @@ __global__ __launch_bounds__(NW * 64) void k_ring_attn(AttnArgs a) {
   //      lane ln); x = dims 16c + 8h + e, y = the same dims + 64.
   half8 qx[MB], qy[MB];
   double2 qcs[MB][8];
+  const uint16_t* qseq = a.q + ((int64_t)seq * a.q_len * a.n_head + g * a.group) * kHeadDim;
 #pragma unroll
   for (int k = 0; k < MB; ++k) {
     const int item = threadIdx.x + k * NT;
     const int c = (item >> 6) & 3, ln = item & 63;
     const int n = min((item >> 8) * 32 + (ln & 31), a.m - 1), h2 = ln >> 5;
-    const int i = n / a.group, hh = n - i * a.group;
-    const uint16_t* qp =
-        a.q + (((int64_t)seq * a.q_len + i) * a.n_head + g * a.group + hh) * kHeadDim;
-    qx[k] = *(const half8*)(qp + 16 * c + 8 * h2);
-    qy[k] = *(const half8*)(qp + 16 * (c + 4) + 8 * h2);
+    const unsigned i = n / a.group, hh = n - i * a.group;
+    const unsigned qo = (i * a.n_head + hh) * kHeadDim + 16 * c + 8 * h2;
+    qx[k] = *(const half8*)(qseq + qo);
+    qy[k] = *(const half8*)(qseq + qo + 64);
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       qcs[k][e] = *(const double2*)(rope + (i * 64 + 16 * c + 8 * h2 + e) * 2);
   }
 
   // ---- 1c. the wave's first ring tile (a wave without tiles loads its
-  //      split's first tile again and ignores it).
+  //      split's last tile again and ignores it).
   auto load_tile = [&](int tile, half8 (&kc)[8], half8 (&vc)[8], uint32_t (&mw)[MB][8]) {
     const half8* kt = (const half8*)(kh + (int64_t)tile * kTileHalves);
     const half8* vt = (const half8*)(vh + (int64_t)tile * kTileHalves);
@@ -387,12 +393,13 @@ __global__ __launch_bounds__(NW * 64) void k_ring_attn(AttnArgs a) {
     for (int c = 0; c < 8; ++c) kc[c] = kt[c * 64 + lane];
 #pragma unroll
     for (int c = 0; c < 8; ++c) vc[c] = vt[c * 64 + lane];
+    const uint16_t* mt = mask_seq + tile * kTile;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      const uint16_t* mr = mask_seq + (int64_t)qrow[mb] * a.kv_total + tile * kTile + 4 * hl;
+      const unsigned mo = qrow[mb] * a.kv_total + 4 * hl;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const uint2 w = *(const uint2*)(mr + 8 * jj);
+        const uint2 w = *(const uint2*)(mt + mo + 8 * jj);
         mw[mb][2 * jj] = w.x;
         mw[mb][2 * jj + 1] = w.y;
       }
@@ -407,7 +414,7 @@ __global__ __launch_bounds__(NW * 64) void k_ring_attn(AttnArgs a) {
   // ---- 2a. queries: rotate at committed + i, scale by log2(e)/sqrt(d),
   //      split into hi + lo F16 (fragment order [mb][hi/lo][chunk][lane]);
   //      queries past q_len * group are zero.
-  __shared__ half8 q_lds[MB * 2 * 8 * 64];
+  half8* q_lds = reinterpret_cast<half8*>(lds);
 #pragma unroll
   for (int k = 0; k < MB; ++k) {
     const int item = threadIdx.x + k * NT;
@@ -442,23 +449,23 @@ __global__ __launch_bounds__(NW * 64) void k_ring_attn(AttnArgs a) {
     q_lds[((mb * 2 + 1) * 8 + c + 4) * 64 + ln] = yl;
   }
 
-  // ---- 2b. noise rows (split 0): rotate K at committed + r (fp64, one
-  //      rounding to F16), stage K and V in LDS as plain rows.
-  __shared__ uint16_t nk_lds[32 * kNoiseStride];
-  __shared__ uint16_t nv_lds[32 * kNoiseStride];
-  //      Every work-group runs this (a few instructions) so that no branch
-  //      holds the loads of 1a; items past q_len * 64 repeat the last item
-  //      and store the same values again.
+  // ---- 2b. noise rows: rotate K at committed + r (fp64, one rounding to
+  //      F16), stage K and V in LDS as plain rows (repeated items store the
+  //      same values again).
+  uint16_t* nk_lds = reinterpret_cast<uint16_t*>(lds + S::kQBytes);
+  uint16_t* nv_lds = nk_lds + 32 * kNoiseStride;
+  if constexpr (NOISE) {
 #pragma unroll
-  for (int u = 0; u < NI; ++u) {
-    const int item = min((int)threadIdx.x + u * NT, a.q_len * 64 - 1);
-    const int r = item >> 6, f = item & 63;
-    double xr, yr;
-    rot_pair(f16_to_f64(nkx[u]), f16_to_f64(nky[u]), ncs[u].x, ncs[u].y, xr, yr);
-    nk_lds[r * kNoiseStride + f] = f64_to_f16_rne(xr);
-    nk_lds[r * kNoiseStride + f + 64] = f64_to_f16_rne(yr);
-    nv_lds[r * kNoiseStride + f] = nvx[u];
-    nv_lds[r * kNoiseStride + f + 64] = nvy[u];
+    for (int u = 0; u < NI; ++u) {
+      const int item = min((int)threadIdx.x + u * NT, a.q_len * 64 - 1);
+      const int r = item >> 6, f = item & 63;
+      double xr, yr;
+      rot_pair(f16_to_f64(nkx[u]), f16_to_f64(nky[u]), ncs[u].x, ncs[u].y, xr, yr);
+      nk_lds[r * kNoiseStride + f] = f64_to_f16_rne(xr);
+      nk_lds[r * kNoiseStride + f + 64] = f64_to_f16_rne(yr);
+      nv_lds[r * kNoiseStride + f] = nvx[u];
+      nv_lds[r * kNoiseStride + f + 64] = nvy[u];
+    }
   }
   lds_barrier();
 
@@ -483,34 +490,35 @@ __global__ __launch_bounds__(NW * 64) void k_ring_attn(AttnArgs a) {
     for (int b = 0; b < 4; ++b) o[mb][b] = f32x16{};
   }
 
-  // ---- 3. noise block, visible to every query.
-  uint32_t nmw[MB][8];
+  // ---- 3. noise block, visible to every query; rows r >= q_len of the
+  //      32-row noise tile are zero (their LDS rows are read, not used).
+  if constexpr (NOISE) {
+    if (noise_wave) {
+      uint32_t nmw[MB][8];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int w2 = 0; w2 < 8; ++w2)
-      nmw[mb][w2] = (uint32_t)nmraw[mb][2 * w2] | ((uint32_t)nmraw[mb][2 * w2 + 1] << 16);
-  if (noise_wave) {
-    // Rows r >= q_len of the 32-row noise tile are zero (their LDS rows are
-    // read but not used).
-    half8 nkc[8], nvc[8];
-    const bool rv = col < a.q_len;
+        for (int w2 = 0; w2 < 8; ++w2)
+          nmw[mb][w2] = (uint32_t)nmraw[mb][2 * w2] | ((uint32_t)nmraw[mb][2 * w2 + 1] << 16);
+      half8 nkc[8], nvc[8];
+      const bool rv = col < a.q_len;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const half8 kk = *(const half8*)(nk_lds + col * kNoiseStride + 16 * c + 8 * hl);
-      nkc[c] = rv ? kk : half8{};
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int b = j >> 1, ks = j & 1;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int slot = 16 * ks + 8 * (e >> 2) + 4 * hl + (e & 3);
-        const uint16_t vv = nv_lds[slot * kNoiseStride + 32 * b + col];
-        nvc[j][e] = __builtin_bit_cast(_Float16, (uint16_t)(slot < a.q_len ? vv : 0));
+      for (int c = 0; c < 8; ++c) {
+        const half8 kk = *(const half8*)(nk_lds + col * kNoiseStride + 16 * c + 8 * hl);
+        nkc[c] = rv ? kk : half8{};
       }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int b = j >> 1, ks = j & 1;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int slot = 16 * ks + 8 * (e >> 2) + 4 * hl + (e & 3);
+          const uint16_t vv = nv_lds[slot * kNoiseStride + 32 * b + col];
+          nvc[j][e] = __builtin_bit_cast(_Float16, (uint16_t)(slot < a.q_len ? vv : 0));
+        }
+      }
+      attend_tile<MB>(nkc, nvc, nmw, a.q_len, hl, qf, q_lds, lane, m_run, l_run, o);
     }
-    attend_tile<MB>(nkc, nvc, nmw, a.q_len, hl, qf, q_lds, lane, m_run, l_run, o);
   }
 
   // ---- 4. ring tiles.  One query block: the next tile's loads are issued
@@ -538,9 +546,10 @@ __global__ __launch_bounds__(NW * 64) void k_ring_attn(AttnArgs a) {
     tile = next;
   }
 
-  // Rotated noise rows into ring rows cap + r of this layer (from LDS, after
-  // the ring loads so these stores delay no wait).
-  if (noise_wg) {
+  // ---- 5. rotated noise rows into ring rows cap + r of this layer (from
+  //      LDS, after the ring loads so these stores delay no wait).
+  if constexpr (NOISE) {
+    const int n_noise_items = a.q_len * 64;
     for (int item = threadIdx.x; item < n_noise_items; item += NT) {
       const int r = item >> 6, f = item & 63;
       const int slot = a.cap + r;
@@ -553,11 +562,10 @@ __global__ __launch_bounds__(NW * 64) void k_ring_attn(AttnArgs a) {
     }
   }
 
-  // ---- 5. merge the waves of this work-group through LDS (fixed wave order).
-  __shared__ float sm_m[NW][MP];
-  __shared__ float sm_l[NW][MP];
-  __shared__ float sm_ml[MP][2];
-  __shared__ float sm_o[MP * OS];
+  // ---- 6. merge the waves of this work-group: running max / sum through
+  //      LDS, then every wave stores its rescaled O^T in its own LDS region
+  //      (over the prologue buffers, free once every wave is past the
+  //      barrier below) and each thread sums the regions for its outputs.
   if (hl == 0) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -566,10 +574,33 @@ __global__ __launch_bounds__(NW * 64) void k_ring_attn(AttnArgs a) {
     }
   }
   lds_barrier();
-  float scale[MB];
+  float* region = reinterpret_cast<float*>(lds) + wave * (MP * OS);
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     const int n = mb * 32 + col;
+    float mx = kNegInf;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, sm_m[w][n]);
+    const float scale = m_run[mb] == kNegInf ? 0.0f : exp2f(m_run[mb] - mx);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        *(float4*)&region[n * OS + 32 * b + 8 * jj + 4 * hl] =
+            make_float4(o[mb][b][4 * jj] * scale, o[mb][b][4 * jj + 1] * scale,
+                        o[mb][b][4 * jj + 2] * scale, o[mb][b][4 * jj + 3] * scale);
+      }
+    }
+  }
+  lds_barrier();
+
+  // ---- write the final output (one split) or this split's partial.
+  const float* regions = reinterpret_cast<const float*>(lds);
+  float* out_unit = a.out + ((int64_t)seq * a.q_len * a.n_head + g * a.group) * kHeadDim;
+  float* pacc = a.part_acc + ((int64_t)unit * a.n_split + split) * MP * kHeadDim;
+  float* pml = a.part_ml + ((int64_t)unit * a.n_split + split) * MP * 2;
+  for (int item = threadIdx.x; item < a.m * 32; item += NT) {
+    const int n = item >> 5, d4 = item & 31;
     float mx = kNegInf;
 #pragma unroll
     for (int w = 0; w < NW; ++w) mx = fmaxf(mx, sm_m[w][n]);
@@ -577,55 +608,49 @@ __global__ __launch_bounds__(NW * 64) void k_ring_attn(AttnArgs a) {
 #pragma unroll
     for (int w = 0; w < NW; ++w)
       lt += sm_m[w][n] == kNegInf ? 0.0f : sm_l[w][n] * exp2f(sm_m[w][n] - mx);
-    scale[mb] = m_run[mb] == kNegInf ? 0.0f : exp2f(m_run[mb] - mx);
-    if (wave == 0 && hl == 0) {
-      sm_ml[n][0] = mx;
-      sm_ml[n][1] = lt;
+    float4 v = *(const float4*)&regions[n * OS + 4 * d4];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+      const float4 u = *(const float4*)&regions[w * (MP * OS) + n * OS + 4 * d4];
+      v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
     }
-  }
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    if (wave == w) {
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const int n = mb * 32 + col;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            float4* dst = (float4*)&sm_o[n * OS + 32 * b + 8 * jj + 4 * hl];
-            float4 v = make_float4(o[mb][b][4 * jj] * scale[mb], o[mb][b][4 * jj + 1] * scale[mb],
-                                   o[mb][b][4 * jj + 2] * scale[mb], o[mb][b][4 * jj + 3] * scale[mb]);
-            if (w != 0) {
-              const float4 u = *dst;
-              v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
-            }
-            *dst = v;
-          }
-        }
-      }
-    }
-    lds_barrier();
-  }
-
-  // ---- write the final output (one split) or this split's partial.
-  for (int item = threadIdx.x; item < a.m * 32; item += NT) {
-    const int n = item >> 5, d4 = item & 31;
-    float4 v = *(const float4*)&sm_o[n * OS + 4 * d4];
     if (a.n_split == 1) {
-      const float inv = 1.0f / sm_ml[n][1];
+      const float inv = 1.0f / lt;
       v.x *= inv; v.y *= inv; v.z *= inv; v.w *= inv;
-      const int i = n / a.group, hh = n - i * a.group;
-      float* dst = a.out + (((int64_t)seq * a.q_len + i) * a.n_head + g * a.group + hh) * kHeadDim;
-      *(float4*)(dst + 4 * d4) = v;
+      const unsigned i = n / a.group, hh = n - i * a.group;
+      *(float4*)(out_unit + (i * a.n_head + hh) * kHeadDim + 4 * d4) = v;
     } else {
-      const int64_t pbase = ((int64_t)unit * a.n_split + split) * MP + n;
-      *(float4*)(a.part_acc + pbase * kHeadDim + 4 * d4) = v;
+      *(float4*)(pacc + n * kHeadDim + 4 * d4) = v;
       if (d4 == 0) {
-        a.part_ml[pbase * 2] = sm_ml[n][0];
-        a.part_ml[pbase * 2 + 1] = sm_ml[n][1];
+        pml[n * 2] = mx;
+        pml[n * 2 + 1] = lt;
       }
     }
+  }
+}
+
+template <int MB, int NW, int NR>
+__global__ __launch_bounds__(NW * 64) void k_ring_attn(AttnArgs a) {
+  using S = AttnShape<MB, NW, NR>;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[S::kLdsBytes];
+  __shared__ float sm_m[NW][S::MP];
+  __shared__ float sm_l[NW][S::MP];
+  // Work-group -> (sequence, KV head, split).  Work-groups are handed to the
+  // eight XCDs round-robin; keep every split of one (sequence, head) on one XCD.
+  const int n_units = a.n_seq * a.n_head_kv;
+  int unit, split;
+  if ((n_units & 7) == 0) {
+    const int xcd = blockIdx.x & 7, k = blockIdx.x >> 3;
+    unit = ((k / a.n_split) << 3) + xcd;
+    split = k % a.n_split;
+  } else {
+    unit = blockIdx.x / a.n_split;
+    split = blockIdx.x % a.n_split;
+  }
+  if (split == 0) {
+    attn_body<MB, NW, NR, true>(a, unit, split, lds, sm_m, sm_l);
+  } else {
+    attn_body<MB, NW, NR, false>(a, unit, split, lds, sm_m, sm_l);
   }
 }
 
