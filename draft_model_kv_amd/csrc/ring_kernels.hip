@@ -7,7 +7,9 @@
 //                 Page "DFLASH2_RING_PORT.md", sections 1.1-1.4.
 //   k_ring_attn   masked GQA attention of the q_len noise queries over the
 //                 ring, split-K over 32-slot ring tiles, matrix-core QK^T and
-//                 PV, online softmax, per-workgroup merge of its waves.
+//                 PV, online softmax, per-workgroup merge of its waves; the
+//                 noise rows are rotated, stored to ring rows cap + r and
+//                 attended one per wave.
 //   k_ring_merge  cross-split merge of the partial (max, sum, acc) triples.
 #include "ring_kernels.h"
 
@@ -22,7 +24,6 @@ constexpr float kNegInf = -__builtin_inff();
 // log2(e) / sqrt(128): folds the 1/sqrt(head_dim) score scale and the
 // change of base for exp2 into the query.
 constexpr double kQScale = 1.4426950408889634074 / 11.313708498984760390;
-constexpr int kNoiseStride = 136;  // LDS row stride (halves) of staged noise rows
 
 // ---------------------------------------------------------------------------
 // F16 helpers
@@ -268,45 +269,155 @@ __device__ inline void attend_tile(const half8 (&kc)[8], const half8 (&vc)[8],
   }
 }
 
-// Work-group: NW waves for one (sequence, KV head, split).  The split-0
-// work-group of each (sequence, head) also owns the noise block; it runs the
-// NOISE instance of the body, chosen by one uniform branch at the top.
+// Work-group: NW waves for one (sequence, KV head, split).  Every split
+// runs the same body; the q_len noise rows of a (sequence, head) are spread
+// one per wave over its waves, so no wave carries more than one ring tile
+// plus one noise row when the tiles divide evenly.
 //
 // Order of work (memory latency is the cost on a 4096-slot ring, so every
 // load is issued as early as its inputs allow):
-//   1. loads for the noise rows (NOISE), for the query build and for the
-//      wave's first ring tile;
-//   2. the work-group rotates/scales/splits the queries into LDS and (NOISE)
-//      rotates the noise K rows and stages noise K/V in LDS; one barrier;
-//   3. (NOISE) one wave attends the noise block from LDS while the ring tiles
-//      are still in flight;
+//   1. loads for the query build, for the wave's noise row and for its first
+//      ring tile;
+//   2. the work-group rotates/scales/splits the queries into LDS; one barrier;
+//   3. a wave that owns a noise row rotates it (fp64, one rounding to F16),
+//      stores it to ring row cap + r and folds it into its online softmax
+//      (dot products on the vector unit, P V on the matrix core) while its
+//      ring tile is still in flight;
 //   4. each wave streams its ring tiles;
-//   5. (NOISE) rotated noise rows are stored to ring rows cap + r;
-//   6. waves merge through LDS; the work-group writes its output or partial.
-// Every global load is issued unconditionally from an in-bounds (clamped)
-// address and selected afterwards: the compiler can then wait for each group
-// of loads alone instead of draining all of them at a control-flow join.
-template <int MB, int NW, int NR>
+//   5. waves merge through LDS; the work-group writes its output or partial.
+// Every global load of the fast path is issued unconditionally from an
+// in-bounds (clamped) address and selected afterwards: the compiler can then
+// wait for each group of loads alone instead of draining all of them at a
+// control-flow join.
+template <int MB, int NW>
 struct AttnShape {
   static constexpr int MP = MB * 32;               // padded queries
   static constexpr int OS = 132;                   // LDS row stride of a merge region (floats)
   static constexpr int NT = NW * 64;               // threads
-  static constexpr int NI = 2 * NR;                // noise items per thread
   static constexpr int kQBytes = MB * 2 * 8 * 64 * 16;
-  static constexpr int kNoiseBytes = 2 * 32 * kNoiseStride * 2;
+  static constexpr int kRowBytes = NW * 2 * kHeadDim * 2;  // one K and one V row per wave
   static constexpr int kMergeBytes = NW * MP * OS * 4;
-  // The query fragments and the staged noise rows live until the end of the
+  // The query fragments and the noise-row buffers live until the end of the
   // tile loop; the per-wave merge regions reuse the same bytes after it.
   static constexpr int kLdsBytes =
-      kQBytes + kNoiseBytes > kMergeBytes ? kQBytes + kNoiseBytes : kMergeBytes;
+      kQBytes + kRowBytes > kMergeBytes ? kQBytes + kRowBytes : kMergeBytes;
 };
 
-template <int MB, int NW, int NR, bool NOISE>
-__device__ __forceinline__ void attn_body(const AttnArgs& a, int unit, int split,
+// One noise row of this wave's (sequence, head), already loaded: lane f holds
+// K and V at dims f and f + 64, (cos, sin) of frequency f at the row's
+// position, and the mask word of its query in each query block.
+template <int MB>
+struct NoiseRow {
+  uint16_t kx, ky, vx, vy;
+  double2 cs;
+  uint16_t mask[MB];
+};
+
+template <int MB>
+__device__ __forceinline__ void load_noise_row(const AttnArgs& a, int seq, int g, int r,
+                                               const uint16_t* mask_seq,
+                                               const unsigned (&qrow)[MB], int lane,
+                                               NoiseRow<MB>& nr) {
+  const int kv_row = a.n_head_kv * kHeadDim;
+  const int64_t ro = ((int64_t)seq * a.q_len + r) * kv_row + g * kHeadDim;
+  nr.kx = a.k_noise[ro + lane];
+  nr.ky = a.k_noise[ro + lane + 64];
+  nr.vx = a.v_noise[ro + lane];
+  nr.vy = a.v_noise[ro + lane + 64];
+  nr.cs = *(const double2*)(a.rope_noise + (((int64_t)seq * a.q_len + r) * 64 + lane) * 2);
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) nr.mask[mb] = mask_seq[qrow[mb] * a.kv_total + a.cap + r];
+}
+
+// Rotate the row, store it to ring row cap + r, and fold it into the wave's
+// running softmax as one more key.  S = Q k on the vector unit (dot products
+// of the hi and lo query fragments with the F16 key); the P V update is one
+// matrix op per 32-dim block with the row as slot 0 of a V fragment.
+template <int MB>
+__device__ __forceinline__ void attend_noise_row(
+    const AttnArgs& a, const NoiseRow<MB>& nr, int r, uint16_t* kh, uint16_t* vh,
+    uint16_t* rowk, uint16_t* rowv, int lane, int hl, int col, const QFrag<MB>& q,
+    const half8* q_lds, float (&m_run)[MB], float (&l_run)[MB], f32x16 (&o)[MB][4]) {
+  double xr, yr;
+  rot_pair(f16_to_f64(nr.kx), f16_to_f64(nr.ky), nr.cs.x, nr.cs.y, xr, yr);
+  const uint16_t kx = f64_to_f16_rne(xr), ky = f64_to_f16_rne(yr);
+  // ring row cap + r of this layer and head
+  const int slot = a.cap + r;
+  uint16_t* kt = kh + (int64_t)(slot >> 5) * kTileHalves;
+  uint16_t* vt = vh + (int64_t)(slot >> 5) * kTileHalves;
+  kt[k_frag_index(slot & 31, lane)] = kx;
+  kt[k_frag_index(slot & 31, lane + 64)] = ky;
+  vt[v_frag_index(slot & 31, lane)] = nr.vx;
+  vt[v_frag_index(slot & 31, lane + 64)] = nr.vy;
+  // the row in LDS, private to this wave
+  rowk[lane] = kx;
+  rowk[lane + 64] = ky;
+  rowv[lane] = nr.vx;
+  rowv[lane + 64] = nr.vy;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+  typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+  half8 kd[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) kd[c] = *(const half8*)(rowk + 16 * c + 8 * hl);
+  // V fragment with the row at slot 0: lanes 0..31, element 0, dim 32 b + col
+  uint16_t vd[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) vd[b] = rowv[32 * b + col];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // four chains keep the unit busy
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      half8 qh, ql;
+      if constexpr (QFrag<MB>::kLds) {
+        qh = q_lds[((mb * 2 + 0) * 8 + c) * 64 + lane];
+        ql = q_lds[((mb * 2 + 1) * 8 + c) * 64 + lane];
+      } else {
+        qh = q.hi[mb][c];
+        ql = q.lo[mb][c];
+      }
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const half2v kk = {kd[c][e], kd[c][e + 1]};
+        acc[e >> 1] = __builtin_amdgcn_fdot2((half2v){qh[e], qh[e + 1]}, kk, acc[e >> 1], false);
+        acc[e >> 1] = __builtin_amdgcn_fdot2((half2v){ql[e], ql[e + 1]}, kk, acc[e >> 1], false);
+      }
+    }
+    const float dot = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    const float sc = dot + __shfl_xor(dot, 32) +
+                     (float)__builtin_bit_cast(_Float16, nr.mask[mb]);
+    const float m_old = m_run[mb];
+    const float mnew = fmaxf(m_old, sc);
+    float alpha = 1.0f, p = 0.0f;
+    if (mnew != kNegInf) {
+      alpha = exp2f(m_old - mnew);
+      p = exp2f(sc - mnew);
+    }
+    l_run[mb] = l_run[mb] * alpha + p;
+    m_run[mb] = mnew;
+    if (__any(alpha != 1.0f && m_old != kNegInf)) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) o[mb][b] *= alpha;
+    }
+    half8 pb = {};
+    pb[0] = hl == 0 ? (_Float16)p : (_Float16)0.0f;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      half8 vf = {};
+      vf[0] = hl == 0 ? __builtin_bit_cast(_Float16, vd[b]) : (_Float16)0.0f;
+      o[mb][b] = mfma32(vf, pb, o[mb][b]);
+    }
+  }
+}
+
+template <int MB, int NW>
+__device__ __forceinline__ void attn_body(const AttnArgs& a, int unit, int split, int win,
                                           unsigned char* lds, float (*sm_m)[MB * 32],
                                           float (*sm_l)[MB * 32]) {
-  using S = AttnShape<MB, NW, NR>;
-  constexpr int MP = S::MP, OS = S::OS, NT = S::NT, NI = S::NI;
+  using S = AttnShape<MB, NW>;
+  constexpr int MP = S::MP, OS = S::OS, NT = S::NT;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hl = lane >> 5;
@@ -314,19 +425,22 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int unit, int split
 
   const int seq = unit / a.n_head_kv;
   const int g = unit - seq * a.n_head_kv;
-  const int kv_row = a.n_head_kv * kHeadDim;
   const double* rope = a.rope_noise + (int64_t)seq * a.q_len * 128;
   const uint16_t* mask_seq = a.mask + (int64_t)seq * a.q_len * a.kv_total;
 
   // Ring tiles of this split: the visible ring slots are [0, win).
-  const int win = a.win[seq];
   const int nvt = (win + kTile - 1) / kTile;
   const int per = (nvt + a.n_split - 1) / a.n_split;
   const int t0 = min(nvt, split * per);
   const int t1 = min(nvt, t0 + per);
   uint16_t* kh = a.kring + seq * a.seq_stride + a.layer_offset + g * a.head_stride;
   uint16_t* vh = a.vring + seq * a.seq_stride + a.layer_offset + g * a.head_stride;
-  const bool noise_wave = NOISE && wave == (t1 - t0) % NW;
+
+  // Noise rows of this wave: r = rank, rank + W, ... with W the waves of the
+  // (sequence, head); rank counts from the last wave of the last split, whose
+  // tile share is the smallest.
+  const int n_waves = a.n_split * NW;
+  const int rank = n_waves - 1 - (split * NW + wave);
 
   // Query row (noise position index) of this lane's query in block mb.
   unsigned qrow[MB];
@@ -336,36 +450,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int unit, int split
     qrow[mb] = n < a.m ? n / a.group : 0;
   }
 
-  // ---- 1a. noise rows: thread item = (row r, freq f), NR rounds of two
-  //      items per thread (NR * 2 * NT >= q_len * 64); items past the last
-  //      repeat it.  Mask words of the noise block for accumulator row j.
-  uint16_t nkx[NI], nky[NI], nvx[NI], nvy[NI];
-  double2 ncs[NI];
-  uint16_t nmraw[MB][16];
-  const uint16_t* knb = a.k_noise + (int64_t)seq * a.q_len * kv_row + g * kHeadDim;
-  const uint16_t* vnb = a.v_noise + (int64_t)seq * a.q_len * kv_row + g * kHeadDim;
-  if constexpr (NOISE) {
-#pragma unroll
-    for (int u = 0; u < NI; ++u) {
-      const unsigned item = min((int)threadIdx.x + u * NT, a.q_len * 64 - 1);
-      const unsigned r = item >> 6, f = item & 63;
-      nkx[u] = knb[r * kv_row + f];
-      nky[u] = knb[r * kv_row + f + 64];
-      nvx[u] = vnb[r * kv_row + f];
-      nvy[u] = vnb[r * kv_row + f + 64];
-      ncs[u] = *(const double2*)(rope + (r * 64 + f) * 2);
-    }
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int r = 8 * (j >> 2) + 4 * hl + (j & 3);
-        nmraw[mb][j] = mask_seq[qrow[mb] * a.kv_total + min(a.cap + r, a.kv_total - 1)];
-      }
-    }
-  }
-
-  // ---- 1b. loads for the query build: thread item = (mb, chunk pair c,
+  // ---- 1a. loads for the query build: thread item = (mb, chunk pair c,
   //      lane ln); x = dims 16c + 8h + e, y = the same dims + 64.
   half8 qx[MB], qy[MB];
   double2 qcs[MB][8];
@@ -383,6 +468,11 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int unit, int split
     for (int e = 0; e < 8; ++e)
       qcs[k][e] = *(const double2*)(rope + (i * 64 + 16 * c + 8 * h2 + e) * 2);
   }
+
+  // ---- 1b. the wave's first noise row (a wave without one loads the last
+  //      row and ignores it).
+  NoiseRow<MB> nr;
+  load_noise_row<MB>(a, seq, g, min(rank, a.q_len - 1), mask_seq, qrow, lane, nr);
 
   // ---- 1c. the wave's first ring tile (a wave without tiles loads its
   //      split's last tile again and ignores it).
@@ -411,7 +501,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int unit, int split
   uint32_t mw[MB][8];
   load_tile(min(tile, tile_last), kc, vc, mw);
 
-  // ---- 2a. queries: rotate at committed + i, scale by log2(e)/sqrt(d),
+  // ---- 2. queries: rotate at committed + i, scale by log2(e)/sqrt(d),
   //      split into hi + lo F16 (fragment order [mb][hi/lo][chunk][lane]);
   //      queries past q_len * group are zero.
   half8* q_lds = reinterpret_cast<half8*>(lds);
@@ -448,25 +538,6 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int unit, int split
     q_lds[((mb * 2 + 1) * 8 + c) * 64 + ln] = xl;
     q_lds[((mb * 2 + 1) * 8 + c + 4) * 64 + ln] = yl;
   }
-
-  // ---- 2b. noise rows: rotate K at committed + r (fp64, one rounding to
-  //      F16), stage K and V in LDS as plain rows (repeated items store the
-  //      same values again).
-  uint16_t* nk_lds = reinterpret_cast<uint16_t*>(lds + S::kQBytes);
-  uint16_t* nv_lds = nk_lds + 32 * kNoiseStride;
-  if constexpr (NOISE) {
-#pragma unroll
-    for (int u = 0; u < NI; ++u) {
-      const int item = min((int)threadIdx.x + u * NT, a.q_len * 64 - 1);
-      const int r = item >> 6, f = item & 63;
-      double xr, yr;
-      rot_pair(f16_to_f64(nkx[u]), f16_to_f64(nky[u]), ncs[u].x, ncs[u].y, xr, yr);
-      nk_lds[r * kNoiseStride + f] = f64_to_f16_rne(xr);
-      nk_lds[r * kNoiseStride + f + 64] = f64_to_f16_rne(yr);
-      nv_lds[r * kNoiseStride + f] = nvx[u];
-      nv_lds[r * kNoiseStride + f + 64] = nvy[u];
-    }
-  }
   lds_barrier();
 
   QFrag<MB> qf;
@@ -490,34 +561,16 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int unit, int split
     for (int b = 0; b < 4; ++b) o[mb][b] = f32x16{};
   }
 
-  // ---- 3. noise block, visible to every query; rows r >= q_len of the
-  //      32-row noise tile are zero (their LDS rows are read, not used).
-  if constexpr (NOISE) {
-    if (noise_wave) {
-      uint32_t nmw[MB][8];
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int w2 = 0; w2 < 8; ++w2)
-          nmw[mb][w2] = (uint32_t)nmraw[mb][2 * w2] | ((uint32_t)nmraw[mb][2 * w2 + 1] << 16);
-      half8 nkc[8], nvc[8];
-      const bool rv = col < a.q_len;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const half8 kk = *(const half8*)(nk_lds + col * kNoiseStride + 16 * c + 8 * hl);
-        nkc[c] = rv ? kk : half8{};
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int b = j >> 1, ks = j & 1;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int slot = 16 * ks + 8 * (e >> 2) + 4 * hl + (e & 3);
-          const uint16_t vv = nv_lds[slot * kNoiseStride + 32 * b + col];
-          nvc[j][e] = __builtin_bit_cast(_Float16, (uint16_t)(slot < a.q_len ? vv : 0));
-        }
-      }
-      attend_tile<MB>(nkc, nvc, nmw, a.q_len, hl, qf, q_lds, lane, m_run, l_run, o);
+  // ---- 3. noise rows, visible to every query.
+  uint16_t* rowk = reinterpret_cast<uint16_t*>(lds + S::kQBytes) + wave * 2 * kHeadDim;
+  uint16_t* rowv = rowk + kHeadDim;
+  if (rank < a.q_len) {
+    attend_noise_row<MB>(a, nr, rank, kh, vh, rowk, rowv, lane, hl, col, qf, q_lds, m_run,
+                         l_run, o);
+    for (int r = rank + n_waves; r < a.q_len; r += n_waves) {
+      load_noise_row<MB>(a, seq, g, r, mask_seq, qrow, lane, nr);
+      attend_noise_row<MB>(a, nr, r, kh, vh, rowk, rowv, lane, hl, col, qf, q_lds, m_run,
+                           l_run, o);
     }
   }
 
@@ -546,26 +599,12 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int unit, int split
     tile = next;
   }
 
-  // ---- 5. rotated noise rows into ring rows cap + r of this layer (from
-  //      LDS, after the ring loads so these stores delay no wait).
-  if constexpr (NOISE) {
-    const int n_noise_items = a.q_len * 64;
-    for (int item = threadIdx.x; item < n_noise_items; item += NT) {
-      const int r = item >> 6, f = item & 63;
-      const int slot = a.cap + r;
-      uint16_t* kt = kh + (int64_t)(slot >> 5) * kTileHalves;
-      uint16_t* vt = vh + (int64_t)(slot >> 5) * kTileHalves;
-      kt[k_frag_index(slot & 31, f)] = nk_lds[r * kNoiseStride + f];
-      kt[k_frag_index(slot & 31, f + 64)] = nk_lds[r * kNoiseStride + f + 64];
-      vt[v_frag_index(slot & 31, f)] = nv_lds[r * kNoiseStride + f];
-      vt[v_frag_index(slot & 31, f + 64)] = nv_lds[r * kNoiseStride + f + 64];
-    }
-  }
-
-  // ---- 6. merge the waves of this work-group: running max / sum through
-  //      LDS, then every wave stores its rescaled O^T in its own LDS region
-  //      (over the prologue buffers, free once every wave is past the
-  //      barrier below) and each thread sums the regions for its outputs.
+  // ---- 5. merge the waves of this work-group.  Each lane owns query
+  //      n = 32 mb + col: it combines the waves' running (max, sum) from LDS
+  //      into the work-group's (mx, lt), scales its O^T by 2^(m - mx) (and by
+  //      1 / lt when this is the only split) into its wave's LDS region (over
+  //      the prologue buffers, free once every wave is past the barrier
+  //      below); the regions are then summed with every read issued at once.
   if (hl == 0) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -575,13 +614,28 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int unit, int split
   }
   lds_barrier();
   float* region = reinterpret_cast<float*>(lds) + wave * (MP * OS);
+  float* pml = a.part_ml + ((int64_t)unit * a.n_split + split) * MP * 2;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     const int n = mb * 32 + col;
+    float mw_[NW];
     float mx = kNegInf;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, sm_m[w][n]);
-    const float scale = m_run[mb] == kNegInf ? 0.0f : exp2f(m_run[mb] - mx);
+    for (int w = 0; w < NW; ++w) {
+      mw_[w] = sm_m[w][n];
+      mx = fmaxf(mx, mw_[w]);
+    }
+    float lt = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+      lt += mw_[w] == kNegInf ? 0.0f : sm_l[w][n] * exp2f(mw_[w] - mx);
+    float scale = m_run[mb] == kNegInf ? 0.0f : exp2f(m_run[mb] - mx);
+    if (a.n_split == 1) {
+      // lt > 0: the noise block is visible to every query of split 0.
+      scale *= 1.0f / lt;
+    } else if (wave == 0 && hl == 0 && n < a.m) {
+      *(float2*)(pml + n * 2) = make_float2(mx, lt);
+    }
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
 #pragma unroll
@@ -594,49 +648,58 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int unit, int split
   }
   lds_barrier();
 
-  // ---- write the final output (one split) or this split's partial.
+  // ---- 6. the final output (one split) or this split's partial: item =
+  //      (query n, dims 4 d4 .. 4 d4 + 3), MP * 32 / NT items per thread.
   const float* regions = reinterpret_cast<const float*>(lds);
   float* out_unit = a.out + ((int64_t)seq * a.q_len * a.n_head + g * a.group) * kHeadDim;
   float* pacc = a.part_acc + ((int64_t)unit * a.n_split + split) * MP * kHeadDim;
-  float* pml = a.part_ml + ((int64_t)unit * a.n_split + split) * MP * 2;
-  for (int item = threadIdx.x; item < a.m * 32; item += NT) {
+  constexpr int kItems = MP * 32 / NT;
+  float4 v[kItems];
+#pragma unroll
+  for (int it = 0; it < kItems; ++it) {
+    const int item = threadIdx.x + it * NT;
     const int n = item >> 5, d4 = item & 31;
-    float mx = kNegInf;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, sm_m[w][n]);
-    float lt = 0.0f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w)
-      lt += sm_m[w][n] == kNegInf ? 0.0f : sm_l[w][n] * exp2f(sm_m[w][n] - mx);
-    float4 v = *(const float4*)&regions[n * OS + 4 * d4];
+    v[it] = *(const float4*)&regions[n * OS + 4 * d4];
 #pragma unroll
     for (int w = 1; w < NW; ++w) {
       const float4 u = *(const float4*)&regions[w * (MP * OS) + n * OS + 4 * d4];
-      v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
+      v[it].x += u.x; v[it].y += u.y; v[it].z += u.z; v[it].w += u.w;
     }
-    if (a.n_split == 1) {
-      const float inv = 1.0f / lt;
-      v.x *= inv; v.y *= inv; v.z *= inv; v.w *= inv;
-      const unsigned i = n / a.group, hh = n - i * a.group;
-      *(float4*)(out_unit + (i * a.n_head + hh) * kHeadDim + 4 * d4) = v;
-    } else {
-      *(float4*)(pacc + n * kHeadDim + 4 * d4) = v;
-      if (d4 == 0) {
-        pml[n * 2] = mx;
-        pml[n * 2 + 1] = lt;
+  }
+#pragma unroll
+  for (int it = 0; it < kItems; ++it) {
+    const int item = threadIdx.x + it * NT;
+    const int n = item >> 5, d4 = item & 31;
+    if (n < a.m) {
+      if (a.n_split == 1) {
+        const unsigned i = n / a.group, hh = n - i * a.group;
+        *(float4*)(out_unit + (i * a.n_head + hh) * kHeadDim + 4 * d4) = v[it];
+      } else {
+        *(float4*)(pacc + n * kHeadDim + 4 * d4) = v[it];
       }
     }
   }
 }
 
-template <int MB, int NW, int NR>
+template <int MB, int NW>
 __global__ __launch_bounds__(NW * 64) void k_ring_attn(AttnArgs a) {
-  using S = AttnShape<MB, NW, NR>;
+  using S = AttnShape<MB, NW>;
   __shared__ __attribute__((aligned(16))) unsigned char lds[S::kLdsBytes];
   __shared__ float sm_m[NW][S::MP];
   __shared__ float sm_l[NW][S::MP];
   // Work-group -> (sequence, KV head, split).  Work-groups are handed to the
   // eight XCDs round-robin; keep every split of one (sequence, head) on one XCD.
+  // Every argument the body reads is fetched here in one batch: left to
+  // itself the compiler loads each field where it is first used, and each
+  // uniform branch in between then costs a full memory round trip before the
+  // first ring load can issue.  win[] comes in as one lane-indexed vector
+  // load and is picked by sequence below.
+  const int winv = a.win[threadIdx.x & 63];
+  asm volatile("" ::"s"(a.kring), "s"(a.vring), "s"(a.mask), "s"(a.rope_noise), "s"(a.q),
+               "s"(a.k_noise), "s"(a.v_noise), "s"(a.out), "s"(a.part_acc), "s"(a.part_ml),
+               "s"(a.seq_stride), "s"(a.layer_offset), "s"(a.head_stride), "s"(a.n_seq),
+               "s"(a.n_head), "s"(a.n_head_kv), "s"(a.group), "s"(a.q_len), "s"(a.m),
+               "s"(a.cap), "s"(a.kv_total), "s"(a.n_split), "v"(winv));
   const int n_units = a.n_seq * a.n_head_kv;
   int unit, split;
   if ((n_units & 7) == 0) {
@@ -647,11 +710,8 @@ __global__ __launch_bounds__(NW * 64) void k_ring_attn(AttnArgs a) {
     unit = blockIdx.x / a.n_split;
     split = blockIdx.x % a.n_split;
   }
-  if (split == 0) {
-    attn_body<MB, NW, NR, true>(a, unit, split, lds, sm_m, sm_l);
-  } else {
-    attn_body<MB, NW, NR, false>(a, unit, split, lds, sm_m, sm_l);
-  }
+  const int win = __builtin_amdgcn_readlane(winv, unit / a.n_head_kv);
+  attn_body<MB, NW>(a, unit, split, win, lds, sm_m, sm_l);
 }
 
 // ---------------------------------------------------------------------------
@@ -680,7 +740,14 @@ __global__ __launch_bounds__(256) void k_ring_merge(MergeArgs a) {
     const int t = hl + 2 * k;
     u[k] = *(const float4*)(acc + (t < a.n_split ? t : 0) * acc_step);
   }
+  // Take every load as one batch: the reductions below start from a value
+  // that the empty asm statements make depend on every loaded register, so
+  // the scheduler cannot interleave them with the loads (it otherwise keeps
+  // only a few in flight).
   float mx = my.x;
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k)
+    asm volatile("" : "+v"(mx) : "v"(u[k].x), "v"(u[k].y), "v"(u[k].z), "v"(u[k].w));
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
   const float w = my.x == kNegInf ? 0.0f : exp2f(my.x - mx);
@@ -728,26 +795,11 @@ hipError_t launch_step(const StepArgs& a, hipStream_t s, hipEvent_t t0, hipEvent
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
   const int grid = a.n_seq * a.n_head_kv * a.n_split;
-  // noise rounds: two (row, frequency) items per thread per round
-  const int nr = (a.q_len * 64 + 511) / 512;
-#define RING_ATTN_LAUNCH(MB_, NR_) \
-  hipExtLaunchKernelGGL((k_ring_attn<MB_, 4, NR_>), dim3(grid), dim3(256), 0, s, t0, t1, 0, a)
   if (a.m <= 32) {
-    switch (nr) {
-      case 1: RING_ATTN_LAUNCH(1, 1); break;
-      case 2: RING_ATTN_LAUNCH(1, 2); break;
-      case 3: RING_ATTN_LAUNCH(1, 3); break;
-      default: RING_ATTN_LAUNCH(1, 4); break;
-    }
+    hipExtLaunchKernelGGL((k_ring_attn<1, 4>), dim3(grid), dim3(256), 0, s, t0, t1, 0, a);
   } else {
-    switch (nr) {
-      case 1: RING_ATTN_LAUNCH(2, 1); break;
-      case 2: RING_ATTN_LAUNCH(2, 2); break;
-      case 3: RING_ATTN_LAUNCH(2, 3); break;
-      default: RING_ATTN_LAUNCH(2, 4); break;
-    }
+    hipExtLaunchKernelGGL((k_ring_attn<2, 4>), dim3(grid), dim3(256), 0, s, t0, t1, 0, a);
   }
-#undef RING_ATTN_LAUNCH
   return hipGetLastError();
 }
 
