@@ -21,6 +21,11 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr float kNegInf = -__builtin_inff();
+
+// 2^x with the hardware instruction: about 1 ulp for normal results; results
+// below 2^-126 flush to zero and 2^-inf = 0.  Softmax weights that small
+// change no output at the precision that is kept.
+__device__ inline float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 // log2(e) / sqrt(128): folds the 1/sqrt(head_dim) score scale and the
 // change of base for exp2 into the query.
 constexpr double kQScale = 1.4426950408889634074 / 11.313708498984760390;
@@ -239,10 +244,10 @@ __device__ inline void attend_tile(const half8 (&kc)[8], const half8 (&vc)[8],
 #pragma unroll
       for (int j = 0; j < 16; ++j) s[j] = 0.0f;
     } else {
-      alpha = exp2f(m_run[mb] - mnew);
+      alpha = exp2_hw(m_run[mb] - mnew);
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        s[j] = exp2f(s[j] - mnew);
+        s[j] = exp2_hw(s[j] - mnew);
         ls += s[j];
       }
     }
@@ -292,13 +297,12 @@ __device__ inline void attend_tile(const half8 (&kc)[8], const half8 (&vc)[8],
 template <int MB, int NW>
 struct AttnShape {
   static constexpr int MP = MB * 32;               // padded queries
-  static constexpr int OS = 132;                   // LDS row stride of a merge region (floats)
   static constexpr int NT = NW * 64;               // threads
   static constexpr int kQBytes = MB * 2 * 8 * 64 * 16;
   static constexpr int kRowBytes = NW * 2 * kHeadDim * 2;  // one K and one V row per wave
-  static constexpr int kMergeBytes = NW * MP * OS * 4;
+  static constexpr int kMergeBytes = MB * 4 * NW * 4 * 64 * 16;  // reduce-scatter buffer
   // The query fragments and the noise-row buffers live until the end of the
-  // tile loop; the per-wave merge regions reuse the same bytes after it.
+  // tile loop; the merge buffer reuses the same bytes after it.
   static constexpr int kLdsBytes =
       kQBytes + kRowBytes > kMergeBytes ? kQBytes + kRowBytes : kMergeBytes;
 };
@@ -392,8 +396,8 @@ __device__ __forceinline__ void attend_noise_row(
     const float mnew = fmaxf(m_old, sc);
     float alpha = 1.0f, p = 0.0f;
     if (mnew != kNegInf) {
-      alpha = exp2f(m_old - mnew);
-      p = exp2f(sc - mnew);
+      alpha = exp2_hw(m_old - mnew);
+      p = exp2_hw(sc - mnew);
     }
     l_run[mb] = l_run[mb] * alpha + p;
     m_run[mb] = mnew;
@@ -417,7 +421,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int unit, int split
                                           unsigned char* lds, float (*sm_m)[MB * 32],
                                           float (*sm_l)[MB * 32]) {
   using S = AttnShape<MB, NW>;
-  constexpr int MP = S::MP, OS = S::OS, NT = S::NT;
+  constexpr int MP = S::MP, NT = S::NT;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hl = lane >> 5;
@@ -601,10 +605,13 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int unit, int split
 
   // ---- 5. merge the waves of this work-group.  Each lane owns query
   //      n = 32 mb + col: it combines the waves' running (max, sum) from LDS
-  //      into the work-group's (mx, lt), scales its O^T by 2^(m - mx) (and by
-  //      1 / lt when this is the only split) into its wave's LDS region (over
-  //      the prologue buffers, free once every wave is past the barrier
-  //      below); the regions are then summed with every read issued at once.
+  //      into the work-group's (mx, lt) and scales its O^T by 2^(m - mx)
+  //      (and by 1 / lt when this is the only split).  Then a reduce-scatter
+  //      over the four 32-dim blocks of O^T: wave w keeps block w, hands the
+  //      other three to their owners through LDS (same fragment order, so
+  //      lane l reads what lane l of the other wave wrote) and stores its
+  //      block of the output or partial from registers.
+  static_assert(NW == 4, "one 32-dim output block per wave");
   if (hl == 0) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -613,70 +620,89 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int unit, int split
     }
   }
   lds_barrier();
-  float* region = reinterpret_cast<float*>(lds) + wave * (MP * OS);
   float* pml = a.part_ml + ((int64_t)unit * a.n_split + split) * MP * 2;
+  // xbuf[mb][block][writer wave][jj][lane] float4
+  float4* xbuf = reinterpret_cast<float4*>(lds);
+  f32x16 own[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     const int n = mb * 32 + col;
-    float mw_[NW];
+    float mw_[NW], lw_[NW];
     float mx = kNegInf;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
       mw_[w] = sm_m[w][n];
+      lw_[w] = sm_l[w][n];
       mx = fmaxf(mx, mw_[w]);
     }
+    // A wave that saw no visible key has m = -inf and l = 0; selects, not
+    // branches, so every LDS read above is issued at once.
     float lt = 0.0f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w)
-      lt += mw_[w] == kNegInf ? 0.0f : sm_l[w][n] * exp2f(mw_[w] - mx);
-    float scale = m_run[mb] == kNegInf ? 0.0f : exp2f(m_run[mb] - mx);
+    for (int w = 0; w < NW; ++w) {
+      const float e = exp2_hw(mw_[w] - mx);
+      lt += mw_[w] == kNegInf ? 0.0f : lw_[w] * e;
+    }
+    const float es = exp2_hw(m_run[mb] - mx);
+    float scale = m_run[mb] == kNegInf ? 0.0f : es;
     if (a.n_split == 1) {
-      // lt > 0: the noise block is visible to every query of split 0.
+      // lt > 0: the noise rows are visible to every query.
       scale *= 1.0f / lt;
     } else if (wave == 0 && hl == 0 && n < a.m) {
       *(float2*)(pml + n * 2) = make_float2(mx, lt);
     }
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
+      const f32x16 ob = o[mb][b] * scale;
+      if (b == wave) {
+        own[mb] = ob;
+      } else {
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        *(float4*)&region[n * OS + 32 * b + 8 * jj + 4 * hl] =
-            make_float4(o[mb][b][4 * jj] * scale, o[mb][b][4 * jj + 1] * scale,
-                        o[mb][b][4 * jj + 2] * scale, o[mb][b][4 * jj + 3] * scale);
+        for (int jj = 0; jj < 4; ++jj)
+          xbuf[(((mb * 4 + b) * NW + wave) * 4 + jj) * 64 + lane] =
+              make_float4(ob[4 * jj], ob[4 * jj + 1], ob[4 * jj + 2], ob[4 * jj + 3]);
       }
     }
   }
   lds_barrier();
 
-  // ---- 6. the final output (one split) or this split's partial: item =
-  //      (query n, dims 4 d4 .. 4 d4 + 3), MP * 32 / NT items per thread.
-  const float* regions = reinterpret_cast<const float*>(lds);
+  // ---- 6. sum the block and write the final output (one split) or this
+  //      split's partial: lane (col, hl) holds dims 32 wave + 8 jj + 4 hl
+  //      + 0..3 of query 32 mb + col.  Rows past m are padding.
   float* out_unit = a.out + ((int64_t)seq * a.q_len * a.n_head + g * a.group) * kHeadDim;
   float* pacc = a.part_acc + ((int64_t)unit * a.n_split + split) * MP * kHeadDim;
-  constexpr int kItems = MP * 32 / NT;
-  float4 v[kItems];
 #pragma unroll
-  for (int it = 0; it < kItems; ++it) {
-    const int item = threadIdx.x + it * NT;
-    const int n = item >> 5, d4 = item & 31;
-    v[it] = *(const float4*)&regions[n * OS + 4 * d4];
+  for (int mb = 0; mb < MB; ++mb) {
+    float4 v[4];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) {
-      const float4 u = *(const float4*)&regions[w * (MP * OS) + n * OS + 4 * d4];
-      v[it].x += u.x; v[it].y += u.y; v[it].z += u.z; v[it].w += u.w;
-    }
-  }
+    for (int jj = 0; jj < 4; ++jj)
+      v[jj] = make_float4(own[mb][4 * jj], own[mb][4 * jj + 1], own[mb][4 * jj + 2],
+                          own[mb][4 * jj + 3]);
 #pragma unroll
-  for (int it = 0; it < kItems; ++it) {
-    const int item = threadIdx.x + it * NT;
-    const int n = item >> 5, d4 = item & 31;
-    if (n < a.m) {
-      if (a.n_split == 1) {
-        const unsigned i = n / a.group, hh = n - i * a.group;
-        *(float4*)(out_unit + (i * a.n_head + hh) * kHeadDim + 4 * d4) = v[it];
-      } else {
-        *(float4*)(pacc + n * kHeadDim + 4 * d4) = v[it];
+    for (int w = 0; w < NW; ++w) {
+      if (w == wave) continue;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const float4 u = xbuf[(((mb * 4 + wave) * NW + w) * 4 + jj) * 64 + lane];
+        v[jj].x += u.x; v[jj].y += u.y; v[jj].z += u.z; v[jj].w += u.w;
       }
+    }
+    const int n = mb * 32 + col;
+    if (a.n_split == 1 && n < a.m) {
+      const int d0 = 32 * wave + 4 * hl;
+      {
+        const unsigned i = n / a.group, hh = n - i * a.group;
+        float* dst = out_unit + (i * a.n_head + hh) * kHeadDim + d0;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) *(float4*)(dst + 8 * jj) = v[jj];
+      }
+    }
+    if (a.n_split > 1) {
+      // partial in fragment order [mb][block][jj][lane] float4: each store
+      // instruction writes 1 KB contiguous.
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        *(float4*)(pacc + (((mb * 4 + wave) * 4 + jj) * 64 + lane) * 4) = v[jj];
     }
   }
 }
@@ -716,63 +742,85 @@ __global__ __launch_bounds__(NW * 64) void k_ring_attn(AttnArgs a) {
 
 // ---------------------------------------------------------------------------
 // Cross-split merge: out = sum_t acc_t 2^(m_t - M) / sum_t l_t 2^(m_t - M),
-// M = max_t m_t.  One wave per (sequence, KV head, query): lane t holds split
-// t's (m, l); lane (h, d4) sums splits h, h + 2, ... of dims 4 d4 .. 4 d4 + 3.
-// Every load is issued before the first use (2 KMAX >= n_split, n_split <= 64).
+// M = max_t m_t.  The partial accumulators are in the attention's fragment
+// order [unit][split][mb][block b][jj][lane] float4, lane = query col + 32 hl
+// holding dims 32 b + 8 jj + 4 hl + 0..3.  One work-group per (unit, mb, b,
+// jj): wave w merges splits w, w + 4, ... (each split's float4 of a lane is
+// one contiguous 1 KB row of the wave and the merge is lane-local, every
+// load of the wave in flight together), then wave 0 combines the four
+// partial merges through LDS and writes the output.
 // ---------------------------------------------------------------------------
 template <int KMAX>
 __global__ __launch_bounds__(256) void k_ring_merge(MergeArgs a) {
+  __shared__ float sM[4][64], sL[4][64];
+  __shared__ float4 sO[4][64];
   const int lane = threadIdx.x & 63;
-  const int wv = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (wv >= a.n_units * a.m) return;
-  const int n = wv % a.m, unit = wv / a.m;
-  const int hl = lane >> 5, d4 = lane & 31;
-  const int64_t base = (int64_t)unit * a.n_split * a.mpad + n;
-  const float* ml = a.part_ml + base * 2;
-  const float* acc = a.part_acc + base * kHeadDim + 4 * d4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int per_unit = (a.mpad / 32) * 16;
+  const int unit = blockIdx.x / per_unit, f = blockIdx.x - unit * per_unit;
+  const int mb = f >> 4, b = (f >> 2) & 3, jj = f & 3;
+  const int col = lane & 31, hl = lane >> 5;
+  const int n = mb * 32 + col;
   const int64_t ml_step = (int64_t)a.mpad * 2, acc_step = (int64_t)a.mpad * kHeadDim;
+  const float* ml = a.part_ml + (int64_t)unit * a.n_split * ml_step + n * 2;
+  const float* acc = a.part_acc + (int64_t)unit * a.n_split * acc_step + (f * 64 + lane) * 4;
 
-  const float2 my = lane < a.n_split ? *(const float2*)(ml + lane * ml_step)
-                                     : make_float2(kNegInf, 0.0f);
+  float2 mlv[KMAX];
   float4 u[KMAX];
 #pragma unroll
   for (int k = 0; k < KMAX; ++k) {
-    const int t = hl + 2 * k;
-    u[k] = *(const float4*)(acc + (t < a.n_split ? t : 0) * acc_step);
+    const int t = min(wave + 4 * k, a.n_split - 1);
+    mlv[k] = *(const float2*)(ml + t * ml_step);
+    u[k] = *(const float4*)(acc + t * acc_step);
   }
   // Take every load as one batch: the reductions below start from a value
   // that the empty asm statements make depend on every loaded register, so
-  // the scheduler cannot interleave them with the loads (it otherwise keeps
-  // only a few in flight).
-  float mx = my.x;
+  // the scheduler cannot interleave them with the loads.
+  float mx = kNegInf;
 #pragma unroll
   for (int k = 0; k < KMAX; ++k)
-    asm volatile("" : "+v"(mx) : "v"(u[k].x), "v"(u[k].y), "v"(u[k].z), "v"(u[k].w));
+    asm volatile("" : "+v"(mx) : "v"(mlv[k].x), "v"(mlv[k].y), "v"(u[k].x), "v"(u[k].y),
+                 "v"(u[k].z), "v"(u[k].w));
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-  const float w = my.x == kNegInf ? 0.0f : exp2f(my.x - mx);
-  float lt = my.y * w;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) lt += __shfl_xor(lt, o);
-  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int k = 0; k < KMAX; ++k)
+    if (wave + 4 * k < a.n_split) mx = fmaxf(mx, mlv[k].x);
+  // A split that saw no visible key has m = -inf and l = 0.
+  float L = 0.0f;
+  float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
   for (int k = 0; k < KMAX; ++k) {
-    const int t = hl + 2 * k;
-    const float wt = __shfl(w, t);
-    const float ws = t < a.n_split ? wt : 0.0f;
-    v.x += ws * u[k].x; v.y += ws * u[k].y; v.z += ws * u[k].z; v.w += ws * u[k].w;
+    const float e = exp2_hw(mlv[k].x - mx);
+    const float w = (wave + 4 * k < a.n_split && mlv[k].x != kNegInf) ? e : 0.0f;
+    L += w * mlv[k].y;
+    O.x += w * u[k].x; O.y += w * u[k].y; O.z += w * u[k].z; O.w += w * u[k].w;
   }
-  v.x += __shfl_xor(v.x, 32);
-  v.y += __shfl_xor(v.y, 32);
-  v.z += __shfl_xor(v.z, 32);
-  v.w += __shfl_xor(v.w, 32);
-  if (hl == 0) {
-    const float inv = 1.0f / lt;
-    v.x *= inv; v.y *= inv; v.z *= inv; v.w *= inv;
+  sM[wave][lane] = mx;
+  sL[wave][lane] = L;
+  sO[wave][lane] = O;
+  lds_barrier();
+  if (wave != 0) return;
+  float M = kNegInf;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) M = fmaxf(M, sM[w][lane]);
+  float Lt = 0.0f;
+  float4 Ot = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float mw = sM[w][lane];
+    const float e = exp2_hw(mw - M);
+    const float s = mw == kNegInf ? 0.0f : e;
+    const float4 ow = sO[w][lane];
+    Lt += s * sL[w][lane];
+    Ot.x += s * ow.x; Ot.y += s * ow.y; Ot.z += s * ow.z; Ot.w += s * ow.w;
+  }
+  if (n < a.m) {
+    // Lt > 0: the noise rows are visible to every query.
+    const float inv = 1.0f / Lt;
+    Ot.x *= inv; Ot.y *= inv; Ot.z *= inv; Ot.w *= inv;
     const int seq = unit / a.n_head_kv, g = unit - seq * a.n_head_kv;
     const int i = n / a.group, hh = n - i * a.group;
     float* dst = a.out + (((int64_t)seq * a.q_len + i) * a.n_head + g * a.group + hh) * kHeadDim;
-    *(float4*)(dst + 4 * d4) = v;
+    *(float4*)(dst + 32 * b + 8 * jj + 4 * hl) = Ot;
   }
 }
 
@@ -804,16 +852,18 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s, hipEvent_t t0, hipEvent
 }
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
-  const int waves = a.n_units * a.m;
-  const dim3 grid((waves + 3) / 4), block(256);
-  if (a.n_split <= 2) {
+  const dim3 grid(a.n_units * (a.mpad / 32) * 16), block(256);
+  const int per_wave = (a.n_split + 3) / 4;  // splits per wave (n_split <= 64)
+  if (per_wave <= 1) {
     hipExtLaunchKernelGGL(k_ring_merge<1>, grid, block, 0, s, t0, t1, 0, a);
-  } else if (a.n_split <= 8) {
+  } else if (per_wave <= 2) {
+    hipExtLaunchKernelGGL(k_ring_merge<2>, grid, block, 0, s, t0, t1, 0, a);
+  } else if (per_wave <= 4) {
     hipExtLaunchKernelGGL(k_ring_merge<4>, grid, block, 0, s, t0, t1, 0, a);
-  } else if (a.n_split <= 32) {
-    hipExtLaunchKernelGGL(k_ring_merge<16>, grid, block, 0, s, t0, t1, 0, a);
+  } else if (per_wave <= 8) {
+    hipExtLaunchKernelGGL(k_ring_merge<8>, grid, block, 0, s, t0, t1, 0, a);
   } else {
-    hipExtLaunchKernelGGL(k_ring_merge<32>, grid, block, 0, s, t0, t1, 0, a);
+    hipExtLaunchKernelGGL(k_ring_merge<16>, grid, block, 0, s, t0, t1, 0, a);
   }
   return hipGetLastError();
 }

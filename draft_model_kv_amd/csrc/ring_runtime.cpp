@@ -48,7 +48,7 @@ struct Layout {
   size_t off_pacc = 0, off_pml = 0, total = 0;
 };
 
-constexpr int kMaxSplits = 64;  // the merge kernel holds one split per lane
+constexpr int kMaxSplits = 64;  // each merge wave holds up to 16 splits in registers
 
 // Splits of the ring tiles per (sequence, KV head): enough work-groups to
 // cover the 256 compute units, and at least one 32-slot tile per wave.
