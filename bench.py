@@ -174,6 +174,149 @@ def prepare(w, pool: int, total: int, dev):
     return rings, calls, steps_in, committed
 
 
+# The rocprofv3 runs behind the committed summaries under profiles/, each run
+# from /tmp (TMPDIR=/tmp) with REPO the repository root and OUT an output
+# directory; `python bench.py --summarize OUT` then writes the summaries.
+PROFILE_RUNS = {
+    "prof_ktrace": "rocprofv3 --kernel-trace --stats --output-format csv -d OUT/prof_ktrace -o run "
+                   "-- python REPO/bench.py --steps 1000 --warmup 100 --no-cpu-baseline",
+    "pmc_fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/pmc_fetch -o run "
+                 "-- python REPO/bench.py --steps 64 --warmup 16 --no-cpu-baseline",
+    "pmc_write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/pmc_write -o run "
+                 "-- python REPO/bench.py --steps 64 --warmup 16 --no-cpu-baseline",
+    "pmc_copy_fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/pmc_copy_fetch -o run "
+                      "-- python REPO/bench.py --calibrate-copy 1024",
+    "pmc_copy_write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/pmc_copy_write -o run "
+                      "-- python REPO/bench.py --calibrate-copy 1024",
+    # the same bench without the profiler (its HIP-event kernel times are
+    # compared with the trace; the tracer itself slows event-bound dispatches)
+    "bench_plain": "python REPO/bench.py --steps 1000 --warmup 100 --no-cpu-baseline",
+}
+CALIBRATE_COPY_MIB = 1024
+KERNELS = ("k_ring_attn", "k_ring_step", "k_ring_merge")
+
+
+def _csv_rows(out_dir: str, run: str, kind: str):
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(out_dir, run, "**", f"*{kind}.csv"), recursive=True))
+    if not files:
+        raise FileNotFoundError(f"no *{kind}.csv under {os.path.join(out_dir, run)}")
+    rows = []
+    for f in files:
+        with open(f, newline="") as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def _kib_per_dispatch(out_dir: str, run: str, counter: str, pick) -> tuple:
+    vals = [float(r["Counter_Value"]) for r in _csv_rows(out_dir, run, "counter_collection")
+            if r["Counter_Name"] == counter and pick(r["Kernel_Name"])]
+    if not vals:
+        raise ValueError(f"{run}: no {counter} values for the kernel")
+    return sum(vals) / len(vals), len(vals)
+
+
+def _bench_line(out_dir: str, run: str):
+    path = os.path.join(out_dir, run + ".log")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        for ln in fh:
+            ln = ln.strip()
+            if ln.startswith("{") and '"metric"' in ln:
+                return json.loads(ln)
+    return None
+
+
+def summarize_profiles(out_dir: str) -> int:
+    """Write profiles/*.md and the traffic JSON from the rocprofv3 CSV output
+    of PROFILE_RUNS (and each run's stdout in OUT/<run>.log when present)."""
+    khash = kernel_source_hash()
+    prof = os.path.join(ROOT, "profiles")
+    os.makedirs(prof, exist_ok=True)
+    wl = "decode_stream (cap 4096, q_len 8, GQA 32/8 x 128, F16, 1 layer, 32-ring pool)"
+    cmd = lambda run: PROFILE_RUNS[run]  # noqa: E731
+
+    # kernel trace
+    stats = _csv_rows(out_dir, "prof_ktrace", "kernel_stats")
+    bl = _bench_line(out_dir, "bench_plain")
+    lines = [f"# Kernel trace: k_ring_attn and the ring step kernels, {wl}", "",
+             f"Kernel source hash: `{khash}`", "", "Command (cd /tmp; TMPDIR=/tmp):", "",
+             f"    {cmd('prof_ktrace')}", "",
+             "| kernel | calls | avg us | min us | max us | share of GPU time |",
+             "|---|---:|---:|---:|---:|---:|"]
+    trace = {}
+    for r in stats:
+        name = r["Name"]
+        short = next((k for k in KERNELS if k in name), None)
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{float(r['Percentage']):.1f}% |")
+        if short:
+            trace[short] = float(r["AverageNs"]) / 1e3
+    if bl:
+        ev = {k: v["avg_us"] for k, v in bl.get("kernels", {}).items()}
+        lines += ["", "The same bench without the profiler (" + f"`{cmd('bench_plain')}`" + "), "
+                  "HIP events bound to the dispatches of its profiled segment: "
+                  + ", ".join(f"{k} {v:.2f} us" for k, v in ev.items() if v)
+                  + f"; {bl['value']:.0f} steps/s in its timed segment."]
+    with open(os.path.join(prof, "k_ring_attn_decode_stream_kernel_trace.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+    # HBM traffic from FETCH_SIZE / WRITE_SIZE, scaled by a plain copy
+    copy_bytes = CALIBRATE_COPY_MIB << 20
+    cf, ncf = _kib_per_dispatch(out_dir, "pmc_copy_fetch", "FETCH_SIZE", lambda n: "copyBuffer" in n)
+    cw, ncw = _kib_per_dispatch(out_dir, "pmc_copy_write", "WRITE_SIZE", lambda n: "copyBuffer" in n)
+    fetch_scale = copy_bytes / (cf * 1024)
+    write_scale = copy_bytes / (cw * 1024)
+    rows = {}
+    for k in KERNELS:
+        f, nf = _kib_per_dispatch(out_dir, "pmc_fetch", "FETCH_SIZE", lambda n, k=k: k in n)
+        w, nw = _kib_per_dispatch(out_dir, "pmc_write", "WRITE_SIZE", lambda n, k=k: k in n)
+        rows[k] = {"fetch_kib": f, "write_kib": w, "dispatches": min(nf, nw),
+                   "hbm_bytes": f * 1024 * fetch_scale + w * 1024 * write_scale}
+    import workload as W
+    w_ = W.WORKLOADS[WORKLOAD]
+    alg = algorithmic_bytes(w_, w_.cap, 0)
+    alg_attn = alg["kv"] + alg["q"] + alg["noise"] + w_.q_len * (w_.cap + 2 * w_.q_len) * 2
+    t = {"kernel_source_hash": khash, "workload": WORKLOAD,
+         "fetch_scale": fetch_scale, "write_scale": write_scale,
+         "copy_calibration": {"bytes": copy_bytes, "fetch_kib": cf, "write_kib": cw,
+                              "dispatches": [ncf, ncw]},
+         "kernels": rows, "hbm_bytes_per_launch": rows["k_ring_attn"]["hbm_bytes"],
+         "commands": {k: PROFILE_RUNS[k] for k in ("pmc_fetch", "pmc_write", "pmc_copy_fetch",
+                                                  "pmc_copy_write")}}
+    with open(os.path.join(prof, "ring_attn_decode_stream_traffic.json"), "w") as fh:
+        json.dump(t, fh, indent=1)
+        fh.write("\n")
+    a = rows["k_ring_attn"]
+    lines = [f"# HBM traffic per dispatch: k_ring_attn and the ring step kernels, {wl}", "",
+             f"Kernel source hash: `{khash}`", "", "Commands (cd /tmp; TMPDIR=/tmp), one counter per run:", ""]
+    lines += [f"    {cmd(r)}" for r in ("pmc_fetch", "pmc_write", "pmc_copy_fetch", "pmc_copy_write")]
+    lines += ["", f"Calibration: a plain {CALIBRATE_COPY_MIB} MiB device copy reads FETCH_SIZE "
+              f"{cf:.0f} KiB and WRITE_SIZE {cw:.0f} KiB per dispatch, so FETCH_SIZE is scaled by "
+              f"{fetch_scale:.3f} and WRITE_SIZE by {write_scale:.3f}.", "",
+              "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled HBM MB |",
+              "|---|---:|---:|---:|---:|"]
+    for k, r in rows.items():
+        lines.append(f"| {k} | {r['dispatches']} | {r['fetch_kib']:.1f} | {r['write_kib']:.1f} | "
+                     f"{r['hbm_bytes'] / 1e6:.3f} |")
+    lines += ["", f"k_ring_attn: scaled reads {a['fetch_kib'] * 1024 * fetch_scale / 1e6:.3f} MB per "
+              f"launch against {alg_attn / 1e6:.3f} MB of algorithmic reads (visible K/V rows, "
+              f"queries, noise rows, mask); writes {a['write_kib'] * 1024 * write_scale / 1e6:.3f} MB "
+              "(split partials and the noise rows stored to the ring)."]
+    if "k_ring_attn" in trace:
+        lines.append(f"Average k_ring_attn duration in the kernel trace: {trace['k_ring_attn']:.2f} us.")
+    with open(os.path.join(prof, "k_ring_attn_decode_stream_hbm_traffic.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(json.dumps({"written": ["profiles/k_ring_attn_decode_stream_kernel_trace.md",
+                                  "profiles/k_ring_attn_decode_stream_hbm_traffic.md",
+                                  "profiles/ring_attn_decode_stream_traffic.json"],
+                      "kernel_source_hash": khash}))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -187,6 +330,8 @@ def main() -> int:
                          "256 MB Infinity Cache; 1 = cache-warm)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--summarize", metavar="OUT", default="",
+                    help="write profiles/ summaries from rocprofv3 output under OUT")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB ten times (scale for the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -195,6 +340,8 @@ def main() -> int:
         print(f"bench.py runs on one GPU: the ring step has no multi-GPU path "
               f"(--gpus {args.gpus} requested)", file=sys.stderr)
         return 2
+    if args.summarize:
+        return summarize_profiles(args.summarize)
 
     import numpy as np
     import torch
