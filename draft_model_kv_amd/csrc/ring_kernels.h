@@ -24,6 +24,7 @@ struct StepArgs {
   int32_t* slot_pos;         // [cap]
   uint16_t* mask;            // [q_len][kv_total]
   double* rope_noise;        // [q_len][64][2] (cos, sin) at committed + i
+  float* rope_q;             // [q_len][64][2] the same values rounded to fp32
   const double* inv_freq;    // [64] theta_i
   int64_t start;             // first new position
   int32_t start_mod;         // start % cap
@@ -43,6 +44,7 @@ struct AttnArgs {
   uint16_t* vring;
   const uint16_t* mask;      // [n_seq][q_len][kv_total]
   const double* rope_noise;  // [n_seq][q_len][64][2]
+  const float* rope_q;       // [n_seq][q_len][64][2] the same values rounded to fp32
   const uint16_t* q;         // [n_seq][q_len][n_head][128]
   const uint16_t* k_noise;   // [n_seq][q_len][kv_row]
   const uint16_t* v_noise;

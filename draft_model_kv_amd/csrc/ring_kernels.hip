@@ -148,6 +148,8 @@ __global__ __launch_bounds__(256) void k_ring_step(StepArgs a) {
       sincos((double)(a.committed + i) * a.inv_freq[f], &sn, &cs);
       a.rope_noise[2 * item] = cs;
       a.rope_noise[2 * item + 1] = sn;
+      a.rope_q[2 * item] = (float)cs;
+      a.rope_q[2 * item + 1] = (float)sn;
     }
   }
   const int s = mblk * 256 + t;
@@ -301,10 +303,15 @@ struct AttnShape {
   static constexpr int kQBytes = MB * 2 * 8 * 64 * 16;
   static constexpr int kRowBytes = NW * 2 * kHeadDim * 2;  // one K and one V row per wave
   static constexpr int kMergeBytes = MB * 4 * NW * 4 * 64 * 16;  // reduce-scatter buffer
-  // The query fragments and the noise-row buffers live until the end of the
-  // tile loop; the merge buffer reuses the same bytes after it.
+  // The query fragments and the noise-row buffers live until a wave's tile
+  // loop ends.  With one query block the merge buffer has bytes of its own,
+  // so a wave writes it as soon as its own loop ends; with two it reuses the
+  // prologue bytes behind a barrier that every wave reaches after its loop.
+  static constexpr bool kOwnMergeBytes = kQBytes + kRowBytes + kMergeBytes <= 96 * 1024;
+  static constexpr int kMergeOffset = kOwnMergeBytes ? kQBytes + kRowBytes : 0;
   static constexpr int kLdsBytes =
-      kQBytes + kRowBytes > kMergeBytes ? kQBytes + kRowBytes : kMergeBytes;
+      kOwnMergeBytes ? kQBytes + kRowBytes + kMergeBytes
+                     : (kQBytes + kRowBytes > kMergeBytes ? kQBytes + kRowBytes : kMergeBytes);
 };
 
 // One noise row of this wave's (sequence, head), already loaded: lane f holds
@@ -429,7 +436,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int unit, int split
 
   const int seq = unit / a.n_head_kv;
   const int g = unit - seq * a.n_head_kv;
-  const double* rope = a.rope_noise + (int64_t)seq * a.q_len * 128;
+  const float* ropeq = a.rope_q + (int64_t)seq * a.q_len * 128;
   const uint16_t* mask_seq = a.mask + (int64_t)seq * a.q_len * a.kv_total;
 
   // Ring tiles of this split: the visible ring slots are [0, win).
@@ -457,7 +464,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int unit, int split
   // ---- 1a. loads for the query build: thread item = (mb, chunk pair c,
   //      lane ln); x = dims 16c + 8h + e, y = the same dims + 64.
   half8 qx[MB], qy[MB];
-  double2 qcs[MB][8];
+  float4 qcs[MB][4];  // (cos, sin) pairs of frequencies 16c + 8h + e, e = 0..7
   const uint16_t* qseq = a.q + ((int64_t)seq * a.q_len * a.n_head + g * a.group) * kHeadDim;
 #pragma unroll
   for (int k = 0; k < MB; ++k) {
@@ -468,9 +475,9 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int unit, int split
     const unsigned qo = (i * a.n_head + hh) * kHeadDim + 16 * c + 8 * h2;
     qx[k] = *(const half8*)(qseq + qo);
     qy[k] = *(const half8*)(qseq + qo + 64);
+    const float4* rq = (const float4*)(ropeq + (i * 64 + 16 * c + 8 * h2) * 2);
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      qcs[k][e] = *(const double2*)(rope + (i * 64 + 16 * c + 8 * h2 + e) * 2);
+    for (int e2 = 0; e2 < 4; ++e2) qcs[k][e2] = rq[e2];
   }
 
   // ---- 1b. the wave's first noise row (a wave without one loads the last
@@ -520,7 +527,8 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int unit, int split
       float xr[2], yr[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const float cs = (float)qcs[k][e + u].x, sn = (float)qcs[k][e + u].y;
+        const float cs = u ? qcs[k][e >> 1].z : qcs[k][e >> 1].x;
+        const float sn = u ? qcs[k][e >> 1].w : qcs[k][e >> 1].y;
         const float x = valid ? (float)qx[k][e + u] : 0.0f;
         const float y = valid ? (float)qy[k][e + u] : 0.0f;
         xr[u] = (x * cs - y * sn) * (float)kQScale;
@@ -603,101 +611,97 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int unit, int split
     tile = next;
   }
 
-  // ---- 5. merge the waves of this work-group.  Each lane owns query
-  //      n = 32 mb + col: it combines the waves' running (max, sum) from LDS
-  //      into the work-group's (mx, lt) and scales its O^T by 2^(m - mx)
-  //      (and by 1 / lt when this is the only split).  Then a reduce-scatter
-  //      over the four 32-dim blocks of O^T: wave w keeps block w, hands the
-  //      other three to their owners through LDS (same fragment order, so
-  //      lane l reads what lane l of the other wave wrote) and stores its
-  //      block of the output or partial from registers.
+  // ---- 5. merge the waves of this work-group by reduce-scatter over the
+  //      four 32-dim blocks of O^T: wave w keeps block w and hands the other
+  //      three, unscaled, to their owners through LDS (same fragment order,
+  //      so lane l reads what lane l of the other wave wrote), together with
+  //      its running (max, sum) per query.  After one barrier each lane owns
+  //      query n = 32 mb + col: it forms the work-group's (mx, lt), weighs
+  //      every wave's block by 2^(m - mx) (and by 1 / lt when this is the only
+  //      split) and stores its block of the output or partial.
   static_assert(NW == 4, "one 32-dim output block per wave");
-  if (hl == 0) {
+  // [mb][block][writer][jj][lane]
+  float4* xbuf = reinterpret_cast<float4*>(lds + S::kMergeOffset);
+  if constexpr (!S::kOwnMergeBytes) lds_barrier();  // every wave is past its loop
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
+  for (int mb = 0; mb < MB; ++mb) {
+    if (hl == 0) {
       sm_m[wave][mb * 32 + col] = m_run[mb];
       sm_l[wave][mb * 32 + col] = l_run[mb];
     }
-  }
-  lds_barrier();
-  float* pml = a.part_ml + ((int64_t)unit * a.n_split + split) * MP * 2;
-  // xbuf[mb][block][writer wave][jj][lane] float4
-  float4* xbuf = reinterpret_cast<float4*>(lds);
-  f32x16 own[MB];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const int n = mb * 32 + col;
-    float mw_[NW], lw_[NW];
-    float mx = kNegInf;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      mw_[w] = sm_m[w][n];
-      lw_[w] = sm_l[w][n];
-      mx = fmaxf(mx, mw_[w]);
-    }
-    // A wave that saw no visible key has m = -inf and l = 0; selects, not
-    // branches, so every LDS read above is issued at once.
-    float lt = 0.0f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float e = exp2_hw(mw_[w] - mx);
-      lt += mw_[w] == kNegInf ? 0.0f : lw_[w] * e;
-    }
-    const float es = exp2_hw(m_run[mb] - mx);
-    float scale = m_run[mb] == kNegInf ? 0.0f : es;
-    if (a.n_split == 1) {
-      // lt > 0: the noise rows are visible to every query.
-      scale *= 1.0f / lt;
-    } else if (wave == 0 && hl == 0 && n < a.m) {
-      *(float2*)(pml + n * 2) = make_float2(mx, lt);
-    }
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      const f32x16 ob = o[mb][b] * scale;
-      if (b == wave) {
-        own[mb] = ob;
-      } else {
+      if (b == wave) continue;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-          xbuf[(((mb * 4 + b) * NW + wave) * 4 + jj) * 64 + lane] =
-              make_float4(ob[4 * jj], ob[4 * jj + 1], ob[4 * jj + 2], ob[4 * jj + 3]);
-      }
+      for (int jj = 0; jj < 4; ++jj)
+        xbuf[(((mb * 4 + b) * NW + wave) * 4 + jj) * 64 + lane] =
+            make_float4(o[mb][b][4 * jj], o[mb][b][4 * jj + 1], o[mb][b][4 * jj + 2],
+                        o[mb][b][4 * jj + 3]);
     }
   }
   lds_barrier();
 
-  // ---- 6. sum the block and write the final output (one split) or this
-  //      split's partial: lane (col, hl) holds dims 32 wave + 8 jj + 4 hl
-  //      + 0..3 of query 32 mb + col.  Rows past m are padding.
+  // ---- 6. the final output (one split) or this split's partial: lane
+  //      (col, hl) holds dims 32 wave + 8 jj + 4 hl + 0..3 of query
+  //      32 mb + col.  Rows past m are padding.
   float* out_unit = a.out + ((int64_t)seq * a.q_len * a.n_head + g * a.group) * kHeadDim;
   float* pacc = a.part_acc + ((int64_t)unit * a.n_split + split) * MP * kHeadDim;
+  float* pml = a.part_ml + ((int64_t)unit * a.n_split + split) * MP * 2;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
-    float4 v[4];
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj)
-      v[jj] = make_float4(own[mb][4 * jj], own[mb][4 * jj + 1], own[mb][4 * jj + 2],
-                          own[mb][4 * jj + 3]);
+    const int n = mb * 32 + col;
+    float mw_[NW], lw_[NW];
+    float4 blk[NW][4];
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
+      mw_[w] = sm_m[w][n];
+      lw_[w] = sm_l[w][n];
       if (w == wave) continue;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const float4 u = xbuf[(((mb * 4 + wave) * NW + w) * 4 + jj) * 64 + lane];
-        v[jj].x += u.x; v[jj].y += u.y; v[jj].z += u.z; v[jj].w += u.w;
-      }
+      for (int jj = 0; jj < 4; ++jj) blk[w][jj] = xbuf[(((mb * 4 + wave) * NW + w) * 4 + jj) * 64 + lane];
     }
-    const int n = mb * 32 + col;
-    if (a.n_split == 1 && n < a.m) {
-      const int d0 = 32 * wave + 4 * hl;
-      {
-        const unsigned i = n / a.group, hh = n - i * a.group;
-        float* dst = out_unit + (i * a.n_head + hh) * kHeadDim + d0;
+    float mx = kNegInf;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) *(float4*)(dst + 8 * jj) = v[jj];
-      }
+    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, mw_[w]);
+    // A wave that saw no visible key has m = -inf and l = 0; selects, not
+    // branches, so every LDS read above is issued at once.
+    float sw[NW], lt = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float e = exp2_hw(mw_[w] - mx);
+      sw[w] = mw_[w] == kNegInf ? 0.0f : e;
+      lt += sw[w] * lw_[w];
     }
-    if (a.n_split > 1) {
+    float4 v[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        float4 u;
+        if (w == wave) {
+          u = make_float4(o[mb][w][4 * jj], o[mb][w][4 * jj + 1], o[mb][w][4 * jj + 2],
+                          o[mb][w][4 * jj + 3]);
+        } else {
+          u = blk[w][jj];
+        }
+        acc.x += sw[w] * u.x; acc.y += sw[w] * u.y; acc.z += sw[w] * u.z; acc.w += sw[w] * u.w;
+      }
+      v[jj] = acc;
+    }
+    if (a.n_split == 1) {
+      // lt > 0: the noise rows are visible to every query.
+      const float inv = 1.0f / lt;
+      if (n < a.m) {
+        const unsigned i = n / a.group, hh = n - i * a.group;
+        float* dst = out_unit + (i * a.n_head + hh) * kHeadDim + 32 * wave + 4 * hl;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          *(float4*)(dst + 8 * jj) = make_float4(v[jj].x * inv, v[jj].y * inv, v[jj].z * inv,
+                                                 v[jj].w * inv);
+      }
+    } else {
+      if (wave == 0 && hl == 0 && n < a.m) *(float2*)(pml + n * 2) = make_float2(mx, lt);
       // partial in fragment order [mb][block][jj][lane] float4: each store
       // instruction writes 1 KB contiguous.
 #pragma unroll
@@ -721,7 +725,8 @@ __global__ __launch_bounds__(NW * 64) void k_ring_attn(AttnArgs a) {
   // first ring load can issue.  win[] comes in as one lane-indexed vector
   // load and is picked by sequence below.
   const int winv = a.win[threadIdx.x & 63];
-  asm volatile("" ::"s"(a.kring), "s"(a.vring), "s"(a.mask), "s"(a.rope_noise), "s"(a.q),
+  asm volatile("" ::"s"(a.kring), "s"(a.vring), "s"(a.mask), "s"(a.rope_noise), "s"(a.rope_q),
+               "s"(a.q),
                "s"(a.k_noise), "s"(a.v_noise), "s"(a.out), "s"(a.part_acc), "s"(a.part_ml),
                "s"(a.seq_stride), "s"(a.layer_offset), "s"(a.head_stride), "s"(a.n_seq),
                "s"(a.n_head), "s"(a.n_head_kv), "s"(a.group), "s"(a.q_len), "s"(a.m),

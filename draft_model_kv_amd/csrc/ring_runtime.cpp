@@ -44,7 +44,8 @@ int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 struct Layout {
   int32_t n_tiles = 0, m = 0, mpad = 0, group = 0, n_split = 1;
   int64_t seq_stride = 0;  // halves per sequence in the K (or V) ring
-  size_t off_k = 0, off_v = 0, off_slot = 0, off_mask = 0, off_rope = 0, off_freq = 0;
+  size_t off_k = 0, off_v = 0, off_slot = 0, off_mask = 0, off_rope = 0, off_ropeq = 0,
+         off_freq = 0;
   size_t off_pacc = 0, off_pml = 0, total = 0;
 };
 
@@ -111,6 +112,7 @@ void geometry_of(const ring_config& c, ring_geometry* g, Layout* L) {
   L->off_slot = take((size_t)c.n_seq * c.cap * 4);
   L->off_mask = take((size_t)c.n_seq * c.q_len * g->kv_total * 2);
   L->off_rope = take((size_t)c.n_seq * c.q_len * 64 * 2 * 8);
+  L->off_ropeq = take((size_t)c.n_seq * c.q_len * 64 * 2 * 4);
   L->off_freq = take(64 * 8);
   const size_t n_part = L->n_split > 1 ? (size_t)c.n_seq * c.n_head_kv * L->n_split * L->mpad : 0;
   L->off_pacc = take(n_part * kHeadDim * 4);
@@ -152,6 +154,7 @@ struct ring {
   int32_t* slot_pos = nullptr;
   uint16_t* mask = nullptr;
   double* rope_noise = nullptr;
+  float* rope_q = nullptr;
   double* inv_freq = nullptr;
   float* part_acc = nullptr;
   float* part_ml = nullptr;
@@ -181,6 +184,7 @@ StepArgs step_args(ring* r, int32_t seq) {
   a.slot_pos = r->slot_pos + (int64_t)seq * r->cfg.cap;
   a.mask = r->mask + (int64_t)seq * r->cfg.q_len * r->geo.kv_total;
   a.rope_noise = r->rope_noise + (int64_t)seq * r->cfg.q_len * 128;
+  a.rope_q = r->rope_q + (int64_t)seq * r->cfg.q_len * 128;
   a.inv_freq = r->inv_freq;
   a.cap = r->cfg.cap;
   a.q_len = r->cfg.q_len;
@@ -268,6 +272,7 @@ int ring_init(const ring_config* cfg, void* workspace, size_t workspace_bytes, v
   r->slot_pos = reinterpret_cast<int32_t*>(r->ws + r->L.off_slot);
   r->mask = reinterpret_cast<uint16_t*>(r->ws + r->L.off_mask);
   r->rope_noise = reinterpret_cast<double*>(r->ws + r->L.off_rope);
+  r->rope_q = reinterpret_cast<float*>(r->ws + r->L.off_ropeq);
   r->inv_freq = reinterpret_cast<double*>(r->ws + r->L.off_freq);
   r->part_acc = reinterpret_cast<float*>(r->ws + r->L.off_pacc);
   r->part_ml = reinterpret_cast<float*>(r->ws + r->L.off_pml);
@@ -414,6 +419,7 @@ int ring_attn(ring_t* r, int32_t layer, const void* q, const void* k_noise, cons
   a.vring = r->vring;
   a.mask = r->mask;
   a.rope_noise = r->rope_noise;
+  a.rope_q = r->rope_q;
   a.q = static_cast<const uint16_t*>(q);
   a.k_noise = static_cast<const uint16_t*>(k_noise);
   a.v_noise = static_cast<const uint16_t*>(v_noise);
