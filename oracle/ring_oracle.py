@@ -11,7 +11,11 @@ section 1 ("what the ring does in Luce"):
   * 1.3  win, lo, start, n_new; bulk append when n_new > a_step, fold-in with
          pad rows to trash_slot otherwise; noise positions committed + i.
   * 1.4  full-attention mask: 0 iff lo <= slot_pos[s] < committed, noise
-         block visible both ways, everything else -inf.
+         block visible both ways, everything else -inf.  Sliding-window
+         mask for SWA layers: the window shrinks to
+         eff_win = min(swa_window, win) positions ending at committed (the
+         same anchor for every noise row) and the noise block is causal
+         (noise row i sees noise slots j <= i).
   * 1.6  the legacy path recomputes the whole window every step.
   * 1.7  the ring equals that legacy full-window recompute (absolute RoPE plus
          masks); memory is 2 * n_layer * kv_row * kv_total * 2 bytes.
@@ -227,19 +231,25 @@ class FullCache:
 
 def attend(cache: FullCache, committed: int, cap: int, q: np.ndarray,
            k_noise: np.ndarray, v_noise: np.ndarray, n_head: int,
-           dtype=np.float64) -> np.ndarray:
+           dtype=np.float64, swa_window: Optional[int] = None) -> np.ndarray:
     """Attention of the noise block over the window [lo, committed) plus noise.
 
     q: [q_len, n_head, head_dim] F16, pre-RoPE; k_noise, v_noise: [q_len, kv_row]
     F16 (k pre-RoPE).  Returns [q_len, n_head, head_dim] in ``dtype``.  With
     dtype float32 the scores, softmax and weighted sum accumulate in fp32
     (inputs are the same F16 values and fp64 RoPE angles).
+
+    ``swa_window`` selects the sliding-window layer form of section 1.4: the
+    window is the last min(swa_window, win) committed positions and noise
+    query i attends noise keys j <= i only.
     """
     d = cache.head_dim
     hk = cache.n_head_kv
     group = n_head // hk
     q_len = q.shape[0]
     win = min(committed, cap)
+    if swa_window is not None:
+        win = min(swa_window, win)
     lo = committed - win
     pq = noise_positions(committed, q_len)
 
@@ -250,10 +260,15 @@ def attend(cache: FullCache, committed: int, cap: int, q: np.ndarray,
 
     qr = rope(q, pq, cache.base).astype(dtype)          # [q_len, n_head, d]
     scale = dtype(1.0 / math.sqrt(d))
+    bias = np.zeros((q_len, keys.shape[0]), dtype=dtype)
+    if swa_window is not None:
+        n_ctx = committed - lo
+        later = np.arange(q_len)[None, :] > np.arange(q_len)[:, None]   # key j > query i
+        bias[:, n_ctx:] = np.where(later, -np.inf, 0.0)
     out = np.empty((q_len, n_head, d), dtype=dtype)
     for h in range(n_head):
         g = h // group
-        s = (qr[:, h, :] @ keys[:, g, :].T) * scale      # [q_len, n_keys]
+        s = (qr[:, h, :] @ keys[:, g, :].T) * scale + bias  # [q_len, n_keys]
         m = s.max(axis=1, keepdims=True)
         w = np.exp(s - m)
         l = w.sum(axis=1, keepdims=True)
@@ -287,6 +302,23 @@ def mask_full(g: Geometry, slot_pos: np.ndarray, committed: int) -> np.ndarray:
     return np.broadcast_to(row, (g.q_len, g.kv_total)).copy()
 
 
+def mask_swa(g: Geometry, slot_pos: np.ndarray, committed: int, swa_window: int) -> np.ndarray:
+    """F16 mask [q_len, kv_total] of a sliding-window layer (section 1.4).
+
+    eff_win = min(swa_window, win) and swa_lo = committed - eff_win: ring slot
+    s is visible to every noise row iff swa_lo <= slot_pos[s] < committed;
+    noise slot cap + j is visible to noise row i iff j <= i.
+    """
+    eff_win = min(swa_window, min(committed, g.cap))
+    swa_lo = committed - eff_win
+    sp = slot_pos.astype(np.int64)
+    m = np.full((g.q_len, g.kv_total), NEG_INF_F16, dtype=np.float16)
+    m[:, : g.cap] = np.where((sp >= swa_lo) & (sp < committed), np.float16(0.0), NEG_INF_F16)
+    for i in range(g.q_len):
+        m[i, g.cap: g.cap + i + 1] = np.float16(0.0)
+    return m
+
+
 class RingStep:
     """One sequence's ring state, driven step by step (test harness helper).
 
@@ -317,3 +349,6 @@ class RingStep:
 
     def mask(self) -> np.ndarray:
         return mask_full(self.g, self.slots.slot_pos, self.committed)
+
+    def mask_swa(self, swa_window: int) -> np.ndarray:
+        return mask_swa(self.g, self.slots.slot_pos, self.committed, swa_window)

@@ -267,8 +267,12 @@ def pin_attention_gqa_map():
         assert np.allclose(out[:, h], h // (nh // hk) + 1, atol=1e-13), h
 
 
-def _brute_attend(rows_k, rows_v, positions, committed, cap, q, kn, vn, nh, hk, d, base):
-    """Pure-Python loops: RoPE, scores, softmax, weighted sum (tiny inputs only)."""
+def _brute_attend(rows_k, rows_v, positions, committed, cap, q, kn, vn, nh, hk, d, base,
+                  swa=None):
+    """Pure-Python loops: RoPE, scores, softmax, weighted sum (tiny inputs only).
+
+    With ``swa`` (page 1 section 1.4, sliding-window layers) the window is the
+    last min(swa, committed, cap) positions and query i sees noise j <= i."""
     def rot(vec, p):
         out = list(vec)
         for i in range(d // 2):
@@ -277,7 +281,7 @@ def _brute_attend(rows_k, rows_v, positions, committed, cap, q, kn, vn, nh, hk, 
             out[i] = a * math.cos(th) - b * math.sin(th)
             out[i + d // 2] = b * math.cos(th) + a * math.sin(th)
         return out
-    lo = committed - min(committed, cap)
+    lo = committed - min(committed, cap, swa if swa is not None else cap)
     keys, vals = [], []
     for p in range(lo, committed):
         j = positions.index(p)
@@ -299,12 +303,15 @@ def _brute_attend(rows_k, rows_v, positions, committed, cap, q, kn, vn, nh, hk, 
         for h in range(nh):
             g = h // grp
             qr = rot([float(t) for t in q[i][h]], committed + i)
-            sc = [sum(qr[e] * kk[g * d + e] for e in range(d)) / math.sqrt(d) for kk in keys]
+            n_ctx = len(keys) - q_len
+            use = [j for j in range(len(keys))
+                   if swa is None or j < n_ctx or j - n_ctx <= i]
+            sc = [sum(qr[e] * keys[j][g * d + e] for e in range(d)) / math.sqrt(d) for j in use]
             mx = max(sc)
             w = [math.exp(s - mx) for s in sc]
             tot = sum(w)
             for e in range(d):
-                out[i][h][e] = sum(w[j] * vals[j][g * d + e] for j in range(len(w))) / tot
+                out[i][h][e] = sum(w[t] * vals[j][g * d + e] for t, j in enumerate(use)) / tot
     return np.array(out)
 
 
@@ -376,6 +383,137 @@ def pin_attention_ring_equals_full():
             assert np.abs(ring - full).max() < 1e-12, (cap, step)
 
 
+def pin_swa_brute_force():
+    """Sliding-window layers (page 1 section 1.4, mask_swa) against pure loops."""
+    d, hk, nh, cap, q_len, base = 4, 2, 4, 6, 3, 1e4
+    for swa in (1, 2, 5, 9):
+        rs = np.random.default_rng(60 + swa)
+        rnd = random.Random(60 + swa)
+        st = ro.RingStep(ro.geometry(cap, q_len, d, hk), 1, hk, d, base)
+        all_k, all_v, positions = [], [], []
+        c = 0
+        for step in range(7):
+            c += rnd.choice([1, 2, 3, 7])
+            p = st.plan(c)
+            k = rs.normal(size=(p.n_new, hk * d)).astype(np.float16)
+            v = rs.normal(size=(p.n_new, hk * d)).astype(np.float16)
+            st.commit(p, [k], [v])
+            for j, pos in enumerate(range(p.start, c)):
+                all_k.append(k[j]); all_v.append(v[j]); positions.append(pos)
+            q = rs.normal(size=(q_len, nh, d)).astype(np.float16)
+            kn = rs.normal(size=(q_len, hk * d)).astype(np.float16)
+            vn = rs.normal(size=(q_len, hk * d)).astype(np.float16)
+            got = ro.attend(st.caches[0], c, cap, q, kn, vn, nh, swa_window=swa)
+            want = _brute_attend(all_k, all_v, positions, c, cap, q, kn, vn, nh, hk, d, base,
+                                 swa=swa)
+            assert np.abs(got - want).max() < 1e-12, (swa, step, np.abs(got - want).max())
+
+
+def pin_swa_ring_equals_window():
+    """Section 1.7 for sliding-window layers: masked attention over every ring
+    slot with the SWA mask equals the full cache restricted to the last
+    min(swa, win) positions with a causal noise block (rewinds included)."""
+    d, hk, nh, base = 8, 2, 4, 1e6
+    rs = np.random.default_rng(61)
+    rnd = random.Random(61)
+    for cap, swa in ((3, 2), (8, 5), (13, 13), (13, 40)):
+        q_len = 3
+        geo = ro.geometry(cap, q_len, d, hk)
+        st = ro.RingStep(geo, 1, hk, d, base)
+        c = 0
+        for step in range(25):
+            c = max(0, c + rnd.choice([1, 2, 4, cap, -2, 3 * cap]))
+            p = st.plan(c)
+            st.commit(p, [rs.normal(size=(p.n_new, hk * d)).astype(np.float16)],
+                      [rs.normal(size=(p.n_new, hk * d)).astype(np.float16)])
+            q = rs.normal(size=(q_len, nh, d)).astype(np.float16)
+            kn = rs.normal(size=(q_len, hk * d)).astype(np.float16)
+            vn = rs.normal(size=(q_len, hk * d)).astype(np.float16)
+            want = ro.attend(st.caches[0], c, cap, q, kn, vn, nh, swa_window=swa)
+            K = np.zeros((geo.kv_total, hk * d)); V = np.zeros((geo.kv_total, hk * d))
+            for s_ in range(cap):
+                sp = int(st.slots.slot_pos[s_])
+                if 0 <= sp < c:
+                    K[s_], V[s_] = st.caches[0].row(sp)
+            pq = ro.noise_positions(c, q_len)
+            K[cap:cap + q_len] = ro.rope_rows_f16(kn, pq, hk, d, base)
+            V[cap:cap + q_len] = vn
+            bias = st.mask_swa(swa).astype(np.float64)
+            qr = ro.rope(q, pq, base)
+            ring = np.empty_like(want)
+            for h in range(nh):
+                g = h // (nh // hk)
+                s_ = qr[:, h] @ K[:, g * d:(g + 1) * d].T / math.sqrt(d) + bias
+                w = np.exp(s_ - s_.max(1, keepdims=True))
+                ring[:, h] = (w @ V[:, g * d:(g + 1) * d]) / w.sum(1, keepdims=True)
+            assert np.abs(ring - want).max() < 1e-12, (cap, swa, step)
+
+
+def pin_swa_invariants():
+    """Properties that fix the sliding-window form: the output of noise row i
+    does not depend on noise rows j > i nor on positions before the window;
+    it does depend on the oldest position inside it; a window of at least
+    cap with one noise row is the full-attention result."""
+    d, hk, nh, cap, q_len, base = 8, 2, 4, 16, 4, 1e6
+    rs = np.random.default_rng(62)
+    n = 40
+    k = rs.normal(size=(n, hk * d)).astype(np.float16)
+    v = rs.normal(size=(n, hk * d)).astype(np.float16)
+    q = rs.normal(size=(q_len, nh, d)).astype(np.float16)
+    kn = rs.normal(size=(q_len, hk * d)).astype(np.float16)
+    vn = rs.normal(size=(q_len, hk * d)).astype(np.float16)
+
+    def run(kk, vv, knn, vnn, swa, ql=q_len):
+        c = ro.FullCache(hk * d, hk, d, base)
+        c.store(np.arange(n), kk, vv)
+        return ro.attend(c, n, cap, q[:ql], knn[:ql], vnn[:ql], nh, swa_window=swa)
+
+    swa = 5
+    base_out = run(k, v, kn, vn, swa)
+    for i in range(q_len - 1):
+        kn2, vn2 = kn.copy(), vn.copy()
+        kn2[i + 1:] = rs.normal(size=kn2[i + 1:].shape).astype(np.float16)
+        vn2[i + 1:] = rs.normal(size=vn2[i + 1:].shape).astype(np.float16)
+        out = run(k, v, kn2, vn2, swa)
+        assert np.array_equal(out[: i + 1], base_out[: i + 1]), i
+        assert not np.allclose(out[i + 1:], base_out[i + 1:]), i
+    k2, v2 = k.copy(), v.copy()
+    k2[: n - swa] = 0; v2[: n - swa] = 7
+    assert np.array_equal(run(k2, v2, kn, vn, swa), base_out)
+    k3, v3 = k.copy(), v.copy()
+    v3[n - swa] = 7
+    assert not np.allclose(run(k3, v3, kn, vn, swa), base_out)
+    c = ro.FullCache(hk * d, hk, d, base)
+    c.store(np.arange(n), k, v)
+    full = ro.attend(c, n, cap, q[:1], kn[:1], vn[:1], nh)
+    assert np.array_equal(run(k, v, kn, vn, cap, ql=1), full)
+    assert np.array_equal(run(k, v, kn, vn, 10 * cap, ql=1), full)
+
+
+def pin_swa_mask_closed_form():
+    """mask_swa on monotone streams: ring slot s is visible iff it holds one
+    of the last min(swa, committed, cap) positions; noise row i sees noise
+    slots cap..cap+i; trash and alignment pad rows never."""
+    rnd = random.Random(63)
+    for cap, q_len, swa in ((5, 2, 3), (64, 8, 20), (40, 8, 100), (33, 4, 1)):
+        g = ro.geometry(cap, q_len, 4, 1)
+        for stream in (_monotone_stream(rnd, cap, 30), [0, 1, cap - 1, cap, cap + 1, 5 * cap + 3]):
+            st = ro.RingStep(g, 1, 1, 4, 1e6)
+            for c in stream:
+                p = st.plan(c)
+                st.commit(p, [np.zeros((p.n_new, g.kv_row), np.float16)],
+                          [np.zeros((p.n_new, g.kv_row), np.float16)])
+                m = st.mask_swa(swa).view(np.uint16)
+                lo = c - min(swa, c, cap)
+                vis = {pos % cap for pos in range(lo, c)}
+                for i in range(q_len):
+                    row = m[i]
+                    assert {int(s_) for s_ in np.flatnonzero(row[:cap] == 0)} == vis, (cap, c, i)
+                    assert (row[:cap][row[:cap] != 0] == 0xFC00).all()
+                    assert list(row[cap: cap + q_len]) == [0] * (i + 1) + [0xFC00] * (q_len - i - 1)
+                    assert (row[cap + q_len:] == 0xFC00).all()
+
+
 def pin_attention_fp32_mode():
     d, hk, nh, cap, q_len = 128, 8, 32, 64, 8
     rs = np.random.default_rng(9)
@@ -398,5 +536,7 @@ ALL_PINS = [
     pin_rope_closed_forms, pin_rope_relative,
     pin_attention_single_key, pin_attention_uniform, pin_attention_two_keys,
     pin_attention_gqa_map, pin_attention_brute_force,
+    pin_swa_brute_force, pin_swa_ring_equals_window, pin_swa_invariants,
+    pin_swa_mask_closed_form,
     pin_attention_ring_equals_full, pin_attention_fp32_mode,
 ]

@@ -50,6 +50,19 @@ MUTATIONS = [
      "self.slot_pos[(pos + 1) % self.g.cap] = pos"),
     ("noise_positions", "committed + np.arange(q_len, dtype=np.int64)",
      "committed + 1 + np.arange(q_len, dtype=np.int64)"),
+    # sliding-window layers (page 1 section 1.4, mask_swa)
+    ("attend", "win = min(swa_window, win)", "win = min(swa_window, cap)"),
+    ("attend", "win = min(swa_window, win)", "win = min(swa_window + 1, win)"),
+    ("attend", "bias[:, n_ctx:] = np.where(later, -np.inf, 0.0)", "bias[:, n_ctx:] = 0.0"),
+    ("attend", "later = np.arange(q_len)[None, :] > np.arange(q_len)[:, None]",
+     "later = np.arange(q_len)[None, :] < np.arange(q_len)[:, None]"),
+    ("mask_swa", "(sp >= swa_lo) & (sp < committed)", "(sp > swa_lo) & (sp < committed)"),
+    ("mask_swa", "eff_win = min(swa_window, min(committed, g.cap))",
+     "eff_win = min(swa_window - 1, min(committed, g.cap))"),
+    ("mask_swa", "m[i, g.cap: g.cap + i + 1] = np.float16(0.0)",
+     "m[i, g.cap: g.cap + i] = np.float16(0.0)"),
+    ("mask_swa", "m[i, g.cap: g.cap + i + 1] = np.float16(0.0)",
+     "m[i, g.cap: g.cap + g.q_len] = np.float16(0.0)"),
 ]
 
 
