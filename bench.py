@@ -126,7 +126,8 @@ def prepare(w, pool: int, total: int, dev):
         raise SystemExit(f"need {n_dec} decode steps per ring, stream has {len(streams[0]) - n_warm}")
     rings = [R.Ring(cap=w.cap, q_len=w.q_len, n_head=w.n_head, n_head_kv=w.n_head_kv,
                     head_dim=w.head_dim, n_layer=w.n_layer, n_seq=w.n_seq,
-                    rope_base=w.rope_base, device=dev) for _ in range(pool)]
+                    rope_base=w.rope_base, device=dev, swa_window=w.swa_window,
+                    swa_layers=w.swa_layers) for _ in range(pool)]
     s = torch.cuda.current_stream(dev).cuda_stream
 
     def rows(seq, lo, hi):
@@ -416,10 +417,18 @@ def main() -> int:
     # algorithmic bytes of one attention launch, averaged over the profiled
     # segment (every sequence's visible window at its step)
     seg = committed[args.warmup + args.steps: total]
-    per_launch = np.mean([sum(algorithmic_bytes(w, min(c, w.cap), geo.kv_total)["attn_kernel"]
-                              for c in cs) for cs in seg])
-    per_call = np.mean([sum(algorithmic_bytes(w, min(c, w.cap), geo.kv_total)["ring_attn"]
-                            for c in cs) for cs in seg])
+
+    def layer_window(c, layer):
+        win = min(c, w.cap)
+        return min(w.swa_window, win) if (w.swa_layers >> layer) & 1 else win
+
+    def mean_bytes(kind):
+        # one launch per (step, layer); each covers every sequence
+        return np.mean([sum(algorithmic_bytes(w, layer_window(c, layer), geo.kv_total)[kind]
+                            for c in cs) for cs in seg for layer in range(w.n_layer)])
+
+    per_launch = mean_bytes("attn_kernel")
+    per_call = mean_bytes("ring_attn")
     attn_us = prof["k_ring_attn"]["avg_us"]
     merge_us = prof["k_ring_merge"]["avg_us"] or 0.0
     achieved = per_launch / (attn_us * 1e-6) / 1e9

@@ -23,6 +23,7 @@ struct StepArgs {
   uint16_t* vring;
   int32_t* slot_pos;         // [cap]
   uint16_t* mask;            // [q_len][kv_total]
+  uint16_t* mask_swa;        // [q_len][kv_total] sliding-window mask, or nullptr
   double* rope_noise;        // [q_len][64][2] (cos, sin) at committed + i
   float* rope_q;             // [q_len][64][2] the same values rounded to fp32
   const double* inv_freq;    // [64] theta_i
@@ -30,6 +31,7 @@ struct StepArgs {
   int32_t start_mod;         // start % cap
   int64_t committed;
   int64_t lo;
+  int64_t swa_lo;            // committed - min(swa_window, win)
   int32_t n_new;             // rows per layer in k_new / v_new
   int32_t row0;              // first new row this launch appends
   int32_t n_rows;            // real rows this launch appends
@@ -56,7 +58,11 @@ struct AttnArgs {
   int64_t head_stride;       // halves between KV heads (n_tiles * 4096)
   int32_t n_seq, n_head, n_head_kv, group, q_len, m, cap, kv_total, n_tiles;
   int32_t n_split;
-  int32_t win[RING_MAX_SEQ_INTERNAL];
+  int32_t ring_tiles;        // tiles holding ring slots: ceil(cap / 32)
+  // Visible ring tiles of each sequence: vis_count tiles from vis_first on,
+  // circularly modulo ring_tiles (the window's slots, slot = position % cap).
+  int32_t vis_first[RING_MAX_SEQ_INTERNAL];
+  int32_t vis_count[RING_MAX_SEQ_INTERNAL];
 };
 
 struct MergeArgs {

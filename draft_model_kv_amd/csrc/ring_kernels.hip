@@ -154,7 +154,7 @@ __global__ __launch_bounds__(256) void k_ring_step(StepArgs a) {
   }
   const int s = mblk * 256 + t;
   if (s >= a.kv_total) return;
-  bool vis;
+  bool vis, vis_swa = false;
   if (s < a.cap) {
     int64_t sp = a.slot_pos[s];
     int d = s - a.start_mod;  // offset of slot s from the first new slot, mod cap
@@ -164,11 +164,20 @@ __global__ __launch_bounds__(256) void k_ring_step(StepArgs a) {
       a.slot_pos[s] = (int32_t)sp;
     }
     vis = sp >= a.lo && sp < a.committed;
+    vis_swa = sp >= a.swa_lo && sp < a.committed;
   } else {
     vis = s < a.cap + a.q_len;  // noise slots: visible to every noise row
   }
   const uint16_t mv = vis ? 0x0000u : 0xFC00u;
   for (int i = 0; i < a.q_len; ++i) a.mask[(int64_t)i * a.kv_total + s] = mv;
+  if (a.mask_swa) {
+    // sliding-window layers: the window above; noise slot cap + j visible to
+    // noise rows i >= j only
+    for (int i = 0; i < a.q_len; ++i) {
+      const bool v = s < a.cap ? vis_swa : (s - a.cap <= i);
+      a.mask_swa[(int64_t)i * a.kv_total + s] = v ? 0x0000u : 0xFC00u;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -424,9 +433,9 @@ __device__ __forceinline__ void attend_noise_row(
 }
 
 template <int MB, int NW>
-__device__ __forceinline__ void attn_body(const AttnArgs& a, int unit, int split, int win,
-                                          unsigned char* lds, float (*sm_m)[MB * 32],
-                                          float (*sm_l)[MB * 32]) {
+__device__ __forceinline__ void attn_body(const AttnArgs& a, int unit, int split, int vis_first,
+                                          int vis_count, unsigned char* lds,
+                                          float (*sm_m)[MB * 32], float (*sm_l)[MB * 32]) {
   using S = AttnShape<MB, NW>;
   constexpr int MP = S::MP, NT = S::NT;
   const int lane = threadIdx.x & 63;
@@ -439,9 +448,14 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int unit, int split
   const float* ropeq = a.rope_q + (int64_t)seq * a.q_len * 128;
   const uint16_t* mask_seq = a.mask + (int64_t)seq * a.q_len * a.kv_total;
 
-  // Ring tiles of this split: the visible ring slots are [0, win).
-  const int nvt = (win + kTile - 1) / kTile;
+  // Ring tiles of this split: logical tiles [t0, t1) of the vis_count
+  // visible ones; logical tile k is ring tile (vis_first + k) mod ring_tiles.
+  const int nvt = vis_count;
   const int per = (nvt + a.n_split - 1) / a.n_split;
+  auto ring_tile = [&](int k) {
+    const int t = vis_first + k;
+    return t >= a.ring_tiles ? t - a.ring_tiles : t;
+  };
   const int t0 = min(nvt, split * per);
   const int t1 = min(nvt, t0 + per);
   uint16_t* kh = a.kring + seq * a.seq_stride + a.layer_offset + g * a.head_stride;
@@ -510,7 +524,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int unit, int split
   const int tile_last = max(t1 - 1, 0);
   half8 kc[8], vc[8];
   uint32_t mw[MB][8];
-  load_tile(min(tile, tile_last), kc, vc, mw);
+  load_tile(ring_tile(min(tile, tile_last)), kc, vc, mw);
 
   // ---- 2. queries: rotate at committed + i, scale by log2(e)/sqrt(d),
   //      split into hi + lo F16 (fragment order [mb][hi/lo][chunk][lane]);
@@ -596,8 +610,9 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int unit, int split
       // The last prefetch re-reads the current tile (already in cache).
       half8 kn[8], vn[8];
       uint32_t mn[MB][8];
-      load_tile(next < t1 ? next : tile, kn, vn, mn);
-      attend_tile<MB>(kc, vc, mw, a.cap - tile * kTile, hl, qf, q_lds, lane, m_run, l_run, o);
+      load_tile(ring_tile(next < t1 ? next : tile), kn, vn, mn);
+      attend_tile<MB>(kc, vc, mw, a.cap - ring_tile(tile) * kTile, hl, qf, q_lds, lane, m_run,
+                      l_run, o);
 #pragma unroll
       for (int c = 0; c < 8; ++c) { kc[c] = kn[c]; vc[c] = vn[c]; }
 #pragma unroll
@@ -605,8 +620,9 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int unit, int split
 #pragma unroll
         for (int j = 0; j < 8; ++j) mw[mb][j] = mn[mb][j];
     } else {
-      attend_tile<MB>(kc, vc, mw, a.cap - tile * kTile, hl, qf, q_lds, lane, m_run, l_run, o);
-      if (next < t1) load_tile(next, kc, vc, mw);
+      attend_tile<MB>(kc, vc, mw, a.cap - ring_tile(tile) * kTile, hl, qf, q_lds, lane, m_run,
+                      l_run, o);
+      if (next < t1) load_tile(ring_tile(next), kc, vc, mw);
     }
     tile = next;
   }
@@ -722,15 +738,17 @@ __global__ __launch_bounds__(NW * 64) void k_ring_attn(AttnArgs a) {
   // Every argument the body reads is fetched here in one batch: left to
   // itself the compiler loads each field where it is first used, and each
   // uniform branch in between then costs a full memory round trip before the
-  // first ring load can issue.  win[] comes in as one lane-indexed vector
-  // load and is picked by sequence below.
-  const int winv = a.win[threadIdx.x & 63];
+  // first ring load can issue.  vis_first[] and vis_count[] come in as one
+  // lane-indexed vector load each and are picked by sequence below.
+  const int firstv = a.vis_first[threadIdx.x & 63];
+  const int countv = a.vis_count[threadIdx.x & 63];
   asm volatile("" ::"s"(a.kring), "s"(a.vring), "s"(a.mask), "s"(a.rope_noise), "s"(a.rope_q),
                "s"(a.q),
                "s"(a.k_noise), "s"(a.v_noise), "s"(a.out), "s"(a.part_acc), "s"(a.part_ml),
                "s"(a.seq_stride), "s"(a.layer_offset), "s"(a.head_stride), "s"(a.n_seq),
                "s"(a.n_head), "s"(a.n_head_kv), "s"(a.group), "s"(a.q_len), "s"(a.m),
-               "s"(a.cap), "s"(a.kv_total), "s"(a.n_split), "v"(winv));
+               "s"(a.cap), "s"(a.kv_total), "s"(a.n_split), "s"(a.ring_tiles), "v"(firstv),
+               "v"(countv));
   const int n_units = a.n_seq * a.n_head_kv;
   int unit, split;
   if ((n_units & 7) == 0) {
@@ -741,8 +759,9 @@ __global__ __launch_bounds__(NW * 64) void k_ring_attn(AttnArgs a) {
     unit = blockIdx.x / a.n_split;
     split = blockIdx.x % a.n_split;
   }
-  const int win = __builtin_amdgcn_readlane(winv, unit / a.n_head_kv);
-  attn_body<MB, NW>(a, unit, split, win, lds, sm_m, sm_l);
+  const int seq = unit / a.n_head_kv;
+  attn_body<MB, NW>(a, unit, split, __builtin_amdgcn_readlane(firstv, seq),
+                    __builtin_amdgcn_readlane(countv, seq), lds, sm_m, sm_l);
 }
 
 // ---------------------------------------------------------------------------

@@ -44,8 +44,8 @@ int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 struct Layout {
   int32_t n_tiles = 0, m = 0, mpad = 0, group = 0, n_split = 1;
   int64_t seq_stride = 0;  // halves per sequence in the K (or V) ring
-  size_t off_k = 0, off_v = 0, off_slot = 0, off_mask = 0, off_rope = 0, off_ropeq = 0,
-         off_freq = 0;
+  size_t off_k = 0, off_v = 0, off_slot = 0, off_mask = 0, off_mask_swa = 0, off_rope = 0,
+         off_ropeq = 0, off_freq = 0;
   size_t off_pacc = 0, off_pml = 0, total = 0;
 };
 
@@ -84,6 +84,11 @@ int validate(const ring_config* c) {
     return fail(RING_EINVAL, "n_seq %d out of [1, %d]", c->n_seq, RING_MAX_SEQ);
   if (!(c->rope_base > 1.0f) || !std::isfinite(c->rope_base))
     return fail(RING_EINVAL, "rope_base must be finite and > 1");
+  if (c->swa_window < 0) return fail(RING_EINVAL, "swa_window %d < 0", c->swa_window);
+  if ((c->swa_window == 0) != (c->swa_layers == 0))
+    return fail(RING_EINVAL, "swa_window and swa_layers must both be zero or both non-zero");
+  if (c->n_layer < 64 && (c->swa_layers >> c->n_layer) != 0)
+    return fail(RING_EINVAL, "swa_layers names a layer >= n_layer %d", c->n_layer);
   return RING_OK;
 }
 
@@ -111,6 +116,7 @@ void geometry_of(const ring_config& c, ring_geometry* g, Layout* L) {
   L->off_v = take(ring_bytes);
   L->off_slot = take((size_t)c.n_seq * c.cap * 4);
   L->off_mask = take((size_t)c.n_seq * c.q_len * g->kv_total * 2);
+  L->off_mask_swa = take(c.swa_window > 0 ? (size_t)c.n_seq * c.q_len * g->kv_total * 2 : 0);
   L->off_rope = take((size_t)c.n_seq * c.q_len * 64 * 2 * 8);
   L->off_ropeq = take((size_t)c.n_seq * c.q_len * 64 * 2 * 4);
   L->off_freq = take(64 * 8);
@@ -153,6 +159,7 @@ struct ring {
   uint16_t* vring = nullptr;
   int32_t* slot_pos = nullptr;
   uint16_t* mask = nullptr;
+  uint16_t* mask_swa = nullptr;  // sliding-window layers' mask, or nullptr
   double* rope_noise = nullptr;
   float* rope_q = nullptr;
   double* inv_freq = nullptr;
@@ -183,6 +190,7 @@ StepArgs step_args(ring* r, int32_t seq) {
   a.vring = r->vring + seq * r->L.seq_stride;
   a.slot_pos = r->slot_pos + (int64_t)seq * r->cfg.cap;
   a.mask = r->mask + (int64_t)seq * r->cfg.q_len * r->geo.kv_total;
+  a.mask_swa = r->mask_swa ? r->mask_swa + (int64_t)seq * r->cfg.q_len * r->geo.kv_total : nullptr;
   a.rope_noise = r->rope_noise + (int64_t)seq * r->cfg.q_len * 128;
   a.rope_q = r->rope_q + (int64_t)seq * r->cfg.q_len * 128;
   a.inv_freq = r->inv_freq;
@@ -272,6 +280,7 @@ int ring_init(const ring_config* cfg, void* workspace, size_t workspace_bytes, v
   r->slot_pos = reinterpret_cast<int32_t*>(r->ws + r->L.off_slot);
   r->mask = reinterpret_cast<uint16_t*>(r->ws + r->L.off_mask);
   r->rope_noise = reinterpret_cast<double*>(r->ws + r->L.off_rope);
+  if (cfg->swa_window > 0) r->mask_swa = reinterpret_cast<uint16_t*>(r->ws + r->L.off_mask_swa);
   r->rope_q = reinterpret_cast<float*>(r->ws + r->L.off_ropeq);
   r->inv_freq = reinterpret_cast<double*>(r->ws + r->L.off_freq);
   r->part_acc = reinterpret_cast<float*>(r->ws + r->L.off_pacc);
@@ -376,6 +385,7 @@ int ring_begin_step(ring_t* r, int32_t seq, int64_t committed, const void* k_new
   a.start_mod = (int32_t)(p.start % r->cfg.cap);
   a.committed = committed;
   a.lo = p.lo;
+  a.swa_lo = committed - std::min<int64_t>(r->cfg.swa_window, p.win);
   a.n_new = (int32_t)p.n_new;
   if (p.bulk) {
     for (int64_t row0 = 0; row0 < p.n_new; row0 += kBulkChunk) {
@@ -439,8 +449,32 @@ int ring_attn(ring_t* r, int32_t layer, const void* q, const void* k_noise, cons
   a.kv_total = r->geo.kv_total;
   a.n_tiles = r->L.n_tiles;
   a.n_split = r->L.n_split;
-  for (int i = 0; i < r->cfg.n_seq; ++i)
-    a.win[i] = (int32_t)std::min<int64_t>(r->committed[i], r->cfg.cap);
+  const int64_t cap = r->cfg.cap;
+  const int32_t ring_tiles = (int32_t)((cap + kTile - 1) / kTile);
+  a.ring_tiles = ring_tiles;
+  const bool swa = layer < 64 && ((r->cfg.swa_layers >> layer) & 1u);
+  if (swa) a.mask = r->mask_swa;
+  for (int i = 0; i < r->cfg.n_seq; ++i) {
+    // Visible positions [committed - w, committed) sit in slots from
+    // (committed - w) % cap on, circularly: w = win for full layers,
+    // min(swa_window, win) for sliding-window layers.
+    const int64_t c = r->committed[i];
+    const int64_t win = std::min<int64_t>(c, cap);
+    const int64_t w = swa ? std::min<int64_t>(r->cfg.swa_window, win) : win;
+    int32_t first = 0, count = 0;
+    if (w > 0 && w < win) {
+      const int64_t s0 = (c - w) % cap, s1 = s0 + w;  // slot range [s0, s1), s1 may pass cap
+      first = (int32_t)(s0 / kTile);
+      const int64_t end_tile = (std::min<int64_t>(s1, cap) + kTile - 1) / kTile;
+      count = (int32_t)(end_tile - first);
+      if (s1 > cap) count += (int32_t)((s1 - cap + kTile - 1) / kTile);
+      if (count > ring_tiles) first = 0, count = ring_tiles;
+    } else if (w > 0) {
+      count = (int32_t)((win + kTile - 1) / kTile);  // slots [0, win)
+    }
+    a.vis_first[i] = first;
+    a.vis_count[i] = count;
+  }
   hipEvent_t t0, t1;
   next_events(r, RING_KERNEL_ATTN, &t0, &t1);
   if (int e = check_launch(launch_attn(a, s, t0, t1), "ring_attn")) return e;
@@ -485,11 +519,14 @@ const char* ring_last_error(void) { return g_err.c_str(); }
 int ring_describe(const ring_t* r, char* buf, size_t len) {
   if (!r || !buf || len == 0) return fail(RING_EINVAL, "NULL argument");
   const double mib = (double)r->cfg.n_layer * r->geo.kv_bytes_per_layer / (1024.0 * 1024.0);
-  snprintf(buf, len,
-           "[draft-kv] ring: cap=%d kv_total=%d a_step=%d layers=%d seqs=%d f16 cache %.1f MiB "
-           "per seq, splits=%d",
-           r->cfg.cap, r->geo.kv_total, r->geo.a_step, r->cfg.n_layer, r->cfg.n_seq, mib,
-           r->L.n_split);
+  const int n = snprintf(buf, len,
+                         "[draft-kv] ring: cap=%d kv_total=%d a_step=%d layers=%d seqs=%d f16 cache "
+                         "%.1f MiB per seq, splits=%d",
+                         r->cfg.cap, r->geo.kv_total, r->geo.a_step, r->cfg.n_layer, r->cfg.n_seq,
+                         mib, r->L.n_split);
+  if (r->cfg.swa_window > 0 && n > 0 && (size_t)n < len)
+    snprintf(buf + n, len - n, ", swa_window=%d swa_layers=0x%llx", r->cfg.swa_window,
+             (unsigned long long)r->cfg.swa_layers);
   return ok();
 }
 
@@ -511,6 +548,18 @@ int ring_read_mask(const ring_t* r, int32_t seq, uint16_t* host_out) {
   if (hipDeviceSynchronize() != hipSuccess) return fail(RING_EDEVICE, "device synchronisation failed");
   const size_t n = (size_t)r->cfg.q_len * r->geo.kv_total;
   if (hipMemcpy(host_out, r->mask + (int64_t)seq * n, n * 2, hipMemcpyDeviceToHost) != hipSuccess)
+    return fail(RING_EDEVICE, "hipMemcpy failed");
+  return ok();
+}
+
+int ring_read_mask_swa(const ring_t* r, int32_t seq, uint16_t* host_out) {
+  if (!r || !host_out) return fail(RING_EINVAL, "NULL argument");
+  if (seq < 0 || seq >= r->cfg.n_seq) return fail(RING_ERANGE, "seq %d out of range", seq);
+  if (!r->mask_swa) return fail(RING_ESTATE, "the ring has no sliding-window layers");
+  if (int e = use_device(r)) return e;
+  if (hipDeviceSynchronize() != hipSuccess) return fail(RING_EDEVICE, "device synchronisation failed");
+  const size_t n = (size_t)r->cfg.q_len * r->geo.kv_total;
+  if (hipMemcpy(host_out, r->mask_swa + (int64_t)seq * n, n * 2, hipMemcpyDeviceToHost) != hipSuccess)
     return fail(RING_EDEVICE, "hipMemcpy failed");
   return ok();
 }

@@ -31,7 +31,8 @@ RING_MAX_SEQ = 64
 EXPORTS = (
     "ring_query_geometry", "ring_init", "ring_plan_step", "ring_plan_from_state",
     "ring_begin_step", "ring_attn", "ring_free", "ring_last_error", "ring_describe",
-    "ring_read_slot_pos", "ring_read_mask", "ring_read_rows", "ring_read_state",
+    "ring_read_slot_pos", "ring_read_mask", "ring_read_mask_swa", "ring_read_rows",
+    "ring_read_state",
     "ring_profile_enable", "ring_profile_read",
 )
 RING_KERNEL_STEP, RING_KERNEL_ATTN, RING_KERNEL_MERGE = 0, 1, 2
@@ -41,7 +42,8 @@ class RingConfig(ctypes.Structure):
     _fields_ = [("cap", ctypes.c_int32), ("q_len", ctypes.c_int32),
                 ("n_head", ctypes.c_int32), ("n_head_kv", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("n_layer", ctypes.c_int32),
-                ("n_seq", ctypes.c_int32), ("rope_base", ctypes.c_float)]
+                ("n_seq", ctypes.c_int32), ("rope_base", ctypes.c_float),
+                ("swa_window", ctypes.c_int32), ("swa_layers", ctypes.c_uint64)]
 
 
 class RingGeometry(ctypes.Structure):
@@ -92,6 +94,7 @@ def _load() -> ctypes.CDLL:
         "ring_describe": [P, ctypes.c_char_p, SZ],
         "ring_read_slot_pos": [P, I32, P],
         "ring_read_mask": [P, I32, P],
+        "ring_read_mask_swa": [P, I32, P],
         "ring_read_rows": [P, I32, I32, I32, I32, P, P],
         "ring_read_state": [P, I32, ctypes.POINTER(I64), ctypes.POINTER(I64)],
         "ring_profile_enable": [P, I32],
@@ -117,8 +120,9 @@ def ring_last_error() -> str:
 
 
 def make_config(cap, q_len=8, n_head=32, n_head_kv=8, head_dim=128, n_layer=1,
-                n_seq=1, rope_base=1.0e6) -> RingConfig:
-    return RingConfig(cap, q_len, n_head, n_head_kv, head_dim, n_layer, n_seq, rope_base)
+                n_seq=1, rope_base=1.0e6, swa_window=0, swa_layers=0) -> RingConfig:
+    return RingConfig(cap, q_len, n_head, n_head_kv, head_dim, n_layer, n_seq, rope_base,
+                      swa_window, swa_layers)
 
 
 def ring_query_geometry(cfg: RingConfig) -> RingGeometry:
@@ -190,6 +194,12 @@ def ring_read_mask(handle: int, seq: int, q_len: int, kv_total: int) -> np.ndarr
     return out
 
 
+def ring_read_mask_swa(handle: int, seq: int, q_len: int, kv_total: int) -> np.ndarray:
+    out = np.empty((q_len, kv_total), dtype=np.uint16)
+    _check(_lib.ring_read_mask_swa(handle, seq, out.ctypes.data), "ring_read_mask_swa")
+    return out
+
+
 def ring_read_rows(handle: int, seq: int, layer: int, slot0: int, n: int,
                    kv_row: int) -> Tuple[np.ndarray, np.ndarray]:
     k = np.empty((n, kv_row), dtype=np.uint16)
@@ -226,10 +236,11 @@ class Ring:
     """
 
     def __init__(self, cap, q_len=8, n_head=32, n_head_kv=8, head_dim=128, n_layer=1,
-                 n_seq=1, rope_base=1.0e6, device=None):
+                 n_seq=1, rope_base=1.0e6, device=None, swa_window=0, swa_layers=0):
         import torch
         self._torch = torch
-        self.cfg = make_config(cap, q_len, n_head, n_head_kv, head_dim, n_layer, n_seq, rope_base)
+        self.cfg = make_config(cap, q_len, n_head, n_head_kv, head_dim, n_layer, n_seq, rope_base,
+                               swa_window, swa_layers)
         self.geo = ring_query_geometry(self.cfg)
         self.device = torch.device(device or "cuda")
         self.workspace = torch.empty(self.geo.workspace_bytes + 256, dtype=torch.uint8,
@@ -283,6 +294,9 @@ class Ring:
 
     def mask(self, seq: int) -> np.ndarray:
         return ring_read_mask(self.handle, seq, self.cfg.q_len, self.geo.kv_total)
+
+    def mask_swa(self, seq: int) -> np.ndarray:
+        return ring_read_mask_swa(self.handle, seq, self.cfg.q_len, self.geo.kv_total)
 
     def rows(self, seq: int, layer: int, slot0: int, n: int):
         return ring_read_rows(self.handle, seq, layer, slot0, n, self.geo.kv_row)

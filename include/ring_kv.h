@@ -52,7 +52,15 @@ extern "C" {
  *   head_dim   must be 128
  *   n_layer    draft layers, each with its own K and V ring (>= 1)
  *   n_seq      independent sequences, 1..RING_MAX_SEQ
- *   rope_base  RoPE base (theta_i = rope_base^(-2i/head_dim)), > 1          */
+ *   rope_base  RoPE base (theta_i = rope_base^(-2i/head_dim)), > 1
+ *   swa_window sliding-window layers (page 1 section 1.4, mask_swa): each
+ *              step also builds their mask, whose window is the last
+ *              eff_win = min(swa_window, win) committed positions (anchored
+ *              at committed for every noise row) and whose noise block is
+ *              causal (noise row i sees noise slots j <= i).  0 = no such
+ *              layers; else >= 1, and swa_layers must be non-zero.
+ *   swa_layers bit l set: layer l attends with that mask; only bits below
+ *              min(n_layer, 64) may be set; 0 when swa_window is 0.         */
 typedef struct ring_config {
   int32_t cap;
   int32_t q_len;
@@ -62,6 +70,8 @@ typedef struct ring_config {
   int32_t n_layer;
   int32_t n_seq;
   float rope_base;
+  int32_t swa_window;   /* sliding-window layers' window; 0 = none        */
+  uint64_t swa_layers;  /* bit l set: layer l is a sliding-window layer   */
 } ring_config;
 
 /* Derived geometry (section 1.1 of the page):
@@ -145,7 +155,10 @@ int ring_plan_from_state(const ring_config* cfg, int64_t next_pos, int64_t held_
  * write zeros to trash_slot; slot_pos[p % cap] = p; the F16 mask
  * [q_len][kv_total] of the sequence becomes 0 (0x0000) for ring slots with
  * lo <= slot_pos < committed and for the q_len noise slots, -inf (0xFC00)
- * elsewhere; the RoPE table of the noise positions committed + i is rebuilt.
+ * elsewhere; with sliding-window layers their mask too (0 for ring slots
+ * with committed - eff_win <= slot_pos < committed, noise slot cap + j for
+ * noise rows i >= j); the RoPE table of the noise positions committed + i is
+ * rebuilt.
  * Errors: RING_ERANGE, RING_ESTATE (n_rows != n_new), RING_EINVAL (NULL),
  * RING_EDEVICE.                                                             */
 int ring_begin_step(ring_t* r, int32_t seq, int64_t committed,
@@ -153,7 +166,9 @@ int ring_begin_step(ring_t* r, int32_t seq, int64_t committed,
                     void* stream);
 
 /* Masked GQA attention of the noise block of every sequence over its ring
- * (one draft layer), section 1.4 masks, noise block visible both ways.
+ * (one draft layer), section 1.4 masks: the full mask with the noise block
+ * visible both ways, or for a sliding-window layer its mask, reading only
+ * the ring tiles that hold its window.
  *   q        device F16 [n_seq][q_len][n_head][head_dim], not yet rotated;
  *            query row i sits at absolute position committed + i
  *   k_noise  device F16 [n_seq][q_len][kv_row], noise K, not yet rotated
@@ -185,6 +200,10 @@ int ring_read_slot_pos(const ring_t* r, int32_t seq, int32_t* host_out);
 
 /* Mask of sequence `seq`, F16 bit patterns uint16 [q_len][kv_total].        */
 int ring_read_mask(const ring_t* r, int32_t seq, uint16_t* host_out);
+
+/* Sliding-window mask of sequence `seq` (same layout); RING_ESTATE when the
+ * ring has no sliding-window layers.                                        */
+int ring_read_mask_swa(const ring_t* r, int32_t seq, uint16_t* host_out);
 
 /* Rows [slot0, slot0 + n) of the (seq, layer) ring, converted from the
  * device layout to plain rows: F16 bit patterns [n][kv_row] for K (rotated)

@@ -87,7 +87,8 @@ class Driver:
         try:
             self.ring = Ring(cap=w.cap, q_len=w.q_len, n_head=w.n_head, n_head_kv=w.n_head_kv,
                              head_dim=w.head_dim, n_layer=w.n_layer, n_seq=w.n_seq,
-                             rope_base=w.rope_base, device=self.dev)
+                             rope_base=w.rope_base, device=self.dev,
+                             swa_window=w.swa_window, swa_layers=w.swa_layers)
         finally:
             if n_split is not None:
                 if old is None:
@@ -163,10 +164,14 @@ class Driver:
         self.n_attn += 1
         return out.cpu().numpy(), q, kn, vn
 
+    def is_swa(self, layer: int) -> bool:
+        return bool((self.w.swa_layers >> layer) & 1)
+
     def oracle_attn(self, seq: int, layer: int, q, kn, vn, dtype=np.float32):
         w = self.w
         return ro.attend(self.orc[seq].caches[layer], self.committed[seq], w.cap,
-                         q[seq], kn[seq], vn[seq], w.n_head, dtype=dtype)
+                         q[seq], kn[seq], vn[seq], w.n_head, dtype=dtype,
+                         swa_window=w.swa_window if self.is_swa(layer) else None)
 
     # ------------------------------------------------------------ comparisons
     def check_index(self, seq: int):
@@ -182,6 +187,12 @@ class Driver:
         if not np.array_equal(m, want_m):
             bad = np.argwhere(m != want_m)
             raise AssertionError(f"mask mismatch seq {seq} at {bad[:4].tolist()}")
+        if self.w.swa_window:
+            m = self.ring.mask_swa(seq)
+            want_m = self.orc[seq].mask_swa(self.w.swa_window).view(np.uint16)
+            if not np.array_equal(m, want_m):
+                bad = np.argwhere(m != want_m)
+                raise AssertionError(f"sliding-window mask mismatch seq {seq} at {bad[:4].tolist()}")
 
     def check_rows(self, seq: int, layer: int, max_ulp: int = 1) -> int:
         """Ring rows against the full cache; returns the count of 1-ulp K rows."""

@@ -57,6 +57,8 @@ def test_describe_format_has_the_log_fields():
     dict(cap=0), dict(q_len=0), dict(q_len=33), dict(head_dim=64), dict(n_head=30),
     dict(n_head_kv=0), dict(n_head=128, n_head_kv=8), dict(n_layer=0), dict(n_seq=0),
     dict(n_seq=65), dict(rope_base=1.0), dict(rope_base=float("inf")),
+    dict(swa_window=-1, swa_layers=1), dict(swa_window=16), dict(swa_layers=1),
+    dict(swa_window=16, swa_layers=0b10),
 ])
 def test_invalid_config_rejected(bad):
     kw = dict(cap=64, q_len=8, n_head=32, n_head_kv=8, head_dim=128, n_layer=1, n_seq=1,
@@ -66,6 +68,16 @@ def test_invalid_config_rejected(bad):
         rk.ring_query_geometry(rk.make_config(**kw))
     assert e.value.code == rk.RING_EINVAL
     assert rk.ring_last_error()
+
+
+def test_sliding_window_config_accepted():
+    """A sliding-window layer set below n_layer is valid and adds one mask."""
+    base = rk.ring_query_geometry(rk.make_config(64, n_layer=3))
+    g = rk.ring_query_geometry(rk.make_config(64, n_layer=3, swa_window=16, swa_layers=0b101))
+    assert (g.a_step, g.trash_slot, g.kv_total) == (base.a_step, base.trash_slot, base.kv_total)
+    assert g.workspace_bytes >= base.workspace_bytes + 8 * base.kv_total * 2
+    g = rk.ring_query_geometry(rk.make_config(64, n_layer=70, swa_window=1, swa_layers=1 << 63))
+    assert g.kv_total == base.kv_total
 
 
 def test_planner_state_validation():

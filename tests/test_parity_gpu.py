@@ -118,6 +118,37 @@ def test_multi_seq_multi_layer():
     d.close()
 
 
+@pytest.mark.parametrize("swa,commits", [
+    (5, [61, 69, 70, 77, 150, 151]),        # window wraps the ring end
+    (1, [3, 4, 12, 64, 65]),                # one visible ring slot at most
+    (40, [30, 39, 40, 41, 100, 90, 91]),    # committed below / above the window, rewind
+    (64, [60, 66, 70, 200]),                # window == cap: the full layer's slots
+    (100, [50, 64, 130]),                   # window > cap
+], ids=["wrap", "one", "rewind", "cap", "over_cap"])
+def test_sliding_window_layers(swa, commits):
+    """Page 1 section 1.4, mask_swa: layers 1 and 2 slide, layer 0 is full."""
+    d = Driver(small(cap=64, n_layer=3, swa_window=swa, swa_layers=0b110, seed=107))
+    run_steps(d, commits)
+    d.close()
+
+
+def test_sliding_window_ragged_cap_split_counts():
+    """cap 100 (a partial last ring tile), q_len 3, windows that start and end
+    inside tiles, the window's tiles spread over several splits."""
+    for n_split in (1, 3):
+        d = Driver(small(cap=100, q_len=3, n_head=16, n_head_kv=4, n_layer=2, swa_window=37,
+                         swa_layers=0b10, seed=108), n_split=n_split)
+        run_steps(d, [7, 57, 99, 100, 101, 130, 205, 206, 240, 263])
+        d.close()
+
+
+def test_sliding_window_single_noise_row():
+    """q_len 1: the causal noise block is the single noise row."""
+    d = Driver(small(cap=96, q_len=1, n_layer=2, swa_window=20, swa_layers=0b11, seed=109))
+    run_steps(d, [0, 1, 2, 50, 120, 121])
+    d.close()
+
+
 @pytest.mark.parametrize("n_split", [1, 2, 3, 7])
 def test_split_counts_agree(n_split):
     w = small(cap=512, seed=106)
@@ -240,3 +271,7 @@ def test_batched_seqs_full():
 
 def test_large_window_full():
     _run_workload("large_window", every=32, rows_at=(255,))
+
+
+def test_swa_stream_full():
+    _run_workload("swa_stream", every=40, rows_at=(599,))

@@ -52,6 +52,8 @@ class Workload:
     start_lo: int = 0           # per-seq start drawn from [start_lo, start_hi) when > 0
     start_hi: int = 0
     forced_starts: Tuple[Tuple[int, int, int], ...] = field(default_factory=tuple)
+    swa_window: int = 0         # sliding-window layers' window (0: none)
+    swa_layers: int = 0         # bit l set: layer l is a sliding-window layer
 
     @property
     def kv_row(self) -> int:
@@ -77,6 +79,11 @@ WORKLOADS: Dict[str, Workload] = {
     "large_window": Workload(
         name="large_window", seed=4, cap=32768, n_head=64, sigma=1.0,
         outlier_p=0.01, prefill=131072, n_steps=256),
+    # interleaved full / sliding-window draft layers (layers 1 and 3 slide
+    # over the last 1024 positions); the window wraps the ring end
+    "swa_stream": Workload(
+        name="swa_stream", seed=5, cap=4096, n_layer=4, prefill=4096, n_steps=600,
+        swa_window=1024, swa_layers=0b1010),
 }
 
 
