@@ -43,6 +43,7 @@ int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
 struct Layout {
   int32_t n_tiles = 0, m = 0, mpad = 0, group = 0, n_split = 1;
+  bool n_split_forced = false;
   int64_t seq_stride = 0;  // halves per sequence in the K (or V) ring
   size_t off_k = 0, off_v = 0, off_slot = 0, off_mask = 0, off_mask_swa = 0, off_rope = 0,
          off_ropeq = 0, off_freq = 0;
@@ -53,7 +54,13 @@ constexpr int kMaxSplits = 64;  // each merge wave holds up to 16 splits in regi
 
 // Splits of the ring tiles per (sequence, KV head): enough work-groups to
 // cover the 256 compute units, and at least one 32-slot tile per wave.
-// RING_ATTN_SPLITS (1..64) overrides the choice, for tuning.
+// RING_ATTN_SPLITS (1..64) overrides the choice, for tuning and tests; the
+// override also holds for launches whose windows are narrower.
+bool splits_forced() {
+  const char* env = std::getenv("RING_ATTN_SPLITS");
+  return env && std::atoi(env) >= 1;
+}
+
 int32_t choose_splits(const ring_config& c) {
   const int n_units = c.n_seq * c.n_head_kv;
   const int ring_tiles = (c.cap + kTile - 1) / kTile;
@@ -104,6 +111,7 @@ void geometry_of(const ring_config& c, ring_geometry* g, Layout* L) {
   L->m = c.q_len * L->group;
   L->mpad = L->m <= 32 ? 32 : 64;
   L->n_split = choose_splits(c);
+  L->n_split_forced = splits_forced();
   L->seq_stride = (int64_t)c.n_layer * c.n_head_kv * L->n_tiles * kTileHalves;
   size_t off = 0;
   auto take = [&off](size_t bytes) {
@@ -454,6 +462,7 @@ int ring_attn(ring_t* r, int32_t layer, const void* q, const void* k_noise, cons
   a.ring_tiles = ring_tiles;
   const bool swa = layer < 64 && ((r->cfg.swa_layers >> layer) & 1u);
   if (swa) a.mask = r->mask_swa;
+  int32_t max_count = 0;
   for (int i = 0; i < r->cfg.n_seq; ++i) {
     // Visible positions [committed - w, committed) sit in slots from
     // (committed - w) % cap on, circularly: w = win for full layers,
@@ -474,17 +483,24 @@ int ring_attn(ring_t* r, int32_t layer, const void* q, const void* k_noise, cons
     }
     a.vis_first[i] = first;
     a.vis_count[i] = count;
+    max_count = std::max(max_count, count);
   }
+  // Splits for this launch: as many as give every wave at least one tile of
+  // the widest window, at most the ring's (partial buffers are sized for it).
+  const int32_t n_split = r->L.n_split_forced
+                              ? r->L.n_split
+                              : std::max(1, std::min(r->L.n_split, (max_count + 3) / 4));
+  a.n_split = n_split;
   hipEvent_t t0, t1;
   next_events(r, RING_KERNEL_ATTN, &t0, &t1);
   if (int e = check_launch(launch_attn(a, s, t0, t1), "ring_attn")) return e;
-  if (r->L.n_split > 1) {
+  if (n_split > 1) {
     MergeArgs m{};
     m.part_acc = r->part_acc;
     m.part_ml = r->part_ml;
     m.out = out;
     m.n_units = r->cfg.n_seq * r->cfg.n_head_kv;
-    m.n_split = r->L.n_split;
+    m.n_split = n_split;
     m.n_head = r->cfg.n_head;
     m.n_head_kv = r->cfg.n_head_kv;
     m.group = r->L.group;
