@@ -21,6 +21,16 @@ section 1 ("what the ring does in Luce"):
          masks); memory is 2 * n_layer * kv_row * kv_total * 2 bytes.
 TL;DR of the same page: absolute RoPE positions, K/V computed for new rows only.
 
+K/V rows from features (the page's notes on the port: Luce keeps a mirror
+of the target's features, DraftFeatureMirror, whose capacity is the ring's,
+section 1.6, and begin_step computes the new rows' context K/V from it; the
+test log's list of refuted hypotheses, item 4, spells the per-layer
+computation out as wk/wv @ fused + k_norm + rope, the shallow injection):
+  * the mirror holds the fused feature vector of the last cap positions at
+    slot p % cap;
+  * K = RoPE_p(k_norm(wk @ fused)), V = wv @ fused, k_norm an RMS norm over
+    each KV head's head_dim values times a learned head_dim weight.
+
 What the oracle computes is the plain definition the ring is equal to: a
 non-ring cache holding every committed position, attended over exactly
 [lo, committed) plus the noise block.  Index expectations (slot_pos, mask,
@@ -195,6 +205,14 @@ class FullCache:
         if positions.size == 0:
             return
         k = rope_rows_f16(k_raw, positions, self.n_head_kv, self.head_dim, self.base)
+        self.store_rotated(positions, k, v_raw)
+
+    def store_rotated(self, positions: np.ndarray, k: np.ndarray, v_raw: np.ndarray) -> None:
+        """Store rows whose K is already rotated (and rounded to F16)."""
+        positions = np.asarray(positions, dtype=np.int64)
+        if positions.size == 0:
+            return
+        k = np.asarray(k, dtype=np.float16)
         v = np.asarray(v_raw, dtype=np.float16)
         for b in np.unique(positions // self.BLOCK):
             sel = (positions // self.BLOCK) == b
@@ -277,6 +295,57 @@ def attend(cache: FullCache, committed: int, cap: int, q: np.ndarray,
 
 
 # --------------------------------------------------------------------------
+# New rows' K/V from the fused feature vector, and the feature mirror.
+# --------------------------------------------------------------------------
+RMS_EPS = 1e-6  # epsilon of the per-head RMS norm of K (reading: not on the page)
+
+
+def project_kv(fused: np.ndarray, wk: np.ndarray, wv: np.ndarray, k_norm: np.ndarray,
+               positions: np.ndarray, n_head_kv: int, head_dim: int, base: float,
+               eps: float = RMS_EPS) -> Tuple[np.ndarray, np.ndarray]:
+    """K and V rows of ``positions`` from their fused feature vectors.
+
+    fused [n, d_model] F16; wk, wv [kv_row, d_model] F16 (output dim first);
+    k_norm [head_dim] fp32.  In fp64: k = wk @ f, each KV head's slice scaled
+    to unit RMS (eps added to the mean square) and multiplied by k_norm, then
+    RoPE at the row's position, then one rounding to F16; v = wv @ f rounded
+    to F16.  Returns (K [n, kv_row] F16 rotated, V [n, kv_row] F16).
+    """
+    n = fused.shape[0]
+    f = np.asarray(fused, dtype=np.float64)
+    k = f @ np.asarray(wk, dtype=np.float64).T
+    v = f @ np.asarray(wv, dtype=np.float64).T
+    k = k.reshape(n, n_head_kv, head_dim)
+    rms = np.sqrt((k * k).mean(axis=-1, keepdims=True) + eps)
+    k = k / rms * np.asarray(k_norm, dtype=np.float64)
+    k = rope(k, positions, base).reshape(n, n_head_kv * head_dim)
+    return k.astype(np.float16), v.astype(np.float16)
+
+
+class FeatureMirror:
+    """Fused feature vectors of the last ``cap`` positions, slot p % cap."""
+
+    def __init__(self, cap: int, d_model: int):
+        self.cap = cap
+        self.slots = np.zeros((cap, d_model), np.float16)
+        self.slot_pos = np.full(cap, -1, dtype=np.int64)
+
+    def write(self, positions: np.ndarray, features: np.ndarray) -> None:
+        for j, p in enumerate(np.asarray(positions, dtype=np.int64)):
+            self.slots[p % self.cap] = features[j]
+            self.slot_pos[p % self.cap] = p
+
+    def read(self, positions: np.ndarray) -> np.ndarray:
+        positions = np.asarray(positions, dtype=np.int64)
+        out = np.empty((len(positions), self.slots.shape[1]), np.float16)
+        for j, p in enumerate(positions):
+            if self.slot_pos[p % self.cap] != p:
+                raise KeyError(f"position {p} is not in the mirror")
+            out[j] = self.slots[p % self.cap]
+        return out
+
+
+# --------------------------------------------------------------------------
 # Sections 1.2 and 1.4: what the ring's index state must be.
 # --------------------------------------------------------------------------
 class SlotHistory:
@@ -342,6 +411,22 @@ class RingStep:
         pos = np.arange(p.start, p.committed, dtype=np.int64)
         for layer, cache in enumerate(self.caches):
             cache.store(pos, k_rows[layer], v_rows[layer])
+        self._advance(p)
+
+    def commit_features(self, p: Plan, mirror: FeatureMirror, wk: List[np.ndarray],
+                        wv: List[np.ndarray], k_norm: List[np.ndarray],
+                        eps: float = RMS_EPS) -> None:
+        """Apply a plan whose rows come from the mirror's fused features."""
+        pos = np.arange(p.start, p.committed, dtype=np.int64)
+        if pos.size:
+            f = mirror.read(pos)
+            for layer, cache in enumerate(self.caches):
+                k, v = project_kv(f, wk[layer], wv[layer], k_norm[layer], pos,
+                                  cache.n_head_kv, cache.head_dim, cache.base, eps)
+                cache.store_rotated(pos, k, v)
+        self._advance(p)
+
+    def _advance(self, p: Plan) -> None:
         self.slots.apply(p)
         self.next_pos = p.committed
         self.held_lo = p.lo

@@ -529,6 +529,190 @@ def pin_attention_fp32_mode():
     assert b.dtype == np.float32 and np.abs(a - b).max() < 1e-5
 
 
+# --------------------------------------------------------------------------
+# New rows' K/V from fused features (the shallow injection named in the test
+# log of the ring port page) and the feature mirror
+# --------------------------------------------------------------------------
+def _one_hot(rows, d_model, cols):
+    w = np.zeros((rows, d_model), np.float16)
+    w[np.arange(rows), cols] = 1.0
+    return w
+
+
+def pin_project_v_selects_features():
+    """V = wv f: rows of wv that pick one feature give that feature exactly;
+    a row that adds two features gives their sum rounded once to F16."""
+    rs = np.random.default_rng(21)
+    n, d_model, hk, d = 5, 40, 2, 8
+    f = rs.normal(size=(n, d_model)).astype(np.float16)
+    cols = rs.integers(0, d_model, size=hk * d)
+    wv = _one_hot(hk * d, d_model, cols)
+    wk = (rs.normal(size=(hk * d, d_model)) / 8).astype(np.float16)
+    _, v = ro.project_kv(f, wk, wv, np.ones(d), np.arange(n), hk, d, 1e6)
+    assert v.dtype == np.float16 and np.array_equal(v, f[:, cols])
+    wv2 = wv.copy()
+    wv2[0, (cols[0] + 1) % d_model] = 1.0
+    _, v2 = ro.project_kv(f, wk, wv2, np.ones(d), np.arange(n), hk, d, 1e6)
+    want = (f[:, cols[0]].astype(np.float64) + f[:, (cols[0] + 1) % d_model]).astype(np.float16)
+    assert np.array_equal(v2[:, 0], want) and np.array_equal(v2[:, 1:], v[:, 1:])
+
+
+def pin_project_k_head_rms():
+    """With k_norm = 1 every KV head's K has RMS 1 at any position (RoPE keeps
+    the norm); the norm is per head, so scaling one head's weights changes
+    nothing, and the projection of one head ignores the other's weights."""
+    rs = np.random.default_rng(22)
+    n, d_model, hk, d = 6, 64, 3, 16
+    f = rs.normal(size=(n, d_model)).astype(np.float16)
+    wk = (rs.normal(size=(hk * d, d_model)) / 8).astype(np.float16)
+    wv = (rs.normal(size=(hk * d, d_model)) / 8).astype(np.float16)
+    for pos in (np.arange(n), np.arange(n) + 4093, np.full(n, 131071)):
+        k, _ = ro.project_kv(f, wk, wv, np.ones(d), pos, hk, d, 1e6)
+        rms = np.sqrt((k.astype(np.float64).reshape(n, hk, d) ** 2).mean(-1))
+        assert np.abs(rms - 1.0).max() < 1e-3, rms
+    k0, _ = ro.project_kv(f, wk, wv, np.ones(d), np.arange(n), hk, d, 1e6, eps=0.0)
+    w2 = wk.copy()
+    w2[d:2 * d] *= np.float16(8.0)            # head 1 only, exact power of two
+    w2[2 * d:] = (rs.normal(size=(d, d_model)) / 8).astype(np.float16)  # head 2 changed
+    k1, _ = ro.project_kv(f, w2, wv, np.ones(d), np.arange(n), hk, d, 1e6, eps=0.0)
+    assert np.array_equal(k0[:, :2 * d], k1[:, :2 * d])
+    assert not np.array_equal(k0[:, 2 * d:], k1[:, 2 * d:])
+
+
+def pin_project_k_constant_slice():
+    """A head whose pre-norm slice is the constant c normalises to sign(c)
+    times k_norm: at p = 0 (RoPE is the identity) K is f16(sign(c) k_norm)."""
+    rs = np.random.default_rng(23)
+    n, d_model, hk, d = 4, 12, 2, 8
+    f = rs.normal(size=(n, d_model)).astype(np.float16)
+    f[:, 3] = np.float16(-2.5)
+    f[:, 7] = np.float16(0.75)
+    wk = np.zeros((hk * d, d_model), np.float16)
+    wk[:d, 3] = 1.0      # head 0: every dim reads feature 3
+    wk[d:, 7] = 1.0      # head 1: every dim reads feature 7
+    knorm = rs.uniform(0.25, 3.0, size=d)
+    k, _ = ro.project_kv(f, wk, wk, knorm, np.zeros(n, np.int64), hk, d, 1e6, eps=0.0)
+    assert np.array_equal(k[:, :d], np.broadcast_to((-knorm).astype(np.float16), (n, d)))
+    assert np.array_equal(k[:, d:], np.broadcast_to(knorm.astype(np.float16), (n, d)))
+
+
+def pin_project_k_rope_after_norm():
+    """Normalised K that is exact in F16 (entries +-1, k_norm powers of two)
+    rotated at p is the same as projecting at p: RoPE comes after the norm and
+    the weight, at the row's own absolute position, with one rounding."""
+    rs = np.random.default_rng(24)
+    n, d_model, hk, d = 5, 2 * 16, 2, 16
+    f = rs.choice([-1.0, 1.0], size=(n, d_model)).astype(np.float16)
+    wk = _one_hot(hk * d, d_model, rs.permutation(d_model)[: hk * d])
+    knorm = np.array([1.0, 2.0, 0.5, 4.0] * (d // 4))
+    pos = np.array([0, 7, 4096, 70001, 131071])
+    k0, _ = ro.project_kv(f, wk, wk, knorm, np.zeros(n, np.int64), hk, d, 1e6, eps=0.0)
+    kp, _ = ro.project_kv(f, wk, wk, knorm, pos, hk, d, 1e6, eps=0.0)
+    assert np.array_equal(kp, ro.rope_rows_f16(k0, pos, hk, d, 1e6))
+    assert not np.array_equal(kp[1:], k0[1:])
+
+
+def pin_project_scale_invariance():
+    """With eps = 0 the K norm ignores a power-of-two scale of the features;
+    V scales with it exactly."""
+    rs = np.random.default_rng(25)
+    n, d_model, hk, d = 7, 48, 2, 8
+    f = rs.normal(size=(n, d_model)).astype(np.float16)
+    wk = (rs.normal(size=(hk * d, d_model)) / 8).astype(np.float16)
+    wv = (rs.normal(size=(hk * d, d_model)) / 8).astype(np.float16)
+    knorm = rs.uniform(0.5, 1.5, size=d)
+    pos = rs.integers(0, 100000, size=n)
+    k1, v1 = ro.project_kv(f, wk, wv, knorm, pos, hk, d, 1e6, eps=0.0)
+    k2, v2 = ro.project_kv(f * np.float16(4.0), wk, wv, knorm, pos, hk, d, 1e6, eps=0.0)
+    assert np.array_equal(k1, k2)
+    assert np.array_equal(v2.astype(np.float64), 4.0 * v1.astype(np.float64))
+
+
+def pin_feature_mirror_brute_force():
+    """The mirror returns, for a position, the features last written for it as
+    long as no later write landed in its slot p % cap, and refuses it
+    otherwise; over plain streams that is exactly the last cap positions."""
+    rs = random.Random(26)
+    for cap in (1, 3, 8):
+        m = ro.FeatureMirror(cap, 4)
+        history = []                  # every (position, features) write, in order
+        hi = 0
+        for step in range(60):
+            rewind = step % 9 == 8 and hi > 2
+            if rewind:
+                hi -= rs.randint(1, min(hi, cap))        # rewind: rewrite from there
+            n = rs.randint(0, 2 * cap)
+            pos = np.arange(hi, hi + n)
+            feats = np.array([[p, step, p % 7, -p] for p in pos], np.float16).reshape(n, 4)
+            m.write(pos, feats)
+            history += [(int(p), feats[j]) for j, p in enumerate(pos)]
+            hi += n
+            written = {p for p, _ in history}
+            for p in sorted(written):
+                later = [q for q, _ in history if q % cap == p % cap]
+                held = later[-1] == p                  # the slot's most recent write
+                if held:
+                    want = [fv for q, fv in history if q == p][-1]
+                    assert np.array_equal(m.read(np.array([p]))[0], want), (cap, step, p)
+                else:
+                    try:
+                        m.read(np.array([p]))
+                        raise AssertionError(f"position {p} read after its slot was reused")
+                    except KeyError:
+                        pass
+            if not rewind and n >= cap:
+                for p in range(hi - cap, hi):
+                    m.read(np.array([p]))
+
+
+def pin_commit_features_equals_commit():
+    """Rows from features through weights that select +-1 features (K exact
+    after the norm) equal rows passed directly, over a stream that wraps the
+    ring and rewinds: the mirror supplies exactly the positions each plan needs."""
+    rs = np.random.default_rng(27)
+    cap, q_len, hk, d, nh, d_model = 6, 2, 2, 8, 4, 40
+    g = ro.geometry(cap, q_len, d, hk)
+    kv_row = hk * d
+    wk = _one_hot(kv_row, d_model, np.arange(kv_row))
+    wv = _one_hot(kv_row, d_model, np.arange(kv_row) + kv_row)
+    a = ro.RingStep(g, 1, hk, d, 1e6)
+    b = ro.RingStep(g, 1, hk, d, 1e6)
+    mirror = ro.FeatureMirror(cap, d_model)
+    feats = {}
+    committed = 0
+    resupplied = 0
+    for step, c in enumerate([4, 5, 9, 10, 12, 11, 7, 8, 15, 16, 19, 30, 31]):
+        # the target supplies features of positions past the last step only
+        new = np.arange(committed, c) if c > committed else np.arange(0)
+        for p in new:
+            feats[int(p)] = np.concatenate([rs.choice([-1.0, 1.0], size=kv_row),
+                                            rs.normal(size=d_model - kv_row)]).astype(np.float16)
+        if new.size:
+            mirror.write(new, np.stack([feats[int(p)] for p in new]))
+        pa, pb = a.plan(c), b.plan(c)
+        assert pa == pb
+        pos = np.arange(pa.start, c)
+        # a rewind below what the ring holds re-appends window rows whose
+        # mirror slots newer positions took: those are supplied again
+        for p in pos:
+            try:
+                mirror.read(np.array([p]))
+            except KeyError:
+                mirror.write(np.array([p]), feats[int(p)][None])
+                resupplied += 1
+        rows = np.stack([feats[int(p)] for p in pos]) if pos.size else np.zeros((0, d_model), np.float16)
+        a.commit(pa, [rows[:, :kv_row]], [rows[:, kv_row:2 * kv_row]])
+        b.commit_features(pb, mirror, [wk], [wv], [np.ones(d)], eps=0.0)
+        committed = c
+        q = rs.normal(size=(q_len, nh, d)).astype(np.float16)
+        kn = rs.normal(size=(q_len, kv_row)).astype(np.float16)
+        vn = rs.normal(size=(q_len, kv_row)).astype(np.float16)
+        oa = ro.attend(a.caches[0], c, cap, q, kn, vn, nh)
+        ob = ro.attend(b.caches[0], c, cap, q, kn, vn, nh)
+        assert np.array_equal(oa, ob), step
+    assert resupplied > 0      # the stream does reach a rewind past the mirror
+
+
 ALL_PINS = [
     pin_geometry_worked_example, pin_geometry_closed_form,
     pin_plan_monotone_closed_form, pin_fold_in_threshold,
@@ -539,4 +723,7 @@ ALL_PINS = [
     pin_swa_brute_force, pin_swa_ring_equals_window, pin_swa_invariants,
     pin_swa_mask_closed_form,
     pin_attention_ring_equals_full, pin_attention_fp32_mode,
+    pin_project_v_selects_features, pin_project_k_head_rms, pin_project_k_constant_slice,
+    pin_project_k_rope_after_norm, pin_project_scale_invariance,
+    pin_feature_mirror_brute_force, pin_commit_features_equals_commit,
 ]

@@ -63,6 +63,22 @@ MUTATIONS = [
      "m[i, g.cap: g.cap + i] = np.float16(0.0)"),
     ("mask_swa", "m[i, g.cap: g.cap + i + 1] = np.float16(0.0)",
      "m[i, g.cap: g.cap + g.q_len] = np.float16(0.0)"),
+    # new rows' K/V from fused features, and the feature mirror
+    ("project_kv", "k = k / rms * np.asarray(k_norm, dtype=np.float64)",
+     "k = k * np.asarray(k_norm, dtype=np.float64)"),
+    ("project_kv", "k = k / rms * np.asarray(k_norm, dtype=np.float64)", "k = k / rms"),
+    ("project_kv", "(k * k).mean(axis=-1, keepdims=True)", "(k * k).sum(axis=-1, keepdims=True)"),
+    ("project_kv", "(k * k).mean(axis=-1, keepdims=True)",
+     "(k * k).mean(axis=(-1, -2), keepdims=True)"),
+    ("project_kv", "k = rope(k, positions, base)", "k = rope(k, positions + 1, base)"),
+    ("project_kv", "k = rope(k, positions, base).reshape(n, n_head_kv * head_dim)",
+     "k = k.reshape(n, n_head_kv * head_dim)"),
+    ("project_kv", "v = f @ np.asarray(wv, dtype=np.float64).T",
+     "v = f @ np.asarray(wk, dtype=np.float64).T"),
+    ("FeatureMirror.write", "self.slots[p % self.cap] = features[j]",
+     "self.slots[(p + 1) % self.cap] = features[j]"),
+    ("FeatureMirror.read", "if self.slot_pos[p % self.cap] != p:", "if False:"),
+    ("RingStep.commit_features", "f = mirror.read(pos)", "f = mirror.read(pos[::-1])"),
 ]
 
 
