@@ -312,6 +312,12 @@ struct AttnShape {
   static constexpr int kQBytes = MB * 2 * 8 * 64 * 16;
   static constexpr int kRowBytes = NW * 2 * kHeadDim * 2;  // one K and one V row per wave
   static constexpr int kMergeBytes = MB * 4 * NW * 4 * 64 * 16;  // reduce-scatter buffer
+  // fp32 (cos, sin) of the noise positions, [q_len <= 32][64][2]: read by the
+  // query build only, so it shares bytes with the merge buffer (written after
+  // the query build's barrier).
+  static constexpr int kRopeOffset = kQBytes + kRowBytes;
+  static constexpr int kRopeBytes = 32 * 64 * 2 * 4;  // = 4 passes of NT float4
+  static_assert(kRopeBytes == 4 * NT * 16, "rope passes fill the table bytes");
   // The query fragments and the noise-row buffers live until a wave's tile
   // loop ends.  With one query block the merge buffer has bytes of its own,
   // so a wave writes it as soon as its own loop ends; with two it reuses the
@@ -321,6 +327,7 @@ struct AttnShape {
   static constexpr int kLdsBytes =
       kOwnMergeBytes ? kQBytes + kRowBytes + kMergeBytes
                      : (kQBytes + kRowBytes > kMergeBytes ? kQBytes + kRowBytes : kMergeBytes);
+  static_assert(kRopeOffset + kRopeBytes <= kLdsBytes, "rope table fits the merge bytes");
 };
 
 // One noise row of this wave's (sequence, head), already loaded: lane f holds
@@ -432,7 +439,136 @@ __device__ __forceinline__ void attend_noise_row(
   }
 }
 
-template <int MB, int NW>
+// Merge of the NW waves of a work-group by reduce-scatter over the four
+// 32-dim blocks of O^T, and the store of the result.  Wave W keeps block W and
+// hands the other three, unscaled, to their owners through LDS (same fragment
+// order, so lane l reads what lane l of the other wave wrote), together with
+// its running (max, sum) per query.  After one barrier each lane owns query
+// n = 32 mb + col: it forms the work-group's (mx, lt), weighs every wave's
+// block by 2^(m - mx) (and by 1 / lt when this is the only split) and stores
+// its block of the output or partial: lane (col, hl) holds dims
+// 32 W + 8 jj + 4 hl + 0..3 of query 32 mb + col; rows past m are padding.
+// A wave-uniform value made opaque to the compiler (it can neither re-load
+// nor re-compute it later, so it stays in SGPRs).
+__device__ inline uint64_t keep_sgpr(uint64_t v) {
+  uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  asm volatile("" : "+s"(lo), "+s"(hi));
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ inline int keep_sgpr(int v) {
+  v = __builtin_amdgcn_readfirstlane(v);
+  asm volatile("" : "+s"(v));
+  return v;
+}
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) float gfloat;
+typedef __attribute__((address_space(1))) f32x2 gf32x2;
+typedef __attribute__((address_space(1))) f32x4 gf32x4;
+
+// What the store of a work-group's result needs: its output rows (one split)
+// or its partial slot, and the query geometry.
+struct EpilogueArgs {
+  gfloat* out_unit;
+  gfloat* pacc;
+  gfloat* pml;
+  bool one_split;
+  int m, group, n_head;
+};
+
+template <int MB, int NW, int W>
+__device__ __forceinline__ void merge_store(const EpilogueArgs& a, unsigned char* lds,
+                                            float (*sm_m)[MB * 32], float (*sm_l)[MB * 32],
+                                            const float (&m_run)[MB], const float (&l_run)[MB],
+                                            const f32x16 (&o)[MB][4], int lane) {
+  using S = AttnShape<MB, NW>;
+  const int hl = lane >> 5, col = lane & 31;
+  // [mb][block][writer][jj][lane]
+  float4* xbuf = reinterpret_cast<float4*>(lds + S::kMergeOffset);
+  if constexpr (!S::kOwnMergeBytes) lds_barrier();  // every wave is past its loop
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    if (hl == 0) {
+      sm_m[W][mb * 32 + col] = m_run[mb];
+      sm_l[W][mb * 32 + col] = l_run[mb];
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      if (b == W) continue;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        xbuf[(((mb * 4 + b) * NW + W) * 4 + jj) * 64 + lane] =
+            make_float4(o[mb][b][4 * jj], o[mb][b][4 * jj + 1], o[mb][b][4 * jj + 2],
+                        o[mb][b][4 * jj + 3]);
+    }
+  }
+  lds_barrier();
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int n = mb * 32 + col;
+    float mw_[NW], lw_[NW];
+    float4 blk[NW][4];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      mw_[w] = sm_m[w][n];
+      lw_[w] = sm_l[w][n];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        if (w == W)
+          blk[w][jj] = make_float4(o[mb][W][4 * jj], o[mb][W][4 * jj + 1], o[mb][W][4 * jj + 2],
+                                   o[mb][W][4 * jj + 3]);
+        else
+          blk[w][jj] = xbuf[(((mb * 4 + W) * NW + w) * 4 + jj) * 64 + lane];
+      }
+    }
+    float mx = kNegInf;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, mw_[w]);
+    // A wave that saw no visible key has m = -inf and l = 0.
+    float sw[NW], lt = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float e = exp2_hw(mw_[w] - mx);
+      sw[w] = mw_[w] == kNegInf ? 0.0f : e;
+      lt += sw[w] * lw_[w];
+    }
+    float4 v[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float4 u = blk[w][jj];
+        acc.x += sw[w] * u.x; acc.y += sw[w] * u.y; acc.z += sw[w] * u.z; acc.w += sw[w] * u.w;
+      }
+      v[jj] = acc;
+    }
+    if (a.one_split) {
+      // lt > 0: the noise rows are visible to every query.
+      const float inv = 1.0f / lt;
+      if (n < a.m) {
+        const unsigned i = n / a.group, hh = n - i * a.group;
+        gfloat* dst = a.out_unit + (i * a.n_head + hh) * kHeadDim + 32 * W + 4 * hl;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          *(gf32x4*)(dst + 8 * jj) = f32x4{v[jj].x * inv, v[jj].y * inv, v[jj].z * inv,
+                                           v[jj].w * inv};
+      }
+    } else {
+      if (W == 0 && hl == 0 && n < a.m) *(gf32x2*)(a.pml + n * 2) = f32x2{mx, lt};
+      // partial in fragment order [mb][block][jj][lane] float4: each store
+      // instruction writes 1 KB contiguous.
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        *(gf32x4*)(a.pacc + (((mb * 4 + W) * 4 + jj) * 64 + lane) * 4) =
+            f32x4{v[jj].x, v[jj].y, v[jj].z, v[jj].w};
+    }
+  }
+}
+
+template <int MB, int NW, int RP>
 __device__ __forceinline__ void attn_body(const AttnArgs& a, int unit, int split, int vis_first,
                                           int vis_count, unsigned char* lds,
                                           float (*sm_m)[MB * 32], float (*sm_l)[MB * 32]) {
@@ -460,6 +596,17 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int unit, int split
   const int t1 = min(nvt, t0 + per);
   uint16_t* kh = a.kring + seq * a.seq_stride + a.layer_offset + g * a.head_stride;
   uint16_t* vh = a.vring + seq * a.seq_stride + a.layer_offset + g * a.head_stride;
+  // The destinations and the few integers the store needs are computed
+  // up front and pass through an empty asm statement that redefines them, so the
+  // compiler keeps them in SGPRs instead of re-loading kernel arguments in
+  // the epilogue (a scalar memory round trip); stores then go through
+  // global-address-space pointers.
+  uint64_t out_unit = (uint64_t)(a.out + ((int64_t)seq * a.q_len * a.n_head + g * a.group) * kHeadDim);
+  uint64_t pacc = (uint64_t)(a.part_acc + ((int64_t)unit * a.n_split + split) * MP * kHeadDim);
+  uint64_t pml = (uint64_t)(a.part_ml + ((int64_t)unit * a.n_split + split) * MP * 2);
+  const EpilogueArgs ep{(gfloat*)keep_sgpr(out_unit), (gfloat*)keep_sgpr(pacc),
+                        (gfloat*)keep_sgpr(pml), keep_sgpr(a.n_split == 1) != 0,
+                        keep_sgpr(a.m), keep_sgpr(a.group), keep_sgpr(a.n_head)};
 
   // Noise rows of this wave: r = rank, rank + W, ... with W the waves of the
   // (sequence, head); rank counts from the last wave of the last split, whose
@@ -475,10 +622,18 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int unit, int split
     qrow[mb] = n < a.m ? n / a.group : 0;
   }
 
-  // ---- 1a. loads for the query build: thread item = (mb, chunk pair c,
-  //      lane ln); x = dims 16c + 8h + e, y = the same dims + 64.
+  // ---- 1a. loads for the query build: the sequence's (cos, sin) table once
+  //      per work-group (q_len * 32 float4, staged through LDS), then per
+  //      thread item = (mb, chunk pair c, lane ln) the query halves x = dims
+  //      16c + 8h + e and y = the same dims + 64.
+  //      RP passes of one float4 per thread cover q_len <= RP * NT / 32; a
+  //      pass past the table re-reads its last float4 (one line for the wave).
+  float4 rope_v[RP];
+#pragma unroll
+  for (int k = 0; k < RP; ++k)
+    rope_v[k] = ((const float4*)ropeq)[min((int)threadIdx.x + k * NT, a.q_len * 32 - 1)];
   half8 qx[MB], qy[MB];
-  float4 qcs[MB][4];  // (cos, sin) pairs of frequencies 16c + 8h + e, e = 0..7
+  unsigned qfreq[MB];  // float4 index of (cos, sin) of frequency 16c + 8h at query row i
   const uint16_t* qseq = a.q + ((int64_t)seq * a.q_len * a.n_head + g * a.group) * kHeadDim;
 #pragma unroll
   for (int k = 0; k < MB; ++k) {
@@ -489,9 +644,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int unit, int split
     const unsigned qo = (i * a.n_head + hh) * kHeadDim + 16 * c + 8 * h2;
     qx[k] = *(const half8*)(qseq + qo);
     qy[k] = *(const half8*)(qseq + qo + 64);
-    const float4* rq = (const float4*)(ropeq + (i * 64 + 16 * c + 8 * h2) * 2);
-#pragma unroll
-    for (int e2 = 0; e2 < 4; ++e2) qcs[k][e2] = rq[e2];
+    qfreq[k] = (i * 64 + 16 * c + 8 * h2) / 2;
   }
 
   // ---- 1b. the wave's first noise row (a wave without one loads the last
@@ -529,6 +682,18 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int unit, int split
   // ---- 2. queries: rotate at committed + i, scale by log2(e)/sqrt(d),
   //      split into hi + lo F16 (fragment order [mb][hi/lo][chunk][lane]);
   //      queries past q_len * group are zero.
+  float4* rope_lds = reinterpret_cast<float4*>(lds + S::kRopeOffset);
+  // unconditional: entries past the table hold copies of its last float4
+  // and are never read (a conditional store would let the compiler sink the
+  // load into the branch and wait for every load in flight there)
+#pragma unroll
+  for (int k = 0; k < RP; ++k) rope_lds[threadIdx.x + k * NT] = rope_v[k];
+  lds_barrier();
+  float4 qcs[MB][4];  // (cos, sin) pairs of frequencies 16c + 8h + e, e = 0..7
+#pragma unroll
+  for (int k = 0; k < MB; ++k)
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) qcs[k][e2] = rope_lds[qfreq[k] + e2];
   half8* q_lds = reinterpret_cast<half8*>(lds);
 #pragma unroll
   for (int k = 0; k < MB; ++k) {
@@ -604,13 +769,12 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int unit, int split
   //      before the current tile is processed (two tiles in registers); two
   //      query blocks have no room for that.
   constexpr bool kPrefetch = MB == 1;
-  while (tile < t1) {
-    const int next = tile + NW;
-    if constexpr (kPrefetch) {
-      // The last prefetch re-reads the current tile (already in cache).
+  if constexpr (kPrefetch) {
+    // every tile but the wave's last one: its successor is fetched first
+    while (tile + NW < t1) {
       half8 kn[8], vn[8];
       uint32_t mn[MB][8];
-      load_tile(ring_tile(next < t1 ? next : tile), kn, vn, mn);
+      load_tile(ring_tile(tile + NW), kn, vn, mn);
       attend_tile<MB>(kc, vc, mw, a.cap - ring_tile(tile) * kTile, hl, qf, q_lds, lane, m_run,
                       l_run, o);
 #pragma unroll
@@ -619,115 +783,35 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int unit, int split
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int j = 0; j < 8; ++j) mw[mb][j] = mn[mb][j];
-    } else {
+      tile += NW;
+    }
+    if (tile < t1)
+      attend_tile<MB>(kc, vc, mw, a.cap - ring_tile(tile) * kTile, hl, qf, q_lds, lane, m_run,
+                      l_run, o);
+  } else {
+    while (tile < t1) {
+      const int next = tile + NW;
       attend_tile<MB>(kc, vc, mw, a.cap - ring_tile(tile) * kTile, hl, qf, q_lds, lane, m_run,
                       l_run, o);
       if (next < t1) load_tile(ring_tile(next), kc, vc, mw);
+      tile = next;
     }
-    tile = next;
   }
 
-  // ---- 5. merge the waves of this work-group by reduce-scatter over the
-  //      four 32-dim blocks of O^T: wave w keeps block w and hands the other
-  //      three, unscaled, to their owners through LDS (same fragment order,
-  //      so lane l reads what lane l of the other wave wrote), together with
-  //      its running (max, sum) per query.  After one barrier each lane owns
-  //      query n = 32 mb + col: it forms the work-group's (mx, lt), weighs
-  //      every wave's block by 2^(m - mx) (and by 1 / lt when this is the only
-  //      split) and stores its block of the output or partial.
+  // ---- 5./6. merge the waves and store: a copy of the code per wave, so
+  //      that the wave's own accumulator block is picked at compile time.
   static_assert(NW == 4, "one 32-dim output block per wave");
-  // [mb][block][writer][jj][lane]
-  float4* xbuf = reinterpret_cast<float4*>(lds + S::kMergeOffset);
-  if constexpr (!S::kOwnMergeBytes) lds_barrier();  // every wave is past its loop
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    if (hl == 0) {
-      sm_m[wave][mb * 32 + col] = m_run[mb];
-      sm_l[wave][mb * 32 + col] = l_run[mb];
-    }
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      if (b == wave) continue;
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        xbuf[(((mb * 4 + b) * NW + wave) * 4 + jj) * 64 + lane] =
-            make_float4(o[mb][b][4 * jj], o[mb][b][4 * jj + 1], o[mb][b][4 * jj + 2],
-                        o[mb][b][4 * jj + 3]);
-    }
-  }
-  lds_barrier();
-
-  // ---- 6. the final output (one split) or this split's partial: lane
-  //      (col, hl) holds dims 32 wave + 8 jj + 4 hl + 0..3 of query
-  //      32 mb + col.  Rows past m are padding.
-  float* out_unit = a.out + ((int64_t)seq * a.q_len * a.n_head + g * a.group) * kHeadDim;
-  float* pacc = a.part_acc + ((int64_t)unit * a.n_split + split) * MP * kHeadDim;
-  float* pml = a.part_ml + ((int64_t)unit * a.n_split + split) * MP * 2;
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const int n = mb * 32 + col;
-    float mw_[NW], lw_[NW];
-    float4 blk[NW][4];
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      mw_[w] = sm_m[w][n];
-      lw_[w] = sm_l[w][n];
-      if (w == wave) continue;
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) blk[w][jj] = xbuf[(((mb * 4 + wave) * NW + w) * 4 + jj) * 64 + lane];
-    }
-    float mx = kNegInf;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, mw_[w]);
-    // A wave that saw no visible key has m = -inf and l = 0; selects, not
-    // branches, so every LDS read above is issued at once.
-    float sw[NW], lt = 0.0f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float e = exp2_hw(mw_[w] - mx);
-      sw[w] = mw_[w] == kNegInf ? 0.0f : e;
-      lt += sw[w] * lw_[w];
-    }
-    float4 v[4];
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        float4 u;
-        if (w == wave) {
-          u = make_float4(o[mb][w][4 * jj], o[mb][w][4 * jj + 1], o[mb][w][4 * jj + 2],
-                          o[mb][w][4 * jj + 3]);
-        } else {
-          u = blk[w][jj];
-        }
-        acc.x += sw[w] * u.x; acc.y += sw[w] * u.y; acc.z += sw[w] * u.z; acc.w += sw[w] * u.w;
-      }
-      v[jj] = acc;
-    }
-    if (a.n_split == 1) {
-      // lt > 0: the noise rows are visible to every query.
-      const float inv = 1.0f / lt;
-      if (n < a.m) {
-        const unsigned i = n / a.group, hh = n - i * a.group;
-        float* dst = out_unit + (i * a.n_head + hh) * kHeadDim + 32 * wave + 4 * hl;
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-          *(float4*)(dst + 8 * jj) = make_float4(v[jj].x * inv, v[jj].y * inv, v[jj].z * inv,
-                                                 v[jj].w * inv);
-      }
-    } else {
-      if (wave == 0 && hl == 0 && n < a.m) *(float2*)(pml + n * 2) = make_float2(mx, lt);
-      // partial in fragment order [mb][block][jj][lane] float4: each store
-      // instruction writes 1 KB contiguous.
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        *(float4*)(pacc + (((mb * 4 + wave) * 4 + jj) * 64 + lane) * 4) = v[jj];
-    }
-  }
+  if (wave == 0)
+    merge_store<MB, NW, 0>(ep, lds, sm_m, sm_l, m_run, l_run, o, lane);
+  else if (wave == 1)
+    merge_store<MB, NW, 1>(ep, lds, sm_m, sm_l, m_run, l_run, o, lane);
+  else if (wave == 2)
+    merge_store<MB, NW, 2>(ep, lds, sm_m, sm_l, m_run, l_run, o, lane);
+  else
+    merge_store<MB, NW, 3>(ep, lds, sm_m, sm_l, m_run, l_run, o, lane);
 }
 
-template <int MB, int NW>
+template <int MB, int NW, int RP>
 __global__ __launch_bounds__(NW * 64) void k_ring_attn(AttnArgs a) {
   using S = AttnShape<MB, NW>;
   __shared__ __attribute__((aligned(16))) unsigned char lds[S::kLdsBytes];
@@ -760,7 +844,7 @@ __global__ __launch_bounds__(NW * 64) void k_ring_attn(AttnArgs a) {
     split = blockIdx.x % a.n_split;
   }
   const int seq = unit / a.n_head_kv;
-  attn_body<MB, NW>(a, unit, split, __builtin_amdgcn_readlane(firstv, seq),
+  attn_body<MB, NW, RP>(a, unit, split, __builtin_amdgcn_readlane(firstv, seq),
                     __builtin_amdgcn_readlane(countv, seq), lds, sm_m, sm_l);
 }
 
@@ -867,10 +951,18 @@ hipError_t launch_step(const StepArgs& a, hipStream_t s, hipEvent_t t0, hipEvent
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
   const int grid = a.n_seq * a.n_head_kv * a.n_split;
+  // rope table passes: one float4 per thread covers q_len <= 8
+  const bool one_pass = a.q_len <= 8;
   if (a.m <= 32) {
-    hipExtLaunchKernelGGL((k_ring_attn<1, 4>), dim3(grid), dim3(256), 0, s, t0, t1, 0, a);
+    if (one_pass)
+      hipExtLaunchKernelGGL((k_ring_attn<1, 4, 1>), dim3(grid), dim3(256), 0, s, t0, t1, 0, a);
+    else
+      hipExtLaunchKernelGGL((k_ring_attn<1, 4, 4>), dim3(grid), dim3(256), 0, s, t0, t1, 0, a);
   } else {
-    hipExtLaunchKernelGGL((k_ring_attn<2, 4>), dim3(grid), dim3(256), 0, s, t0, t1, 0, a);
+    if (one_pass)
+      hipExtLaunchKernelGGL((k_ring_attn<2, 4, 1>), dim3(grid), dim3(256), 0, s, t0, t1, 0, a);
+    else
+      hipExtLaunchKernelGGL((k_ring_attn<2, 4, 4>), dim3(grid), dim3(256), 0, s, t0, t1, 0, a);
   }
   return hipGetLastError();
 }
