@@ -35,6 +35,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "ring_attn steps/s + achieved HBM GB/s (% peak), cap=4096, q_len=8, GQA 32/8x128"
+RMS_EPS = 1e-6   # epsilon of the K norm of rows projected from features
 HBM_PEAK_GBS = 8000.0
 WORKLOAD = "decode_stream"
 
@@ -127,8 +128,17 @@ def prepare(w, pool: int, total: int, dev):
     rings = [R.Ring(cap=w.cap, q_len=w.q_len, n_head=w.n_head, n_head_kv=w.n_head_kv,
                     head_dim=w.head_dim, n_layer=w.n_layer, n_seq=w.n_seq,
                     rope_base=w.rope_base, device=dev, swa_window=w.swa_window,
-                    swa_layers=w.swa_layers) for _ in range(pool)]
+                    swa_layers=w.swa_layers, d_model=w.d_model) for _ in range(pool)]
     s = torch.cuda.current_stream(dev).cuda_stream
+    mirror = w.d_model > 0
+    if mirror:
+        wk, wv, kn = W.projection_weights(w)
+        weights = (torch.from_numpy(wk).to(dev), torch.from_numpy(wv).to(dev),
+                   torch.from_numpy(kn).to(dev))
+        wptr = (weights[0].data_ptr(), weights[1].data_ptr(), weights[2].data_ptr(), RMS_EPS)
+
+    def feats(seq, lo, hi):
+        return torch.from_numpy(W.fused_features(w, seq, np.arange(lo, hi))).to(dev)
 
     def rows(seq, lo, hi):
         pos = np.arange(lo, hi)
@@ -142,6 +152,15 @@ def prepare(w, pool: int, total: int, dev):
         for seq in range(w.n_seq):
             c = streams[seq][t]
             plan, _ = rings[0].plan(seq, c)
+            if mirror:
+                f = feats(seq, prev[seq], c)
+                for r in rings:
+                    R.ring_mirror_write(r.handle, seq, prev[seq], c - prev[seq], f.data_ptr(), s)
+                    R.ring_begin_step_mirror(r.handle, seq, c, *wptr, s)
+                torch.cuda.synchronize(dev)
+                prev[seq] = c
+                del f
+                continue
             k, v, n = rows(seq, plan.start, c)
             for r in rings:
                 R.ring_begin_step(r.handle, seq, c, k.data_ptr(), v.data_ptr(), n, s)
@@ -154,6 +173,11 @@ def prepare(w, pool: int, total: int, dev):
         seqs = []
         for seq in range(w.n_seq):
             c0, c = streams[seq][n_warm + j - 1], streams[seq][n_warm + j]
+            if mirror:
+                # the features of the newly committed positions (the mirror
+                # write is part of the step), no K/V rows
+                seqs.append((seq, c, feats(seq, c0, c), c0, c - c0))
+                continue
             k, v, n = rows(seq, c0, c)
             seqs.append((seq, c, k, v, n))
         layers = []
@@ -166,13 +190,17 @@ def prepare(w, pool: int, total: int, dev):
     calls = []
     for t in range(total):
         r, (seqs, layers) = rings[t % pool], steps_in[t // pool]
-        calls.append((r.handle,
-                      [(seq, c, k.data_ptr(), v.data_ptr(), n) for seq, c, k, v, n in seqs],
+        if mirror:
+            sq = [(seq, c, f.data_ptr(), c0, n) for seq, c, f, c0, n in seqs]
+        else:
+            sq = [(seq, c, k.data_ptr(), v.data_ptr(), n) for seq, c, k, v, n in seqs]
+        calls.append((r.handle, sq,
                       [(layer, q.data_ptr(), kn.data_ptr(), vn.data_ptr())
                        for layer, q, kn, vn in layers]))
     committed = [[streams[seq][n_warm + t // pool] for seq in range(w.n_seq)]
                  for t in range(total)]
-    return rings, calls, steps_in, committed
+    extra = (weights, wptr) if mirror else None
+    return rings, calls, (steps_in, extra), committed
 
 
 # The rocprofv3 runs behind the committed summaries under profiles/, each run
@@ -364,7 +392,8 @@ def main() -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     geo = R.ring_query_geometry(R.make_config(w.cap, w.q_len, w.n_head, w.n_head_kv,
-                                              w.head_dim, w.n_layer, w.n_seq, w.rope_base))
+                                              w.head_dim, w.n_layer, w.n_seq, w.rope_base,
+                                              d_model=w.d_model))
     ring_bytes = w.n_seq * w.n_layer * geo.kv_bytes_per_layer
     pool = args.pool or max(1, -(-(512 << 20) // ring_bytes))
     # warm-up, the timed steps, then as many steps again with per-kernel
@@ -375,12 +404,20 @@ def main() -> int:
     s = torch.cuda.current_stream(dev).cuda_stream
     out = torch.empty((w.n_seq, w.q_len, w.n_head, w.head_dim), dtype=torch.float32, device=dev)
     begin, attn, optr = R.ring_begin_step, R.ring_attn, out.data_ptr()
+    mirror = w.d_model > 0
+    mwrite, mbegin = R.ring_mirror_write, R.ring_begin_step_mirror
+    wptr = steps_in[1][1] if mirror else None
 
     def run(lo, hi):
         for t in range(lo, hi):
             h, seqs, layers = calls[t]
-            for seq, c, kp, vp, n in seqs:
-                begin(h, seq, c, kp, vp, n, s)
+            if mirror:
+                for seq, c, fp, c0, n in seqs:
+                    mwrite(h, seq, c0, n, fp, s)
+                    mbegin(h, seq, c, *wptr, s)
+            else:
+                for seq, c, kp, vp, n in seqs:
+                    begin(h, seq, c, kp, vp, n, s)
             for layer, qp, knp, vnp in layers:
                 attn(h, layer, qp, knp, vnp, optr, s)
 
@@ -402,7 +439,7 @@ def main() -> int:
 
     prof = {}
     for kind, name in ((R.RING_KERNEL_STEP, "k_ring_step"), (R.RING_KERNEL_ATTN, "k_ring_attn"),
-                       (R.RING_KERNEL_MERGE, "k_ring_merge")):
+                       (R.RING_KERNEL_MERGE, "k_ring_merge"), (R.RING_KERNEL_PROJ, "k_ring_project")):
         n_l, ms = 0, 0.0
         for r in rings:
             a, b = r.profile_read(kind)
@@ -434,6 +471,24 @@ def main() -> int:
     achieved = per_launch / (attn_us * 1e-6) / 1e9
     khash = kernel_source_hash()
     traffic = traffic_from_profiles(khash) if args.workload == WORKLOAD else None
+    roof_attn = {"kernel": "k_ring_attn", "bound": "hbm", "achieved": achieved,
+                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                 "traffic": traffic, "bytes_per_launch": int(per_launch),
+                 "avg_launch_us": attn_us}
+    roofline = roof_attn
+    if mirror:
+        # the projection launch of a decode step reads every layer's wk and wv
+        # once and the new rows' features (n <= a_step rows of d_model F16)
+        seg_rows = [sum(n for _, _, _, _, n in steps_in[0][t // pool][0])
+                    for t in range(args.warmup + args.steps, total)]
+        proj_bytes = (2 * w.n_layer * w.kv_row * w.d_model * 2 +
+                      float(np.mean(seg_rows)) * w.d_model * 2)
+        proj_us = prof["k_ring_project"]["avg_us"]
+        pa = proj_bytes / (proj_us * 1e-6) / 1e9
+        roofline = {"kernel": "k_ring_project", "bound": "hbm", "achieved": pa,
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": pa / HBM_PEAK_GBS,
+                    "traffic": None, "bytes_per_launch": int(proj_bytes),
+                    "avg_launch_us": proj_us}
     line = {
         "metric": METRIC if args.workload == WORKLOAD else
         f"ring step steps/s + achieved HBM GB/s, workload {args.workload}",
@@ -454,15 +509,13 @@ def main() -> int:
                    "n_layer": w.n_layer, "n_seq": w.n_seq, "kv_total": geo.kv_total,
                    "ring_pool": pool, "infinity_cache": "cold" if pool > 1 or ring_bytes > (256 << 20) else "warm",
                    "ring": split_desc},
-        "roofline": {"kernel": "k_ring_attn", "bound": "hbm", "achieved": achieved,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic, "bytes_per_launch": int(per_launch),
-                     "avg_launch_us": attn_us},
+        "roofline": roofline,
         "ring_attn": {"kernels": "k_ring_attn + k_ring_merge",
                       "avg_us": attn_us + merge_us,
                       "calls_per_s": 1e6 / (attn_us + merge_us),
                       "achieved_GBps": per_call / ((attn_us + merge_us) * 1e-6) / 1e9},
         "kernels": prof,
+        **({"roofline_attn": roof_attn} if mirror else {}),
         "profiled_segment_steps_per_s": args.steps / elapsed_prof,
         "kernel_source_hash": khash,
     }

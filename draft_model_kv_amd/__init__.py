@@ -1,20 +1,23 @@
 """Draft-KV ring of a block-diffusion speculative decoder, MI355X-native.
 
 The ring path (append with absolute RoPE, window mask, masked GQA attention
-of the noise block) runs in HIP kernels for gfx950 behind the C ABI declared
-in include/ring_kv.h; ``draft_model_kv_amd.ring`` is its Python binding.
+of the noise block, and the new rows' K/V projected from a feature mirror)
+runs in HIP kernels for gfx950 behind the C ABI declared in
+include/ring_kv.h; ``draft_model_kv_amd.ring`` is its Python binding.
 """
 
-from .ring import (Ring, RingConfig, RingError, RingGeometry, RingPlan, make_config,
-                   ring_attn, ring_begin_step, ring_describe, ring_free, ring_init,
-                   ring_last_error, ring_plan_from_state, ring_plan_step,
-                   ring_query_geometry, ring_read_mask, ring_read_mask_swa, ring_read_rows,
-                   ring_read_slot_pos, ring_read_state, ring_profile_enable,
-                   ring_profile_read, RING_KERNEL_STEP, RING_KERNEL_ATTN, RING_KERNEL_MERGE)
+from .ring import (Ring, RingConfig, RingError, RingGeometry, RingKvWeights, RingPlan,
+                   make_config, ring_attn, ring_begin_step, ring_begin_step_mirror,
+                   ring_describe, ring_free, ring_init, ring_last_error, ring_mirror_write,
+                   ring_plan_from_state, ring_plan_step, ring_query_geometry, ring_read_mask,
+                   ring_read_mask_swa, ring_read_rows, ring_read_slot_pos, ring_read_state,
+                   ring_profile_enable, ring_profile_read, RING_KERNEL_STEP, RING_KERNEL_ATTN,
+                   RING_KERNEL_MERGE, RING_KERNEL_PROJ)
 
-__all__ = ["Ring", "RingConfig", "RingError", "RingGeometry", "RingPlan", "make_config",
-           "ring_attn", "ring_begin_step", "ring_describe", "ring_free", "ring_init",
-           "ring_last_error", "ring_plan_from_state", "ring_plan_step",
-           "ring_query_geometry", "ring_read_mask", "ring_read_mask_swa", "ring_read_rows",
-           "ring_read_slot_pos", "ring_read_state", "ring_profile_enable",
-           "ring_profile_read", "RING_KERNEL_STEP", "RING_KERNEL_ATTN", "RING_KERNEL_MERGE"]
+__all__ = ["Ring", "RingConfig", "RingError", "RingGeometry", "RingKvWeights", "RingPlan",
+           "make_config", "ring_attn", "ring_begin_step", "ring_begin_step_mirror",
+           "ring_describe", "ring_free", "ring_init", "ring_last_error", "ring_mirror_write",
+           "ring_plan_from_state", "ring_plan_step", "ring_query_geometry", "ring_read_mask",
+           "ring_read_mask_swa", "ring_read_rows", "ring_read_slot_pos", "ring_read_state",
+           "ring_profile_enable", "ring_profile_read", "RING_KERNEL_STEP", "RING_KERNEL_ATTN",
+           "RING_KERNEL_MERGE", "RING_KERNEL_PROJ"]

@@ -38,6 +38,29 @@ struct StepArgs {
   int32_t n_pad;             // pad rows (fold-in only)
   int32_t cap, q_len, kv_total, n_head_kv, n_layer, trash_slot, n_tiles;
   int32_t do_mask;
+  // Rows from projected features instead of k_new / v_new (proj != nullptr):
+  // row i of this launch is the sum over the n_ds d-slices of
+  // proj[layer][ds][i][0 .. 2 kv_row) (K raw, then V), K normalised per KV
+  // head (RMS with eps, times k_norm[layer][dim]) before its rotation.
+  const float* proj;         // [n_layer][n_ds][kProjRows][2 * kv_row]
+  const float* k_norm;       // [n_layer][128]
+  double eps;
+  int32_t n_ds;
+};
+
+// Projection of new rows' K and V from fused features (one launch projects
+// at most kProjRows rows of every layer): raw K and V, in fp32, per d-slice
+// of kProjSlice feature dimensions, into the scratch the step kernel reads.
+constexpr int kProjRows = 64;
+constexpr int kProjSlice = 256;
+struct ProjArgs {
+  const uint16_t* mirror;    // this sequence's fused features [cap][d_model] F16, slot p % cap
+  const uint16_t* wk;        // [n_layer][kv_row][d_model] F16
+  const uint16_t* wv;        // [n_layer][kv_row][d_model] F16
+  float* scratch;            // [n_layer][n_ds][kProjRows][2 * kv_row]
+  int64_t pos0;              // position of this launch's row 0
+  int32_t n_rows;            // rows of this launch, 1..kProjRows
+  int32_t cap, d_model, kv_row, n_head_kv, n_layer, n_ds;
 };
 
 // One ring_attn launch over every sequence of the ring for one layer.
@@ -77,6 +100,7 @@ struct MergeArgs {
 hipError_t launch_step(const StepArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
+hipError_t launch_project(const ProjArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
 hipError_t launch_fill_u16(uint16_t* p, uint16_t value, int64_t n, hipStream_t s);
 
 }  // namespace ringkv

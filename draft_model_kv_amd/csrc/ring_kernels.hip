@@ -99,8 +99,10 @@ __global__ __launch_bounds__(256) void k_ring_step(StepArgs a) {
       const int idx = a.row0 + i;
       p = a.start + idx;
       slot = (int)(p % a.cap);
-      ksrc = a.k_new + ((int64_t)layer * a.n_new + idx) * kv_row;
-      vsrc = a.v_new + ((int64_t)layer * a.n_new + idx) * kv_row;
+      if (!a.proj) {
+        ksrc = a.k_new + ((int64_t)layer * a.n_new + idx) * kv_row;
+        vsrc = a.v_new + ((int64_t)layer * a.n_new + idx) * kv_row;
+      }
       if (t < 64) {
         double sn, cs;
         sincos((double)p * a.inv_freq[t], &sn, &cs);
@@ -123,6 +125,35 @@ __global__ __launch_bounds__(256) void k_ring_step(StepArgs a) {
         kd[k_frag_index(s_t, f + 64)] = 0;
         vd[v_frag_index(s_t, f)] = 0;
         vd[v_frag_index(s_t, f + 64)] = 0;
+      } else if (a.proj) {
+        // Row from projected features: sum the d-slices (fixed order), scale
+        // K to unit RMS over its KV head (the 64 lanes of this wave hold head
+        // h, two dims each) times k_norm, rotate, round once to F16.
+        const int64_t ds_stride = (int64_t)kProjRows * 2 * kv_row;
+        const float* pr = a.proj + ((int64_t)layer * a.n_ds * kProjRows + i) * 2 * kv_row +
+                          h * kHeadDim + f;
+        float xs = 0.0f, ys = 0.0f, vxs = 0.0f, vys = 0.0f;
+        for (int ds = 0; ds < a.n_ds; ++ds) {
+          const float* q = pr + ds * ds_stride;
+          xs += q[0];
+          ys += q[64];
+          vxs += q[kv_row];
+          vys += q[kv_row + 64];
+        }
+        double x = xs, y = ys;
+        double ss = x * x + y * y;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+        const double inv = 1.0 / sqrt(ss / (double)kHeadDim + a.eps);
+        x = x * inv * (double)a.k_norm[layer * kHeadDim + f];
+        y = y * inv * (double)a.k_norm[layer * kHeadDim + f + 64];
+        const double2 cs = cs_row[f];
+        double xr, yr;
+        rot_pair(x, y, cs.x, cs.y, xr, yr);
+        kd[k_frag_index(s_t, f)] = f64_to_f16_rne(xr);
+        kd[k_frag_index(s_t, f + 64)] = f64_to_f16_rne(yr);
+        vd[v_frag_index(s_t, f)] = __builtin_bit_cast(uint16_t, (_Float16)vxs);
+        vd[v_frag_index(s_t, f + 64)] = __builtin_bit_cast(uint16_t, (_Float16)vys);
       } else {
         const double x = f16_to_f64(ksrc[h * kHeadDim + f]);
         const double y = f16_to_f64(ksrc[h * kHeadDim + f + 64]);
@@ -932,6 +963,85 @@ __global__ __launch_bounds__(256) void k_ring_merge(MergeArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Projection of new rows from fused features: raw = W f for W = wk and wv of
+// every layer, on the matrix cores, one d-slice per work-group.
+//   Work-group (layer, head part hp, d-slice ds, 32-row tile rt): hp < n_head_kv
+//   is K head hp, else V head hp - n_head_kv; wave w computes its 32 output
+//   dims [32 w, 32 w + 32) for the tile's rows over the slice's 256 feature
+//   dims.  The slice of the 32 feature rows is staged once in LDS (rows past
+//   n_rows repeat the last row and are never stored).  The sum over d is
+//   order-free, so each lane takes 64 contiguous bytes of its W row and of
+//   its feature row per 64-d block: MFMA step j of a block pairs, for both
+//   operands, dims 64 blk + 32 (lane / 32) + 8 j + e.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_ring_project(ProjArgs a) {
+  constexpr int kRowStride = kProjSlice / 8 + 1;  // half8 per staged row (+1: no bank conflicts)
+  __shared__ half8 f_lds[32 * kRowStride];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n_rt = (a.n_rows + 31) >> 5;
+  int b = blockIdx.x;
+  const int rt = b % n_rt;
+  b /= n_rt;
+  const int ds = b % a.n_ds;
+  b /= a.n_ds;
+  const int n_hp = 2 * a.n_head_kv;
+  const int hp = b % n_hp;
+  const int layer = b / n_hp;
+  const int r0 = rt * 32;
+  const int d0 = ds * kProjSlice;
+
+  // weights: row 32 w + lane % 32 of the head part, 4 blocks x 64 B
+  const bool is_v = hp >= a.n_head_kv;
+  const int head = is_v ? hp - a.n_head_kv : hp;
+  const uint16_t* wrow = (is_v ? a.wv : a.wk) +
+                         ((int64_t)layer * a.kv_row + head * kHeadDim + 32 * wave + (lane & 31)) *
+                             a.d_model +
+                         d0 + 32 * (lane >> 5);
+  half8 wa[4][4];
+#pragma unroll
+  for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) wa[blk][j] = *(const half8*)(wrow + blk * 64 + 8 * j);
+
+  // features of the tile's rows: 32 rows x 32 chunks of 16 B, 4 per thread
+  half8 fv[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int c = threadIdx.x + 256 * k;
+    const int row = c >> 5, dc = c & 31;
+    const int64_t pos = a.pos0 + min(r0 + row, a.n_rows - 1);
+    const uint16_t* src = a.mirror + (pos % a.cap) * a.d_model + d0 + 8 * dc;
+    fv[k] = *(const half8*)src;
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int c = threadIdx.x + 256 * k;
+    f_lds[(c >> 5) * kRowStride + (c & 31)] = fv[k];
+  }
+  lds_barrier();
+
+  f32x16 acc = {};
+  const half8* frow = f_lds + (lane & 31) * kRowStride + 4 * (lane >> 5);
+#pragma unroll
+  for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc = mfma32(wa[blk][j], frow[blk * 8 + j], acc);
+
+  // acc[r] = raw[out dim 8 (r / 4) + 4 (lane / 32) + r % 4][row lane % 32]
+  const int n = r0 + (lane & 31);
+  if (n < a.n_rows) {
+    float* dst = a.scratch +
+                 (((int64_t)layer * a.n_ds + ds) * kProjRows + n) * 2 * a.kv_row +
+                 hp * kHeadDim + 32 * wave + 4 * (lane >> 5);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *(float4*)(dst + 8 * q) = make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2],
+                                            acc[4 * q + 3]);
+  }
+}
+
 __global__ void k_fill_u16(uint16_t* p, uint16_t value, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = value;
@@ -981,6 +1091,13 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t s, hipEvent_t t0, hipEve
   } else {
     hipExtLaunchKernelGGL(k_ring_merge<16>, grid, block, 0, s, t0, t1, 0, a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_project(const ProjArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+  if (a.n_rows <= 0) return hipSuccess;
+  const int grid = a.n_layer * 2 * a.n_head_kv * a.n_ds * ((a.n_rows + 31) / 32);
+  hipExtLaunchKernelGGL(k_ring_project, dim3(grid), dim3(256), 0, s, t0, t1, 0, a);
   return hipGetLastError();
 }
 

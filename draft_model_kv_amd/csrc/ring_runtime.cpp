@@ -48,6 +48,8 @@ struct Layout {
   size_t off_k = 0, off_v = 0, off_slot = 0, off_mask = 0, off_mask_swa = 0, off_rope = 0,
          off_ropeq = 0, off_freq = 0;
   size_t off_pacc = 0, off_pml = 0, total = 0;
+  int32_t n_ds = 0;                       // d-slices of the projection
+  size_t off_mirror = 0, off_proj = 0;    // feature mirror, projection scratch
 };
 
 constexpr int kMaxSplits = 64;  // each merge wave holds up to 16 splits in registers
@@ -96,6 +98,9 @@ int validate(const ring_config* c) {
     return fail(RING_EINVAL, "swa_window and swa_layers must both be zero or both non-zero");
   if (c->n_layer < 64 && (c->swa_layers >> c->n_layer) != 0)
     return fail(RING_EINVAL, "swa_layers names a layer >= n_layer %d", c->n_layer);
+  if (c->d_model < 0 || c->d_model > 65536 || c->d_model % kProjSlice != 0)
+    return fail(RING_EINVAL, "d_model %d must be a multiple of %d in [0, 65536]", c->d_model,
+                kProjSlice);
   return RING_OK;
 }
 
@@ -131,6 +136,9 @@ void geometry_of(const ring_config& c, ring_geometry* g, Layout* L) {
   const size_t n_part = L->n_split > 1 ? (size_t)c.n_seq * c.n_head_kv * L->n_split * L->mpad : 0;
   L->off_pacc = take(n_part * kHeadDim * 4);
   L->off_pml = take(n_part * 2 * 4);
+  L->n_ds = c.d_model / kProjSlice;
+  L->off_mirror = take((size_t)c.n_seq * c.cap * c.d_model * 2);
+  L->off_proj = take((size_t)c.n_layer * L->n_ds * kProjRows * 2 * g->kv_row * 4);
   L->total = off;
   g->workspace_bytes = (int64_t)L->total;
 }
@@ -173,13 +181,16 @@ struct ring {
   double* inv_freq = nullptr;
   float* part_acc = nullptr;
   float* part_ml = nullptr;
+  uint16_t* mirror = nullptr;   // fused features [n_seq][cap][d_model], or nullptr
+  float* proj = nullptr;        // projection scratch
   std::vector<int64_t> next_pos, held_lo, committed;
+  std::vector<std::vector<int64_t>> mirror_pos;  // per sequence: position in each mirror slot, -1 empty
   std::vector<double> inv_freq_host;
   hipStream_t last_stream = nullptr;
   // profiling: per kernel kind, event pairs (start, end) and how many are used
   int32_t prof_max = 0;
-  std::vector<hipEvent_t> prof_ev[3];
-  int32_t prof_used[3] = {0, 0, 0};
+  std::vector<hipEvent_t> prof_ev[4];
+  int32_t prof_used[4] = {0, 0, 0, 0};
 };
 
 namespace {
@@ -228,7 +239,7 @@ void destroy_events(ring* r) {
     v.clear();
   }
   r->prof_max = 0;
-  r->prof_used[0] = r->prof_used[1] = r->prof_used[2] = 0;
+  for (int32_t& u : r->prof_used) u = 0;
 }
 
 int check_launch(hipError_t e, const char* what) {
@@ -293,6 +304,11 @@ int ring_init(const ring_config* cfg, void* workspace, size_t workspace_bytes, v
   r->inv_freq = reinterpret_cast<double*>(r->ws + r->L.off_freq);
   r->part_acc = reinterpret_cast<float*>(r->ws + r->L.off_pacc);
   r->part_ml = reinterpret_cast<float*>(r->ws + r->L.off_pml);
+  if (cfg->d_model > 0) {
+    r->mirror = reinterpret_cast<uint16_t*>(r->ws + r->L.off_mirror);
+    r->proj = reinterpret_cast<float*>(r->ws + r->L.off_proj);
+    r->mirror_pos.assign(cfg->n_seq, std::vector<int64_t>(cfg->cap, -1));
+  }
   r->next_pos.assign(cfg->n_seq, 0);
   r->held_lo.assign(cfg->n_seq, 0);
   r->committed.assign(cfg->n_seq, 0);
@@ -420,6 +436,109 @@ int ring_begin_step(ring_t* r, int32_t seq, int64_t committed, const void* k_new
   return ok();
 }
 
+int ring_mirror_write(ring_t* r, int32_t seq, int64_t pos0, int64_t n, const void* features,
+                      void* stream) {
+  if (!r) return fail(RING_EINVAL, "ring is NULL");
+  if (!r->mirror) return fail(RING_ESTATE, "the ring has no feature mirror (d_model = 0)");
+  if (seq < 0 || seq >= r->cfg.n_seq) return fail(RING_ERANGE, "seq %d out of range", seq);
+  if (pos0 < 0 || n < 0 || pos0 + n + r->cfg.q_len > INT32_MAX)
+    return fail(RING_ERANGE, "positions [%lld, %lld) out of range", (long long)pos0,
+                (long long)(pos0 + n));
+  if (n == 0) return ok();
+  if (!features) return fail(RING_EINVAL, "features is NULL");
+  if (int e = use_device(r)) return e;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  r->last_stream = s;
+  // Only the last cap rows can stay: earlier ones share their slots with later ones.
+  const int64_t cap = r->cfg.cap, d = r->cfg.d_model;
+  const int64_t skip = std::max<int64_t>(0, n - cap);
+  const int64_t first = pos0 + skip, m = n - skip;
+  const int64_t s0 = first % cap;
+  const int64_t piece1 = std::min<int64_t>(m, cap - s0);
+  const uint8_t* src = static_cast<const uint8_t*>(features) + skip * d * 2;
+  uint16_t* base = r->mirror + (int64_t)seq * cap * d;
+  hipError_t e = hipMemcpyAsync(base + s0 * d, src, (size_t)(piece1 * d * 2),
+                                hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess && m > piece1)
+    e = hipMemcpyAsync(base, src + piece1 * d * 2, (size_t)((m - piece1) * d * 2),
+                       hipMemcpyDeviceToDevice, s);
+  if (e != hipSuccess) return fail(RING_EDEVICE, "mirror copy: %s", hipGetErrorString(e));
+  std::vector<int64_t>& mp = r->mirror_pos[seq];
+  for (int64_t p = first; p < pos0 + n; ++p) mp[p % cap] = p;
+  return ok();
+}
+
+int ring_begin_step_mirror(ring_t* r, int32_t seq, int64_t committed, const ring_kv_weights* w,
+                           void* stream) {
+  if (!r) return fail(RING_EINVAL, "ring is NULL");
+  if (!r->mirror) return fail(RING_ESTATE, "the ring has no feature mirror (d_model = 0)");
+  if (seq < 0 || seq >= r->cfg.n_seq) return fail(RING_ERANGE, "seq %d out of range", seq);
+  if (committed < 0 || committed + r->cfg.q_len > INT32_MAX)
+    return fail(RING_ERANGE, "committed %lld out of range", (long long)committed);
+  if (!w || !w->wk || !w->wv || !w->k_norm) return fail(RING_EINVAL, "weights are NULL");
+  if (((reinterpret_cast<uintptr_t>(w->wk) | reinterpret_cast<uintptr_t>(w->wv)) & 15) ||
+      (reinterpret_cast<uintptr_t>(w->k_norm) & 3))
+    return fail(RING_EINVAL, "wk / wv must be 16-byte and k_norm 4-byte aligned");
+  if (!(w->eps >= 0.0f) || !std::isfinite(w->eps)) return fail(RING_EINVAL, "eps must be finite and >= 0");
+  const Plan p = plan_of(r->cfg.cap, r->geo.a_step, committed, r->next_pos[seq], r->held_lo[seq]);
+  const std::vector<int64_t>& mp = r->mirror_pos[seq];
+  for (int64_t q = p.start; q < committed; ++q)
+    if (mp[q % r->cfg.cap] != q)
+      return fail(RING_ESTATE, "position %lld is not in the feature mirror (write it first)",
+                  (long long)q);
+  if (int e = use_device(r)) return e;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  r->last_stream = s;
+
+  StepArgs a = step_args(r, seq);
+  a.start = p.start;
+  a.start_mod = (int32_t)(p.start % r->cfg.cap);
+  a.committed = committed;
+  a.lo = p.lo;
+  a.swa_lo = committed - std::min<int64_t>(r->cfg.swa_window, p.win);
+  a.n_new = (int32_t)p.n_new;
+  a.proj = r->proj;
+  a.k_norm = w->k_norm;
+  a.eps = (double)w->eps;
+  a.n_ds = r->L.n_ds;
+  ProjArgs pa{};
+  pa.mirror = r->mirror + (int64_t)seq * r->cfg.cap * r->cfg.d_model;
+  pa.wk = static_cast<const uint16_t*>(w->wk);
+  pa.wv = static_cast<const uint16_t*>(w->wv);
+  pa.scratch = r->proj;
+  pa.cap = r->cfg.cap;
+  pa.d_model = r->cfg.d_model;
+  pa.kv_row = r->geo.kv_row;
+  pa.n_head_kv = r->cfg.n_head_kv;
+  pa.n_layer = r->cfg.n_layer;
+  pa.n_ds = r->L.n_ds;
+  // Rows go in launches of at most kProjRows (projection, then the append
+  // that normalises, rotates and stores them); a fold-in is one such pair
+  // with its pad rows, and the last pair of a step also rebuilds the mask.
+  int64_t row0 = 0;
+  do {
+    const int32_t n = (int32_t)std::min<int64_t>(kProjRows, p.n_new - row0);
+    pa.pos0 = p.start + row0;
+    pa.n_rows = n;
+    hipEvent_t t0, t1;
+    if (n > 0) {
+      next_events(r, RING_KERNEL_PROJ, &t0, &t1);
+      if (int e = check_launch(launch_project(pa, s, t0, t1), "projection")) return e;
+    }
+    a.row0 = (int32_t)row0;
+    a.n_rows = n;
+    a.n_pad = p.bulk ? 0 : r->geo.a_step - n;
+    a.do_mask = row0 + n >= p.n_new;
+    next_events(r, RING_KERNEL_STEP, &t0, &t1);
+    if (int e = check_launch(launch_step(a, s, t0, t1), "append from features")) return e;
+    row0 += n;
+  } while (row0 < p.n_new);
+  r->next_pos[seq] = committed;
+  r->held_lo[seq] = p.lo;
+  r->committed[seq] = committed;
+  return ok();
+}
+
 int ring_attn(ring_t* r, int32_t layer, const void* q, const void* k_noise, const void* v_noise,
               float* out, void* stream) {
   if (!r) return fail(RING_EINVAL, "ring is NULL");
@@ -540,8 +659,13 @@ int ring_describe(const ring_t* r, char* buf, size_t len) {
                          "%.1f MiB per seq, splits=%d",
                          r->cfg.cap, r->geo.kv_total, r->geo.a_step, r->cfg.n_layer, r->cfg.n_seq,
                          mib, r->L.n_split);
+  if (r->cfg.d_model > 0 && n > 0 && (size_t)n < len) {
+    const size_t used = strlen(buf);
+    snprintf(buf + used, len - used, ", feature mirror d_model=%d", r->cfg.d_model);
+  }
   if (r->cfg.swa_window > 0 && n > 0 && (size_t)n < len)
-    snprintf(buf + n, len - n, ", swa_window=%d swa_layers=0x%llx", r->cfg.swa_window,
+    snprintf(buf + strlen(buf), len - strlen(buf), ", swa_window=%d swa_layers=0x%llx",
+             r->cfg.swa_window,
              (unsigned long long)r->cfg.swa_layers);
   return ok();
 }
@@ -646,7 +770,7 @@ int ring_profile_enable(ring_t* r, int32_t max_launches) {
 }
 
 int ring_profile_read(ring_t* r, int32_t kernel, int32_t* n_launches, double* total_ms) {
-  if (!r || !n_launches || !total_ms || kernel < 0 || kernel > 2)
+  if (!r || !n_launches || !total_ms || kernel < 0 || kernel > 3)
     return fail(RING_EINVAL, "bad argument");
   if (int e = use_device(r)) return e;
   double total = 0.0;

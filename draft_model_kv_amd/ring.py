@@ -30,12 +30,13 @@ RING_MAX_SEQ = 64
 # Every function the header declares, in header order.
 EXPORTS = (
     "ring_query_geometry", "ring_init", "ring_plan_step", "ring_plan_from_state",
-    "ring_begin_step", "ring_attn", "ring_free", "ring_last_error", "ring_describe",
+    "ring_begin_step", "ring_mirror_write", "ring_begin_step_mirror", "ring_attn", "ring_free",
+    "ring_last_error", "ring_describe",
     "ring_read_slot_pos", "ring_read_mask", "ring_read_mask_swa", "ring_read_rows",
     "ring_read_state",
     "ring_profile_enable", "ring_profile_read",
 )
-RING_KERNEL_STEP, RING_KERNEL_ATTN, RING_KERNEL_MERGE = 0, 1, 2
+RING_KERNEL_STEP, RING_KERNEL_ATTN, RING_KERNEL_MERGE, RING_KERNEL_PROJ = 0, 1, 2, 3
 
 
 class RingConfig(ctypes.Structure):
@@ -43,7 +44,13 @@ class RingConfig(ctypes.Structure):
                 ("n_head", ctypes.c_int32), ("n_head_kv", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("n_layer", ctypes.c_int32),
                 ("n_seq", ctypes.c_int32), ("rope_base", ctypes.c_float),
-                ("swa_window", ctypes.c_int32), ("swa_layers", ctypes.c_uint64)]
+                ("swa_window", ctypes.c_int32), ("swa_layers", ctypes.c_uint64),
+                ("d_model", ctypes.c_int32)]
+
+
+class RingKvWeights(ctypes.Structure):
+    _fields_ = [("wk", ctypes.c_void_p), ("wv", ctypes.c_void_p), ("k_norm", ctypes.c_void_p),
+                ("eps", ctypes.c_float)]
 
 
 class RingGeometry(ctypes.Structure):
@@ -88,6 +95,8 @@ def _load() -> ctypes.CDLL:
         "ring_plan_from_state": [ctypes.POINTER(RingConfig), I64, I64, I64,
                                  ctypes.POINTER(RingPlan), P],
         "ring_begin_step": [P, I32, I64, P, P, I64, P],
+        "ring_mirror_write": [P, I32, I64, I64, P, P],
+        "ring_begin_step_mirror": [P, I32, I64, ctypes.POINTER(RingKvWeights), P],
         "ring_attn": [P, I32, P, P, P, P, P],
         "ring_free": [P],
         "ring_last_error": [],
@@ -120,9 +129,9 @@ def ring_last_error() -> str:
 
 
 def make_config(cap, q_len=8, n_head=32, n_head_kv=8, head_dim=128, n_layer=1,
-                n_seq=1, rope_base=1.0e6, swa_window=0, swa_layers=0) -> RingConfig:
+                n_seq=1, rope_base=1.0e6, swa_window=0, swa_layers=0, d_model=0) -> RingConfig:
     return RingConfig(cap, q_len, n_head, n_head_kv, head_dim, n_layer, n_seq, rope_base,
-                      swa_window, swa_layers)
+                      swa_window, swa_layers, d_model)
 
 
 def ring_query_geometry(cfg: RingConfig) -> RingGeometry:
@@ -164,6 +173,19 @@ def ring_begin_step(handle: int, seq: int, committed: int, k_new: int, v_new: in
                     n_rows: int, stream: int = 0) -> None:
     _check(_lib.ring_begin_step(handle, seq, committed, k_new or None, v_new or None,
                                 n_rows, stream or None), "ring_begin_step")
+
+
+def ring_mirror_write(handle: int, seq: int, pos0: int, n: int, features: int,
+                      stream: int = 0) -> None:
+    _check(_lib.ring_mirror_write(handle, seq, pos0, n, features or None, stream or None),
+           "ring_mirror_write")
+
+
+def ring_begin_step_mirror(handle: int, seq: int, committed: int, wk: int, wv: int, k_norm: int,
+                           eps: float, stream: int = 0) -> None:
+    w = RingKvWeights(wk or None, wv or None, k_norm or None, eps)
+    _check(_lib.ring_begin_step_mirror(handle, seq, committed, ctypes.byref(w), stream or None),
+           "ring_begin_step_mirror")
 
 
 def ring_attn(handle: int, layer: int, q: int, k_noise: int, v_noise: int, out: int,
@@ -236,11 +258,11 @@ class Ring:
     """
 
     def __init__(self, cap, q_len=8, n_head=32, n_head_kv=8, head_dim=128, n_layer=1,
-                 n_seq=1, rope_base=1.0e6, device=None, swa_window=0, swa_layers=0):
+                 n_seq=1, rope_base=1.0e6, device=None, swa_window=0, swa_layers=0, d_model=0):
         import torch
         self._torch = torch
         self.cfg = make_config(cap, q_len, n_head, n_head_kv, head_dim, n_layer, n_seq, rope_base,
-                               swa_window, swa_layers)
+                               swa_window, swa_layers, d_model)
         self.geo = ring_query_geometry(self.cfg)
         self.device = torch.device(device or "cuda")
         self.workspace = torch.empty(self.geo.workspace_bytes + 256, dtype=torch.uint8,
@@ -274,6 +296,25 @@ class Ring:
         ring_begin_step(self.handle, seq, committed,
                         self._ptr(k_new, torch.float16, shape, "k_new"),
                         self._ptr(v_new, torch.float16, shape, "v_new"), n, self._stream())
+
+    def mirror_write(self, seq: int, pos0: int, features) -> None:
+        """features: F16 [n, d_model] of positions [pos0, pos0 + n)."""
+        torch = self._torch
+        n = features.shape[0]
+        ring_mirror_write(self.handle, seq, pos0, n,
+                          self._ptr(features, torch.float16, (n, self.cfg.d_model), "features"),
+                          self._stream())
+
+    def begin_step_mirror(self, seq: int, committed: int, wk, wv, k_norm, eps: float) -> None:
+        """wk, wv: F16 [n_layer, kv_row, d_model]; k_norm: F32 [n_layer, head_dim]."""
+        torch = self._torch
+        c = self.cfg
+        wshape = (c.n_layer, self.geo.kv_row, c.d_model)
+        ring_begin_step_mirror(self.handle, seq, committed,
+                               self._ptr(wk, torch.float16, wshape, "wk"),
+                               self._ptr(wv, torch.float16, wshape, "wv"),
+                               self._ptr(k_norm, torch.float32, (c.n_layer, c.head_dim), "k_norm"),
+                               eps, self._stream())
 
     def attn(self, layer: int, q, k_noise, v_noise, out=None):
         torch = self._torch

@@ -60,7 +60,12 @@ extern "C" {
  *              causal (noise row i sees noise slots j <= i).  0 = no such
  *              layers; else >= 1, and swa_layers must be non-zero.
  *   swa_layers bit l set: layer l attends with that mask; only bits below
- *              min(n_layer, 64) may be set; 0 when swa_window is 0.         */
+ *              min(n_layer, 64) may be set; 0 when swa_window is 0.
+ *   d_model    width of the fused feature vector the draft's K/V projection
+ *              reads (the page's notes on the port: Luce keeps a mirror of
+ *              the target's features whose capacity is the ring's, and
+ *              begin_step computes the new rows' K/V from it).  0 = no
+ *              feature mirror; else a multiple of 256, at most 65536.       */
 typedef struct ring_config {
   int32_t cap;
   int32_t q_len;
@@ -72,6 +77,7 @@ typedef struct ring_config {
   float rope_base;
   int32_t swa_window;   /* sliding-window layers' window; 0 = none        */
   uint64_t swa_layers;  /* bit l set: layer l is a sliding-window layer   */
+  int32_t d_model;      /* fused feature width of the mirror; 0 = none    */
 } ring_config;
 
 /* Derived geometry (section 1.1 of the page):
@@ -165,6 +171,52 @@ int ring_begin_step(ring_t* r, int32_t seq, int64_t committed,
                     const void* k_new, const void* v_new, int64_t n_rows,
                     void* stream);
 
+/* ---- New rows from fused features (feature mirror + K/V projection) ----
+ * The page's notes on the port describe Luce's begin_step: the draft keeps a
+ * mirror of the target's fused feature vectors with the ring's capacity
+ * (section 1.6: the ring capacity is the mirror's), and the context K/V of
+ * each new position are computed from it per layer as the shallow injection
+ * wk/wv @ fused + k_norm + rope (the test log's list of refuted hypotheses,
+ * item 4).  Both need a ring created with d_model > 0.                      */
+
+/* Projection weights of every layer, device memory:
+ *   wk, wv   F16 [n_layer][kv_row][d_model] (output dim first, feature dim
+ *            contiguous), 16-byte aligned
+ *   k_norm   F32 [n_layer][head_dim], the learned weight of the K norm
+ *   eps      epsilon of the K norm (>= 0)
+ * For a position p with fused features f: k = wk f, v = wv f; each KV head's
+ * 128 values of k are divided by sqrt(mean of their squares + eps) and
+ * multiplied by k_norm; K is then rotated at p (the ring's RoPE) and both are
+ * rounded once to F16.  The products accumulate in fp32 on the matrix cores;
+ * norm and rotation are done in fp64.                                       */
+typedef struct ring_kv_weights {
+  const void* wk;
+  const void* wv;
+  const float* k_norm;
+  float eps;
+} ring_kv_weights;
+
+/* Store the fused features of positions [pos0, pos0 + n) of sequence `seq`
+ * in its mirror: position p goes to mirror slot p % cap (when n > cap only
+ * the last cap rows can stay and only those are copied).
+ *   features  device F16 [n][d_model]
+ * The mirror then holds, for each slot, the position last written to it.
+ * Errors: RING_ESTATE (no mirror), RING_ERANGE (seq, positions),
+ * RING_EINVAL (NULL), RING_EDEVICE.                                         */
+int ring_mirror_write(ring_t* r, int32_t seq, int64_t pos0, int64_t n,
+                      const void* features, void* stream);
+
+/* ring_begin_step with the new rows computed from the mirror: the same plan
+ * (positions [start, committed)), every one of which the mirror must hold
+ * (else RING_ESTATE before any device work: after a rewind that re-appends
+ * the whole window, write the positions the mirror lost again), projected
+ * through `w` for every layer as described above and appended like
+ * ring_begin_step's rows (pads, slot_pos, masks and noise RoPE table alike).
+ * Errors: RING_ESTATE (no mirror, position missing), RING_ERANGE,
+ * RING_EINVAL (NULL weights, alignment, eps), RING_EDEVICE.                 */
+int ring_begin_step_mirror(ring_t* r, int32_t seq, int64_t committed,
+                           const ring_kv_weights* w, void* stream);
+
 /* Masked GQA attention of the noise block of every sequence over its ring
  * (one draft layer), section 1.4 masks: the full mask with the noise block
  * visible both ways, or for a sliding-window layer its mask, reading only
@@ -217,12 +269,15 @@ int ring_read_state(const ring_t* r, int32_t seq, int64_t* next_pos,
                     int64_t* held_lo);
 
 /* ---- Profiling ----
- * Kernel kinds: RING_KERNEL_STEP (append + mask launches of ring_begin_step),
- * RING_KERNEL_ATTN (attention launch of ring_attn), RING_KERNEL_MERGE
- * (cross-split merge launch of ring_attn, absent when one split suffices). */
+ * Kernel kinds: RING_KERNEL_STEP (append + mask launches of ring_begin_step
+ * and ring_begin_step_mirror), RING_KERNEL_ATTN (attention launch of
+ * ring_attn), RING_KERNEL_MERGE (cross-split merge launch of ring_attn,
+ * absent when one split suffices), RING_KERNEL_PROJ (projection launches of
+ * ring_begin_step_mirror).                                                  */
 #define RING_KERNEL_STEP  0
 #define RING_KERNEL_ATTN  1
 #define RING_KERNEL_MERGE 2
+#define RING_KERNEL_PROJ  3
 
 /* Time the next `max_launches` launches of each kernel kind with HIP events
  * bound to the dispatch itself (kernel start to kernel end, no launch gaps).

@@ -139,3 +139,19 @@ def test_ring_init_without_device_fails_cleanly():
     with pytest.raises(rk.RingError) as e:
         rk.ring_init(rk.make_config(64))
     assert e.value.code == rk.RING_EDEVICE
+
+
+@pytest.mark.parametrize("d_model", [-256, 100, 255, 65536 + 256])
+def test_invalid_mirror_width_rejected(d_model):
+    with pytest.raises(rk.RingError) as e:
+        rk.ring_query_geometry(rk.make_config(64, d_model=d_model))
+    assert e.value.code == rk.RING_EINVAL
+
+
+def test_feature_mirror_sizes_the_workspace():
+    """A feature mirror adds cap * d_model F16 per sequence plus the fp32
+    projection scratch (n_layer * d_model / 256 slices of 64 rows x 2 kv_row)."""
+    base = rk.ring_query_geometry(rk.make_config(4096, n_layer=5, n_seq=2))
+    g = rk.ring_query_geometry(rk.make_config(4096, n_layer=5, n_seq=2, d_model=2048))
+    need = 2 * 4096 * 2048 * 2 + 5 * (2048 // 256) * 64 * 2 * 1024 * 4
+    assert need <= g.workspace_bytes - base.workspace_bytes <= need + 512

@@ -28,6 +28,7 @@ ACCEPT_SHARES = (24.5, 19.5, 15.0, 9.9, 7.7, 5.0, 3.6, 14.7)
 # Tensor tags used in the value keys.
 T_K, T_V, T_Q, T_KN, T_VN = 1, 2, 3, 4, 5
 T_ACC, T_START, T_OUTLIER = 10, 11, 12
+T_FEAT, T_WK, T_WV, T_KNORM = 20, 21, 22, 23
 
 
 @dataclass(frozen=True)
@@ -54,6 +55,7 @@ class Workload:
     forced_starts: Tuple[Tuple[int, int, int], ...] = field(default_factory=tuple)
     swa_window: int = 0         # sliding-window layers' window (0: none)
     swa_layers: int = 0         # bit l set: layer l is a sliding-window layer
+    d_model: int = 0            # fused feature width (0: rows supplied directly)
 
     @property
     def kv_row(self) -> int:
@@ -84,6 +86,13 @@ WORKLOADS: Dict[str, Workload] = {
     "swa_stream": Workload(
         name="swa_stream", seed=5, cap=4096, n_layer=4, prefill=4096, n_steps=600,
         swa_window=1024, swa_layers=0b1010),
+    # new rows computed from a feature mirror through synthetic projection
+    # weights; d_model = 2048 is the hidden size of the DFlash draft that the
+    # ring notes convert (6 dense layers, hidden 2048); 5 layers as in the
+    # Luce log line of the same notes
+    "mirror_stream": Workload(
+        name="mirror_stream", seed=6, cap=4096, n_layer=5, prefill=4096, n_steps=600,
+        d_model=2048),
 }
 
 
@@ -181,3 +190,36 @@ def n_warmup_steps(w: Workload) -> int:
     if w.prefill_step > 0:
         return -(-start_positions(w)[0] // w.prefill_step)
     return 1
+
+
+def fused_features(w: Workload, seq: int, positions, epoch: int = 0) -> np.ndarray:
+    """Fused feature vectors ``[len(positions), d_model]`` F16, N(0, 1).
+
+    Like the context rows, a position's features depend only on (seed, seq,
+    epoch, position).
+    """
+    positions = np.asarray(positions, dtype=np.int64).reshape(-1)
+    keys = rng.row_keys(rng.key_of(w.seed, seq, T_FEAT, epoch), positions)
+    return (rng.normal(keys, w.d_model)).astype(np.float16)
+
+
+def projection_weights(w: Workload):
+    """Synthetic projection weights of every layer.
+
+    ``wk``, ``wv``: F16 ``[n_layer, kv_row, d_model]`` drawn N(0, sigma^2 / d_model)
+    so that V = wv f has the workload's sigma for N(0, 1) features;
+    ``k_norm``: F32 ``[n_layer, head_dim]`` drawn 1 + 0.1 N(0, 1).
+    """
+    rows = np.arange(w.kv_row, dtype=np.int64)
+    scale = w.sigma / np.sqrt(w.d_model)
+    wk = np.empty((w.n_layer, w.kv_row, w.d_model), np.float16)
+    wv = np.empty((w.n_layer, w.kv_row, w.d_model), np.float16)
+    kn = np.empty((w.n_layer, w.head_dim), np.float32)
+    for layer in range(w.n_layer):
+        wk[layer] = (rng.normal(rng.row_keys(rng.key_of(w.seed, layer, T_WK), rows), w.d_model)
+                     * scale).astype(np.float16)
+        wv[layer] = (rng.normal(rng.row_keys(rng.key_of(w.seed, layer, T_WV), rows), w.d_model)
+                     * scale).astype(np.float16)
+        kn[layer] = (1.0 + 0.1 * rng.normal(np.array([rng.key_of(w.seed, layer, T_KNORM)],
+                                                     dtype=np.uint64), w.head_dim)[0])
+    return wk, wv, kn
