@@ -132,10 +132,13 @@ def prepare(w, pool: int, total: int, dev):
     s = torch.cuda.current_stream(dev).cuda_stream
     mirror = w.d_model > 0
     if mirror:
+        # one copy of the projection weights per ring of the pool, so that a
+        # step reads its weights from HBM as it would in a decode where the
+        # target model runs between draft steps
         wk, wv, kn = W.projection_weights(w)
-        weights = (torch.from_numpy(wk).to(dev), torch.from_numpy(wv).to(dev),
-                   torch.from_numpy(kn).to(dev))
-        wptr = (weights[0].data_ptr(), weights[1].data_ptr(), weights[2].data_ptr(), RMS_EPS)
+        weights = [(torch.from_numpy(wk).to(dev), torch.from_numpy(wv).to(dev),
+                    torch.from_numpy(kn).to(dev)) for _ in range(pool)]
+        wptrs = [(a.data_ptr(), b.data_ptr(), c.data_ptr(), RMS_EPS) for a, b, c in weights]
 
     def feats(seq, lo, hi):
         return torch.from_numpy(W.fused_features(w, seq, np.arange(lo, hi))).to(dev)
@@ -154,9 +157,9 @@ def prepare(w, pool: int, total: int, dev):
             plan, _ = rings[0].plan(seq, c)
             if mirror:
                 f = feats(seq, prev[seq], c)
-                for r in rings:
+                for r, wp in zip(rings, wptrs):
                     R.ring_mirror_write(r.handle, seq, prev[seq], c - prev[seq], f.data_ptr(), s)
-                    R.ring_begin_step_mirror(r.handle, seq, c, *wptr, s)
+                    R.ring_begin_step_mirror(r.handle, seq, c, *wp, s)
                 torch.cuda.synchronize(dev)
                 prev[seq] = c
                 del f
@@ -196,10 +199,11 @@ def prepare(w, pool: int, total: int, dev):
             sq = [(seq, c, k.data_ptr(), v.data_ptr(), n) for seq, c, k, v, n in seqs]
         calls.append((r.handle, sq,
                       [(layer, q.data_ptr(), kn.data_ptr(), vn.data_ptr())
-                       for layer, q, kn, vn in layers]))
+                       for layer, q, kn, vn in layers],
+                      wptrs[t % pool] if mirror else None))
     committed = [[streams[seq][n_warm + t // pool] for seq in range(w.n_seq)]
                  for t in range(total)]
-    extra = (weights, wptr) if mirror else None
+    extra = weights if mirror else None
     return rings, calls, (steps_in, extra), committed
 
 
@@ -395,6 +399,9 @@ def main() -> int:
                                               w.head_dim, w.n_layer, w.n_seq, w.rope_base,
                                               d_model=w.d_model))
     ring_bytes = w.n_seq * w.n_layer * geo.kv_bytes_per_layer
+    if w.d_model:
+        # each pool member also holds its feature mirror and weight copy
+        ring_bytes += w.n_seq * w.cap * w.d_model * 2 + 2 * w.n_layer * w.kv_row * w.d_model * 2
     pool = args.pool or max(1, -(-(512 << 20) // ring_bytes))
     # warm-up, the timed steps, then as many steps again with per-kernel
     # timing events (they slow back-to-back launches, so they stay out of the
@@ -406,11 +413,10 @@ def main() -> int:
     begin, attn, optr = R.ring_begin_step, R.ring_attn, out.data_ptr()
     mirror = w.d_model > 0
     mwrite, mbegin = R.ring_mirror_write, R.ring_begin_step_mirror
-    wptr = steps_in[1][1] if mirror else None
 
     def run(lo, hi):
         for t in range(lo, hi):
-            h, seqs, layers = calls[t]
+            h, seqs, layers, wptr = calls[t]
             if mirror:
                 for seq, c, fp, c0, n in seqs:
                     mwrite(h, seq, c0, n, fp, s)

@@ -53,6 +53,7 @@ struct StepArgs {
 // of kProjSlice feature dimensions, into the scratch the step kernel reads.
 constexpr int kProjRows = 64;
 constexpr int kProjSlice = 256;
+constexpr int kProjMaxKvHeads = 16;   // KV heads a ring with a feature mirror may have
 struct ProjArgs {
   const uint16_t* mirror;    // this sequence's fused features [cap][d_model] F16, slot p % cap
   const uint16_t* wk;        // [n_layer][kv_row][d_model] F16

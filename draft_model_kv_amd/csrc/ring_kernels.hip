@@ -111,6 +111,26 @@ __global__ __launch_bounds__(256) void k_ring_step(StepArgs a) {
     } else {
       slot = a.trash_slot;
     }
+    // Row from projected features: the sum of the d-slices (fixed order) of
+    // every column, K then V, staged in LDS; all loads of a thread in flight
+    // together.
+    __shared__ float raw[2 * kProjMaxKvHeads * kHeadDim];
+    if (a.proj && !pad) {
+      const int n4 = 2 * kv_row / 4;
+      const int64_t ds4 = (int64_t)kProjRows * 2 * kv_row / 4;
+      const float4* pr =
+          (const float4*)(a.proj + ((int64_t)layer * a.n_ds * kProjRows + i) * 2 * kv_row);
+#pragma unroll 2
+      for (int c = t; c < n4; c += 256) {
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
+        for (int ds = 0; ds < a.n_ds; ++ds) {
+          const float4 v = pr[ds * ds4 + c];
+          acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+        }
+        ((float4*)raw)[c] = acc;
+      }
+    }
     lds_barrier();
     const int s_t = slot & (kTile - 1);
     const int64_t tile_off = (int64_t)(slot >> 5) * kTileHalves;
@@ -126,20 +146,10 @@ __global__ __launch_bounds__(256) void k_ring_step(StepArgs a) {
         vd[v_frag_index(s_t, f)] = 0;
         vd[v_frag_index(s_t, f + 64)] = 0;
       } else if (a.proj) {
-        // Row from projected features: sum the d-slices (fixed order), scale
-        // K to unit RMS over its KV head (the 64 lanes of this wave hold head
-        // h, two dims each) times k_norm, rotate, round once to F16.
-        const int64_t ds_stride = (int64_t)kProjRows * 2 * kv_row;
-        const float* pr = a.proj + ((int64_t)layer * a.n_ds * kProjRows + i) * 2 * kv_row +
-                          h * kHeadDim + f;
-        float xs = 0.0f, ys = 0.0f, vxs = 0.0f, vys = 0.0f;
-        for (int ds = 0; ds < a.n_ds; ++ds) {
-          const float* q = pr + ds * ds_stride;
-          xs += q[0];
-          ys += q[64];
-          vxs += q[kv_row];
-          vys += q[kv_row + 64];
-        }
+        // Scale K to unit RMS over its KV head (the 64 lanes of this wave
+        // hold head h, two dims each) times k_norm, rotate, round once to F16.
+        const float xs = raw[h * kHeadDim + f], ys = raw[h * kHeadDim + f + 64];
+        const float vxs = raw[kv_row + h * kHeadDim + f], vys = raw[kv_row + h * kHeadDim + f + 64];
         double x = xs, y = ys;
         double ss = x * x + y * y;
 #pragma unroll

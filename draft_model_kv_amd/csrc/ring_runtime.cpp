@@ -101,6 +101,8 @@ int validate(const ring_config* c) {
   if (c->d_model < 0 || c->d_model > 65536 || c->d_model % kProjSlice != 0)
     return fail(RING_EINVAL, "d_model %d must be a multiple of %d in [0, 65536]", c->d_model,
                 kProjSlice);
+  if (c->d_model > 0 && c->n_head_kv > kProjMaxKvHeads)
+    return fail(RING_EINVAL, "a feature mirror supports at most %d KV heads", kProjMaxKvHeads);
   return RING_OK;
 }
 

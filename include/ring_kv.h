@@ -65,7 +65,8 @@ extern "C" {
  *              reads (the page's notes on the port: Luce keeps a mirror of
  *              the target's features whose capacity is the ring's, and
  *              begin_step computes the new rows' K/V from it).  0 = no
- *              feature mirror; else a multiple of 256, at most 65536.       */
+ *              feature mirror; else a multiple of 256, at most 65536, and
+ *              then n_head_kv <= 16.                                        */
 typedef struct ring_config {
   int32_t cap;
   int32_t q_len;

@@ -155,3 +155,10 @@ def test_feature_mirror_sizes_the_workspace():
     g = rk.ring_query_geometry(rk.make_config(4096, n_layer=5, n_seq=2, d_model=2048))
     need = 2 * 4096 * 2048 * 2 + 5 * (2048 // 256) * 64 * 2 * 1024 * 4
     assert need <= g.workspace_bytes - base.workspace_bytes <= need + 512
+
+
+def test_mirror_needs_at_most_16_kv_heads():
+    rk.ring_query_geometry(rk.make_config(64, n_head=16, n_head_kv=16, d_model=256))
+    with pytest.raises(rk.RingError) as e:
+        rk.ring_query_geometry(rk.make_config(64, n_head=32, n_head_kv=32, d_model=256))
+    assert e.value.code == rk.RING_EINVAL
