@@ -361,6 +361,10 @@ def main() -> int:
     ap.add_argument("--pool", type=int, default=0,
                     help="independent rings cycled through (default: enough to exceed the "
                          "256 MB Infinity Cache; 1 = cache-warm)")
+    ap.add_argument("--step", choices=("eager", "fused"), default="eager",
+                    help="eager: ring_begin_step's own append launch (default); fused: "
+                         "ring_begin_step_deferred, the fold-in append and index rebuild "
+                         "run inside the attention launch")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--summarize", metavar="OUT", default="",
@@ -410,7 +414,9 @@ def main() -> int:
     rings, calls, steps_in, committed = prepare(w, pool, total, dev)
     s = torch.cuda.current_stream(dev).cuda_stream
     out = torch.empty((w.n_seq, w.q_len, w.n_head, w.head_dim), dtype=torch.float32, device=dev)
-    begin, attn, optr = R.ring_begin_step, R.ring_attn, out.data_ptr()
+    fused = args.step == "fused"
+    begin = R.ring_begin_step_deferred if fused else R.ring_begin_step
+    attn, optr = R.ring_attn, out.data_ptr()
     mirror = w.d_model > 0
     mwrite, mbegin = R.ring_mirror_write, R.ring_begin_step_mirror
 
@@ -471,6 +477,17 @@ def main() -> int:
                             for c in cs) for cs in seg for layer in range(w.n_layer)])
 
     per_launch = mean_bytes("attn_kernel")
+    if fused and not mirror:
+        # the fused launch also reads each new row (K and V, F16) and writes it
+        # to the ring, reads slot_pos instead of the mask, and (first layer of
+        # a step) writes slot_pos entries, the mask and the noise RoPE table
+        seg_rows = [sum(n for _, _, _, _, n in steps_in[0][t // pool][0])
+                    for t in range(args.warmup + args.steps, total)]
+        rows = float(np.mean(seg_rows))
+        per_launch += (rows * w.kv_row * 2 * 2 * 2 + w.n_seq * w.cap * 4
+                       - w.n_seq * w.q_len * geo.kv_total * 2
+                       + (w.n_seq * (w.q_len * geo.kv_total * 2 + w.q_len * 64 * 2 * 12)
+                          + rows * 4) / w.n_layer)
     per_call = mean_bytes("ring_attn")
     attn_us = prof["k_ring_attn"]["avg_us"]
     merge_us = prof["k_ring_merge"]["avg_us"] or 0.0
@@ -510,7 +527,7 @@ def main() -> int:
         "dtype": "f16",
         "data": "synthetic (seeded normal F16 rows; accepted counts drawn from the "
                 "pages' 1422-verification share table)",
-        "config": {"workload": args.workload, "cap": w.cap, "q_len": w.q_len,
+        "config": {"workload": args.workload, "step": args.step, "cap": w.cap, "q_len": w.q_len,
                    "n_head": w.n_head, "n_head_kv": w.n_head_kv, "head_dim": w.head_dim,
                    "n_layer": w.n_layer, "n_seq": w.n_seq, "kv_total": geo.kv_total,
                    "ring_pool": pool, "infinity_cache": "cold" if pool > 1 or ring_bytes > (256 << 20) else "warm",

@@ -38,6 +38,7 @@ struct StepArgs {
   int32_t n_pad;             // pad rows (fold-in only)
   int32_t cap, q_len, kv_total, n_head_kv, n_layer, trash_slot, n_tiles;
   int32_t do_mask;
+  uint64_t layer_skip;       // bit l set: no rows for layer l in this launch
   // Rows from projected features instead of k_new / v_new (proj != nullptr):
   // row i of this launch is the sum over the n_ds d-slices of
   // proj[layer][ds][i][0 .. 2 kv_row) (K raw, then V), K normalised per KV
@@ -62,6 +63,26 @@ struct ProjArgs {
   int64_t pos0;              // position of this launch's row 0
   int32_t n_rows;            // rows of this launch, 1..kProjRows
   int32_t cap, d_model, kv_row, n_head_kv, n_layer, n_ds;
+};
+
+// Sequences' deferred fold-in steps, carried out by the next attention
+// launch of each layer (the fused launch): this layer's new rows, and the
+// window the attention sees.  Positions are below 2^31.  Per-sequence fields
+// are arrays of kFusedMaxSeq, so that a kernel fetches each with one
+// lane-indexed load.
+constexpr int kFusedMaxSeq = 8;
+struct FusedSeqs {
+  uint64_t k_new[kFusedMaxSeq];      // this layer's K rows [n_new][kv_row] F16, not rotated, or 0
+  uint64_t v_new[kFusedMaxSeq];      // this layer's V rows
+  int32_t start[kFusedMaxSeq];       // first new position
+  int32_t start_mod[kFusedMaxSeq];   // its slot
+  int32_t n_new[kFusedMaxSeq];       // new rows this launch appends for this layer (0: none)
+  int32_t n_step_rows[kFusedMaxSeq]; // new rows of the step (for the index rebuild)
+  int32_t committed[kFusedMaxSeq];   // noise positions committed + i
+  int32_t lo[kFusedMaxSeq];          // this layer's visible ring positions: [lo, committed)
+  int32_t index[kFusedMaxSeq];       // nonzero: this launch also rebuilds the index state
+  int32_t full_lo[kFusedMaxSeq];     // lo of the full mask
+  int32_t swa_lo[kFusedMaxSeq];      // lo of the sliding-window mask
 };
 
 // One ring_attn launch over every sequence of the ring for one layer.
@@ -89,6 +110,28 @@ struct AttnArgs {
   int32_t vis_count[RING_MAX_SEQ_INTERNAL];
 };
 
+// The fused launch: the attention's arguments plus the deferred steps.
+struct FusedAttnArgs {
+  AttnArgs a;
+  int32_t swa_layer;         // this layer attends with the sliding-window mask
+  int32_t n_attn_blocks;     // attention work-groups; index work-groups follow
+  int32_t n_index_blocks;    // index blocks (256 slots each) per indexed sequence
+  int32_t index_in_attn;     // 1: attention work-groups of the sequence do its index
+                             // blocks (rank g * n_split + split < n_index_blocks);
+                             // 0: n_index_blocks extra work-groups per sequence
+  int32_t slot_stride;       // int32 per sequence in slot_pos
+  int32_t n_layer, a_step, trash_slot;
+  int64_t layer_stride;      // halves between layers of a sequence's ring
+  const double* inv_freq;    // [64] theta_i (device copy, for the extra index work-groups)
+  double theta[64];          // the same values, fetched by lane at kernel entry
+  int32_t* slot_pos;         // [n_seq][slot_stride]
+  uint16_t* mask_full;       // [n_seq][q_len][kv_total]
+  uint16_t* mask_swa;        // [n_seq][q_len][kv_total] or nullptr
+  double* rope_noise_w;      // [n_seq][q_len][64][2]
+  float* rope_q_w;           // [n_seq][q_len][64][2]
+  FusedSeqs fs;
+};
+
 struct MergeArgs {
   const float* part_acc;
   const float* part_ml;
@@ -100,6 +143,8 @@ struct MergeArgs {
 // kernel itself), or nullptr.
 hipError_t launch_step(const StepArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
+// The fused launch: appends and index work of a.fs[] plus the attention.
+hipError_t launch_attn_fused(const FusedAttnArgs& f, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
 hipError_t launch_project(const ProjArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
 hipError_t launch_fill_u16(uint16_t* p, uint16_t value, int64_t n, hipStream_t s);

@@ -26,6 +26,15 @@ constexpr float kNegInf = -__builtin_inff();
 // below 2^-126 flush to zero and 2^-inf = 0.  Softmax weights that small
 // change no output at the precision that is kept.
 __device__ inline float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+// sin and cos of an angle x (radians, fp64): x is reduced to the nearest
+// whole turn in fp64 (exact for the positions and frequencies here: |x| <
+// 2^31), the remaining fraction of a turn (|f| <= 1/2) goes to fp32 sincos.
+__device__ inline void sincos_turns_f32(double x, float& s, float& c) {
+  const double turns = x * 0.15915494309189533577;  // 1 / (2 pi)
+  const double f = turns - rint(turns);
+  sincosf((float)(f * 6.283185307179586477), &s, &c);
+}
+
 // log2(e) / sqrt(128): folds the 1/sqrt(head_dim) score scale and the
 // change of base for exp2 into the query.
 constexpr double kQScale = 1.4426950408889634074 / 11.313708498984760390;
@@ -73,6 +82,56 @@ __device__ inline void rot_pair(double x, double y, double c, double s,
   yr = y * c + x * s;
 }
 
+// Index state of one sequence after a step, one work-group of 256 threads per
+// 256 slots (block mblk): slot_pos of the new slots, the 0 / -inf window mask
+// (and the sliding-window mask), and in block 0 the cos / sin table of the
+// noise positions committed + i.
+// Slot s of the index state, given its slot_pos before the step (sp, read
+// by the caller; anything for s >= cap).
+__device__ inline void index_slot(const StepArgs& a, int s, int64_t sp) {
+  if (s >= a.kv_total) return;
+  bool vis, vis_swa = false;
+  if (s < a.cap) {
+    int d = s - a.start_mod;  // offset of slot s from the first new slot, mod cap
+    if (d < 0) d += a.cap;
+    if (d < a.n_new) {
+      sp = a.start + d;
+      a.slot_pos[s] = (int32_t)sp;
+    }
+    vis = sp >= a.lo && sp < a.committed;
+    vis_swa = sp >= a.swa_lo && sp < a.committed;
+  } else {
+    vis = s < a.cap + a.q_len;  // noise slots: visible to every noise row
+  }
+  const uint16_t mv = vis ? 0x0000u : 0xFC00u;
+  for (int i = 0; i < a.q_len; ++i) a.mask[(int64_t)i * a.kv_total + s] = mv;
+  if (a.mask_swa) {
+    // sliding-window layers: the window above; noise slot cap + j visible to
+    // noise rows i >= j only
+    for (int i = 0; i < a.q_len; ++i) {
+      const bool v = s < a.cap ? vis_swa : (s - a.cap <= i);
+      a.mask_swa[(int64_t)i * a.kv_total + s] = v ? 0x0000u : 0xFC00u;
+    }
+  }
+}
+
+__device__ inline void index_block(const StepArgs& a, int mblk, int t) {
+  if (mblk == 0) {
+    // cos / sin of the noise positions committed + i, for every frequency.
+    for (int item = t; item < a.q_len * 64; item += 256) {
+      const int i = item >> 6, f = item & 63;
+      double sn, cs;
+      sincos((double)(a.committed + i) * a.inv_freq[f], &sn, &cs);
+      a.rope_noise[2 * item] = cs;
+      a.rope_noise[2 * item + 1] = sn;
+      a.rope_q[2 * item] = (float)cs;
+      a.rope_q[2 * item + 1] = (float)sn;
+    }
+  }
+  const int s = mblk * 256 + t;
+  index_slot(a, s, s < a.cap ? a.slot_pos[s] : 0);
+}
+
 // ---------------------------------------------------------------------------
 // begin_step: append + slot_pos + mask + noise RoPE table
 // ---------------------------------------------------------------------------
@@ -89,6 +148,7 @@ __global__ __launch_bounds__(256) void k_ring_step(StepArgs a) {
     // One row (one position, all KV heads of one layer) per work-group.
     __shared__ double2 cs_row[64];  // (cos, sin) of p * theta_f
     const int layer = blk / rows_per_layer;
+    if (layer < 64 && ((a.layer_skip >> layer) & 1u)) return;
     const int i = blk - layer * rows_per_layer;
     const bool pad = i >= a.n_rows;
     int slot;
@@ -179,46 +239,7 @@ __global__ __launch_bounds__(256) void k_ring_step(StepArgs a) {
     return;
   }
   if (!a.do_mask) return;
-
-  const int mblk = blk - n_row_blocks;
-  if (mblk == 0) {
-    // cos / sin of the noise positions committed + i, for every frequency.
-    for (int item = t; item < a.q_len * 64; item += 256) {
-      const int i = item >> 6, f = item & 63;
-      double sn, cs;
-      sincos((double)(a.committed + i) * a.inv_freq[f], &sn, &cs);
-      a.rope_noise[2 * item] = cs;
-      a.rope_noise[2 * item + 1] = sn;
-      a.rope_q[2 * item] = (float)cs;
-      a.rope_q[2 * item + 1] = (float)sn;
-    }
-  }
-  const int s = mblk * 256 + t;
-  if (s >= a.kv_total) return;
-  bool vis, vis_swa = false;
-  if (s < a.cap) {
-    int64_t sp = a.slot_pos[s];
-    int d = s - a.start_mod;  // offset of slot s from the first new slot, mod cap
-    if (d < 0) d += a.cap;
-    if (d < a.n_new) {
-      sp = a.start + d;
-      a.slot_pos[s] = (int32_t)sp;
-    }
-    vis = sp >= a.lo && sp < a.committed;
-    vis_swa = sp >= a.swa_lo && sp < a.committed;
-  } else {
-    vis = s < a.cap + a.q_len;  // noise slots: visible to every noise row
-  }
-  const uint16_t mv = vis ? 0x0000u : 0xFC00u;
-  for (int i = 0; i < a.q_len; ++i) a.mask[(int64_t)i * a.kv_total + s] = mv;
-  if (a.mask_swa) {
-    // sliding-window layers: the window above; noise slot cap + j visible to
-    // noise rows i >= j only
-    for (int i = 0; i < a.q_len; ++i) {
-      const bool v = s < a.cap ? vis_swa : (s - a.cap <= i);
-      a.mask_swa[(int64_t)i * a.kv_total + s] = v ? 0x0000u : 0xFC00u;
-    }
-  }
+  index_block(a, blk - n_row_blocks, t);
 }
 
 // ---------------------------------------------------------------------------
@@ -326,6 +347,247 @@ __device__ inline void attend_tile(const half8 (&kc)[8], const half8 (&vc)[8],
   }
 }
 
+// A fused launch's per-sequence fields of one sequence (wave-uniform).
+struct FusedLane {
+  uint64_t k_new, v_new;
+  int start, start_mod, n_new, n_step_rows, committed, lo, index, full_lo, swa_lo;
+};
+
+// Fetch them for every sequence at kernel entry, lane i holding sequence
+// i % kFusedMaxSeq (one vector load per field, issued together), then pick
+// sequence `seq` with readlane once it is known.
+struct FusedLaneVec {
+  uint64_t k_new, v_new;
+  int start, start_mod, n_new, n_step_rows, committed, lo, index, full_lo, swa_lo;
+  double theta;   // theta of frequency lane
+};
+
+__device__ inline FusedLaneVec fused_fetch(const FusedAttnArgs& f) {
+  const int i = threadIdx.x & (kFusedMaxSeq - 1);
+  FusedLaneVec v;
+  v.k_new = f.fs.k_new[i];
+  v.v_new = f.fs.v_new[i];
+  v.start = f.fs.start[i];
+  v.start_mod = f.fs.start_mod[i];
+  v.n_new = f.fs.n_new[i];
+  v.n_step_rows = f.fs.n_step_rows[i];
+  v.committed = f.fs.committed[i];
+  v.lo = f.fs.lo[i];
+  v.index = f.fs.index[i];
+  v.full_lo = f.fs.full_lo[i];
+  v.swa_lo = f.fs.swa_lo[i];
+  v.theta = f.theta[threadIdx.x & 63];
+  return v;
+}
+
+__device__ inline uint64_t readlane64(uint64_t x, int l) {
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)x, l);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(x >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ inline FusedLane fused_pick(const FusedLaneVec& v, int seq) {
+  FusedLane u;
+  u.k_new = readlane64(v.k_new, seq);
+  u.v_new = readlane64(v.v_new, seq);
+  u.start = __builtin_amdgcn_readlane(v.start, seq);
+  u.start_mod = __builtin_amdgcn_readlane(v.start_mod, seq);
+  u.n_new = __builtin_amdgcn_readlane(v.n_new, seq);
+  u.n_step_rows = __builtin_amdgcn_readlane(v.n_step_rows, seq);
+  u.committed = __builtin_amdgcn_readlane(v.committed, seq);
+  u.lo = __builtin_amdgcn_readlane(v.lo, seq);
+  u.index = __builtin_amdgcn_readlane(v.index, seq);
+  u.full_lo = __builtin_amdgcn_readlane(v.full_lo, seq);
+  u.swa_lo = __builtin_amdgcn_readlane(v.swa_lo, seq);
+  return u;
+}
+
+// Index-state arguments of sequence `seq` in a fused launch.
+__device__ inline StepArgs fused_index_args(const FusedAttnArgs& f, const FusedLane& fs, int seq) {
+  StepArgs sa{};
+  sa.slot_pos = f.slot_pos + (int64_t)seq * f.slot_stride;
+  sa.mask = f.mask_full + (int64_t)seq * f.a.q_len * f.a.kv_total;
+  sa.mask_swa = f.mask_swa ? f.mask_swa + (int64_t)seq * f.a.q_len * f.a.kv_total : nullptr;
+  sa.rope_noise = f.rope_noise_w + (int64_t)seq * f.a.q_len * 128;
+  sa.rope_q = f.rope_q_w + (int64_t)seq * f.a.q_len * 128;
+  sa.inv_freq = f.inv_freq;
+  sa.start = fs.start;
+  sa.start_mod = fs.start_mod;
+  sa.committed = fs.committed;
+  sa.lo = fs.full_lo;
+  sa.swa_lo = fs.swa_lo;
+  sa.n_new = fs.n_step_rows;
+  sa.cap = f.a.cap;
+  sa.q_len = f.a.q_len;
+  sa.kv_total = f.a.kv_total;
+  return sa;
+}
+
+// What a fused launch tells the attention body about its sequence's
+// deferred step (unused in a plain launch).
+struct FusedCtx {
+  const uint16_t* k_new;    // this layer's new K rows, at this KV head's column
+  const uint16_t* v_new;
+  const int32_t* slot_pos;  // the sequence's slot_pos row
+  double invf;              // theta of frequency `lane`
+  int kv_row;
+  int start, start_mod, n_new, committed, lo, cap;
+  int swa;                  // sliding-window layer: causal noise block
+};
+
+// New rows of this layer in ring tile `tile`, for a wave about to attend it:
+// rotate them (fp64, one rounding), store them to the ring (K and V tiles in
+// global memory) and into the wave's LDS rows pk / pv [32][128], then replace
+// the tile's loaded K and V fragments of those slots (which may predate the
+// store) by the new values.  Raw rows come in groups of four: lane l loads
+// 16 bytes of row l / 16 (K and V), the group is staged in `raw` [4][256].
+// Which of the tile's 32 slots hold new rows (slot s: row d = s - start_mod
+// mod cap), as a wave-uniform bit mask.
+__device__ inline uint32_t new_rows_mask(const FusedCtx& fx, int tile, int lane) {
+  const int s = tile * kTile + (lane & 31);
+  int d = s - fx.start_mod;
+  if (d < 0) d += fx.cap;
+  const bool is_new = lane < 32 && s < fx.cap && d < fx.n_new;
+  return (uint32_t)__ballot(is_new);
+}
+
+// Raw K and V of the first four new rows of a tile (mask nm), 16 bytes per
+// lane: lane l holds bytes [16 (l % 16), +16) of row l / 16's head slice.
+__device__ inline void load_new_rows4(const FusedCtx& fx, int tile, uint32_t nm, int lane,
+                                      half8& kraw, half8& vraw) {
+  uint32_t left = nm;
+  int r[4], nr = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    r[k] = left ? __builtin_ctz(left) : r[0];
+    if (left) { left &= left - 1; ++nr; }
+  }
+  const int rl = r[min(lane >> 4, nr - 1)];
+  int dl = tile * kTile + rl - fx.start_mod;
+  if (dl < 0) dl += fx.cap;
+  const int64_t ro = (int64_t)dl * fx.kv_row + 8 * (lane & 15);
+  kraw = *(const half8*)(fx.k_new + ro);
+  vraw = *(const half8*)(fx.v_new + ro);
+}
+
+// Rotate the new rows of ring tile `tile` (slot mask nm, nonzero): K at its
+// absolute position (fp64, one rounding to F16), store K and V to the ring
+// tile in global memory, and into this wave's LDS rows: pk [32 slots][128]
+// and pvt [128 dims][32 slots] (transposed, for the V fragments).  Raw rows
+// go in groups of four through `raw` [4][256]; the first group may come
+// preloaded (pre_k / pre_v, for tile pre_tile).
+__device__ __forceinline__ void prepare_new_rows(const FusedCtx& fx, int tile, uint32_t nm,
+                                                 uint16_t* kh, uint16_t* vh, uint16_t* raw,
+                                                 uint16_t* pk, uint16_t* pvt, int lane,
+                                                 int pre_tile, const half8& pre_k,
+                                                 const half8& pre_v) {
+  uint16_t* kt = kh + (int64_t)tile * kTileHalves;
+  uint16_t* vt = vh + (int64_t)tile * kTileHalves;
+  uint32_t left = nm;
+  while (left) {
+    const uint32_t left_before = left;
+    int r[4], nr = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      r[k] = left ? __builtin_ctz(left) : r[0];
+      if (left) { left &= left - 1; ++nr; }
+    }
+    const int k_of_lane = lane >> 4, part = lane & 15;
+    half8 kraw, vraw;
+    if (left_before == nm && tile == pre_tile) {
+      kraw = pre_k;            // the first group, loaded before the tile
+      vraw = pre_v;
+    } else {
+      load_new_rows4(fx, tile, left_before, lane, kraw, vraw);
+    }
+    *(half8*)(raw + k_of_lane * 256 + 8 * part) = kraw;
+    *(half8*)(raw + k_of_lane * 256 + 128 + 8 * part) = vraw;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+    for (int k = 0; k < nr; ++k) {
+      const int rr = r[k];
+      int dd = tile * kTile + rr - fx.start_mod;
+      if (dd < 0) dd += fx.cap;
+      const uint16_t* rk = raw + k * 256;
+      double sn, cs;
+      sincos((double)(fx.start + dd) * fx.invf, &sn, &cs);
+      double xr, yr;
+      rot_pair(f16_to_f64(rk[lane]), f16_to_f64(rk[lane + 64]), cs, sn, xr, yr);
+      const uint16_t kx = f64_to_f16_rne(xr), ky = f64_to_f16_rne(yr);
+      const uint16_t vx = rk[128 + lane], vy = rk[128 + lane + 64];
+      kt[k_frag_index(rr, lane)] = kx;
+      kt[k_frag_index(rr, lane + 64)] = ky;
+      vt[v_frag_index(rr, lane)] = vx;
+      vt[v_frag_index(rr, lane + 64)] = vy;
+      pk[rr * kHeadDim + lane] = kx;
+      pk[rr * kHeadDim + lane + 64] = ky;
+      pvt[lane * kTile + rr] = vx;
+      pvt[(lane + 64) * kTile + rr] = vy;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+  }
+}
+
+// Replace the tile's loaded K and V fragments of the new slots (mask nm) by
+// the rows prepare_new_rows left in LDS (the loaded values may predate the
+// store); every LDS read is issued and the choice made by selects.
+__device__ __forceinline__ void apply_new_rows(uint32_t nm, const uint16_t* pk,
+                                               const uint16_t* pvt, int lane, half8 (&kc)[8],
+                                               half8 (&vc)[8]) {
+  const int hl = lane >> 5, col = lane & 31;
+  // K fragment of lane l: slot l % 32, dims 16 c + 8 (l / 32) + 0..7
+  const bool knew = (nm >> col) & 1u;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const half8 nv = *(const half8*)(pk + col * kHeadDim + 16 * c + 8 * hl);
+    kc[c] = knew ? nv : kc[c];
+  }
+  // V fragment 2 b + ks of lane l, element e: slot 16 ks + 8 (e / 4) +
+  // 4 (l / 32) + e % 4, dim 32 b + l % 32: four consecutive slots per read
+  typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int eh = 0; eh < 2; ++eh) {
+        const int base = 16 * ks + 8 * eh + 4 * hl;
+        const half4 nv = *(const half4*)(pvt + (32 * b + col) * kTile + base);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if ((nm >> (base + u)) & 1u) vc[2 * b + ks][4 * eh + u] = nv[u];
+      }
+}
+
+// Mask words of a tile from its slot_pos (fused launch): slot s is visible
+// when its position (the new one for a new slot) lies in [lo, committed);
+// the same for every query.  spv[jj] holds slots 8 jj + 4 (lane / 32) + 0..3.
+template <int MB>
+__device__ __forceinline__ void tile_mask_words(const FusedCtx& fx, int tile, int hl,
+                                                const int4 (&spv)[4], uint32_t (&mw)[MB][8]) {
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const int sp4[4] = {spv[jj].x, spv[jj].y, spv[jj].z, spv[jj].w};
+    uint32_t h[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int s = tile * kTile + 8 * jj + 4 * hl + u;
+      int d = s - fx.start_mod;
+      if (d < 0) d += fx.cap;
+      const int sp = (s < fx.cap && d < fx.n_new) ? fx.start + d : sp4[u];
+      h[u] = (sp >= fx.lo && sp < fx.committed) ? 0x0000u : 0xFC00u;
+    }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      mw[mb][2 * jj] = h[0] | (h[1] << 16);
+      mw[mb][2 * jj + 1] = h[2] | (h[3] << 16);
+    }
+  }
+}
+
 // Work-group: NW waves for one (sequence, KV head, split).  Every split
 // runs the same body; the q_len noise rows of a (sequence, head) are spread
 // one per wave over its waves, so no wave carries more than one ring tile
@@ -346,7 +608,7 @@ __device__ inline void attend_tile(const half8 (&kc)[8], const half8 (&vc)[8],
 // in-bounds (clamped) address and selected afterwards: the compiler can then
 // wait for each group of loads alone instead of draining all of them at a
 // control-flow join.
-template <int MB, int NW>
+template <int MB, int NW, bool FUSED = false>
 struct AttnShape {
   static constexpr int MP = MB * 32;               // padded queries
   static constexpr int NT = NW * 64;               // threads
@@ -369,6 +631,19 @@ struct AttnShape {
       kOwnMergeBytes ? kQBytes + kRowBytes + kMergeBytes
                      : (kQBytes + kRowBytes > kMergeBytes ? kQBytes + kRowBytes : kMergeBytes);
   static_assert(kRopeOffset + kRopeBytes <= kLdsBytes, "rope table fits the merge bytes");
+  // Fused launch: per wave, raw new rows [4][256] and rotated rows K, V
+  // [32][128] F16 (used inside the tile loop: own bytes with one query
+  // block, whose merge buffer is written while other waves are still in
+  // their loops; with two they share the merge buffer's bytes past the
+  // prologue's, which are written only after every wave has left its loop).
+  static constexpr int kPatchWaveBytes = (4 * 256 + 2 * 32 * 128) * 2;
+  static constexpr int kPatchOffset =
+      kOwnMergeBytes ? kLdsBytes : kRopeOffset + kRopeBytes;
+  static constexpr int kFusedLdsBytes =
+      kOwnMergeBytes ? kLdsBytes + NW * kPatchWaveBytes
+                     : (kPatchOffset + NW * kPatchWaveBytes > kLdsBytes
+                            ? kPatchOffset + NW * kPatchWaveBytes : kLdsBytes);
+  static constexpr int kTotalLds = FUSED ? kFusedLdsBytes : kLdsBytes;
 };
 
 // One noise row of this wave's (sequence, head), already loaded: lane f holds
@@ -381,9 +656,9 @@ struct NoiseRow {
   uint16_t mask[MB];
 };
 
-template <int MB>
-__device__ __forceinline__ void load_noise_row(const AttnArgs& a, int seq, int g, int r,
-                                               const uint16_t* mask_seq,
+template <int MB, bool FUSED>
+__device__ __forceinline__ void load_noise_row(const AttnArgs& a, const FusedCtx& fx, int seq,
+                                               int g, int r, const uint16_t* mask_seq,
                                                const unsigned (&qrow)[MB], int lane,
                                                NoiseRow<MB>& nr) {
   const int kv_row = a.n_head_kv * kHeadDim;
@@ -392,22 +667,34 @@ __device__ __forceinline__ void load_noise_row(const AttnArgs& a, int seq, int g
   nr.ky = a.k_noise[ro + lane + 64];
   nr.vx = a.v_noise[ro + lane];
   nr.vy = a.v_noise[ro + lane + 64];
-  nr.cs = *(const double2*)(a.rope_noise + (((int64_t)seq * a.q_len + r) * 64 + lane) * 2);
+  if constexpr (FUSED) {
+    // computed where the row is attended: (cos, sin) at committed + r, and
+    // the mask (the noise block is visible to every query, or causal in a
+    // sliding-window layer)
+    nr.cs = make_double2(0.0, 0.0);
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) nr.mask[mb] = mask_seq[qrow[mb] * a.kv_total + a.cap + r];
+    for (int mb = 0; mb < MB; ++mb)
+      nr.mask[mb] = (fx.swa && (unsigned)r > qrow[mb]) ? 0xFC00u : 0x0000u;
+  } else {
+    nr.cs = *(const double2*)(a.rope_noise + (((int64_t)seq * a.q_len + r) * 64 + lane) * 2);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) nr.mask[mb] = mask_seq[qrow[mb] * a.kv_total + a.cap + r];
+  }
 }
 
 // Rotate the row, store it to ring row cap + r, and fold it into the wave's
 // running softmax as one more key.  S = Q k on the vector unit (dot products
 // of the hi and lo query fragments with the F16 key); the P V update is one
 // matrix op per 32-dim block with the row as slot 0 of a V fragment.
-template <int MB>
+template <int MB, bool FUSED>
 __device__ __forceinline__ void attend_noise_row(
-    const AttnArgs& a, const NoiseRow<MB>& nr, int r, uint16_t* kh, uint16_t* vh,
-    uint16_t* rowk, uint16_t* rowv, int lane, int hl, int col, const QFrag<MB>& q,
+    const AttnArgs& a, const FusedCtx& fx, const NoiseRow<MB>& nr, int r, uint16_t* kh,
+    uint16_t* vh, uint16_t* rowk, uint16_t* rowv, int lane, int hl, int col, const QFrag<MB>& q,
     const half8* q_lds, float (&m_run)[MB], float (&l_run)[MB], f32x16 (&o)[MB][4]) {
+  double2 cs = nr.cs;
+  if constexpr (FUSED) sincos((double)(fx.committed + r) * fx.invf, &cs.y, &cs.x);
   double xr, yr;
-  rot_pair(f16_to_f64(nr.kx), f16_to_f64(nr.ky), nr.cs.x, nr.cs.y, xr, yr);
+  rot_pair(f16_to_f64(nr.kx), f16_to_f64(nr.ky), cs.x, cs.y, xr, yr);
   const uint16_t kx = f64_to_f16_rne(xr), ky = f64_to_f16_rne(yr);
   // ring row cap + r of this layer and head
   const int slot = a.cap + r;
@@ -609,11 +896,13 @@ __device__ __forceinline__ void merge_store(const EpilogueArgs& a, unsigned char
   }
 }
 
-template <int MB, int NW, int RP>
-__device__ __forceinline__ void attn_body(const AttnArgs& a, int unit, int split, int vis_first,
-                                          int vis_count, unsigned char* lds,
-                                          float (*sm_m)[MB * 32], float (*sm_l)[MB * 32]) {
-  using S = AttnShape<MB, NW>;
+template <int MB, int NW, int RP, bool FUSED>
+__device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs* fa,
+                                          const FusedLane& fl, double theta_lane, int unit,
+                                          int split, int vis_first, int vis_count,
+                                          unsigned char* lds, float (*sm_m)[MB * 32],
+                                          float (*sm_l)[MB * 32]) {
+  using S = AttnShape<MB, NW, FUSED>;
   constexpr int MP = S::MP, NT = S::NT;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -637,6 +926,33 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int unit, int split
   const int t1 = min(nvt, t0 + per);
   uint16_t* kh = a.kring + seq * a.seq_stride + a.layer_offset + g * a.head_stride;
   uint16_t* vh = a.vring + seq * a.seq_stride + a.layer_offset + g * a.head_stride;
+  // Fused launch: this sequence's deferred step (new rows of this layer,
+  // window) and theta of frequency `lane`.
+  FusedCtx fx{};
+  if constexpr (FUSED) {
+    const int kv_row = a.n_head_kv * kHeadDim;
+    fx.k_new = fl.k_new ? (const uint16_t*)fl.k_new + g * kHeadDim : nullptr;
+    fx.v_new = fl.v_new ? (const uint16_t*)fl.v_new + g * kHeadDim : nullptr;
+    fx.slot_pos = fa->slot_pos + (int64_t)seq * fa->slot_stride;
+    fx.invf = theta_lane;
+    fx.kv_row = kv_row;
+    fx.start = fl.start;
+    fx.start_mod = fl.start_mod;
+    fx.n_new = fl.n_new;
+    fx.committed = fl.committed;
+    fx.lo = fl.lo;
+    fx.cap = a.cap;
+    fx.swa = fa->swa_layer;
+  }
+  // Index block of this work-group (fused launch, when the attention
+  // work-groups carry them): block ix_blk of its own sequence; block 0 also
+  // writes the noise RoPE tables.
+  int ix_blk = -1;
+  if constexpr (FUSED) {
+    const int rank_in_seq = g * a.n_split + split;
+    if (fa->index_in_attn && fl.index && rank_in_seq < fa->n_index_blocks)
+      ix_blk = rank_in_seq;
+  }
   // The destinations and the few integers the store needs are computed
   // up front and pass through an empty asm statement that redefines them, so the
   // compiler keeps them in SGPRs instead of re-loading kernel arguments in
@@ -669,10 +985,20 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int unit, int split
   //      16c + 8h + e and y = the same dims + 64.
   //      RP passes of one float4 per thread cover q_len <= RP * NT / 32; a
   //      pass past the table re-reads its last float4 (one line for the wave).
+  //      (Fused launch: the table is computed here from theta, loaded now,
+  //      after the other loads are issued.)
   float4 rope_v[RP];
+  double2 rope_th[RP];
 #pragma unroll
-  for (int k = 0; k < RP; ++k)
-    rope_v[k] = ((const float4*)ropeq)[min((int)threadIdx.x + k * NT, a.q_len * 32 - 1)];
+  for (int k = 0; k < RP; ++k) {
+    const int o = min((int)threadIdx.x + k * NT, a.q_len * 32 - 1);
+    if constexpr (FUSED) {
+      const int f0 = (2 * o) & 63;
+      rope_th[k] = make_double2(__shfl(theta_lane, f0), __shfl(theta_lane, f0 + 1));
+    } else {
+      rope_v[k] = ((const float4*)ropeq)[o];
+    }
+  }
   half8 qx[MB], qy[MB];
   unsigned qfreq[MB];  // float4 index of (cos, sin) of frequency 16c + 8h at query row i
   const uint16_t* qseq = a.q + ((int64_t)seq * a.q_len * a.n_head + g * a.group) * kHeadDim;
@@ -691,39 +1017,104 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int unit, int split
   // ---- 1b. the wave's first noise row (a wave without one loads the last
   //      row and ignores it).
   NoiseRow<MB> nr;
-  load_noise_row<MB>(a, seq, g, min(rank, a.q_len - 1), mask_seq, qrow, lane, nr);
+  load_noise_row<MB, FUSED>(a, fx, seq, g, min(rank, a.q_len - 1), mask_seq, qrow, lane, nr);
 
   // ---- 1c. the wave's first ring tile (a wave without tiles loads its
   //      split's last tile again and ignores it).
-  auto load_tile = [&](int tile, half8 (&kc)[8], half8 (&vc)[8], uint32_t (&mw)[MB][8]) {
+  // (Fused launch: the slot_pos of the tile's slots instead of the mask,
+  //  spv[jj] = slots 8 jj + 4 (lane / 32) + 0..3.)
+  auto load_tile = [&](int tile, half8 (&kc)[8], half8 (&vc)[8], uint32_t (&mw)[MB][8],
+                       int4 (&spv)[4]) {
     const half8* kt = (const half8*)(kh + (int64_t)tile * kTileHalves);
     const half8* vt = (const half8*)(vh + (int64_t)tile * kTileHalves);
 #pragma unroll
     for (int c = 0; c < 8; ++c) kc[c] = kt[c * 64 + lane];
 #pragma unroll
     for (int c = 0; c < 8; ++c) vc[c] = vt[c * 64 + lane];
-    const uint16_t* mt = mask_seq + tile * kTile;
+    if constexpr (FUSED) {
+      const int4* sp = (const int4*)(fx.slot_pos + tile * kTile + 4 * hl);
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const unsigned mo = qrow[mb] * a.kv_total + 4 * hl;
+      for (int jj = 0; jj < 4; ++jj) spv[jj] = sp[2 * jj];
+    } else {
+      const uint16_t* mt = mask_seq + tile * kTile;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const uint2 w = *(const uint2*)(mt + mo + 8 * jj);
-        mw[mb][2 * jj] = w.x;
-        mw[mb][2 * jj + 1] = w.y;
+      for (int mb = 0; mb < MB; ++mb) {
+        const unsigned mo = qrow[mb] * a.kv_total + 4 * hl;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const uint2 w = *(const uint2*)(mt + mo + 8 * jj);
+          mw[mb][2 * jj] = w.x;
+          mw[mb][2 * jj + 1] = w.y;
+        }
       }
     }
   };
   int tile = t0 + wave;
   const int tile_last = max(t1 - 1, 0);
+  // Fused launch: the first group of new rows of the wave's first tile is
+  // loaded ahead of the tile, so that their rotation overlaps its arrival.
+  int pre_tile = -1;
+  half8 pre_k = {}, pre_v = {};
+  if constexpr (FUSED) {
+    if (fx.n_new > 0 && tile < t1) {
+      const int rt0 = ring_tile(tile);
+      const uint32_t nm0 = new_rows_mask(fx, rt0, lane);
+      if (nm0) {
+        load_new_rows4(fx, rt0, nm0, lane, pre_k, pre_v);
+        pre_tile = rt0;
+      }
+    }
+  }
   half8 kc[8], vc[8];
   uint32_t mw[MB][8];
-  load_tile(ring_tile(min(tile, tile_last)), kc, vc, mw);
+  int4 spv[4];
+  load_tile(ring_tile(min(tile, tile_last)), kc, vc, mw, spv);
+  // slot_pos of this work-group's index slot (read by every fused work-group,
+  // used by those with an index block; issued with the other loads)
+  int ix_sp = 0;
+  if constexpr (FUSED)
+    ix_sp = fx.slot_pos[min(max(ix_blk, 0) * 256 + (int)threadIdx.x, a.cap - 1)];
+  // Fused launch, before a tile is attended: its mask words from slot_pos,
+  // and its new rows of this layer (stored, and patched into the fragments).
+  uint16_t* patch = reinterpret_cast<uint16_t*>(lds + S::kPatchOffset + wave * S::kPatchWaveBytes);
+  uint16_t* p_raw = patch;
+  uint16_t* p_k = patch + 4 * 256;
+  uint16_t* p_vt = patch + 4 * 256 + 32 * 128;
+  uint32_t early_nm = 0;   // new-row mask of tile pre_tile, prepared before the tile loop
+  auto prep_tile = [&](int rt, half8 (&kc)[8], half8 (&vc)[8], uint32_t (&mw)[MB][8],
+                       const int4 (&spv)[4]) {
+    if constexpr (FUSED) {
+      tile_mask_words<MB>(fx, rt, hl, spv, mw);
+      if (fx.n_new > 0) {
+        uint32_t nm = early_nm;
+        if (rt != pre_tile) {
+          nm = new_rows_mask(fx, rt, lane);
+          if (nm) prepare_new_rows(fx, rt, nm, kh, vh, p_raw, p_k, p_vt, lane, -1, pre_k, pre_v);
+        }
+        if (nm) apply_new_rows(nm, p_k, p_vt, lane, kc, vc);
+      }
+    }
+  };
 
   // ---- 2. queries: rotate at committed + i, scale by log2(e)/sqrt(d),
   //      split into hi + lo F16 (fragment order [mb][hi/lo][chunk][lane]);
   //      queries past q_len * group are zero.
   float4* rope_lds = reinterpret_cast<float4*>(lds + S::kRopeOffset);
+  if constexpr (FUSED) {
+    // (cos, sin) of frequencies f0, f0 + 1 at noise position committed + i,
+    // entry o = items 2o, 2o + 1 of [q_len][64], for the query rotation only:
+    // the angle reduced modulo a turn in fp64, then fp32 sincos (error about
+    // 3e-7, below the 2^-22 of the hi + lo F16 split the queries get)
+#pragma unroll
+    for (int k = 0; k < RP; ++k) {
+      const int o = min((int)threadIdx.x + k * NT, a.q_len * 32 - 1);
+      const double pos = (double)(fx.committed + ((2 * o) >> 6));
+      float s0, c0, s1, c1;
+      sincos_turns_f32(pos * rope_th[k].x, s0, c0);
+      sincos_turns_f32(pos * rope_th[k].y, s1, c1);
+      rope_v[k] = make_float4(c0, s0, c1, s1);
+    }
+  }
   // unconditional: entries past the table hold copies of its last float4
   // and are never read (a conditional store would let the compiler sink the
   // load into the branch and wait for every load in flight there)
@@ -797,12 +1188,22 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int unit, int split
   uint16_t* rowk = reinterpret_cast<uint16_t*>(lds + S::kQBytes) + wave * 2 * kHeadDim;
   uint16_t* rowv = rowk + kHeadDim;
   if (rank < a.q_len) {
-    attend_noise_row<MB>(a, nr, rank, kh, vh, rowk, rowv, lane, hl, col, qf, q_lds, m_run,
+    attend_noise_row<MB, FUSED>(a, fx, nr, rank, kh, vh, rowk, rowv, lane, hl, col, qf, q_lds, m_run,
                          l_run, o);
     for (int r = rank + n_waves; r < a.q_len; r += n_waves) {
-      load_noise_row<MB>(a, seq, g, r, mask_seq, qrow, lane, nr);
-      attend_noise_row<MB>(a, nr, r, kh, vh, rowk, rowv, lane, hl, col, qf, q_lds, m_run,
+      load_noise_row<MB, FUSED>(a, fx, seq, g, r, mask_seq, qrow, lane, nr);
+      attend_noise_row<MB, FUSED>(a, fx, nr, r, kh, vh, rowk, rowv, lane, hl, col, qf, q_lds, m_run,
                            l_run, o);
+    }
+  }
+
+  // ---- 3b. (fused launch) the new rows of the wave's first tile, rotated
+  //      and stored while the tile is still in flight
+  if constexpr (FUSED) {
+    if (pre_tile >= 0) {
+      early_nm = new_rows_mask(fx, pre_tile, lane);
+      prepare_new_rows(fx, pre_tile, early_nm, kh, vh, p_raw, p_k, p_vt, lane, pre_tile, pre_k,
+                       pre_v);
     }
   }
 
@@ -815,7 +1216,9 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int unit, int split
     while (tile + NW < t1) {
       half8 kn[8], vn[8];
       uint32_t mn[MB][8];
-      load_tile(ring_tile(tile + NW), kn, vn, mn);
+      int4 spn[4];
+      load_tile(ring_tile(tile + NW), kn, vn, mn, spn);
+      prep_tile(ring_tile(tile), kc, vc, mw, spv);
       attend_tile<MB>(kc, vc, mw, a.cap - ring_tile(tile) * kTile, hl, qf, q_lds, lane, m_run,
                       l_run, o);
 #pragma unroll
@@ -824,17 +1227,24 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int unit, int split
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int j = 0; j < 8; ++j) mw[mb][j] = mn[mb][j];
+      if constexpr (FUSED) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) spv[jj] = spn[jj];
+      }
       tile += NW;
     }
-    if (tile < t1)
+    if (tile < t1) {
+      prep_tile(ring_tile(tile), kc, vc, mw, spv);
       attend_tile<MB>(kc, vc, mw, a.cap - ring_tile(tile) * kTile, hl, qf, q_lds, lane, m_run,
                       l_run, o);
+    }
   } else {
     while (tile < t1) {
       const int next = tile + NW;
+      prep_tile(ring_tile(tile), kc, vc, mw, spv);
       attend_tile<MB>(kc, vc, mw, a.cap - ring_tile(tile) * kTile, hl, qf, q_lds, lane, m_run,
                       l_run, o);
-      if (next < t1) load_tile(ring_tile(next), kc, vc, mw);
+      if (next < t1) load_tile(ring_tile(next), kc, vc, mw, spv);
       tile = next;
     }
   }
@@ -850,12 +1260,31 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int unit, int split
     merge_store<MB, NW, 2>(ep, lds, sm_m, sm_l, m_run, l_run, o, lane);
   else
     merge_store<MB, NW, 3>(ep, lds, sm_m, sm_l, m_run, l_run, o, lane);
+  if constexpr (FUSED) {
+    if (ix_blk >= 0) {
+      const StepArgs sa = fused_index_args(*fa, fl, seq);
+      index_slot(sa, ix_blk * 256 + threadIdx.x, ix_sp);
+      if (ix_blk == 0) {
+        // the noise RoPE table for later plain launches, as the append kernel
+        // builds it (fp64 sincos, and its fp32 rounding)
+        for (int item = threadIdx.x; item < a.q_len * 64; item += NT) {
+          const int i = item >> 6, f = item & 63;
+          double sn, cs;
+          sincos((double)(fx.committed + i) * fa->theta[f], &sn, &cs);
+          sa.rope_noise[2 * item] = cs;
+          sa.rope_noise[2 * item + 1] = sn;
+          sa.rope_q[2 * item] = (float)cs;
+          sa.rope_q[2 * item + 1] = (float)sn;
+        }
+      }
+    }
+  }
 }
 
-template <int MB, int NW, int RP>
-__global__ __launch_bounds__(NW * 64) void k_ring_attn(AttnArgs a) {
-  using S = AttnShape<MB, NW>;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[S::kLdsBytes];
+template <int MB, int NW, int RP, bool FUSED>
+__device__ __forceinline__ void attn_entry(const AttnArgs& a, const FusedAttnArgs* fa) {
+  using S = AttnShape<MB, NW, FUSED>;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[S::kTotalLds];
   __shared__ float sm_m[NW][S::MP];
   __shared__ float sm_l[NW][S::MP];
   // Work-group -> (sequence, KV head, split).  Work-groups are handed to the
@@ -867,6 +1296,15 @@ __global__ __launch_bounds__(NW * 64) void k_ring_attn(AttnArgs a) {
   // lane-indexed vector load each and are picked by sequence below.
   const int firstv = a.vis_first[threadIdx.x & 63];
   const int countv = a.vis_count[threadIdx.x & 63];
+  FusedLaneVec fv{};
+  if constexpr (FUSED) {
+    fv = fused_fetch(*fa);
+    asm volatile("" ::"v"(fv.k_new), "v"(fv.v_new), "v"(fv.start), "v"(fv.start_mod),
+                 "v"(fv.n_new), "v"(fv.n_step_rows), "v"(fv.committed), "v"(fv.lo),
+                 "v"(fv.index), "v"(fv.full_lo), "v"(fv.swa_lo), "v"(fv.theta),
+                 "s"(fa->slot_pos), "s"(fa->slot_stride), "s"(fa->swa_layer),
+                 "s"(fa->index_in_attn), "s"(fa->n_index_blocks));
+  }
   asm volatile("" ::"s"(a.kring), "s"(a.vring), "s"(a.mask), "s"(a.rope_noise), "s"(a.rope_q),
                "s"(a.q),
                "s"(a.k_noise), "s"(a.v_noise), "s"(a.out), "s"(a.part_acc), "s"(a.part_ml),
@@ -885,8 +1323,44 @@ __global__ __launch_bounds__(NW * 64) void k_ring_attn(AttnArgs a) {
     split = blockIdx.x % a.n_split;
   }
   const int seq = unit / a.n_head_kv;
-  attn_body<MB, NW, RP>(a, unit, split, __builtin_amdgcn_readlane(firstv, seq),
-                    __builtin_amdgcn_readlane(countv, seq), lds, sm_m, sm_l);
+  FusedLane fl{};
+  if constexpr (FUSED) fl = fused_pick(fv, seq);
+  attn_body<MB, NW, RP, FUSED>(a, fa, fl, fv.theta, unit, split,
+                               __builtin_amdgcn_readlane(firstv, seq),
+                               __builtin_amdgcn_readlane(countv, seq), lds, sm_m, sm_l);
+}
+
+template <int MB, int NW, int RP>
+__global__ __launch_bounds__(NW * 64) void k_ring_attn(AttnArgs a) {
+  attn_entry<MB, NW, RP, false>(a, nullptr);
+}
+
+// The fused launch: the attention work-groups first (same mapping as
+// k_ring_attn), then n_index_blocks work-groups per sequence whose index
+// state this launch rebuilds (slot_pos, masks, noise RoPE table).
+template <int MB, int NW, int RP>
+__global__ __launch_bounds__(NW * 64) void k_ring_attn_fused(FusedAttnArgs f) {
+  if ((int)blockIdx.x >= f.n_attn_blocks) {
+    static_assert(NW * 64 == 256, "index work-groups have 256 threads");
+    int b = blockIdx.x - f.n_attn_blocks;
+    int seq = 0;
+    for (; seq < f.a.n_seq; ++seq) {
+      if (!f.fs.index[seq]) continue;
+      if (b < f.n_index_blocks) break;
+      b -= f.n_index_blocks;
+    }
+    if (seq >= f.a.n_seq) return;
+    FusedLane fl{};
+    fl.start = f.fs.start[seq];
+    fl.start_mod = f.fs.start_mod[seq];
+    fl.n_step_rows = f.fs.n_step_rows[seq];
+    fl.committed = f.fs.committed[seq];
+    fl.full_lo = f.fs.full_lo[seq];
+    fl.swa_lo = f.fs.swa_lo[seq];
+    index_block(fused_index_args(f, fl, seq), b, threadIdx.x);
+    return;
+  }
+  attn_entry<MB, NW, RP, true>(f.a, &f);
 }
 
 // ---------------------------------------------------------------------------
@@ -1083,6 +1557,27 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s, hipEvent_t t0, hipEvent
       hipExtLaunchKernelGGL((k_ring_attn<2, 4, 1>), dim3(grid), dim3(256), 0, s, t0, t1, 0, a);
     else
       hipExtLaunchKernelGGL((k_ring_attn<2, 4, 4>), dim3(grid), dim3(256), 0, s, t0, t1, 0, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_fused(const FusedAttnArgs& f, hipStream_t s, hipEvent_t t0,
+                             hipEvent_t t1) {
+  const AttnArgs& a = f.a;
+  int n_indexed = 0;
+  for (int i = 0; i < a.n_seq && i < kFusedMaxSeq; ++i) n_indexed += f.fs.index[i] != 0;
+  const int grid = f.n_attn_blocks + (f.index_in_attn ? 0 : n_indexed * f.n_index_blocks);
+  const bool one_pass = a.q_len <= 8;
+  if (a.m <= 32) {
+    if (one_pass)
+      hipExtLaunchKernelGGL((k_ring_attn_fused<1, 4, 1>), dim3(grid), dim3(256), 0, s, t0, t1, 0, f);
+    else
+      hipExtLaunchKernelGGL((k_ring_attn_fused<1, 4, 4>), dim3(grid), dim3(256), 0, s, t0, t1, 0, f);
+  } else {
+    if (one_pass)
+      hipExtLaunchKernelGGL((k_ring_attn_fused<2, 4, 1>), dim3(grid), dim3(256), 0, s, t0, t1, 0, f);
+    else
+      hipExtLaunchKernelGGL((k_ring_attn_fused<2, 4, 4>), dim3(grid), dim3(256), 0, s, t0, t1, 0, f);
   }
   return hipGetLastError();
 }

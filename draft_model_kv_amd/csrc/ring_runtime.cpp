@@ -49,6 +49,7 @@ struct Layout {
          off_ropeq = 0, off_freq = 0;
   size_t off_pacc = 0, off_pml = 0, total = 0;
   int32_t n_ds = 0;                       // d-slices of the projection
+  int64_t slot_stride = 0;                // int32 per sequence in slot_pos (cap padded)
   size_t off_mirror = 0, off_proj = 0;    // feature mirror, projection scratch
 };
 
@@ -129,7 +130,10 @@ void geometry_of(const ring_config& c, ring_geometry* g, Layout* L) {
   const size_t ring_bytes = (size_t)c.n_seq * L->seq_stride * 2;
   L->off_k = take(ring_bytes);
   L->off_v = take(ring_bytes);
-  L->off_slot = take((size_t)c.n_seq * c.cap * 4);
+  // slot_pos rows padded to 64 entries, so that 16-byte loads of four slots
+  // stay aligned and inside the sequence's row
+  L->slot_stride = align_up(c.cap, 64);
+  L->off_slot = take((size_t)c.n_seq * L->slot_stride * 4);
   L->off_mask = take((size_t)c.n_seq * c.q_len * g->kv_total * 2);
   L->off_mask_swa = take(c.swa_window > 0 ? (size_t)c.n_seq * c.q_len * g->kv_total * 2 : 0);
   L->off_rope = take((size_t)c.n_seq * c.q_len * 64 * 2 * 8);
@@ -166,6 +170,18 @@ Plan plan_of(int64_t cap, int64_t a_step, int64_t committed, int64_t next_pos, i
 
 }  // namespace
 
+// A sequence's deferred fold-in step (ring_begin_step_deferred): its rows are
+// appended, layer by layer, by the next attention launch of each layer, and
+// the first such launch also rebuilds the index state.
+struct Pending {
+  bool active = false;
+  const uint16_t* k = nullptr;  // [n_layer][n_new][kv_row] F16, not rotated
+  const uint16_t* v = nullptr;
+  int64_t start = 0, n_new = 0, committed = 0, lo = 0, swa_lo = 0;
+  uint64_t layers_left = 0;     // bit l: layer l's rows are not appended yet
+  bool index_left = false;      // slot_pos, masks and RoPE table not rebuilt yet
+};
+
 struct ring {
   ring_config cfg{};
   ring_geometry geo{};
@@ -187,6 +203,7 @@ struct ring {
   float* proj = nullptr;        // projection scratch
   std::vector<int64_t> next_pos, held_lo, committed;
   std::vector<std::vector<int64_t>> mirror_pos;  // per sequence: position in each mirror slot, -1 empty
+  std::vector<Pending> pending;                   // per sequence
   std::vector<double> inv_freq_host;
   hipStream_t last_stream = nullptr;
   // profiling: per kernel kind, event pairs (start, end) and how many are used
@@ -209,7 +226,7 @@ StepArgs step_args(ring* r, int32_t seq) {
   StepArgs a{};
   a.kring = r->kring + seq * r->L.seq_stride;
   a.vring = r->vring + seq * r->L.seq_stride;
-  a.slot_pos = r->slot_pos + (int64_t)seq * r->cfg.cap;
+  a.slot_pos = r->slot_pos + (int64_t)seq * r->L.slot_stride;
   a.mask = r->mask + (int64_t)seq * r->cfg.q_len * r->geo.kv_total;
   a.mask_swa = r->mask_swa ? r->mask_swa + (int64_t)seq * r->cfg.q_len * r->geo.kv_total : nullptr;
   a.rope_noise = r->rope_noise + (int64_t)seq * r->cfg.q_len * 128;
@@ -246,6 +263,42 @@ void destroy_events(ring* r) {
 
 int check_launch(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(RING_EDEVICE, "%s: %s", what, hipGetErrorString(e));
+  return RING_OK;
+}
+
+// Carry out what a deferred step of `seq` still owes (rows of the layers
+// whose attention has not run, the index state) with the ordinary append
+// kernel, on the ring's last stream.
+int flush_seq(ring* r, int32_t seq) {
+  Pending& p = r->pending[seq];
+  if (!p.active) return RING_OK;
+  if (p.layers_left || p.index_left) {
+    StepArgs a = step_args(r, seq);
+    a.k_new = p.k;
+    a.v_new = p.v;
+    a.start = p.start;
+    a.start_mod = (int32_t)(p.start % r->cfg.cap);
+    a.committed = p.committed;
+    a.lo = p.lo;
+    a.swa_lo = p.swa_lo;
+    a.n_new = (int32_t)p.n_new;
+    a.row0 = 0;
+    a.n_rows = (int32_t)p.n_new;
+    a.n_pad = r->geo.a_step - (int32_t)p.n_new;
+    a.do_mask = p.index_left ? 1 : 0;
+    a.layer_skip = ~p.layers_left;
+    hipEvent_t t0, t1;
+    next_events(r, RING_KERNEL_STEP, &t0, &t1);
+    if (int e = check_launch(launch_step(a, r->last_stream, t0, t1), "deferred append"))
+      return e;
+  }
+  p = Pending{};
+  return RING_OK;
+}
+
+int flush_all(ring* r) {
+  for (int32_t seq = 0; seq < r->cfg.n_seq; ++seq)
+    if (int e = flush_seq(r, seq)) return e;
   return RING_OK;
 }
 
@@ -311,6 +364,7 @@ int ring_init(const ring_config* cfg, void* workspace, size_t workspace_bytes, v
     r->proj = reinterpret_cast<float*>(r->ws + r->L.off_proj);
     r->mirror_pos.assign(cfg->n_seq, std::vector<int64_t>(cfg->cap, -1));
   }
+  r->pending.assign(cfg->n_seq, Pending{});
   r->next_pos.assign(cfg->n_seq, 0);
   r->held_lo.assign(cfg->n_seq, 0);
   r->committed.assign(cfg->n_seq, 0);
@@ -323,7 +377,7 @@ int ring_init(const ring_config* cfg, void* workspace, size_t workspace_bytes, v
   const size_t ring_bytes = (size_t)cfg->n_seq * r->L.seq_stride * 2;
   hipError_t e = hipMemsetAsync(r->kring, 0, ring_bytes, s);
   if (e == hipSuccess) e = hipMemsetAsync(r->vring, 0, ring_bytes, s);
-  if (e == hipSuccess) e = hipMemsetAsync(r->slot_pos, 0xFF, (size_t)cfg->n_seq * cfg->cap * 4, s);
+  if (e == hipSuccess) e = hipMemsetAsync(r->slot_pos, 0xFF, (size_t)cfg->n_seq * r->L.slot_stride * 4, s);
   if (e == hipSuccess)
     e = launch_fill_u16(r->mask, 0xFC00u, (int64_t)cfg->n_seq * cfg->q_len * r->geo.kv_total, s);
   if (e == hipSuccess)
@@ -401,6 +455,7 @@ int ring_begin_step(ring_t* r, int32_t seq, int64_t committed, const void* k_new
                 (long long)p.n_new, (long long)p.start);
   if (p.n_new > 0 && (!k_new || !v_new)) return fail(RING_EINVAL, "k_new / v_new is NULL");
   if (int e = use_device(r)) return e;
+  if (int e = flush_seq(r, seq)) return e;
   hipStream_t s = static_cast<hipStream_t>(stream);
   r->last_stream = s;
 
@@ -432,6 +487,42 @@ int ring_begin_step(ring_t* r, int32_t seq, int64_t committed, const void* k_new
     next_events(r, RING_KERNEL_STEP, &t0, &t1);
     if (int e = check_launch(launch_step(a, s, t0, t1), "fold-in append")) return e;
   }
+  r->next_pos[seq] = committed;
+  r->held_lo[seq] = p.lo;
+  r->committed[seq] = committed;
+  return ok();
+}
+
+int ring_begin_step_deferred(ring_t* r, int32_t seq, int64_t committed, const void* k_new,
+                             const void* v_new, int64_t n_rows, void* stream) {
+  if (!r) return fail(RING_EINVAL, "ring is NULL");
+  if (seq < 0 || seq >= r->cfg.n_seq) return fail(RING_ERANGE, "seq %d out of range", seq);
+  if (committed < 0 || committed + r->cfg.q_len > INT32_MAX)
+    return fail(RING_ERANGE, "committed %lld out of range", (long long)committed);
+  const Plan p = plan_of(r->cfg.cap, r->geo.a_step, committed, r->next_pos[seq], r->held_lo[seq]);
+  // Bulk appends, and rings beyond what one fused launch carries, append now.
+  if (p.bulk || r->cfg.n_seq > kFusedMaxSeq || r->cfg.n_layer > 64)
+    return ring_begin_step(r, seq, committed, k_new, v_new, n_rows, stream);
+  if (n_rows != p.n_new)
+    return fail(RING_ESTATE, "n_rows %lld != planned n_new %lld (start %lld)", (long long)n_rows,
+                (long long)p.n_new, (long long)p.start);
+  if (p.n_new > 0 && (!k_new || !v_new)) return fail(RING_EINVAL, "k_new / v_new is NULL");
+  if (((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) & 15) != 0)
+    return fail(RING_EINVAL, "k_new / v_new must be 16-byte aligned");
+  if (int e = use_device(r)) return e;
+  if (int e = flush_seq(r, seq)) return e;
+  r->last_stream = static_cast<hipStream_t>(stream);
+  Pending& d = r->pending[seq];
+  d.active = true;
+  d.k = static_cast<const uint16_t*>(k_new);
+  d.v = static_cast<const uint16_t*>(v_new);
+  d.start = p.start;
+  d.n_new = p.n_new;
+  d.committed = committed;
+  d.lo = p.lo;
+  d.swa_lo = committed - std::min<int64_t>(r->cfg.swa_window, p.win);
+  d.layers_left = r->cfg.n_layer == 64 ? ~0ull : ((1ull << r->cfg.n_layer) - 1);
+  d.index_left = true;
   r->next_pos[seq] = committed;
   r->held_lo[seq] = p.lo;
   r->committed[seq] = committed;
@@ -489,6 +580,7 @@ int ring_begin_step_mirror(ring_t* r, int32_t seq, int64_t committed, const ring
       return fail(RING_ESTATE, "position %lld is not in the feature mirror (write it first)",
                   (long long)q);
   if (int e = use_device(r)) return e;
+  if (int e = flush_seq(r, seq)) return e;
   hipStream_t s = static_cast<hipStream_t>(stream);
   r->last_stream = s;
 
@@ -583,14 +675,19 @@ int ring_attn(ring_t* r, int32_t layer, const void* q, const void* k_noise, cons
   a.ring_tiles = ring_tiles;
   const bool swa = layer < 64 && ((r->cfg.swa_layers >> layer) & 1u);
   if (swa) a.mask = r->mask_swa;
+  const uint64_t bit = layer < 64 ? (1ull << layer) : 0;
   int32_t max_count = 0;
   for (int i = 0; i < r->cfg.n_seq; ++i) {
     // Visible positions [committed - w, committed) sit in slots from
     // (committed - w) % cap on, circularly: w = win for full layers,
-    // min(swa_window, win) for sliding-window layers.
+    // min(swa_window, win) for sliding-window layers.  A deferred step whose
+    // rows this launch appends reads the whole window's tiles (its new rows
+    // may lie before a sliding window; the mask hides them there).
     const int64_t c = r->committed[i];
     const int64_t win = std::min<int64_t>(c, cap);
-    const int64_t w = swa ? std::min<int64_t>(r->cfg.swa_window, win) : win;
+    const Pending& pd = r->pending[i];
+    const bool appends = pd.active && (pd.layers_left & bit) && pd.n_new > 0;
+    const int64_t w = (swa && !appends) ? std::min<int64_t>(r->cfg.swa_window, win) : win;
     int32_t first = 0, count = 0;
     if (w > 0 && w < win) {
       const int64_t s0 = (c - w) % cap, s1 = s0 + w;  // slot range [s0, s1), s1 may pass cap
@@ -614,7 +711,63 @@ int ring_attn(ring_t* r, int32_t layer, const void* q, const void* k_noise, cons
   a.n_split = n_split;
   hipEvent_t t0, t1;
   next_events(r, RING_KERNEL_ATTN, &t0, &t1);
-  if (int e = check_launch(launch_attn(a, s, t0, t1), "ring_attn")) return e;
+  // Deferred steps owing this layer's rows or the index state: one fused
+  // launch appends and rebuilds them and attends.
+  bool fuse = false;
+  for (const Pending& p : r->pending) fuse |= p.active && ((p.layers_left & bit) || p.index_left);
+  if (fuse) {
+    FusedAttnArgs f{};
+    f.a = a;
+    f.swa_layer = swa ? 1 : 0;
+    f.n_attn_blocks = r->cfg.n_seq * r->cfg.n_head_kv * n_split;
+    f.n_index_blocks = (r->geo.kv_total + 255) / 256;
+    // the attention work-groups of a sequence carry its index blocks when
+    // there are enough of them (extra work-groups would each take a compute
+    // unit, the attention's LDS being that large)
+    f.index_in_attn = r->cfg.n_head_kv * n_split >= f.n_index_blocks ? 1 : 0;
+    f.slot_stride = (int32_t)r->L.slot_stride;
+    f.n_layer = r->cfg.n_layer;
+    f.a_step = r->geo.a_step;
+    f.trash_slot = r->geo.trash_slot;
+    f.layer_stride = (int64_t)r->cfg.n_head_kv * a.head_stride;
+    f.inv_freq = r->inv_freq;
+    f.slot_pos = r->slot_pos;
+    f.mask_full = r->mask;
+    f.mask_swa = r->mask_swa;
+    f.rope_noise_w = r->rope_noise;
+    f.rope_q_w = r->rope_q;
+    const int64_t kv_row = r->geo.kv_row;
+    for (int i = 0; i < 64; ++i) f.theta[i] = r->inv_freq_host[i];
+    FusedSeqs& fs = f.fs;
+    for (int i = 0; i < r->cfg.n_seq; ++i) {
+      const Pending& p = r->pending[i];
+      const int64_t c = r->committed[i];
+      const int64_t win = std::min<int64_t>(c, cap);
+      fs.committed[i] = (int32_t)c;
+      fs.lo[i] = (int32_t)(c - (swa ? std::min<int64_t>(r->cfg.swa_window, win) : win));
+      if (!p.active) continue;
+      fs.start[i] = (int32_t)p.start;
+      fs.start_mod[i] = (int32_t)(p.start % cap);
+      fs.n_step_rows[i] = (int32_t)p.n_new;
+      fs.full_lo[i] = (int32_t)p.lo;
+      fs.swa_lo[i] = (int32_t)p.swa_lo;
+      fs.index[i] = p.index_left ? 1 : 0;
+      if ((p.layers_left & bit) && p.n_new > 0) {
+        fs.k_new[i] = reinterpret_cast<uint64_t>(p.k + (int64_t)layer * p.n_new * kv_row);
+        fs.v_new[i] = reinterpret_cast<uint64_t>(p.v + (int64_t)layer * p.n_new * kv_row);
+        fs.n_new[i] = (int32_t)p.n_new;
+      }
+    }
+    if (int e = check_launch(launch_attn_fused(f, s, t0, t1), "ring_attn (fused step)")) return e;
+    for (Pending& p : r->pending) {
+      if (!p.active) continue;
+      p.layers_left &= ~bit;
+      p.index_left = false;
+      if (!p.layers_left) p = Pending{};
+    }
+  } else {
+    if (int e = check_launch(launch_attn(a, s, t0, t1), "ring_attn")) return e;
+  }
   if (n_split > 1) {
     MergeArgs m{};
     m.part_acc = r->part_acc;
@@ -676,8 +829,9 @@ int ring_read_slot_pos(const ring_t* r, int32_t seq, int32_t* host_out) {
   if (!r || !host_out) return fail(RING_EINVAL, "NULL argument");
   if (seq < 0 || seq >= r->cfg.n_seq) return fail(RING_ERANGE, "seq %d out of range", seq);
   if (int e = use_device(r)) return e;
+  if (int e = flush_all(const_cast<ring*>(r))) return e;
   if (hipDeviceSynchronize() != hipSuccess) return fail(RING_EDEVICE, "device synchronisation failed");
-  if (hipMemcpy(host_out, r->slot_pos + (int64_t)seq * r->cfg.cap, (size_t)r->cfg.cap * 4,
+  if (hipMemcpy(host_out, r->slot_pos + (int64_t)seq * r->L.slot_stride, (size_t)r->cfg.cap * 4,
                 hipMemcpyDeviceToHost) != hipSuccess)
     return fail(RING_EDEVICE, "hipMemcpy failed");
   return ok();
@@ -687,6 +841,7 @@ int ring_read_mask(const ring_t* r, int32_t seq, uint16_t* host_out) {
   if (!r || !host_out) return fail(RING_EINVAL, "NULL argument");
   if (seq < 0 || seq >= r->cfg.n_seq) return fail(RING_ERANGE, "seq %d out of range", seq);
   if (int e = use_device(r)) return e;
+  if (int e = flush_all(const_cast<ring*>(r))) return e;
   if (hipDeviceSynchronize() != hipSuccess) return fail(RING_EDEVICE, "device synchronisation failed");
   const size_t n = (size_t)r->cfg.q_len * r->geo.kv_total;
   if (hipMemcpy(host_out, r->mask + (int64_t)seq * n, n * 2, hipMemcpyDeviceToHost) != hipSuccess)
@@ -699,6 +854,7 @@ int ring_read_mask_swa(const ring_t* r, int32_t seq, uint16_t* host_out) {
   if (seq < 0 || seq >= r->cfg.n_seq) return fail(RING_ERANGE, "seq %d out of range", seq);
   if (!r->mask_swa) return fail(RING_ESTATE, "the ring has no sliding-window layers");
   if (int e = use_device(r)) return e;
+  if (int e = flush_all(const_cast<ring*>(r))) return e;
   if (hipDeviceSynchronize() != hipSuccess) return fail(RING_EDEVICE, "device synchronisation failed");
   const size_t n = (size_t)r->cfg.q_len * r->geo.kv_total;
   if (hipMemcpy(host_out, r->mask_swa + (int64_t)seq * n, n * 2, hipMemcpyDeviceToHost) != hipSuccess)
@@ -715,6 +871,7 @@ int ring_read_rows(const ring_t* r, int32_t seq, int32_t layer, int32_t slot0, i
     return fail(RING_ERANGE, "slots [%d, %d) out of [0, %d)", slot0, slot0 + n, r->geo.kv_total);
   if (n == 0) return ok();
   if (int e = use_device(r)) return e;
+  if (int e = flush_all(const_cast<ring*>(r))) return e;
   if (hipDeviceSynchronize() != hipSuccess) return fail(RING_EDEVICE, "device synchronisation failed");
   const int t0 = slot0 / kTile, t1 = (slot0 + n - 1) / kTile + 1;
   const int64_t head_stride = (int64_t)r->L.n_tiles * kTileHalves;

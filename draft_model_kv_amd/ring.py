@@ -30,7 +30,7 @@ RING_MAX_SEQ = 64
 # Every function the header declares, in header order.
 EXPORTS = (
     "ring_query_geometry", "ring_init", "ring_plan_step", "ring_plan_from_state",
-    "ring_begin_step", "ring_mirror_write", "ring_begin_step_mirror", "ring_attn", "ring_free",
+    "ring_begin_step", "ring_begin_step_deferred", "ring_mirror_write", "ring_begin_step_mirror", "ring_attn", "ring_free",
     "ring_last_error", "ring_describe",
     "ring_read_slot_pos", "ring_read_mask", "ring_read_mask_swa", "ring_read_rows",
     "ring_read_state",
@@ -95,6 +95,7 @@ def _load() -> ctypes.CDLL:
         "ring_plan_from_state": [ctypes.POINTER(RingConfig), I64, I64, I64,
                                  ctypes.POINTER(RingPlan), P],
         "ring_begin_step": [P, I32, I64, P, P, I64, P],
+        "ring_begin_step_deferred": [P, I32, I64, P, P, I64, P],
         "ring_mirror_write": [P, I32, I64, I64, P, P],
         "ring_begin_step_mirror": [P, I32, I64, ctypes.POINTER(RingKvWeights), P],
         "ring_attn": [P, I32, P, P, P, P, P],
@@ -173,6 +174,12 @@ def ring_begin_step(handle: int, seq: int, committed: int, k_new: int, v_new: in
                     n_rows: int, stream: int = 0) -> None:
     _check(_lib.ring_begin_step(handle, seq, committed, k_new or None, v_new or None,
                                 n_rows, stream or None), "ring_begin_step")
+
+
+def ring_begin_step_deferred(handle: int, seq: int, committed: int, k_new: int, v_new: int,
+                             n_rows: int, stream: int = 0) -> None:
+    _check(_lib.ring_begin_step_deferred(handle, seq, committed, k_new or None, v_new or None,
+                                         n_rows, stream or None), "ring_begin_step_deferred")
 
 
 def ring_mirror_write(handle: int, seq: int, pos0: int, n: int, features: int,
@@ -288,14 +295,17 @@ class Ring:
     def plan(self, seq: int, committed: int):
         return ring_plan_step(self.handle, seq, committed, self.a_step)
 
-    def begin_step(self, seq: int, committed: int, k_new, v_new) -> None:
+    def begin_step(self, seq: int, committed: int, k_new, v_new, deferred: bool = False) -> None:
+        """deferred: the rows are appended by the next attention of each layer
+        (k_new / v_new must then stay alive until those have run)."""
         torch = self._torch
         c = self.cfg
         n = 0 if k_new is None else k_new.shape[1]
         shape = (c.n_layer, n, self.geo.kv_row)
-        ring_begin_step(self.handle, seq, committed,
-                        self._ptr(k_new, torch.float16, shape, "k_new"),
-                        self._ptr(v_new, torch.float16, shape, "v_new"), n, self._stream())
+        fn = ring_begin_step_deferred if deferred else ring_begin_step
+        fn(self.handle, seq, committed,
+           self._ptr(k_new, torch.float16, shape, "k_new"),
+           self._ptr(v_new, torch.float16, shape, "v_new"), n, self._stream())
 
     def mirror_write(self, seq: int, pos0: int, features) -> None:
         """features: F16 [n, d_model] of positions [pos0, pos0 + n)."""

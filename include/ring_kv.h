@@ -172,6 +172,25 @@ int ring_begin_step(ring_t* r, int32_t seq, int64_t committed,
                     const void* k_new, const void* v_new, int64_t n_rows,
                     void* stream);
 
+/* ring_begin_step deferred into the attention launches (fused step).  Same
+ * arguments, plan, checks and result as ring_begin_step, and k_new / v_new
+ * must be 16-byte aligned.  For a fold-in plan nothing is enqueued here: the
+ * next ring_attn of each layer appends that layer's rows itself (before it
+ * reads their tiles) and the first of them also rebuilds slot_pos, the masks
+ * and the noise RoPE table, all in its one launch; pad rows are not written
+ * (the trash slot keeps its zeros).  k_new and v_new must therefore stay
+ * valid until every layer's ring_attn has been enqueued and the stream has
+ * passed them.  Whatever a deferred step still owes (layers whose attention
+ * has not run) is appended by the ordinary append kernel on the ring's last
+ * stream before any other call that needs it: a begin_step of the same
+ * sequence and the ring_read_* inspection calls.  A bulk plan, and rings
+ * with more than 8 sequences or 64 layers, append right away as
+ * ring_begin_step does.
+ * Errors: as ring_begin_step, and RING_EINVAL for misaligned rows.          */
+int ring_begin_step_deferred(ring_t* r, int32_t seq, int64_t committed,
+                             const void* k_new, const void* v_new, int64_t n_rows,
+                             void* stream);
+
 /* ---- New rows from fused features (feature mirror + K/V projection) ----
  * The page's notes on the port describe Luce's begin_step: the draft keeps a
  * mirror of the target's fused feature vectors with the ring's capacity

@@ -187,8 +187,10 @@ class Driver:
             written += len(pos)
         return written
 
-    def step(self, seq: int, committed: int):
-        """begin_step on both sides; the plans must agree exactly."""
+    def step(self, seq: int, committed: int, deferred: bool = False):
+        """begin_step on both sides; the plans must agree exactly.  deferred:
+        ring_begin_step_deferred (the rows are appended by the attention
+        launches; their tensors are kept alive until the next step)."""
         torch = self.torch
         if committed < self.committed[seq]:
             self.epochs[seq].rewind(committed)
@@ -213,9 +215,11 @@ class Driver:
         if len(pos):
             kt = torch.from_numpy(k).to(self.dev)
             vt = torch.from_numpy(v).to(self.dev)
-            self.ring.begin_step(seq, committed, kt, vt)
+            self.ring.begin_step(seq, committed, kt, vt, deferred=deferred)
+            self._keep = getattr(self, "_keep", {})
+            self._keep[seq] = (kt, vt)
         else:
-            self.ring.begin_step(seq, committed, None, None)
+            self.ring.begin_step(seq, committed, None, None, deferred=deferred)
         self.orc[seq].commit(op, list(k), list(v))
         self.committed[seq] = committed
         return op
@@ -316,6 +320,20 @@ class Driver:
         want = ro.rope_rows_f16(kn[seq], pq, w.n_head_kv, w.head_dim, w.rope_base)
         assert f16_ulp_diff(k, want).max() <= 1
         assert np.array_equal(v.view(np.uint16), vn[seq].view(np.uint16))
+
+    def check_attn_layers(self, step: int, seqs=None) -> Dict[str, float]:
+        """Attention of every layer first (so that a deferred step is carried
+        out by the attention launches themselves), then every comparison."""
+        res = [(layer,) + self.attn(layer, step) for layer in range(self.w.n_layer)]
+        worst = {"max_abs": 0.0, "max_rel": 0.0, "max_ratio": 0.0}
+        for layer, out, q, kn, vn in res:
+            for seq in (range(self.w.n_seq) if seqs is None else seqs):
+                ref = self.oracle_attn(seq, layer, q, kn, vn)
+                st = check_close(out[seq], ref, f"attn seq {seq} layer {layer} step {step}")
+                self.check_noise_rows(seq, layer, kn, vn)
+                for k_ in worst:
+                    worst[k_] = max(worst[k_], st[k_])
+        return worst
 
     def check_attn(self, layer: int, step: int, seqs=None, noise_rows: bool = True) -> Dict[str, float]:
         out, q, kn, vn = self.attn(layer, step)

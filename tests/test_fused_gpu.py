@@ -1,0 +1,155 @@
+"""The fused step (ring_begin_step_deferred): a fold-in's rows appended, and
+slot_pos, masks and noise RoPE table rebuilt, by the attention launch itself,
+against the CPU oracle (needs the GPU).
+
+Same bars as the other parity tests: index state bit-exact, ring K rows
+within one F16 ulp (V exact), attention within 2e-3 + 1e-2 |ref|.  Every
+check runs after the attention of all layers, so that the fused launches do
+the appending; the flush paths (a read, a partial set of layers, two steps in
+a row) are tested on their own.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+import workload as W
+from tests.harness import Driver
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def small(**kw):
+    base = dict(name="fused_edge", seed=300, cap=64, q_len=8, n_head=32, n_head_kv=8)
+    base.update(kw)
+    return W.Workload(**base)
+
+
+def run_fused(d, commits, seq=0, rows=True):
+    for t, c in enumerate(commits):
+        d.step(seq, c, deferred=True)
+        d.check_attn_layers(d.n_attn)
+        d.check_index(seq)
+        if rows:
+            for layer in range(d.w.n_layer):
+                d.check_rows(seq, layer)
+
+
+@pytest.mark.parametrize("commits", [
+    [40, 41, 47, 59, 64, 70, 77, 78],          # folds, one wrapping the ring end
+    [100, 118, 119, 127, 128],                 # n_new == a_step (no pads), then folds
+    [50, 40, 45, 20, 64, 70],                  # rewinds inside the window
+    [200, 150, 151, 300, 290, 291],            # rewinds that re-append (bulk: immediate)
+    [5, 5, 6, 6, 7],                           # zero-row steps
+], ids=["fold_wrap", "a_step", "rewind_near", "rewind_far", "zero_rows"])
+def test_fused_streams(commits):
+    d = Driver(small())
+    run_fused(d, commits)
+    d.close()
+
+
+def test_fused_ragged_cap_short_block():
+    d = Driver(small(cap=100, q_len=3, n_head=16, n_head_kv=4, seed=301))
+    run_fused(d, [7, 20, 57, 60, 99, 100, 101, 105, 130])
+    d.close()
+
+
+def test_fused_multi_layer_sliding_window():
+    """4 layers, layers 1 and 3 sliding over 16 positions (new rows that fall
+    before the window are still appended), full acceptance steps."""
+    d = Driver(small(cap=64, n_layer=4, swa_window=16, swa_layers=0b1010, seed=302))
+    run_fused(d, [40, 49, 58, 59, 60, 69, 78, 87, 88])
+    d.close()
+
+
+def test_fused_gqa8_outliers():
+    d = Driver(small(cap=256, n_head=64, sigma=1.0, outlier_p=0.01, seed=303))
+    run_fused(d, [300, 301, 309, 318, 330])
+    d.close()
+
+
+def test_fused_multi_seq():
+    w = small(cap=128, n_layer=2, n_seq=3, seed=304)
+    d = Driver(w)
+    plan = {0: [10, 11, 19, 140, 148], 1: [500, 501, 509, 510, 515], 2: [127, 128, 129, 136, 140]}
+    for t in range(5):
+        for seq in range(3):
+            d.step(seq, plan[seq][t], deferred=(t % 2 == 0 or seq != 1))
+        d.check_attn_layers(t)
+        for seq in range(3):
+            d.check_index(seq)
+            for layer in range(2):
+                d.check_rows(seq, layer)
+    d.close()
+
+
+def test_fused_flush_paths():
+    """A read right after the deferred step, attention of one layer of two,
+    and two deferred steps in a row: the owed rows go in by the ordinary
+    append kernel, and everything still matches."""
+    d = Driver(small(n_layer=2, seed=305))
+    d.step(0, 40, deferred=True)
+    d.check_index(0)                   # flush: rows of both layers appended now
+    for layer in range(2):
+        d.check_rows(0, layer)
+    d.check_attn_layers(0)
+    d.step(0, 45, deferred=True)
+    out0, q0, kn0, vn0 = d.attn(0, 1)  # layer 0 fused; layer 1 still owed
+    from tests.harness import check_close
+    check_close(out0[0], d.oracle_attn(0, 0, q0, kn0, vn0), "layer 0 alone")
+    d.step(0, 47, deferred=True)       # flushes layer 1 of the previous step
+    d.check_attn_layers(2)
+    d.check_index(0)
+    for layer in range(2):
+        d.check_rows(0, layer)
+    d.step(0, 49, deferred=True)
+    d.step(0, 52, deferred=True)       # nothing ran in between: all owed work flushed
+    d.check_attn_layers(3)
+    d.check_index(0)
+    for layer in range(2):
+        d.check_rows(0, layer)
+    d.close()
+
+
+def test_fused_decode_stream_full():
+    """The headline workload through the fused step: 4096-token prompt, then
+    60 decode steps, every one checked."""
+    w = W.WORKLOADS["decode_stream"]
+    d = Driver(w)
+    stream = W.commit_stream(w, 0)[: 1 + 60]
+    say("decode_stream fused", len(stream), "steps")
+    for t, c in enumerate(stream):
+        d.step(0, c, deferred=True)
+        d.check_attn_layers(t)
+        d.check_index(0)
+        if t in (0, 1, 30, len(stream) - 1):
+            d.check_rows(0, 0)
+    d.close()
+
+
+def test_fused_long_prompt_wrap_layers():
+    """5 layers of the long-prompt workload, 24 decode steps (every 4th
+    commits 8), fused."""
+    w = W.WORKLOADS["long_prompt_wrap"]
+    d = Driver(w)
+    stream = W.commit_stream(w, 0)
+    n_warm = W.n_warmup_steps(w)
+    for c in stream[:n_warm]:
+        d.step(0, c)
+    for t, c in enumerate(stream[n_warm:n_warm + 24]):
+        d.step(0, c, deferred=True)
+        if t % 3 == 0 or t == 23:
+            d.check_attn_layers(t)
+            d.check_index(0)
+        else:
+            for layer in range(w.n_layer):
+                d.attn(layer, t)
+    for layer in range(w.n_layer):
+        d.check_rows(0, layer)
+    d.close()
