@@ -224,9 +224,22 @@ PROFILE_RUNS = {
     # the same bench without the profiler (its HIP-event kernel times are
     # compared with the trace; the tracer itself slows event-bound dispatches)
     "bench_plain": "python REPO/bench.py --steps 1000 --warmup 100 --no-cpu-baseline",
+    # rows from the feature mirror: the projection kernel
+    "prof_ktrace_mirror": "rocprofv3 --kernel-trace --stats --output-format csv -d "
+                          "OUT/prof_ktrace_mirror -o run -- python REPO/bench.py --workload "
+                          "mirror_stream --steps 300 --warmup 30 --no-cpu-baseline",
+    "pmc_fetch_mirror": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/pmc_fetch_mirror "
+                        "-o run -- python REPO/bench.py --workload mirror_stream --steps 32 "
+                        "--warmup 8 --no-cpu-baseline",
+    "pmc_write_mirror": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/pmc_write_mirror "
+                        "-o run -- python REPO/bench.py --workload mirror_stream --steps 32 "
+                        "--warmup 8 --no-cpu-baseline",
+    "bench_plain_mirror": "python REPO/bench.py --workload mirror_stream --steps 300 --warmup 30 "
+                          "--no-cpu-baseline",
 }
 CALIBRATE_COPY_MIB = 1024
 KERNELS = ("k_ring_attn", "k_ring_step", "k_ring_merge")
+KERNELS_MIRROR = ("k_ring_project", "k_ring_step", "k_ring_attn", "k_ring_merge")
 
 
 def _csv_rows(out_dir: str, run: str, kind: str):
@@ -242,9 +255,10 @@ def _csv_rows(out_dir: str, run: str, kind: str):
     return rows
 
 
-def _kib_per_dispatch(out_dir: str, run: str, counter: str, pick) -> tuple:
+def _kib_per_dispatch(out_dir: str, run: str, counter: str, pick, grid=None) -> tuple:
     vals = [float(r["Counter_Value"]) for r in _csv_rows(out_dir, run, "counter_collection")
-            if r["Counter_Name"] == counter and pick(r["Kernel_Name"])]
+            if r["Counter_Name"] == counter and pick(r["Kernel_Name"])
+            and (grid is None or int(r["Grid_Size"]) == grid)]
     if not vals:
         raise ValueError(f"{run}: no {counter} values for the kernel")
     return sum(vals) / len(vals), len(vals)
@@ -343,11 +357,83 @@ def summarize_profiles(out_dir: str) -> int:
         lines.append(f"Average k_ring_attn duration in the kernel trace: {trace['k_ring_attn']:.2f} us.")
     with open(os.path.join(prof, "k_ring_attn_decode_stream_hbm_traffic.md"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
-    print(json.dumps({"written": ["profiles/k_ring_attn_decode_stream_kernel_trace.md",
-                                  "profiles/k_ring_attn_decode_stream_hbm_traffic.md",
-                                  "profiles/ring_attn_decode_stream_traffic.json"],
-                      "kernel_source_hash": khash}))
+    written = ["profiles/k_ring_attn_decode_stream_kernel_trace.md",
+               "profiles/k_ring_attn_decode_stream_hbm_traffic.md",
+               "profiles/ring_attn_decode_stream_traffic.json"]
+    if os.path.isdir(os.path.join(out_dir, "prof_ktrace_mirror")):
+        written += summarize_mirror(out_dir, khash, fetch_scale, write_scale)
+    print(json.dumps({"written": written, "kernel_source_hash": khash}))
     return 0
+
+
+def summarize_mirror(out_dir: str, khash: str, fetch_scale: float, write_scale: float):
+    """Kernel trace and HBM traffic of the mirror_stream workload (rows from
+    the feature mirror through the projection kernel)."""
+    import workload as W
+    prof = os.path.join(ROOT, "profiles")
+    w = W.WORKLOADS["mirror_stream"]
+    wl = (f"mirror_stream (cap {w.cap}, {w.n_layer} layers, d_model {w.d_model}, "
+          f"GQA {w.n_head}/{w.n_head_kv} x {w.head_dim}, cold weights)")
+    stats = _csv_rows(out_dir, "prof_ktrace_mirror", "kernel_stats")
+    bl = _bench_line(out_dir, "bench_plain_mirror")
+    lines = [f"# Kernel trace: k_ring_project and the ring kernels, {wl}", "",
+             f"Kernel source hash: `{khash}`", "", "Command (cd /tmp; TMPDIR=/tmp):", "",
+             f"    {PROFILE_RUNS['prof_ktrace_mirror']}", "",
+             "| kernel | calls | avg us | min us | max us | share of GPU time |",
+             "|---|---:|---:|---:|---:|---:|"]
+    trace = {}
+    for r in stats:
+        name = r["Name"]
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{float(r['Percentage']):.1f}% |")
+        short = next((k for k in KERNELS_MIRROR if k in name), None)
+        if short and short not in trace:
+            trace[short] = float(r["AverageNs"]) / 1e3
+    if bl:
+        ev = {k: v["avg_us"] for k, v in bl.get("kernels", {}).items()}
+        lines += ["", f"The same bench without the profiler (`{PROFILE_RUNS['bench_plain_mirror']}`), "
+                  "HIP events bound to the dispatches of its profiled segment: "
+                  + ", ".join(f"{k} {v:.2f} us" for k, v in ev.items() if v)
+                  + f"; {bl['value']:.0f} steps/s in its timed segment."]
+    with open(os.path.join(prof, "k_ring_project_mirror_stream_kernel_trace.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    # decode-step projection launches: one 32-row tile (grid = layers x K/V
+    # heads x d-slices work-groups of 256 threads); the prefill's 64-row
+    # launches have two
+    decode_grid = w.n_layer * 2 * w.n_head_kv * (w.d_model // 256) * 256
+    rows = {}
+    for k, grid in (("k_ring_project", decode_grid), ("k_ring_project (prefill)", 2 * decode_grid)):
+        f, nf = _kib_per_dispatch(out_dir, "pmc_fetch_mirror", "FETCH_SIZE",
+                                  lambda n: "k_ring_project" in n, grid)
+        wv, nw = _kib_per_dispatch(out_dir, "pmc_write_mirror", "WRITE_SIZE",
+                                   lambda n: "k_ring_project" in n, grid)
+        rows[k] = {"fetch_kib": f, "write_kib": wv, "dispatches": min(nf, nw),
+                   "hbm_bytes": f * 1024 * fetch_scale + wv * 1024 * write_scale}
+    weights = 2 * w.n_layer * w.kv_row * w.d_model * 2
+    p = rows["k_ring_project"]
+    lines = [f"# HBM traffic per dispatch: k_ring_project, {wl}", "",
+             f"Kernel source hash: `{khash}`", "", "Commands (cd /tmp; TMPDIR=/tmp), one counter per run:", "",
+             f"    {PROFILE_RUNS['pmc_fetch_mirror']}", f"    {PROFILE_RUNS['pmc_write_mirror']}", "",
+             f"Counters scaled as for the decode-stream summary (FETCH_SIZE x {fetch_scale:.3f}, "
+             f"WRITE_SIZE x {write_scale:.3f}, from a plain {CALIBRATE_COPY_MIB} MiB device copy).  "
+             "Decode-step launches (one 32-row tile, at most 18 rows) and the prefill's 64-row "
+             "launches (two tiles, the weights read once per tile) apart.", "",
+             "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled HBM MB |",
+             "|---|---:|---:|---:|---:|"]
+    for k, r in rows.items():
+        lines.append(f"| {k} | {r['dispatches']} | {r['fetch_kib']:.1f} | {r['write_kib']:.1f} | "
+                     f"{r['hbm_bytes'] / 1e6:.3f} |")
+    lines += ["", f"k_ring_project in a decode step: {p['fetch_kib'] * 1024 * fetch_scale / 1e6:.3f} MB "
+              f"read per launch against {weights / 1e6:.3f} MB of weights (every layer's wk and "
+              "wv, read once; the features add under 0.1 MB); writes are the fp32 partial sums of "
+              "the 256-dim feature slices."]
+    if "k_ring_project" in trace:
+        lines.append(f"Average k_ring_project duration in the kernel trace: {trace['k_ring_project']:.2f} us.")
+    with open(os.path.join(prof, "k_ring_project_mirror_stream_hbm_traffic.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    return ["profiles/k_ring_project_mirror_stream_kernel_trace.md",
+            "profiles/k_ring_project_mirror_stream_hbm_traffic.md"]
 
 
 def main() -> int:
