@@ -896,7 +896,7 @@ __device__ __forceinline__ void merge_store(const EpilogueArgs& a, unsigned char
   }
 }
 
-template <int MB, int NW, int RP, bool FUSED>
+template <int MB, int NW, int RP, bool FUSED, bool DEEP>
 __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs* fa,
                                           const FusedLane& fl, double theta_lane, int unit,
                                           int split, int vis_first, int vis_count,
@@ -1211,7 +1211,46 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
   //      before the current tile is processed (two tiles in registers); two
   //      query blocks have no room for that.
   constexpr bool kPrefetch = MB == 1;
-  if constexpr (kPrefetch) {
+  if constexpr (kPrefetch && DEEP) {
+    // waves with many tiles: the next two tiles are in flight while one is
+    // attended (a wave that has fewer loads its last tile again, unused)
+    half8 k1[8], v1[8];
+    uint32_t m1[MB][8];
+    int4 s1[4];
+    load_tile(ring_tile(min(tile + NW, tile_last)), k1, v1, m1, s1);
+    while (tile + 2 * NW < t1) {
+      half8 k2[8], v2[8];
+      uint32_t m2[MB][8];
+      int4 s2[4];
+      load_tile(ring_tile(tile + 2 * NW), k2, v2, m2, s2);
+      attend_tile<MB>(kc, vc, mw, a.cap - ring_tile(tile) * kTile, hl, qf, q_lds, lane, m_run,
+                      l_run, o);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        kc[c] = k1[c]; vc[c] = v1[c];
+        k1[c] = k2[c]; v1[c] = v2[c];
+      }
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) { mw[mb][j] = m1[mb][j]; m1[mb][j] = m2[mb][j]; }
+      tile += NW;
+    }
+    if (tile + NW < t1) {
+      attend_tile<MB>(kc, vc, mw, a.cap - ring_tile(tile) * kTile, hl, qf, q_lds, lane, m_run,
+                      l_run, o);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) { kc[c] = k1[c]; vc[c] = v1[c]; }
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) mw[mb][j] = m1[mb][j];
+      tile += NW;
+    }
+    if (tile < t1)
+      attend_tile<MB>(kc, vc, mw, a.cap - ring_tile(tile) * kTile, hl, qf, q_lds, lane, m_run,
+                      l_run, o);
+  } else if constexpr (kPrefetch) {
     // every tile but the wave's last one: its successor is fetched first
     while (tile + NW < t1) {
       half8 kn[8], vn[8];
@@ -1281,7 +1320,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
   }
 }
 
-template <int MB, int NW, int RP, bool FUSED>
+template <int MB, int NW, int RP, bool FUSED, bool DEEP = false>
 __device__ __forceinline__ void attn_entry(const AttnArgs& a, const FusedAttnArgs* fa) {
   using S = AttnShape<MB, NW, FUSED>;
   __shared__ __attribute__((aligned(16))) unsigned char lds[S::kTotalLds];
@@ -1325,14 +1364,14 @@ __device__ __forceinline__ void attn_entry(const AttnArgs& a, const FusedAttnArg
   const int seq = unit / a.n_head_kv;
   FusedLane fl{};
   if constexpr (FUSED) fl = fused_pick(fv, seq);
-  attn_body<MB, NW, RP, FUSED>(a, fa, fl, fv.theta, unit, split,
+  attn_body<MB, NW, RP, FUSED, DEEP>(a, fa, fl, fv.theta, unit, split,
                                __builtin_amdgcn_readlane(firstv, seq),
                                __builtin_amdgcn_readlane(countv, seq), lds, sm_m, sm_l);
 }
 
-template <int MB, int NW, int RP>
+template <int MB, int NW, int RP, bool DEEP>
 __global__ __launch_bounds__(NW * 64) void k_ring_attn(AttnArgs a) {
-  attn_entry<MB, NW, RP, false>(a, nullptr);
+  attn_entry<MB, NW, RP, false, DEEP>(a, nullptr);
 }
 
 // The fused launch: the attention work-groups first (same mapping as
@@ -1547,16 +1586,26 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s, hipEvent_t t0, hipEvent
   const int grid = a.n_seq * a.n_head_kv * a.n_split;
   // rope table passes: one float4 per thread covers q_len <= 8
   const bool one_pass = a.q_len <= 8;
+  // tiles per wave of the widest window: three or more take the two-deep prefetch
+  int max_count = 0;
+  for (int i = 0; i < a.n_seq && i < RING_MAX_SEQ_INTERNAL; ++i)
+    max_count = max_count > a.vis_count[i] ? max_count : a.vis_count[i];
+  const int per_wave = ((max_count + a.n_split - 1) / a.n_split + 3) / 4;
+  const bool deep = per_wave >= 3;
   if (a.m <= 32) {
-    if (one_pass)
-      hipExtLaunchKernelGGL((k_ring_attn<1, 4, 1>), dim3(grid), dim3(256), 0, s, t0, t1, 0, a);
-    else
-      hipExtLaunchKernelGGL((k_ring_attn<1, 4, 4>), dim3(grid), dim3(256), 0, s, t0, t1, 0, a);
+    if (one_pass) {
+      if (deep)
+        hipExtLaunchKernelGGL((k_ring_attn<1, 4, 1, true>), dim3(grid), dim3(256), 0, s, t0, t1, 0, a);
+      else
+        hipExtLaunchKernelGGL((k_ring_attn<1, 4, 1, false>), dim3(grid), dim3(256), 0, s, t0, t1, 0, a);
+    } else {
+      hipExtLaunchKernelGGL((k_ring_attn<1, 4, 4, false>), dim3(grid), dim3(256), 0, s, t0, t1, 0, a);
+    }
   } else {
     if (one_pass)
-      hipExtLaunchKernelGGL((k_ring_attn<2, 4, 1>), dim3(grid), dim3(256), 0, s, t0, t1, 0, a);
+      hipExtLaunchKernelGGL((k_ring_attn<2, 4, 1, false>), dim3(grid), dim3(256), 0, s, t0, t1, 0, a);
     else
-      hipExtLaunchKernelGGL((k_ring_attn<2, 4, 4>), dim3(grid), dim3(256), 0, s, t0, t1, 0, a);
+      hipExtLaunchKernelGGL((k_ring_attn<2, 4, 4, false>), dim3(grid), dim3(256), 0, s, t0, t1, 0, a);
   }
   return hipGetLastError();
 }
