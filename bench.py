@@ -4,6 +4,8 @@
 A step is one pass of the whole ring path for one sequence: ring_begin_step
 (fold-in append with RoPE + slot_pos + window mask) and ring_attn (masked GQA
 attention of the 8 noise queries over the 4096-slot ring, split-K + merge).
+On a ring of several sequences (batched_seqs) a step is one
+ring_begin_step_batch over all of them, then one ring_attn per layer.
 Workload: the draft-window decode stream (cap 4096, q_len 8, 32 query / 8 KV
 heads x 128, F16), warmed by a 4096-token bulk prefill; synthetic seeded
 inputs, already resident in device memory when timing starts.
@@ -451,6 +453,10 @@ def main() -> int:
                     help="eager: ring_begin_step's own append launch (default); fused: "
                          "ring_begin_step_deferred, the fold-in append and index rebuild "
                          "run inside the attention launch")
+    ap.add_argument("--begin", choices=("auto", "per_seq"), default="auto",
+                    help="eager step of a ring with several sequences: auto takes one "
+                         "ring_begin_step_batch call for all of them (default), per_seq one "
+                         "ring_begin_step call per sequence")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--summarize", metavar="OUT", default="",
@@ -505,6 +511,10 @@ def main() -> int:
     attn, optr = R.ring_attn, out.data_ptr()
     mirror = w.d_model > 0
     mwrite, mbegin = R.ring_mirror_write, R.ring_begin_step_mirror
+    batched = not fused and not mirror and w.n_seq > 1 and args.begin == "auto"
+    begin_batch = R.ring_begin_step_batch
+    # the batched call's argument lists, per call
+    columns = [[list(col) for col in zip(*c[1])] for c in calls] if batched else None
 
     def run(lo, hi):
         for t in range(lo, hi):
@@ -513,6 +523,8 @@ def main() -> int:
                 for seq, c, fp, c0, n in seqs:
                     mwrite(h, seq, c0, n, fp, s)
                     mbegin(h, seq, c, *wptr, s)
+            elif batched:
+                begin_batch(h, *columns[t], s)
             else:
                 for seq, c, kp, vp, n in seqs:
                     begin(h, seq, c, kp, vp, n, s)
@@ -613,7 +625,9 @@ def main() -> int:
         "dtype": "f16",
         "data": "synthetic (seeded normal F16 rows; accepted counts drawn from the "
                 "pages' 1422-verification share table)",
-        "config": {"workload": args.workload, "step": args.step, "cap": w.cap, "q_len": w.q_len,
+        "config": {"workload": args.workload, "step": args.step,
+                   **({"begin": "batch" if batched else "per_seq"} if w.n_seq > 1 else {}),
+                   "cap": w.cap, "q_len": w.q_len,
                    "n_head": w.n_head, "n_head_kv": w.n_head_kv, "head_dim": w.head_dim,
                    "n_layer": w.n_layer, "n_seq": w.n_seq, "kv_total": geo.kv_total,
                    "ring_pool": pool, "infinity_cache": "cold" if pool > 1 or ring_bytes > (256 << 20) else "warm",

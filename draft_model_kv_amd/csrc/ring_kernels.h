@@ -49,6 +49,30 @@ struct StepArgs {
   int32_t n_ds;
 };
 
+// Fold-in steps of several sequences in one append launch: the fields of
+// StepArgs that differ between sequences, per sequence.  Every sequence takes
+// blocks_per_seq work-groups (a_step rows of every layer, then the index
+// blocks), so that a work-group finds its sequence by one division.
+// Positions are below 2^31.
+constexpr int kStepBatch = 16;
+struct StepBatchArgs {
+  StepArgs a;                        // shared geometry; base pointers of sequence 0
+  int64_t seq_stride;                // halves between sequences in kring / vring
+  int32_t slot_stride;               // int32 per sequence in slot_pos
+  int32_t blocks_per_seq;
+  int32_t a_step;                    // rows per layer of a fold-in (new rows, then pad rows)
+  int32_t n_seq;                     // sequences of this launch, 1..kStepBatch
+  int32_t seq[kStepBatch];           // ring sequence index
+  int32_t start[kStepBatch];         // first new position
+  int32_t start_mod[kStepBatch];     // its slot
+  int32_t n_new[kStepBatch];         // new rows (0..a_step)
+  int32_t committed[kStepBatch];
+  int32_t lo[kStepBatch];
+  int32_t swa_lo[kStepBatch];
+  uint64_t k_new[kStepBatch];        // [n_layer][n_new][kv_row] F16, not rotated
+  uint64_t v_new[kStepBatch];
+};
+
 // Projection of new rows' K and V from fused features (one launch projects
 // at most kProjRows rows of every layer): raw K and V, in fp32, per d-slice
 // of kProjSlice feature dimensions, into the scratch the step kernel reads.
@@ -142,6 +166,7 @@ struct MergeArgs {
 // t0 / t1: optional events bound to the dispatch (start and end of the
 // kernel itself), or nullptr.
 hipError_t launch_step(const StepArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
+hipError_t launch_step_batch(const StepBatchArgs& b, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
 // The fused launch: appends and index work of a.fs[] plus the attention.
 hipError_t launch_attn_fused(const FusedAttnArgs& f, hipStream_t s, hipEvent_t t0, hipEvent_t t1);

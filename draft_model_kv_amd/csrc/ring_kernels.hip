@@ -5,6 +5,8 @@
 //                 fold-in with pad rows to the trash slot), then slot_pos,
 //                 the 0/-inf window mask and the noise RoPE table.
 //                 Page "DFLASH2_RING_PORT.md", sections 1.1-1.4.
+//                 k_ring_step_batch: the fold-in steps of several sequences
+//                 in one launch.
 //   k_ring_attn   masked GQA attention of the q_len noise queries over the
 //                 ring, split-K over 32-slot ring tiles, matrix-core QK^T and
 //                 PV, online softmax, per-workgroup merge of its waves; the
@@ -135,11 +137,12 @@ __device__ inline void index_block(const StepArgs& a, int mblk, int t) {
 // ---------------------------------------------------------------------------
 // begin_step: append + slot_pos + mask + noise RoPE table
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_ring_step(StepArgs a) {
+// Work-group blk of one sequence's launch: rows first (n_rows + n_pad of
+// every layer), then the index blocks.
+__device__ inline void step_block(const StepArgs& a, const int blk) {
   const int t = threadIdx.x;
   const int rows_per_layer = a.n_rows + a.n_pad;
   const int n_row_blocks = rows_per_layer * a.n_layer;
-  const int blk = blockIdx.x;
   const int kv_row = a.n_head_kv * kHeadDim;
   const int64_t head_stride = (int64_t)a.n_tiles * kTileHalves;
   const int64_t layer_stride = head_stride * a.n_head_kv;
@@ -240,6 +243,36 @@ __global__ __launch_bounds__(256) void k_ring_step(StepArgs a) {
   }
   if (!a.do_mask) return;
   index_block(a, blk - n_row_blocks, t);
+}
+
+__global__ __launch_bounds__(256) void k_ring_step(StepArgs a) { step_block(a, blockIdx.x); }
+
+// Fold-in steps of b.n_seq sequences: blocks_per_seq work-groups each.
+__global__ __launch_bounds__(256) void k_ring_step_batch(StepBatchArgs b) {
+  const int j = blockIdx.x / b.blocks_per_seq;
+  const int blk = blockIdx.x - j * b.blocks_per_seq;
+  StepArgs a = b.a;
+  const int64_t seq = b.seq[j];
+  a.kring += seq * b.seq_stride;
+  a.vring += seq * b.seq_stride;
+  a.slot_pos += seq * b.slot_stride;
+  const int64_t mask_stride = (int64_t)a.q_len * a.kv_total;
+  a.mask += seq * mask_stride;
+  if (a.mask_swa) a.mask_swa += seq * mask_stride;
+  a.rope_noise += seq * a.q_len * 128;
+  a.rope_q += seq * a.q_len * 128;
+  a.k_new = reinterpret_cast<const uint16_t*>(b.k_new[j]);
+  a.v_new = reinterpret_cast<const uint16_t*>(b.v_new[j]);
+  a.start = b.start[j];
+  a.start_mod = b.start_mod[j];
+  a.committed = b.committed[j];
+  a.lo = b.lo[j];
+  a.swa_lo = b.swa_lo[j];
+  a.n_new = b.n_new[j];
+  a.row0 = 0;
+  a.n_rows = a.n_new;
+  a.n_pad = b.a_step - a.n_new;
+  step_block(a, blk);
 }
 
 // ---------------------------------------------------------------------------
@@ -1579,6 +1612,14 @@ hipError_t launch_step(const StepArgs& a, hipStream_t s, hipEvent_t t0, hipEvent
   const int grid = row_blocks + mask_blocks;
   if (grid == 0) return hipSuccess;
   hipExtLaunchKernelGGL(k_ring_step, dim3(grid), dim3(256), 0, s, t0, t1, 0, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_step_batch(const StepBatchArgs& b, hipStream_t s, hipEvent_t t0,
+                             hipEvent_t t1) {
+  const int grid = b.n_seq * b.blocks_per_seq;
+  if (grid == 0) return hipSuccess;
+  hipExtLaunchKernelGGL(k_ring_step_batch, dim3(grid), dim3(256), 0, s, t0, t1, 0, b);
   return hipGetLastError();
 }
 

@@ -30,7 +30,7 @@ RING_MAX_SEQ = 64
 # Every function the header declares, in header order.
 EXPORTS = (
     "ring_query_geometry", "ring_init", "ring_plan_step", "ring_plan_from_state",
-    "ring_begin_step", "ring_begin_step_deferred", "ring_mirror_write", "ring_begin_step_mirror", "ring_attn", "ring_free",
+    "ring_begin_step", "ring_begin_step_deferred", "ring_begin_step_batch", "ring_mirror_write", "ring_begin_step_mirror", "ring_attn", "ring_free",
     "ring_last_error", "ring_describe",
     "ring_read_slot_pos", "ring_read_mask", "ring_read_mask_swa", "ring_read_rows",
     "ring_read_state",
@@ -96,6 +96,7 @@ def _load() -> ctypes.CDLL:
                                  ctypes.POINTER(RingPlan), P],
         "ring_begin_step": [P, I32, I64, P, P, I64, P],
         "ring_begin_step_deferred": [P, I32, I64, P, P, I64, P],
+        "ring_begin_step_batch": [P, I32, P, P, P, P, P, P],
         "ring_mirror_write": [P, I32, I64, I64, P, P],
         "ring_begin_step_mirror": [P, I32, I64, ctypes.POINTER(RingKvWeights), P],
         "ring_attn": [P, I32, P, P, P, P, P],
@@ -180,6 +181,22 @@ def ring_begin_step_deferred(handle: int, seq: int, committed: int, k_new: int, 
                              n_rows: int, stream: int = 0) -> None:
     _check(_lib.ring_begin_step_deferred(handle, seq, committed, k_new or None, v_new or None,
                                          n_rows, stream or None), "ring_begin_step_deferred")
+
+
+def ring_begin_step_batch(handle: int, seqs, committed, k_new, v_new, n_rows,
+                          stream: int = 0) -> None:
+    """seqs, committed, k_new, v_new (device addresses), n_rows: sequences of
+    equal length n, one entry per sequence."""
+    n = len(seqs)
+    if not (len(committed) == len(k_new) == len(v_new) == len(n_rows) == n):
+        raise ValueError("ring_begin_step_batch: argument lists differ in length")
+    a_seq = (ctypes.c_int32 * max(n, 1))(*seqs)
+    a_com = (ctypes.c_int64 * max(n, 1))(*committed)
+    a_k = (ctypes.c_void_p * max(n, 1))(*[p or None for p in k_new])
+    a_v = (ctypes.c_void_p * max(n, 1))(*[p or None for p in v_new])
+    a_n = (ctypes.c_int64 * max(n, 1))(*n_rows)
+    _check(_lib.ring_begin_step_batch(handle, n, a_seq, a_com, a_k, a_v, a_n, stream or None),
+           "ring_begin_step_batch")
 
 
 def ring_mirror_write(handle: int, seq: int, pos0: int, n: int, features: int,
@@ -306,6 +323,21 @@ class Ring:
         fn(self.handle, seq, committed,
            self._ptr(k_new, torch.float16, shape, "k_new"),
            self._ptr(v_new, torch.float16, shape, "v_new"), n, self._stream())
+
+    def begin_step_batch(self, steps) -> None:
+        """steps: (seq, committed, k_new, v_new) per sequence, as begin_step."""
+        torch = self._torch
+        c = self.cfg
+        seqs, com, kp, vp, ns = [], [], [], [], []
+        for seq, committed, k_new, v_new in steps:
+            n = 0 if k_new is None else k_new.shape[1]
+            shape = (c.n_layer, n, self.geo.kv_row)
+            seqs.append(seq)
+            com.append(committed)
+            kp.append(self._ptr(k_new, torch.float16, shape, "k_new"))
+            vp.append(self._ptr(v_new, torch.float16, shape, "v_new"))
+            ns.append(n)
+        ring_begin_step_batch(self.handle, seqs, com, kp, vp, ns, self._stream())
 
     def mirror_write(self, seq: int, pos0: int, features) -> None:
         """features: F16 [n, d_model] of positions [pos0, pos0 + n)."""

@@ -191,6 +191,24 @@ int ring_begin_step_deferred(ring_t* r, int32_t seq, int64_t committed,
                              const void* k_new, const void* v_new, int64_t n_rows,
                              void* stream);
 
+/* ring_begin_step for n distinct sequences at once (the batched decode, where
+ * every sequence commits its own accepted tokens each step; section 1.3's
+ * plan is per sequence).  Entry i is the call
+ *   ring_begin_step(r, seqs[i], committed[i], k_new[i], v_new[i], n_rows[i])
+ * with host arrays of n entries (the row pointers are device addresses).
+ * The result is that of those n calls; the fold-in plans among them are
+ * appended together, up to 16 sequences per launch of one append kernel,
+ * and bulk plans append as ring_begin_step does.  Every entry is checked
+ * before anything is enqueued, so a rejected call changes nothing.
+ *   n  0..n_seq (0: nothing to do)
+ * Errors: RING_ERANGE (n, a seq, a committed), RING_EINVAL (NULL array or
+ * rows, a sequence listed twice), RING_ESTATE (an n_rows != n_new),
+ * RING_EDEVICE.                                                             */
+int ring_begin_step_batch(ring_t* r, int32_t n, const int32_t* seqs,
+                          const int64_t* committed, const void* const* k_new,
+                          const void* const* v_new, const int64_t* n_rows,
+                          void* stream);
+
 /* ---- New rows from fused features (feature mirror + K/V projection) ----
  * The page's notes on the port describe Luce's begin_step: the draft keeps a
  * mirror of the target's fused feature vectors with the ring's capacity

@@ -187,6 +187,44 @@ class Driver:
             written += len(pos)
         return written
 
+    def _plan(self, seq: int, committed: int):
+        """The step's plan on both sides (they must agree exactly)."""
+        if committed < self.committed[seq]:
+            self.epochs[seq].rewind(committed)
+        lib_plan, lib_ap = self.ring.plan(seq, committed)
+        op = self.orc[seq].plan(committed)
+        got = (lib_plan.win, lib_plan.lo, lib_plan.start, lib_plan.n_new, bool(lib_plan.bulk))
+        want = (op.win, op.lo, op.start, op.n_new, op.bulk)
+        assert got == want, f"plan mismatch seq {seq} committed {committed}: {got} != {want}"
+        if op.bulk:
+            assert lib_plan.n_chunks == len(op.chunks)
+        else:
+            assert list(lib_ap[: self.geo.a_step]) == op.ap_rows
+        return op
+
+    def step_batch(self, items):
+        """ring_begin_step_batch over (seq, committed) pairs of distinct
+        sequences; the oracle commits each sequence's step."""
+        torch = self.torch
+        steps, keep, commits = [], {}, []
+        for seq, committed in items:
+            op = self._plan(seq, committed)
+            k, v = self.rows(seq, np.arange(op.start, committed, dtype=np.int64))
+            if op.n_new:
+                kt = torch.from_numpy(k).to(self.dev)
+                vt = torch.from_numpy(v).to(self.dev)
+                keep[seq] = (kt, vt)
+                steps.append((seq, committed, kt, vt))
+            else:
+                steps.append((seq, committed, None, None))
+            commits.append((seq, committed, op, k, v))
+        self.ring.begin_step_batch(steps)
+        torch.cuda.synchronize(self.dev)
+        for seq, committed, op, k, v in commits:
+            self.orc[seq].commit(op, list(k), list(v))
+            self.committed[seq] = committed
+        return [c[2] for c in commits]
+
     def step(self, seq: int, committed: int, deferred: bool = False):
         """begin_step on both sides; the plans must agree exactly.  deferred:
         ring_begin_step_deferred (the rows are appended by the attention
