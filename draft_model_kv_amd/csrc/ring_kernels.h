@@ -127,6 +127,8 @@ struct AttnArgs {
   int64_t head_stride;       // halves between KV heads (n_tiles * 4096)
   int32_t n_seq, n_head, n_head_kv, group, q_len, m, cap, kv_total, n_tiles;
   int32_t n_split;
+  int32_t n_rb;              // work-groups per (sequence, head, split), one per block of
+                             // 32 query rows (one-block kernel; 1 for the others)
   int32_t ring_tiles;        // tiles holding ring slots: ceil(cap / 32)
   // Visible ring tiles of each sequence: vis_count tiles from vis_first on,
   // circularly modulo ring_tiles (the window's slots, slot = position % cap).

@@ -723,7 +723,8 @@ template <int MB, bool FUSED>
 __device__ __forceinline__ void attend_noise_row(
     const AttnArgs& a, const FusedCtx& fx, const NoiseRow<MB>& nr, int r, uint16_t* kh,
     uint16_t* vh, uint16_t* rowk, uint16_t* rowv, int lane, int hl, int col, const QFrag<MB>& q,
-    const half8* q_lds, float (&m_run)[MB], float (&l_run)[MB], f32x16 (&o)[MB][4]) {
+    const half8* q_lds, float (&m_run)[MB], float (&l_run)[MB], f32x16 (&o)[MB][4],
+    bool store_row) {
   double2 cs = nr.cs;
   if constexpr (FUSED) sincos((double)(fx.committed + r) * fx.invf, &cs.y, &cs.x);
   double xr, yr;
@@ -731,12 +732,14 @@ __device__ __forceinline__ void attend_noise_row(
   const uint16_t kx = f64_to_f16_rne(xr), ky = f64_to_f16_rne(yr);
   // ring row cap + r of this layer and head
   const int slot = a.cap + r;
-  uint16_t* kt = kh + (int64_t)(slot >> 5) * kTileHalves;
-  uint16_t* vt = vh + (int64_t)(slot >> 5) * kTileHalves;
-  kt[k_frag_index(slot & 31, lane)] = kx;
-  kt[k_frag_index(slot & 31, lane + 64)] = ky;
-  vt[v_frag_index(slot & 31, lane)] = nr.vx;
-  vt[v_frag_index(slot & 31, lane + 64)] = nr.vy;
+  if (store_row) {
+    uint16_t* kt = kh + (int64_t)(slot >> 5) * kTileHalves;
+    uint16_t* vt = vh + (int64_t)(slot >> 5) * kTileHalves;
+    kt[k_frag_index(slot & 31, lane)] = kx;
+    kt[k_frag_index(slot & 31, lane + 64)] = ky;
+    vt[v_frag_index(slot & 31, lane)] = nr.vx;
+    vt[v_frag_index(slot & 31, lane + 64)] = nr.vy;
+  }
   // the row in LDS, private to this wave
   rowk[lane] = kx;
   rowk[lane + 64] = ky;
@@ -837,6 +840,7 @@ struct EpilogueArgs {
   gfloat* pml;
   bool one_split;
   int m, group, n_head;
+  int row0;  // first query row of this work-group's block(s)
 };
 
 template <int MB, int NW, int W>
@@ -868,13 +872,14 @@ __device__ __forceinline__ void merge_store(const EpilogueArgs& a, unsigned char
   lds_barrier();
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
-    const int n = mb * 32 + col;
+    const int nl = mb * 32 + col;   // row within the work-group's block(s)
+    const int n = a.row0 + nl;      // query row
     float mw_[NW], lw_[NW];
     float4 blk[NW][4];
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      mw_[w] = sm_m[w][n];
-      lw_[w] = sm_l[w][n];
+      mw_[w] = sm_m[w][nl];
+      lw_[w] = sm_l[w][nl];
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         if (w == W)
@@ -918,7 +923,7 @@ __device__ __forceinline__ void merge_store(const EpilogueArgs& a, unsigned char
                                            v[jj].w * inv};
       }
     } else {
-      if (W == 0 && hl == 0 && n < a.m) *(gf32x2*)(a.pml + n * 2) = f32x2{mx, lt};
+      if (W == 0 && hl == 0 && n < a.m) *(gf32x2*)(a.pml + nl * 2) = f32x2{mx, lt};
       // partial in fragment order [mb][block][jj][lane] float4: each store
       // instruction writes 1 KB contiguous.
 #pragma unroll
@@ -932,7 +937,7 @@ __device__ __forceinline__ void merge_store(const EpilogueArgs& a, unsigned char
 template <int MB, int NW, int RP, bool FUSED, bool DEEP>
 __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs* fa,
                                           const FusedLane& fl, double theta_lane, int unit,
-                                          int split, int vis_first, int vis_count,
+                                          int split, int row0, int vis_first, int vis_count,
                                           unsigned char* lds, float (*sm_m)[MB * 32],
                                           float (*sm_l)[MB * 32]) {
   using S = AttnShape<MB, NW, FUSED>;
@@ -992,11 +997,14 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
   // the epilogue (a scalar memory round trip); stores then go through
   // global-address-space pointers.
   uint64_t out_unit = (uint64_t)(a.out + ((int64_t)seq * a.q_len * a.n_head + g * a.group) * kHeadDim);
-  uint64_t pacc = (uint64_t)(a.part_acc + ((int64_t)unit * a.n_split + split) * MP * kHeadDim);
-  uint64_t pml = (uint64_t)(a.part_ml + ((int64_t)unit * a.n_split + split) * MP * 2);
+  // partial rows [row0, row0 + MP) of the split's n_rb * MP
+  const int64_t prow = ((int64_t)unit * a.n_split + split) * (MP * a.n_rb) + row0;
+  uint64_t pacc = (uint64_t)(a.part_acc + prow * kHeadDim);
+  uint64_t pml = (uint64_t)(a.part_ml + prow * 2);
   const EpilogueArgs ep{(gfloat*)keep_sgpr(out_unit), (gfloat*)keep_sgpr(pacc),
                         (gfloat*)keep_sgpr(pml), keep_sgpr(a.n_split == 1) != 0,
-                        keep_sgpr(a.m), keep_sgpr(a.group), keep_sgpr(a.n_head)};
+                        keep_sgpr(a.m), keep_sgpr(a.group), keep_sgpr(a.n_head),
+                        keep_sgpr(row0)};
 
   // Noise rows of this wave: r = rank, rank + W, ... with W the waves of the
   // (sequence, head); rank counts from the last wave of the last split, whose
@@ -1008,7 +1016,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
   unsigned qrow[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
-    const int n = mb * 32 + col;
+    const int n = row0 + mb * 32 + col;
     qrow[mb] = n < a.m ? n / a.group : 0;
   }
 
@@ -1039,7 +1047,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
   for (int k = 0; k < MB; ++k) {
     const int item = threadIdx.x + k * NT;
     const int c = (item >> 6) & 3, ln = item & 63;
-    const int n = min((item >> 8) * 32 + (ln & 31), a.m - 1), h2 = ln >> 5;
+    const int n = min(row0 + (item >> 8) * 32 + (ln & 31), a.m - 1), h2 = ln >> 5;
     const unsigned i = n / a.group, hh = n - i * a.group;
     const unsigned qo = (i * a.n_head + hh) * kHeadDim + 16 * c + 8 * h2;
     qx[k] = *(const half8*)(qseq + qo);
@@ -1164,7 +1172,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
   for (int k = 0; k < MB; ++k) {
     const int item = threadIdx.x + k * NT;
     const int mb = item >> 8, c = (item >> 6) & 3, ln = item & 63;
-    const bool valid = mb * 32 + (ln & 31) < a.m;
+    const bool valid = row0 + mb * 32 + (ln & 31) < a.m;
     half8 xh, xl, yh, yl;
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
@@ -1221,12 +1229,13 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
   uint16_t* rowk = reinterpret_cast<uint16_t*>(lds + S::kQBytes) + wave * 2 * kHeadDim;
   uint16_t* rowv = rowk + kHeadDim;
   if (rank < a.q_len) {
+    const bool store_rows = row0 == 0;  // one row block stores the rotated rows
     attend_noise_row<MB, FUSED>(a, fx, nr, rank, kh, vh, rowk, rowv, lane, hl, col, qf, q_lds, m_run,
-                         l_run, o);
+                         l_run, o, store_rows);
     for (int r = rank + n_waves; r < a.q_len; r += n_waves) {
       load_noise_row<MB, FUSED>(a, fx, seq, g, r, mask_seq, qrow, lane, nr);
       attend_noise_row<MB, FUSED>(a, fx, nr, r, kh, vh, rowk, rowv, lane, hl, col, qf, q_lds, m_run,
-                           l_run, o);
+                           l_run, o, store_rows);
     }
   }
 
@@ -1382,22 +1391,27 @@ __device__ __forceinline__ void attn_entry(const AttnArgs& a, const FusedAttnArg
                "s"(a.k_noise), "s"(a.v_noise), "s"(a.out), "s"(a.part_acc), "s"(a.part_ml),
                "s"(a.seq_stride), "s"(a.layer_offset), "s"(a.head_stride), "s"(a.n_seq),
                "s"(a.n_head), "s"(a.n_head_kv), "s"(a.group), "s"(a.q_len), "s"(a.m),
-               "s"(a.cap), "s"(a.kv_total), "s"(a.n_split), "s"(a.ring_tiles), "v"(firstv),
-               "v"(countv));
+               "s"(a.cap), "s"(a.kv_total), "s"(a.n_split), "s"(a.n_rb), "s"(a.ring_tiles),
+               "v"(firstv), "v"(countv));
+  // (the row blocks of one split follow each other, on the same XCD, so
+  // that the second read of a tile finds it in that XCD's L2)
   const int n_units = a.n_seq * a.n_head_kv;
-  int unit, split;
+  const int per_unit = a.n_split * a.n_rb;
+  int unit, r;
   if ((n_units & 7) == 0) {
     const int xcd = blockIdx.x & 7, k = blockIdx.x >> 3;
-    unit = ((k / a.n_split) << 3) + xcd;
-    split = k % a.n_split;
+    unit = ((k / per_unit) << 3) + xcd;
+    r = k % per_unit;
   } else {
-    unit = blockIdx.x / a.n_split;
-    split = blockIdx.x % a.n_split;
+    unit = blockIdx.x / per_unit;
+    r = blockIdx.x % per_unit;
   }
+  const int split = r / a.n_rb;
+  const int rb = r - split * a.n_rb;
   const int seq = unit / a.n_head_kv;
   FusedLane fl{};
   if constexpr (FUSED) fl = fused_pick(fv, seq);
-  attn_body<MB, NW, RP, FUSED, DEEP>(a, fa, fl, fv.theta, unit, split,
+  attn_body<MB, NW, RP, FUSED, DEEP>(a, fa, fl, fv.theta, unit, split, rb * S::MP,
                                __builtin_amdgcn_readlane(firstv, seq),
                                __builtin_amdgcn_readlane(countv, seq), lds, sm_m, sm_l);
 }
@@ -1624,7 +1638,7 @@ hipError_t launch_step_batch(const StepBatchArgs& b, hipStream_t s, hipEvent_t t
 }
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
-  const int grid = a.n_seq * a.n_head_kv * a.n_split;
+  const int grid = a.n_seq * a.n_head_kv * a.n_split * a.n_rb;
   // rope table passes: one float4 per thread covers q_len <= 8
   const bool one_pass = a.q_len <= 8;
   // tiles per wave of the widest window: three or more take the two-deep prefetch
@@ -1633,7 +1647,8 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s, hipEvent_t t0, hipEvent
     max_count = max_count > a.vis_count[i] ? max_count : a.vis_count[i];
   const int per_wave = ((max_count + a.n_split - 1) / a.n_split + 3) / 4;
   const bool deep = per_wave >= 3;
-  if (a.m <= 32) {
+  // one query block per work-group: m <= 32, or one work-group per row block
+  if (a.m <= 32 || a.n_rb > 1) {
     if (one_pass) {
       if (deep)
         hipExtLaunchKernelGGL((k_ring_attn<1, 4, 1, true>), dim3(grid), dim3(256), 0, s, t0, t1, 0, a);

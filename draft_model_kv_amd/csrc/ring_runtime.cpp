@@ -44,6 +44,9 @@ int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 struct Layout {
   int32_t n_tiles = 0, m = 0, mpad = 0, group = 0, n_split = 1;
   bool n_split_forced = false;
+  // attention work-groups per (sequence, head, split): one per 32 query rows
+  // (RING_ATTN_ROW_BLOCKS=0: one work-group holds both blocks of m > 32)
+  int32_t n_rb = 1;
   int64_t seq_stride = 0;  // halves per sequence in the K (or V) ring
   size_t off_k = 0, off_v = 0, off_slot = 0, off_mask = 0, off_mask_swa = 0, off_rope = 0,
          off_ropeq = 0, off_freq = 0;
@@ -56,10 +59,12 @@ struct Layout {
 constexpr int kMaxSplits = 64;  // each merge wave holds up to 16 splits in registers
 
 // Splits of the ring tiles per (sequence, KV head): enough work-groups to
-// cover the 256 compute units, at most 8 tiles per wave (measured: 16 ring
-// sequences of 4096 slots read 15% faster at 4 splits than at 2, where each
-// work-group's four waves stream 16 tiles each with one work-group per
-// compute unit), and at least one 32-slot tile per wave.
+// cover the 256 compute units, and about 8 tiles per wave read from HBM
+// (the n_rb work-groups of a split read the same tiles, the later ones from
+// L2), but at least one 32-slot tile per wave.  Measured (one work-group
+// per compute unit): 16 ring sequences of 4096 slots attend 15% faster at 4
+// splits than at 2 (16 tiles per wave); one 32768-slot ring with two query
+// blocks 17% faster at 16 splits than at 32 and 30% faster than at 8.
 // RING_ATTN_SPLITS (1..64) overrides the choice, for tuning and tests; the
 // override also holds for launches whose windows are narrower.
 bool splits_forced() {
@@ -67,11 +72,11 @@ bool splits_forced() {
   return env && std::atoi(env) >= 1;
 }
 
-int32_t choose_splits(const ring_config& c) {
-  const int n_units = c.n_seq * c.n_head_kv;
+int32_t choose_splits(const ring_config& c, int32_t n_rb) {
+  const int n_groups = c.n_seq * c.n_head_kv * n_rb;
   const int ring_tiles = (c.cap + kTile - 1) / kTile;
-  int s = std::max(1, (256 + n_units - 1) / n_units);
-  s = std::max(s, (ring_tiles + 31) / 32);
+  int s = std::max(1, (256 + n_groups - 1) / n_groups);
+  s = std::max(s, (ring_tiles + 32 * n_rb - 1) / (32 * n_rb));
   s = std::min(s, std::max(1, (ring_tiles + 3) / 4));
   if (const char* env = std::getenv("RING_ATTN_SPLITS")) {
     const int v = std::atoi(env);
@@ -122,7 +127,12 @@ void geometry_of(const ring_config& c, ring_geometry* g, Layout* L) {
   L->group = c.n_head / c.n_head_kv;
   L->m = c.q_len * L->group;
   L->mpad = L->m <= 32 ? 32 : 64;
-  L->n_split = choose_splits(c);
+  {
+    const char* env = std::getenv("RING_ATTN_ROW_BLOCKS");
+    const bool row_blocks = !(env && std::atoi(env) == 0);
+    L->n_rb = row_blocks ? L->mpad / 32 : 1;
+  }
+  L->n_split = choose_splits(c, L->n_rb);
   L->n_split_forced = splits_forced();
   L->seq_stride = (int64_t)c.n_layer * c.n_head_kv * L->n_tiles * kTileHalves;
   size_t off = 0;
@@ -761,6 +771,7 @@ int ring_attn(ring_t* r, int32_t layer, const void* q, const void* k_noise, cons
   a.kv_total = r->geo.kv_total;
   a.n_tiles = r->L.n_tiles;
   a.n_split = r->L.n_split;
+  a.n_rb = 1;
   const int64_t cap = r->cfg.cap;
   const int32_t ring_tiles = (int32_t)((cap + kTile - 1) / kTile);
   a.ring_tiles = ring_tiles;
@@ -857,6 +868,7 @@ int ring_attn(ring_t* r, int32_t layer, const void* q, const void* k_noise, cons
       if (!p.layers_left) p = Pending{};
     }
   } else {
+    a.n_rb = r->L.n_rb;
     if (int e = check_launch(launch_attn(a, s, t0, t1), "ring_attn")) return e;
   }
   if (n_split > 1) {

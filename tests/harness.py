@@ -104,15 +104,23 @@ class Epochs:
 class Driver:
     """One ring (all sequences, all layers) and its oracle twin."""
 
-    def __init__(self, w: W.Workload, n_split: Optional[int] = None, device: str = "cuda:0"):
+    def __init__(self, w: W.Workload, n_split: Optional[int] = None, device: str = "cuda:0",
+                 row_blocks: Optional[bool] = None):
+        """n_split: attention splits forced; row_blocks: False puts both
+        32-row query blocks of a KV head in one work-group (the library reads
+        both settings when the ring is created)."""
         import torch
         from draft_model_kv_amd import Ring
         self.torch = torch
         self.w = w
         self.dev = torch.device(device)
-        old = os.environ.get("RING_ATTN_SPLITS")
+        env = {}
         if n_split is not None:
-            os.environ["RING_ATTN_SPLITS"] = str(n_split)
+            env["RING_ATTN_SPLITS"] = str(n_split)
+        if row_blocks is not None:
+            env["RING_ATTN_ROW_BLOCKS"] = "1" if row_blocks else "0"
+        saved = {k: os.environ.get(k) for k in env}
+        os.environ.update(env)
         try:
             self.ring = Ring(cap=w.cap, q_len=w.q_len, n_head=w.n_head, n_head_kv=w.n_head_kv,
                              head_dim=w.head_dim, n_layer=w.n_layer, n_seq=w.n_seq,
@@ -120,11 +128,11 @@ class Driver:
                              swa_window=w.swa_window, swa_layers=w.swa_layers,
                              d_model=w.d_model)
         finally:
-            if n_split is not None:
-                if old is None:
-                    del os.environ["RING_ATTN_SPLITS"]
+            for k, v in saved.items():
+                if v is None:
+                    del os.environ[k]
                 else:
-                    os.environ["RING_ATTN_SPLITS"] = old
+                    os.environ[k] = v
         self.geo = ro.geometry(w.cap, w.q_len, w.head_dim, w.n_head_kv)
         self.orc = [ro.RingStep(self.geo, w.n_layer, w.n_head_kv, w.head_dim, w.rope_base)
                     for _ in range(w.n_seq)]

@@ -95,11 +95,27 @@ def test_ragged_cap_and_short_block():
     d.close()
 
 
-def test_gqa8_outliers_two_query_blocks():
-    """64 query heads over 8 KV heads: 64 queries per KV head, +-30 outliers."""
+@pytest.mark.parametrize("row_blocks,n_split", [(True, None), (False, None), (True, 1),
+                                                (True, 3)],
+                         ids=["row_blocks", "one_workgroup", "row_blocks_one_split",
+                              "row_blocks_3_splits"])
+def test_gqa8_outliers_two_query_blocks(row_blocks, n_split):
+    """64 query heads over 8 KV heads: 64 queries per KV head, +-30 outliers;
+    the two 32-row query blocks in work-groups of their own (default) or in
+    one work-group."""
     w = small(cap=256, n_head=64, sigma=1.0, outlier_p=0.01, seed=104)
-    d = Driver(w)
+    d = Driver(w, n_split=n_split, row_blocks=row_blocks)
     run_steps(d, [300, 301, 305, 313, 330])
+    d.close()
+
+
+@pytest.mark.parametrize("row_blocks", [True, False], ids=["row_blocks", "one_workgroup"])
+def test_long_noise_block_two_query_blocks(row_blocks):
+    """q_len 16 with GQA 4 (m = 64): several rope-table passes, noise rows
+    spread over more waves, a ragged cap, two query blocks."""
+    w = small(cap=200, q_len=16, n_head=32, seed=110)
+    d = Driver(w, row_blocks=row_blocks)
+    run_steps(d, [150, 151, 170, 203, 230, 231])
     d.close()
 
 
