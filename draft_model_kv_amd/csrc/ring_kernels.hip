@@ -29,12 +29,16 @@ constexpr float kNegInf = -__builtin_inff();
 // change no output at the precision that is kept.
 __device__ inline float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 // sin and cos of an angle x (radians, fp64): x is reduced to the nearest
-// whole turn in fp64 (exact for the positions and frequencies here: |x| <
-// 2^31), the remaining fraction of a turn (|f| <= 1/2) goes to fp32 sincos.
+// whole turn in fp64 (|x| < 2^31 here, so the reduction loses at most about
+// 2e-7 rad), and the remaining fraction of a turn (|f| <= 1/2), rounded to
+// fp32, goes to the hardware sine and cosine, which take their argument in
+// turns (measured on gfx950 over [-1/2, 1/2] against fp64: at most 1.25e-7
+// absolute error, below the fp32 sincosf of f * 2 pi at 2.1e-7).
 __device__ inline void sincos_turns_f32(double x, float& s, float& c) {
   const double turns = x * 0.15915494309189533577;  // 1 / (2 pi)
-  const double f = turns - rint(turns);
-  sincosf((float)(f * 6.283185307179586477), &s, &c);
+  const float f = (float)(turns - rint(turns));
+  s = __builtin_amdgcn_sinf(f);
+  c = __builtin_amdgcn_cosf(f);
 }
 
 // log2(e) / sqrt(128): folds the 1/sqrt(head_dim) score scale and the
@@ -456,11 +460,17 @@ __device__ inline StepArgs fused_index_args(const FusedAttnArgs& f, const FusedL
   return sa;
 }
 
+// Global-memory pointers for rows that arrive as integer addresses: loads
+// through a generic pointer become flat loads, and a flat load in flight
+// makes the compiler wait for every other load before the next use of any.
+typedef const __attribute__((address_space(1))) uint16_t gcu16;
+typedef const __attribute__((address_space(1))) half8 gchalf8;
+
 // What a fused launch tells the attention body about its sequence's
 // deferred step (unused in a plain launch).
 struct FusedCtx {
-  const uint16_t* k_new;    // this layer's new K rows, at this KV head's column
-  const uint16_t* v_new;
+  gcu16* k_new;             // this layer's new K rows, at this KV head's column
+  gcu16* v_new;
   const int32_t* slot_pos;  // the sequence's slot_pos row
   double invf;              // theta of frequency `lane`
   int kv_row;
@@ -486,8 +496,7 @@ __device__ inline uint32_t new_rows_mask(const FusedCtx& fx, int tile, int lane)
 
 // Raw K and V of the first four new rows of a tile (mask nm), 16 bytes per
 // lane: lane l holds bytes [16 (l % 16), +16) of row l / 16's head slice.
-__device__ inline void load_new_rows4(const FusedCtx& fx, int tile, uint32_t nm, int lane,
-                                      half8& kraw, half8& vraw) {
+__device__ inline int64_t new_rows4_offset(const FusedCtx& fx, int tile, uint32_t nm, int lane) {
   uint32_t left = nm;
   int r[4], nr = 0;
 #pragma unroll
@@ -498,9 +507,13 @@ __device__ inline void load_new_rows4(const FusedCtx& fx, int tile, uint32_t nm,
   const int rl = r[min(lane >> 4, nr - 1)];
   int dl = tile * kTile + rl - fx.start_mod;
   if (dl < 0) dl += fx.cap;
-  const int64_t ro = (int64_t)dl * fx.kv_row + 8 * (lane & 15);
-  kraw = *(const half8*)(fx.k_new + ro);
-  vraw = *(const half8*)(fx.v_new + ro);
+  return (int64_t)dl * fx.kv_row + 8 * (lane & 15);
+}
+__device__ inline void load_new_rows4(const FusedCtx& fx, int tile, uint32_t nm, int lane,
+                                      half8& kraw, half8& vraw) {
+  const int64_t ro = new_rows4_offset(fx, tile, nm, lane);
+  kraw = *(gchalf8*)(fx.k_new + ro);
+  vraw = *(gchalf8*)(fx.v_new + ro);
 }
 
 // Rotate the new rows of ring tile `tile` (slot mask nm, nonzero): K at its
@@ -969,8 +982,8 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
   FusedCtx fx{};
   if constexpr (FUSED) {
     const int kv_row = a.n_head_kv * kHeadDim;
-    fx.k_new = fl.k_new ? (const uint16_t*)fl.k_new + g * kHeadDim : nullptr;
-    fx.v_new = fl.v_new ? (const uint16_t*)fl.v_new + g * kHeadDim : nullptr;
+    fx.k_new = fl.k_new ? (gcu16*)fl.k_new + g * kHeadDim : nullptr;
+    fx.v_new = fl.v_new ? (gcu16*)fl.v_new + g * kHeadDim : nullptr;
     fx.slot_pos = fa->slot_pos + (int64_t)seq * fa->slot_stride;
     fx.invf = theta_lane;
     fx.kv_row = kv_row;
@@ -1066,12 +1079,12 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
   //  spv[jj] = slots 8 jj + 4 (lane / 32) + 0..3.)
   auto load_tile = [&](int tile, half8 (&kc)[8], half8 (&vc)[8], uint32_t (&mw)[MB][8],
                        int4 (&spv)[4]) {
+    // K, then the mask words (or slot_pos), then V: loads return in issue
+    // order, so S = Q K^T and the softmax can run while V is in flight.
     const half8* kt = (const half8*)(kh + (int64_t)tile * kTileHalves);
     const half8* vt = (const half8*)(vh + (int64_t)tile * kTileHalves);
 #pragma unroll
     for (int c = 0; c < 8; ++c) kc[c] = kt[c * 64 + lane];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) vc[c] = vt[c * 64 + lane];
     if constexpr (FUSED) {
       const int4* sp = (const int4*)(fx.slot_pos + tile * kTile + 4 * hl);
 #pragma unroll
@@ -1089,22 +1102,31 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
         }
       }
     }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) vc[c] = vt[c * 64 + lane];
   };
   int tile = t0 + wave;
   const int tile_last = max(t1 - 1, 0);
   // Fused launch: the first group of new rows of the wave's first tile is
   // loaded ahead of the tile, so that their rotation overlaps its arrival.
+  // The loads are issued whether or not that tile has new rows (from the
+  // tile's own ring rows when it has none, and ignored): a load in a branch
+  // makes the compiler drain every load in flight where the branch joins.
   int pre_tile = -1;
   half8 pre_k = {}, pre_v = {};
   if constexpr (FUSED) {
-    if (fx.n_new > 0 && tile < t1) {
-      const int rt0 = ring_tile(tile);
-      const uint32_t nm0 = new_rows_mask(fx, rt0, lane);
-      if (nm0) {
-        load_new_rows4(fx, rt0, nm0, lane, pre_k, pre_v);
-        pre_tile = rt0;
-      }
+    const int rt0 = ring_tile(min(tile, tile_last));
+    const uint32_t nm0 = (fx.n_new > 0 && tile < t1) ? new_rows_mask(fx, rt0, lane) : 0u;
+    gchalf8* ks = (gchalf8*)(kh + (int64_t)rt0 * kTileHalves) + lane;
+    gchalf8* vs = (gchalf8*)(vh + (int64_t)rt0 * kTileHalves) + lane;
+    if (nm0) {
+      const int64_t ro = new_rows4_offset(fx, rt0, nm0, lane);
+      ks = (gchalf8*)(fx.k_new + ro);
+      vs = (gchalf8*)(fx.v_new + ro);
+      pre_tile = rt0;
     }
+    pre_k = *ks;
+    pre_v = *vs;
   }
   half8 kc[8], vc[8];
   uint32_t mw[MB][8];
@@ -1144,8 +1166,9 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
   if constexpr (FUSED) {
     // (cos, sin) of frequencies f0, f0 + 1 at noise position committed + i,
     // entry o = items 2o, 2o + 1 of [q_len][64], for the query rotation only:
-    // the angle reduced modulo a turn in fp64, then fp32 sincos (error about
-    // 3e-7, below the 2^-22 of the hi + lo F16 split the queries get)
+    // the angle reduced modulo a turn in fp64, then the hardware sine and
+    // cosine of the fraction (at most about 4e-7 rad in all, the order of
+    // the 2^-22 relative precision that the hi + lo F16 split of a query keeps)
 #pragma unroll
     for (int k = 0; k < RP; ++k) {
       const int o = min((int)threadIdx.x + k * NT, a.q_len * 32 - 1);
