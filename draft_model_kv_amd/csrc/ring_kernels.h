@@ -85,6 +85,7 @@ struct ProjArgs {
   const uint16_t* wv;        // [n_layer][kv_row][d_model] F16
   float* scratch;            // [n_layer][n_ds][kProjRows][2 * kv_row]
   int64_t pos0;              // position of this launch's row 0
+  int32_t slot0;             // its mirror slot, pos0 % cap
   int32_t n_rows;            // rows of this launch, 1..kProjRows
   int32_t cap, d_model, kv_row, n_head_kv, n_layer, n_ds;
 };

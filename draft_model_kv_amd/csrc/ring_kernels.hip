@@ -1571,6 +1571,10 @@ __global__ __launch_bounds__(256) void k_ring_merge(MergeArgs a) {
 __global__ __launch_bounds__(256) void k_ring_project(ProjArgs a) {
   constexpr int kRowStride = kProjSlice / 8 + 1;  // half8 per staged row (+1: no bank conflicts)
   __shared__ half8 f_lds[32 * kRowStride];
+  // every argument fetched in one batch at entry (see attn_entry)
+  asm volatile("" ::"s"(a.mirror), "s"(a.wk), "s"(a.wv), "s"(a.scratch), "s"(a.slot0),
+               "s"(a.n_rows), "s"(a.cap), "s"(a.d_model), "s"(a.kv_row), "s"(a.n_head_kv),
+               "s"(a.n_ds));
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n_rt = (a.n_rows + 31) >> 5;
@@ -1585,6 +1589,19 @@ __global__ __launch_bounds__(256) void k_ring_project(ProjArgs a) {
   const int r0 = rt * 32;
   const int d0 = ds * kProjSlice;
 
+  // features of the tile's rows, first (loads return in issue order, and
+  // the LDS staging needs them): 32 rows x 32 chunks of 16 B, 4 per thread;
+  // row i sits in mirror slot (slot0 + i) % cap
+  half8 fv[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int c = threadIdx.x + 256 * k;
+    const int row = c >> 5, dc = c & 31;
+    const int slot = (a.slot0 + min(r0 + row, a.n_rows - 1)) % a.cap;
+    const uint16_t* src = a.mirror + (int64_t)slot * a.d_model + d0 + 8 * dc;
+    fv[k] = *(const half8*)src;
+  }
+
   // weights: row 32 w + lane % 32 of the head part, 4 blocks x 64 B
   const bool is_v = hp >= a.n_head_kv;
   const int head = is_v ? hp - a.n_head_kv : hp;
@@ -1597,17 +1614,8 @@ __global__ __launch_bounds__(256) void k_ring_project(ProjArgs a) {
   for (int blk = 0; blk < 4; ++blk)
 #pragma unroll
     for (int j = 0; j < 4; ++j) wa[blk][j] = *(const half8*)(wrow + blk * 64 + 8 * j);
-
-  // features of the tile's rows: 32 rows x 32 chunks of 16 B, 4 per thread
-  half8 fv[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int c = threadIdx.x + 256 * k;
-    const int row = c >> 5, dc = c & 31;
-    const int64_t pos = a.pos0 + min(r0 + row, a.n_rows - 1);
-    const uint16_t* src = a.mirror + (pos % a.cap) * a.d_model + d0 + 8 * dc;
-    fv[k] = *(const half8*)src;
-  }
+  // every weight load is issued before the wait for the features
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int c = threadIdx.x + 256 * k;

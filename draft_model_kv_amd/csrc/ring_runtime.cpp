@@ -714,6 +714,7 @@ int ring_begin_step_mirror(ring_t* r, int32_t seq, int64_t committed, const ring
   do {
     const int32_t n = (int32_t)std::min<int64_t>(kProjRows, p.n_new - row0);
     pa.pos0 = p.start + row0;
+    pa.slot0 = (int32_t)(pa.pos0 % r->cfg.cap);
     pa.n_rows = n;
     hipEvent_t t0, t1;
     if (n > 0) {
