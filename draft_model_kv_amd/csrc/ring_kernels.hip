@@ -41,6 +41,19 @@ __device__ inline void sincos_turns_f32(double x, float& s, float& c) {
   c = __builtin_amdgcn_cosf(f);
 }
 
+// sin and cos (fp64) of a rotary angle x = p * theta (|x| < 2^31): x less
+// the nearest whole number of turns, with 2 pi split into two doubles (Cody
+// and Waite, "Software Manual for the Elementary Functions", 1980) and each
+// product taken off by one fused multiply-add (error below 1e-15 for
+// |x| < 2^31), then the library sincos of the reduced angle, |r| <= pi, which
+// needs none of its long argument reduction.
+__device__ inline void sincos_angle(double x, double* s, double* c) {
+  const double k = rint(x * 0.15915494309189535);       // 1 / (2 pi)
+  double r = fma(-k, 6.283185307179586, x);             // 2 pi, leading double
+  r = fma(-k, 2.4492935982947064e-16, r);               // 2 pi, the rest
+  sincos(r, s, c);
+}
+
 // log2(e) / sqrt(128): folds the 1/sqrt(head_dim) score scale and the
 // change of base for exp2 into the query.
 constexpr double kQScale = 1.4426950408889634074 / 11.313708498984760390;
@@ -127,7 +140,7 @@ __device__ inline void index_block(const StepArgs& a, int mblk, int t) {
     for (int item = t; item < a.q_len * 64; item += 256) {
       const int i = item >> 6, f = item & 63;
       double sn, cs;
-      sincos((double)(a.committed + i) * a.inv_freq[f], &sn, &cs);
+      sincos_angle((double)(a.committed + i) * a.inv_freq[f], &sn, &cs);
       a.rope_noise[2 * item] = cs;
       a.rope_noise[2 * item + 1] = sn;
       a.rope_q[2 * item] = (float)cs;
@@ -172,7 +185,7 @@ __device__ inline void step_block(const StepArgs& a, const int blk) {
       }
       if (t < 64) {
         double sn, cs;
-        sincos((double)p * a.inv_freq[t], &sn, &cs);
+        sincos_angle((double)p * a.inv_freq[t], &sn, &cs);
         cs_row[t] = make_double2(cs, sn);
       }
     } else {
@@ -557,7 +570,7 @@ __device__ __forceinline__ void prepare_new_rows(const FusedCtx& fx, int tile, u
       if (dd < 0) dd += fx.cap;
       const uint16_t* rk = raw + k * 256;
       double sn, cs;
-      sincos((double)(fx.start + dd) * fx.invf, &sn, &cs);
+      sincos_angle((double)(fx.start + dd) * fx.invf, &sn, &cs);
       double xr, yr;
       rot_pair(f16_to_f64(rk[lane]), f16_to_f64(rk[lane + 64]), cs, sn, xr, yr);
       const uint16_t kx = f64_to_f16_rne(xr), ky = f64_to_f16_rne(yr);
@@ -739,7 +752,7 @@ __device__ __forceinline__ void attend_noise_row(
     const half8* q_lds, float (&m_run)[MB], float (&l_run)[MB], f32x16 (&o)[MB][4],
     bool store_row) {
   double2 cs = nr.cs;
-  if constexpr (FUSED) sincos((double)(fx.committed + r) * fx.invf, &cs.y, &cs.x);
+  if constexpr (FUSED) sincos_angle((double)(fx.committed + r) * fx.invf, &cs.y, &cs.x);
   double xr, yr;
   rot_pair(f16_to_f64(nr.kx), f16_to_f64(nr.ky), cs.x, cs.y, xr, yr);
   const uint16_t kx = f64_to_f16_rne(xr), ky = f64_to_f16_rne(yr);
@@ -1374,7 +1387,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
         for (int item = threadIdx.x; item < a.q_len * 64; item += NT) {
           const int i = item >> 6, f = item & 63;
           double sn, cs;
-          sincos((double)(fx.committed + i) * fa->theta[f], &sn, &cs);
+          sincos_angle((double)(fx.committed + i) * fa->theta[f], &sn, &cs);
           sa.rope_noise[2 * item] = cs;
           sa.rope_noise[2 * item + 1] = sn;
           sa.rope_q[2 * item] = (float)cs;
