@@ -239,6 +239,19 @@ PROFILE_RUNS = {
     "bench_plain_mirror": "python REPO/bench.py --workload mirror_stream --steps 300 --warmup 30 "
                           "--no-cpu-baseline",
 }
+# the attention on the wider workloads (16 rings; one 32768-slot ring with
+# two query blocks per KV head)
+WIDE_WORKLOADS = ("batched_seqs", "large_window")
+for _wl in WIDE_WORKLOADS:
+    PROFILE_RUNS[f"bench_plain_{_wl}"] = (f"python REPO/bench.py --workload {_wl} --steps 200 "
+                                          "--warmup 20 --no-cpu-baseline")
+    PROFILE_RUNS[f"prof_ktrace_{_wl}"] = (f"rocprofv3 --kernel-trace --stats --output-format csv -d "
+                                          f"OUT/prof_ktrace_{_wl} -o run -- python REPO/bench.py "
+                                          f"--workload {_wl} --steps 200 --warmup 20 --no-cpu-baseline")
+    for _c in ("fetch", "write"):
+        PROFILE_RUNS[f"pmc_{_c}_{_wl}"] = (f"rocprofv3 --pmc {_c.upper()}_SIZE --output-format csv "
+                                           f"-d OUT/pmc_{_c}_{_wl} -o run -- python REPO/bench.py "
+                                           f"--workload {_wl} --steps 16 --warmup 4 --no-cpu-baseline")
 CALIBRATE_COPY_MIB = 1024
 KERNELS = ("k_ring_attn", "k_ring_step", "k_ring_merge")
 KERNELS_MIRROR = ("k_ring_project", "k_ring_step", "k_ring_attn", "k_ring_merge")
@@ -364,6 +377,9 @@ def summarize_profiles(out_dir: str) -> int:
                "profiles/ring_attn_decode_stream_traffic.json"]
     if os.path.isdir(os.path.join(out_dir, "prof_ktrace_mirror")):
         written += summarize_mirror(out_dir, khash, fetch_scale, write_scale)
+    for wl_name in WIDE_WORKLOADS:
+        if os.path.isdir(os.path.join(out_dir, f"prof_ktrace_{wl_name}")):
+            written.append(summarize_wide(out_dir, wl_name, khash, fetch_scale, write_scale))
     print(json.dumps({"written": written, "kernel_source_hash": khash}))
     return 0
 
@@ -436,6 +452,52 @@ def summarize_mirror(out_dir: str, khash: str, fetch_scale: float, write_scale: 
         fh.write("\n".join(lines) + "\n")
     return ["profiles/k_ring_project_mirror_stream_kernel_trace.md",
             "profiles/k_ring_project_mirror_stream_hbm_traffic.md"]
+
+
+def summarize_wide(out_dir: str, wl_name: str, khash: str, fetch_scale: float,
+                   write_scale: float) -> str:
+    """Kernel trace and HBM traffic of k_ring_attn on one of the wider
+    workloads, with the bench line's algorithmic bytes per launch."""
+    import workload as W
+    prof = os.path.join(ROOT, "profiles")
+    w = W.WORKLOADS[wl_name]
+    wl = (f"{wl_name} ({w.n_seq} x cap {w.cap}, q_len {w.q_len}, GQA {w.n_head}/{w.n_head_kv} x "
+          f"{w.head_dim}, {w.n_layer} layer)")
+    stats = _csv_rows(out_dir, f"prof_ktrace_{wl_name}", "kernel_stats")
+    bl = _bench_line(out_dir, f"bench_plain_{wl_name}")
+    lines = [f"# k_ring_attn on {wl}", "", f"Kernel source hash: `{khash}`", "",
+             "Commands (cd /tmp; TMPDIR=/tmp):", ""]
+    lines += [f"    {PROFILE_RUNS[r]}" for r in (f"prof_ktrace_{wl_name}", f"pmc_fetch_{wl_name}",
+                                                 f"pmc_write_{wl_name}", f"bench_plain_{wl_name}")]
+    lines += ["", "| kernel | calls | avg us | min us | max us | share of GPU time |",
+              "|---|---:|---:|---:|---:|---:|"]
+    trace = None
+    for r in stats:
+        name = r["Name"]
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{float(r['Percentage']):.1f}% |")
+        if "k_ring_attn" in name and trace is None:
+            trace = float(r["AverageNs"]) / 1e3
+    f, nf = _kib_per_dispatch(out_dir, f"pmc_fetch_{wl_name}", "FETCH_SIZE", lambda n: "k_ring_attn" in n)
+    wv, nw = _kib_per_dispatch(out_dir, f"pmc_write_{wl_name}", "WRITE_SIZE", lambda n: "k_ring_attn" in n)
+    lines += ["", f"HBM traffic per k_ring_attn dispatch ({min(nf, nw)} dispatches; counters scaled "
+              f"as for the decode-stream summary, FETCH_SIZE x {fetch_scale:.3f}, WRITE_SIZE x "
+              f"{write_scale:.3f}): read {f * 1024 * fetch_scale / 1e6:.2f} MB, written "
+              f"{wv * 1024 * write_scale / 1e6:.2f} MB."]
+    if bl:
+        r = bl["roofline"]
+        lines.append(
+            f"The same bench without the profiler: {bl['value']:.0f} steps/s; k_ring_attn "
+            f"{r['avg_launch_us']:.2f} us per launch (HIP events bound to its dispatches) for "
+            f"{r['bytes_per_launch'] / 1e6:.2f} MB of algorithmic bytes = {r['achieved']:.0f} GB/s, "
+            f"{100 * r['frac']:.1f}% of 8 TB/s; splits: {bl['config']['ring'].split('splits=')[-1]}.")
+    if trace:
+        lines.append(f"Average k_ring_attn duration in the kernel trace: {trace:.2f} us.")
+    path = f"profiles/k_ring_attn_{wl_name}.md"
+    with open(os.path.join(ROOT, path), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    return path
 
 
 def main() -> int:
