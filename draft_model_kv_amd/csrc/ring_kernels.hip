@@ -1501,8 +1501,19 @@ __global__ __launch_bounds__(256) void k_ring_merge(MergeArgs a) {
   __shared__ float4 sO[4][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // (unit, item) of this work-group; the items of a unit run on the XCD
+  // whose attention work-groups wrote its partials (same mapping), so the
+  // partials are read from that XCD's L2
   const int per_unit = (a.mpad / 32) * 16;
-  const int unit = blockIdx.x / per_unit, f = blockIdx.x - unit * per_unit;
+  int unit, f;
+  if ((a.n_units & 7) == 0) {
+    const int xcd = blockIdx.x & 7, k = blockIdx.x >> 3;
+    unit = ((k / per_unit) << 3) + xcd;
+    f = k % per_unit;
+  } else {
+    unit = blockIdx.x / per_unit;
+    f = blockIdx.x - unit * per_unit;
+  }
   const int mb = f >> 4, b = (f >> 2) & 3, jj = f & 3;
   const int col = lane & 31, hl = lane >> 5;
   const int n = mb * 32 + col;
