@@ -530,18 +530,15 @@ __device__ inline void load_new_rows4(const FusedCtx& fx, int tile, uint32_t nm,
 }
 
 // Rotate the new rows of ring tile `tile` (slot mask nm, nonzero): K at its
-// absolute position (fp64, one rounding to F16), store K and V to the ring
-// tile in global memory, and into this wave's LDS rows: pk [32 slots][128]
-// and pvt [128 dims][32 slots] (transposed, for the V fragments).  Raw rows
-// go in groups of four through `raw` [4][256]; the first group may come
-// preloaded (pre_k / pre_v, for tile pre_tile).
+// absolute position (fp64, one rounding to F16), into this wave's LDS rows:
+// pk [32 slots][128] and pvt [128 dims][32 slots] (transposed, for the V
+// fragments); store_new_rows writes them to the ring later.  Raw rows go in
+// groups of four through `raw` [4][256]; the first group may come preloaded
+// (pre_k / pre_v, for tile pre_tile).
 __device__ __forceinline__ void prepare_new_rows(const FusedCtx& fx, int tile, uint32_t nm,
-                                                 uint16_t* kh, uint16_t* vh, uint16_t* raw,
-                                                 uint16_t* pk, uint16_t* pvt, int lane,
-                                                 int pre_tile, const half8& pre_k,
+                                                 uint16_t* raw, uint16_t* pk, uint16_t* pvt,
+                                                 int lane, int pre_tile, const half8& pre_k,
                                                  const half8& pre_v) {
-  uint16_t* kt = kh + (int64_t)tile * kTileHalves;
-  uint16_t* vt = vh + (int64_t)tile * kTileHalves;
   uint32_t left = nm;
   while (left) {
     const uint32_t left_before = left;
@@ -575,10 +572,6 @@ __device__ __forceinline__ void prepare_new_rows(const FusedCtx& fx, int tile, u
       rot_pair(f16_to_f64(rk[lane]), f16_to_f64(rk[lane + 64]), cs, sn, xr, yr);
       const uint16_t kx = f64_to_f16_rne(xr), ky = f64_to_f16_rne(yr);
       const uint16_t vx = rk[128 + lane], vy = rk[128 + lane + 64];
-      kt[k_frag_index(rr, lane)] = kx;
-      kt[k_frag_index(rr, lane + 64)] = ky;
-      vt[v_frag_index(rr, lane)] = vx;
-      vt[v_frag_index(rr, lane + 64)] = vy;
       pk[rr * kHeadDim + lane] = kx;
       pk[rr * kHeadDim + lane + 64] = ky;
       pvt[lane * kTile + rr] = vx;
@@ -587,6 +580,25 @@ __device__ __forceinline__ void prepare_new_rows(const FusedCtx& fx, int tile, u
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+  }
+}
+
+// Store the new rows that prepare_new_rows left in LDS (slots nm of ring
+// tile `tile`) to the ring.  Done once the wave's attention no longer needs
+// its memory pipeline for loads: stores issued while every wave's loads are
+// queued wait behind them (2 us for four rows, measured).
+__device__ __forceinline__ void store_new_rows(int tile, uint32_t nm, uint16_t* kh, uint16_t* vh,
+                                               const uint16_t* pk, const uint16_t* pvt,
+                                               int lane) {
+  uint16_t* kt = kh + (int64_t)tile * kTileHalves;
+  uint16_t* vt = vh + (int64_t)tile * kTileHalves;
+  while (nm) {
+    const int rr = __builtin_ctz(nm);
+    nm &= nm - 1;
+    kt[k_frag_index(rr, lane)] = pk[rr * kHeadDim + lane];
+    kt[k_frag_index(rr, lane + 64)] = pk[rr * kHeadDim + lane + 64];
+    vt[v_frag_index(rr, lane)] = pvt[lane * kTile + rr];
+    vt[v_frag_index(rr, lane + 64)] = pvt[(lane + 64) * kTile + rr];
   }
 }
 
@@ -1157,6 +1169,9 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
   uint16_t* p_k = patch + 4 * 256;
   uint16_t* p_vt = patch + 4 * 256 + 32 * 128;
   uint32_t early_nm = 0;   // new-row mask of tile pre_tile, prepared before the tile loop
+  // new rows prepared in LDS and not yet stored to the ring (tile, slots)
+  int owed_tile = 0;
+  uint32_t owed_nm = 0;
   auto prep_tile = [&](int rt, half8 (&kc)[8], half8 (&vc)[8], uint32_t (&mw)[MB][8],
                        const int4 (&spv)[4]) {
     if constexpr (FUSED) {
@@ -1165,7 +1180,13 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
         uint32_t nm = early_nm;
         if (rt != pre_tile) {
           nm = new_rows_mask(fx, rt, lane);
-          if (nm) prepare_new_rows(fx, rt, nm, kh, vh, p_raw, p_k, p_vt, lane, -1, pre_k, pre_v);
+          if (nm) {
+            // the LDS rows are about to be reused: the previous tile's go out first
+            if (owed_nm) store_new_rows(owed_tile, owed_nm, kh, vh, p_k, p_vt, lane);
+            prepare_new_rows(fx, rt, nm, p_raw, p_k, p_vt, lane, -1, pre_k, pre_v);
+            owed_tile = rt;
+            owed_nm = nm;
+          }
         }
         if (nm) apply_new_rows(nm, p_k, p_vt, lane, kc, vc);
       }
@@ -1280,8 +1301,9 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
   if constexpr (FUSED) {
     if (pre_tile >= 0) {
       early_nm = new_rows_mask(fx, pre_tile, lane);
-      prepare_new_rows(fx, pre_tile, early_nm, kh, vh, p_raw, p_k, p_vt, lane, pre_tile, pre_k,
-                       pre_v);
+      prepare_new_rows(fx, pre_tile, early_nm, p_raw, p_k, p_vt, lane, pre_tile, pre_k, pre_v);
+      owed_tile = pre_tile;
+      owed_nm = early_nm;
     }
   }
 
@@ -1364,6 +1386,12 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
       if (next < t1) load_tile(ring_tile(next), kc, vc, mw, spv);
       tile = next;
     }
+  }
+
+  // (fused launch) the last prepared new rows to the ring, before the merge
+  // may reuse their LDS bytes
+  if constexpr (FUSED) {
+    if (owed_nm) store_new_rows(owed_tile, owed_nm, kh, vh, p_k, p_vt, lane);
   }
 
   // ---- 5./6. merge the waves and store: a copy of the code per wave, so
