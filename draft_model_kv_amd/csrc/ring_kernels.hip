@@ -491,151 +491,11 @@ struct FusedCtx {
   int swa;                  // sliding-window layer: causal noise block
 };
 
-// New rows of this layer in ring tile `tile`, for a wave about to attend it:
-// rotate them (fp64, one rounding), store them to the ring (K and V tiles in
-// global memory) and into the wave's LDS rows pk / pv [32][128], then replace
-// the tile's loaded K and V fragments of those slots (which may predate the
-// store) by the new values.  Raw rows come in groups of four: lane l loads
-// 16 bytes of row l / 16 (K and V), the group is staged in `raw` [4][256].
-// Which of the tile's 32 slots hold new rows (slot s: row d = s - start_mod
-// mod cap), as a wave-uniform bit mask.
-__device__ inline uint32_t new_rows_mask(const FusedCtx& fx, int tile, int lane) {
-  const int s = tile * kTile + (lane & 31);
-  int d = s - fx.start_mod;
-  if (d < 0) d += fx.cap;
-  const bool is_new = lane < 32 && s < fx.cap && d < fx.n_new;
-  return (uint32_t)__ballot(is_new);
-}
-
-// Raw K and V of the first four new rows of a tile (mask nm), 16 bytes per
-// lane: lane l holds bytes [16 (l % 16), +16) of row l / 16's head slice.
-__device__ inline int64_t new_rows4_offset(const FusedCtx& fx, int tile, uint32_t nm, int lane) {
-  uint32_t left = nm;
-  int r[4], nr = 0;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    r[k] = left ? __builtin_ctz(left) : r[0];
-    if (left) { left &= left - 1; ++nr; }
-  }
-  const int rl = r[min(lane >> 4, nr - 1)];
-  int dl = tile * kTile + rl - fx.start_mod;
-  if (dl < 0) dl += fx.cap;
-  return (int64_t)dl * fx.kv_row + 8 * (lane & 15);
-}
-__device__ inline void load_new_rows4(const FusedCtx& fx, int tile, uint32_t nm, int lane,
-                                      half8& kraw, half8& vraw) {
-  const int64_t ro = new_rows4_offset(fx, tile, nm, lane);
-  kraw = *(gchalf8*)(fx.k_new + ro);
-  vraw = *(gchalf8*)(fx.v_new + ro);
-}
-
-// Rotate the new rows of ring tile `tile` (slot mask nm, nonzero): K at its
-// absolute position (fp64, one rounding to F16), into this wave's LDS rows:
-// pk [32 slots][128] and pvt [128 dims][32 slots] (transposed, for the V
-// fragments); store_new_rows writes them to the ring later.  Raw rows go in
-// groups of four through `raw` [4][256]; the first group may come preloaded
-// (pre_k / pre_v, for tile pre_tile).
-__device__ __forceinline__ void prepare_new_rows(const FusedCtx& fx, int tile, uint32_t nm,
-                                                 uint16_t* raw, uint16_t* pk, uint16_t* pvt,
-                                                 int lane, int pre_tile, const half8& pre_k,
-                                                 const half8& pre_v) {
-  uint32_t left = nm;
-  while (left) {
-    const uint32_t left_before = left;
-    int r[4], nr = 0;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      r[k] = left ? __builtin_ctz(left) : r[0];
-      if (left) { left &= left - 1; ++nr; }
-    }
-    const int k_of_lane = lane >> 4, part = lane & 15;
-    half8 kraw, vraw;
-    if (left_before == nm && tile == pre_tile) {
-      kraw = pre_k;            // the first group, loaded before the tile
-      vraw = pre_v;
-    } else {
-      load_new_rows4(fx, tile, left_before, lane, kraw, vraw);
-    }
-    *(half8*)(raw + k_of_lane * 256 + 8 * part) = kraw;
-    *(half8*)(raw + k_of_lane * 256 + 128 + 8 * part) = vraw;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-    for (int k = 0; k < nr; ++k) {
-      const int rr = r[k];
-      int dd = tile * kTile + rr - fx.start_mod;
-      if (dd < 0) dd += fx.cap;
-      const uint16_t* rk = raw + k * 256;
-      double sn, cs;
-      sincos_angle((double)(fx.start + dd) * fx.invf, &sn, &cs);
-      double xr, yr;
-      rot_pair(f16_to_f64(rk[lane]), f16_to_f64(rk[lane + 64]), cs, sn, xr, yr);
-      const uint16_t kx = f64_to_f16_rne(xr), ky = f64_to_f16_rne(yr);
-      const uint16_t vx = rk[128 + lane], vy = rk[128 + lane + 64];
-      pk[rr * kHeadDim + lane] = kx;
-      pk[rr * kHeadDim + lane + 64] = ky;
-      pvt[lane * kTile + rr] = vx;
-      pvt[(lane + 64) * kTile + rr] = vy;
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-  }
-}
-
-// Store the new rows that prepare_new_rows left in LDS (slots nm of ring
-// tile `tile`) to the ring.  Done once the wave's attention no longer needs
-// its memory pipeline for loads: stores issued while every wave's loads are
-// queued wait behind them (2 us for four rows, measured).
-__device__ __forceinline__ void store_new_rows(int tile, uint32_t nm, uint16_t* kh, uint16_t* vh,
-                                               const uint16_t* pk, const uint16_t* pvt,
-                                               int lane) {
-  uint16_t* kt = kh + (int64_t)tile * kTileHalves;
-  uint16_t* vt = vh + (int64_t)tile * kTileHalves;
-  while (nm) {
-    const int rr = __builtin_ctz(nm);
-    nm &= nm - 1;
-    kt[k_frag_index(rr, lane)] = pk[rr * kHeadDim + lane];
-    kt[k_frag_index(rr, lane + 64)] = pk[rr * kHeadDim + lane + 64];
-    vt[v_frag_index(rr, lane)] = pvt[lane * kTile + rr];
-    vt[v_frag_index(rr, lane + 64)] = pvt[(lane + 64) * kTile + rr];
-  }
-}
-
-// Replace the tile's loaded K and V fragments of the new slots (mask nm) by
-// the rows prepare_new_rows left in LDS (the loaded values may predate the
-// store); every LDS read is issued and the choice made by selects.
-__device__ __forceinline__ void apply_new_rows(uint32_t nm, const uint16_t* pk,
-                                               const uint16_t* pvt, int lane, half8 (&kc)[8],
-                                               half8 (&vc)[8]) {
-  const int hl = lane >> 5, col = lane & 31;
-  // K fragment of lane l: slot l % 32, dims 16 c + 8 (l / 32) + 0..7
-  const bool knew = (nm >> col) & 1u;
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const half8 nv = *(const half8*)(pk + col * kHeadDim + 16 * c + 8 * hl);
-    kc[c] = knew ? nv : kc[c];
-  }
-  // V fragment 2 b + ks of lane l, element e: slot 16 ks + 8 (e / 4) +
-  // 4 (l / 32) + e % 4, dim 32 b + l % 32: four consecutive slots per read
-  typedef _Float16 half4 __attribute__((ext_vector_type(4)));
-#pragma unroll
-  for (int b = 0; b < 4; ++b)
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int eh = 0; eh < 2; ++eh) {
-        const int base = 16 * ks + 8 * eh + 4 * hl;
-        const half4 nv = *(const half4*)(pvt + (32 * b + col) * kTile + base);
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if ((nm >> (base + u)) & 1u) vc[2 * b + ks][4 * eh + u] = nv[u];
-      }
-}
-
 // Mask words of a tile from its slot_pos (fused launch): slot s is visible
-// when its position (the new one for a new slot) lies in [lo, committed);
-// the same for every query.  spv[jj] holds slots 8 jj + 4 (lane / 32) + 0..3.
+// when its position lies in [lo, committed), the same for every query; the
+// step's new slots are not (their rows are attended as extra keys, and the
+// tile may hold their old rows or, being written by another wave of this
+// launch, the new ones).  spv[jj] holds slots 8 jj + 4 (lane / 32) + 0..3.
 template <int MB>
 __device__ __forceinline__ void tile_mask_words(const FusedCtx& fx, int tile, int hl,
                                                 const int4 (&spv)[4], uint32_t (&mw)[MB][8]) {
@@ -648,8 +508,8 @@ __device__ __forceinline__ void tile_mask_words(const FusedCtx& fx, int tile, in
       const int s = tile * kTile + 8 * jj + 4 * hl + u;
       int d = s - fx.start_mod;
       if (d < 0) d += fx.cap;
-      const int sp = (s < fx.cap && d < fx.n_new) ? fx.start + d : sp4[u];
-      h[u] = (sp >= fx.lo && sp < fx.committed) ? 0x0000u : 0xFC00u;
+      const bool is_new = s < fx.cap && d < fx.n_new;
+      h[u] = (!is_new && sp4[u] >= fx.lo && sp4[u] < fx.committed) ? 0x0000u : 0xFC00u;
     }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -666,13 +526,15 @@ __device__ __forceinline__ void tile_mask_words(const FusedCtx& fx, int tile, in
 //
 // Order of work (memory latency is the cost on a 4096-slot ring, so every
 // load is issued as early as its inputs allow):
-//   1. loads for the query build, for the wave's noise row and for its first
+//   1. loads for the query build, for the wave's extra key row (a noise row,
+//      or in a fused launch one of the step's new rows) and for its first
 //      ring tile;
 //   2. the work-group rotates/scales/splits the queries into LDS; one barrier;
-//   3. a wave that owns a noise row rotates it (fp64, one rounding to F16),
-//      stores it to ring row cap + r and folds it into its online softmax
+//   3. a wave that owns an extra row rotates it (fp64, one rounding to F16),
+//      stores it to its ring row and folds it into its online softmax
 //      (dot products on the vector unit, P V on the matrix core) while its
-//      ring tile is still in flight;
+//      ring tile is still in flight (a fused launch's tile pass hides the
+//      new slots, which it attends this way);
 //   4. each wave streams its ring tiles;
 //   5. waves merge through LDS; the work-group writes its output or partial.
 // Every global load of the fast path is issued unconditionally from an
@@ -702,24 +564,14 @@ struct AttnShape {
       kOwnMergeBytes ? kQBytes + kRowBytes + kMergeBytes
                      : (kQBytes + kRowBytes > kMergeBytes ? kQBytes + kRowBytes : kMergeBytes);
   static_assert(kRopeOffset + kRopeBytes <= kLdsBytes, "rope table fits the merge bytes");
-  // Fused launch: per wave, raw new rows [4][256] and rotated rows K, V
-  // [32][128] F16 (used inside the tile loop: own bytes with one query
-  // block, whose merge buffer is written while other waves are still in
-  // their loops; with two they share the merge buffer's bytes past the
-  // prologue's, which are written only after every wave has left its loop).
-  static constexpr int kPatchWaveBytes = (4 * 256 + 2 * 32 * 128) * 2;
-  static constexpr int kPatchOffset =
-      kOwnMergeBytes ? kLdsBytes : kRopeOffset + kRopeBytes;
-  static constexpr int kFusedLdsBytes =
-      kOwnMergeBytes ? kLdsBytes + NW * kPatchWaveBytes
-                     : (kPatchOffset + NW * kPatchWaveBytes > kLdsBytes
-                            ? kPatchOffset + NW * kPatchWaveBytes : kLdsBytes);
-  static constexpr int kTotalLds = FUSED ? kFusedLdsBytes : kLdsBytes;
+  static constexpr int kTotalLds = kLdsBytes;
 };
 
-// One noise row of this wave's (sequence, head), already loaded: lane f holds
-// K and V at dims f and f + 64, (cos, sin) of frequency f at the row's
-// position, and the mask word of its query in each query block.
+// One extra key row of this wave's (sequence, head), already loaded: lane f
+// holds K and V at dims f and f + 64, (cos, sin) of frequency f at the row's
+// position (plain launch), and the mask word of its query in each query
+// block.  Extra row e < q_len is noise row e; in a fused launch, extra row
+// q_len + j is the step's new row j of this layer (position start + j).
 template <int MB>
 struct NoiseRow {
   uint16_t kx, ky, vx, vy;
@@ -733,30 +585,47 @@ __device__ __forceinline__ void load_noise_row(const AttnArgs& a, const FusedCtx
                                                const unsigned (&qrow)[MB], int lane,
                                                NoiseRow<MB>& nr) {
   const int kv_row = a.n_head_kv * kHeadDim;
-  const int64_t ro = ((int64_t)seq * a.q_len + r) * kv_row + g * kHeadDim;
-  nr.kx = a.k_noise[ro + lane];
-  nr.ky = a.k_noise[ro + lane + 64];
-  nr.vx = a.v_noise[ro + lane];
-  nr.vy = a.v_noise[ro + lane + 64];
   if constexpr (FUSED) {
-    // computed where the row is attended: (cos, sin) at committed + r, and
-    // the mask (the noise block is visible to every query, or causal in a
-    // sliding-window layer)
+    // noise row r, or new row r - q_len (loaded from a pointer picked
+    // without a branch, so that the load is not sunk behind later ones);
+    // (cos, sin) are computed where the row is attended
+    const bool is_new = r >= a.q_len;
+    const int j = r - a.q_len;
+    gcu16* kb = is_new ? fx.k_new + (int64_t)j * kv_row
+                       : (gcu16*)a.k_noise + ((int64_t)seq * a.q_len + r) * kv_row + g * kHeadDim;
+    gcu16* vb = is_new ? fx.v_new + (int64_t)j * kv_row
+                       : (gcu16*)a.v_noise + ((int64_t)seq * a.q_len + r) * kv_row + g * kHeadDim;
+    nr.kx = kb[lane];
+    nr.ky = kb[lane + 64];
+    nr.vx = vb[lane];
+    nr.vy = vb[lane + 64];
     nr.cs = make_double2(0.0, 0.0);
+    // the noise block is visible to every query, or causal in a sliding-
+    // window layer; a new row (a committed position) is visible when it lies
+    // in the layer's window [lo, committed)
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
-      nr.mask[mb] = (fx.swa && (unsigned)r > qrow[mb]) ? 0xFC00u : 0x0000u;
+      nr.mask[mb] = is_new ? (fx.start + j >= fx.lo ? 0x0000u : 0xFC00u)
+                           : ((fx.swa && (unsigned)r > qrow[mb]) ? 0xFC00u : 0x0000u);
+    return;
   } else {
+    const int64_t ro = ((int64_t)seq * a.q_len + r) * kv_row + g * kHeadDim;
+    nr.kx = a.k_noise[ro + lane];
+    nr.ky = a.k_noise[ro + lane + 64];
+    nr.vx = a.v_noise[ro + lane];
+    nr.vy = a.v_noise[ro + lane + 64];
     nr.cs = *(const double2*)(a.rope_noise + (((int64_t)seq * a.q_len + r) * 64 + lane) * 2);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) nr.mask[mb] = mask_seq[qrow[mb] * a.kv_total + a.cap + r];
   }
 }
 
-// Rotate the row, store it to ring row cap + r, and fold it into the wave's
-// running softmax as one more key.  S = Q k on the vector unit (dot products
-// of the hi and lo query fragments with the F16 key); the P V update is one
-// matrix op per 32-dim block with the row as slot 0 of a V fragment.
+// Rotate extra row r at its position (fp64, one rounding to F16), store it
+// to its ring row (noise row r: row cap + r; new row j: slot (start + j) %
+// cap), and fold it into the wave's running softmax as one more key.  S = Q k
+// on the vector unit (dot products of the hi and lo query fragments with the
+// F16 key); the P V update is one matrix op per 32-dim block with the row as
+// slot 0 of a V fragment.
 template <int MB, bool FUSED>
 __device__ __forceinline__ void attend_noise_row(
     const AttnArgs& a, const FusedCtx& fx, const NoiseRow<MB>& nr, int r, uint16_t* kh,
@@ -764,12 +633,20 @@ __device__ __forceinline__ void attend_noise_row(
     const half8* q_lds, float (&m_run)[MB], float (&l_run)[MB], f32x16 (&o)[MB][4],
     bool store_row) {
   double2 cs = nr.cs;
-  if constexpr (FUSED) sincos_angle((double)(fx.committed + r) * fx.invf, &cs.y, &cs.x);
+  int slot = a.cap + r;  // ring row of this layer and head
+  if constexpr (FUSED) {
+    const int j = r - a.q_len;
+    int pos = fx.committed + r;
+    if (j >= 0) {
+      pos = fx.start + j;
+      slot = fx.start_mod + j;
+      if (slot >= fx.cap) slot -= fx.cap;
+    }
+    sincos_angle((double)pos * fx.invf, &cs.y, &cs.x);
+  }
   double xr, yr;
   rot_pair(f16_to_f64(nr.kx), f16_to_f64(nr.ky), cs.x, cs.y, xr, yr);
   const uint16_t kx = f64_to_f16_rne(xr), ky = f64_to_f16_rne(yr);
-  // ring row cap + r of this layer and head
-  const int slot = a.cap + r;
   if (store_row) {
     uint16_t* kt = kh + (int64_t)(slot >> 5) * kTileHalves;
     uint16_t* vt = vh + (int64_t)(slot >> 5) * kTileHalves;
@@ -1026,7 +903,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
   int ix_blk = -1;
   if constexpr (FUSED) {
     const int rank_in_seq = g * a.n_split + split;
-    if (fa->index_in_attn && fl.index && rank_in_seq < fa->n_index_blocks)
+    if (fa->index_in_attn && fl.index && rank_in_seq < fa->n_index_blocks && row0 == 0)
       ix_blk = rank_in_seq;
   }
   // The destinations and the few integers the store needs are computed
@@ -1093,10 +970,12 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
     qfreq[k] = (i * 64 + 16 * c + 8 * h2) / 2;
   }
 
-  // ---- 1b. the wave's first noise row (a wave without one loads the last
-  //      row and ignores it).
+  // ---- 1b. the wave's first extra key row: noise rows, then (fused
+  //      launch) the step's new rows of this layer (a wave without one
+  //      loads the last row and ignores it).
+  const int n_extra = a.q_len + (FUSED ? fx.n_new : 0);
   NoiseRow<MB> nr;
-  load_noise_row<MB, FUSED>(a, fx, seq, g, min(rank, a.q_len - 1), mask_seq, qrow, lane, nr);
+  load_noise_row<MB, FUSED>(a, fx, seq, g, min(rank, n_extra - 1), mask_seq, qrow, lane, nr);
 
   // ---- 1c. the wave's first ring tile (a wave without tiles loads its
   //      split's last tile again and ignores it).
@@ -1132,27 +1011,6 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
   };
   int tile = t0 + wave;
   const int tile_last = max(t1 - 1, 0);
-  // Fused launch: the first group of new rows of the wave's first tile is
-  // loaded ahead of the tile, so that their rotation overlaps its arrival.
-  // The loads are issued whether or not that tile has new rows (from the
-  // tile's own ring rows when it has none, and ignored): a load in a branch
-  // makes the compiler drain every load in flight where the branch joins.
-  int pre_tile = -1;
-  half8 pre_k = {}, pre_v = {};
-  if constexpr (FUSED) {
-    const int rt0 = ring_tile(min(tile, tile_last));
-    const uint32_t nm0 = (fx.n_new > 0 && tile < t1) ? new_rows_mask(fx, rt0, lane) : 0u;
-    gchalf8* ks = (gchalf8*)(kh + (int64_t)rt0 * kTileHalves) + lane;
-    gchalf8* vs = (gchalf8*)(vh + (int64_t)rt0 * kTileHalves) + lane;
-    if (nm0) {
-      const int64_t ro = new_rows4_offset(fx, rt0, nm0, lane);
-      ks = (gchalf8*)(fx.k_new + ro);
-      vs = (gchalf8*)(fx.v_new + ro);
-      pre_tile = rt0;
-    }
-    pre_k = *ks;
-    pre_v = *vs;
-  }
   half8 kc[8], vc[8];
   uint32_t mw[MB][8];
   int4 spv[4];
@@ -1162,35 +1020,10 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
   int ix_sp = 0;
   if constexpr (FUSED)
     ix_sp = fx.slot_pos[min(max(ix_blk, 0) * 256 + (int)threadIdx.x, a.cap - 1)];
-  // Fused launch, before a tile is attended: its mask words from slot_pos,
-  // and its new rows of this layer (stored, and patched into the fragments).
-  uint16_t* patch = reinterpret_cast<uint16_t*>(lds + S::kPatchOffset + wave * S::kPatchWaveBytes);
-  uint16_t* p_raw = patch;
-  uint16_t* p_k = patch + 4 * 256;
-  uint16_t* p_vt = patch + 4 * 256 + 32 * 128;
-  uint32_t early_nm = 0;   // new-row mask of tile pre_tile, prepared before the tile loop
-  // new rows prepared in LDS and not yet stored to the ring (tile, slots)
-  int owed_tile = 0;
-  uint32_t owed_nm = 0;
+  // Fused launch, before a tile is attended: its mask words from slot_pos.
   auto prep_tile = [&](int rt, half8 (&kc)[8], half8 (&vc)[8], uint32_t (&mw)[MB][8],
                        const int4 (&spv)[4]) {
-    if constexpr (FUSED) {
-      tile_mask_words<MB>(fx, rt, hl, spv, mw);
-      if (fx.n_new > 0) {
-        uint32_t nm = early_nm;
-        if (rt != pre_tile) {
-          nm = new_rows_mask(fx, rt, lane);
-          if (nm) {
-            // the LDS rows are about to be reused: the previous tile's go out first
-            if (owed_nm) store_new_rows(owed_tile, owed_nm, kh, vh, p_k, p_vt, lane);
-            prepare_new_rows(fx, rt, nm, p_raw, p_k, p_vt, lane, -1, pre_k, pre_v);
-            owed_tile = rt;
-            owed_nm = nm;
-          }
-        }
-        if (nm) apply_new_rows(nm, p_k, p_vt, lane, kc, vc);
-      }
-    }
+    if constexpr (FUSED) tile_mask_words<MB>(fx, rt, hl, spv, mw);
   };
 
   // ---- 2. queries: rotate at committed + i, scale by log2(e)/sqrt(d),
@@ -1282,28 +1115,17 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
     for (int b = 0; b < 4; ++b) o[mb][b] = f32x16{};
   }
 
-  // ---- 3. noise rows, visible to every query.
+  // ---- 3. extra key rows (noise rows, and a fused launch's new rows).
   uint16_t* rowk = reinterpret_cast<uint16_t*>(lds + S::kQBytes) + wave * 2 * kHeadDim;
   uint16_t* rowv = rowk + kHeadDim;
-  if (rank < a.q_len) {
+  if (rank < n_extra) {
     const bool store_rows = row0 == 0;  // one row block stores the rotated rows
     attend_noise_row<MB, FUSED>(a, fx, nr, rank, kh, vh, rowk, rowv, lane, hl, col, qf, q_lds, m_run,
                          l_run, o, store_rows);
-    for (int r = rank + n_waves; r < a.q_len; r += n_waves) {
+    for (int r = rank + n_waves; r < n_extra; r += n_waves) {
       load_noise_row<MB, FUSED>(a, fx, seq, g, r, mask_seq, qrow, lane, nr);
       attend_noise_row<MB, FUSED>(a, fx, nr, r, kh, vh, rowk, rowv, lane, hl, col, qf, q_lds, m_run,
                            l_run, o, store_rows);
-    }
-  }
-
-  // ---- 3b. (fused launch) the new rows of the wave's first tile, rotated
-  //      and stored while the tile is still in flight
-  if constexpr (FUSED) {
-    if (pre_tile >= 0) {
-      early_nm = new_rows_mask(fx, pre_tile, lane);
-      prepare_new_rows(fx, pre_tile, early_nm, p_raw, p_k, p_vt, lane, pre_tile, pre_k, pre_v);
-      owed_tile = pre_tile;
-      owed_nm = early_nm;
     }
   }
 
@@ -1386,12 +1208,6 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
       if (next < t1) load_tile(ring_tile(next), kc, vc, mw, spv);
       tile = next;
     }
-  }
-
-  // (fused launch) the last prepared new rows to the ring, before the merge
-  // may reuse their LDS bytes
-  if constexpr (FUSED) {
-    if (owed_nm) store_new_rows(owed_tile, owed_nm, kh, vh, p_k, p_vt, lane);
   }
 
   // ---- 5./6. merge the waves and store: a copy of the code per wave, so
@@ -1756,7 +1572,7 @@ hipError_t launch_attn_fused(const FusedAttnArgs& f, hipStream_t s, hipEvent_t t
   for (int i = 0; i < a.n_seq && i < kFusedMaxSeq; ++i) n_indexed += f.fs.index[i] != 0;
   const int grid = f.n_attn_blocks + (f.index_in_attn ? 0 : n_indexed * f.n_index_blocks);
   const bool one_pass = a.q_len <= 8;
-  if (a.m <= 32) {
+  if (a.m <= 32 || a.n_rb > 1) {
     if (one_pass)
       hipExtLaunchKernelGGL((k_ring_attn_fused<1, 4, 1>), dim3(grid), dim3(256), 0, s, t0, t1, 0, f);
     else

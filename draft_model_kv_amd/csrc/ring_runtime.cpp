@@ -783,14 +783,11 @@ int ring_attn(ring_t* r, int32_t layer, const void* q, const void* k_noise, cons
   for (int i = 0; i < r->cfg.n_seq; ++i) {
     // Visible positions [committed - w, committed) sit in slots from
     // (committed - w) % cap on, circularly: w = win for full layers,
-    // min(swa_window, win) for sliding-window layers.  A deferred step whose
-    // rows this launch appends reads the whole window's tiles (its new rows
-    // may lie before a sliding window; the mask hides them there).
+    // min(swa_window, win) for sliding-window layers.  (A deferred step's
+    // new rows, which a fused launch attends as extra keys, need no tiles.)
     const int64_t c = r->committed[i];
     const int64_t win = std::min<int64_t>(c, cap);
-    const Pending& pd = r->pending[i];
-    const bool appends = pd.active && (pd.layers_left & bit) && pd.n_new > 0;
-    const int64_t w = (swa && !appends) ? std::min<int64_t>(r->cfg.swa_window, win) : win;
+    const int64_t w = swa ? std::min<int64_t>(r->cfg.swa_window, win) : win;
     int32_t first = 0, count = 0;
     if (w > 0 && w < win) {
       const int64_t s0 = (c - w) % cap, s1 = s0 + w;  // slot range [s0, s1), s1 may pass cap
@@ -821,8 +818,9 @@ int ring_attn(ring_t* r, int32_t layer, const void* q, const void* k_noise, cons
   if (fuse) {
     FusedAttnArgs f{};
     f.a = a;
+    f.a.n_rb = r->L.n_rb;
     f.swa_layer = swa ? 1 : 0;
-    f.n_attn_blocks = r->cfg.n_seq * r->cfg.n_head_kv * n_split;
+    f.n_attn_blocks = r->cfg.n_seq * r->cfg.n_head_kv * n_split * r->L.n_rb;
     f.n_index_blocks = (r->geo.kv_total + 255) / 256;
     // the attention work-groups of a sequence carry its index blocks when
     // there are enough of them (extra work-groups would each take a compute
