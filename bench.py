@@ -1,11 +1,15 @@
 #!/usr/bin/env python3
 """Throughput of the draft-KV ring step on one MI355X.
 
-A step is one pass of the whole ring path for one sequence: ring_begin_step
-(fold-in append with RoPE + slot_pos + window mask) and ring_attn (masked GQA
-attention of the 8 noise queries over the 4096-slot ring, split-K + merge).
-On a ring of several sequences (batched_seqs) a step is one
-ring_begin_step_batch over all of them, then one ring_attn per layer.
+A step is one pass of the whole ring path for one sequence: the fold-in
+(append with RoPE at absolute positions, slot_pos, window mask, noise RoPE
+table) and ring_attn (masked GQA attention of the 8 noise queries over the
+4096-slot ring, split-K + merge).  By default the fold-in is handed to the
+attention launch (ring_begin_step_deferred, then ring_attn: one attention
+launch that appends, rebuilds the index state and attends, then the merge);
+--step eager gives it a launch of its own (ring_begin_step).  On a ring of
+several sequences (batched_seqs) a step is one ring_begin_step_batch over all
+of them, then one ring_attn per layer.
 Workload: the draft-window decode stream (cap 4096, q_len 8, 32 query / 8 KV
 heads x 128, F16), warmed by a 4096-token bulk prefill; synthetic seeded
 inputs, already resident in device memory when timing starts.
@@ -511,10 +515,12 @@ def main() -> int:
     ap.add_argument("--pool", type=int, default=0,
                     help="independent rings cycled through (default: enough to exceed the "
                          "256 MB Infinity Cache; 1 = cache-warm)")
-    ap.add_argument("--step", choices=("eager", "fused"), default="eager",
-                    help="eager: ring_begin_step's own append launch (default); fused: "
-                         "ring_begin_step_deferred, the fold-in append and index rebuild "
-                         "run inside the attention launch")
+    ap.add_argument("--step", choices=("eager", "fused"), default="fused",
+                    help="fused (default): ring_begin_step_deferred, the fold-in append and "
+                         "index rebuild run inside the attention launch; eager: "
+                         "ring_begin_step's own append launch.  Rings of several sequences "
+                         "take ring_begin_step_batch, rows from features "
+                         "ring_begin_step_mirror, whatever this says")
     ap.add_argument("--begin", choices=("auto", "per_seq"), default="auto",
                     help="eager step of a ring with several sequences: auto takes one "
                          "ring_begin_step_batch call for all of them (default), per_seq one "
@@ -568,12 +574,13 @@ def main() -> int:
     rings, calls, steps_in, committed = prepare(w, pool, total, dev)
     s = torch.cuda.current_stream(dev).cuda_stream
     out = torch.empty((w.n_seq, w.q_len, w.n_head, w.head_dim), dtype=torch.float32, device=dev)
-    fused = args.step == "fused"
+    mirror = w.d_model > 0
+    batched = not mirror and w.n_seq > 1 and args.begin == "auto"
+    fused = args.step == "fused" and not mirror and not batched
+    step_mode = "mirror" if mirror else "batch" if batched else "fused" if fused else "eager"
     begin = R.ring_begin_step_deferred if fused else R.ring_begin_step
     attn, optr = R.ring_attn, out.data_ptr()
-    mirror = w.d_model > 0
     mwrite, mbegin = R.ring_mirror_write, R.ring_begin_step_mirror
-    batched = not fused and not mirror and w.n_seq > 1 and args.begin == "auto"
     begin_batch = R.ring_begin_step_batch
     # the batched call's argument lists, per call
     columns = [[list(col) for col in zip(*c[1])] for c in calls] if batched else None
@@ -637,6 +644,10 @@ def main() -> int:
                             for c in cs) for cs in seg for layer in range(w.n_layer)])
 
     per_launch = mean_bytes("attn_kernel")
+    if fused and prof["k_ring_step"]["launches"]:
+        # the library appended the deferred steps at once (a ring whose
+        # attention waves stream several tiles each): an eager step
+        fused, step_mode = False, "eager"
     if fused and not mirror:
         # the fused launch also reads each new row (K and V, F16) and writes it
         # to the ring, reads slot_pos instead of the mask, and (first layer of
@@ -687,8 +698,7 @@ def main() -> int:
         "dtype": "f16",
         "data": "synthetic (seeded normal F16 rows; accepted counts drawn from the "
                 "pages' 1422-verification share table)",
-        "config": {"workload": args.workload, "step": args.step,
-                   **({"begin": "batch" if batched else "per_seq"} if w.n_seq > 1 else {}),
+        "config": {"workload": args.workload, "step": step_mode,
                    "cap": w.cap, "q_len": w.q_len,
                    "n_head": w.n_head, "n_head_kv": w.n_head_kv, "head_dim": w.head_dim,
                    "n_layer": w.n_layer, "n_seq": w.n_seq, "kv_total": geo.kv_total,

@@ -141,15 +141,15 @@ struct AttnArgs {
 struct FusedAttnArgs {
   AttnArgs a;
   int32_t swa_layer;         // this layer attends with the sliding-window mask
-  int32_t n_attn_blocks;     // attention work-groups; index work-groups follow
-  int32_t n_index_blocks;    // index blocks (256 slots each) per indexed sequence
-  int32_t index_in_attn;     // 1: attention work-groups of the sequence do its index
-                             // blocks (rank g * n_split + split < n_index_blocks);
-                             // 0: n_index_blocks extra work-groups per sequence
+  int32_t n_attn_blocks;     // work-groups of the launch
+  int32_t n_index_blocks;    // index blocks (256 slots each) per indexed sequence: the
+                             // sequence's work-groups take them in turn, work-group r
+                             // (in (KV head, split, row block) order) blocks r, r + R, ...
+                             // for R work-groups per sequence
   int32_t slot_stride;       // int32 per sequence in slot_pos
   int32_t n_layer, a_step, trash_slot;
   int64_t layer_stride;      // halves between layers of a sequence's ring
-  const double* inv_freq;    // [64] theta_i (device copy, for the extra index work-groups)
+  const double* inv_freq;    // [64] theta_i (device copy)
   double theta[64];          // the same values, fetched by lane at kernel entry
   int32_t* slot_pos;         // [n_seq][slot_stride]
   uint16_t* mask_full;       // [n_seq][q_len][kv_total]

@@ -897,14 +897,15 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
     fx.cap = a.cap;
     fx.swa = fa->swa_layer;
   }
-  // Index block of this work-group (fused launch, when the attention
-  // work-groups carry them): block ix_blk of its own sequence; block 0 also
-  // writes the noise RoPE tables.
-  int ix_blk = -1;
+  // Index blocks of this work-group (fused launch, when the launch rebuilds
+  // the sequence's index state): blocks ix_blk, ix_blk + ix_step, ... of its
+  // own sequence (the work-groups of a sequence take them in turn, after
+  // their attention); block 0 also writes the noise RoPE tables.
+  int ix_blk = -1, ix_step = 1;
   if constexpr (FUSED) {
-    const int rank_in_seq = g * a.n_split + split;
-    if (fa->index_in_attn && fl.index && rank_in_seq < fa->n_index_blocks && row0 == 0)
-      ix_blk = rank_in_seq;
+    ix_step = a.n_head_kv * a.n_split * a.n_rb;
+    const int rank_in_seq = (g * a.n_split + split) * a.n_rb + row0 / MP;
+    if (fl.index && rank_in_seq < fa->n_index_blocks) ix_blk = rank_in_seq;
   }
   // The destinations and the few integers the store needs are computed
   // up front and pass through an empty asm statement that redefines them, so the
@@ -1145,6 +1146,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
       uint32_t m2[MB][8];
       int4 s2[4];
       load_tile(ring_tile(tile + 2 * NW), k2, v2, m2, s2);
+      prep_tile(ring_tile(tile), kc, vc, mw, spv);
       attend_tile<MB>(kc, vc, mw, a.cap - ring_tile(tile) * kTile, hl, qf, q_lds, lane, m_run,
                       l_run, o);
 #pragma unroll
@@ -1156,9 +1158,14 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int j = 0; j < 8; ++j) { mw[mb][j] = m1[mb][j]; m1[mb][j] = m2[mb][j]; }
+      if constexpr (FUSED) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) { spv[jj] = s1[jj]; s1[jj] = s2[jj]; }
+      }
       tile += NW;
     }
     if (tile + NW < t1) {
+      prep_tile(ring_tile(tile), kc, vc, mw, spv);
       attend_tile<MB>(kc, vc, mw, a.cap - ring_tile(tile) * kTile, hl, qf, q_lds, lane, m_run,
                       l_run, o);
 #pragma unroll
@@ -1167,11 +1174,17 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int j = 0; j < 8; ++j) mw[mb][j] = m1[mb][j];
+      if constexpr (FUSED) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) spv[jj] = s1[jj];
+      }
       tile += NW;
     }
-    if (tile < t1)
+    if (tile < t1) {
+      prep_tile(ring_tile(tile), kc, vc, mw, spv);
       attend_tile<MB>(kc, vc, mw, a.cap - ring_tile(tile) * kTile, hl, qf, q_lds, lane, m_run,
                       l_run, o);
+    }
   } else if constexpr (kPrefetch) {
     // every tile but the wave's last one: its successor is fetched first
     while (tile + NW < t1) {
@@ -1222,10 +1235,14 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
   else
     merge_store<MB, NW, 3>(ep, lds, sm_m, sm_l, m_run, l_run, o, lane);
   if constexpr (FUSED) {
-    if (ix_blk >= 0) {
-      const StepArgs sa = fused_index_args(*fa, fl, seq);
-      index_slot(sa, ix_blk * 256 + threadIdx.x, ix_sp);
-      if (ix_blk == 0) {
+    const StepArgs sa = fused_index_args(*fa, fl, seq);
+    for (int ix = ix_blk; ix >= 0 && ix < fa->n_index_blocks; ix += ix_step) {
+      const int sidx = ix * 256 + (int)threadIdx.x;
+      // slot_pos before the step (anything past cap); the first block's was
+      // loaded with the other loads
+      const int sp = ix == ix_blk ? ix_sp : fx.slot_pos[min(sidx, a.cap - 1)];
+      index_slot(sa, sidx, sp);
+      if (ix == 0) {
         // the noise RoPE table for later plain launches, as the append kernel
         // builds it (fp64 sincos, and its fp32 rounding)
         for (int item = threadIdx.x; item < a.q_len * 64; item += NT) {
@@ -1264,7 +1281,7 @@ __device__ __forceinline__ void attn_entry(const AttnArgs& a, const FusedAttnArg
                  "v"(fv.n_new), "v"(fv.n_step_rows), "v"(fv.committed), "v"(fv.lo),
                  "v"(fv.index), "v"(fv.full_lo), "v"(fv.swa_lo), "v"(fv.theta),
                  "s"(fa->slot_pos), "s"(fa->slot_stride), "s"(fa->swa_layer),
-                 "s"(fa->index_in_attn), "s"(fa->n_index_blocks));
+                 "s"(fa->n_index_blocks));
   }
   asm volatile("" ::"s"(a.kring), "s"(a.vring), "s"(a.mask), "s"(a.rope_noise), "s"(a.rope_q),
                "s"(a.q),
@@ -1301,31 +1318,12 @@ __global__ __launch_bounds__(NW * 64) void k_ring_attn(AttnArgs a) {
   attn_entry<MB, NW, RP, false, DEEP>(a, nullptr);
 }
 
-// The fused launch: the attention work-groups first (same mapping as
-// k_ring_attn), then n_index_blocks work-groups per sequence whose index
-// state this launch rebuilds (slot_pos, masks, noise RoPE table).
+// The fused launch: the attention work-groups (same mapping as k_ring_attn),
+// which also append the step's new rows and rebuild the index state (slot_pos,
+// masks, noise RoPE table) of the sequences that owe it.
 template <int MB, int NW, int RP>
 __global__ __launch_bounds__(NW * 64) void k_ring_attn_fused(FusedAttnArgs f) {
-  if ((int)blockIdx.x >= f.n_attn_blocks) {
-    static_assert(NW * 64 == 256, "index work-groups have 256 threads");
-    int b = blockIdx.x - f.n_attn_blocks;
-    int seq = 0;
-    for (; seq < f.a.n_seq; ++seq) {
-      if (!f.fs.index[seq]) continue;
-      if (b < f.n_index_blocks) break;
-      b -= f.n_index_blocks;
-    }
-    if (seq >= f.a.n_seq) return;
-    FusedLane fl{};
-    fl.start = f.fs.start[seq];
-    fl.start_mod = f.fs.start_mod[seq];
-    fl.n_step_rows = f.fs.n_step_rows[seq];
-    fl.committed = f.fs.committed[seq];
-    fl.full_lo = f.fs.full_lo[seq];
-    fl.swa_lo = f.fs.swa_lo[seq];
-    index_block(fused_index_args(f, fl, seq), b, threadIdx.x);
-    return;
-  }
+  static_assert(NW * 64 == 256, "an index block is one slot per thread");
   attn_entry<MB, NW, RP, true>(f.a, &f);
 }
 
@@ -1568,9 +1566,7 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s, hipEvent_t t0, hipEvent
 hipError_t launch_attn_fused(const FusedAttnArgs& f, hipStream_t s, hipEvent_t t0,
                              hipEvent_t t1) {
   const AttnArgs& a = f.a;
-  int n_indexed = 0;
-  for (int i = 0; i < a.n_seq && i < kFusedMaxSeq; ++i) n_indexed += f.fs.index[i] != 0;
-  const int grid = f.n_attn_blocks + (f.index_in_attn ? 0 : n_indexed * f.n_index_blocks);
+  const int grid = f.n_attn_blocks;
   const bool one_pass = a.q_len <= 8;
   if (a.m <= 32 || a.n_rb > 1) {
     if (one_pass)

@@ -601,8 +601,13 @@ int ring_begin_step_deferred(ring_t* r, int32_t seq, int64_t committed, const vo
   if (committed < 0 || committed + r->cfg.q_len > INT32_MAX)
     return fail(RING_ERANGE, "committed %lld out of range", (long long)committed);
   const Plan p = plan_of(r->cfg.cap, r->geo.a_step, committed, r->next_pos[seq], r->held_lo[seq]);
-  // Bulk appends, and rings beyond what one fused launch carries, append now.
-  if (p.bulk || r->cfg.n_seq > kFusedMaxSeq || r->cfg.n_layer > 64)
+  // Bulk appends, rings beyond what one fused launch carries, and rings whose
+  // attention waves stream three or more tiles each (there the append launch
+  // is a small part of the step, and the plain attention keeps two tiles in
+  // flight, which the fused one has no registers for) append now.
+  const int32_t ring_tiles = (r->cfg.cap + kTile - 1) / kTile;
+  const int32_t wave_tiles = ((ring_tiles + r->L.n_split - 1) / r->L.n_split + 3) / 4;
+  if (p.bulk || r->cfg.n_seq > kFusedMaxSeq || r->cfg.n_layer > 64 || wave_tiles >= 3)
     return ring_begin_step(r, seq, committed, k_new, v_new, n_rows, stream);
   if (n_rows != p.n_new)
     return fail(RING_ESTATE, "n_rows %lld != planned n_new %lld (start %lld)", (long long)n_rows,
@@ -822,10 +827,6 @@ int ring_attn(ring_t* r, int32_t layer, const void* q, const void* k_noise, cons
     f.swa_layer = swa ? 1 : 0;
     f.n_attn_blocks = r->cfg.n_seq * r->cfg.n_head_kv * n_split * r->L.n_rb;
     f.n_index_blocks = (r->geo.kv_total + 255) / 256;
-    // the attention work-groups of a sequence carry its index blocks when
-    // there are enough of them (extra work-groups would each take a compute
-    // unit, the attention's LDS being that large)
-    f.index_in_attn = r->cfg.n_head_kv * n_split >= f.n_index_blocks ? 1 : 0;
     f.slot_stride = (int32_t)r->L.slot_stride;
     f.n_layer = r->cfg.n_layer;
     f.a_step = r->geo.a_step;

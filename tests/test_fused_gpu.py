@@ -60,6 +60,19 @@ def test_fused_ragged_cap_short_block():
     d.close()
 
 
+@pytest.mark.parametrize("cap,commits", [
+    (300, [310, 313, 320, 330]),       # 10 tiles (last ragged): waves of 3, 3, 2 and 2 tiles
+    (1000, [200, 204, 990, 1003]),     # window below cap, then across it
+], ids=["ragged", "window_grows"])
+def test_deferred_on_wide_rings(cap, commits):
+    """One split per KV head, so the waves stream three or more tiles: the
+    deferred steps append at once (the plain attention keeps two tiles in
+    flight), with the same results."""
+    d = Driver(small(cap=cap, seed=306), n_split=1)
+    run_fused(d, commits, rows=False)
+    d.close()
+
+
 def test_fused_multi_layer_sliding_window():
     """4 layers, layers 1 and 3 sliding over 16 positions (new rows that fall
     before the window are still appended), full acceptance steps."""
