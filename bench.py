@@ -368,10 +368,21 @@ def summarize_profiles(out_dir: str) -> int:
     for k, r in rows.items():
         lines.append(f"| {k} | {r['dispatches']} | {r['fetch_kib']:.1f} | {r['write_kib']:.1f} | "
                      f"{r['hbm_bytes'] / 1e6:.3f} |")
-    lines += ["", f"k_ring_attn: scaled reads {a['fetch_kib'] * 1024 * fetch_scale / 1e6:.3f} MB per "
-              f"launch against {alg_attn / 1e6:.3f} MB of algorithmic reads (visible K/V rows, "
-              f"queries, noise rows, mask); writes {a['write_kib'] * 1024 * write_scale / 1e6:.3f} MB "
-              "(split partials and the noise rows stored to the ring)."]
+    step = (bl or {}).get("config", {}).get("step", "eager")
+    if step == "fused":
+        # the bench line's bytes of the fused launch (it also reads the new
+        # rows and slot_pos and writes the rows and the index state)
+        alg_attn = bl["roofline"]["bytes_per_launch"]
+        what = ("visible K/V rows, queries, noise rows, the step's new rows, slot_pos; the "
+                "index state it rebuilds")
+        wrote = "split partials, the noise and new rows stored to the ring, the index state"
+    else:
+        what = "visible K/V rows, queries, noise rows, mask"
+        wrote = "split partials and the noise rows stored to the ring"
+    lines += ["", f"k_ring_attn ({step} step): scaled reads "
+              f"{a['fetch_kib'] * 1024 * fetch_scale / 1e6:.3f} MB per launch against "
+              f"{alg_attn / 1e6:.3f} MB of algorithmic bytes ({what}); writes "
+              f"{a['write_kib'] * 1024 * write_scale / 1e6:.3f} MB ({wrote})."]
     if "k_ring_attn" in trace:
         lines.append(f"Average k_ring_attn duration in the kernel trace: {trace['k_ring_attn']:.2f} us.")
     with open(os.path.join(prof, "k_ring_attn_decode_stream_hbm_traffic.md"), "w") as fh:
