@@ -676,7 +676,8 @@ def main() -> int:
     achieved = per_launch / (attn_us * 1e-6) / 1e9
     khash = kernel_source_hash()
     traffic = traffic_from_profiles(khash) if args.workload == WORKLOAD else None
-    roof_attn = {"kernel": "k_ring_attn", "bound": "hbm", "achieved": achieved,
+    roof_attn = {"kernel": "k_ring_attn_fused" if fused else "k_ring_attn", "bound": "hbm",
+                 "achieved": achieved,
                  "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                  "traffic": traffic, "bytes_per_launch": int(per_launch),
                  "avg_launch_us": attn_us}

@@ -81,8 +81,12 @@ def test_fused_multi_layer_sliding_window():
     d.close()
 
 
-def test_fused_gqa8_outliers():
-    d = Driver(small(cap=256, n_head=64, sigma=1.0, outlier_p=0.01, seed=303))
+@pytest.mark.parametrize("row_blocks", [True, False], ids=["row_blocks", "one_workgroup"])
+def test_fused_gqa8_outliers(row_blocks):
+    """64 queries per KV head: each 32-query block in a work-group of its own
+    (both attend the new rows, one stores them), or both blocks in one."""
+    d = Driver(small(cap=256, n_head=64, sigma=1.0, outlier_p=0.01, seed=303),
+               row_blocks=row_blocks)
     run_fused(d, [300, 301, 309, 318, 330])
     d.close()
 
