@@ -24,6 +24,11 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr float kNegInf = -__builtin_inff();
 
+// Global-memory pointers for rows that arrive as integer addresses: loads
+// through a generic pointer become flat loads, and a flat load in flight
+// makes the compiler wait for every other load before the next use of any.
+typedef const __attribute__((address_space(1))) uint16_t gcu16;
+
 // 2^x with the hardware instruction: about 1 ulp for normal results; results
 // below 2^-126 flush to zero and 2^-inf = 0.  Softmax weights that small
 // change no output at the precision that is kept.
@@ -173,15 +178,15 @@ __device__ inline void step_block(const StepArgs& a, const int blk) {
     const bool pad = i >= a.n_rows;
     int slot;
     int64_t p = 0;
-    const uint16_t* ksrc = nullptr;
-    const uint16_t* vsrc = nullptr;
+    gcu16* ksrc = nullptr;
+    gcu16* vsrc = nullptr;
     if (!pad) {
       const int idx = a.row0 + i;
       p = a.start + idx;
       slot = (int)(p % a.cap);
       if (!a.proj) {
-        ksrc = a.k_new + ((int64_t)layer * a.n_new + idx) * kv_row;
-        vsrc = a.v_new + ((int64_t)layer * a.n_new + idx) * kv_row;
+        ksrc = (gcu16*)a.k_new + ((int64_t)layer * a.n_new + idx) * kv_row;
+        vsrc = (gcu16*)a.v_new + ((int64_t)layer * a.n_new + idx) * kv_row;
       }
       if (t < 64) {
         double sn, cs;
@@ -473,11 +478,6 @@ __device__ inline StepArgs fused_index_args(const FusedAttnArgs& f, const FusedL
   return sa;
 }
 
-// Global-memory pointers for rows that arrive as integer addresses: loads
-// through a generic pointer become flat loads, and a flat load in flight
-// makes the compiler wait for every other load before the next use of any.
-typedef const __attribute__((address_space(1))) uint16_t gcu16;
-typedef const __attribute__((address_space(1))) half8 gchalf8;
 
 // What a fused launch tells the attention body about its sequence's
 // deferred step (unused in a plain launch).

@@ -613,8 +613,6 @@ int ring_begin_step_deferred(ring_t* r, int32_t seq, int64_t committed, const vo
     return fail(RING_ESTATE, "n_rows %lld != planned n_new %lld (start %lld)", (long long)n_rows,
                 (long long)p.n_new, (long long)p.start);
   if (p.n_new > 0 && (!k_new || !v_new)) return fail(RING_EINVAL, "k_new / v_new is NULL");
-  if (((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) & 15) != 0)
-    return fail(RING_EINVAL, "k_new / v_new must be 16-byte aligned");
   if (int e = use_device(r)) return e;
   if (int e = flush_seq(r, seq)) return e;
   r->last_stream = static_cast<hipStream_t>(stream);

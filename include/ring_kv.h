@@ -173,11 +173,12 @@ int ring_begin_step(ring_t* r, int32_t seq, int64_t committed,
                     void* stream);
 
 /* ring_begin_step deferred into the attention launches (fused step).  Same
- * arguments, plan, checks and result as ring_begin_step, and k_new / v_new
- * must be 16-byte aligned.  For a fold-in plan nothing is enqueued here: the
- * next ring_attn of each layer appends that layer's rows itself (before it
- * reads their tiles) and the first of them also rebuilds slot_pos, the masks
- * and the noise RoPE table, all in its one launch; pad rows are not written
+ * arguments, plan, checks and result as ring_begin_step.  For a fold-in plan
+ * nothing is enqueued here: the next ring_attn of each layer appends that
+ * layer's rows itself (and attends them as keys of their own, not through
+ * the ring tiles that hold their slots) and the first of them also rebuilds
+ * slot_pos, the masks and the noise RoPE table, all in its one launch; pad
+ * rows are not written
  * (the trash slot keeps its zeros).  k_new and v_new must therefore stay
  * valid until every layer's ring_attn has been enqueued and the stream has
  * passed them.  Whatever a deferred step still owes (layers whose attention
@@ -187,7 +188,7 @@ int ring_begin_step(ring_t* r, int32_t seq, int64_t committed,
  * with more than 8 sequences or 64 layers or whose attention streams three
  * or more 32-slot tiles per wave (cap above about 12 k slots at 32 splits),
  * append right away as ring_begin_step does.
- * Errors: as ring_begin_step, and RING_EINVAL for misaligned rows.          */
+ * Errors: as ring_begin_step.                                               */
 int ring_begin_step_deferred(ring_t* r, int32_t seq, int64_t committed,
                              const void* k_new, const void* v_new, int64_t n_rows,
                              void* stream);
