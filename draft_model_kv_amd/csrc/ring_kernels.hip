@@ -1135,56 +1135,42 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
   //      query blocks have no room for that.
   constexpr bool kPrefetch = MB == 1;
   if constexpr (kPrefetch && DEEP) {
-    // waves with many tiles: the next two tiles are in flight while one is
-    // attended (a wave that has fewer loads its last tile again, unused)
-    half8 k1[8], v1[8];
-    uint32_t m1[MB][8];
-    int4 s1[4];
-    load_tile(ring_tile(min(tile + NW, tile_last)), k1, v1, m1, s1);
-    while (tile + 2 * NW < t1) {
-      half8 k2[8], v2[8];
-      uint32_t m2[MB][8];
-      int4 s2[4];
-      load_tile(ring_tile(tile + 2 * NW), k2, v2, m2, s2);
-      prep_tile(ring_tile(tile), kc, vc, mw, spv);
-      attend_tile<MB>(kc, vc, mw, a.cap - ring_tile(tile) * kTile, hl, qf, q_lds, lane, m_run,
+    // Waves with many tiles: tiles i = 0, 1, ... of the wave (tile + i NW)
+    // go through three register buffers in turn, two loaded ahead of the
+    // one attended.  Unrolled by three so that no buffer is ever copied: a
+    // copy of a buffer waits for its loads, which would leave one tile in
+    // flight instead of two.  Buffer A = (kc, vc, mw) holds tile 0.  (Plain
+    // launches only: a fused launch's waves never stream that many tiles.)
+    static_assert(!FUSED, "two tiles in flight in plain launches only");
+    half8 kb[8], vb[8], kq[8], vq[8];
+    uint32_t mwb[MB][8], mwq[MB][8];
+    load_tile(ring_tile(min(tile + NW, tile_last)), kb, vb, mwb, spv);
+    const int n = t1 > tile ? (t1 - tile + NW - 1) / NW : 0;  // tiles of this wave
+    auto attend = [&](const half8 (&k)[8], const half8 (&v)[8], const uint32_t (&m)[MB][8]) {
+      attend_tile<MB>(k, v, m, a.cap - ring_tile(tile) * kTile, hl, qf, q_lds, lane, m_run,
                       l_run, o);
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        kc[c] = k1[c]; vc[c] = v1[c];
-        k1[c] = k2[c]; v1[c] = v2[c];
-      }
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) { mw[mb][j] = m1[mb][j]; m1[mb][j] = m2[mb][j]; }
-      if constexpr (FUSED) {
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) { spv[jj] = s1[jj]; s1[jj] = s2[jj]; }
-      }
       tile += NW;
+    };
+    int i = 0;
+    for (; i + 5 <= n; i += 3) {
+      load_tile(ring_tile(tile + 2 * NW), kq, vq, mwq, spv);
+      attend(kc, vc, mw);
+      load_tile(ring_tile(tile + 2 * NW), kc, vc, mw, spv);
+      attend(kb, vb, mwb);
+      load_tile(ring_tile(tile + 2 * NW), kb, vb, mwb, spv);
+      attend(kq, vq, mwq);
     }
-    if (tile + NW < t1) {
-      prep_tile(ring_tile(tile), kc, vc, mw, spv);
-      attend_tile<MB>(kc, vc, mw, a.cap - ring_tile(tile) * kTile, hl, qf, q_lds, lane, m_run,
-                      l_run, o);
-#pragma unroll
-      for (int c = 0; c < 8; ++c) { kc[c] = k1[c]; vc[c] = v1[c]; }
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) mw[mb][j] = m1[mb][j];
-      if constexpr (FUSED) {
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) spv[jj] = s1[jj];
-      }
-      tile += NW;
+    // the last n - i <= 4 tiles: A, B, C, A
+    if (i < n) {
+      if (i + 2 < n) load_tile(ring_tile(tile + 2 * NW), kq, vq, mwq, spv);
+      attend(kc, vc, mw);
     }
-    if (tile < t1) {
-      prep_tile(ring_tile(tile), kc, vc, mw, spv);
-      attend_tile<MB>(kc, vc, mw, a.cap - ring_tile(tile) * kTile, hl, qf, q_lds, lane, m_run,
-                      l_run, o);
+    if (i + 1 < n) {
+      if (i + 3 < n) load_tile(ring_tile(tile + 2 * NW), kc, vc, mw, spv);
+      attend(kb, vb, mwb);
     }
+    if (i + 2 < n) attend(kq, vq, mwq);
+    if (i + 3 < n) attend(kc, vc, mw);
   } else if constexpr (kPrefetch) {
     // every tile but the wave's last one: its successor is fetched first
     while (tile + NW < t1) {
