@@ -1,0 +1,103 @@
+"""bench.py's host logic on the CPU: the one-GPU refusal, the algorithmic
+bytes its roofline divides by, the counter summary parsing and the rule that
+drops stale traffic figures."""
+
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+import bench
+import workload as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout.strip() == ""
+
+
+def test_algorithmic_bytes_decode_stream():
+    """cap 4096, q_len 8, 32/8 heads x 128: visible K and V rows (window plus
+    noise block) 4104 x 1024 x 2 B x 2, queries 8 x 32 x 128 x 2 B, noise K and
+    V 2 x 8 x 1024 x 2 B, mask 8 x 4128 x 2 B, output 8 x 32 x 128 x 4 B."""
+    w = W.WORKLOADS["decode_stream"]
+    b = bench.algorithmic_bytes(w, 4096, 4128)
+    assert b["kv"] == 16_809_984
+    assert b["q"] == 65_536
+    assert b["noise"] == 32_768
+    assert b["mask"] == 66_048
+    assert b["attn_kernel"] == 16_974_336
+    assert b["ring_attn"] == 16_974_336 + 131_072
+
+
+def test_algorithmic_bytes_follow_the_window():
+    """A window below cap reads only its own rows; GQA 8 doubles the queries."""
+    w = W.WORKLOADS["large_window"]
+    small = bench.algorithmic_bytes(w, 1000, 32800)
+    full = bench.algorithmic_bytes(w, 32768, 32800)
+    assert full["kv"] - small["kv"] == (32768 - 1000) * w.kv_row * 4
+    assert small["q"] == 8 * 64 * 128 * 2
+
+
+def _write_counter_csv(path, rows):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as fh:
+        wr = csv.DictWriter(fh, fieldnames=["Kernel_Name", "Grid_Size", "Counter_Name",
+                                            "Counter_Value"])
+        wr.writeheader()
+        wr.writerows(rows)
+
+
+def test_counter_summary_averages_per_dispatch(tmp_path):
+    """FETCH_SIZE rows of the kernel (and only of the asked grid size) are
+    averaged; other kernels and counters are ignored."""
+    _write_counter_csv(str(tmp_path / "pmc" / "run" / "x_counter_collection.csv"), [
+        {"Kernel_Name": "ringkv::k_ring_attn<1>", "Grid_Size": 65536,
+         "Counter_Name": "FETCH_SIZE", "Counter_Value": 100.0},
+        {"Kernel_Name": "ringkv::k_ring_attn<1>", "Grid_Size": 65536,
+         "Counter_Name": "FETCH_SIZE", "Counter_Value": 300.0},
+        {"Kernel_Name": "ringkv::k_ring_attn<1>", "Grid_Size": 131072,
+         "Counter_Name": "FETCH_SIZE", "Counter_Value": 900.0},
+        {"Kernel_Name": "ringkv::k_ring_merge<8>", "Grid_Size": 32768,
+         "Counter_Name": "FETCH_SIZE", "Counter_Value": 7.0},
+        {"Kernel_Name": "ringkv::k_ring_attn<1>", "Grid_Size": 65536,
+         "Counter_Name": "WRITE_SIZE", "Counter_Value": 5.0},
+    ])
+    v, n = bench._kib_per_dispatch(str(tmp_path), "pmc", "FETCH_SIZE",
+                                   lambda k: "k_ring_attn" in k, 65536)
+    assert (v, n) == (200.0, 2)
+    v, n = bench._kib_per_dispatch(str(tmp_path), "pmc", "FETCH_SIZE",
+                                   lambda k: "k_ring_attn" in k)
+    assert n == 3 and v == pytest.approx(1300.0 / 3)
+    with pytest.raises(ValueError):
+        bench._kib_per_dispatch(str(tmp_path), "pmc", "FETCH_SIZE",
+                                lambda k: "k_ring_project" in k)
+
+
+def test_traffic_is_dropped_when_the_kernels_changed(tmp_path, monkeypatch):
+    """The committed traffic figure counts only for the kernel source it was
+    measured on."""
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    (prof / "ring_attn_decode_stream_traffic.json").write_text(
+        json.dumps({"kernel_source_hash": "abc", "hbm_bytes_per_launch": 123.0}))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.traffic_from_profiles("abc") == 123.0
+    assert bench.traffic_from_profiles("def") is None
+
+
+def test_bench_line_reader(tmp_path):
+    """The summaries take the bench's JSON line from a log that also holds
+    other output."""
+    (tmp_path / "run.log").write_text("warning: x\n" + json.dumps(
+        {"metric": "m", "value": 1.0}) + "\ntrailing\n")
+    assert bench._bench_line(str(tmp_path), "run") == {"metric": "m", "value": 1.0}
+    assert bench._bench_line(str(tmp_path), "missing") is None
