@@ -849,7 +849,7 @@ __device__ __forceinline__ void merge_store(const EpilogueArgs& a, unsigned char
   }
 }
 
-template <int MB, int NW, int RP, bool FUSED, bool DEEP>
+template <int MB, int NW, int RP, bool FUSED>
 __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs* fa,
                                           const FusedLane& fl, double theta_lane, int unit,
                                           int split, int row0, int vis_first, int vis_count,
@@ -1132,46 +1132,10 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
 
   // ---- 4. ring tiles.  One query block: the next tile's loads are issued
   //      before the current tile is processed (two tiles in registers); two
-  //      query blocks have no room for that.
+  //      query blocks have no room for that.  (Two tiles ahead, through three
+  //      rotating register buffers, measured slower on long waves.)
   constexpr bool kPrefetch = MB == 1;
-  if constexpr (kPrefetch && DEEP) {
-    // Waves with many tiles: tiles i = 0, 1, ... of the wave (tile + i NW)
-    // go through three register buffers in turn, two loaded ahead of the
-    // one attended.  Unrolled by three so that no buffer is ever copied: a
-    // copy of a buffer waits for its loads, which would leave one tile in
-    // flight instead of two.  Buffer A = (kc, vc, mw) holds tile 0.  (Plain
-    // launches only: a fused launch's waves never stream that many tiles.)
-    static_assert(!FUSED, "two tiles in flight in plain launches only");
-    half8 kb[8], vb[8], kq[8], vq[8];
-    uint32_t mwb[MB][8], mwq[MB][8];
-    load_tile(ring_tile(min(tile + NW, tile_last)), kb, vb, mwb, spv);
-    const int n = t1 > tile ? (t1 - tile + NW - 1) / NW : 0;  // tiles of this wave
-    auto attend = [&](const half8 (&k)[8], const half8 (&v)[8], const uint32_t (&m)[MB][8]) {
-      attend_tile<MB>(k, v, m, a.cap - ring_tile(tile) * kTile, hl, qf, q_lds, lane, m_run,
-                      l_run, o);
-      tile += NW;
-    };
-    int i = 0;
-    for (; i + 5 <= n; i += 3) {
-      load_tile(ring_tile(tile + 2 * NW), kq, vq, mwq, spv);
-      attend(kc, vc, mw);
-      load_tile(ring_tile(tile + 2 * NW), kc, vc, mw, spv);
-      attend(kb, vb, mwb);
-      load_tile(ring_tile(tile + 2 * NW), kb, vb, mwb, spv);
-      attend(kq, vq, mwq);
-    }
-    // the last n - i <= 4 tiles: A, B, C, A
-    if (i < n) {
-      if (i + 2 < n) load_tile(ring_tile(tile + 2 * NW), kq, vq, mwq, spv);
-      attend(kc, vc, mw);
-    }
-    if (i + 1 < n) {
-      if (i + 3 < n) load_tile(ring_tile(tile + 2 * NW), kc, vc, mw, spv);
-      attend(kb, vb, mwb);
-    }
-    if (i + 2 < n) attend(kq, vq, mwq);
-    if (i + 3 < n) attend(kc, vc, mw);
-  } else if constexpr (kPrefetch) {
+  if constexpr (kPrefetch) {
     // every tile but the wave's last one: its successor is fetched first
     while (tile + NW < t1) {
       half8 kn[8], vn[8];
@@ -1245,7 +1209,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
   }
 }
 
-template <int MB, int NW, int RP, bool FUSED, bool DEEP = false>
+template <int MB, int NW, int RP, bool FUSED>
 __device__ __forceinline__ void attn_entry(const AttnArgs& a, const FusedAttnArgs* fa) {
   using S = AttnShape<MB, NW, FUSED>;
   __shared__ __attribute__((aligned(16))) unsigned char lds[S::kTotalLds];
@@ -1294,14 +1258,14 @@ __device__ __forceinline__ void attn_entry(const AttnArgs& a, const FusedAttnArg
   const int seq = unit / a.n_head_kv;
   FusedLane fl{};
   if constexpr (FUSED) fl = fused_pick(fv, seq);
-  attn_body<MB, NW, RP, FUSED, DEEP>(a, fa, fl, fv.theta, unit, split, rb * S::MP,
+  attn_body<MB, NW, RP, FUSED>(a, fa, fl, fv.theta, unit, split, rb * S::MP,
                                __builtin_amdgcn_readlane(firstv, seq),
                                __builtin_amdgcn_readlane(countv, seq), lds, sm_m, sm_l);
 }
 
-template <int MB, int NW, int RP, bool DEEP>
+template <int MB, int NW, int RP>
 __global__ __launch_bounds__(NW * 64) void k_ring_attn(AttnArgs a) {
-  attn_entry<MB, NW, RP, false, DEEP>(a, nullptr);
+  attn_entry<MB, NW, RP, false>(a, nullptr);
 }
 
 // The fused launch: the attention work-groups (same mapping as k_ring_attn),
@@ -1524,27 +1488,17 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s, hipEvent_t t0, hipEvent
   const int grid = a.n_seq * a.n_head_kv * a.n_split * a.n_rb;
   // rope table passes: one float4 per thread covers q_len <= 8
   const bool one_pass = a.q_len <= 8;
-  // tiles per wave of the widest window: three or more take the two-deep prefetch
-  int max_count = 0;
-  for (int i = 0; i < a.n_seq && i < RING_MAX_SEQ_INTERNAL; ++i)
-    max_count = max_count > a.vis_count[i] ? max_count : a.vis_count[i];
-  const int per_wave = ((max_count + a.n_split - 1) / a.n_split + 3) / 4;
-  const bool deep = per_wave >= 3;
   // one query block per work-group: m <= 32, or one work-group per row block
   if (a.m <= 32 || a.n_rb > 1) {
-    if (one_pass) {
-      if (deep)
-        hipExtLaunchKernelGGL((k_ring_attn<1, 4, 1, true>), dim3(grid), dim3(256), 0, s, t0, t1, 0, a);
-      else
-        hipExtLaunchKernelGGL((k_ring_attn<1, 4, 1, false>), dim3(grid), dim3(256), 0, s, t0, t1, 0, a);
-    } else {
-      hipExtLaunchKernelGGL((k_ring_attn<1, 4, 4, false>), dim3(grid), dim3(256), 0, s, t0, t1, 0, a);
-    }
+    if (one_pass)
+      hipExtLaunchKernelGGL((k_ring_attn<1, 4, 1>), dim3(grid), dim3(256), 0, s, t0, t1, 0, a);
+    else
+      hipExtLaunchKernelGGL((k_ring_attn<1, 4, 4>), dim3(grid), dim3(256), 0, s, t0, t1, 0, a);
   } else {
     if (one_pass)
-      hipExtLaunchKernelGGL((k_ring_attn<2, 4, 1, false>), dim3(grid), dim3(256), 0, s, t0, t1, 0, a);
+      hipExtLaunchKernelGGL((k_ring_attn<2, 4, 1>), dim3(grid), dim3(256), 0, s, t0, t1, 0, a);
     else
-      hipExtLaunchKernelGGL((k_ring_attn<2, 4, 4, false>), dim3(grid), dim3(256), 0, s, t0, t1, 0, a);
+      hipExtLaunchKernelGGL((k_ring_attn<2, 4, 4>), dim3(grid), dim3(256), 0, s, t0, t1, 0, a);
   }
   return hipGetLastError();
 }

@@ -66,8 +66,8 @@ def test_fused_ragged_cap_short_block():
 ], ids=["ragged", "window_grows"])
 def test_deferred_on_wide_rings(cap, commits):
     """One split per KV head, so the waves stream three or more tiles: the
-    deferred steps append at once (the plain attention keeps two tiles in
-    flight), with the same results."""
+    deferred steps append at once (there the plain attention is the faster
+    one), with the same results."""
     d = Driver(small(cap=cap, seed=306), n_split=1)
     run_fused(d, commits, rows=False)
     d.close()

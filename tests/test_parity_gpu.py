@@ -177,8 +177,9 @@ def test_split_counts_agree(n_split):
     (300, [310, 313, 320, 330]),       # 10 tiles (last ragged): waves of 3, 3, 2 and 2 tiles
     (1000, [200, 204, 990, 1003]),     # window below cap, then across it
 ], ids=["ragged", "window_grows"])
-def test_two_deep_prefetch(cap, commits):
-    """One split per KV head: waves stream three or more tiles with two in flight."""
+def test_long_waves(cap, commits):
+    """One split per KV head: waves stream three or more tiles, each one's
+    successor in flight while it is attended."""
     d = Driver(small(cap=cap, seed=108), n_split=1)
     run_steps(d, commits, check_rows=False)
     d.close()
