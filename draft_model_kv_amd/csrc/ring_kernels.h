@@ -110,6 +110,12 @@ struct FusedSeqs {
   int32_t swa_lo[kFusedMaxSeq];      // lo of the sliding-window mask
 };
 
+// Quotients by a launch constant d without a division: with
+// recip32(d) = ceil(2^32 / d), floor(n / d) = (n * recip32(d)) >> 32 for every
+// n with n * d <= 2^32 (the excess n * (recip32(d) - 2^32 / d) / 2^32 stays
+// below 1 / d, so it never carries into the integer part).
+inline uint64_t recip32(uint32_t d) { return ((uint64_t(1) << 32) + d - 1) / d; }
+
 // One ring_attn launch over every sequence of the ring for one layer.
 struct AttnArgs {
   uint16_t* kring;           // ring base (all sequences and layers)
@@ -131,6 +137,9 @@ struct AttnArgs {
   int32_t n_rb;              // work-groups per (sequence, head, split), one per block of
                              // 32 query rows (one-block kernel; 1 for the others)
   int32_t ring_tiles;        // tiles holding ring slots: ceil(cap / 32)
+  // recip32() of the launch's divisors n_split * n_rb, n_rb, n_head_kv,
+  // n_split and group, filled in by launch_attn / launch_attn_fused.
+  uint64_t rcp_per_unit, rcp_n_rb, rcp_n_head_kv, rcp_n_split, rcp_group;
   // Visible ring tiles of each sequence: vis_count tiles from vis_first on,
   // circularly modulo ring_tiles (the window's slots, slot = position % cap).
   int32_t vis_first[RING_MAX_SEQ_INTERNAL];
@@ -164,6 +173,9 @@ struct MergeArgs {
   const float* part_ml;
   float* out;
   int32_t n_units, n_split, n_head, n_head_kv, group, q_len, m, mpad;
+  // recip32() of the work-groups per unit, n_head_kv and group, filled in
+  // by launch_merge.
+  uint64_t rcp_per_unit, rcp_n_head_kv, rcp_group;
 };
 
 // t0 / t1: optional events bound to the dispatch (start and end of the

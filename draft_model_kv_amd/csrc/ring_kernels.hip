@@ -300,6 +300,11 @@ __global__ __launch_bounds__(256) void k_ring_step_batch(StepBatchArgs b) {
 // ---------------------------------------------------------------------------
 // ring_attn
 // ---------------------------------------------------------------------------
+// floor(n / d) from r = recip32(d), exact for n * d <= 2^32.
+__device__ __forceinline__ uint32_t quot32(uint32_t n, uint64_t r) {
+  return (uint32_t)(((uint64_t)n * r) >> 32);
+}
+
 __device__ inline f32x16 mfma32(half8 a, half8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
@@ -862,7 +867,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
   const int hl = lane >> 5;
   const int col = lane & 31;
 
-  const int seq = unit / a.n_head_kv;
+  const int seq = quot32(unit, a.rcp_n_head_kv);
   const int g = unit - seq * a.n_head_kv;
   const float* ropeq = a.rope_q + (int64_t)seq * a.q_len * 128;
   const uint16_t* mask_seq = a.mask + (int64_t)seq * a.q_len * a.kv_total;
@@ -870,7 +875,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
   // Ring tiles of this split: logical tiles [t0, t1) of the vis_count
   // visible ones; logical tile k is ring tile (vis_first + k) mod ring_tiles.
   const int nvt = vis_count;
-  const int per = (nvt + a.n_split - 1) / a.n_split;
+  const int per = quot32(nvt + a.n_split - 1, a.rcp_n_split);
   auto ring_tile = [&](int k) {
     const int t = vis_first + k;
     return t >= a.ring_tiles ? t - a.ring_tiles : t;
@@ -933,7 +938,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     const int n = row0 + mb * 32 + col;
-    qrow[mb] = n < a.m ? n / a.group : 0;
+    qrow[mb] = n < a.m ? quot32(n, a.rcp_group) : 0;
   }
 
   // ---- 1a. loads for the query build: the sequence's (cos, sin) table once
@@ -964,7 +969,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
     const int item = threadIdx.x + k * NT;
     const int c = (item >> 6) & 3, ln = item & 63;
     const int n = min(row0 + (item >> 8) * 32 + (ln & 31), a.m - 1), h2 = ln >> 5;
-    const unsigned i = n / a.group, hh = n - i * a.group;
+    const unsigned i = quot32(n, a.rcp_group), hh = n - i * a.group;
     const unsigned qo = (i * a.n_head + hh) * kHeadDim + 16 * c + 8 * h2;
     qx[k] = *(const half8*)(qseq + qo);
     qy[k] = *(const half8*)(qseq + qo + 64);
@@ -1239,7 +1244,8 @@ __device__ __forceinline__ void attn_entry(const AttnArgs& a, const FusedAttnArg
                "s"(a.seq_stride), "s"(a.layer_offset), "s"(a.head_stride), "s"(a.n_seq),
                "s"(a.n_head), "s"(a.n_head_kv), "s"(a.group), "s"(a.q_len), "s"(a.m),
                "s"(a.cap), "s"(a.kv_total), "s"(a.n_split), "s"(a.n_rb), "s"(a.ring_tiles),
-               "v"(firstv), "v"(countv));
+               "s"(a.rcp_per_unit), "s"(a.rcp_n_rb), "s"(a.rcp_n_head_kv), "s"(a.rcp_n_split),
+               "s"(a.rcp_group), "v"(firstv), "v"(countv));
   // (the row blocks of one split follow each other, on the same XCD, so
   // that the second read of a tile finds it in that XCD's L2)
   const int n_units = a.n_seq * a.n_head_kv;
@@ -1247,15 +1253,16 @@ __device__ __forceinline__ void attn_entry(const AttnArgs& a, const FusedAttnArg
   int unit, r;
   if ((n_units & 7) == 0) {
     const int xcd = blockIdx.x & 7, k = blockIdx.x >> 3;
-    unit = ((k / per_unit) << 3) + xcd;
-    r = k % per_unit;
+    const int q = quot32(k, a.rcp_per_unit);
+    unit = (q << 3) + xcd;
+    r = k - q * per_unit;
   } else {
-    unit = blockIdx.x / per_unit;
-    r = blockIdx.x % per_unit;
+    unit = quot32(blockIdx.x, a.rcp_per_unit);
+    r = blockIdx.x - unit * per_unit;
   }
-  const int split = r / a.n_rb;
+  const int split = quot32(r, a.rcp_n_rb);
   const int rb = r - split * a.n_rb;
-  const int seq = unit / a.n_head_kv;
+  const int seq = quot32(unit, a.rcp_n_head_kv);
   FusedLane fl{};
   if constexpr (FUSED) fl = fused_pick(fv, seq);
   attn_body<MB, NW, RP, FUSED>(a, fa, fl, fv.theta, unit, split, rb * S::MP,
@@ -1300,10 +1307,11 @@ __global__ __launch_bounds__(256) void k_ring_merge(MergeArgs a) {
   int unit, f;
   if ((a.n_units & 7) == 0) {
     const int xcd = blockIdx.x & 7, k = blockIdx.x >> 3;
-    unit = ((k / per_unit) << 3) + xcd;
-    f = k % per_unit;
+    const int q = quot32(k, a.rcp_per_unit);
+    unit = (q << 3) + xcd;
+    f = k - q * per_unit;
   } else {
-    unit = blockIdx.x / per_unit;
+    unit = quot32(blockIdx.x, a.rcp_per_unit);
     f = blockIdx.x - unit * per_unit;
   }
   const int mb = f >> 4, b = (f >> 2) & 3, jj = f & 3;
@@ -1365,8 +1373,8 @@ __global__ __launch_bounds__(256) void k_ring_merge(MergeArgs a) {
     // Lt > 0: the noise rows are visible to every query.
     const float inv = 1.0f / Lt;
     Ot.x *= inv; Ot.y *= inv; Ot.z *= inv; Ot.w *= inv;
-    const int seq = unit / a.n_head_kv, g = unit - seq * a.n_head_kv;
-    const int i = n / a.group, hh = n - i * a.group;
+    const int seq = quot32(unit, a.rcp_n_head_kv), g = unit - seq * a.n_head_kv;
+    const int i = quot32(n, a.rcp_group), hh = n - i * a.group;
     float* dst = a.out + (((int64_t)seq * a.q_len + i) * a.n_head + g * a.group + hh) * kHeadDim;
     *(float4*)(dst + 32 * b + 8 * jj + 4 * hl) = Ot;
   }
@@ -1484,7 +1492,28 @@ hipError_t launch_step_batch(const StepBatchArgs& b, hipStream_t s, hipEvent_t t
   return hipGetLastError();
 }
 
-hipError_t launch_attn(const AttnArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+// The reciprocals of an attention launch's divisors; false if a quotient
+// could be inexact (a dividend times its divisor above 2^32).
+static bool set_attn_recips(AttnArgs& a) {
+  const uint64_t lim = uint64_t(1) << 32;
+  const uint64_t per_unit = (uint64_t)a.n_split * a.n_rb;
+  const uint64_t grid = (uint64_t)a.n_seq * a.n_head_kv * per_unit;
+  if (a.n_split < 1 || a.n_rb < 1 || a.n_head_kv < 1 || a.group < 1 || grid * per_unit > lim ||
+      (uint64_t)a.n_seq * a.n_head_kv * a.n_head_kv > lim ||
+      (uint64_t)(a.ring_tiles + a.n_split) * a.n_split > lim ||
+      (uint64_t)(a.m + 32 * a.n_rb) * a.group > lim)
+    return false;
+  a.rcp_per_unit = recip32((uint32_t)per_unit);
+  a.rcp_n_rb = recip32(a.n_rb);
+  a.rcp_n_head_kv = recip32(a.n_head_kv);
+  a.rcp_n_split = recip32(a.n_split);
+  a.rcp_group = recip32(a.group);
+  return true;
+}
+
+hipError_t launch_attn(const AttnArgs& args, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+  AttnArgs a = args;
+  if (!set_attn_recips(a)) return hipErrorInvalidValue;
   const int grid = a.n_seq * a.n_head_kv * a.n_split * a.n_rb;
   // rope table passes: one float4 per thread covers q_len <= 8
   const bool one_pass = a.q_len <= 8;
@@ -1503,8 +1532,10 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s, hipEvent_t t0, hipEvent
   return hipGetLastError();
 }
 
-hipError_t launch_attn_fused(const FusedAttnArgs& f, hipStream_t s, hipEvent_t t0,
+hipError_t launch_attn_fused(const FusedAttnArgs& args, hipStream_t s, hipEvent_t t0,
                              hipEvent_t t1) {
+  FusedAttnArgs f = args;
+  if (!set_attn_recips(f.a)) return hipErrorInvalidValue;
   const AttnArgs& a = f.a;
   const int grid = f.n_attn_blocks;
   const bool one_pass = a.q_len <= 8;
@@ -1522,7 +1553,17 @@ hipError_t launch_attn_fused(const FusedAttnArgs& f, hipStream_t s, hipEvent_t t
   return hipGetLastError();
 }
 
-hipError_t launch_merge(const MergeArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+hipError_t launch_merge(const MergeArgs& args, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+  MergeArgs a = args;
+  const uint64_t per_unit = (uint64_t)(a.mpad / 32) * 16;
+  if (a.n_head_kv < 1 || a.group < 1 || per_unit < 1 ||
+      (uint64_t)a.n_units * per_unit * per_unit > (uint64_t(1) << 32) ||
+      (uint64_t)a.n_units * a.n_head_kv > (uint64_t(1) << 32) ||
+      (uint64_t)a.mpad * a.group > (uint64_t(1) << 32))
+    return hipErrorInvalidValue;
+  a.rcp_per_unit = recip32((uint32_t)per_unit);
+  a.rcp_n_head_kv = recip32(a.n_head_kv);
+  a.rcp_group = recip32(a.group);
   const dim3 grid(a.n_units * (a.mpad / 32) * 16), block(256);
   const int per_wave = (a.n_split + 3) / 4;  // splits per wave (n_split <= 64)
   if (per_wave <= 1) {
