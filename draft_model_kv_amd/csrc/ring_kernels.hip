@@ -317,10 +317,11 @@ __device__ inline float f16_hi(uint32_t w) {
 }
 
 // Query fragments (B operand of S^T = K Q^T): query block mb, chunk c, lane.
-// Kept in registers for one query block, read from LDS for two.
-template <int MB>
+// Kept in registers (QL false) or read from LDS at each use (QL true: two
+// query blocks, or waves that attend one tile).
+template <int MB, bool QL = (MB > 1)>
 struct QFrag {
-  static constexpr bool kLds = MB > 1;
+  static constexpr bool kLds = QL;
   half8 hi[kLds ? 1 : MB][kLds ? 1 : 8];
   half8 lo[kLds ? 1 : MB][kLds ? 1 : 8];
 };
@@ -331,10 +332,10 @@ struct QFrag {
 //   mw       mask of accumulator rows j = 4 jj + u, two F16 per word:
 //            mw[mb][2 jj + (u >> 1)], low half for even u
 //   limit    rows r >= limit of this tile are hidden (-inf)
-template <int MB>
+template <int MB, bool QL>
 __device__ inline void attend_tile(const half8 (&kc)[8], const half8 (&vc)[8],
                                    const uint32_t (&mw)[MB][8], int limit, int hl,
-                                   const QFrag<MB>& q, const half8* q_lds, int lane,
+                                   const QFrag<MB, QL>& q, const half8* q_lds, int lane,
                                    float (&m_run)[MB], float (&l_run)[MB],
                                    f32x16 (&o)[MB][4]) {
 #pragma unroll
@@ -343,7 +344,7 @@ __device__ inline void attend_tile(const half8 (&kc)[8], const half8 (&vc)[8],
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       half8 qh, ql;
-      if constexpr (QFrag<MB>::kLds) {
+      if constexpr (QL) {
         qh = q_lds[((mb * 2 + 0) * 8 + c) * 64 + lane];
         ql = q_lds[((mb * 2 + 1) * 8 + c) * 64 + lane];
       } else {
@@ -546,7 +547,9 @@ __device__ __forceinline__ void tile_mask_words(const FusedCtx& fx, int tile, in
 // in-bounds (clamped) address and selected afterwards: the compiler can then
 // wait for each group of loads alone instead of draining all of them at a
 // control-flow join.
-template <int MB, int NW, bool FUSED = false>
+// SHARE: the merge buffer reuses the prologue bytes (a work-group small
+// enough for two per CU).
+template <int MB, int NW, bool FUSED = false, bool SHARE = false>
 struct AttnShape {
   static constexpr int MP = MB * 32;               // padded queries
   static constexpr int NT = NW * 64;               // threads
@@ -563,7 +566,7 @@ struct AttnShape {
   // loop ends.  With one query block the merge buffer has bytes of its own,
   // so a wave writes it as soon as its own loop ends; with two it reuses the
   // prologue bytes behind a barrier that every wave reaches after its loop.
-  static constexpr bool kOwnMergeBytes = kQBytes + kRowBytes + kMergeBytes <= 96 * 1024;
+  static constexpr bool kOwnMergeBytes = !SHARE && kQBytes + kRowBytes + kMergeBytes <= 96 * 1024;
   static constexpr int kMergeOffset = kOwnMergeBytes ? kQBytes + kRowBytes : 0;
   static constexpr int kLdsBytes =
       kOwnMergeBytes ? kQBytes + kRowBytes + kMergeBytes
@@ -631,10 +634,10 @@ __device__ __forceinline__ void load_noise_row(const AttnArgs& a, const FusedCtx
 // on the vector unit (dot products of the hi and lo query fragments with the
 // F16 key); the P V update is one matrix op per 32-dim block with the row as
 // slot 0 of a V fragment.
-template <int MB, bool FUSED>
+template <int MB, bool FUSED, bool QL>
 __device__ __forceinline__ void attend_noise_row(
     const AttnArgs& a, const FusedCtx& fx, const NoiseRow<MB>& nr, int r, uint16_t* kh,
-    uint16_t* vh, uint16_t* rowk, uint16_t* rowv, int lane, int hl, int col, const QFrag<MB>& q,
+    uint16_t* vh, uint16_t* rowk, uint16_t* rowv, int lane, int hl, int col, const QFrag<MB, QL>& q,
     const half8* q_lds, float (&m_run)[MB], float (&l_run)[MB], f32x16 (&o)[MB][4],
     bool store_row) {
   double2 cs = nr.cs;
@@ -682,7 +685,7 @@ __device__ __forceinline__ void attend_noise_row(
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       half8 qh, ql;
-      if constexpr (QFrag<MB>::kLds) {
+      if constexpr (QL) {
         qh = q_lds[((mb * 2 + 0) * 8 + c) * 64 + lane];
         ql = q_lds[((mb * 2 + 1) * 8 + c) * 64 + lane];
       } else {
@@ -763,12 +766,12 @@ struct EpilogueArgs {
   int row0;  // first query row of this work-group's block(s)
 };
 
-template <int MB, int NW, int W>
+template <int MB, int NW, int W, bool SHARE>
 __device__ __forceinline__ void merge_store(const EpilogueArgs& a, unsigned char* lds,
                                             float (*sm_m)[MB * 32], float (*sm_l)[MB * 32],
                                             const float (&m_run)[MB], const float (&l_run)[MB],
                                             const f32x16 (&o)[MB][4], int lane) {
-  using S = AttnShape<MB, NW>;
+  using S = AttnShape<MB, NW, false, SHARE>;
   const int hl = lane >> 5, col = lane & 31;
   // [mb][block][writer][jj][lane]
   float4* xbuf = reinterpret_cast<float4*>(lds + S::kMergeOffset);
@@ -854,13 +857,19 @@ __device__ __forceinline__ void merge_store(const EpilogueArgs& a, unsigned char
   }
 }
 
-template <int MB, int NW, int RP, bool FUSED>
+// SHORT: every wave attends at most one ring tile.  Then nothing is fetched
+// ahead, the query fragments are read from LDS at each use instead of held in
+// registers, and a plain launch's work-group shares its merge bytes with the
+// prologue, so that two work-groups fit one CU.
+template <int MB, int NW, int RP, bool FUSED, bool SHORT>
 __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs* fa,
                                           const FusedLane& fl, double theta_lane, int unit,
                                           int split, int row0, int vis_first, int vis_count,
                                           unsigned char* lds, float (*sm_m)[MB * 32],
                                           float (*sm_l)[MB * 32]) {
-  using S = AttnShape<MB, NW, FUSED>;
+  constexpr bool QL = MB > 1 || SHORT;
+  constexpr bool SHARE = SHORT && !FUSED;
+  using S = AttnShape<MB, NW, FUSED, SHARE>;
   constexpr int MP = S::MP, NT = S::NT;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1100,8 +1109,8 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
   }
   lds_barrier();
 
-  QFrag<MB> qf;
-  if constexpr (!QFrag<MB>::kLds) {
+  QFrag<MB, QL> qf;
+  if constexpr (!QL) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -1126,11 +1135,11 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
   uint16_t* rowv = rowk + kHeadDim;
   if (rank < n_extra) {
     const bool store_rows = row0 == 0;  // one row block stores the rotated rows
-    attend_noise_row<MB, FUSED>(a, fx, nr, rank, kh, vh, rowk, rowv, lane, hl, col, qf, q_lds, m_run,
+    attend_noise_row<MB, FUSED, QL>(a, fx, nr, rank, kh, vh, rowk, rowv, lane, hl, col, qf, q_lds, m_run,
                          l_run, o, store_rows);
     for (int r = rank + n_waves; r < n_extra; r += n_waves) {
       load_noise_row<MB, FUSED>(a, fx, seq, g, r, mask_seq, qrow, lane, nr);
-      attend_noise_row<MB, FUSED>(a, fx, nr, r, kh, vh, rowk, rowv, lane, hl, col, qf, q_lds, m_run,
+      attend_noise_row<MB, FUSED, QL>(a, fx, nr, r, kh, vh, rowk, rowv, lane, hl, col, qf, q_lds, m_run,
                            l_run, o, store_rows);
     }
   }
@@ -1139,7 +1148,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
   //      before the current tile is processed (two tiles in registers); two
   //      query blocks have no room for that.  (Two tiles ahead, through three
   //      rotating register buffers, measured slower on long waves.)
-  constexpr bool kPrefetch = MB == 1;
+  constexpr bool kPrefetch = MB == 1 && !SHORT;
   if constexpr (kPrefetch) {
     // every tile but the wave's last one: its successor is fetched first
     while (tile + NW < t1) {
@@ -1148,7 +1157,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
       int4 spn[4];
       load_tile(ring_tile(tile + NW), kn, vn, mn, spn);
       prep_tile(ring_tile(tile), kc, vc, mw, spv);
-      attend_tile<MB>(kc, vc, mw, a.cap - ring_tile(tile) * kTile, hl, qf, q_lds, lane, m_run,
+      attend_tile<MB, QL>(kc, vc, mw, a.cap - ring_tile(tile) * kTile, hl, qf, q_lds, lane, m_run,
                       l_run, o);
 #pragma unroll
       for (int c = 0; c < 8; ++c) { kc[c] = kn[c]; vc[c] = vn[c]; }
@@ -1164,14 +1173,14 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
     }
     if (tile < t1) {
       prep_tile(ring_tile(tile), kc, vc, mw, spv);
-      attend_tile<MB>(kc, vc, mw, a.cap - ring_tile(tile) * kTile, hl, qf, q_lds, lane, m_run,
+      attend_tile<MB, QL>(kc, vc, mw, a.cap - ring_tile(tile) * kTile, hl, qf, q_lds, lane, m_run,
                       l_run, o);
     }
   } else {
     while (tile < t1) {
       const int next = tile + NW;
       prep_tile(ring_tile(tile), kc, vc, mw, spv);
-      attend_tile<MB>(kc, vc, mw, a.cap - ring_tile(tile) * kTile, hl, qf, q_lds, lane, m_run,
+      attend_tile<MB, QL>(kc, vc, mw, a.cap - ring_tile(tile) * kTile, hl, qf, q_lds, lane, m_run,
                       l_run, o);
       if (next < t1) load_tile(ring_tile(next), kc, vc, mw, spv);
       tile = next;
@@ -1182,13 +1191,13 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
   //      that the wave's own accumulator block is picked at compile time.
   static_assert(NW == 4, "one 32-dim output block per wave");
   if (wave == 0)
-    merge_store<MB, NW, 0>(ep, lds, sm_m, sm_l, m_run, l_run, o, lane);
+    merge_store<MB, NW, 0, SHARE>(ep, lds, sm_m, sm_l, m_run, l_run, o, lane);
   else if (wave == 1)
-    merge_store<MB, NW, 1>(ep, lds, sm_m, sm_l, m_run, l_run, o, lane);
+    merge_store<MB, NW, 1, SHARE>(ep, lds, sm_m, sm_l, m_run, l_run, o, lane);
   else if (wave == 2)
-    merge_store<MB, NW, 2>(ep, lds, sm_m, sm_l, m_run, l_run, o, lane);
+    merge_store<MB, NW, 2, SHARE>(ep, lds, sm_m, sm_l, m_run, l_run, o, lane);
   else
-    merge_store<MB, NW, 3>(ep, lds, sm_m, sm_l, m_run, l_run, o, lane);
+    merge_store<MB, NW, 3, SHARE>(ep, lds, sm_m, sm_l, m_run, l_run, o, lane);
   if constexpr (FUSED) {
     const StepArgs sa = fused_index_args(*fa, fl, seq);
     for (int ix = ix_blk; ix >= 0 && ix < fa->n_index_blocks; ix += ix_step) {
@@ -1214,9 +1223,9 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
   }
 }
 
-template <int MB, int NW, int RP, bool FUSED>
+template <int MB, int NW, int RP, bool FUSED, bool SHORT>
 __device__ __forceinline__ void attn_entry(const AttnArgs& a, const FusedAttnArgs* fa) {
-  using S = AttnShape<MB, NW, FUSED>;
+  using S = AttnShape<MB, NW, FUSED, SHORT && !FUSED>;
   __shared__ __attribute__((aligned(16))) unsigned char lds[S::kTotalLds];
   __shared__ float sm_m[NW][S::MP];
   __shared__ float sm_l[NW][S::MP];
@@ -1265,23 +1274,23 @@ __device__ __forceinline__ void attn_entry(const AttnArgs& a, const FusedAttnArg
   const int seq = quot32(unit, a.rcp_n_head_kv);
   FusedLane fl{};
   if constexpr (FUSED) fl = fused_pick(fv, seq);
-  attn_body<MB, NW, RP, FUSED>(a, fa, fl, fv.theta, unit, split, rb * S::MP,
+  attn_body<MB, NW, RP, FUSED, SHORT>(a, fa, fl, fv.theta, unit, split, rb * S::MP,
                                __builtin_amdgcn_readlane(firstv, seq),
                                __builtin_amdgcn_readlane(countv, seq), lds, sm_m, sm_l);
 }
 
-template <int MB, int NW, int RP>
-__global__ __launch_bounds__(NW * 64) void k_ring_attn(AttnArgs a) {
-  attn_entry<MB, NW, RP, false>(a, nullptr);
+template <int MB, int NW, int RP, bool SHORT>
+__global__ __launch_bounds__(NW * 64, SHORT ? 2 : 1) void k_ring_attn(AttnArgs a) {
+  attn_entry<MB, NW, RP, false, SHORT>(a, nullptr);
 }
 
 // The fused launch: the attention work-groups (same mapping as k_ring_attn),
 // which also append the step's new rows and rebuild the index state (slot_pos,
 // masks, noise RoPE table) of the sequences that owe it.
-template <int MB, int NW, int RP>
+template <int MB, int NW, int RP, bool SHORT>
 __global__ __launch_bounds__(NW * 64) void k_ring_attn_fused(FusedAttnArgs f) {
   static_assert(NW * 64 == 256, "an index block is one slot per thread");
-  attn_entry<MB, NW, RP, true>(f.a, &f);
+  attn_entry<MB, NW, RP, true, SHORT>(f.a, &f);
 }
 
 // ---------------------------------------------------------------------------
@@ -1511,23 +1520,38 @@ static bool set_attn_recips(AttnArgs& a) {
   return true;
 }
 
+// Whether every wave of the launch attends at most one ring tile (the widest
+// window's tiles over n_split splits of 4 waves).
+static bool short_waves(const AttnArgs& a) {
+  int max_count = 0;
+  for (int i = 0; i < a.n_seq && i < RING_MAX_SEQ_INTERNAL; ++i)
+    max_count = max_count > a.vis_count[i] ? max_count : a.vis_count[i];
+  const int per_split = (max_count + a.n_split - 1) / a.n_split;
+  return per_split <= 4;
+}
+
 hipError_t launch_attn(const AttnArgs& args, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
   AttnArgs a = args;
   if (!set_attn_recips(a)) return hipErrorInvalidValue;
   const int grid = a.n_seq * a.n_head_kv * a.n_split * a.n_rb;
   // rope table passes: one float4 per thread covers q_len <= 8
   const bool one_pass = a.q_len <= 8;
+  const bool sw = short_waves(a);
   // one query block per work-group: m <= 32, or one work-group per row block
   if (a.m <= 32 || a.n_rb > 1) {
-    if (one_pass)
-      hipExtLaunchKernelGGL((k_ring_attn<1, 4, 1>), dim3(grid), dim3(256), 0, s, t0, t1, 0, a);
+    if (one_pass && sw)
+      hipExtLaunchKernelGGL((k_ring_attn<1, 4, 1, true>), dim3(grid), dim3(256), 0, s, t0, t1, 0, a);
+    else if (one_pass)
+      hipExtLaunchKernelGGL((k_ring_attn<1, 4, 1, false>), dim3(grid), dim3(256), 0, s, t0, t1, 0, a);
+    else if (sw)
+      hipExtLaunchKernelGGL((k_ring_attn<1, 4, 4, true>), dim3(grid), dim3(256), 0, s, t0, t1, 0, a);
     else
-      hipExtLaunchKernelGGL((k_ring_attn<1, 4, 4>), dim3(grid), dim3(256), 0, s, t0, t1, 0, a);
+      hipExtLaunchKernelGGL((k_ring_attn<1, 4, 4, false>), dim3(grid), dim3(256), 0, s, t0, t1, 0, a);
   } else {
     if (one_pass)
-      hipExtLaunchKernelGGL((k_ring_attn<2, 4, 1>), dim3(grid), dim3(256), 0, s, t0, t1, 0, a);
+      hipExtLaunchKernelGGL((k_ring_attn<2, 4, 1, false>), dim3(grid), dim3(256), 0, s, t0, t1, 0, a);
     else
-      hipExtLaunchKernelGGL((k_ring_attn<2, 4, 4>), dim3(grid), dim3(256), 0, s, t0, t1, 0, a);
+      hipExtLaunchKernelGGL((k_ring_attn<2, 4, 4, false>), dim3(grid), dim3(256), 0, s, t0, t1, 0, a);
   }
   return hipGetLastError();
 }
@@ -1539,16 +1563,21 @@ hipError_t launch_attn_fused(const FusedAttnArgs& args, hipStream_t s, hipEvent_
   const AttnArgs& a = f.a;
   const int grid = f.n_attn_blocks;
   const bool one_pass = a.q_len <= 8;
+  const bool sw = short_waves(a);
   if (a.m <= 32 || a.n_rb > 1) {
-    if (one_pass)
-      hipExtLaunchKernelGGL((k_ring_attn_fused<1, 4, 1>), dim3(grid), dim3(256), 0, s, t0, t1, 0, f);
+    if (one_pass && sw)
+      hipExtLaunchKernelGGL((k_ring_attn_fused<1, 4, 1, true>), dim3(grid), dim3(256), 0, s, t0, t1, 0, f);
+    else if (one_pass)
+      hipExtLaunchKernelGGL((k_ring_attn_fused<1, 4, 1, false>), dim3(grid), dim3(256), 0, s, t0, t1, 0, f);
+    else if (sw)
+      hipExtLaunchKernelGGL((k_ring_attn_fused<1, 4, 4, true>), dim3(grid), dim3(256), 0, s, t0, t1, 0, f);
     else
-      hipExtLaunchKernelGGL((k_ring_attn_fused<1, 4, 4>), dim3(grid), dim3(256), 0, s, t0, t1, 0, f);
+      hipExtLaunchKernelGGL((k_ring_attn_fused<1, 4, 4, false>), dim3(grid), dim3(256), 0, s, t0, t1, 0, f);
   } else {
     if (one_pass)
-      hipExtLaunchKernelGGL((k_ring_attn_fused<2, 4, 1>), dim3(grid), dim3(256), 0, s, t0, t1, 0, f);
+      hipExtLaunchKernelGGL((k_ring_attn_fused<2, 4, 1, false>), dim3(grid), dim3(256), 0, s, t0, t1, 0, f);
     else
-      hipExtLaunchKernelGGL((k_ring_attn_fused<2, 4, 4>), dim3(grid), dim3(256), 0, s, t0, t1, 0, f);
+      hipExtLaunchKernelGGL((k_ring_attn_fused<2, 4, 4, false>), dim3(grid), dim3(256), 0, s, t0, t1, 0, f);
   }
   return hipGetLastError();
 }
