@@ -176,6 +176,10 @@ __device__ inline void step_block(const StepArgs& a, const int blk) {
     if (layer < 64 && ((a.layer_skip >> layer) & 1u)) return;
     const int i = blk - layer * rows_per_layer;
     const bool pad = i >= a.n_rows;
+    // Every pad row is the same zero row for the same trash slot: the first
+    // pad block writes it and the others have nothing to add (many blocks
+    // storing to one row's cache lines at once queue behind each other).
+    if (pad && i != a.n_rows) return;
     int slot;
     int64_t p = 0;
     gcu16* ksrc = nullptr;
