@@ -73,6 +73,16 @@ def test_deferred_on_wide_rings(cap, commits):
     d.close()
 
 
+@pytest.mark.parametrize("q_len,n_head", [(8, 32), (16, 32)], ids=["q8", "q16_two_blocks"])
+def test_fused_two_tiles_per_wave(q_len, n_head):
+    """7 ring tiles (the last ragged) in one split: waves of two tiles, so
+    the fused launch keeps the next tile in flight (the deferred steps stay
+    fused at this width)."""
+    d = Driver(small(cap=200, q_len=q_len, n_head=n_head, seed=307 + q_len), n_split=1)
+    run_fused(d, [150, 151, 159, 203, 210, 211, 190, 199])
+    d.close()
+
+
 def test_fused_multi_layer_sliding_window():
     """4 layers, layers 1 and 3 sliding over 16 positions (new rows that fall
     before the window are still appended), full acceptance steps."""

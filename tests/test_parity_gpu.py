@@ -119,6 +119,16 @@ def test_long_noise_block_two_query_blocks(row_blocks):
     d.close()
 
 
+def test_long_noise_block_long_waves():
+    """q_len 16 with GQA 4 and one split per KV head: waves stream several
+    tiles (the kernel that keeps the next tile in flight) with the noise
+    rows of the long block on the same waves."""
+    w = small(cap=1000, q_len=16, n_head=32, seed=111)
+    d = Driver(w, n_split=1)
+    run_steps(d, [600, 601, 617, 990, 1003, 1020])
+    d.close()
+
+
 def test_multi_seq_multi_layer():
     w = small(cap=128, n_layer=2, n_seq=3, seed=105)
     d = Driver(w)
