@@ -115,6 +115,10 @@ struct FusedSeqs {
 // n with n * d <= 2^32 (the excess n * (recip32(d) - 2^32 / d) / 2^32 stays
 // below 1 / d, so it never carries into the integer part).
 inline uint64_t recip32(uint32_t d) { return ((uint64_t(1) << 32) + d - 1) / d; }
+// floor(n / d) from r = recip32(d), exact for n * d <= 2^32.
+__host__ __device__ inline uint32_t quot32(uint32_t n, uint64_t r) {
+  return (uint32_t)(((uint64_t)n * r) >> 32);
+}
 
 // One ring_attn launch over every sequence of the ring for one layer.
 struct AttnArgs {

@@ -304,11 +304,6 @@ __global__ __launch_bounds__(256) void k_ring_step_batch(StepBatchArgs b) {
 // ---------------------------------------------------------------------------
 // ring_attn
 // ---------------------------------------------------------------------------
-// floor(n / d) from r = recip32(d), exact for n * d <= 2^32.
-__device__ __forceinline__ uint32_t quot32(uint32_t n, uint64_t r) {
-  return (uint32_t)(((uint64_t)n * r) >> 32);
-}
-
 __device__ inline f32x16 mfma32(half8 a, half8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
