@@ -129,6 +129,30 @@ def test_long_noise_block_long_waves():
     d.close()
 
 
+@pytest.mark.parametrize("q_len,n_head,n_head_kv", [
+    (8, 8, 8),      # group 1: one query head per KV head
+    (1, 16, 8),     # group 2, a one-row noise block
+    (3, 16, 1),     # one KV head for 16 query heads (m = 48, a ragged second block;
+                    # one unit, so the work-groups are not pinned to XCDs)
+    (13, 24, 8),    # group 3, q_len 13 (m = 39: a ragged second query block)
+], ids=["g1_q8", "g2_q1", "g16_q3", "g3_q13"])
+@pytest.mark.parametrize("deferred", [False, True], ids=["eager", "fused"])
+def test_head_groupings(q_len, n_head, n_head_kv, deferred):
+    """Group sizes and noise-block lengths the headline shape does not
+    have: every quotient the kernels take by a launch constant (query row
+    by group, unit by KV heads, work-group by splits and row blocks) with
+    divisors other than the headline's."""
+    w = small(cap=160, q_len=q_len, n_head=n_head, n_head_kv=n_head_kv,
+              seed=120 + q_len + n_head + n_head_kv)
+    d = Driver(w)
+    for c in [90, 91, 97, 160, 171, 172]:
+        d.step(0, c, deferred=deferred)
+        d.check_attn_layers(c)
+        d.check_index(0)
+        d.check_rows(0, 0)
+    d.close()
+
+
 def test_multi_seq_multi_layer():
     w = small(cap=128, n_layer=2, n_seq=3, seed=105)
     d = Driver(w)
