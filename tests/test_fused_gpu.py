@@ -116,6 +116,24 @@ def test_fused_multi_seq():
     d.close()
 
 
+@pytest.mark.parametrize("n_seq", [8, 9], ids=["eight_fused", "nine_append_at_once"])
+def test_fused_sequence_limit(n_seq):
+    """Eight sequences fill every lane of a fused launch's per-sequence
+    fields; a ninth makes the deferred steps append at once.  Each sequence
+    starts at its own position, some below cap, some past a wrap."""
+    w = small(cap=96, n_seq=n_seq, seed=310 + n_seq)
+    d = Driver(w)
+    starts = [20 + 37 * s for s in range(n_seq)]
+    for t, inc in enumerate([0, 1, 7, 3, 9, 2]):
+        for s in range(n_seq):
+            d.step(s, starts[s] + 5 * t + inc, deferred=True)
+        d.check_attn_layers(t)
+        for s in range(n_seq):
+            d.check_index(s)
+            d.check_rows(s, 0)
+    d.close()
+
+
 def test_fused_flush_paths():
     """A read right after the deferred step, attention of one layer of two,
     and two deferred steps in a row: the owed rows go in by the ordinary
