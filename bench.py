@@ -78,23 +78,18 @@ def traffic_from_profiles(kernel_hash: str):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, seconds: float) -> dict:
-    """The oracle (full cache, fp32-accumulated attention) on the host cores."""
+def _oracle_steps(w, seconds: float):
+    """Steps of the decode stream through the oracle for about `seconds` of
+    CPU time: (steps, seconds), inputs generated outside the timed part."""
     import numpy as np
     import oracle.ring_oracle as ro
     import workload as W
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
     geo = ro.geometry(w.cap, w.q_len, w.head_dim, w.n_head_kv)
     st = ro.RingStep(geo, 1, w.n_head_kv, w.head_dim, w.rope_base)
     stream = W.commit_stream(w, 0)
     p = st.plan(stream[0])
     pos = np.arange(p.start, stream[0])
     st.commit(p, [W.context_rows(w, 0, 0, W.T_K, pos)], [W.context_rows(w, 0, 0, W.T_V, pos)])
-    inputs = []
     n_steps, t_total = 0, 0.0
     for j in range(1, len(stream)):
         c = stream[j]
@@ -110,17 +105,41 @@ def cpu_baseline(w, seconds: float) -> dict:
         n_steps += 1
         if t_total >= seconds and n_steps >= 5:
             break
-    return {"value": n_steps / t_total, "unit": "steps/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{n_steps} decode steps of the cap-4096 stream after a 4096-row prefill "
-                      f"(store new rows with fp64 RoPE + fp32 attention), {t_total:.1f} s"}
+    return n_steps, t_total
 
 
-def prepare(w, pool: int, total: int, dev):
+def cpu_baseline(w, seconds: float) -> dict:
+    """The oracle (full cache, fp32-accumulated attention) on the host cores,
+    with numpy's own thread count and with one thread."""
+    avail = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except ImportError:
+        threadpool_limits, blas = None, 1
+    n, t = _oracle_steps(w, seconds)
+    one = None
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            n1, t1 = _oracle_steps(w, seconds / 2)
+        one = {"value": n1 / t1, "steps": n1, "seconds": round(t1, 2)}
+    return {"value": n / t, "unit": "steps/s", "cores": int(min(blas, avail)), "kind": "oracle",
+            "cores_available": avail, "blas_threads": int(blas),
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
+            "one_thread": one,
+            "sample": f"{n} decode steps of the cap-4096 stream after a 4096-row prefill "
+                      f"(store new rows with fp64 RoPE + fp32 attention), {t:.1f} s; the "
+                      f"attention's matrix products run on numpy's BLAS threads ({blas}), "
+                      f"the rest of the oracle on one"}
+
+
+def prepare(w, pool: int, total: int, dev, extra0: int = 0):
     """Rings of workload ``w`` warmed up, and the device-resident inputs of
-    ``total`` steps cycled over ``pool`` rings.  Returns (rings, calls, geo,
-    committed), calls[t] = (handle, [(seq, committed, k, v, n)...],
-    [(layer, q, kn, vn)...])."""
+    ``total`` steps cycled over ``pool`` rings, plus ``extra0`` further steps
+    of ring 0 alone (fewer if its stream ends first).  Returns (rings, calls,
+    (steps_in, extra), committed, calls0), calls[t] = (handle, [(seq,
+    committed, k, v, n)...], [(layer, q, kn, vn)...], weights) and calls0 the
+    further steps of ring 0 in the same form."""
     import numpy as np
     import torch
     import workload as W
@@ -128,8 +147,9 @@ def prepare(w, pool: int, total: int, dev):
 
     streams = [W.commit_stream(w, s_) for s_ in range(w.n_seq)]
     n_warm = W.n_warmup_steps(w)
-    n_dec = -(-total // pool)
-    if n_dec + n_warm > len(streams[0]):
+    n_used0 = -(-total // pool)          # steps ring 0 takes in the cycled calls
+    n_dec = min(n_used0 + extra0, len(streams[0]) - n_warm)
+    if n_used0 + n_warm > len(streams[0]):
         raise SystemExit(f"need {n_dec} decode steps per ring, stream has {len(streams[0]) - n_warm}")
     rings = [R.Ring(cap=w.cap, q_len=w.q_len, n_head=w.n_head, n_head_kv=w.n_head_kv,
                     head_dim=w.head_dim, n_layer=w.n_layer, n_seq=w.n_seq,
@@ -196,21 +216,22 @@ def prepare(w, pool: int, total: int, dev):
                            torch.from_numpy(np.stack(ks)).to(dev),
                            torch.from_numpy(np.stack(vs)).to(dev)))
         steps_in.append((seqs, layers))
-    calls = []
-    for t in range(total):
-        r, (seqs, layers) = rings[t % pool], steps_in[t // pool]
+    def call(r_i, j):
+        seqs, layers = steps_in[j]
         if mirror:
             sq = [(seq, c, f.data_ptr(), c0, n) for seq, c, f, c0, n in seqs]
         else:
             sq = [(seq, c, k.data_ptr(), v.data_ptr(), n) for seq, c, k, v, n in seqs]
-        calls.append((r.handle, sq,
-                      [(layer, q.data_ptr(), kn.data_ptr(), vn.data_ptr())
-                       for layer, q, kn, vn in layers],
-                      wptrs[t % pool] if mirror else None))
+        return (rings[r_i].handle, sq,
+                [(layer, q.data_ptr(), kn.data_ptr(), vn.data_ptr()) for layer, q, kn, vn in layers],
+                wptrs[r_i] if mirror else None)
+
+    calls = [call(t % pool, t // pool) for t in range(total)]
+    calls0 = [call(0, j) for j in range(n_used0, n_dec)]
     committed = [[streams[seq][n_warm + t // pool] for seq in range(w.n_seq)]
                  for t in range(total)]
     extra = weights if mirror else None
-    return rings, calls, (steps_in, extra), committed
+    return rings, calls, (steps_in, extra), committed, calls0
 
 
 # The rocprofv3 runs behind the committed summaries under profiles/, each run
@@ -218,7 +239,13 @@ def prepare(w, pool: int, total: int, dev):
 # directory; `python bench.py --summarize OUT` then writes the summaries.
 PROFILE_RUNS = {
     "prof_ktrace": "rocprofv3 --kernel-trace --stats --output-format csv -d OUT/prof_ktrace -o run "
-                   "-- python REPO/bench.py --steps 1000 --warmup 100 --no-cpu-baseline",
+                   "-- python REPO/bench.py --steps 1000 --warmup 100 --no-cpu-baseline "
+                   "--floor-launches 0",
+    # the floors of the decode stream's attention launch (ring_profile_floor)
+    "prof_ktrace_floor": "rocprofv3 --kernel-trace --stats --output-format csv -d "
+                         "OUT/prof_ktrace_floor -o run -- python REPO/bench.py --floor "
+                         "--floor-launches 400 --warmup 100",
+    "bench_floor": "python REPO/bench.py --floor --floor-launches 400 --warmup 100",
     "pmc_fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/pmc_fetch -o run "
                  "-- python REPO/bench.py --steps 64 --warmup 16 --no-cpu-baseline",
     "pmc_write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/pmc_write -o run "
@@ -229,7 +256,8 @@ PROFILE_RUNS = {
                       "-- python REPO/bench.py --calibrate-copy 1024",
     # the same bench without the profiler (its HIP-event kernel times are
     # compared with the trace; the tracer itself slows event-bound dispatches)
-    "bench_plain": "python REPO/bench.py --steps 1000 --warmup 100 --no-cpu-baseline",
+    "bench_plain": "python REPO/bench.py --steps 1000 --warmup 100 --no-cpu-baseline "
+                   "--floor-launches 0",
     # rows from the feature mirror: the projection kernel
     "prof_ktrace_mirror": "rocprofv3 --kernel-trace --stats --output-format csv -d "
                           "OUT/prof_ktrace_mirror -o run -- python REPO/bench.py --workload "
@@ -295,6 +323,40 @@ def _bench_line(out_dir: str, run: str):
     return None
 
 
+def trace_timeline(out_dir: str, run: str, steps: int) -> dict:
+    """Per-dispatch timestamps of the kernel trace: the first `steps`
+    consecutive attention dispatches after the clock warm-up's fill kernels
+    (the timed steps), each followed by its merge.  Medians in us of the
+    attention and merge durations, the gaps between them and the period from
+    one attention start to the next."""
+    import statistics as stt
+    rows = sorted(_csv_rows(out_dir, run, "kernel_trace"), key=lambda r: int(r["Start_Timestamp"]))
+    last_fill = max((i for i, r in enumerate(rows) if "Fill" in r["Kernel_Name"]
+                     and "rocclr" not in r["Kernel_Name"]), default=-1)
+    seq = [r for r in rows[last_fill + 1:] if "k_ring_attn" in r["Kernel_Name"]
+           or "k_ring_merge" in r["Kernel_Name"] or "k_ring_step" in r["Kernel_Name"]]
+    attn = [i for i, r in enumerate(seq) if "k_ring_attn" in r["Kernel_Name"]][:steps]
+    if len(attn) < 3:
+        return {}
+    t = lambda r, k: int(r[k]) / 1e3  # noqa: E731  ns -> us
+    dur_a, dur_m, gap_am, gap_ma, period = [], [], [], [], []
+    for j, i in enumerate(attn):
+        a = seq[i]
+        dur_a.append(t(a, "End_Timestamp") - t(a, "Start_Timestamp"))
+        if i + 1 < len(seq) and "k_ring_merge" in seq[i + 1]["Kernel_Name"]:
+            m = seq[i + 1]
+            dur_m.append(t(m, "End_Timestamp") - t(m, "Start_Timestamp"))
+            gap_am.append(t(m, "Start_Timestamp") - t(a, "End_Timestamp"))
+            if j + 1 < len(attn):
+                gap_ma.append(t(seq[attn[j + 1]], "Start_Timestamp") - t(m, "End_Timestamp"))
+        if j + 1 < len(attn):
+            period.append(t(seq[attn[j + 1]], "Start_Timestamp") - t(a, "Start_Timestamp"))
+    med = lambda v: round(stt.median(v), 3) if v else None  # noqa: E731
+    return {"steps": len(attn), "period_us": med(period), "attn_us": med(dur_a),
+            "merge_us": med(dur_m), "gap_attn_to_merge_us": med(gap_am),
+            "gap_merge_to_next_us": med(gap_ma)}
+
+
 def summarize_profiles(out_dir: str) -> int:
     """Write profiles/*.md and the traffic JSON from the rocprofv3 CSV output
     of PROFILE_RUNS (and each run's stdout in OUT/<run>.log when present)."""
@@ -321,12 +383,22 @@ def summarize_profiles(out_dir: str) -> int:
                      f"{float(r['Percentage']):.1f}% |")
         if short:
             trace[short] = float(r["AverageNs"]) / 1e3
+    tl = trace_timeline(out_dir, "prof_ktrace", 1000)
+    if tl:
+        lines += ["", f"Timed steps in this trace (median over {tl['steps']} steps, per-dispatch "
+                  f"start and end timestamps): one step every {tl['period_us']} us = attention "
+                  f"{tl['attn_us']} us + gap {tl['gap_attn_to_merge_us']} us + merge "
+                  f"{tl['merge_us']} us + gap {tl['gap_merge_to_next_us']} us to the next "
+                  "attention.  The dispatches do not overlap: each kernel's duration runs from "
+                  "its first wave's start to its last wave's end, and the gaps are the "
+                  "dependent launch's turnaround."]
     if bl:
         ev = {k: v["avg_us"] for k, v in bl.get("kernels", {}).items()}
         lines += ["", "The same bench without the profiler (" + f"`{cmd('bench_plain')}`" + "), "
                   "HIP events bound to the dispatches of its profiled segment: "
                   + ", ".join(f"{k} {v:.2f} us" for k, v in ev.items() if v)
-                  + f"; {bl['value']:.0f} steps/s in its timed segment."]
+                  + f"; {bl['value']:.0f} steps/s in its timed segment "
+                  f"({1e3 * bl['ms_per_step']:.2f} us per step)."]
     with open(os.path.join(prof, "k_ring_attn_decode_stream_kernel_trace.md"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
 
@@ -351,6 +423,7 @@ def summarize_profiles(out_dir: str) -> int:
          "copy_calibration": {"bytes": copy_bytes, "fetch_kib": cf, "write_kib": cw,
                               "dispatches": [ncf, ncw]},
          "kernels": rows, "hbm_bytes_per_launch": rows["k_ring_attn"]["hbm_bytes"],
+         "trace_avg_us": trace.get("k_ring_attn"), "trace_timeline": tl,
          "commands": {k: PROFILE_RUNS[k] for k in ("pmc_fetch", "pmc_write", "pmc_copy_fetch",
                                                   "pmc_copy_write")}}
     with open(os.path.join(prof, "ring_attn_decode_stream_traffic.json"), "w") as fh:
@@ -395,8 +468,55 @@ def summarize_profiles(out_dir: str) -> int:
     for wl_name in WIDE_WORKLOADS:
         if os.path.isdir(os.path.join(out_dir, f"prof_ktrace_{wl_name}")):
             written.append(summarize_wide(out_dir, wl_name, khash, fetch_scale, write_scale))
+    if os.path.isdir(os.path.join(out_dir, "prof_ktrace_floor")):
+        written.append(summarize_floor(out_dir, khash))
     print(json.dumps({"written": written, "kernel_source_hash": khash}))
     return 0
+
+
+def summarize_floor(out_dir: str, khash: str) -> str:
+    """Kernel trace of the floor launches (ring_profile_floor) on the decode
+    stream, next to the bench's own floor figures."""
+    stats = _csv_rows(out_dir, "prof_ktrace_floor", "kernel_stats")
+    bl = None
+    path = os.path.join(out_dir, "bench_floor.log")
+    if os.path.exists(path):
+        with open(path) as fh:
+            for ln in fh:
+                if ln.strip().startswith("{") and '"floors"' in ln:
+                    bl = json.loads(ln)
+    names = {"0": "empty", "1": "read", "2": "partials (+ k_ring_merge: two_launch)",
+             "3": "last_arriver", "4": "barrier"}
+    lines = ["# Floors of the attention launch: decode_stream (cap 4096, q_len 8, GQA 32/8 x 128, "
+             "F16, 1 layer, 32-ring pool)", "", f"Kernel source hash: `{khash}`", "",
+             "Command (cd /tmp; TMPDIR=/tmp):", "", f"    {PROFILE_RUNS['prof_ktrace_floor']}", "",
+             "Each floor kernel runs on the attention's grid (256 work-groups of 4 waves: 8 KV "
+             "heads x 32 splits), work-group order and tiles, with a trivial consumer; "
+             "include/ring_kv.h (ring_profile_floor) describes the kinds.", "",
+             "| kernel | kind | calls | avg us | min us | max us |", "|---|---|---:|---:|---:|---:|"]
+    for r in stats:
+        name = r["Name"]
+        kind = next((v for k, v in names.items() if f"k_ring_floor<{k}>" in name), "")
+        if not kind and "k_ring_merge" not in name:
+            continue
+        lines.append(f"| `{name}` | {kind or 'merge of the two_launch kind'} | {r['Calls']} | "
+                     f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                     f"{float(r['MaxNs']) / 1e3:.2f} |")
+    if bl:
+        fl = bl["floors"]
+        lines += ["", f"The same floors without the profiler (`{PROFILE_RUNS['bench_floor']}`), "
+                  f"{fl['launches']} launches each cycled over the pool; per launch, back to back "
+                  "(wall clock between two synchronisations) and one dispatch bound to HIP events:", "",
+                  "| kind | back to back us | event us |", "|---|---:|---:|"]
+        for k, v in fl.items():
+            if isinstance(v, dict) and "b2b_us" in v:
+                ev = f"{v['event_us']:.2f}" if v.get("event_us") else "-"
+                lines.append(f"| {k} | {v['b2b_us']:.2f} | {ev} |")
+        lines.append(f"\nBarrier waits that hit their poll limit: {fl.get('barrier_timeouts')}.")
+    p_ = "profiles/k_ring_floor_decode_stream_kernel_trace.md"
+    with open(os.path.join(ROOT, p_), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    return p_
 
 
 def summarize_mirror(out_dir: str, khash: str, fetch_scale: float, write_scale: float):
@@ -515,6 +635,99 @@ def summarize_wide(out_dir: str, wl_name: str, khash: str, fetch_scale: float,
     return path
 
 
+FLOOR_KINDS = (("empty", 0), ("read", 1), ("partials", 2), ("two_launch", 5),
+               ("last_arriver", 3), ("barrier", 4))
+
+
+def clock_warmup(dev, seconds: float, flush_mib: int) -> int:
+    """Keep the GPU busy reading a scratch buffer of `flush_mib` MiB for about
+    `seconds` (clocks up).  The buffer is written once and then only read, so
+    the Infinity Cache ends up holding its clean lines and nothing of the
+    rings, and no write-back of dirty lines is left for the timed steps to
+    wait behind.  Returns the number of full reads."""
+    import torch
+    buf = torch.zeros(flush_mib << 20, dtype=torch.uint8, device=dev).view(torch.int64)
+    n, t0 = 0, time.perf_counter()
+    while True:
+        for _ in range(16):
+            torch.amax(buf)
+            n += 1
+        torch.cuda.synchronize(dev)
+        if time.perf_counter() - t0 >= seconds:
+            break
+    del buf
+    return n
+
+
+def floor_segment(rings, pool, launches, dev, R, attn_us, step_us, bytes_read):
+    """The ring_profile_floor kinds on layer 0, cycled over the pool (cold).
+    Per launch: the device's back-to-back time (HIP events around a batch
+    queued behind a RING_FLOOR_HOLD launch, so that the host's submission
+    rate does not bound it), and the event-bound duration of one dispatch."""
+    import torch
+    s = torch.cuda.current_stream(dev).cuda_stream
+    fl = R.ring_profile_floor
+    out = {"launches": launches, "layer": 0, "kv_bytes_read_per_launch": int(bytes_read)}
+    for name, kind in FLOOR_KINDS:
+        try:
+            for t in range(min(pool, launches)):        # one launch per ring first
+                fl(rings[t % pool].handle, 0, kind, s)
+            torch.cuda.synchronize(dev)
+        except R.RingError as e:
+            out[name] = {"skipped": str(e)}
+            continue
+        fl(rings[0].handle, 0, R.RING_FLOOR_HOLD, s)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        th = time.perf_counter()
+        for t in range(launches):
+            fl(rings[t % pool].handle, 0, kind, s)
+        e1.record()
+        host_us = (time.perf_counter() - th) / launches * 1e6
+        queued = not e0.query()     # the hold still ran when the batch was in
+        torch.cuda.synchronize(dev)
+        b2b = e0.elapsed_time(e1) * 1e3 / launches
+        per_ring = -(-launches // pool) * 2
+        for r in rings:
+            r.profile_enable(per_ring)
+        for t in range(launches):
+            fl(rings[t % pool].handle, 0, kind, s)
+        torch.cuda.synchronize(dev)
+        n_l, ms = 0, 0.0
+        for r in rings:
+            a_, b_ = r.profile_read(R.RING_KERNEL_FLOOR)
+            n_l += a_
+            ms += b_
+        for r in rings:
+            r.profile_enable(0)
+        # the two-launch kind times its two dispatches apiece
+        ev = 1e3 * ms / launches if n_l else None
+        out[name] = {"b2b_us": b2b, "event_us": ev, "host_submit_us": host_us,
+                     "queued_behind_hold": bool(queued)}
+    out["barrier_timeouts"] = int(sum(R.ring_profile_floor_timeouts(r.handle) for r in rings))
+    ceil = {}
+    rd = out.get("read", {}).get("event_us")
+    if rd and attn_us:
+        ceil["attn_kernel"] = rd / attn_us
+    tl = out.get("two_launch", {}).get("b2b_us")
+    if tl and step_us:
+        ceil["step"] = tl / step_us
+    return out, ceil
+
+
+def committed_trace_us(kernel_hash: str):
+    """Average duration of the attention kernel in the committed kernel-trace
+    summary of the decode stream, if it was taken on this kernel source."""
+    path = os.path.join(ROOT, "profiles", "ring_attn_decode_stream_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_hash:
+        return None
+    return t.get("trace_avg_us")
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -536,6 +749,15 @@ def main() -> int:
                     help="eager step of a ring with several sequences: auto takes one "
                          "ring_begin_step_batch call for all of them (default), per_seq one "
                          "ring_begin_step call per sequence")
+    ap.add_argument("--warm-seconds", type=float, default=0.25,
+                    help="GPU clock warm-up before the timed steps (scratch writes that also "
+                         "evict the Infinity Cache)")
+    ap.add_argument("--flush-mib", type=int, default=512,
+                    help="size of that scratch buffer (above the 256 MB Infinity Cache)")
+    ap.add_argument("--floor-launches", type=int, default=400,
+                    help="launches per ring_profile_floor kind (0: no floor segment)")
+    ap.add_argument("--floor", action="store_true",
+                    help="only the floor segment (after the same warm-up), one JSON line")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--summarize", metavar="OUT", default="",
@@ -580,9 +802,11 @@ def main() -> int:
     pool = args.pool or max(1, -(-(512 << 20) // ring_bytes))
     # warm-up, the timed steps, then as many steps again with per-kernel
     # timing events (they slow back-to-back launches, so they stay out of the
-    # timed region)
+    # timed region); ring 0 alone then takes up to min(steps, 1000) more
+    # steps for the cache-warm figure
     total = args.warmup + 2 * args.steps
-    rings, calls, steps_in, committed = prepare(w, pool, total, dev)
+    warm_steps = min(args.steps, 1000) if pool > 1 and not args.floor else 0
+    rings, calls, steps_in, committed, calls0 = prepare(w, pool, total, dev, warm_steps)
     s = torch.cuda.current_stream(dev).cuda_stream
     out = torch.empty((w.n_seq, w.q_len, w.n_head, w.head_dim), dtype=torch.float32, device=dev)
     mirror = w.d_model > 0
@@ -593,28 +817,44 @@ def main() -> int:
     attn, optr = R.ring_attn, out.data_ptr()
     mwrite, mbegin = R.ring_mirror_write, R.ring_begin_step_mirror
     begin_batch = R.ring_begin_step_batch
-    # the batched call's argument lists, per call
-    columns = [[list(col) for col in zip(*c[1])] for c in calls] if batched else None
+    if batched:
+        # the batched call's argument lists, built once per call
+        calls = [(h, [list(col) for col in zip(*seqs)], layers, wp) for h, seqs, layers, wp in calls]
+        calls0 = [(h, [list(col) for col in zip(*seqs)], layers, wp) for h, seqs, layers, wp in calls0]
 
-    def run(lo, hi):
-        for t in range(lo, hi):
-            h, seqs, layers, wptr = calls[t]
+    def run(seq_calls):
+        for h, seqs, layers, wptr in seq_calls:
             if mirror:
                 for seq, c, fp, c0, n in seqs:
                     mwrite(h, seq, c0, n, fp, s)
                     mbegin(h, seq, c, *wptr, s)
             elif batched:
-                begin_batch(h, *columns[t], s)
+                begin_batch(h, *seqs, s)
             else:
                 for seq, c, kp, vp, n in seqs:
                     begin(h, seq, c, kp, vp, n, s)
             for layer, qp, knp, vnp in layers:
                 attn(h, layer, qp, knp, vnp, optr, s)
 
-    run(0, args.warmup)
+    run(calls[:args.warmup])
     torch.cuda.synchronize(dev)
+    # clocks up and the Infinity Cache evicted, then the timed steps: each
+    # cycles to the ring touched longest ago (pool x ring bytes >= 512 MB)
+    n_fills = clock_warmup(dev, args.warm_seconds, args.flush_mib)
+
+    if args.floor:
+        fl, ceil = floor_segment(rings, pool, args.floor_launches, dev, R, None, None,
+                                 np.mean([sum(algorithmic_bytes(w, min(c, w.cap), geo.kv_total)["kv"]
+                                              for c in cs) for cs in committed]))
+        print(json.dumps({"workload": args.workload, "ring": rings[0].describe(), "floors": fl,
+                          "ring_pool": pool}), flush=True)
+        for r in rings:
+            r.close()
+        return 0
+
     t0 = time.perf_counter()
-    run(args.warmup, args.warmup + args.steps)
+    run(calls[args.warmup:args.warmup + args.steps])
+    enqueued = time.perf_counter() - t0
     torch.cuda.synchronize(dev)
     elapsed = time.perf_counter() - t0
 
@@ -623,7 +863,7 @@ def main() -> int:
         r.profile_enable(per_ring)
     torch.cuda.synchronize(dev)
     t1 = time.perf_counter()
-    run(args.warmup + args.steps, total)
+    run(calls[args.warmup + args.steps: total])
     torch.cuda.synchronize(dev)
     elapsed_prof = time.perf_counter() - t1
 
@@ -636,10 +876,25 @@ def main() -> int:
             n_l += a
             ms += b
         prof[name] = {"launches": n_l, "avg_us": (1e3 * ms / n_l) if n_l else None}
+    for r in rings:
+        r.profile_enable(0)
+
+    # cache-warm figure: ring 0 alone (its ring stays in the Infinity Cache),
+    # continuing its stream after the profiled segment
+    mall_warm = None
+    if calls0:
+        n0 = min(len(calls0) // 4, 20)
+        run(calls0[:n0])
+        torch.cuda.synchronize(dev)
+        tw = time.perf_counter()
+        run(calls0[n0:])
+        torch.cuda.synchronize(dev)
+        tw = time.perf_counter() - tw
+        nw = len(calls0) - n0
+        mall_warm = {"value": nw / tw, "steps": nw, "ms_per_step": 1e3 * tw / nw,
+                     "what": "ring 0 of the pool alone, so that its ring stays in the Infinity Cache"}
 
     split_desc = rings[0].describe()
-    for r in rings:
-        r.close()
 
     # algorithmic bytes of one attention launch, averaged over the profiled
     # segment (every sequence's visible window at its step)
@@ -659,6 +914,7 @@ def main() -> int:
         # the library appended the deferred steps at once (a ring whose
         # attention waves stream several tiles each): an eager step
         fused, step_mode = False, "eager"
+    fused_extra = 0.0
     if fused and not mirror:
         # the fused launch also reads each new row (K and V, F16) and writes it
         # to the ring, reads slot_pos instead of the mask, and (first layer of
@@ -666,21 +922,29 @@ def main() -> int:
         seg_rows = [sum(n for _, _, _, _, n in steps_in[0][t // pool][0])
                     for t in range(args.warmup + args.steps, total)]
         rows = float(np.mean(seg_rows))
-        per_launch += (rows * w.kv_row * 2 * 2 * 2 + w.n_seq * w.cap * 4
+        fused_extra = (rows * w.kv_row * 2 * 2 * 2 + w.n_seq * w.cap * 4
                        - w.n_seq * w.q_len * geo.kv_total * 2
                        + (w.n_seq * (w.q_len * geo.kv_total * 2 + w.q_len * 64 * 2 * 12)
                           + rows * 4) / w.n_layer)
-    per_call = mean_bytes("ring_attn")
+        per_launch += fused_extra
+    per_call = mean_bytes("ring_attn") + fused_extra
     attn_us = prof["k_ring_attn"]["avg_us"]
     merge_us = prof["k_ring_merge"]["avg_us"] or 0.0
     achieved = per_launch / (attn_us * 1e-6) / 1e9
     khash = kernel_source_hash()
-    traffic = traffic_from_profiles(khash) if args.workload == WORKLOAD else None
+    headline = args.workload == WORKLOAD
+    traffic = traffic_from_profiles(khash) if headline else None
+    trace_us = committed_trace_us(khash) if headline and fused else None
+    ms_per_step = 1e3 * elapsed / args.steps
     roof_attn = {"kernel": "k_ring_attn_fused" if fused else "k_ring_attn", "bound": "hbm",
                  "achieved": achieved,
                  "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                  "traffic": traffic, "bytes_per_launch": int(per_launch),
-                 "avg_launch_us": attn_us}
+                 "avg_launch_us": attn_us,
+                 "timing": "HIP events bound to each dispatch of a segment like the timed one",
+                 "trace_avg_us": trace_us,
+                 "frac_trace": (per_launch / (trace_us * 1e-6) / 1e9 / HBM_PEAK_GBS)
+                 if trace_us else None}
     roofline = roof_attn
     if mirror:
         # the projection launch of a decode step reads every layer's wk and wv
@@ -695,15 +959,27 @@ def main() -> int:
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": pa / HBM_PEAK_GBS,
                     "traffic": None, "bytes_per_launch": int(proj_bytes),
                     "avg_launch_us": proj_us}
+    # the whole step as the timed loop saw it: every attention launch's
+    # algorithmic bytes (all layers) per step time
+    step_bytes = per_call * w.n_layer
+    floors, ceiling = None, None
+    if args.floor_launches and not mirror:
+        floors, ceiling = floor_segment(
+            rings, pool, args.floor_launches, dev, R, attn_us, ms_per_step * 1e3,
+            np.mean([sum(algorithmic_bytes(w, layer_window(c, 0), geo.kv_total)["kv"] for c in cs)
+                     for cs in seg]))
+    for r in rings:
+        r.close()
     line = {
-        "metric": METRIC if args.workload == WORKLOAD else
+        "metric": METRIC if headline else
         f"ring step steps/s + achieved HBM GB/s, workload {args.workload}",
         "value": args.steps / elapsed,
         "unit": "steps/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": 1e3 * elapsed / args.steps,
+        "ms_per_step": ms_per_step,
+        "host_submit_ms_per_step": 1e3 * enqueued / args.steps,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -714,19 +990,31 @@ def main() -> int:
                    "cap": w.cap, "q_len": w.q_len,
                    "n_head": w.n_head, "n_head_kv": w.n_head_kv, "head_dim": w.head_dim,
                    "n_layer": w.n_layer, "n_seq": w.n_seq, "kv_total": geo.kv_total,
-                   "ring_pool": pool, "infinity_cache": "cold" if pool > 1 or ring_bytes > (256 << 20) else "warm",
+                   "ring_pool": pool,
+                   "infinity_cache": "cold" if pool * ring_bytes > (256 << 20) else "warm",
+                   "before_timing": f"{n_fills} writes of a {args.flush_mib} MiB scratch buffer "
+                                    f"over >= {args.warm_seconds} s (clocks up, Infinity Cache "
+                                    f"evicted); each timed step takes the ring touched longest ago",
                    "ring": split_desc},
         "roofline": roofline,
-        "ring_attn": {"kernels": "k_ring_attn + k_ring_merge",
+        "ring_attn": {"kernels": "k_ring_attn_fused + k_ring_merge" if fused else
+                      "k_ring_attn + k_ring_merge",
                       "avg_us": attn_us + merge_us,
                       "calls_per_s": 1e6 / (attn_us + merge_us),
-                      "achieved_GBps": per_call / ((attn_us + merge_us) * 1e-6) / 1e9},
+                      "achieved_GBps": per_call / ((attn_us + merge_us) * 1e-6) / 1e9,
+                      "frac": per_call / ((attn_us + merge_us) * 1e-6) / 1e9 / HBM_PEAK_GBS},
+        "step": {"bytes": int(step_bytes),
+                 "achieved_GBps": step_bytes / (ms_per_step * 1e-3) / 1e9,
+                 "frac": step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "mall_warm": mall_warm,
         "kernels": prof,
         **({"roofline_attn": roof_attn} if mirror else {}),
+        "floors": floors,
+        "ceiling_frac": ceiling,
         "profiled_segment_steps_per_s": args.steps / elapsed_prof,
         "kernel_source_hash": khash,
     }
-    if not args.no_cpu_baseline and args.workload == WORKLOAD:
+    if not args.no_cpu_baseline and headline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(line), flush=True)
     return 0

@@ -12,8 +12,11 @@ from .ring import (Ring, RingConfig, RingError, RingGeometry, RingKvWeights, Rin
                    ring_describe, ring_free, ring_init, ring_last_error, ring_mirror_write,
                    ring_plan_from_state, ring_plan_step, ring_query_geometry, ring_read_mask,
                    ring_read_mask_swa, ring_read_rows, ring_read_slot_pos, ring_read_state,
-                   ring_profile_enable, ring_profile_read, RING_KERNEL_STEP, RING_KERNEL_ATTN,
-                   RING_KERNEL_MERGE, RING_KERNEL_PROJ)
+                   ring_profile_enable, ring_profile_read, ring_profile_floor,
+                   ring_profile_floor_timeouts, RING_KERNEL_STEP, RING_KERNEL_ATTN,
+                   RING_KERNEL_MERGE, RING_KERNEL_PROJ, RING_KERNEL_FLOOR, RING_FLOOR_EMPTY,
+                   RING_FLOOR_READ, RING_FLOOR_PARTIALS, RING_FLOOR_LAST_ARRIVER,
+                   RING_FLOOR_BARRIER, RING_FLOOR_TWO_LAUNCH, RING_FLOOR_HOLD)
 
 __all__ = ["Ring", "RingConfig", "RingError", "RingGeometry", "RingKvWeights", "RingPlan",
            "make_config", "ring_attn", "ring_begin_step", "ring_begin_step_batch",
@@ -22,5 +25,8 @@ __all__ = ["Ring", "RingConfig", "RingError", "RingGeometry", "RingKvWeights", "
            "ring_describe", "ring_free", "ring_init", "ring_last_error", "ring_mirror_write",
            "ring_plan_from_state", "ring_plan_step", "ring_query_geometry", "ring_read_mask",
            "ring_read_mask_swa", "ring_read_rows", "ring_read_slot_pos", "ring_read_state",
-           "ring_profile_enable", "ring_profile_read", "RING_KERNEL_STEP", "RING_KERNEL_ATTN",
-           "RING_KERNEL_MERGE", "RING_KERNEL_PROJ"]
+           "ring_profile_enable", "ring_profile_read", "ring_profile_floor",
+           "ring_profile_floor_timeouts", "RING_KERNEL_STEP", "RING_KERNEL_ATTN",
+           "RING_KERNEL_MERGE", "RING_KERNEL_PROJ", "RING_KERNEL_FLOOR", "RING_FLOOR_EMPTY",
+           "RING_FLOOR_READ", "RING_FLOOR_PARTIALS", "RING_FLOOR_LAST_ARRIVER",
+           "RING_FLOOR_BARRIER", "RING_FLOOR_TWO_LAUNCH", "RING_FLOOR_HOLD"]

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libringkv.so")
-SOURCES = ["ring_runtime.cpp", "ring_kernels.hip"]
+SOURCES = ["ring_runtime.cpp", "ring_kernels.hip", "ring_floor.hip"]
 ARCH = "gfx950"
 
 

@@ -1,0 +1,237 @@
+// ring_floor.hip -- profiling-only kernels that measure what bounds the
+// attention launch of a ring (ring_profile_floor in include/ring_kv.h).
+//
+// Each one runs on the attention's own grid: one work-group of four waves per
+// (sequence, KV head, split, row block), the same XCD-pinned work-group order
+// and the same tiles per wave (tile t0 + wave, t0 + wave + 4, ...) of the
+// ring's visible window, but with a trivial consumer instead of the softmax:
+//   kind 0  empty kernel (launch and drain only)
+//   kind 1  every visible K and V tile loaded once (16-byte loads per lane,
+//           the attention's fragment order) and folded by xor
+//   kind 2  kind 1, then the work-group's 16 KiB fp32 split partial and its
+//           (max, sum) pairs stored where the attention stores them
+//   kind 3  kind 2 with an in-kernel cross-split merge by the last arriver:
+//           partials stored with device-scope coherence (sc1, write-through),
+//           the stores waited for, one atomic ticket per work-group on a
+//           counter per (sequence, head, row block); the work-group that
+//           draws the last ticket loads every split's partial (sc1) and
+//           writes their sum
+//   kind 4  kind 2 with a bounded barrier instead: every work-group of a
+//           (sequence, head, row block) waits for all its splits' tickets
+//           (at most 2^20 polls with s_sleep, then an error count), then
+//           sums its 1/n_split slice of every split's partial
+//   kind 5  (host side) kind 2, then the ring's own merge launch over those
+//           partials
+//   kind 6  one wave that sleeps for several milliseconds (a bounded loop of
+//           s_sleep): the host queues a batch of launches behind it, so that
+//           their back-to-back time on the device is not bounded by how fast
+//           the host submits them
+// The merges sum partials without the softmax weights: these kernels time
+// data movement and synchronisation, not the attention's arithmetic.
+#include "ring_kernels.h"
+
+namespace ringkv {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Cache-policy bits of the buffer instructions on gfx950: sc1 = device scope
+// (stores write through to memory, loads are coherent across the XCDs' L2s).
+constexpr int kPolicySc1 = 16;
+// Word 3 of a raw buffer descriptor on gfx9 parts (32-bit data format).
+constexpr int kBufferWord3 = 0x00020000;
+
+__device__ inline __amdgpu_buffer_rsrc_t floor_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, kBufferWord3);
+}
+
+template <int KIND>
+__global__ __launch_bounds__(256) void k_ring_floor(FloorArgs a) {
+  if constexpr (KIND == 0) {
+    return;
+  } else {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n_units = a.n_seq * a.n_head_kv;
+    const int per_unit = a.n_split * a.n_rb;
+    int unit, r;
+    if ((n_units & 7) == 0) {
+      const int xcd = blockIdx.x & 7, k = blockIdx.x >> 3;
+      const int q = quot32(k, a.rcp_per_unit);
+      unit = (q << 3) + xcd;
+      r = k - q * per_unit;
+    } else {
+      unit = quot32(blockIdx.x, a.rcp_per_unit);
+      r = blockIdx.x - unit * per_unit;
+    }
+    const int split = quot32(r, a.rcp_n_rb);
+    const int rb = r - split * a.n_rb;
+    const int seq = quot32(unit, a.rcp_n_head_kv);
+    const int g = unit - seq * a.n_head_kv;
+    const int nvt = a.vis_count[seq];
+    const int first = a.vis_first[seq];
+    const int per = quot32(nvt + a.n_split - 1, a.rcp_n_split);
+    const int t0 = min(nvt, split * per);
+    const int t1 = min(nvt, t0 + per);
+    const uint16_t* kh = a.kring + seq * a.seq_stride + a.layer_offset + g * a.head_stride;
+    const uint16_t* vh = a.vring + seq * a.seq_stride + a.layer_offset + g * a.head_stride;
+    u32x4 x = {0u, 0u, 0u, 0u};
+    for (int t = t0 + wave; t < t1; t += 4) {
+      int rt = first + t;
+      if (rt >= a.ring_tiles) rt -= a.ring_tiles;
+      const u32x4* kt = (const u32x4*)(kh + (int64_t)rt * kTileHalves);
+      const u32x4* vt = (const u32x4*)(vh + (int64_t)rt * kTileHalves);
+      u32x4 kc[8], vc[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) kc[c] = kt[c * 64 + lane];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) vc[c] = vt[c * 64 + lane];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) x ^= kc[c] ^ vc[c];
+    }
+    if constexpr (KIND == 1) {
+      // one word per wave keeps every load live
+      uint32_t w = x.x ^ x.y ^ x.z ^ x.w;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) w ^= __shfl_xor(w, off);
+      if (lane == 0) a.out[blockIdx.x * 4 + wave] = (float)(w & 0xFFFFu);
+      return;
+    } else {
+      // the split partial: 32 rows x 128 dims fp32 where the attention puts
+      // the partial of (unit, split, row block), and its (max, sum) pairs
+      const f32x4 v = {(float)(x.x & 0xFFu), (float)(x.y & 0xFFu), (float)(x.z & 0xFFu), 1.0f};
+      const int64_t prow = ((int64_t)(unit * a.n_split + split) * a.n_rb + rb) * 32;
+      const uint32_t pbytes = (uint32_t)a.part_bytes;
+      const __amdgpu_buffer_rsrc_t pr = floor_rsrc(a.part_acc, pbytes);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t off = (uint32_t)((prow * kHeadDim + (i * 256 + threadIdx.x) * 4) * 4);
+        if constexpr (KIND == 2)
+          *(f32x4*)(a.part_acc + prow * kHeadDim + (i * 256 + threadIdx.x) * 4) = v + (float)i;
+        else
+          __builtin_amdgcn_raw_buffer_store_b128(v + (float)i, pr, off, 0, kPolicySc1);
+      }
+      if (threadIdx.x < 32) *(float2*)(a.part_ml + (prow + threadIdx.x) * 2) = make_float2(v.x, 1.0f);
+      if constexpr (KIND == 2) return;
+      // every partial store of the work-group has completed (device scope)
+      // before its ticket is drawn
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      __shared__ uint32_t ticket;
+      uint32_t* cnt = a.counter + unit * a.n_rb + rb;
+      if (threadIdx.x == 0)
+        ticket = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      const int64_t base_row = ((int64_t)unit * a.n_split * a.n_rb + rb) * 32;  // split 0
+      const int64_t split_f4 = (int64_t)a.n_rb * 32 * kHeadDim / 4;            // between splits
+      float* outp = a.out + ((int64_t)unit * a.n_rb + rb) * 32 * kHeadDim;
+      if constexpr (KIND == 3) {
+        if (ticket + 1 != (uint32_t)a.n_split) return;
+        if (threadIdx.x == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        f32x4 o[4] = {};
+        for (int t = 0; t < a.n_split; ++t) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t off =
+                (uint32_t)(((base_row * kHeadDim / 4) + t * split_f4 + i * 256 + threadIdx.x) * 16);
+            o[i] += __builtin_amdgcn_raw_buffer_load_b128(pr, off, 0, kPolicySc1);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *(f32x4*)(outp + (i * 256 + threadIdx.x) * 4) = o[i];
+      } else {
+        // KIND 4: every split's ticket is in (tickets count up from
+        // epoch * n_split; the counter is never reset), bounded wait
+        if (threadIdx.x == 0) {
+          const uint32_t target = (a.epoch + 1u) * (uint32_t)a.n_split;
+          int n = 0;
+          while ((int32_t)(__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) -
+                           target) < 0) {
+            __builtin_amdgcn_s_sleep(1);
+            if (++n > (1 << 20)) {
+              __hip_atomic_fetch_add(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              break;
+            }
+          }
+        }
+        __syncthreads();
+        // slice `split` of the 1024 float4 of a partial
+        const int sf = (1024 + a.n_split - 1) / a.n_split;
+        __shared__ f32x4 red[256];
+        if (sf >= 256) {
+          for (int i = threadIdx.x; i < sf; i += 256) {
+            const int idx = split * sf + i;
+            if (idx >= 1024) break;
+            f32x4 o = {};
+            for (int t = 0; t < a.n_split; ++t)
+              o += __builtin_amdgcn_raw_buffer_load_b128(
+                  pr, (uint32_t)(((base_row * kHeadDim / 4) + t * split_f4 + idx) * 16), 0,
+                  kPolicySc1);
+            *(f32x4*)(outp + idx * 4) = o;
+          }
+        } else {
+          const int groups = 256 / sf;
+          const int grp = threadIdx.x / sf, e = threadIdx.x - grp * sf;
+          const int idx = min(split * sf + e, 1023);
+          f32x4 o = {};
+          if (grp < groups)
+            for (int t = grp; t < a.n_split; t += groups)
+              o += __builtin_amdgcn_raw_buffer_load_b128(
+                  pr, (uint32_t)(((base_row * kHeadDim / 4) + t * split_f4 + idx) * 16), 0,
+                  kPolicySc1);
+          red[threadIdx.x] = o;
+          __syncthreads();
+          if (grp == 0 && split * sf + e < 1024) {
+            f32x4 s = red[e];
+            for (int j = 1; j < groups; ++j) s += red[j * sf + e];
+            *(f32x4*)(outp + idx * 4) = s;
+          }
+        }
+      }
+    }
+  }
+}
+
+// 4096 sleeps of 64 x 127 clocks each: about 14 ms at 2.4 GHz
+__global__ __launch_bounds__(64) void k_ring_floor_hold() {
+  for (int i = 0; i < 4096; ++i) __builtin_amdgcn_s_sleep(127);
+}
+
+hipError_t launch_floor(const FloorArgs& args, int kind, hipStream_t s, hipEvent_t t0,
+                        hipEvent_t t1) {
+  if (kind == 6) {
+    hipExtLaunchKernelGGL(k_ring_floor_hold, dim3(1), dim3(64), 0, s, t0, t1, 0);
+    return hipGetLastError();
+  }
+  FloorArgs a = args;
+  const uint64_t per_unit = (uint64_t)a.n_split * a.n_rb;
+  const uint64_t grid = (uint64_t)a.n_seq * a.n_head_kv * per_unit;
+  if (a.n_split < 1 || a.n_rb < 1 || grid * per_unit > (uint64_t(1) << 32) ||
+      (uint64_t)(a.ring_tiles + a.n_split) * a.n_split > (uint64_t(1) << 32))
+    return hipErrorInvalidValue;
+  a.rcp_per_unit = recip32((uint32_t)per_unit);
+  a.rcp_n_rb = recip32(a.n_rb);
+  a.rcp_n_head_kv = recip32(a.n_head_kv);
+  a.rcp_n_split = recip32(a.n_split);
+  const dim3 g((unsigned)grid), b(256);
+  switch (kind) {
+    case 0: hipExtLaunchKernelGGL(k_ring_floor<0>, g, b, 0, s, t0, t1, 0, a); break;
+    case 1: hipExtLaunchKernelGGL(k_ring_floor<1>, g, b, 0, s, t0, t1, 0, a); break;
+    case 2: hipExtLaunchKernelGGL(k_ring_floor<2>, g, b, 0, s, t0, t1, 0, a); break;
+    case 3: hipExtLaunchKernelGGL(k_ring_floor<3>, g, b, 0, s, t0, t1, 0, a); break;
+    case 4: hipExtLaunchKernelGGL(k_ring_floor<4>, g, b, 0, s, t0, t1, 0, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+int floor_resident_blocks() {
+  int dev = 0, per_cu = 0;
+  hipDeviceProp_t prop;
+  if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_ring_floor<4>, 256, 0) != hipSuccess)
+    return 0;
+  return per_cu * prop.multiProcessorCount;
+}
+
+}  // namespace ringkv

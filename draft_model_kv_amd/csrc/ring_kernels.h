@@ -182,6 +182,26 @@ struct MergeArgs {
   uint64_t rcp_per_unit, rcp_n_head_kv, rcp_group;
 };
 
+// Profiling-only floor launches (ring_floor.hip): the attention's grid and
+// tile order with a trivial consumer, optionally its partial stores and an
+// in-kernel cross-split merge.  Kinds as in ring_floor.hip.
+struct FloorArgs {
+  const uint16_t* kring;
+  const uint16_t* vring;
+  int64_t seq_stride, layer_offset, head_stride;
+  float* part_acc;           // the ring's split partials, [unit][split][n_rb * 32][128]
+  float* part_ml;            // [unit][split][n_rb * 32][2]
+  int64_t part_bytes;        // bytes of part_acc (below 2^31 for kinds 3 and 4)
+  float* out;                // profiling buffer, [unit * n_rb][32 * 128] fp32
+  uint32_t* counter;         // [unit * n_rb] tickets
+  uint32_t* err;             // bounded-wait timeouts
+  uint32_t epoch;            // kind 4: launches of that kind since the counters were zeroed
+  int32_t n_seq, n_head_kv, n_split, n_rb, ring_tiles;
+  uint64_t rcp_per_unit, rcp_n_rb, rcp_n_head_kv, rcp_n_split;
+  int32_t vis_first[RING_MAX_SEQ_INTERNAL];
+  int32_t vis_count[RING_MAX_SEQ_INTERNAL];
+};
+
 // t0 / t1: optional events bound to the dispatch (start and end of the
 // kernel itself), or nullptr.
 hipError_t launch_step(const StepArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
@@ -192,5 +212,8 @@ hipError_t launch_attn_fused(const FusedAttnArgs& f, hipStream_t s, hipEvent_t t
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
 hipError_t launch_project(const ProjArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
 hipError_t launch_fill_u16(uint16_t* p, uint16_t value, int64_t n, hipStream_t s);
+hipError_t launch_floor(const FloorArgs& a, int kind, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
+// Work-groups of the floor kernel that fit the device at once (0 on error).
+int floor_resident_blocks();
 
 }  // namespace ringkv

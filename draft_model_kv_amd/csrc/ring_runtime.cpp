@@ -222,8 +222,13 @@ struct ring {
   hipStream_t last_stream = nullptr;
   // profiling: per kernel kind, event pairs (start, end) and how many are used
   int32_t prof_max = 0;
-  std::vector<hipEvent_t> prof_ev[4];
-  int32_t prof_used[4] = {0, 0, 0, 0};
+  std::vector<hipEvent_t> prof_ev[5];
+  int32_t prof_used[5] = {0, 0, 0, 0, 0};
+  // profiling-only floor launches (ring_profile_floor): counters, timeout
+  // count and output of the in-kernel merge variants, allocated on first use
+  uint8_t* floor_buf = nullptr;
+  int32_t floor_last_kind = -1;
+  uint32_t floor_epoch = 0;
 };
 
 namespace {
@@ -739,28 +744,17 @@ int ring_begin_step_mirror(ring_t* r, int32_t seq, int64_t committed, const ring
   return ok();
 }
 
-int ring_attn(ring_t* r, int32_t layer, const void* q, const void* k_noise, const void* v_noise,
-              float* out, void* stream) {
-  if (!r) return fail(RING_EINVAL, "ring is NULL");
-  if (layer < 0 || layer >= r->cfg.n_layer) return fail(RING_ERANGE, "layer %d out of range", layer);
-  if (!q || !k_noise || !v_noise || !out) return fail(RING_EINVAL, "NULL tensor pointer");
-  const uintptr_t al = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_noise) |
-                       reinterpret_cast<uintptr_t>(v_noise) | reinterpret_cast<uintptr_t>(out);
-  if (al & 15) return fail(RING_EINVAL, "q, k_noise, v_noise and out must be 16-byte aligned");
-  if (int e = use_device(r)) return e;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  r->last_stream = s;
-
+namespace {
+// The attention launch of `layer` over every sequence of the ring, without
+// its tensors: ring geometry, each sequence's visible tiles (from its state
+// of the last begin_step) and the split count.  Returns n_split.
+int32_t attn_geometry(const ring* r, int32_t layer, AttnArgs* out, bool* swa_out) {
   AttnArgs a{};
   a.kring = r->kring;
   a.vring = r->vring;
   a.mask = r->mask;
   a.rope_noise = r->rope_noise;
   a.rope_q = r->rope_q;
-  a.q = static_cast<const uint16_t*>(q);
-  a.k_noise = static_cast<const uint16_t*>(k_noise);
-  a.v_noise = static_cast<const uint16_t*>(v_noise);
-  a.out = out;
   a.part_acc = r->part_acc;
   a.part_ml = r->part_ml;
   a.seq_stride = r->L.seq_stride;
@@ -782,7 +776,6 @@ int ring_attn(ring_t* r, int32_t layer, const void* q, const void* k_noise, cons
   a.ring_tiles = ring_tiles;
   const bool swa = layer < 64 && ((r->cfg.swa_layers >> layer) & 1u);
   if (swa) a.mask = r->mask_swa;
-  const uint64_t bit = layer < 64 ? (1ull << layer) : 0;
   int32_t max_count = 0;
   for (int i = 0; i < r->cfg.n_seq; ++i) {
     // Visible positions [committed - w, committed) sit in slots from
@@ -813,6 +806,33 @@ int ring_attn(ring_t* r, int32_t layer, const void* q, const void* k_noise, cons
                               ? r->L.n_split
                               : std::max(1, std::min(r->L.n_split, (max_count + 3) / 4));
   a.n_split = n_split;
+  *out = a;
+  if (swa_out) *swa_out = swa;
+  return n_split;
+}
+}  // namespace
+
+int ring_attn(ring_t* r, int32_t layer, const void* q, const void* k_noise, const void* v_noise,
+              float* out, void* stream) {
+  if (!r) return fail(RING_EINVAL, "ring is NULL");
+  if (layer < 0 || layer >= r->cfg.n_layer) return fail(RING_ERANGE, "layer %d out of range", layer);
+  if (!q || !k_noise || !v_noise || !out) return fail(RING_EINVAL, "NULL tensor pointer");
+  const uintptr_t al = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_noise) |
+                       reinterpret_cast<uintptr_t>(v_noise) | reinterpret_cast<uintptr_t>(out);
+  if (al & 15) return fail(RING_EINVAL, "q, k_noise, v_noise and out must be 16-byte aligned");
+  if (int e = use_device(r)) return e;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  r->last_stream = s;
+
+  AttnArgs a;
+  bool swa = false;
+  const int32_t n_split = attn_geometry(r, layer, &a, &swa);
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_noise = static_cast<const uint16_t*>(k_noise);
+  a.v_noise = static_cast<const uint16_t*>(v_noise);
+  a.out = out;
+  const int64_t cap = r->cfg.cap;
+  const uint64_t bit = layer < 64 ? (1ull << layer) : 0;
   hipEvent_t t0, t1;
   next_events(r, RING_KERNEL_ATTN, &t0, &t1);
   // Deferred steps owing this layer's rows or the index state: one fused
@@ -889,6 +909,124 @@ int ring_attn(ring_t* r, int32_t layer, const void* q, const void* k_noise, cons
   return ok();
 }
 
+namespace {
+// Bytes of the floor buffer: counters, the timeout count, then the output.
+size_t floor_counter_bytes(const ring* r) {
+  return (size_t)align_up((int64_t)r->cfg.n_seq * r->cfg.n_head_kv * r->L.n_rb * 4, 256);
+}
+size_t floor_out_bytes(const ring* r) {
+  return (size_t)r->cfg.n_seq * r->cfg.n_head_kv * r->L.n_rb * 32 * kHeadDim * 4;
+}
+}  // namespace
+
+int ring_profile_floor(ring_t* r, int32_t layer, int32_t kind, void* stream) {
+  if (!r) return fail(RING_EINVAL, "ring is NULL");
+  if (layer < 0 || layer >= r->cfg.n_layer) return fail(RING_ERANGE, "layer %d out of range", layer);
+  if (kind < RING_FLOOR_EMPTY || kind > RING_FLOOR_HOLD)
+    return fail(RING_EINVAL, "floor kind %d out of range", kind);
+  if (kind == RING_FLOOR_HOLD) {
+    if (int e = use_device(r)) return e;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    r->last_stream = s;
+    FloorArgs none{};
+    return check_launch(launch_floor(none, kind, s, nullptr, nullptr), "floor hold launch")
+               ? RING_EDEVICE : ok();
+  }
+  if (r->L.n_rb * 32 != r->L.mpad)
+    return fail(RING_EINVAL, "floor launches need one work-group per 32-query block");
+  AttnArgs a;
+  const int32_t n_split = attn_geometry(r, layer, &a, nullptr);
+  const size_t part_bytes =
+      (size_t)r->cfg.n_seq * r->cfg.n_head_kv * r->L.n_split * r->L.mpad * kHeadDim * 4;
+  if (kind >= RING_FLOOR_PARTIALS && n_split < 2)
+    return fail(RING_EINVAL, "this launch has one split: there are no partials to store");
+  const bool ticketed = kind == RING_FLOOR_LAST_ARRIVER || kind == RING_FLOOR_BARRIER;
+  if (ticketed && part_bytes >= (size_t(1) << 31))
+    return fail(RING_EINVAL, "partials of %zu bytes exceed a buffer descriptor's range", part_bytes);
+  const int64_t grid = (int64_t)r->cfg.n_seq * r->cfg.n_head_kv * n_split * r->L.n_rb;
+  if (kind == RING_FLOOR_BARRIER && grid > floor_resident_blocks())
+    return fail(RING_EINVAL, "%lld work-groups do not fit the device at once: no barrier",
+                (long long)grid);
+  if (int e = use_device(r)) return e;
+  if (int e = flush_all(r)) return e;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  r->last_stream = s;
+  const size_t cb = floor_counter_bytes(r);
+  if (!r->floor_buf) {
+    void* p = nullptr;
+    if (hipMalloc(&p, cb + 256 + floor_out_bytes(r)) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(RING_ENOMEM, "floor buffer allocation failed");
+    }
+    r->floor_buf = static_cast<uint8_t*>(p);
+    r->floor_last_kind = -1;
+  }
+  if (ticketed && kind != r->floor_last_kind) {
+    // tickets count from zero for a series of one kind
+    if (hipMemsetAsync(r->floor_buf, 0, cb + 256, s) != hipSuccess)
+      return fail(RING_EDEVICE, "floor counter reset failed");
+    r->floor_epoch = 0;
+  }
+  FloorArgs f{};
+  f.kring = a.kring;
+  f.vring = a.vring;
+  f.seq_stride = a.seq_stride;
+  f.layer_offset = a.layer_offset;
+  f.head_stride = a.head_stride;
+  f.part_acc = r->part_acc;
+  f.part_ml = r->part_ml;
+  f.part_bytes = (int64_t)part_bytes;
+  f.counter = reinterpret_cast<uint32_t*>(r->floor_buf);
+  f.err = reinterpret_cast<uint32_t*>(r->floor_buf + cb);
+  f.out = reinterpret_cast<float*>(r->floor_buf + cb + 256);
+  f.epoch = r->floor_epoch;
+  f.n_seq = a.n_seq;
+  f.n_head_kv = a.n_head_kv;
+  f.n_split = n_split;
+  f.n_rb = r->L.n_rb;
+  f.ring_tiles = a.ring_tiles;
+  for (int i = 0; i < RING_MAX_SEQ_INTERNAL; ++i) {
+    f.vis_first[i] = a.vis_first[i];
+    f.vis_count[i] = a.vis_count[i];
+  }
+  hipEvent_t t0, t1;
+  next_events(r, RING_KERNEL_FLOOR, &t0, &t1);
+  const int fk = kind == RING_FLOOR_TWO_LAUNCH ? RING_FLOOR_PARTIALS : kind;
+  if (int e = check_launch(launch_floor(f, fk, s, t0, t1), "floor launch")) return e;
+  if (kind == RING_FLOOR_TWO_LAUNCH) {
+    // the ring's own merge launch over those partials, into the floor buffer
+    MergeArgs m{};
+    m.part_acc = r->part_acc;
+    m.part_ml = r->part_ml;
+    m.out = f.out;
+    m.n_units = r->cfg.n_seq * r->cfg.n_head_kv;
+    m.n_split = n_split;
+    m.n_head = r->cfg.n_head;
+    m.n_head_kv = r->cfg.n_head_kv;
+    m.group = r->L.group;
+    m.q_len = r->cfg.q_len;
+    m.m = r->L.m;
+    m.mpad = r->L.mpad;
+    next_events(r, RING_KERNEL_FLOOR, &t0, &t1);
+    if (int e = check_launch(launch_merge(m, s, t0, t1), "floor merge launch")) return e;
+  }
+  r->floor_last_kind = kind;
+  if (kind == RING_FLOOR_BARRIER) ++r->floor_epoch;
+  return ok();
+}
+
+int ring_profile_floor_timeouts(ring_t* r, uint32_t* timeouts) {
+  if (!r || !timeouts) return fail(RING_EINVAL, "NULL argument");
+  *timeouts = 0;
+  if (!r->floor_buf) return ok();
+  if (int e = use_device(r)) return e;
+  if (hipStreamSynchronize(r->last_stream) != hipSuccess ||
+      hipMemcpy(timeouts, r->floor_buf + floor_counter_bytes(r), 4, hipMemcpyDeviceToHost) !=
+          hipSuccess)
+    return fail(RING_EDEVICE, "reading the floor timeout count failed");
+  return ok();
+}
+
 int ring_free(ring_t* r) {
   if (!r) return ok();
   int code = RING_OK;
@@ -896,6 +1034,8 @@ int ring_free(ring_t* r) {
     if (hipStreamSynchronize(r->last_stream) != hipSuccess)
       code = fail(RING_EDEVICE, "stream synchronisation failed in ring_free");
     if (r->owns_ws && hipFree(r->ws) != hipSuccess)
+      code = fail(RING_EDEVICE, "hipFree failed");
+    if (r->floor_buf && hipFree(r->floor_buf) != hipSuccess)
       code = fail(RING_EDEVICE, "hipFree failed");
     destroy_events(r);
   } else {
@@ -1031,7 +1171,7 @@ int ring_profile_enable(ring_t* r, int32_t max_launches) {
 }
 
 int ring_profile_read(ring_t* r, int32_t kernel, int32_t* n_launches, double* total_ms) {
-  if (!r || !n_launches || !total_ms || kernel < 0 || kernel > 3)
+  if (!r || !n_launches || !total_ms || kernel < 0 || kernel > RING_KERNEL_FLOOR)
     return fail(RING_EINVAL, "bad argument");
   if (int e = use_device(r)) return e;
   double total = 0.0;

@@ -34,9 +34,14 @@ EXPORTS = (
     "ring_last_error", "ring_describe",
     "ring_read_slot_pos", "ring_read_mask", "ring_read_mask_swa", "ring_read_rows",
     "ring_read_state",
-    "ring_profile_enable", "ring_profile_read",
+    "ring_profile_enable", "ring_profile_read", "ring_profile_floor",
+    "ring_profile_floor_timeouts",
 )
 RING_KERNEL_STEP, RING_KERNEL_ATTN, RING_KERNEL_MERGE, RING_KERNEL_PROJ = 0, 1, 2, 3
+RING_KERNEL_FLOOR = 4
+# kinds of ring_profile_floor
+(RING_FLOOR_EMPTY, RING_FLOOR_READ, RING_FLOOR_PARTIALS, RING_FLOOR_LAST_ARRIVER,
+ RING_FLOOR_BARRIER, RING_FLOOR_TWO_LAUNCH, RING_FLOOR_HOLD) = 0, 1, 2, 3, 4, 5, 6
 
 
 class RingConfig(ctypes.Structure):
@@ -110,6 +115,8 @@ def _load() -> ctypes.CDLL:
         "ring_read_state": [P, I32, ctypes.POINTER(I64), ctypes.POINTER(I64)],
         "ring_profile_enable": [P, I32],
         "ring_profile_read": [P, I32, ctypes.POINTER(I32), ctypes.POINTER(ctypes.c_double)],
+        "ring_profile_floor": [P, I32, I32, P],
+        "ring_profile_floor_timeouts": [P, ctypes.POINTER(ctypes.c_uint32)],
     }
     for name in EXPORTS:
         fn = getattr(lib, name)
@@ -273,6 +280,16 @@ def ring_profile_read(handle: int, kernel: int) -> Tuple[int, float]:
     return n.value, ms.value
 
 
+def ring_profile_floor(handle: int, layer: int, kind: int, stream: int = 0) -> None:
+    _check(_lib.ring_profile_floor(handle, layer, kind, stream or None), "ring_profile_floor")
+
+
+def ring_profile_floor_timeouts(handle: int) -> int:
+    n = ctypes.c_uint32()
+    _check(_lib.ring_profile_floor_timeouts(handle, ctypes.byref(n)), "ring_profile_floor_timeouts")
+    return n.value
+
+
 class Ring:
     """One ring on the current GPU, its workspace a torch uint8 tensor.
 
@@ -392,6 +409,10 @@ class Ring:
 
     def profile_enable(self, max_launches: int) -> None:
         ring_profile_enable(self.handle, max_launches)
+
+    def floor(self, layer: int, kind: int) -> None:
+        """One profiling-only floor launch of `layer` (RING_FLOOR_*)."""
+        ring_profile_floor(self.handle, layer, kind, self._stream())
 
     def profile_read(self, kernel: int) -> Tuple[int, float]:
         return ring_profile_read(self.handle, kernel)

@@ -313,11 +313,12 @@ int ring_read_state(const ring_t* r, int32_t seq, int64_t* next_pos,
  * and ring_begin_step_mirror), RING_KERNEL_ATTN (attention launch of
  * ring_attn), RING_KERNEL_MERGE (cross-split merge launch of ring_attn,
  * absent when one split suffices), RING_KERNEL_PROJ (projection launches of
- * ring_begin_step_mirror).                                                  */
+ * ring_begin_step_mirror), RING_KERNEL_FLOOR (ring_profile_floor).          */
 #define RING_KERNEL_STEP  0
 #define RING_KERNEL_ATTN  1
 #define RING_KERNEL_MERGE 2
 #define RING_KERNEL_PROJ  3
+#define RING_KERNEL_FLOOR 4
 
 /* Time the next `max_launches` launches of each kernel kind with HIP events
  * bound to the dispatch itself (kernel start to kernel end, no launch gaps).
@@ -328,6 +329,59 @@ int ring_profile_enable(ring_t* r, int32_t max_launches);
  * were and their summed duration in milliseconds, and start counting anew.
  * Errors: RING_EINVAL, RING_EDEVICE.                                        */
 int ring_profile_read(ring_t* r, int32_t kernel, int32_t* n_launches, double* total_ms);
+
+/* ---- Floors of the attention launch (profiling only) ----
+ * What bounds one ring_attn launch of `layer` on this hardware, measured with
+ * the attention's own launch shape: the same grid (one work-group of four
+ * waves per sequence, KV head, split and 32-query block), the same
+ * work-group order (a KV head's splits on one XCD) and the same ring tiles
+ * per wave from each sequence's window at its last begin_step, with a
+ * trivial consumer in place of the attention's arithmetic:
+ *   RING_FLOOR_EMPTY         a kernel that returns at once (launch + drain)
+ *   RING_FLOOR_READ          every visible K and V tile loaded once with the
+ *                            attention's 16-byte loads, folded by xor
+ *   RING_FLOOR_PARTIALS      RING_FLOOR_READ plus the 16 KiB fp32 split
+ *                            partial (and its max/sum pairs) each work-group
+ *                            of the attention stores
+ *   RING_FLOOR_TWO_LAUNCH    RING_FLOOR_PARTIALS, then the ring's own merge
+ *                            launch over those partials: the data movement
+ *                            of ring_attn's two launches (timed as two
+ *                            RING_KERNEL_FLOOR launches)
+ *   RING_FLOOR_HOLD          one wave that sleeps for about 14 ms (a bounded
+ *                            loop) and reads nothing: launches queued behind
+ *                            it then run back to back on the device, however
+ *                            slowly the host submits them (not timed)
+ *   RING_FLOOR_LAST_ARRIVER  RING_FLOOR_PARTIALS with the cross-split merge
+ *                            in the same launch: partials stored write-through
+ *                            at device scope, one atomic ticket per
+ *                            work-group, and the work-group with the last
+ *                            ticket of its (sequence, head) sums every
+ *                            split's partial
+ *   RING_FLOOR_BARRIER       RING_FLOOR_PARTIALS with a bounded barrier per
+ *                            (sequence, head): every work-group waits for all
+ *                            tickets of its head (at most 2^20 polls, then it
+ *                            counts a timeout and goes on), then sums its
+ *                            share of every split's partial
+ * These launches read the ring but change none of its state or outputs (the
+ * split partials are scratch; the sums go to a buffer of their own, which
+ * the first floor launch allocates and ring_free releases).  Deferred steps
+ * are appended first.  They run on `stream`; ring_profile_enable /
+ * ring_profile_read time them as RING_KERNEL_FLOOR.
+ * Errors: RING_ERANGE (layer), RING_EINVAL (kind; a launch with one split
+ * for the kinds with partials; RING_FLOOR_BARRIER when the grid does not fit the
+ * device at once), RING_ENOMEM, RING_EDEVICE.                               */
+#define RING_FLOOR_EMPTY        0
+#define RING_FLOOR_READ         1
+#define RING_FLOOR_PARTIALS     2
+#define RING_FLOOR_LAST_ARRIVER 3
+#define RING_FLOOR_BARRIER      4
+#define RING_FLOOR_TWO_LAUNCH    5
+#define RING_FLOOR_HOLD          6
+int ring_profile_floor(ring_t* r, int32_t layer, int32_t kind, void* stream);
+
+/* Number of RING_FLOOR_BARRIER waits that ended by their poll limit rather
+ * than by the last ticket (synchronous; 0 when no floor launch ran).        */
+int ring_profile_floor_timeouts(ring_t* r, uint32_t* timeouts);
 
 #ifdef __cplusplus
 }

@@ -31,8 +31,14 @@ def f16_ulp_diff(a: np.ndarray, b: np.ndarray) -> np.ndarray:
     return np.abs(ia - ib)
 
 
-def check_close(got: np.ndarray, ref: np.ndarray, what: str = "") -> Dict[str, float]:
-    """|got - ref| <= ATOL + RTOL |ref| element by element; returns error stats."""
+def check_close(got: np.ndarray, ref: np.ndarray, what: str = "",
+                abs_bar: bool = True) -> Dict[str, float]:
+    """|got - ref| <= ATOL + RTOL |ref| element by element; with ``abs_bar``
+    (every workload whose values are N(0, 0.5)) also |got - ref| <= ATOL for
+    every element: the stated max-abs bound on its own.  Workloads with +-30
+    outliers keep the combined bound only: there outputs reach tens, where
+    one F16 step of the inputs is already 2^-6.  Returns error stats, with
+    ``abs_ratio`` = max_abs / ATOL and ``max_ratio`` = max of err / bound."""
     assert got.shape == ref.shape, (got.shape, ref.shape)
     assert np.isfinite(got).all(), f"{what}: non-finite output"
     err = np.abs(got.astype(np.float64) - ref.astype(np.float64))
@@ -41,11 +47,16 @@ def check_close(got: np.ndarray, ref: np.ndarray, what: str = "") -> Dict[str, f
     stats = {"max_abs": float(err.max()) if err.size else 0.0,
              "max_rel": float((err / np.maximum(np.abs(ref), 1e-30)).max()) if err.size else 0.0,
              "max_ratio": float((err / tol).max()) if err.size else 0.0}
+    stats["abs_ratio"] = stats["max_abs"] / ATOL
     if bad.any():
         idx = np.argwhere(bad)[0]
         raise AssertionError(
             f"{what}: {int(bad.sum())} of {bad.size} elements out of tolerance; first at "
             f"{tuple(idx)} got {got[tuple(idx)]} ref {ref[tuple(idx)]}; stats {stats}")
+    if abs_bar and stats["max_abs"] > ATOL:
+        idx = np.unravel_index(int(np.argmax(err)), err.shape)
+        raise AssertionError(f"{what}: max abs error {stats['max_abs']:.3g} > {ATOL} at {idx} "
+                             f"(got {got[idx]} ref {ref[idx]}); stats {stats}")
     return stats
 
 
@@ -139,6 +150,8 @@ class Driver:
         self.epochs = [Epochs() for _ in range(w.n_seq)]
         self.committed = [0] * w.n_seq
         self.n_attn = 0
+        # the max-abs bound on its own for N(0, 0.5) values (not for +-30 outliers)
+        self.abs_bar = w.outlier_p == 0.0
         # rows from fused features: the mirror on both sides, and the weights
         self.mirror = w.d_model > 0
         if self.mirror:
@@ -371,11 +384,12 @@ class Driver:
         """Attention of every layer first (so that a deferred step is carried
         out by the attention launches themselves), then every comparison."""
         res = [(layer,) + self.attn(layer, step) for layer in range(self.w.n_layer)]
-        worst = {"max_abs": 0.0, "max_rel": 0.0, "max_ratio": 0.0}
+        worst = {"max_abs": 0.0, "max_rel": 0.0, "max_ratio": 0.0, "abs_ratio": 0.0}
         for layer, out, q, kn, vn in res:
             for seq in (range(self.w.n_seq) if seqs is None else seqs):
                 ref = self.oracle_attn(seq, layer, q, kn, vn)
-                st = check_close(out[seq], ref, f"attn seq {seq} layer {layer} step {step}")
+                st = check_close(out[seq], ref, f"attn seq {seq} layer {layer} step {step}",
+                                 abs_bar=self.abs_bar)
                 self.check_noise_rows(seq, layer, kn, vn)
                 for k_ in worst:
                     worst[k_] = max(worst[k_], st[k_])
@@ -383,10 +397,11 @@ class Driver:
 
     def check_attn(self, layer: int, step: int, seqs=None, noise_rows: bool = True) -> Dict[str, float]:
         out, q, kn, vn = self.attn(layer, step)
-        worst = {"max_abs": 0.0, "max_rel": 0.0, "max_ratio": 0.0}
+        worst = {"max_abs": 0.0, "max_rel": 0.0, "max_ratio": 0.0, "abs_ratio": 0.0}
         for seq in (range(self.w.n_seq) if seqs is None else seqs):
             ref = self.oracle_attn(seq, layer, q, kn, vn)
-            st = check_close(out[seq], ref, f"attn seq {seq} layer {layer} step {step}")
+            st = check_close(out[seq], ref, f"attn seq {seq} layer {layer} step {step}",
+                             abs_bar=self.abs_bar)
             if noise_rows:
                 self.check_noise_rows(seq, layer, kn, vn)
             for k_ in worst:
@@ -395,3 +410,71 @@ class Driver:
 
     def close(self):
         self.ring.close()
+
+
+# ---------------------------------------------------------------------------
+# Whole workloads at full size: every step runs on the device, checkpoints are
+# compared element by element.
+# ---------------------------------------------------------------------------
+def checkpoints(n: int, every: int, extra=()) -> set:
+    """Steps 0, 1, every `every`-th, the last one and `extra` (of range(n))."""
+    pts = set(range(0, n, every)) | {0, 1, n - 1} | set(extra)
+    return {p for p in pts if 0 <= p < n}
+
+
+def run_workload(name: str, every: int, rows_at=(0,), deferred: bool = False,
+                 max_steps: Optional[int] = None, say=print) -> float:
+    """The named workload through its warm-up and decode steps.
+
+    Checkpoints: every `every`-th step, the first two, the last, and each step
+    where a sequence's committed count crosses cap.  At a checkpoint, every
+    layer's attention output (and layer 0's noise rows) against the oracle,
+    and the index state bit-exact; ring rows of layer 0 at the steps in
+    `rows_at` (and of every layer at the last step).  deferred: every decode
+    step through ring_begin_step_deferred, so each layer's attention launch
+    appends that layer's rows (a checkpoint then runs all layers before any
+    comparison, and a step between checkpoints runs them without one).
+    Returns the worst err / bound ratio seen."""
+    w = W.WORKLOADS[name]
+    d = Driver(w)
+    streams = [W.commit_stream(w, s) for s in range(w.n_seq)]
+    n_warm = W.n_warmup_steps(w)
+    say(name, "warm-up", n_warm, "steps", "deferred" if deferred else "eager")
+    for t in range(n_warm):
+        for seq in range(w.n_seq):
+            d.step(seq, streams[seq][t])
+    for seq in range(w.n_seq):
+        d.check_index(seq)
+        for layer in range(w.n_layer):
+            d.check_rows(seq, layer)
+    n = len(streams[0]) - n_warm if max_steps is None else min(max_steps, len(streams[0]) - n_warm)
+    crossings = [t for t in range(n) for seq in range(w.n_seq)
+                 if streams[seq][n_warm + t - 1] < w.cap <= streams[seq][n_warm + t]]
+    pts = checkpoints(n, every, crossings)
+    worst = {"max_ratio": 0.0, "abs_ratio": 0.0}
+    for t in range(n):
+        for seq in range(w.n_seq):
+            d.step(seq, streams[seq][n_warm + t], deferred=deferred)
+        if t in pts:
+            if deferred:
+                st = d.check_attn_layers(t)
+            else:
+                st = {"max_ratio": 0.0, "abs_ratio": 0.0}
+                for layer in range(w.n_layer):
+                    s_ = d.check_attn(layer, t, noise_rows=(layer == 0))
+                    st = {k: max(st[k], s_[k]) for k in st}
+            worst = {k: max(worst[k], st[k]) for k in worst}
+            for seq in range(w.n_seq):
+                d.check_index(seq)
+        else:
+            for layer in range(w.n_layer):
+                d.attn(layer, t)
+        if t in rows_at or t == n - 1:
+            for seq in range(min(w.n_seq, 2)):
+                for layer in (range(w.n_layer) if t == n - 1 else (0,)):
+                    d.check_rows(seq, layer)
+    say(name, "steps", n, "checked", len(pts), "worst err/bound", round(worst["max_ratio"], 4),
+        "worst abs err/2e-3", round(worst["abs_ratio"], 4))
+    d.close()
+    return worst["max_ratio"]
+

@@ -162,3 +162,50 @@ def test_mirror_needs_at_most_16_kv_heads():
     with pytest.raises(rk.RingError) as e:
         rk.ring_query_geometry(rk.make_config(64, n_head=32, n_head_kv=32, d_model=256))
     assert e.value.code == rk.RING_EINVAL
+
+
+def _absurd_config():
+    """Every size at its limit: 64 sequences x 1024 layers of 2^26-slot rings."""
+    return rk.make_config(1 << 26, 8, 32, 8, 128, n_layer=1024, n_seq=64)
+
+
+def test_absurd_cap_geometry_is_exact():
+    """The geometry of the largest accepted ring is computed without overflow:
+    2 (K, V) x kv_row x kv_total x 2 B per (sequence, layer)."""
+    g = rk.ring_query_geometry(_absurd_config())
+    kv_total = ((1 << 26) + 8 + 1 + 31) // 32 * 32
+    assert g.kv_total == kv_total
+    assert g.kv_bytes_per_layer == 2 * 1024 * kv_total * 2
+    assert g.workspace_bytes >= 64 * 1024 * g.kv_bytes_per_layer > 2 ** 53
+
+
+def _rss_bytes() -> int:
+    with open("/proc/self/statm") as f:
+        return int(f.read().split()[1]) * os.sysconf("SC_PAGE_SIZE")
+
+
+def test_absurd_cap_small_workspace_is_enomem_and_leaks_nothing():
+    """A caller workspace smaller than the geometry's workspace_bytes is
+    refused with RING_ENOMEM before any device call (so this runs without a
+    GPU), and the host state of a refused ring_init is released: 5000
+    refusals leave the resident set within 4 MiB."""
+    cfg = _absurd_config()
+    fake = 1 << 20   # 256-byte aligned address, never dereferenced
+    with pytest.raises(rk.RingError) as e:
+        rk.ring_init(cfg, workspace=fake, workspace_bytes=1 << 30)
+    assert e.value.code == rk.RING_ENOMEM
+    assert "workspace" in rk.ring_last_error()
+    for _ in range(200):   # let allocator pools reach their steady size first
+        with pytest.raises(rk.RingError):
+            rk.ring_init(cfg, workspace=fake, workspace_bytes=1 << 30)
+    before = _rss_bytes()
+    for _ in range(5000):
+        with pytest.raises(rk.RingError):
+            rk.ring_init(cfg, workspace=fake, workspace_bytes=1 << 30)
+    assert _rss_bytes() - before < 4 << 20
+
+
+def test_misaligned_workspace_is_einval():
+    with pytest.raises(rk.RingError) as e:
+        rk.ring_init(rk.make_config(64), workspace=(1 << 20) + 16, workspace_bytes=1 << 30)
+    assert e.value.code == rk.RING_EINVAL

@@ -15,7 +15,7 @@ import numpy as np
 import pytest
 
 import workload as W
-from tests.harness import Driver
+from tests.harness import Driver, run_workload
 
 pytestmark = pytest.mark.gpu
 
@@ -162,39 +162,25 @@ def test_fused_flush_paths():
     d.close()
 
 
+# ---------------------------------------------------------------------------
+# Whole workloads through the fused step (the bench's default step), at full
+# size: checkpoints every 50 / 32 / 40 steps, at every cap crossing and at
+# the last step, each with every layer's output, the index state bit-exact
+# and ring rows.
+# ---------------------------------------------------------------------------
 def test_fused_decode_stream_full():
-    """The headline workload through the fused step: 4096-token prompt, then
-    60 decode steps, every one checked."""
-    w = W.WORKLOADS["decode_stream"]
-    d = Driver(w)
-    stream = W.commit_stream(w, 0)[: 1 + 60]
-    say("decode_stream fused", len(stream), "steps")
-    for t, c in enumerate(stream):
-        d.step(0, c, deferred=True)
-        d.check_attn_layers(t)
-        d.check_index(0)
-        if t in (0, 1, 30, len(stream) - 1):
-            d.check_rows(0, 0)
-    d.close()
+    """The headline workload: 4096-token bulk prompt, then all 2000 fold-in
+    steps deferred into the attention launch."""
+    run_workload("decode_stream", every=50, rows_at=(0, 1, 1000), deferred=True, say=say)
 
 
-def test_fused_long_prompt_wrap_layers():
-    """5 layers of the long-prompt workload, 24 decode steps (every 4th
-    commits 8), fused."""
-    w = W.WORKLOADS["long_prompt_wrap"]
-    d = Driver(w)
-    stream = W.commit_stream(w, 0)
-    n_warm = W.n_warmup_steps(w)
-    for c in stream[:n_warm]:
-        d.step(0, c)
-    for t, c in enumerate(stream[n_warm:n_warm + 24]):
-        d.step(0, c, deferred=True)
-        if t % 3 == 0 or t == 23:
-            d.check_attn_layers(t)
-            d.check_index(0)
-        else:
-            for layer in range(w.n_layer):
-                d.attn(layer, t)
-    for layer in range(w.n_layer):
-        d.check_rows(0, layer)
-    d.close()
+def test_fused_long_prompt_wrap_full():
+    """5 layers, 32768-token prompt (28672 rows overwritten), all 512 decode
+    steps (every 4th commits 8) fused."""
+    run_workload("long_prompt_wrap", every=32, rows_at=(0, 255), deferred=True, say=say)
+
+
+def test_fused_swa_stream_full():
+    """4 layers, layers 1 and 3 sliding over 1024 positions (their window
+    wraps the ring end as the stream advances), all 600 steps fused."""
+    run_workload("swa_stream", every=40, rows_at=(0, 300), deferred=True, say=say)

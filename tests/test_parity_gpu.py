@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 import workload as W
-from tests.harness import Driver, check_close
+from tests.harness import Driver, check_close, run_workload
 
 pytestmark = pytest.mark.gpu
 
@@ -277,46 +277,8 @@ def test_error_paths_leave_state_unchanged():
 # ---------------------------------------------------------------------------
 # Full workload sizes, sampled checkpoints (every step runs on the device).
 # ---------------------------------------------------------------------------
-def _checkpoints(n, every, extra=()):
-    pts = set(range(0, n, every)) | {0, 1, n - 1} | set(extra)
-    return {p for p in pts if 0 <= p < n}
-
-
 def _run_workload(name, every, rows_at=(0,), max_steps=None):
-    w = W.WORKLOADS[name]
-    d = Driver(w)
-    streams = [W.commit_stream(w, s) for s in range(w.n_seq)]
-    n_warm = W.n_warmup_steps(w)
-    say(name, "warm-up", n_warm, "steps")
-    for t in range(n_warm):
-        for seq in range(w.n_seq):
-            d.step(seq, streams[seq][t])
-    for seq in range(w.n_seq):
-        d.check_index(seq)
-        for layer in range(w.n_layer):
-            d.check_rows(seq, layer)
-    n = len(streams[0]) - n_warm if max_steps is None else min(max_steps, len(streams[0]) - n_warm)
-    crossings = [t for t in range(n) for seq in range(w.n_seq)
-                 if streams[seq][n_warm + t - 1] < w.cap <= streams[seq][n_warm + t]]
-    pts = _checkpoints(n, every, crossings)
-    worst = 0.0
-    for t in range(n):
-        for seq in range(w.n_seq):
-            d.step(seq, streams[seq][n_warm + t])
-        for layer in range(w.n_layer):
-            if t in pts:
-                st = d.check_attn(layer, t, noise_rows=(layer == 0))
-                worst = max(worst, st["max_ratio"])
-            else:
-                d.attn(layer, t)
-        if t in pts:
-            for seq in range(w.n_seq):
-                d.check_index(seq)
-        if t in rows_at:
-            for seq in range(min(w.n_seq, 2)):
-                d.check_rows(seq, 0)
-    say(name, "steps", n, "checked", len(pts), "worst err/tol", round(worst, 4))
-    d.close()
+    run_workload(name, every, rows_at=rows_at, max_steps=max_steps, say=say)
 
 
 def test_decode_stream_full():
@@ -337,3 +299,22 @@ def test_large_window_full():
 
 def test_swa_stream_full():
     _run_workload("swa_stream", every=40, rows_at=(599,))
+
+
+def test_absurd_cap_library_workspace_is_enomem_and_leaks_nothing():
+    """ring_init with no caller workspace and a geometry far beyond the GPU's
+    memory (2^54 bytes): the library's hipMalloc fails, the call returns
+    RING_ENOMEM, and the device's free memory is what it was before."""
+    import torch
+    from draft_model_kv_amd import RingError, make_config, ring_init
+    from draft_model_kv_amd.ring import RING_ENOMEM
+    torch.cuda.synchronize()
+    free0, _ = torch.cuda.mem_get_info()
+    cfg = make_config(1 << 26, 8, 32, 8, 128, n_layer=1024, n_seq=64)
+    for _ in range(3):
+        with pytest.raises(RingError) as e:
+            ring_init(cfg)
+        assert e.value.code == RING_ENOMEM
+    torch.cuda.synchronize()
+    free1, _ = torch.cuda.mem_get_info()
+    assert abs(free1 - free0) < (64 << 20), (free0, free1)
