@@ -7,7 +7,7 @@ include/ring_kv.h; ``draft_model_kv_amd.ring`` is its Python binding.
 """
 
 from .ring import (Ring, RingConfig, RingError, RingGeometry, RingKvWeights, RingPlan,
-                   make_config, ring_attn, ring_begin_step, ring_begin_step_batch,
+                   make_config, ring_attn, ring_attn_noalloc, ring_begin_step, ring_begin_step_batch,
                    ring_begin_step_deferred, ring_begin_step_mirror,
                    ring_describe, ring_free, ring_init, ring_last_error, ring_mirror_write,
                    ring_plan_from_state, ring_plan_step, ring_query_geometry, ring_read_mask,
@@ -19,7 +19,7 @@ from .ring import (Ring, RingConfig, RingError, RingGeometry, RingKvWeights, Rin
                    RING_FLOOR_BARRIER, RING_FLOOR_TWO_LAUNCH, RING_FLOOR_HOLD)
 
 __all__ = ["Ring", "RingConfig", "RingError", "RingGeometry", "RingKvWeights", "RingPlan",
-           "make_config", "ring_attn", "ring_begin_step", "ring_begin_step_batch",
+           "make_config", "ring_attn", "ring_attn_noalloc", "ring_begin_step", "ring_begin_step_batch",
            "ring_begin_step_deferred",
            "ring_begin_step_mirror",
            "ring_describe", "ring_free", "ring_init", "ring_last_error", "ring_mirror_write",

@@ -212,6 +212,14 @@ hipError_t launch_attn_fused(const FusedAttnArgs& f, hipStream_t s, hipEvent_t t
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
 hipError_t launch_project(const ProjArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
 hipError_t launch_fill_u16(uint16_t* p, uint16_t value, int64_t n, hipStream_t s);
+
+// The static split-partial array of ring_attn_noalloc (ring_kernels.hip):
+// its size, the call that resolves its address on `device` (which must be
+// current; once per device, thread-safe), and that address (nullptr until
+// resolved).
+constexpr size_t kStaticScratchBytes = size_t(16) << 20;
+hipError_t resolve_static_scratch(int device);
+void* static_scratch(int device);
 hipError_t launch_floor(const FloorArgs& a, int kind, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
 // Work-groups of the floor kernel that fit the device at once (0 on error).
 int floor_resident_blocks();

@@ -17,6 +17,8 @@
 
 #include <math.h>
 
+#include <mutex>
+
 namespace ringkv {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
@@ -1620,6 +1622,38 @@ hipError_t launch_fill_u16(uint16_t* p, uint16_t value, int64_t n, hipStream_t s
   const int64_t grid = (n + 255) / 256;
   hipLaunchKernelGGL(k_fill_u16, dim3((unsigned)grid), dim3(256), 0, s, p, value, n);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Split partials of ring_attn_noalloc: one array per device, in the code
+// object's static data, shared by every call on that device (it keeps the
+// last call's contents; nothing in it needs to start at zero, since each call
+// writes every partial it reads).  Host code takes its device address from
+// hipGetSymbolAddress, resolved once per device at ring_init; the array's
+// name itself is a host-side stand-in and is never passed to a kernel.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t resolve_static_scratch(int device) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  if (g_scratch_ptr[device]) return hipSuccess;
+  void* ptr = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  g_scratch_ptr[device] = ptr;
+  return hipSuccess;
+}
+
+void* static_scratch(int device) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  return device >= 0 && device < kMaxDevices ? g_scratch_ptr[device] : nullptr;
 }
 
 }  // namespace ringkv

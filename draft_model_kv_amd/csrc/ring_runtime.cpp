@@ -356,6 +356,11 @@ int ring_init(const ring_config* cfg, void* workspace, size_t workspace_bytes, v
     delete r;
     return fail(RING_EDEVICE, "no HIP device");
   }
+  // device address of ring_attn_noalloc's static partials on this device
+  if (hipError_t e = resolve_static_scratch(r->device); e != hipSuccess) {
+    delete r;
+    return fail(RING_EDEVICE, "static scratch of device %d: %s", r->device, hipGetErrorString(e));
+  }
   if (workspace) {
     r->ws = static_cast<uint8_t*>(workspace);
   } else {
@@ -812,14 +817,32 @@ int32_t attn_geometry(const ring* r, int32_t layer, AttnArgs* out, bool* swa_out
 }
 }  // namespace
 
-int ring_attn(ring_t* r, int32_t layer, const void* q, const void* k_noise, const void* v_noise,
-              float* out, void* stream) {
+namespace {
+// Checks of a ring_attn call (before any device work).
+int check_attn(const ring* r, int32_t layer, const void* q, const void* k_noise,
+               const void* v_noise, const float* out) {
   if (!r) return fail(RING_EINVAL, "ring is NULL");
   if (layer < 0 || layer >= r->cfg.n_layer) return fail(RING_ERANGE, "layer %d out of range", layer);
   if (!q || !k_noise || !v_noise || !out) return fail(RING_EINVAL, "NULL tensor pointer");
   const uintptr_t al = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_noise) |
                        reinterpret_cast<uintptr_t>(v_noise) | reinterpret_cast<uintptr_t>(out);
   if (al & 15) return fail(RING_EINVAL, "q, k_noise, v_noise and out must be 16-byte aligned");
+  return RING_OK;
+}
+
+// Bytes of the split partials (accumulators, then (max, sum) pairs 256-byte
+// aligned) of a launch with n_split splits.
+size_t partial_bytes(const ring* r, int32_t n_split, size_t* ml_offset) {
+  const size_t rows = (size_t)r->cfg.n_seq * r->cfg.n_head_kv * n_split * r->L.mpad;
+  const size_t acc = (size_t)align_up((int64_t)(rows * kHeadDim * 4), 256);
+  if (ml_offset) *ml_offset = acc;
+  return acc + rows * 2 * 4;
+}
+
+// The attention launches of a checked call, split partials in part_acc /
+// part_ml (sized for the launch's splits).
+int attn_launch(ring* r, int32_t layer, const void* q, const void* k_noise, const void* v_noise,
+                float* out, void* stream, float* part_acc, float* part_ml) {
   if (int e = use_device(r)) return e;
   hipStream_t s = static_cast<hipStream_t>(stream);
   r->last_stream = s;
@@ -827,6 +850,8 @@ int ring_attn(ring_t* r, int32_t layer, const void* q, const void* k_noise, cons
   AttnArgs a;
   bool swa = false;
   const int32_t n_split = attn_geometry(r, layer, &a, &swa);
+  a.part_acc = part_acc;
+  a.part_ml = part_ml;
   a.q = static_cast<const uint16_t*>(q);
   a.k_noise = static_cast<const uint16_t*>(k_noise);
   a.v_noise = static_cast<const uint16_t*>(v_noise);
@@ -892,8 +917,8 @@ int ring_attn(ring_t* r, int32_t layer, const void* q, const void* k_noise, cons
   }
   if (n_split > 1) {
     MergeArgs m{};
-    m.part_acc = r->part_acc;
-    m.part_ml = r->part_ml;
+    m.part_acc = part_acc;
+    m.part_ml = part_ml;
     m.out = out;
     m.n_units = r->cfg.n_seq * r->cfg.n_head_kv;
     m.n_split = n_split;
@@ -908,6 +933,32 @@ int ring_attn(ring_t* r, int32_t layer, const void* q, const void* k_noise, cons
   }
   return ok();
 }
+}  // namespace
+
+int ring_attn(ring_t* r, int32_t layer, const void* q, const void* k_noise, const void* v_noise,
+              float* out, void* stream) {
+  if (int e = check_attn(r, layer, q, k_noise, v_noise, out)) return e;
+  return attn_launch(r, layer, q, k_noise, v_noise, out, stream, r->part_acc, r->part_ml);
+}
+
+int ring_attn_noalloc(ring_t* r, int32_t layer, const void* q, const void* k_noise,
+                      const void* v_noise, float* out, void* stream) {
+  if (int e = check_attn(r, layer, q, k_noise, v_noise, out)) return e;
+  AttnArgs a;
+  const int32_t n_split = attn_geometry(r, layer, &a, nullptr);
+  size_t ml_off = 0;
+  const size_t need = n_split > 1 ? partial_bytes(r, n_split, &ml_off) : 0;
+  if (need > kStaticScratchBytes)
+    return fail(RING_EINVAL,
+                "ring_attn_noalloc: this launch's split partials need %zu bytes, more than the "
+                "%zu of the static scratch (%d sequences x %d KV heads x %d splits); use ring_attn",
+                need, kStaticScratchBytes, r->cfg.n_seq, r->cfg.n_head_kv, n_split);
+  uint8_t* base = static_cast<uint8_t*>(static_scratch(r->device));
+  if (!base) return fail(RING_EDEVICE, "static scratch of device %d is not resolved", r->device);
+  return attn_launch(r, layer, q, k_noise, v_noise, out, stream, reinterpret_cast<float*>(base),
+                     reinterpret_cast<float*>(base + ml_off));
+}
+
 
 namespace {
 // Bytes of the floor buffer: counters, the timeout count, then the output.

@@ -30,7 +30,8 @@ RING_MAX_SEQ = 64
 # Every function the header declares, in header order.
 EXPORTS = (
     "ring_query_geometry", "ring_init", "ring_plan_step", "ring_plan_from_state",
-    "ring_begin_step", "ring_begin_step_deferred", "ring_begin_step_batch", "ring_mirror_write", "ring_begin_step_mirror", "ring_attn", "ring_free",
+    "ring_begin_step", "ring_begin_step_deferred", "ring_begin_step_batch", "ring_mirror_write", "ring_begin_step_mirror", "ring_attn", "ring_attn_noalloc",
+    "ring_free",
     "ring_last_error", "ring_describe",
     "ring_read_slot_pos", "ring_read_mask", "ring_read_mask_swa", "ring_read_rows",
     "ring_read_state",
@@ -105,6 +106,7 @@ def _load() -> ctypes.CDLL:
         "ring_mirror_write": [P, I32, I64, I64, P, P],
         "ring_begin_step_mirror": [P, I32, I64, ctypes.POINTER(RingKvWeights), P],
         "ring_attn": [P, I32, P, P, P, P, P],
+        "ring_attn_noalloc": [P, I32, P, P, P, P, P],
         "ring_free": [P],
         "ring_last_error": [],
         "ring_describe": [P, ctypes.c_char_p, SZ],
@@ -223,6 +225,12 @@ def ring_attn(handle: int, layer: int, q: int, k_noise: int, v_noise: int, out: 
               stream: int = 0) -> None:
     _check(_lib.ring_attn(handle, layer, q or None, k_noise or None, v_noise or None,
                           out or None, stream or None), "ring_attn")
+
+
+def ring_attn_noalloc(handle: int, layer: int, q: int, k_noise: int, v_noise: int, out: int,
+                      stream: int = 0) -> None:
+    _check(_lib.ring_attn_noalloc(handle, layer, q or None, k_noise or None, v_noise or None,
+                                  out or None, stream or None), "ring_attn_noalloc")
 
 
 def ring_free(handle: int) -> None:
@@ -375,13 +383,18 @@ class Ring:
                                self._ptr(k_norm, torch.float32, (c.n_layer, c.head_dim), "k_norm"),
                                eps, self._stream())
 
-    def attn(self, layer: int, q, k_noise, v_noise, out=None):
+    def attn(self, layer: int, q, k_noise, v_noise, out=None, noalloc: bool = False):
+        """ring_attn (noalloc: ring_attn_noalloc, split partials in the
+        library's static array; `out` must then be given, so that the call
+        allocates nothing)."""
         torch = self._torch
         c = self.cfg
         if out is None:
+            if noalloc:
+                raise ValueError("ring_attn_noalloc writes into a given `out`")
             out = torch.empty((c.n_seq, c.q_len, c.n_head, c.head_dim), dtype=torch.float32,
                               device=self.device)
-        ring_attn(self.handle, layer,
+        (ring_attn_noalloc if noalloc else ring_attn)(self.handle, layer,
                   self._ptr(q, torch.float16, (c.n_seq, c.q_len, c.n_head, c.head_dim), "q"),
                   self._ptr(k_noise, torch.float16, (c.n_seq, c.q_len, self.geo.kv_row), "k_noise"),
                   self._ptr(v_noise, torch.float16, (c.n_seq, c.q_len, self.geo.kv_row), "v_noise"),

@@ -273,6 +273,21 @@ int ring_begin_step_mirror(ring_t* r, int32_t seq, int64_t committed,
 int ring_attn(ring_t* r, int32_t layer, const void* q, const void* k_noise,
               const void* v_noise, float* out, void* stream);
 
+/* ring_attn for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same arguments, checks, kernels and results as ring_attn, but the split
+ * partials of the attention (fp32 accumulators and (max, sum) pairs, for a
+ * launch with more than one split) go to a static array of 16 MiB in the
+ * library's device code instead of the ring's workspace.  The call allocates
+ * and frees nothing; ring_init resolves the array's address once per device.
+ * Every call on one GPU shares that GPU's array: two calls whose work
+ * overlaps on the device (different streams, not ordered) race on it, so
+ * order them on one stream.  Launches whose partials need more than 16 MiB
+ * (n_seq x n_head_kv x splits x 32 or 64 query rows x 520 B) are refused.
+ * Errors: as ring_attn, and RING_EINVAL when the partials exceed the array. */
+int ring_attn_noalloc(ring_t* r, int32_t layer, const void* q, const void* k_noise,
+                      const void* v_noise, float* out, void* stream);
+
 /* Synchronise the ring's last stream and release what the library
  * allocated.  A caller-owned workspace is not freed.  NULL is accepted.    */
 int ring_free(ring_t* r);
