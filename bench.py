@@ -133,7 +133,7 @@ def cpu_baseline(w, seconds: float) -> dict:
                       f"the rest of the oracle on one"}
 
 
-def prepare(w, pool: int, total: int, dev, extra0: int = 0):
+def prepare(w, pool: int, total: int, dev, extra0: int = 0, proj: str = "registered"):
     """Rings of workload ``w`` warmed up, and the device-resident inputs of
     ``total`` steps cycled over ``pool`` rings, plus ``extra0`` further steps
     of ring 0 alone (fewer if its stream ends first).  Returns (rings, calls,
@@ -165,6 +165,12 @@ def prepare(w, pool: int, total: int, dev, extra0: int = 0):
         weights = [(torch.from_numpy(wk).to(dev), torch.from_numpy(wv).to(dev),
                     torch.from_numpy(kn).to(dev)) for _ in range(pool)]
         wptrs = [(a.data_ptr(), b.data_ptr(), c.data_ptr(), RMS_EPS) for a, b, c in weights]
+        if proj == "registered":
+            # each ring keeps its own packed copy in its workspace
+            for r, wp in zip(rings, wptrs):
+                R.ring_set_kv_weights(r.handle, *wp, s)
+            torch.cuda.synchronize(dev)
+            weights, wptrs = None, [None] * pool
 
     def feats(seq, lo, hi):
         return torch.from_numpy(W.fused_features(w, seq, np.arange(lo, hi))).to(dev)
@@ -185,7 +191,10 @@ def prepare(w, pool: int, total: int, dev, extra0: int = 0):
                 f = feats(seq, prev[seq], c)
                 for r, wp in zip(rings, wptrs):
                     R.ring_mirror_write(r.handle, seq, prev[seq], c - prev[seq], f.data_ptr(), s)
-                    R.ring_begin_step_mirror(r.handle, seq, c, *wp, s)
+                    if wp is None:
+                        R.ring_begin_step_mirror_registered(r.handle, seq, c, s)
+                    else:
+                        R.ring_begin_step_mirror(r.handle, seq, c, *wp, s)
                 torch.cuda.synchronize(dev)
                 prev[seq] = c
                 del f
@@ -749,6 +758,10 @@ def main() -> int:
                     help="eager step of a ring with several sequences: auto takes one "
                          "ring_begin_step_batch call for all of them (default), per_seq one "
                          "ring_begin_step call per sequence")
+    ap.add_argument("--proj", choices=("registered", "caller"), default="registered",
+                    help="rows from features: weights registered once per ring "
+                         "(ring_set_kv_weights, packed in the projection's load order; "
+                         "default) or the caller's weights passed every step")
     ap.add_argument("--warm-seconds", type=float, default=0.25,
                     help="GPU clock warm-up before the timed steps (scratch writes that also "
                          "evict the Infinity Cache)")
@@ -806,7 +819,7 @@ def main() -> int:
     # steps for the cache-warm figure
     total = args.warmup + 2 * args.steps
     warm_steps = min(args.steps, 1000) if pool > 1 and not args.floor else 0
-    rings, calls, steps_in, committed, calls0 = prepare(w, pool, total, dev, warm_steps)
+    rings, calls, steps_in, committed, calls0 = prepare(w, pool, total, dev, warm_steps, args.proj)
     s = torch.cuda.current_stream(dev).cuda_stream
     out = torch.empty((w.n_seq, w.q_len, w.n_head, w.head_dim), dtype=torch.float32, device=dev)
     mirror = w.d_model > 0
@@ -816,6 +829,7 @@ def main() -> int:
     begin = R.ring_begin_step_deferred if fused else R.ring_begin_step
     attn, optr = R.ring_attn, out.data_ptr()
     mwrite, mbegin = R.ring_mirror_write, R.ring_begin_step_mirror
+    mbegin_reg = R.ring_begin_step_mirror_registered
     begin_batch = R.ring_begin_step_batch
     if batched:
         # the batched call's argument lists, built once per call
@@ -827,7 +841,10 @@ def main() -> int:
             if mirror:
                 for seq, c, fp, c0, n in seqs:
                     mwrite(h, seq, c0, n, fp, s)
-                    mbegin(h, seq, c, *wptr, s)
+                    if wptr is None:
+                        mbegin_reg(h, seq, c, s)
+                    else:
+                        mbegin(h, seq, c, *wptr, s)
             elif batched:
                 begin_batch(h, *seqs, s)
             else:
@@ -955,7 +972,8 @@ def main() -> int:
                       float(np.mean(seg_rows)) * w.d_model * 2)
         proj_us = prof["k_ring_project"]["avg_us"]
         pa = proj_bytes / (proj_us * 1e-6) / 1e9
-        roofline = {"kernel": "k_ring_project", "bound": "hbm", "achieved": pa,
+        roofline = {"kernel": "k_ring_project", "weights": args.proj, "bound": "hbm",
+                    "achieved": pa,
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": pa / HBM_PEAK_GBS,
                     "traffic": None, "bytes_per_launch": int(proj_bytes),
                     "avg_launch_us": proj_us}
@@ -987,6 +1005,7 @@ def main() -> int:
         "data": "synthetic (seeded normal F16 rows; accepted counts drawn from the "
                 "pages' 1422-verification share table)",
         "config": {"workload": args.workload, "step": step_mode,
+                   **({"proj_weights": args.proj} if mirror else {}),
                    "cap": w.cap, "q_len": w.q_len,
                    "n_head": w.n_head, "n_head_kv": w.n_head_kv, "head_dim": w.head_dim,
                    "n_layer": w.n_layer, "n_seq": w.n_seq, "kv_total": geo.kv_total,

@@ -8,7 +8,8 @@ include/ring_kv.h; ``draft_model_kv_amd.ring`` is its Python binding.
 
 from .ring import (Ring, RingConfig, RingError, RingGeometry, RingKvWeights, RingPlan,
                    make_config, ring_attn, ring_attn_noalloc, ring_begin_step, ring_begin_step_batch,
-                   ring_begin_step_deferred, ring_begin_step_mirror,
+                   ring_begin_step_deferred, ring_begin_step_mirror, ring_begin_step_mirror_registered,
+                   ring_set_kv_weights,
                    ring_describe, ring_free, ring_init, ring_last_error, ring_mirror_write,
                    ring_plan_from_state, ring_plan_step, ring_query_geometry, ring_read_mask,
                    ring_read_mask_swa, ring_read_rows, ring_read_slot_pos, ring_read_state,
@@ -21,7 +22,7 @@ from .ring import (Ring, RingConfig, RingError, RingGeometry, RingKvWeights, Rin
 __all__ = ["Ring", "RingConfig", "RingError", "RingGeometry", "RingKvWeights", "RingPlan",
            "make_config", "ring_attn", "ring_attn_noalloc", "ring_begin_step", "ring_begin_step_batch",
            "ring_begin_step_deferred",
-           "ring_begin_step_mirror",
+           "ring_begin_step_mirror", "ring_begin_step_mirror_registered", "ring_set_kv_weights",
            "ring_describe", "ring_free", "ring_init", "ring_last_error", "ring_mirror_write",
            "ring_plan_from_state", "ring_plan_step", "ring_query_geometry", "ring_read_mask",
            "ring_read_mask_swa", "ring_read_rows", "ring_read_slot_pos", "ring_read_state",

@@ -81,13 +81,31 @@ constexpr int kProjSlice = 256;
 constexpr int kProjMaxKvHeads = 16;   // KV heads a ring with a feature mirror may have
 struct ProjArgs {
   const uint16_t* mirror;    // this sequence's fused features [cap][d_model] F16, slot p % cap
-  const uint16_t* wk;        // [n_layer][kv_row][d_model] F16
-  const uint16_t* wv;        // [n_layer][kv_row][d_model] F16
+  const uint16_t* wk;        // [n_layer][kv_row][d_model] F16 (packed: the packed K and V weights)
+  const uint16_t* wv;        // [n_layer][kv_row][d_model] F16 (packed: unused)
+  int32_t packed;            // weights in the kernel's load order (pack_weights below)
   float* scratch;            // [n_layer][n_ds][kProjRows][2 * kv_row]
   int64_t pos0;              // position of this launch's row 0
   int32_t slot0;             // its mirror slot, pos0 % cap
   int32_t n_rows;            // rows of this launch, 1..kProjRows
   int32_t cap, d_model, kv_row, n_head_kv, n_layer, n_ds;
+  // recip32() of the row tiles, n_ds and 2 n_head_kv (set by launch_project)
+  uint64_t rcp_n_rt, rcp_n_ds, rcp_n_hp;
+};
+
+// Projection weights in the projection kernel's load order: for each work-group
+// block (layer, head part hp = K head 0..n_head_kv-1 then V head, d-slice ds,
+// wave w) 16 KiB [blk 0..3][j 0..3][lane 0..63][e 0..7] holding
+//   W[head row 32 w + lane % 32][dim 256 ds + 64 blk + 32 (lane / 32) + 8 j + e]
+// of wk (hp < n_head_kv) or wv, so that each of the wave's 16 loads of 16 B
+// per lane reads 1 KiB of consecutive bytes.  Blocks in (layer, hp, ds, w)
+// order; the whole is 2 n_layer kv_row d_model halves, as wk and wv.
+struct PackArgs {
+  const uint16_t* wk;        // [n_layer][kv_row][d_model] F16
+  const uint16_t* wv;
+  uint16_t* packed;
+  int64_t n_chunks;          // 16-byte chunks of the packed weights
+  int32_t d_model, kv_row, n_head_kv, n_ds;
 };
 
 // Sequences' deferred fold-in steps, carried out by the next attention
@@ -211,6 +229,7 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s, hipEvent_t t0, hipEvent
 hipError_t launch_attn_fused(const FusedAttnArgs& f, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
 hipError_t launch_project(const ProjArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
+hipError_t launch_pack_weights(const PackArgs& a, hipStream_t s);
 hipError_t launch_fill_u16(uint16_t* p, uint16_t value, int64_t n, hipStream_t s);
 
 // The static split-partial array of ring_attn_noalloc (ring_kernels.hip):

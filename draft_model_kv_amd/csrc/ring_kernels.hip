@@ -1402,52 +1402,67 @@ __global__ __launch_bounds__(256) void k_ring_merge(MergeArgs a) {
 //   its feature row per 64-d block: MFMA step j of a block pairs, for both
 //   operands, dims 64 blk + 32 (lane / 32) + 8 j + e.
 // ---------------------------------------------------------------------------
+template <bool PACKED>
 __global__ __launch_bounds__(256) void k_ring_project(ProjArgs a) {
   constexpr int kRowStride = kProjSlice / 8 + 1;  // half8 per staged row (+1: no bank conflicts)
   __shared__ half8 f_lds[32 * kRowStride];
   // every argument fetched in one batch at entry (see attn_entry)
   asm volatile("" ::"s"(a.mirror), "s"(a.wk), "s"(a.wv), "s"(a.scratch), "s"(a.slot0),
                "s"(a.n_rows), "s"(a.cap), "s"(a.d_model), "s"(a.kv_row), "s"(a.n_head_kv),
-               "s"(a.n_ds));
+               "s"(a.n_ds), "s"(a.rcp_n_rt), "s"(a.rcp_n_ds), "s"(a.rcp_n_hp));
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n_rt = (a.n_rows + 31) >> 5;
-  int b = blockIdx.x;
-  const int rt = b % n_rt;
-  b /= n_rt;
-  const int ds = b % a.n_ds;
-  b /= a.n_ds;
+  // work-group -> (layer, head part, d-slice, row tile) by quotients with
+  // host-computed reciprocals (no integer division)
+  const uint32_t b0 = blockIdx.x;
+  const uint32_t b1 = quot32(b0, a.rcp_n_rt);
+  const int rt = (int)(b0 - b1 * n_rt);
+  const uint32_t b2 = quot32(b1, a.rcp_n_ds);
+  const int ds = (int)(b1 - b2 * a.n_ds);
   const int n_hp = 2 * a.n_head_kv;
-  const int hp = b % n_hp;
-  const int layer = b / n_hp;
+  const int layer = (int)quot32(b2, a.rcp_n_hp);
+  const int hp = (int)(b2 - layer * n_hp);
   const int r0 = rt * 32;
   const int d0 = ds * kProjSlice;
 
   // features of the tile's rows, first (loads return in issue order, and
   // the LDS staging needs them): 32 rows x 32 chunks of 16 B, 4 per thread;
-  // row i sits in mirror slot (slot0 + i) % cap
+  // row i sits in mirror slot (slot0 + i) % cap (slot0 < cap, i < 64)
   half8 fv[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int c = threadIdx.x + 256 * k;
     const int row = c >> 5, dc = c & 31;
-    const int slot = (a.slot0 + min(r0 + row, a.n_rows - 1)) % a.cap;
+    int slot = a.slot0 + min(r0 + row, a.n_rows - 1);
+    while (slot >= a.cap) slot -= a.cap;
     const uint16_t* src = a.mirror + (int64_t)slot * a.d_model + d0 + 8 * dc;
     fv[k] = *(const half8*)src;
   }
 
-  // weights: row 32 w + lane % 32 of the head part, 4 blocks x 64 B
-  const bool is_v = hp >= a.n_head_kv;
-  const int head = is_v ? hp - a.n_head_kv : hp;
-  const uint16_t* wrow = (is_v ? a.wv : a.wk) +
-                         ((int64_t)layer * a.kv_row + head * kHeadDim + 32 * wave + (lane & 31)) *
-                             a.d_model +
-                         d0 + 32 * (lane >> 5);
+  // weights: row 32 w + lane % 32 of the head part, 4 blocks x 64 B (dims
+  // 64 blk + 32 (lane / 32) + 8 j + e of the slice); packed weights hold the
+  // wave's 16 KiB in exactly this load order
   half8 wa[4][4];
+  if constexpr (PACKED) {
+    const half8* wp = (const half8*)a.wk +
+                      ((((int64_t)layer * n_hp + hp) * a.n_ds + ds) * 4 + wave) * 1024;
 #pragma unroll
-  for (int blk = 0; blk < 4; ++blk)
+    for (int blk = 0; blk < 4; ++blk)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) wa[blk][j] = *(const half8*)(wrow + blk * 64 + 8 * j);
+      for (int j = 0; j < 4; ++j) wa[blk][j] = wp[(blk * 4 + j) * 64 + lane];
+  } else {
+    const bool is_v = hp >= a.n_head_kv;
+    const int head = is_v ? hp - a.n_head_kv : hp;
+    const uint16_t* wrow = (is_v ? a.wv : a.wk) +
+                           ((int64_t)layer * a.kv_row + head * kHeadDim + 32 * wave + (lane & 31)) *
+                               a.d_model +
+                           d0 + 32 * (lane >> 5);
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) wa[blk][j] = *(const half8*)(wrow + blk * 64 + 8 * j);
+  }
   // every weight load is issued before the wait for the features
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -1475,6 +1490,32 @@ __global__ __launch_bounds__(256) void k_ring_project(ProjArgs a) {
       *(float4*)(dst + 8 * q) = make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2],
                                             acc[4 * q + 3]);
   }
+}
+
+// Weights into the projection's load order (PackArgs): one 16-byte chunk
+// per thread, read from its row of wk or wv, written contiguously.
+__global__ __launch_bounds__(256) void k_ring_pack_weights(PackArgs a) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= a.n_chunks) return;
+  const int lane = (int)(i & 63);
+  int64_t t = i >> 6;
+  const int j = (int)(t & 3);
+  t >>= 2;
+  const int blk = (int)(t & 3);
+  t >>= 2;
+  const int w = (int)(t & 3);
+  t >>= 2;
+  const int ds = (int)(t % a.n_ds);
+  t /= a.n_ds;
+  const int n_hp = 2 * a.n_head_kv;
+  const int hp = (int)(t % n_hp);
+  const int64_t layer = t / n_hp;
+  const bool is_v = hp >= a.n_head_kv;
+  const int head = is_v ? hp - a.n_head_kv : hp;
+  const int64_t row = layer * a.kv_row + head * kHeadDim + 32 * w + (lane & 31);
+  const int64_t col = (int64_t)ds * kProjSlice + 64 * blk + 32 * (lane >> 5) + 8 * j;
+  const uint16_t* src = (is_v ? a.wv : a.wk) + row * a.d_model + col;
+  *(half8*)(a.packed + i * 8) = *(const half8*)src;
 }
 
 __global__ void k_fill_u16(uint16_t* p, uint16_t value, int64_t n) {
@@ -1610,10 +1651,27 @@ hipError_t launch_merge(const MergeArgs& args, hipStream_t s, hipEvent_t t0, hip
   return hipGetLastError();
 }
 
-hipError_t launch_project(const ProjArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
-  if (a.n_rows <= 0) return hipSuccess;
-  const int grid = a.n_layer * 2 * a.n_head_kv * a.n_ds * ((a.n_rows + 31) / 32);
-  hipExtLaunchKernelGGL(k_ring_project, dim3(grid), dim3(256), 0, s, t0, t1, 0, a);
+hipError_t launch_project(const ProjArgs& args, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+  if (args.n_rows <= 0) return hipSuccess;
+  ProjArgs a = args;
+  const uint32_t n_rt = (a.n_rows + 31) / 32, n_hp = 2 * a.n_head_kv;
+  const uint64_t grid = (uint64_t)a.n_layer * n_hp * a.n_ds * n_rt;
+  // every quotient exact: dividend times divisor at most 2^32
+  if (grid * n_rt > (uint64_t(1) << 32) || grid > (uint64_t(1) << 31)) return hipErrorInvalidValue;
+  a.rcp_n_rt = recip32(n_rt);
+  a.rcp_n_ds = recip32(a.n_ds);
+  a.rcp_n_hp = recip32(n_hp);
+  if (a.packed)
+    hipExtLaunchKernelGGL(k_ring_project<true>, dim3((unsigned)grid), dim3(256), 0, s, t0, t1, 0, a);
+  else
+    hipExtLaunchKernelGGL(k_ring_project<false>, dim3((unsigned)grid), dim3(256), 0, s, t0, t1, 0, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_weights(const PackArgs& a, hipStream_t s) {
+  if (a.n_chunks <= 0) return hipSuccess;
+  const int64_t grid = (a.n_chunks + 255) / 256;
+  hipLaunchKernelGGL(k_ring_pack_weights, dim3((unsigned)grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -54,6 +54,7 @@ struct Layout {
   int32_t n_ds = 0;                       // d-slices of the projection
   int64_t slot_stride = 0;                // int32 per sequence in slot_pos (cap padded)
   size_t off_mirror = 0, off_proj = 0;    // feature mirror, projection scratch
+  size_t off_wpack = 0, off_knorm = 0;    // registered weights (packed), their k_norm
 };
 
 constexpr int kMaxSplits = 64;  // each merge wave holds up to 16 splits in registers
@@ -159,6 +160,10 @@ void geometry_of(const ring_config& c, ring_geometry* g, Layout* L) {
   L->n_ds = c.d_model / kProjSlice;
   L->off_mirror = take((size_t)c.n_seq * c.cap * c.d_model * 2);
   L->off_proj = take((size_t)c.n_layer * L->n_ds * kProjRows * 2 * g->kv_row * 4);
+  // registered projection weights (ring_set_kv_weights): wk and wv packed in
+  // the projection kernel's load order, and k_norm
+  L->off_wpack = take((size_t)c.n_layer * 2 * g->kv_row * c.d_model * 2);
+  L->off_knorm = take(c.d_model > 0 ? (size_t)c.n_layer * kHeadDim * 4 : 0);
   L->total = off;
   g->workspace_bytes = (int64_t)L->total;
 }
@@ -215,6 +220,10 @@ struct ring {
   float* part_ml = nullptr;
   uint16_t* mirror = nullptr;   // fused features [n_seq][cap][d_model], or nullptr
   float* proj = nullptr;        // projection scratch
+  uint16_t* wpack = nullptr;    // registered weights, packed (ring_set_kv_weights)
+  float* knorm = nullptr;       // their k_norm [n_layer][head_dim]
+  float weights_eps = 0.0f;
+  bool weights_set = false;
   std::vector<int64_t> next_pos, held_lo, committed;
   std::vector<std::vector<int64_t>> mirror_pos;  // per sequence: position in each mirror slot, -1 empty
   std::vector<Pending> pending;                   // per sequence
@@ -386,6 +395,8 @@ int ring_init(const ring_config* cfg, void* workspace, size_t workspace_bytes, v
   if (cfg->d_model > 0) {
     r->mirror = reinterpret_cast<uint16_t*>(r->ws + r->L.off_mirror);
     r->proj = reinterpret_cast<float*>(r->ws + r->L.off_proj);
+    r->wpack = reinterpret_cast<uint16_t*>(r->ws + r->L.off_wpack);
+    r->knorm = reinterpret_cast<float*>(r->ws + r->L.off_knorm);
     r->mirror_pos.assign(cfg->n_seq, std::vector<int64_t>(cfg->cap, -1));
   }
   r->pending.assign(cfg->n_seq, Pending{});
@@ -676,6 +687,42 @@ int ring_mirror_write(ring_t* r, int32_t seq, int64_t pos0, int64_t n, const voi
   return ok();
 }
 
+namespace {
+int check_weights(const ring_kv_weights* w) {
+  if (!w || !w->wk || !w->wv || !w->k_norm) return fail(RING_EINVAL, "weights are NULL");
+  if (((reinterpret_cast<uintptr_t>(w->wk) | reinterpret_cast<uintptr_t>(w->wv)) & 15) ||
+      (reinterpret_cast<uintptr_t>(w->k_norm) & 3))
+    return fail(RING_EINVAL, "wk / wv must be 16-byte and k_norm 4-byte aligned");
+  if (!(w->eps >= 0.0f) || !std::isfinite(w->eps)) return fail(RING_EINVAL, "eps must be finite and >= 0");
+  return RING_OK;
+}
+}  // namespace
+
+int ring_set_kv_weights(ring_t* r, const ring_kv_weights* w, void* stream) {
+  if (!r) return fail(RING_EINVAL, "ring is NULL");
+  if (!r->mirror) return fail(RING_ESTATE, "the ring has no feature mirror (d_model = 0)");
+  if (int e = check_weights(w)) return e;
+  if (int e = use_device(r)) return e;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  r->last_stream = s;
+  PackArgs pk{};
+  pk.wk = static_cast<const uint16_t*>(w->wk);
+  pk.wv = static_cast<const uint16_t*>(w->wv);
+  pk.packed = r->wpack;
+  pk.n_chunks = (int64_t)r->cfg.n_layer * 2 * r->geo.kv_row * r->cfg.d_model / 8;
+  pk.d_model = r->cfg.d_model;
+  pk.kv_row = r->geo.kv_row;
+  pk.n_head_kv = r->cfg.n_head_kv;
+  pk.n_ds = r->L.n_ds;
+  if (int e = check_launch(launch_pack_weights(pk, s), "weight packing")) return e;
+  if (hipMemcpyAsync(r->knorm, w->k_norm, (size_t)r->cfg.n_layer * kHeadDim * 4,
+                     hipMemcpyDeviceToDevice, s) != hipSuccess)
+    return fail(RING_EDEVICE, "k_norm copy failed");
+  r->weights_eps = w->eps;
+  r->weights_set = true;
+  return ok();
+}
+
 int ring_begin_step_mirror(ring_t* r, int32_t seq, int64_t committed, const ring_kv_weights* w,
                            void* stream) {
   if (!r) return fail(RING_EINVAL, "ring is NULL");
@@ -683,11 +730,11 @@ int ring_begin_step_mirror(ring_t* r, int32_t seq, int64_t committed, const ring
   if (seq < 0 || seq >= r->cfg.n_seq) return fail(RING_ERANGE, "seq %d out of range", seq);
   if (committed < 0 || committed + r->cfg.q_len > INT32_MAX)
     return fail(RING_ERANGE, "committed %lld out of range", (long long)committed);
-  if (!w || !w->wk || !w->wv || !w->k_norm) return fail(RING_EINVAL, "weights are NULL");
-  if (((reinterpret_cast<uintptr_t>(w->wk) | reinterpret_cast<uintptr_t>(w->wv)) & 15) ||
-      (reinterpret_cast<uintptr_t>(w->k_norm) & 3))
-    return fail(RING_EINVAL, "wk / wv must be 16-byte and k_norm 4-byte aligned");
-  if (!(w->eps >= 0.0f) || !std::isfinite(w->eps)) return fail(RING_EINVAL, "eps must be finite and >= 0");
+  if (!w && !r->weights_set)
+    return fail(RING_ESTATE, "no weights given and none registered (ring_set_kv_weights)");
+  if (w) {
+    if (int e = check_weights(w)) return e;
+  }
   const Plan p = plan_of(r->cfg.cap, r->geo.a_step, committed, r->next_pos[seq], r->held_lo[seq]);
   const std::vector<int64_t>& mp = r->mirror_pos[seq];
   for (int64_t q = p.start; q < committed; ++q)
@@ -707,13 +754,14 @@ int ring_begin_step_mirror(ring_t* r, int32_t seq, int64_t committed, const ring
   a.swa_lo = committed - std::min<int64_t>(r->cfg.swa_window, p.win);
   a.n_new = (int32_t)p.n_new;
   a.proj = r->proj;
-  a.k_norm = w->k_norm;
-  a.eps = (double)w->eps;
+  a.k_norm = w ? w->k_norm : r->knorm;
+  a.eps = (double)(w ? w->eps : r->weights_eps);
   a.n_ds = r->L.n_ds;
   ProjArgs pa{};
   pa.mirror = r->mirror + (int64_t)seq * r->cfg.cap * r->cfg.d_model;
-  pa.wk = static_cast<const uint16_t*>(w->wk);
-  pa.wv = static_cast<const uint16_t*>(w->wv);
+  pa.wk = w ? static_cast<const uint16_t*>(w->wk) : r->wpack;
+  pa.wv = w ? static_cast<const uint16_t*>(w->wv) : nullptr;
+  pa.packed = w ? 0 : 1;
   pa.scratch = r->proj;
   pa.cap = r->cfg.cap;
   pa.d_model = r->cfg.d_model;

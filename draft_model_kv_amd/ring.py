@@ -30,7 +30,7 @@ RING_MAX_SEQ = 64
 # Every function the header declares, in header order.
 EXPORTS = (
     "ring_query_geometry", "ring_init", "ring_plan_step", "ring_plan_from_state",
-    "ring_begin_step", "ring_begin_step_deferred", "ring_begin_step_batch", "ring_mirror_write", "ring_begin_step_mirror", "ring_attn", "ring_attn_noalloc",
+    "ring_begin_step", "ring_begin_step_deferred", "ring_begin_step_batch", "ring_mirror_write", "ring_set_kv_weights", "ring_begin_step_mirror", "ring_attn", "ring_attn_noalloc",
     "ring_free",
     "ring_last_error", "ring_describe",
     "ring_read_slot_pos", "ring_read_mask", "ring_read_mask_swa", "ring_read_rows",
@@ -104,6 +104,7 @@ def _load() -> ctypes.CDLL:
         "ring_begin_step_deferred": [P, I32, I64, P, P, I64, P],
         "ring_begin_step_batch": [P, I32, P, P, P, P, P, P],
         "ring_mirror_write": [P, I32, I64, I64, P, P],
+        "ring_set_kv_weights": [P, ctypes.POINTER(RingKvWeights), P],
         "ring_begin_step_mirror": [P, I32, I64, ctypes.POINTER(RingKvWeights), P],
         "ring_attn": [P, I32, P, P, P, P, P],
         "ring_attn_noalloc": [P, I32, P, P, P, P, P],
@@ -214,10 +215,23 @@ def ring_mirror_write(handle: int, seq: int, pos0: int, n: int, features: int,
            "ring_mirror_write")
 
 
+def ring_set_kv_weights(handle: int, wk: int, wv: int, k_norm: int, eps: float,
+                        stream: int = 0) -> None:
+    w = RingKvWeights(wk or None, wv or None, k_norm or None, eps)
+    _check(_lib.ring_set_kv_weights(handle, ctypes.byref(w), stream or None), "ring_set_kv_weights")
+
+
 def ring_begin_step_mirror(handle: int, seq: int, committed: int, wk: int, wv: int, k_norm: int,
                            eps: float, stream: int = 0) -> None:
     w = RingKvWeights(wk or None, wv or None, k_norm or None, eps)
     _check(_lib.ring_begin_step_mirror(handle, seq, committed, ctypes.byref(w), stream or None),
+           "ring_begin_step_mirror")
+
+
+def ring_begin_step_mirror_registered(handle: int, seq: int, committed: int,
+                                      stream: int = 0) -> None:
+    """ring_begin_step_mirror with w == NULL: the weights of ring_set_kv_weights."""
+    _check(_lib.ring_begin_step_mirror(handle, seq, committed, None, stream or None),
            "ring_begin_step_mirror")
 
 
@@ -372,10 +386,25 @@ class Ring:
                           self._ptr(features, torch.float16, (n, self.cfg.d_model), "features"),
                           self._stream())
 
-    def begin_step_mirror(self, seq: int, committed: int, wk, wv, k_norm, eps: float) -> None:
-        """wk, wv: F16 [n_layer, kv_row, d_model]; k_norm: F32 [n_layer, head_dim]."""
+    def set_kv_weights(self, wk, wv, k_norm, eps: float) -> None:
+        """Register the projection weights (shapes as for begin_step_mirror)."""
         torch = self._torch
         c = self.cfg
+        wshape = (c.n_layer, self.geo.kv_row, c.d_model)
+        ring_set_kv_weights(self.handle, self._ptr(wk, torch.float16, wshape, "wk"),
+                            self._ptr(wv, torch.float16, wshape, "wv"),
+                            self._ptr(k_norm, torch.float32, (c.n_layer, c.head_dim), "k_norm"),
+                            eps, self._stream())
+
+    def begin_step_mirror(self, seq: int, committed: int, wk=None, wv=None, k_norm=None,
+                          eps: float = 0.0) -> None:
+        """wk, wv: F16 [n_layer, kv_row, d_model]; k_norm: F32 [n_layer, head_dim].
+        All None: the weights registered with set_kv_weights."""
+        torch = self._torch
+        c = self.cfg
+        if wk is None and wv is None and k_norm is None:
+            ring_begin_step_mirror_registered(self.handle, seq, committed, self._stream())
+            return
         wshape = (c.n_layer, self.geo.kv_row, c.d_model)
         ring_begin_step_mirror(self.handle, seq, committed,
                                self._ptr(wk, torch.float16, wshape, "wk"),

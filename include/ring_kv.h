@@ -88,7 +88,9 @@ typedef struct ring_config {
  *   kv_row     = head_dim * n_head_kv, F16 values per row
  *   kv_bytes_per_layer  K plus V bytes of one (sequence, layer) ring
  *   workspace_bytes     device bytes ring_init needs when the caller
- *                       provides the workspace                              */
+ *                       provides the workspace (with a feature mirror this
+ *                       includes the mirror, the projection scratch and room
+ *                       for the registered weights, ring_set_kv_weights)    */
 typedef struct ring_geometry {
   int32_t a_step;
   int32_t trash_slot;
@@ -246,14 +248,30 @@ typedef struct ring_kv_weights {
 int ring_mirror_write(ring_t* r, int32_t seq, int64_t pos0, int64_t n,
                       const void* features, void* stream);
 
+/* Register the projection weights of every layer once (the draft model's
+ * wk / wv and k_norm are constant: the page's test log, item 4 of the list
+ * of refuted hypotheses, names the projection as the shallow injection
+ * wk/wv @ fused + k_norm + rope).  The library copies wk and wv into its
+ * workspace in the order the projection kernel loads them (each wave's
+ * 16-byte loads then read consecutive bytes), and k_norm and eps beside
+ * them; ring_begin_step_mirror with w == NULL then projects through this copy
+ * with the same arithmetic and results as through the caller's weights.  A
+ * later call replaces the registered weights.  The copy is enqueued on
+ * `stream`; the caller's buffers must stay valid until the stream has passed
+ * it.  Errors: RING_ESTATE (no mirror), RING_EINVAL (NULL, alignment, eps),
+ * RING_EDEVICE.                                                             */
+int ring_set_kv_weights(ring_t* r, const ring_kv_weights* w, void* stream);
+
 /* ring_begin_step with the new rows computed from the mirror: the same plan
  * (positions [start, committed)), every one of which the mirror must hold
  * (else RING_ESTATE before any device work: after a rewind that re-appends
  * the whole window, write the positions the mirror lost again), projected
- * through `w` for every layer as described above and appended like
+ * through `w` for every layer as described above (w == NULL: through the
+ * weights registered with ring_set_kv_weights) and appended like
  * ring_begin_step's rows (pads, slot_pos, masks and noise RoPE table alike).
- * Errors: RING_ESTATE (no mirror, position missing), RING_ERANGE,
- * RING_EINVAL (NULL weights, alignment, eps), RING_EDEVICE.                 */
+ * Errors: RING_ESTATE (no mirror, position missing, w == NULL with no
+ * weights registered), RING_ERANGE, RING_EINVAL (NULL weight pointers,
+ * alignment, eps), RING_EDEVICE.                                            */
 int ring_begin_step_mirror(ring_t* r, int32_t seq, int64_t committed,
                            const ring_kv_weights* w, void* stream);
 

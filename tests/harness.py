@@ -116,10 +116,12 @@ class Driver:
     """One ring (all sequences, all layers) and its oracle twin."""
 
     def __init__(self, w: W.Workload, n_split: Optional[int] = None, device: str = "cuda:0",
-                 row_blocks: Optional[bool] = None):
+                 row_blocks: Optional[bool] = None, registered_weights: bool = False):
         """n_split: attention splits forced; row_blocks: False puts both
         32-row query blocks of a KV head in one work-group (the library reads
-        both settings when the ring is created)."""
+        both settings when the ring is created); registered_weights: rows
+        from features go through the weights registered with
+        ring_set_kv_weights instead of the caller's."""
         import torch
         from draft_model_kv_amd import Ring
         self.torch = torch
@@ -161,6 +163,9 @@ class Driver:
             self.wv_t = torch.from_numpy(self.wv).to(self.dev)
             self.kn_t = torch.from_numpy(self.kn).to(self.dev)
             self.orc_mirror = [ro.FeatureMirror(w.cap, w.d_model) for _ in range(w.n_seq)]
+            self.registered = registered_weights
+            if registered_weights:
+                self.ring.set_kv_weights(self.wk_t, self.wv_t, self.kn_t, self.eps)
             # (position, epoch) in each mirror slot, as written to both mirrors
             self.mirror_held = [dict() for _ in range(w.n_seq)]
 
@@ -265,7 +270,11 @@ class Driver:
         pos = np.arange(op.start, committed, dtype=np.int64)
         if self.mirror:
             self.write_features(seq, pos)
-            self.ring.begin_step_mirror(seq, committed, self.wk_t, self.wv_t, self.kn_t, self.eps)
+            if self.registered:
+                self.ring.begin_step_mirror(seq, committed)
+            else:
+                self.ring.begin_step_mirror(seq, committed, self.wk_t, self.wv_t, self.kn_t,
+                                            self.eps)
             self.orc[seq].commit_features(op, self.orc_mirror[seq], list(self.wk), list(self.wv),
                                           list(self.kn), self.eps)
             self.committed[seq] = committed

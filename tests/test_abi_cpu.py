@@ -149,12 +149,14 @@ def test_invalid_mirror_width_rejected(d_model):
 
 
 def test_feature_mirror_sizes_the_workspace():
-    """A feature mirror adds cap * d_model F16 per sequence plus the fp32
-    projection scratch (n_layer * d_model / 256 slices of 64 rows x 2 kv_row)."""
+    """A feature mirror adds cap * d_model F16 per sequence, the fp32
+    projection scratch (n_layer * d_model / 256 slices of 64 rows x 2 kv_row)
+    and room for the registered weights (wk, wv F16 and k_norm fp32)."""
     base = rk.ring_query_geometry(rk.make_config(4096, n_layer=5, n_seq=2))
     g = rk.ring_query_geometry(rk.make_config(4096, n_layer=5, n_seq=2, d_model=2048))
-    need = 2 * 4096 * 2048 * 2 + 5 * (2048 // 256) * 64 * 2 * 1024 * 4
-    assert need <= g.workspace_bytes - base.workspace_bytes <= need + 512
+    need = (2 * 4096 * 2048 * 2 + 5 * (2048 // 256) * 64 * 2 * 1024 * 4
+            + 5 * 2 * 1024 * 2048 * 2 + 5 * 128 * 4)   # + registered weights, k_norm
+    assert need <= g.workspace_bytes - base.workspace_bytes <= need + 1024
 
 
 def test_mirror_needs_at_most_16_kv_heads():

@@ -128,3 +128,77 @@ def test_mirror_stream_full():
             for layer in range(w.n_layer):
                 d.check_attn(layer, t)
     d.close()
+
+
+# ---------------------------------------------------------------------------
+# Weights registered once (ring_set_kv_weights): packed in the projection
+# kernel's load order, same arithmetic and order of the products.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("commits", [
+    [40, 41, 47, 59, 64, 70, 90, 91],
+    [200, 201, 209, 218],
+    [200, 150, 151, 300, 290, 291],
+], ids=["fold_wrap", "bulk_chunks", "rewind_far"])
+def test_registered_weights_streams(commits):
+    d = Driver(small(seed=210), registered_weights=True)
+    run(d, commits)
+    d.close()
+
+
+@pytest.mark.parametrize("d_model,n_head_kv", [(512, 4), (2048, 8), (768, 16)])
+def test_registered_equals_caller_weights_bit_for_bit(d_model, n_head_kv):
+    """The same stream through the caller's weights and through the
+    registered ones: identical ring rows and attention outputs."""
+    w = small(d_model=d_model, seed=211 + d_model, n_layer=2, cap=100, q_len=3,
+              n_head=2 * n_head_kv, n_head_kv=n_head_kv)
+    a, b = Driver(w), Driver(w, registered_weights=True)
+    for t, c in enumerate([70, 71, 75, 140, 141]):
+        a.step(0, c)
+        b.step(0, c)
+        for layer in range(w.n_layer):
+            # ring slots (the noise rows past cap hold each ring's last noise block)
+            ka, va = a.ring.rows(0, layer, 0, a.geo.cap)
+            kb, vb = b.ring.rows(0, layer, 0, b.geo.cap)
+            assert np.array_equal(ka.view(np.uint16), kb.view(np.uint16)), (t, layer)
+            assert np.array_equal(va.view(np.uint16), vb.view(np.uint16)), (t, layer)
+            oa = a.attn(layer, t)[0]
+            ob = b.attn(layer, t)[0]
+            assert np.array_equal(oa, ob), (t, layer)
+        a.check_index(0)
+        b.check_index(0)
+        b.check_attn(0, 100 + t)
+    a.close()
+    b.close()
+
+
+def test_registered_weights_needed_for_null():
+    from draft_model_kv_amd import ring as rk
+    d = Driver(small(seed=212))
+    d.write_features(0, np.arange(0, 10))
+    with pytest.raises(rk.RingError) as e:
+        d.ring.begin_step_mirror(0, 10)          # no weights given, none registered
+    assert e.value.code == rk.RING_ESTATE
+    with pytest.raises(rk.RingError) as e:
+        rk.ring_set_kv_weights(d.ring.handle, d.wk_t.data_ptr() + 2, d.wv_t.data_ptr(),
+                               d.kn_t.data_ptr(), d.eps)
+    assert e.value.code == rk.RING_EINVAL
+    d.close()
+
+
+def test_mirror_stream_full_registered():
+    """The full-size workload through registered weights: 4096-token prompt,
+    then 40 decode steps."""
+    w = W.WORKLOADS["mirror_stream"]
+    d = Driver(w, registered_weights=True)
+    stream = W.commit_stream(w, 0)[: 1 + 40]
+    for t, c in enumerate(stream):
+        d.step(0, c)
+        d.check_index(0)
+        if t in (0, 1, len(stream) - 1):
+            for layer in range(w.n_layer):
+                d.check_rows(0, layer)
+        if t % 8 == 0 or t == len(stream) - 1:
+            for layer in range(w.n_layer):
+                d.check_attn(layer, t)
+    d.close()
+
