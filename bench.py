@@ -133,7 +133,8 @@ def cpu_baseline(w, seconds: float) -> dict:
                       f"the rest of the oracle on one"}
 
 
-def prepare(w, pool: int, total: int, dev, extra0: int = 0, proj: str = "registered"):
+def prepare(w, pool: int, total: int, dev, extra0: int = 0, proj: str = "registered",
+            workspace: str = "torch"):
     """Rings of workload ``w`` warmed up, and the device-resident inputs of
     ``total`` steps cycled over ``pool`` rings, plus ``extra0`` further steps
     of ring 0 alone (fewer if its stream ends first).  Returns (rings, calls,
@@ -154,7 +155,8 @@ def prepare(w, pool: int, total: int, dev, extra0: int = 0, proj: str = "registe
     rings = [R.Ring(cap=w.cap, q_len=w.q_len, n_head=w.n_head, n_head_kv=w.n_head_kv,
                     head_dim=w.head_dim, n_layer=w.n_layer, n_seq=w.n_seq,
                     rope_base=w.rope_base, device=dev, swa_window=w.swa_window,
-                    swa_layers=w.swa_layers, d_model=w.d_model) for _ in range(pool)]
+                    swa_layers=w.swa_layers, d_model=w.d_model, workspace=workspace)
+             for _ in range(pool)]
     s = torch.cuda.current_stream(dev).cuda_stream
     mirror = w.d_model > 0
     if mirror:
@@ -645,7 +647,7 @@ def summarize_wide(out_dir: str, wl_name: str, khash: str, fetch_scale: float,
 
 
 FLOOR_KINDS = (("empty", 0), ("read", 1), ("partials", 2), ("two_launch", 5),
-               ("last_arriver", 3), ("barrier", 4))
+               ("last_arriver", 3), ("barrier", 4), ("matrix_math", 7), ("vector_math", 8))
 
 
 def clock_warmup(dev, seconds: float, flush_mib: int) -> int:
@@ -762,6 +764,9 @@ def main() -> int:
                     help="rows from features: weights registered once per ring "
                          "(ring_set_kv_weights, packed in the projection's load order; "
                          "default) or the caller's weights passed every step")
+    ap.add_argument("--workspace", choices=("torch", "library"), default="torch",
+                    help="each ring's workspace: a torch tensor (default) or allocated by "
+                         "ring_init itself")
     ap.add_argument("--warm-seconds", type=float, default=0.25,
                     help="GPU clock warm-up before the timed steps (scratch writes that also "
                          "evict the Infinity Cache)")
@@ -817,9 +822,10 @@ def main() -> int:
     # timing events (they slow back-to-back launches, so they stay out of the
     # timed region); ring 0 alone then takes up to min(steps, 1000) more
     # steps for the cache-warm figure
-    total = args.warmup + 2 * args.steps
+    total = args.warmup + (0 if args.floor else 2 * args.steps)
     warm_steps = min(args.steps, 1000) if pool > 1 and not args.floor else 0
-    rings, calls, steps_in, committed, calls0 = prepare(w, pool, total, dev, warm_steps, args.proj)
+    rings, calls, steps_in, committed, calls0 = prepare(w, pool, total, dev, warm_steps, args.proj,
+                                                        args.workspace)
     s = torch.cuda.current_stream(dev).cuda_stream
     out = torch.empty((w.n_seq, w.q_len, w.n_head, w.head_dim), dtype=torch.float32, device=dev)
     mirror = w.d_model > 0
@@ -1004,7 +1010,7 @@ def main() -> int:
         "dtype": "f16",
         "data": "synthetic (seeded normal F16 rows; accepted counts drawn from the "
                 "pages' 1422-verification share table)",
-        "config": {"workload": args.workload, "step": step_mode,
+        "config": {"workload": args.workload, "step": step_mode, "workspace": args.workspace,
                    **({"proj_weights": args.proj} if mirror else {}),
                    "cap": w.cap, "q_len": w.q_len,
                    "n_head": w.n_head, "n_head_kv": w.n_head_kv, "head_dim": w.head_dim,

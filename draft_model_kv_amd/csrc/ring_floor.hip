@@ -22,6 +22,12 @@
 //           sums its 1/n_split slice of every split's partial
 //   kind 5  (host side) kind 2, then the ring's own merge launch over those
 //           partials
+//   kind 7  kind 1 plus, per tile, the attention's matrix-core contractions
+//           on the loaded K and V fragments: 16 v_mfma_f32_32x32x16_f16 for
+//           S^T = K Q^T with Q as hi + lo F16, 8 for O^T += V^T P^T (query
+//           fragments are stand-ins; the products are what is timed)
+//   kind 8  kind 1 plus the same 393,216 products per tile and wave on the
+//           vector unit (v_dot2_f32_f16), for the matrix-core A/B
 //   kind 6  one wave that sleeps for several milliseconds (a bounded loop of
 //           s_sleep): the host queues a batch of launches behind it, so that
 //           their back-to-back time on the device is not bounded by how fast
@@ -33,7 +39,13 @@
 namespace ringkv {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+
+__device__ inline f32x16 floor_mfma(half8 a, half8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
 
 // Cache-policy bits of the buffer instructions on gfx950: sc1 = device scope
 // (stores write through to memory, loads are coherent across the XCDs' L2s).
@@ -76,6 +88,16 @@ __global__ __launch_bounds__(256) void k_ring_floor(FloorArgs a) {
     const uint16_t* kh = a.kring + seq * a.seq_stride + a.layer_offset + g * a.head_stride;
     const uint16_t* vh = a.vring + seq * a.seq_stride + a.layer_offset + g * a.head_stride;
     u32x4 x = {0u, 0u, 0u, 0u};
+    // kinds 7 and 8: the attention's tile contractions on the loaded tiles,
+    // with the query fragments stand-ins built from the lane index
+    f32x16 acc[4] = {};
+    float vacc[8] = {};
+    half8 qh, ql;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      qh[e] = (_Float16)(0.01f * (float)(lane + e));
+      ql[e] = (_Float16)(1e-4f * (float)(lane - e));
+    }
     for (int t = t0 + wave; t < t1; t += 4) {
       int rt = first + t;
       if (rt >= a.ring_tiles) rt -= a.ring_tiles;
@@ -86,10 +108,62 @@ __global__ __launch_bounds__(256) void k_ring_floor(FloorArgs a) {
       for (int c = 0; c < 8; ++c) kc[c] = kt[c * 64 + lane];
 #pragma unroll
       for (int c = 0; c < 8; ++c) vc[c] = vt[c * 64 + lane];
+      if constexpr (KIND == 7) {
+        // 16 matrix ops for S^T = K Q^T (Q as hi + lo), 8 for O^T += V^T P^T
+        f32x16 sacc = {};
 #pragma unroll
-      for (int c = 0; c < 8; ++c) x ^= kc[c] ^ vc[c];
+        for (int c = 0; c < 8; ++c) {
+          sacc = floor_mfma(__builtin_bit_cast(half8, kc[c]), qh, sacc);
+          sacc = floor_mfma(__builtin_bit_cast(half8, kc[c]), ql, sacc);
+        }
+        half8 p0, p1;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          p0[e] = (_Float16)sacc[e];
+          p1[e] = (_Float16)sacc[8 + e];
+        }
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          acc[b] = floor_mfma(__builtin_bit_cast(half8, vc[2 * b]), p0, acc[b]);
+          acc[b] = floor_mfma(__builtin_bit_cast(half8, vc[2 * b + 1]), p1, acc[b]);
+        }
+      } else if constexpr (KIND == 8) {
+        // the same 393,216 products per wave on the vector unit: for each of
+        // the 32 queries, its hi and lo halves against the lane's 64 K
+        // halves (2 x 32 v_dot2), and 32 v_dot2 against its 64 V halves
+        typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+#pragma unroll 4
+        for (int n = 0; n < 32; ++n) {
+          const half8 qa = qh * (_Float16)(float)n, qb = ql * (_Float16)(float)n;
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            const half8 kk = __builtin_bit_cast(half8, kc[c]);
+            const half8 vv = __builtin_bit_cast(half8, vc[c]);
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+              const half2v k2 = {kk[e], kk[e + 1]}, v2 = {vv[e], vv[e + 1]};
+              vacc[(e >> 1)] = __builtin_amdgcn_fdot2((half2v){qa[e], qa[e + 1]}, k2, vacc[e >> 1], false);
+              vacc[4 + (e >> 1)] = __builtin_amdgcn_fdot2((half2v){qb[e], qb[e + 1]}, k2, vacc[4 + (e >> 1)], false);
+              vacc[(e >> 1)] = __builtin_amdgcn_fdot2((half2v){qa[e + 1], qb[e]}, v2, vacc[e >> 1], false);
+            }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) x ^= kc[c] ^ vc[c];
+      }
     }
-    if constexpr (KIND == 1) {
+    if constexpr (KIND == 7 || KIND == 8) {
+      float r = 0.0f;
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) r += acc[b][j];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) r += vacc[i];
+      x.x = __builtin_bit_cast(uint32_t, r);
+    }
+    if constexpr (KIND == 1 || KIND == 7 || KIND == 8) {
       // one word per wave keeps every load live
       uint32_t w = x.x ^ x.y ^ x.z ^ x.w;
 #pragma unroll
@@ -220,6 +294,8 @@ hipError_t launch_floor(const FloorArgs& args, int kind, hipStream_t s, hipEvent
     case 2: hipExtLaunchKernelGGL(k_ring_floor<2>, g, b, 0, s, t0, t1, 0, a); break;
     case 3: hipExtLaunchKernelGGL(k_ring_floor<3>, g, b, 0, s, t0, t1, 0, a); break;
     case 4: hipExtLaunchKernelGGL(k_ring_floor<4>, g, b, 0, s, t0, t1, 0, a); break;
+    case 7: hipExtLaunchKernelGGL(k_ring_floor<7>, g, b, 0, s, t0, t1, 0, a); break;
+    case 8: hipExtLaunchKernelGGL(k_ring_floor<8>, g, b, 0, s, t0, t1, 0, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

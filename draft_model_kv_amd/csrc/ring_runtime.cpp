@@ -1021,7 +1021,7 @@ size_t floor_out_bytes(const ring* r) {
 int ring_profile_floor(ring_t* r, int32_t layer, int32_t kind, void* stream) {
   if (!r) return fail(RING_EINVAL, "ring is NULL");
   if (layer < 0 || layer >= r->cfg.n_layer) return fail(RING_ERANGE, "layer %d out of range", layer);
-  if (kind < RING_FLOOR_EMPTY || kind > RING_FLOOR_HOLD)
+  if (kind < RING_FLOOR_EMPTY || kind > RING_FLOOR_VECTOR_MATH)
     return fail(RING_EINVAL, "floor kind %d out of range", kind);
   if (kind == RING_FLOOR_HOLD) {
     if (int e = use_device(r)) return e;
@@ -1037,7 +1037,9 @@ int ring_profile_floor(ring_t* r, int32_t layer, int32_t kind, void* stream) {
   const int32_t n_split = attn_geometry(r, layer, &a, nullptr);
   const size_t part_bytes =
       (size_t)r->cfg.n_seq * r->cfg.n_head_kv * r->L.n_split * r->L.mpad * kHeadDim * 4;
-  if (kind >= RING_FLOOR_PARTIALS && n_split < 2)
+  const bool with_partials = kind == RING_FLOOR_PARTIALS || kind == RING_FLOOR_LAST_ARRIVER ||
+                             kind == RING_FLOOR_BARRIER || kind == RING_FLOOR_TWO_LAUNCH;
+  if (with_partials && n_split < 2)
     return fail(RING_EINVAL, "this launch has one split: there are no partials to store");
   const bool ticketed = kind == RING_FLOOR_LAST_ARRIVER || kind == RING_FLOOR_BARRIER;
   if (ticketed && part_bytes >= (size_t(1) << 31))

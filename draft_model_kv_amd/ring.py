@@ -42,7 +42,8 @@ RING_KERNEL_STEP, RING_KERNEL_ATTN, RING_KERNEL_MERGE, RING_KERNEL_PROJ = 0, 1, 
 RING_KERNEL_FLOOR = 4
 # kinds of ring_profile_floor
 (RING_FLOOR_EMPTY, RING_FLOOR_READ, RING_FLOOR_PARTIALS, RING_FLOOR_LAST_ARRIVER,
- RING_FLOOR_BARRIER, RING_FLOOR_TWO_LAUNCH, RING_FLOOR_HOLD) = 0, 1, 2, 3, 4, 5, 6
+ RING_FLOOR_BARRIER, RING_FLOOR_TWO_LAUNCH, RING_FLOOR_HOLD, RING_FLOOR_MATRIX_MATH,
+ RING_FLOOR_VECTOR_MATH) = 0, 1, 2, 3, 4, 5, 6, 7, 8
 
 
 class RingConfig(ctypes.Structure):
@@ -321,18 +322,28 @@ class Ring:
     """
 
     def __init__(self, cap, q_len=8, n_head=32, n_head_kv=8, head_dim=128, n_layer=1,
-                 n_seq=1, rope_base=1.0e6, device=None, swa_window=0, swa_layers=0, d_model=0):
+                 n_seq=1, rope_base=1.0e6, device=None, swa_window=0, swa_layers=0, d_model=0,
+                 workspace: str = "torch"):
+        """workspace: "torch" (a torch uint8 tensor, the default) or
+        "library" (ring_init allocates it, ring_free releases it)."""
         import torch
         self._torch = torch
         self.cfg = make_config(cap, q_len, n_head, n_head_kv, head_dim, n_layer, n_seq, rope_base,
                                swa_window, swa_layers, d_model)
         self.geo = ring_query_geometry(self.cfg)
         self.device = torch.device(device or "cuda")
-        self.workspace = torch.empty(self.geo.workspace_bytes + 256, dtype=torch.uint8,
-                                     device=self.device)
-        base = self.workspace.data_ptr()
-        off = (-base) % 256
-        self.handle = ring_init(self.cfg, base + off, self.geo.workspace_bytes, self._stream())
+        if workspace == "library":
+            with torch.cuda.device(self.device):
+                self.workspace = None
+                self.handle = ring_init(self.cfg, 0, 0, self._stream())
+        elif workspace == "torch":
+            self.workspace = torch.empty(self.geo.workspace_bytes + 256, dtype=torch.uint8,
+                                         device=self.device)
+            base = self.workspace.data_ptr()
+            off = (-base) % 256
+            self.handle = ring_init(self.cfg, base + off, self.geo.workspace_bytes, self._stream())
+        else:
+            raise ValueError(f"workspace {workspace!r}: 'torch' or 'library'")
         self.a_step = self.geo.a_step
 
     def _stream(self) -> int:

@@ -380,6 +380,14 @@ int ring_profile_read(ring_t* r, int32_t kernel, int32_t* n_launches, double* to
  *                            launch over those partials: the data movement
  *                            of ring_attn's two launches (timed as two
  *                            RING_KERNEL_FLOOR launches)
+ *   RING_FLOOR_MATRIX_MATH   RING_FLOOR_READ plus, per tile and wave, the
+ *                            attention's contractions on the matrix cores:
+ *                            16 v_mfma_f32_32x32x16_f16 for the scores (query
+ *                            as two F16 halves) and 8 for P V, on the loaded
+ *                            K and V fragments
+ *   RING_FLOOR_VECTOR_MATH   RING_FLOOR_READ plus the same 393,216 products
+ *                            per tile and wave on the vector unit (v_dot2),
+ *                            the other side of the matrix-core A/B
  *   RING_FLOOR_HOLD          one wave that sleeps for about 14 ms (a bounded
  *                            loop) and reads nothing: launches queued behind
  *                            it then run back to back on the device, however
@@ -410,6 +418,8 @@ int ring_profile_read(ring_t* r, int32_t kernel, int32_t* n_launches, double* to
 #define RING_FLOOR_BARRIER      4
 #define RING_FLOOR_TWO_LAUNCH    5
 #define RING_FLOOR_HOLD          6
+#define RING_FLOOR_MATRIX_MATH   7
+#define RING_FLOOR_VECTOR_MATH   8
 int ring_profile_floor(ring_t* r, int32_t layer, int32_t kind, void* stream);
 
 /* Number of RING_FLOOR_BARRIER waits that ended by their poll limit rather
