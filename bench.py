@@ -257,10 +257,12 @@ PROFILE_RUNS = {
                          "OUT/prof_ktrace_floor -o run -- python REPO/bench.py --floor "
                          "--floor-launches 400 --warmup 100",
     "bench_floor": "python REPO/bench.py --floor --floor-launches 400 --warmup 100",
+    # the step captured in HIP graphs and replayed, against plain launches
+    "bench_graph": "python REPO/bench.py --graph --warmup 50",
     "pmc_fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/pmc_fetch -o run "
-                 "-- python REPO/bench.py --steps 64 --warmup 16 --no-cpu-baseline",
+                 "-- python REPO/bench.py --steps 64 --warmup 16 --no-cpu-baseline --floor-launches 0",
     "pmc_write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/pmc_write -o run "
-                 "-- python REPO/bench.py --steps 64 --warmup 16 --no-cpu-baseline",
+                 "-- python REPO/bench.py --steps 64 --warmup 16 --no-cpu-baseline --floor-launches 0",
     "pmc_copy_fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/pmc_copy_fetch -o run "
                       "-- python REPO/bench.py --calibrate-copy 1024",
     "pmc_copy_write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/pmc_copy_write -o run "
@@ -287,14 +289,16 @@ PROFILE_RUNS = {
 WIDE_WORKLOADS = ("batched_seqs", "large_window")
 for _wl in WIDE_WORKLOADS:
     PROFILE_RUNS[f"bench_plain_{_wl}"] = (f"python REPO/bench.py --workload {_wl} --steps 200 "
-                                          "--warmup 20 --no-cpu-baseline")
+                                          "--warmup 20 --no-cpu-baseline --floor-launches 60")
     PROFILE_RUNS[f"prof_ktrace_{_wl}"] = (f"rocprofv3 --kernel-trace --stats --output-format csv -d "
                                           f"OUT/prof_ktrace_{_wl} -o run -- python REPO/bench.py "
-                                          f"--workload {_wl} --steps 200 --warmup 20 --no-cpu-baseline")
+                                          f"--workload {_wl} --steps 200 --warmup 20 --no-cpu-baseline "
+                                          "--floor-launches 0")
     for _c in ("fetch", "write"):
         PROFILE_RUNS[f"pmc_{_c}_{_wl}"] = (f"rocprofv3 --pmc {_c.upper()}_SIZE --output-format csv "
                                            f"-d OUT/pmc_{_c}_{_wl} -o run -- python REPO/bench.py "
-                                           f"--workload {_wl} --steps 16 --warmup 4 --no-cpu-baseline")
+                                           f"--workload {_wl} --steps 16 --warmup 4 --no-cpu-baseline "
+                                           "--floor-launches 0")
 CALIBRATE_COPY_MIB = 1024
 KERNELS = ("k_ring_attn", "k_ring_step", "k_ring_merge")
 KERNELS_MIRROR = ("k_ring_project", "k_ring_step", "k_ring_attn", "k_ring_merge")
@@ -400,9 +404,10 @@ def summarize_profiles(out_dir: str) -> int:
                   f"start and end timestamps): one step every {tl['period_us']} us = attention "
                   f"{tl['attn_us']} us + gap {tl['gap_attn_to_merge_us']} us + merge "
                   f"{tl['merge_us']} us + gap {tl['gap_merge_to_next_us']} us to the next "
-                  "attention.  The dispatches do not overlap: each kernel's duration runs from "
-                  "its first wave's start to its last wave's end, and the gaps are the "
-                  "dependent launch's turnaround."]
+                  "attention.  The dispatches do not overlap (each duration runs from the "
+                  "kernel's start to its end).  The tracer slows the host's submission, so "
+                  "here the device waits for the next step (the last gap); without it the "
+                  "step is device-bound (below)."]
     if bl:
         ev = {k: v["avg_us"] for k, v in bl.get("kernels", {}).items()}
         lines += ["", "The same bench without the profiler (" + f"`{cmd('bench_plain')}`" + "), "
@@ -481,8 +486,52 @@ def summarize_profiles(out_dir: str) -> int:
             written.append(summarize_wide(out_dir, wl_name, khash, fetch_scale, write_scale))
     if os.path.isdir(os.path.join(out_dir, "prof_ktrace_floor")):
         written.append(summarize_floor(out_dir, khash))
+    if os.path.exists(os.path.join(out_dir, "bench_graph.log")):
+        written.append(summarize_graph(out_dir, khash))
     print(json.dumps({"written": written, "kernel_source_hash": khash}))
     return 0
+
+
+def _json_line(path: str, key: str):
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        for ln in fh:
+            if ln.strip().startswith("{") and f'"{key}"' in ln:
+                return json.loads(ln)
+    return None
+
+
+def floor_table(fl: dict) -> list:
+    lines = ["| kind | back to back us | event us |", "|---|---:|---:|"]
+    for k, v in fl.items():
+        if isinstance(v, dict) and "b2b_us" in v:
+            ev = f"{v['event_us']:.2f}" if v.get("event_us") else "-"
+            lines.append(f"| {k} | {v['b2b_us']:.2f} | {ev} |")
+    return lines
+
+
+def summarize_graph(out_dir: str, khash: str) -> str:
+    """Graph replay against plain launches (bench.py --graph)."""
+    bl = _json_line(os.path.join(out_dir, "bench_graph.log"), "graph")
+    g = bl["graph"]
+    lines = ["# The decode step as plain launches and as replayed HIP graphs (decode_stream, "
+             "cap 4096, 32-ring pool)", "", f"Kernel source hash: `{khash}`", "",
+             "Command (cd /tmp; TMPDIR=/tmp):", "", f"    {PROFILE_RUNS['bench_graph']}", "",
+             g["what"] + ".  Host: time to submit, per step.  Device: a batch queued behind a "
+             "hold launch, HIP events around it, per step (when the batch was not queued in time "
+             "the host's pace sets it).", "",
+             "| step as | steps per graph | host us per step | device us per step | batch queued |",
+             "|---|---:|---:|---:|---|"]
+    for k in ("plain", "graph_1", "graph_8"):
+        v = g[k]
+        lines.append(f"| {'plain launches' if k == 'plain' else 'graph replay'} | "
+                     f"{v.get('steps_per_graph', '-')} | {v['host_us']:.2f} | {v['device_us']:.2f} | "
+                     f"{'yes' if v['queued_behind_hold'] else 'no'} |")
+    p_ = "profiles/ring_step_graph_replay_decode_stream.md"
+    with open(os.path.join(ROOT, p_), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    return p_
 
 
 def summarize_floor(out_dir: str, khash: str) -> str:
@@ -497,7 +546,8 @@ def summarize_floor(out_dir: str, khash: str) -> str:
                 if ln.strip().startswith("{") and '"floors"' in ln:
                     bl = json.loads(ln)
     names = {"0": "empty", "1": "read", "2": "partials (+ k_ring_merge: two_launch)",
-             "3": "last_arriver", "4": "barrier"}
+             "3": "last_arriver", "4": "barrier", "6": "hold", "7": "matrix_math",
+             "8": "vector_math"}
     lines = ["# Floors of the attention launch: decode_stream (cap 4096, q_len 8, GQA 32/8 x 128, "
              "F16, 1 layer, 32-ring pool)", "", f"Kernel source hash: `{khash}`", "",
              "Command (cd /tmp; TMPDIR=/tmp):", "", f"    {PROFILE_RUNS['prof_ktrace_floor']}", "",
@@ -517,12 +567,8 @@ def summarize_floor(out_dir: str, khash: str) -> str:
         fl = bl["floors"]
         lines += ["", f"The same floors without the profiler (`{PROFILE_RUNS['bench_floor']}`), "
                   f"{fl['launches']} launches each cycled over the pool; per launch, back to back "
-                  "(wall clock between two synchronisations) and one dispatch bound to HIP events:", "",
-                  "| kind | back to back us | event us |", "|---|---:|---:|"]
-        for k, v in fl.items():
-            if isinstance(v, dict) and "b2b_us" in v:
-                ev = f"{v['event_us']:.2f}" if v.get("event_us") else "-"
-                lines.append(f"| {k} | {v['b2b_us']:.2f} | {ev} |")
+                  "(a batch queued behind a hold launch, HIP events around it) and one dispatch "
+                  "bound to HIP events:", ""] + floor_table(fl)
         lines.append(f"\nBarrier waits that hit their poll limit: {fl.get('barrier_timeouts')}.")
     p_ = "profiles/k_ring_floor_decode_stream_kernel_trace.md"
     with open(os.path.join(ROOT, p_), "w") as fh:
@@ -640,6 +686,10 @@ def summarize_wide(out_dir: str, wl_name: str, khash: str, fetch_scale: float,
             f"{100 * r['frac']:.1f}% of 8 TB/s; splits: {bl['config']['ring'].split('splits=')[-1]}.")
     if trace:
         lines.append(f"Average k_ring_attn duration in the kernel trace: {trace:.2f} us.")
+    if bl and bl.get("floors"):
+        lines += ["", "Floors of this launch in the same bench run (ring_profile_floor: the "
+                  "attention's grid and tiles with a trivial consumer; "
+                  f"ceiling_frac {bl.get('ceiling_frac')}):", ""] + floor_table(bl["floors"])
     path = f"profiles/k_ring_attn_{wl_name}.md"
     with open(os.path.join(ROOT, path), "w") as fh:
         fh.write("\n".join(lines) + "\n")
@@ -726,6 +776,67 @@ def floor_segment(rings, pool, launches, dev, R, attn_us, step_us, bytes_read):
     return out, ceil
 
 
+GRAPH_PLAIN_STEPS = 400
+GRAPH_REPLAYS = 400
+
+
+def graph_segment(rings, pool, calls, warmup, run, dev, R) -> dict:
+    """The step as plain launches against the same step captured in HIP
+    graphs (torch.cuda.graph around the C-ABI calls) and replayed unchanged.
+
+    Plain: GRAPH_PLAIN_STEPS steps cycled over the pool.  Graphs: one per
+    pool ring holding that ring's next step (so that replays cycle over the
+    pool and stay cold), then graphs of 8 steps (8 rings each).  Per step:
+    host time to submit, and device time of a batch queued behind a
+    RING_FLOOR_HOLD launch (HIP events around the batch)."""
+    import torch
+    s = torch.cuda.current_stream(dev).cuda_stream
+
+    def timed(submit, n):
+        R.ring_profile_floor(rings[0].handle, 0, R.RING_FLOOR_HOLD, s)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        th = time.perf_counter()
+        submit()
+        host = time.perf_counter() - th
+        e1.record()
+        queued = not e0.query()
+        torch.cuda.synchronize(dev)
+        return {"host_us": host / n * 1e6, "device_us": e0.elapsed_time(e1) * 1e3 / n,
+                "queued_behind_hold": bool(queued)}
+
+    out = {}
+    plain = calls[warmup: warmup + GRAPH_PLAIN_STEPS]
+    out["plain"] = timed(lambda: run(plain), len(plain))
+    base = warmup + GRAPH_PLAIN_STEPS
+    for per in (1, 8):
+        graphs = []
+        for g0 in range(0, pool, per):
+            # the next step of rings g0 .. g0 + per - 1, captured as issued
+            step_calls = calls[base + g0: base + g0 + per]
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                run(step_calls, s=torch.cuda.current_stream(dev).cuda_stream)
+            graphs.append(g)
+        base += pool
+        for g in graphs:            # first replays (uploads the graphs)
+            g.replay()
+        torch.cuda.synchronize(dev)
+        n_rep = GRAPH_REPLAYS // len(graphs) * len(graphs)
+
+        def replays():
+            for i in range(n_rep):
+                graphs[i % len(graphs)].replay()
+        r_ = timed(replays, n_rep * per)
+        r_["steps_per_graph"] = per
+        out[f"graph_{per}"] = r_
+        del graphs
+    out["what"] = ("the fused step (ring_begin_step_deferred + ring_attn: attention launch with "
+                   "the fold-in append, then the merge) per step; graphs hold a ring's step "
+                   "with its arguments fixed and are replayed unchanged")
+    return out
+
+
 def committed_trace_us(kernel_hash: str):
     """Average duration of the attention kernel in the committed kernel-trace
     summary of the decode stream, if it was taken on this kernel source."""
@@ -776,6 +887,10 @@ def main() -> int:
                     help="launches per ring_profile_floor kind (0: no floor segment)")
     ap.add_argument("--floor", action="store_true",
                     help="only the floor segment (after the same warm-up), one JSON line")
+    ap.add_argument("--graph", action="store_true",
+                    help="only the graph-replay comparison (after the same warm-up), one JSON "
+                         "line: the step captured in HIP graphs and replayed, against plain "
+                         "launches")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--summarize", metavar="OUT", default="",
@@ -823,6 +938,9 @@ def main() -> int:
     # timed region); ring 0 alone then takes up to min(steps, 1000) more
     # steps for the cache-warm figure
     total = args.warmup + (0 if args.floor else 2 * args.steps)
+    if args.graph:
+        # plain steps, then one step per pool ring for the captured graphs
+        total = args.warmup + GRAPH_PLAIN_STEPS + 8 * pool
     warm_steps = min(args.steps, 1000) if pool > 1 and not args.floor else 0
     rings, calls, steps_in, committed, calls0 = prepare(w, pool, total, dev, warm_steps, args.proj,
                                                         args.workspace)
@@ -842,7 +960,7 @@ def main() -> int:
         calls = [(h, [list(col) for col in zip(*seqs)], layers, wp) for h, seqs, layers, wp in calls]
         calls0 = [(h, [list(col) for col in zip(*seqs)], layers, wp) for h, seqs, layers, wp in calls0]
 
-    def run(seq_calls):
+    def run(seq_calls, s=s):
         for h, seqs, layers, wptr in seq_calls:
             if mirror:
                 for seq, c, fp, c0, n in seqs:
@@ -864,6 +982,14 @@ def main() -> int:
     # clocks up and the Infinity Cache evicted, then the timed steps: each
     # cycles to the ring touched longest ago (pool x ring bytes >= 512 MB)
     n_fills = clock_warmup(dev, args.warm_seconds, args.flush_mib)
+
+    if args.graph:
+        print(json.dumps({"workload": args.workload, "step": step_mode, "ring_pool": pool,
+                          "graph": graph_segment(rings, pool, calls, args.warmup, run, dev, R)}),
+              flush=True)
+        for r in rings:
+            r.close()
+        return 0
 
     if args.floor:
         fl, ceil = floor_segment(rings, pool, args.floor_launches, dev, R, None, None,
