@@ -720,7 +720,7 @@ def clock_warmup(dev, seconds: float, flush_mib: int) -> int:
     return n
 
 
-def floor_segment(rings, pool, launches, dev, R, attn_us, step_us, bytes_read):
+def floor_segment(rings, pool, launches, dev, R, attn_us, step_us, bytes_read, n_layer=1):
     """The ring_profile_floor kinds on layer 0, cycled over the pool (cold).
     Per launch: the device's back-to-back time (HIP events around a batch
     queued behind a RING_FLOOR_HOLD launch, so that the host's submission
@@ -772,7 +772,8 @@ def floor_segment(rings, pool, launches, dev, R, attn_us, step_us, bytes_read):
         ceil["attn_kernel"] = rd / attn_us
     tl = out.get("two_launch", {}).get("b2b_us")
     if tl and step_us:
-        ceil["step"] = tl / step_us
+        # layer 0's two-launch floor once per layer of the step
+        ceil["step"] = tl * n_layer / step_us
     return out, ceil
 
 
@@ -1117,7 +1118,7 @@ def main() -> int:
         floors, ceiling = floor_segment(
             rings, pool, args.floor_launches, dev, R, attn_us, ms_per_step * 1e3,
             np.mean([sum(algorithmic_bytes(w, layer_window(c, 0), geo.kv_total)["kv"] for c in cs)
-                     for cs in seg]))
+                     for cs in seg]), w.n_layer)
     for r in rings:
         r.close()
     line = {
