@@ -120,12 +120,8 @@ struct FusedSeqs {
   int32_t start[kFusedMaxSeq];       // first new position
   int32_t start_mod[kFusedMaxSeq];   // its slot
   int32_t n_new[kFusedMaxSeq];       // new rows this launch appends for this layer (0: none)
-  int32_t n_step_rows[kFusedMaxSeq]; // new rows of the step (for the index rebuild)
   int32_t committed[kFusedMaxSeq];   // noise positions committed + i
   int32_t lo[kFusedMaxSeq];          // this layer's visible ring positions: [lo, committed)
-  int32_t index[kFusedMaxSeq];       // nonzero: this launch also rebuilds the index state
-  int32_t full_lo[kFusedMaxSeq];     // lo of the full mask
-  int32_t swa_lo[kFusedMaxSeq];      // lo of the sliding-window mask
 };
 
 // Quotients by a launch constant d without a division: with
@@ -168,25 +164,17 @@ struct AttnArgs {
   int32_t vis_count[RING_MAX_SEQ_INTERNAL];
 };
 
-// The fused launch: the attention's arguments plus the deferred steps.
+// The fused launch: the attention's arguments plus the deferred steps.  It
+// appends the step's rows of this layer and writes their slot_pos entries;
+// the masks and the noise RoPE table are rebuilt later, by an append launch
+// without rows, before anything reads them (the fused launch does not).
 struct FusedAttnArgs {
   AttnArgs a;
   int32_t swa_layer;         // this layer attends with the sliding-window mask
   int32_t n_attn_blocks;     // work-groups of the launch
-  int32_t n_index_blocks;    // index blocks (256 slots each) per indexed sequence: the
-                             // sequence's work-groups take them in turn, work-group r
-                             // (in (KV head, split, row block) order) blocks r, r + R, ...
-                             // for R work-groups per sequence
   int32_t slot_stride;       // int32 per sequence in slot_pos
-  int32_t n_layer, a_step, trash_slot;
-  int64_t layer_stride;      // halves between layers of a sequence's ring
-  const double* inv_freq;    // [64] theta_i (device copy)
-  double theta[64];          // the same values, fetched by lane at kernel entry
+  double theta[64];          // theta_i, fetched by lane at kernel entry
   int32_t* slot_pos;         // [n_seq][slot_stride]
-  uint16_t* mask_full;       // [n_seq][q_len][kv_total]
-  uint16_t* mask_swa;        // [n_seq][q_len][kv_total] or nullptr
-  double* rope_noise_w;      // [n_seq][q_len][64][2]
-  float* rope_q_w;           // [n_seq][q_len][64][2]
   FusedSeqs fs;
 };
 

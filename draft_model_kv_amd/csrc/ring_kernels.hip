@@ -412,7 +412,7 @@ __device__ inline void attend_tile(const half8 (&kc)[8], const half8 (&vc)[8],
 // A fused launch's per-sequence fields of one sequence (wave-uniform).
 struct FusedLane {
   uint64_t k_new, v_new;
-  int start, start_mod, n_new, n_step_rows, committed, lo, index, full_lo, swa_lo;
+  int start, start_mod, n_new, committed, lo;
 };
 
 // Fetch them for every sequence at kernel entry, lane i holding sequence
@@ -420,7 +420,7 @@ struct FusedLane {
 // sequence `seq` with readlane once it is known.
 struct FusedLaneVec {
   uint64_t k_new, v_new;
-  int start, start_mod, n_new, n_step_rows, committed, lo, index, full_lo, swa_lo;
+  int start, start_mod, n_new, committed, lo;
   double theta;   // theta of frequency lane
 };
 
@@ -432,12 +432,8 @@ __device__ inline FusedLaneVec fused_fetch(const FusedAttnArgs& f) {
   v.start = f.fs.start[i];
   v.start_mod = f.fs.start_mod[i];
   v.n_new = f.fs.n_new[i];
-  v.n_step_rows = f.fs.n_step_rows[i];
   v.committed = f.fs.committed[i];
   v.lo = f.fs.lo[i];
-  v.index = f.fs.index[i];
-  v.full_lo = f.fs.full_lo[i];
-  v.swa_lo = f.fs.swa_lo[i];
   v.theta = f.theta[threadIdx.x & 63];
   return v;
 }
@@ -455,43 +451,18 @@ __device__ inline FusedLane fused_pick(const FusedLaneVec& v, int seq) {
   u.start = __builtin_amdgcn_readlane(v.start, seq);
   u.start_mod = __builtin_amdgcn_readlane(v.start_mod, seq);
   u.n_new = __builtin_amdgcn_readlane(v.n_new, seq);
-  u.n_step_rows = __builtin_amdgcn_readlane(v.n_step_rows, seq);
   u.committed = __builtin_amdgcn_readlane(v.committed, seq);
   u.lo = __builtin_amdgcn_readlane(v.lo, seq);
-  u.index = __builtin_amdgcn_readlane(v.index, seq);
-  u.full_lo = __builtin_amdgcn_readlane(v.full_lo, seq);
-  u.swa_lo = __builtin_amdgcn_readlane(v.swa_lo, seq);
   return u;
 }
-
-// Index-state arguments of sequence `seq` in a fused launch.
-__device__ inline StepArgs fused_index_args(const FusedAttnArgs& f, const FusedLane& fs, int seq) {
-  StepArgs sa{};
-  sa.slot_pos = f.slot_pos + (int64_t)seq * f.slot_stride;
-  sa.mask = f.mask_full + (int64_t)seq * f.a.q_len * f.a.kv_total;
-  sa.mask_swa = f.mask_swa ? f.mask_swa + (int64_t)seq * f.a.q_len * f.a.kv_total : nullptr;
-  sa.rope_noise = f.rope_noise_w + (int64_t)seq * f.a.q_len * 128;
-  sa.rope_q = f.rope_q_w + (int64_t)seq * f.a.q_len * 128;
-  sa.inv_freq = f.inv_freq;
-  sa.start = fs.start;
-  sa.start_mod = fs.start_mod;
-  sa.committed = fs.committed;
-  sa.lo = fs.full_lo;
-  sa.swa_lo = fs.swa_lo;
-  sa.n_new = fs.n_step_rows;
-  sa.cap = f.a.cap;
-  sa.q_len = f.a.q_len;
-  sa.kv_total = f.a.kv_total;
-  return sa;
-}
-
 
 // What a fused launch tells the attention body about its sequence's
 // deferred step (unused in a plain launch).
 struct FusedCtx {
   gcu16* k_new;             // this layer's new K rows, at this KV head's column
   gcu16* v_new;
-  const int32_t* slot_pos;  // the sequence's slot_pos row
+  int32_t* slot_pos;        // the sequence's slot_pos row (the new rows' entries are
+                            // written by the waves that store those rows)
   double invf;              // theta of frequency `lane`
   int kv_row;
   int start, start_mod, n_new, committed, lo, cap;
@@ -640,7 +611,7 @@ __device__ __forceinline__ void attend_noise_row(
     const AttnArgs& a, const FusedCtx& fx, const NoiseRow<MB>& nr, int r, uint16_t* kh,
     uint16_t* vh, uint16_t* rowk, uint16_t* rowv, int lane, int hl, int col, const QFrag<MB, QL>& q,
     const half8* q_lds, float (&m_run)[MB], float (&l_run)[MB], f32x16 (&o)[MB][4],
-    bool store_row) {
+    bool store_row, bool store_slot_pos) {
   double2 cs = nr.cs;
   int slot = a.cap + r;  // ring row of this layer and head
   if constexpr (FUSED) {
@@ -656,6 +627,11 @@ __device__ __forceinline__ void attend_noise_row(
   double xr, yr;
   rot_pair(f16_to_f64(nr.kx), f16_to_f64(nr.ky), cs.x, cs.y, xr, yr);
   const uint16_t kx = f64_to_f16_rne(xr), ky = f64_to_f16_rne(yr);
+  if constexpr (FUSED) {
+    // a new row's slot now holds its position (the tile pass of this launch
+    // hides the new slots whatever slot_pos says)
+    if (store_slot_pos && r >= a.q_len && lane == 0) fx.slot_pos[slot] = fx.start + (r - a.q_len);
+  }
   if (store_row) {
     uint16_t* kt = kh + (int64_t)(slot >> 5) * kTileHalves;
     uint16_t* vt = vh + (int64_t)(slot >> 5) * kTileHalves;
@@ -912,16 +888,6 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
     fx.cap = a.cap;
     fx.swa = fa->swa_layer;
   }
-  // Index blocks of this work-group (fused launch, when the launch rebuilds
-  // the sequence's index state): blocks ix_blk, ix_blk + ix_step, ... of its
-  // own sequence (the work-groups of a sequence take them in turn, after
-  // their attention); block 0 also writes the noise RoPE tables.
-  int ix_blk = -1, ix_step = 1;
-  if constexpr (FUSED) {
-    ix_step = a.n_head_kv * a.n_split * a.n_rb;
-    const int rank_in_seq = (g * a.n_split + split) * a.n_rb + row0 / MP;
-    if (fl.index && rank_in_seq < fa->n_index_blocks) ix_blk = rank_in_seq;
-  }
   // The destinations and the few integers the store needs are computed
   // up front and pass through an empty asm statement that redefines them, so the
   // compiler keeps them in SGPRs instead of re-loading kernel arguments in
@@ -1031,11 +997,6 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
   uint32_t mw[MB][8];
   int4 spv[4];
   load_tile(ring_tile(min(tile, tile_last)), kc, vc, mw, spv);
-  // slot_pos of this work-group's index slot (read by every fused work-group,
-  // used by those with an index block; issued with the other loads)
-  int ix_sp = 0;
-  if constexpr (FUSED)
-    ix_sp = fx.slot_pos[min(max(ix_blk, 0) * 256 + (int)threadIdx.x, a.cap - 1)];
   // Fused launch, before a tile is attended: its mask words from slot_pos.
   auto prep_tile = [&](int rt, half8 (&kc)[8], half8 (&vc)[8], uint32_t (&mw)[MB][8],
                        const int4 (&spv)[4]) {
@@ -1136,12 +1097,13 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
   uint16_t* rowv = rowk + kHeadDim;
   if (rank < n_extra) {
     const bool store_rows = row0 == 0;  // one row block stores the rotated rows
+    const bool store_sp = store_rows && g == 0;  // and KV head 0 their slot_pos entries
     attend_noise_row<MB, FUSED, QL>(a, fx, nr, rank, kh, vh, rowk, rowv, lane, hl, col, qf, q_lds, m_run,
-                         l_run, o, store_rows);
+                         l_run, o, store_rows, store_sp);
     for (int r = rank + n_waves; r < n_extra; r += n_waves) {
       load_noise_row<MB, FUSED>(a, fx, seq, g, r, mask_seq, qrow, lane, nr);
       attend_noise_row<MB, FUSED, QL>(a, fx, nr, r, kh, vh, rowk, rowv, lane, hl, col, qf, q_lds, m_run,
-                           l_run, o, store_rows);
+                           l_run, o, store_rows, store_sp);
     }
   }
 
@@ -1199,29 +1161,6 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
     merge_store<MB, NW, 2, SHARE>(ep, lds, sm_m, sm_l, m_run, l_run, o, lane);
   else
     merge_store<MB, NW, 3, SHARE>(ep, lds, sm_m, sm_l, m_run, l_run, o, lane);
-  if constexpr (FUSED) {
-    const StepArgs sa = fused_index_args(*fa, fl, seq);
-    for (int ix = ix_blk; ix >= 0 && ix < fa->n_index_blocks; ix += ix_step) {
-      const int sidx = ix * 256 + (int)threadIdx.x;
-      // slot_pos before the step (anything past cap); the first block's was
-      // loaded with the other loads
-      const int sp = ix == ix_blk ? ix_sp : fx.slot_pos[min(sidx, a.cap - 1)];
-      index_slot(sa, sidx, sp);
-      if (ix == 0) {
-        // the noise RoPE table for later plain launches, as the append kernel
-        // builds it (fp64 sincos, and its fp32 rounding)
-        for (int item = threadIdx.x; item < a.q_len * 64; item += NT) {
-          const int i = item >> 6, f = item & 63;
-          double sn, cs;
-          sincos_angle((double)(fx.committed + i) * fa->theta[f], &sn, &cs);
-          sa.rope_noise[2 * item] = cs;
-          sa.rope_noise[2 * item + 1] = sn;
-          sa.rope_q[2 * item] = (float)cs;
-          sa.rope_q[2 * item + 1] = (float)sn;
-        }
-      }
-    }
-  }
 }
 
 template <int MB, int NW, int RP, bool FUSED, bool SHORT>
@@ -1243,10 +1182,8 @@ __device__ __forceinline__ void attn_entry(const AttnArgs& a, const FusedAttnArg
   if constexpr (FUSED) {
     fv = fused_fetch(*fa);
     asm volatile("" ::"v"(fv.k_new), "v"(fv.v_new), "v"(fv.start), "v"(fv.start_mod),
-                 "v"(fv.n_new), "v"(fv.n_step_rows), "v"(fv.committed), "v"(fv.lo),
-                 "v"(fv.index), "v"(fv.full_lo), "v"(fv.swa_lo), "v"(fv.theta),
-                 "s"(fa->slot_pos), "s"(fa->slot_stride), "s"(fa->swa_layer),
-                 "s"(fa->n_index_blocks));
+                 "v"(fv.n_new), "v"(fv.committed), "v"(fv.lo), "v"(fv.theta),
+                 "s"(fa->slot_pos), "s"(fa->slot_stride), "s"(fa->swa_layer));
   }
   asm volatile("" ::"s"(a.kring), "s"(a.vring), "s"(a.mask), "s"(a.rope_noise), "s"(a.rope_q),
                "s"(a.q),

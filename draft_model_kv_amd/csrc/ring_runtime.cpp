@@ -227,6 +227,11 @@ struct ring {
   std::vector<int64_t> next_pos, held_lo, committed;
   std::vector<std::vector<int64_t>> mirror_pos;  // per sequence: position in each mirror slot, -1 empty
   std::vector<Pending> pending;                   // per sequence
+  // per sequence: slot_pos is current but the masks and the noise RoPE table
+  // still hold an earlier step's (a fused launch wrote the new rows' slot_pos
+  // entries and left the rest for an index-only append launch, which runs
+  // before anything reads them: a plain attention launch or a mask read)
+  std::vector<uint8_t> index_owed;
   std::vector<double> inv_freq_host;
   hipStream_t last_stream = nullptr;
   // profiling: per kernel kind, event pairs (start, end) and how many are used
@@ -313,20 +318,48 @@ int flush_seq(ring* r, int32_t seq) {
     a.row0 = 0;
     a.n_rows = (int32_t)p.n_new;
     a.n_pad = r->geo.a_step - (int32_t)p.n_new;
-    a.do_mask = p.index_left ? 1 : 0;
+    a.do_mask = (p.index_left || r->index_owed[seq]) ? 1 : 0;
     a.layer_skip = ~p.layers_left;
     hipEvent_t t0, t1;
     next_events(r, RING_KERNEL_STEP, &t0, &t1);
     if (int e = check_launch(launch_step(a, r->last_stream, t0, t1), "deferred append"))
       return e;
+    if (a.do_mask) r->index_owed[seq] = 0;
   }
   p = Pending{};
   return RING_OK;
 }
 
+// Rebuild the masks and the noise RoPE table of `seq` from its slot_pos and
+// state if a fused launch left them owed: an append launch with no rows.
+int flush_index(ring* r, int32_t seq) {
+  if (!r->index_owed[seq]) return RING_OK;
+  StepArgs a = step_args(r, seq);
+  const int64_t c = r->committed[seq];
+  const int64_t win = std::min<int64_t>(c, r->cfg.cap);
+  a.start = c;
+  a.start_mod = (int32_t)(c % r->cfg.cap);
+  a.committed = c;
+  a.lo = r->held_lo[seq];
+  a.swa_lo = c - std::min<int64_t>(r->cfg.swa_window, win);
+  a.n_new = 0;
+  a.row0 = 0;
+  a.n_rows = 0;
+  a.n_pad = 0;
+  a.do_mask = 1;
+  hipEvent_t t0, t1;
+  next_events(r, RING_KERNEL_STEP, &t0, &t1);
+  if (int e = check_launch(launch_step(a, r->last_stream, t0, t1), "index rebuild")) return e;
+  r->index_owed[seq] = 0;
+  return RING_OK;
+}
+
+// Everything deferred steps still owe, for every sequence.
 int flush_all(ring* r) {
-  for (int32_t seq = 0; seq < r->cfg.n_seq; ++seq)
+  for (int32_t seq = 0; seq < r->cfg.n_seq; ++seq) {
     if (int e = flush_seq(r, seq)) return e;
+    if (int e = flush_index(r, seq)) return e;
+  }
   return RING_OK;
 }
 
@@ -400,6 +433,7 @@ int ring_init(const ring_config* cfg, void* workspace, size_t workspace_bytes, v
     r->mirror_pos.assign(cfg->n_seq, std::vector<int64_t>(cfg->cap, -1));
   }
   r->pending.assign(cfg->n_seq, Pending{});
+  r->index_owed.assign(cfg->n_seq, 0);
   r->next_pos.assign(cfg->n_seq, 0);
   r->held_lo.assign(cfg->n_seq, 0);
   r->committed.assign(cfg->n_seq, 0);
@@ -494,10 +528,12 @@ int check_step(const ring* r, int32_t seq, int64_t committed, const void* k_new,
   return RING_OK;
 }
 
+// State after an append whose last launch rebuilt the index state.
 void set_state(ring* r, int32_t seq, int64_t committed, const Plan& p) {
   r->next_pos[seq] = committed;
   r->held_lo[seq] = p.lo;
   r->committed[seq] = committed;
+  r->index_owed[seq] = 0;
 }
 
 // The append launches of one checked step (bulk chunks or the fold-in).
@@ -791,9 +827,7 @@ int ring_begin_step_mirror(ring_t* r, int32_t seq, int64_t committed, const ring
     if (int e = check_launch(launch_step(a, s, t0, t1), "append from features")) return e;
     row0 += n;
   } while (row0 < p.n_new);
-  r->next_pos[seq] = committed;
-  r->held_lo[seq] = p.lo;
-  r->committed[seq] = committed;
+  set_state(r, seq, committed, p);
   return ok();
 }
 
@@ -911,25 +945,15 @@ int attn_launch(ring* r, int32_t layer, const void* q, const void* k_noise, cons
   // Deferred steps owing this layer's rows or the index state: one fused
   // launch appends and rebuilds them and attends.
   bool fuse = false;
-  for (const Pending& p : r->pending) fuse |= p.active && ((p.layers_left & bit) || p.index_left);
+  for (const Pending& p : r->pending) fuse |= p.active && (p.layers_left & bit);
   if (fuse) {
     FusedAttnArgs f{};
     f.a = a;
     f.a.n_rb = r->L.n_rb;
     f.swa_layer = swa ? 1 : 0;
     f.n_attn_blocks = r->cfg.n_seq * r->cfg.n_head_kv * n_split * r->L.n_rb;
-    f.n_index_blocks = (r->geo.kv_total + 255) / 256;
     f.slot_stride = (int32_t)r->L.slot_stride;
-    f.n_layer = r->cfg.n_layer;
-    f.a_step = r->geo.a_step;
-    f.trash_slot = r->geo.trash_slot;
-    f.layer_stride = (int64_t)r->cfg.n_head_kv * a.head_stride;
-    f.inv_freq = r->inv_freq;
     f.slot_pos = r->slot_pos;
-    f.mask_full = r->mask;
-    f.mask_swa = r->mask_swa;
-    f.rope_noise_w = r->rope_noise;
-    f.rope_q_w = r->rope_q;
     const int64_t kv_row = r->geo.kv_row;
     for (int i = 0; i < 64; ++i) f.theta[i] = r->inv_freq_host[i];
     FusedSeqs& fs = f.fs;
@@ -942,10 +966,6 @@ int attn_launch(ring* r, int32_t layer, const void* q, const void* k_noise, cons
       if (!p.active) continue;
       fs.start[i] = (int32_t)p.start;
       fs.start_mod[i] = (int32_t)(p.start % cap);
-      fs.n_step_rows[i] = (int32_t)p.n_new;
-      fs.full_lo[i] = (int32_t)p.lo;
-      fs.swa_lo[i] = (int32_t)p.swa_lo;
-      fs.index[i] = p.index_left ? 1 : 0;
       if ((p.layers_left & bit) && p.n_new > 0) {
         fs.k_new[i] = reinterpret_cast<uint64_t>(p.k + (int64_t)layer * p.n_new * kv_row);
         fs.v_new[i] = reinterpret_cast<uint64_t>(p.v + (int64_t)layer * p.n_new * kv_row);
@@ -953,13 +973,21 @@ int attn_launch(ring* r, int32_t layer, const void* q, const void* k_noise, cons
       }
     }
     if (int e = check_launch(launch_attn_fused(f, s, t0, t1), "ring_attn (fused step)")) return e;
-    for (Pending& p : r->pending) {
+    for (int32_t i = 0; i < r->cfg.n_seq; ++i) {
+      Pending& p = r->pending[i];
       if (!p.active) continue;
       p.layers_left &= ~bit;
-      p.index_left = false;
+      if (p.index_left) {
+        // slot_pos of the new rows is written; the masks and table are owed
+        p.index_left = false;
+        r->index_owed[i] = 1;
+      }
       if (!p.layers_left) p = Pending{};
     }
   } else {
+    // a plain launch reads the masks and the noise RoPE table
+    for (int32_t i = 0; i < r->cfg.n_seq; ++i)
+      if (int e = flush_index(r, i)) return e;
     a.n_rb = r->L.n_rb;
     if (int e = check_launch(launch_attn(a, s, t0, t1), "ring_attn")) return e;
   }

@@ -178,10 +178,12 @@ int ring_begin_step(ring_t* r, int32_t seq, int64_t committed,
  * arguments, plan, checks and result as ring_begin_step.  For a fold-in plan
  * nothing is enqueued here: the next ring_attn of each layer appends that
  * layer's rows itself (and attends them as keys of their own, not through
- * the ring tiles that hold their slots) and the first of them also rebuilds
- * slot_pos, the masks and the noise RoPE table, all in its one launch; pad
- * rows are not written
- * (the trash slot keeps its zeros).  k_new and v_new must therefore stay
+ * the ring tiles that hold their slots) and writes their slot_pos entries,
+ * all in its one launch; the masks and the noise RoPE table, which that
+ * launch does not read, are rebuilt by an append launch without rows before
+ * anything reads them (a plain attention launch, ring_read_mask*, an append
+ * of the sequence).  Pad rows are not written (the trash slot keeps its
+ * zeros).  k_new and v_new must therefore stay
  * valid until every layer's ring_attn has been enqueued and the stream has
  * passed them.  Whatever a deferred step still owes (layers whose attention
  * has not run) is appended by the ordinary append kernel on the ring's last

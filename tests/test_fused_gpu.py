@@ -162,6 +162,43 @@ def test_fused_flush_paths():
     d.close()
 
 
+def test_plain_launch_after_fused_rebuilds_index():
+    """The fused launch leaves the masks and the noise RoPE table owed; a
+    second attention of the same layer and step is a plain launch, which reads
+    them, so they are rebuilt first.  Two layers, one sliding-window."""
+    w = small(cap=64, n_layer=2, swa_window=12, swa_layers=0b10, seed=320)
+    d = Driver(w)
+    for t, c in enumerate([40, 41, 49, 58, 70, 60, 61]):
+        d.step(0, c, deferred=True)
+        d.check_attn_layers(2 * t)       # fused launches append and attend
+        d.check_attn_layers(2 * t + 1)   # plain launches on the rebuilt state
+        d.check_index(0)
+        for layer in range(2):
+            d.check_rows(0, layer)
+    d.close()
+
+
+def test_eager_step_after_fused_steps():
+    """Fused steps, then an eager step and a mask read in between: the owed
+    index state is rebuilt by the eager append itself."""
+    d = Driver(small(cap=96, seed=321))
+    for c in [50, 51, 59]:
+        d.step(0, c, deferred=True)
+        d.check_attn_layers(c)
+    d.step(0, 62)                        # eager
+    d.check_attn(0, 62)
+    d.check_index(0)
+    d.step(0, 70, deferred=True)
+    d.check_attn_layers(70)
+    d.check_index(0)
+    d.step(0, 71, deferred=True)
+    d.check_attn_layers(71)
+    d.step(0, 80)                        # eager right after a fused launch
+    d.check_attn_layers(80)
+    d.check_index(0)
+    d.close()
+
+
 # ---------------------------------------------------------------------------
 # Whole workloads through the fused step (the bench's default step), at full
 # size: checkpoints every 50 / 32 / 40 steps, at every cap crossing and at
