@@ -327,15 +327,52 @@ struct QFrag {
   half8 lo[kLds ? 1 : MB][kLds ? 1 : 8];
 };
 
-// One 32-slot tile: S^T = K Q^T (Q as hi + lo F16), additive mask, online
-// softmax, O^T += V^T P^T.
+// Additive mask of a tile from its mask words (plain launch): accumulator
+// row j = 4 jj + u of query block mb takes mw[mb][2 jj + (u >> 1)], two F16
+// per word, the low half for even u.
+template <int MB>
+struct MaskWords {
+  const uint32_t (&mw)[MB][8];
+  __device__ inline void operator()(int mb, f32x16& s) const {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const uint32_t w = mw[mb][2 * (j >> 2) + ((j & 3) >> 1)];
+      s[j] += (j & 1) ? f16_hi(w) : f16_lo(w);
+    }
+  }
+};
+
+// Visibility of a tile from its slot_pos (fused launch): slot s is visible
+// when its position p lies in [lo, hi), tested as (unsigned)(p - lo) < span
+// with span = hi - lo; a hidden slot's score becomes -inf.  When the launch
+// attends the step's new rows as extra keys, hi is their first position
+// `start`, which hides their slots whatever the tile's load finds there: the
+// new rows' positions (written by another wave of this launch) are >= start,
+// and an older occupant of such a slot lies below lo (evicted: position
+// start + j - cap < committed - cap <= lo) or at or above start (a rolled-back
+// row).  Otherwise hi = committed.  sp[jj] holds slots 8 jj + 4 hl + 0..3,
+// accumulator rows j = 4 jj + 0..3.
+struct SlotVis {
+  const int4 (&sp)[4];
+  uint32_t lo, span;
+  __device__ static inline int pos(const int4& v, int u) {
+    return u == 0 ? v.x : u == 1 ? v.y : u == 2 ? v.z : v.w;
+  }
+  __device__ inline void operator()(int, f32x16& s) const {
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      s[j] = (uint32_t)pos(sp[j >> 2], j & 3) - lo < span ? s[j] : kNegInf;
+  }
+};
+
+// One 32-slot tile: S^T = K Q^T (Q as hi + lo F16), mask, online softmax,
+// O^T += V^T P^T.
 //   kc, vc   K and V chunks (fragment order, see ring_layout.h)
-//   mw       mask of accumulator rows j = 4 jj + u, two F16 per word:
-//            mw[mb][2 jj + (u >> 1)], low half for even u
+//   mask     MaskWords or SlotVis, applied to S^T of each query block
 //   limit    rows r >= limit of this tile are hidden (-inf)
-template <int MB, bool QL>
+template <int MB, bool QL, class Mask>
 __device__ inline void attend_tile(const half8 (&kc)[8], const half8 (&vc)[8],
-                                   const uint32_t (&mw)[MB][8], int limit, int hl,
+                                   const Mask& mask, int limit, int hl,
                                    const QFrag<MB, QL>& q, const half8* q_lds, int lane,
                                    float (&m_run)[MB], float (&l_run)[MB],
                                    f32x16 (&o)[MB][4]) {
@@ -356,11 +393,7 @@ __device__ inline void attend_tile(const half8 (&kc)[8], const half8 (&vc)[8],
       s = mfma32(kc[c], ql, s);
     }
     float mx = kNegInf;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const uint32_t w = mw[mb][2 * (j >> 2) + ((j & 3) >> 1)];
-      s[j] += (j & 1) ? f16_hi(w) : f16_lo(w);
-    }
+    mask(mb, s);
     if (limit < kTile) {  // ragged tile: rows r >= limit are not ring slots
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
@@ -468,34 +501,6 @@ struct FusedCtx {
   int start, start_mod, n_new, committed, lo, cap;
   int swa;                  // sliding-window layer: causal noise block
 };
-
-// Mask words of a tile from its slot_pos (fused launch): slot s is visible
-// when its position lies in [lo, committed), the same for every query; the
-// step's new slots are not (their rows are attended as extra keys, and the
-// tile may hold their old rows or, being written by another wave of this
-// launch, the new ones).  spv[jj] holds slots 8 jj + 4 (lane / 32) + 0..3.
-template <int MB>
-__device__ __forceinline__ void tile_mask_words(const FusedCtx& fx, int tile, int hl,
-                                                const int4 (&spv)[4], uint32_t (&mw)[MB][8]) {
-#pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
-    const int sp4[4] = {spv[jj].x, spv[jj].y, spv[jj].z, spv[jj].w};
-    uint32_t h[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int s = tile * kTile + 8 * jj + 4 * hl + u;
-      int d = s - fx.start_mod;
-      if (d < 0) d += fx.cap;
-      const bool is_new = s < fx.cap && d < fx.n_new;
-      h[u] = (!is_new && sp4[u] >= fx.lo && sp4[u] < fx.committed) ? 0x0000u : 0xFC00u;
-    }
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      mw[mb][2 * jj] = h[0] | (h[1] << 16);
-      mw[mb][2 * jj + 1] = h[2] | (h[3] << 16);
-    }
-  }
-}
 
 // Work-group: NW waves for one (sequence, KV head, split).  Every split
 // runs the same body; the q_len noise rows of a (sequence, head) are spread
@@ -836,8 +841,8 @@ __device__ __forceinline__ void merge_store(const EpilogueArgs& a, unsigned char
 
 // SHORT: every wave attends at most one ring tile.  Then nothing is fetched
 // ahead, the query fragments are read from LDS at each use instead of held in
-// registers, and a plain launch's work-group shares its merge bytes with the
-// prologue, so that two work-groups fit one CU.
+// registers, and the work-group shares its merge bytes with the prologue, so
+// that two work-groups fit one CU.
 template <int MB, int NW, int RP, bool FUSED, bool SHORT>
 __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs* fa,
                                           const FusedLane& fl, double theta_lane, int unit,
@@ -845,7 +850,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
                                           unsigned char* lds, float (*sm_m)[MB * 32],
                                           float (*sm_l)[MB * 32]) {
   constexpr bool QL = MB > 1 || SHORT;
-  constexpr bool SHARE = SHORT && !FUSED;
+  constexpr bool SHARE = SHORT;
   using S = AttnShape<MB, NW, FUSED, SHARE>;
   constexpr int MP = S::MP, NT = S::NT;
   const int lane = threadIdx.x & 63;
@@ -997,12 +1002,6 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
   uint32_t mw[MB][8];
   int4 spv[4];
   load_tile(ring_tile(min(tile, tile_last)), kc, vc, mw, spv);
-  // Fused launch, before a tile is attended: its mask words from slot_pos.
-  auto prep_tile = [&](int rt, half8 (&kc)[8], half8 (&vc)[8], uint32_t (&mw)[MB][8],
-                       const int4 (&spv)[4]) {
-    if constexpr (FUSED) tile_mask_words<MB>(fx, rt, hl, spv, mw);
-  };
-
   // ---- 2. queries: rotate at committed + i, scale by log2(e)/sqrt(d),
   //      split into hi + lo F16 (fragment order [mb][hi/lo][chunk][lane]);
   //      queries past q_len * group are zero.
@@ -1107,6 +1106,20 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
     }
   }
 
+  // Attend ring tile rt with its mask words (plain launch) or with the
+  // visibility of its slots from their slot_pos (fused launch).
+  auto attend = [&](int rt, const half8 (&kc)[8], const half8 (&vc)[8],
+                    const uint32_t (&mw)[MB][8], const int4 (&spv)[4]) {
+    const int limit = a.cap - rt * kTile;
+    if constexpr (FUSED) {
+      const int hi = fx.n_new > 0 ? fx.start : fx.committed;
+      const SlotVis vis{spv, (uint32_t)fx.lo, (uint32_t)(hi - fx.lo)};
+      attend_tile<MB, QL>(kc, vc, vis, limit, hl, qf, q_lds, lane, m_run, l_run, o);
+    } else {
+      attend_tile<MB, QL>(kc, vc, MaskWords<MB>{mw}, limit, hl, qf, q_lds, lane, m_run, l_run, o);
+    }
+  };
+
   // ---- 4. ring tiles.  One query block: the next tile's loads are issued
   //      before the current tile is processed (two tiles in registers); two
   //      query blocks have no room for that.  (Two tiles ahead, through three
@@ -1119,9 +1132,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
       uint32_t mn[MB][8];
       int4 spn[4];
       load_tile(ring_tile(tile + NW), kn, vn, mn, spn);
-      prep_tile(ring_tile(tile), kc, vc, mw, spv);
-      attend_tile<MB, QL>(kc, vc, mw, a.cap - ring_tile(tile) * kTile, hl, qf, q_lds, lane, m_run,
-                      l_run, o);
+      attend(ring_tile(tile), kc, vc, mw, spv);
 #pragma unroll
       for (int c = 0; c < 8; ++c) { kc[c] = kn[c]; vc[c] = vn[c]; }
 #pragma unroll
@@ -1134,17 +1145,14 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
       }
       tile += NW;
     }
-    if (tile < t1) {
-      prep_tile(ring_tile(tile), kc, vc, mw, spv);
-      attend_tile<MB, QL>(kc, vc, mw, a.cap - ring_tile(tile) * kTile, hl, qf, q_lds, lane, m_run,
-                      l_run, o);
-    }
+    if (tile < t1) attend(ring_tile(tile), kc, vc, mw, spv);
+  } else if constexpr (SHORT) {
+    // at most NW tiles per split: at most one per wave
+    if (tile < t1) attend(ring_tile(tile), kc, vc, mw, spv);
   } else {
     while (tile < t1) {
       const int next = tile + NW;
-      prep_tile(ring_tile(tile), kc, vc, mw, spv);
-      attend_tile<MB, QL>(kc, vc, mw, a.cap - ring_tile(tile) * kTile, hl, qf, q_lds, lane, m_run,
-                      l_run, o);
+      attend(ring_tile(tile), kc, vc, mw, spv);
       if (next < t1) load_tile(ring_tile(next), kc, vc, mw, spv);
       tile = next;
     }
@@ -1165,7 +1173,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
 
 template <int MB, int NW, int RP, bool FUSED, bool SHORT>
 __device__ __forceinline__ void attn_entry(const AttnArgs& a, const FusedAttnArgs* fa) {
-  using S = AttnShape<MB, NW, FUSED, SHORT && !FUSED>;
+  using S = AttnShape<MB, NW, FUSED, SHORT>;
   __shared__ __attribute__((aligned(16))) unsigned char lds[S::kTotalLds];
   __shared__ float sm_m[NW][S::MP];
   __shared__ float sm_l[NW][S::MP];
@@ -1223,11 +1231,10 @@ __global__ __launch_bounds__(NW * 64, SHORT ? 2 : 1) void k_ring_attn(AttnArgs a
 }
 
 // The fused launch: the attention work-groups (same mapping as k_ring_attn),
-// which also append the step's new rows and rebuild the index state (slot_pos,
-// masks, noise RoPE table) of the sequences that owe it.
+// which also append the step's new rows of this layer (K rotated at its
+// position, V) and write their slot_pos entries.
 template <int MB, int NW, int RP, bool SHORT>
-__global__ __launch_bounds__(NW * 64) void k_ring_attn_fused(FusedAttnArgs f) {
-  static_assert(NW * 64 == 256, "an index block is one slot per thread");
+__global__ __launch_bounds__(NW * 64, SHORT ? 2 : 1) void k_ring_attn_fused(FusedAttnArgs f) {
   attn_entry<MB, NW, RP, true, SHORT>(f.a, &f);
 }
 
