@@ -6,7 +6,9 @@ A step is one pass of the whole ring path for one sequence: the fold-in
 table) and ring_attn (masked GQA attention of the 8 noise queries over the
 4096-slot ring, split-K + merge).  By default the fold-in is handed to the
 attention launch (ring_begin_step_deferred, then ring_attn: one attention
-launch that appends, rebuilds the index state and attends, then the merge);
+launch that appends the new rows, writes their slot_pos entries and attends,
+then the merge; the masks and noise RoPE table, which that launch does not
+read, are rebuilt only when a plain launch or a read needs them);
 --step eager gives it a launch of its own (ring_begin_step).  On a ring of
 several sequences (batched_seqs) a step is one ring_begin_step_batch over all
 of them, then one ring_attn per layer.
@@ -460,11 +462,11 @@ def summarize_profiles(out_dir: str) -> int:
     step = (bl or {}).get("config", {}).get("step", "eager")
     if step == "fused":
         # the bench line's bytes of the fused launch (it also reads the new
-        # rows and slot_pos and writes the rows and the index state)
+        # rows and slot_pos, and writes the rows and their slot_pos entries)
         alg_attn = bl["roofline"]["bytes_per_launch"]
-        what = ("visible K/V rows, queries, noise rows, the step's new rows, slot_pos; the "
-                "index state it rebuilds")
-        wrote = "split partials, the noise and new rows stored to the ring, the index state"
+        what = "visible K/V rows, queries, noise rows, the step's new rows, slot_pos"
+        wrote = ("split partials, the noise and new rows stored to the ring, the new rows' "
+                 "slot_pos entries")
     else:
         what = "visible K/V rows, queries, noise rows, mask"
         wrote = "split partials and the noise rows stored to the ring"
@@ -1067,15 +1069,13 @@ def main() -> int:
     fused_extra = 0.0
     if fused and not mirror:
         # the fused launch also reads each new row (K and V, F16) and writes it
-        # to the ring, reads slot_pos instead of the mask, and (first layer of
-        # a step) writes slot_pos entries, the mask and the noise RoPE table
+        # to the ring, reads slot_pos instead of the mask, and writes the new
+        # rows' slot_pos entries
         seg_rows = [sum(n for _, _, _, _, n in steps_in[0][t // pool][0])
                     for t in range(args.warmup + args.steps, total)]
         rows = float(np.mean(seg_rows))
         fused_extra = (rows * w.kv_row * 2 * 2 * 2 + w.n_seq * w.cap * 4
-                       - w.n_seq * w.q_len * geo.kv_total * 2
-                       + (w.n_seq * (w.q_len * geo.kv_total * 2 + w.q_len * 64 * 2 * 12)
-                          + rows * 4) / w.n_layer)
+                       - w.n_seq * w.q_len * geo.kv_total * 2 + rows * 4)
         per_launch += fused_extra
     per_call = mean_bytes("ring_attn") + fused_extra
     attn_us = prof["k_ring_attn"]["avg_us"]
