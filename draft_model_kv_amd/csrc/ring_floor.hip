@@ -14,12 +14,13 @@
 //           partials stored with device-scope coherence (sc1, write-through),
 //           the stores waited for, one atomic ticket per work-group on a
 //           counter per (sequence, head, row block); the work-group that
-//           draws the last ticket loads every split's partial (sc1) and
-//           writes their sum
+//           draws the last ticket loads every split's partial (sc1, eight
+//           splits' loads in flight at a time) and writes their sum
 //   kind 4  kind 2 with a bounded barrier instead: every work-group of a
 //           (sequence, head, row block) waits for all its splits' tickets
 //           (at most 2^20 polls with s_sleep, then an error count), then
-//           sums its 1/n_split slice of every split's partial
+//           sums its 1/n_split slice of every split's partial (loads
+//           batched as in kind 3)
 //   kind 5  (host side) kind 2, then the ring's own merge launch over those
 //           partials
 //   kind 7  kind 1 plus, per tile, the attention's matrix-core contractions
@@ -199,17 +200,42 @@ __global__ __launch_bounds__(256) void k_ring_floor(FloorArgs a) {
       const int64_t base_row = ((int64_t)unit * a.n_split * a.n_rb + rb) * 32;  // split 0
       const int64_t split_f4 = (int64_t)a.n_rb * 32 * kHeadDim / 4;            // between splits
       float* outp = a.out + ((int64_t)unit * a.n_rb + rb) * 32 * kHeadDim;
+      // float4 idx of split t's partial (sc1 load; past the buffer: zero)
+      auto load_f4 = [&](int t, int idx) {
+        const uint32_t off = (uint32_t)(((base_row * kHeadDim / 4) + t * split_f4 + idx) * 16);
+        return __builtin_amdgcn_raw_buffer_load_b128(pr, off, 0, kPolicySc1);
+      };
+      // sum over splits t = t_first, t_first + t_step, ... < n_split of float4
+      // idx: eight loads in flight at a time, issued before any is added
+      auto sum_splits = [&](int t_first, int t_step, int idx) {
+        f32x4 o = {};
+        for (int tb = t_first; tb < a.n_split; tb += 8 * t_step) {
+          f32x4 ld[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) ld[u] = load_f4(min(tb + u * t_step, a.n_split - 1), idx);
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            if (tb + u * t_step < a.n_split) o += ld[u];
+        }
+        return o;
+      };
       if constexpr (KIND == 3) {
         if (ticket + 1 != (uint32_t)a.n_split) return;
         if (threadIdx.x == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // the four float4 of each thread: 32 loads in flight per batch
         f32x4 o[4] = {};
-        for (int t = 0; t < a.n_split; ++t) {
+        for (int tb = 0; tb < a.n_split; tb += 8) {
+          f32x4 ld[8][4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint32_t off =
-                (uint32_t)(((base_row * kHeadDim / 4) + t * split_f4 + i * 256 + threadIdx.x) * 16);
-            o[i] += __builtin_amdgcn_raw_buffer_load_b128(pr, off, 0, kPolicySc1);
-          }
+          for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              ld[u][i] = load_f4(min(tb + u, a.n_split - 1), i * 256 + threadIdx.x);
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            if (tb + u < a.n_split)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) o[i] += ld[u][i];
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) *(f32x4*)(outp + (i * 256 + threadIdx.x) * 4) = o[i];
@@ -236,23 +262,14 @@ __global__ __launch_bounds__(256) void k_ring_floor(FloorArgs a) {
           for (int i = threadIdx.x; i < sf; i += 256) {
             const int idx = split * sf + i;
             if (idx >= 1024) break;
-            f32x4 o = {};
-            for (int t = 0; t < a.n_split; ++t)
-              o += __builtin_amdgcn_raw_buffer_load_b128(
-                  pr, (uint32_t)(((base_row * kHeadDim / 4) + t * split_f4 + idx) * 16), 0,
-                  kPolicySc1);
-            *(f32x4*)(outp + idx * 4) = o;
+            *(f32x4*)(outp + idx * 4) = sum_splits(0, 1, idx);
           }
         } else {
           const int groups = 256 / sf;
           const int grp = threadIdx.x / sf, e = threadIdx.x - grp * sf;
           const int idx = min(split * sf + e, 1023);
           f32x4 o = {};
-          if (grp < groups)
-            for (int t = grp; t < a.n_split; t += groups)
-              o += __builtin_amdgcn_raw_buffer_load_b128(
-                  pr, (uint32_t)(((base_row * kHeadDim / 4) + t * split_f4 + idx) * 16), 0,
-                  kPolicySc1);
+          if (grp < groups) o = sum_splits(grp, groups, idx);
           red[threadIdx.x] = o;
           __syncthreads();
           if (grp == 0 && split * sf + e < 1024) {

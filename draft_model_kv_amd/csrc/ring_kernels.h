@@ -162,6 +162,12 @@ struct AttnArgs {
   // circularly modulo ring_tiles (the window's slots, slot = position % cap).
   int32_t vis_first[RING_MAX_SEQ_INTERNAL];
   int32_t vis_count[RING_MAX_SEQ_INTERNAL];
+  // Cross-split merge inside the launch (kernels whose waves stream several
+  // tiles, 2..kInKernelMergeMaxSplits splits): one ticket counter per
+  // (sequence x KV head, row block), zero before the launch and left zero by
+  // it; nullptr: the partials are merged by launch_merge.  (Last, so that
+  // the other fields keep their kernel-argument offsets.)
+  uint32_t* tickets;
 };
 
 // The fused launch: the attention's arguments plus the deferred steps.  It
@@ -213,6 +219,11 @@ struct FloorArgs {
 hipError_t launch_step(const StepArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
 hipError_t launch_step_batch(const StepBatchArgs& b, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
+// Whether launch_attn / launch_attn_fused pick the kernel whose waves attend
+// at most one ring tile each (at most 4 tiles per split); that kernel ignores
+// a.tickets and always leaves the merge to launch_merge.
+bool attn_short_waves(const AttnArgs& a);
+constexpr int kInKernelMergeMaxSplits = 16;
 // The fused launch: appends and index work of a.fs[] plus the attention.
 hipError_t launch_attn_fused(const FusedAttnArgs& f, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1);

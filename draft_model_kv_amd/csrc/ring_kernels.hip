@@ -733,6 +733,14 @@ __device__ inline int keep_sgpr(int v) {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer accesses with device-scope coherence on gfx950: cache policy sc1
+// (a store writes through to memory, a load is coherent across the XCDs'
+// L2 caches); word 3 of a raw gfx9 buffer descriptor, 32-bit data format.
+constexpr int kScDevice = 16;
+__device__ inline __amdgpu_buffer_rsrc_t dev_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
+}
 typedef __attribute__((address_space(1))) float gfloat;
 typedef __attribute__((address_space(1))) f32x2 gf32x2;
 typedef __attribute__((address_space(1))) f32x4 gf32x4;
@@ -744,6 +752,8 @@ struct EpilogueArgs {
   gfloat* pacc;
   gfloat* pml;
   bool one_split;
+  bool coherent;  // the partial is stored with device-scope coherence for the
+                  // in-launch merge (last_arriver_merge)
   int m, group, n_head;
   int row0;  // first query row of this work-group's block(s)
 };
@@ -828,13 +838,119 @@ __device__ __forceinline__ void merge_store(const EpilogueArgs& a, unsigned char
                                            v[jj].w * inv};
       }
     } else {
-      if (W == 0 && hl == 0 && n < a.m) *(gf32x2*)(a.pml + nl * 2) = f32x2{mx, lt};
       // partial in fragment order [mb][block][jj][lane] float4: each store
       // instruction writes 1 KB contiguous.
+      if (a.coherent) {
+        const __amdgpu_buffer_rsrc_t ra = dev_rsrc((const float*)a.pacc, MB * 32 * kHeadDim * 4);
+        const __amdgpu_buffer_rsrc_t rm = dev_rsrc((const float*)a.pml, MB * 32 * 2 * 4);
+        if (W == 0 && hl == 0 && n < a.m)
+          __builtin_amdgcn_raw_buffer_store_b64(f32x2{mx, lt}, rm, nl * 8, 0, kScDevice);
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        *(gf32x4*)(a.pacc + (((mb * 4 + W) * 4 + jj) * 64 + lane) * 4) =
-            f32x4{v[jj].x, v[jj].y, v[jj].z, v[jj].w};
+        for (int jj = 0; jj < 4; ++jj)
+          __builtin_amdgcn_raw_buffer_store_b128(f32x4{v[jj].x, v[jj].y, v[jj].z, v[jj].w}, ra,
+                                                 (((mb * 4 + W) * 4 + jj) * 64 + lane) * 16, 0,
+                                                 kScDevice);
+      } else {
+        if (W == 0 && hl == 0 && n < a.m) *(gf32x2*)(a.pml + nl * 2) = f32x2{mx, lt};
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          *(gf32x4*)(a.pacc + (((mb * 4 + W) * 4 + jj) * 64 + lane) * 4) =
+              f32x4{v[jj].x, v[jj].y, v[jj].z, v[jj].w};
+      }
+    }
+  }
+}
+
+// Cross-split merge inside the launch (the kernels whose waves stream
+// several tiles, with 2..kInKernelMergeMaxSplits splits): every work-group
+// has stored its partial and (max, sum) pairs with device-scope coherence;
+// once those stores are complete it draws a ticket from the counter of its
+// (sequence x KV head, row block), and the work-group that draws the last
+// one resets the counter and merges every split's partial into the output
+// as k_ring_merge does: M = max_t m_t, out = sum_t 2^(m_t - M) acc_t /
+// sum_t 2^(m_t - M) l_t (a split without a visible key has m = -inf, l = 0).
+// Thread x holds float4 f = 256 i + x of the work-group's partial, i <
+// 4 MB, in its fragment order [mb][block][jj][lane]; KB splits' loads are
+// in flight at a time and merged online.
+template <int MB>
+__device__ __forceinline__ void last_arriver_merge(const AttnArgs& a, const EpilogueArgs& ep, int unit,
+                                                   int rb) {
+  constexpr int MP = MB * 32, NF = 4 * MB, KB = MB == 1 ? 8 : 4;
+  __shared__ uint32_t ticket;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's partial stores are done
+  __syncthreads();
+  uint32_t* cnt = a.tickets + unit * a.n_rb + rb;
+  if (threadIdx.x == 0)
+    ticket = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  // (the ticket through an SGPR: compared with it, n_split must not be
+  // replaced by a value the compiler takes for a per-lane one)
+  if (__builtin_amdgcn_readfirstlane(ticket) + 1 != (uint32_t)a.n_split) return;
+  if (threadIdx.x == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  // split t's partial rows start split_rows * t rows after split 0's;
+  // descriptors in SGPRs (the values are wave-uniform)
+  const int split_rows = keep_sgpr(MP * a.n_rb);
+  const int64_t row00 = (int64_t)unit * a.n_split * split_rows + rb * MP;
+  const uint32_t span = (uint32_t)keep_sgpr((a.n_split - 1) * split_rows + MP);
+  const __amdgpu_buffer_rsrc_t ra = dev_rsrc(
+      (const float*)keep_sgpr((uint64_t)(a.part_acc + row00 * kHeadDim)), span * kHeadDim * 4);
+  const __amdgpu_buffer_rsrc_t rm = dev_rsrc(
+      (const float*)keep_sgpr((uint64_t)(a.part_ml + row00 * 2)), span * 2 * 4);
+  const int x = threadIdx.x, ln = x & 63, col = ln & 31;
+  float M[MB], L[MB];
+  f32x4 O[NF];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) { M[mb] = kNegInf; L[mb] = 0.0f; }
+#pragma unroll
+  for (int i = 0; i < NF; ++i) O[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int tb = 0; tb < a.n_split; tb += KB) {
+    f32x2 ml[KB][MB];
+    f32x4 v[KB][NF];
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      const uint32_t t = (uint32_t)min(tb + u, a.n_split - 1);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        ml[u][mb] = __builtin_amdgcn_raw_buffer_load_b64(
+            rm, (t * split_rows + mb * 32 + col) * 8, 0, kScDevice);
+#pragma unroll
+      for (int i = 0; i < NF; ++i)
+        v[u][i] = __builtin_amdgcn_raw_buffer_load_b128(
+            ra, (t * split_rows * kHeadDim + (i * 256 + x) * 4) * 4, 0, kScDevice);
+    }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      float mx = M[mb];
+#pragma unroll
+      for (int u = 0; u < KB; ++u)
+        if (tb + u < a.n_split) mx = fmaxf(mx, ml[u][mb].x);
+      // rescale what the earlier batches summed (nothing yet: M = -inf)
+      const float so = M[mb] == kNegInf ? 0.0f : exp2_hw(M[mb] - mx);
+      L[mb] *= so;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) O[4 * mb + k] *= so;
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+        const float e = exp2_hw(ml[u][mb].x - mx);
+        const float w = (tb + u < a.n_split && ml[u][mb].x != kNegInf) ? e : 0.0f;
+        L[mb] += w * ml[u][mb].y;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) O[4 * mb + k] += w * v[u][4 * mb + k];
+      }
+      M[mb] = mx;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NF; ++i) {
+    const int f = i * 256 + x, mb = i >> 2, b = (f >> 8) & 3, jj = (f >> 6) & 3, hl = ln >> 5;
+    const int n = rb * MP + mb * 32 + col;  // query row
+    if (n < a.m) {
+      // L > 0: the noise rows are visible to every query.
+      const float inv = 1.0f / L[mb];
+      const unsigned q = quot32(n, a.rcp_group), hh = n - q * a.group;
+      gfloat* dst = ep.out_unit + (q * a.n_head + hh) * kHeadDim + 32 * b + 8 * jj + 4 * hl;
+      *(gf32x4*)dst = O[i] * inv;
     }
   }
 }
@@ -905,6 +1021,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
   uint64_t pml = (uint64_t)(a.part_ml + prow * 2);
   const EpilogueArgs ep{(gfloat*)keep_sgpr(out_unit), (gfloat*)keep_sgpr(pacc),
                         (gfloat*)keep_sgpr(pml), keep_sgpr(a.n_split == 1) != 0,
+                        !SHORT && keep_sgpr(a.n_split > 1 && a.tickets != nullptr) != 0,
                         keep_sgpr(a.m), keep_sgpr(a.group), keep_sgpr(a.n_head),
                         keep_sgpr(row0)};
 
@@ -1169,6 +1286,9 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
     merge_store<MB, NW, 2, SHARE>(ep, lds, sm_m, sm_l, m_run, l_run, o, lane);
   else
     merge_store<MB, NW, 3, SHARE>(ep, lds, sm_m, sm_l, m_run, l_run, o, lane);
+  if constexpr (!SHORT) {
+    if (ep.coherent) last_arriver_merge<MB>(a, ep, unit, row0 / MP);
+  }
 }
 
 template <int MB, int NW, int RP, bool FUSED, bool SHORT>
@@ -1508,7 +1628,7 @@ static bool set_attn_recips(AttnArgs& a) {
 
 // Whether every wave of the launch attends at most one ring tile (the widest
 // window's tiles over n_split splits of 4 waves).
-static bool short_waves(const AttnArgs& a) {
+bool attn_short_waves(const AttnArgs& a) {
   int max_count = 0;
   for (int i = 0; i < a.n_seq && i < RING_MAX_SEQ_INTERNAL; ++i)
     max_count = max_count > a.vis_count[i] ? max_count : a.vis_count[i];
@@ -1522,7 +1642,7 @@ hipError_t launch_attn(const AttnArgs& args, hipStream_t s, hipEvent_t t0, hipEv
   const int grid = a.n_seq * a.n_head_kv * a.n_split * a.n_rb;
   // rope table passes: one float4 per thread covers q_len <= 8
   const bool one_pass = a.q_len <= 8;
-  const bool sw = short_waves(a);
+  const bool sw = attn_short_waves(a);
   // one query block per work-group: m <= 32, or one work-group per row block
   if (a.m <= 32 || a.n_rb > 1) {
     if (one_pass && sw)
@@ -1549,7 +1669,7 @@ hipError_t launch_attn_fused(const FusedAttnArgs& args, hipStream_t s, hipEvent_
   const AttnArgs& a = f.a;
   const int grid = f.n_attn_blocks;
   const bool one_pass = a.q_len <= 8;
-  const bool sw = short_waves(a);
+  const bool sw = attn_short_waves(a);
   if (a.m <= 32 || a.n_rb > 1) {
     if (one_pass && sw)
       hipExtLaunchKernelGGL((k_ring_attn_fused<1, 4, 1, true>), dim3(grid), dim3(256), 0, s, t0, t1, 0, f);

@@ -51,6 +51,7 @@ struct Layout {
   size_t off_k = 0, off_v = 0, off_slot = 0, off_mask = 0, off_mask_swa = 0, off_rope = 0,
          off_ropeq = 0, off_freq = 0;
   size_t off_pacc = 0, off_pml = 0, total = 0;
+  size_t off_ticket = 0;                  // in-launch merge tickets, one per (seq x head, row block)
   int32_t n_ds = 0;                       // d-slices of the projection
   int64_t slot_stride = 0;                // int32 per sequence in slot_pos (cap padded)
   size_t off_mirror = 0, off_proj = 0;    // feature mirror, projection scratch
@@ -157,6 +158,7 @@ void geometry_of(const ring_config& c, ring_geometry* g, Layout* L) {
   const size_t n_part = L->n_split > 1 ? (size_t)c.n_seq * c.n_head_kv * L->n_split * L->mpad : 0;
   L->off_pacc = take(n_part * kHeadDim * 4);
   L->off_pml = take(n_part * 2 * 4);
+  L->off_ticket = take(L->n_split > 1 ? (size_t)c.n_seq * c.n_head_kv * L->n_rb * 4 : 0);
   L->n_ds = c.d_model / kProjSlice;
   L->off_mirror = take((size_t)c.n_seq * c.cap * c.d_model * 2);
   L->off_proj = take((size_t)c.n_layer * L->n_ds * kProjRows * 2 * g->kv_row * 4);
@@ -218,6 +220,10 @@ struct ring {
   double* inv_freq = nullptr;
   float* part_acc = nullptr;
   float* part_ml = nullptr;
+  // ticket counters of the in-launch cross-split merge (zero between
+  // launches), or nullptr; used only with RING_ATTN_MERGE=kernel
+  uint32_t* tickets = nullptr;
+  bool merge_in_launch = false;
   uint16_t* mirror = nullptr;   // fused features [n_seq][cap][d_model], or nullptr
   float* proj = nullptr;        // projection scratch
   uint16_t* wpack = nullptr;    // registered weights, packed (ring_set_kv_weights)
@@ -425,6 +431,15 @@ int ring_init(const ring_config* cfg, void* workspace, size_t workspace_bytes, v
   r->inv_freq = reinterpret_cast<double*>(r->ws + r->L.off_freq);
   r->part_acc = reinterpret_cast<float*>(r->ws + r->L.off_pacc);
   r->part_ml = reinterpret_cast<float*>(r->ws + r->L.off_pml);
+  if (r->L.n_split > 1) r->tickets = reinterpret_cast<uint32_t*>(r->ws + r->L.off_ticket);
+  {
+    // RING_ATTN_MERGE=kernel: merge the splits inside the attention launch
+    // where it applies (measured no faster than the merge launch on the
+    // wide rings: the coherent partial stores, the ticket and the last
+    // arriver's loads cost the attention as much as the launch it saves)
+    const char* env = std::getenv("RING_ATTN_MERGE");
+    r->merge_in_launch = env && std::strcmp(env, "kernel") == 0;
+  }
   if (cfg->d_model > 0) {
     r->mirror = reinterpret_cast<uint16_t*>(r->ws + r->L.off_mirror);
     r->proj = reinterpret_cast<float*>(r->ws + r->L.off_proj);
@@ -447,6 +462,8 @@ int ring_init(const ring_config* cfg, void* workspace, size_t workspace_bytes, v
   hipError_t e = hipMemsetAsync(r->kring, 0, ring_bytes, s);
   if (e == hipSuccess) e = hipMemsetAsync(r->vring, 0, ring_bytes, s);
   if (e == hipSuccess) e = hipMemsetAsync(r->slot_pos, 0xFF, (size_t)cfg->n_seq * r->L.slot_stride * 4, s);
+  if (e == hipSuccess && r->tickets)
+    e = hipMemsetAsync(r->tickets, 0, (size_t)cfg->n_seq * cfg->n_head_kv * r->L.n_rb * 4, s);
   if (e == hipSuccess)
     e = launch_fill_u16(r->mask, 0xFC00u, (int64_t)cfg->n_seq * cfg->q_len * r->geo.kv_total, s);
   if (e == hipSuccess)
@@ -940,6 +957,14 @@ int attn_launch(ring* r, int32_t layer, const void* q, const void* k_noise, cons
   a.out = out;
   const int64_t cap = r->cfg.cap;
   const uint64_t bit = layer < 64 ? (1ull << layer) : 0;
+  // With RING_ATTN_MERGE=kernel, the cross-split merge inside the attention
+  // launch (a last-arriver merge per sequence x head and row block) where
+  // the waves stream several tiles and the splits are few; else (default)
+  // the merge launch below.
+  a.n_rb = r->L.n_rb;
+  const bool merge_in_launch = r->merge_in_launch && r->tickets && n_split > 1 &&
+                               n_split <= kInKernelMergeMaxSplits && !attn_short_waves(a);
+  if (merge_in_launch) a.tickets = r->tickets;
   hipEvent_t t0, t1;
   next_events(r, RING_KERNEL_ATTN, &t0, &t1);
   // Deferred steps owing this layer's rows or the index state: one fused
@@ -991,7 +1016,7 @@ int attn_launch(ring* r, int32_t layer, const void* q, const void* k_noise, cons
     a.n_rb = r->L.n_rb;
     if (int e = check_launch(launch_attn(a, s, t0, t1), "ring_attn")) return e;
   }
-  if (n_split > 1) {
+  if (n_split > 1 && !merge_in_launch) {
     MergeArgs m{};
     m.part_acc = part_acc;
     m.part_ml = part_ml;

@@ -289,7 +289,14 @@ int ring_begin_step_mirror(ring_t* r, int32_t seq, int64_t committed,
  * Query head h reads KV head h / (n_head / n_head_kv); scores are scaled by
  * 1/sqrt(head_dim).  The rotated noise K and V are also written to ring rows
  * cap + j of this layer.  Uses each sequence's state from its last
- * begin_step.  Errors: RING_ERANGE (layer), RING_EINVAL (NULL), RING_EDEVICE.*/
+ * begin_step.  Errors: RING_ERANGE (layer), RING_EINVAL (NULL), RING_EDEVICE.
+ * The attention is split over ring tiles (split-K) and the splits' partials
+ * are merged by a second launch.  Tuning switches, read by ring_init from
+ * the environment: RING_ATTN_SPLITS=n forces n splits (1..64);
+ * RING_ATTN_ROW_BLOCKS=0 keeps both 32-query blocks of a KV head in one
+ * work-group; RING_ATTN_MERGE=kernel merges the splits inside the attention
+ * launch where its waves stream several tiles and it has at most 16 splits
+ * (the work-group that finishes last merges; counters in the workspace). */
 int ring_attn(ring_t* r, int32_t layer, const void* q, const void* k_noise,
               const void* v_noise, float* out, void* stream);
 

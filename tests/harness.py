@@ -116,12 +116,15 @@ class Driver:
     """One ring (all sequences, all layers) and its oracle twin."""
 
     def __init__(self, w: W.Workload, n_split: Optional[int] = None, device: str = "cuda:0",
-                 row_blocks: Optional[bool] = None, registered_weights: bool = False):
+                 row_blocks: Optional[bool] = None, registered_weights: bool = False,
+                 merge: Optional[str] = None):
         """n_split: attention splits forced; row_blocks: False puts both
-        32-row query blocks of a KV head in one work-group (the library reads
-        both settings when the ring is created); registered_weights: rows
-        from features go through the weights registered with
-        ring_set_kv_weights instead of the caller's."""
+        32-row query blocks of a KV head in one work-group; merge: "kernel"
+        merges the splits inside the attention launch where the library
+        supports it, instead of in a launch of its own (the library reads
+        these settings when the ring is created); registered_weights: rows from
+        features go through the weights registered with ring_set_kv_weights
+        instead of the caller's."""
         import torch
         from draft_model_kv_amd import Ring
         self.torch = torch
@@ -132,6 +135,8 @@ class Driver:
             env["RING_ATTN_SPLITS"] = str(n_split)
         if row_blocks is not None:
             env["RING_ATTN_ROW_BLOCKS"] = "1" if row_blocks else "0"
+        if merge is not None:
+            env["RING_ATTN_MERGE"] = merge
         saved = {k: os.environ.get(k) for k in env}
         os.environ.update(env)
         try:

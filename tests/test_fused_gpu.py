@@ -91,6 +91,16 @@ def test_fused_multi_layer_sliding_window():
     d.close()
 
 
+@pytest.mark.parametrize("cap,n_split", [(1024, 4), (1024, 7), (4096, 16)])
+def test_fused_merge_in_launch(cap, n_split):
+    """RING_ATTN_MERGE=kernel on fused launches whose waves stream two tiles:
+    the cross-split merge runs inside the launch (last arriver per sequence
+    x KV head)."""
+    d = Driver(small(cap=cap, n_layer=2, seed=310 + n_split), n_split=n_split, merge="kernel")
+    run_fused(d, [cap - 100, cap - 99, cap - 91, cap + 3, cap + 12, cap + 13, cap + 21])
+    d.close()
+
+
 @pytest.mark.parametrize("row_blocks", [True, False], ids=["row_blocks", "one_workgroup"])
 def test_fused_gqa8_outliers(row_blocks):
     """64 queries per KV head: each 32-query block in a work-group of its own

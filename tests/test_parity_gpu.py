@@ -109,6 +109,22 @@ def test_gqa8_outliers_two_query_blocks(row_blocks, n_split):
     d.close()
 
 
+@pytest.mark.parametrize("n_split", [2, 3, 7, 16])
+@pytest.mark.parametrize("n_head,row_blocks", [(32, None), (64, True), (64, False)],
+                         ids=["gqa4", "gqa8_row_blocks", "gqa8_one_workgroup"])
+def test_merge_in_launch(n_split, n_head, row_blocks):
+    """RING_ATTN_MERGE=kernel: the cross-split merge inside the attention
+    launch (waves that stream several tiles, 2..16 splits); the work-group
+    that draws the last ticket of its (sequence x KV head, row block) merges
+    every split's partial.  Split counts that divide the 128 ring tiles
+    evenly and not; 32 or 64 queries per KV head, +-30 outliers; windows
+    that wrap the ring end."""
+    w = small(cap=4096, n_head=n_head, sigma=1.0, outlier_p=0.01, seed=120 + n_split)
+    d = Driver(w, n_split=n_split, row_blocks=row_blocks, merge="kernel")
+    run_steps(d, [4000, 4001, 4096, 4100, 4111, 5000, 5003])
+    d.close()
+
+
 @pytest.mark.parametrize("row_blocks", [True, False], ids=["row_blocks", "one_workgroup"])
 def test_long_noise_block_two_query_blocks(row_blocks):
     """q_len 16 with GQA 4 (m = 64): several rope-table passes, noise rows
