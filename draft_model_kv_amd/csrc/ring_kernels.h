@@ -89,8 +89,9 @@ struct ProjArgs {
   int32_t slot0;             // its mirror slot, pos0 % cap
   int32_t n_rows;            // rows of this launch, 1..kProjRows
   int32_t cap, d_model, kv_row, n_head_kv, n_layer, n_ds;
-  // recip32() of the row tiles, n_ds and 2 n_head_kv (set by launch_project)
-  uint64_t rcp_n_rt, rcp_n_ds, rcp_n_hp;
+  // recip32() of the row tiles, n_ds and 4 n_head_kv (half head parts; set
+  // by launch_project)
+  uint64_t rcp_n_rt, rcp_n_ds, rcp_n_hh;
 };
 
 // Projection weights in the projection kernel's load order: for each work-group

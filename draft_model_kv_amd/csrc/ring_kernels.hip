@@ -1457,46 +1457,55 @@ __global__ __launch_bounds__(256) void k_ring_merge(MergeArgs a) {
 // ---------------------------------------------------------------------------
 // Projection of new rows from fused features: raw = W f for W = wk and wv of
 // every layer, on the matrix cores, one d-slice per work-group.
-//   Work-group (layer, head part hp, d-slice ds, 32-row tile rt): hp < n_head_kv
-//   is K head hp, else V head hp - n_head_kv; wave w computes its 32 output
-//   dims [32 w, 32 w + 32) for the tile's rows over the slice's 256 feature
-//   dims.  The slice of the 32 feature rows is staged once in LDS (rows past
-//   n_rows repeat the last row and are never stored).  The sum over d is
+//   Work-group (layer, half of head part hp, d-slice ds, 32-row tile rt):
+//   hp < n_head_kv is K head hp, else V head hp - n_head_kv; its two waves
+//   compute 32 output dims each, [32 pw, 32 pw + 32) with pw = 2 half +
+//   wave, for the tile's rows over the slice's 256 feature dims (two-wave
+//   work-groups: 1280 at 5 layers of 8 KV heads and d_model 2048, five per
+//   compute unit, where 640 of four waves leave half the compute units three
+//   and half two; 8.7 against 8.9 us in isolation, within the run-to-run
+//   spread in the step).  The slice of the 32 feature rows is
+//   staged in LDS by each work-group (rows past n_rows repeat the last row
+//   and are never stored).  The sum over d is
 //   order-free, so each lane takes 64 contiguous bytes of its W row and of
 //   its feature row per 64-d block: MFMA step j of a block pairs, for both
 //   operands, dims 64 blk + 32 (lane / 32) + 8 j + e.
 // ---------------------------------------------------------------------------
 template <bool PACKED>
-__global__ __launch_bounds__(256) void k_ring_project(ProjArgs a) {
+__global__ __launch_bounds__(128) void k_ring_project(ProjArgs a) {
   constexpr int kRowStride = kProjSlice / 8 + 1;  // half8 per staged row (+1: no bank conflicts)
   __shared__ half8 f_lds[32 * kRowStride];
   // every argument fetched in one batch at entry (see attn_entry)
   asm volatile("" ::"s"(a.mirror), "s"(a.wk), "s"(a.wv), "s"(a.scratch), "s"(a.slot0),
                "s"(a.n_rows), "s"(a.cap), "s"(a.d_model), "s"(a.kv_row), "s"(a.n_head_kv),
-               "s"(a.n_ds), "s"(a.rcp_n_rt), "s"(a.rcp_n_ds), "s"(a.rcp_n_hp));
+               "s"(a.n_ds), "s"(a.rcp_n_rt), "s"(a.rcp_n_ds), "s"(a.rcp_n_hh));
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n_rt = (a.n_rows + 31) >> 5;
-  // work-group -> (layer, head part, d-slice, row tile) by quotients with
-  // host-computed reciprocals (no integer division)
+  // work-group -> (layer, half head part, d-slice, row tile) by quotients
+  // with host-computed reciprocals (no integer division); the two waves of
+  // half hh & 1 of head part hh >> 1 compute its output dims
+  // 64 (hh & 1) + 32 wave + 0..31
   const uint32_t b0 = blockIdx.x;
   const uint32_t b1 = quot32(b0, a.rcp_n_rt);
   const int rt = (int)(b0 - b1 * n_rt);
   const uint32_t b2 = quot32(b1, a.rcp_n_ds);
   const int ds = (int)(b1 - b2 * a.n_ds);
-  const int n_hp = 2 * a.n_head_kv;
-  const int layer = (int)quot32(b2, a.rcp_n_hp);
-  const int hp = (int)(b2 - layer * n_hp);
+  const int n_hp = 2 * a.n_head_kv, n_hh = 2 * n_hp;
+  const int layer = (int)quot32(b2, a.rcp_n_hh);
+  const int hh = (int)(b2 - layer * n_hh);
+  const int hp = hh >> 1;
+  const int pw = 2 * (hh & 1) + wave;  // the wave's 32 output dims of the head part
   const int r0 = rt * 32;
   const int d0 = ds * kProjSlice;
 
   // features of the tile's rows, first (loads return in issue order, and
-  // the LDS staging needs them): 32 rows x 32 chunks of 16 B, 4 per thread;
+  // the LDS staging needs them): 32 rows x 32 chunks of 16 B, 8 per thread;
   // row i sits in mirror slot (slot0 + i) % cap (slot0 < cap, i < 64)
-  half8 fv[4];
+  half8 fv[8];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int c = threadIdx.x + 256 * k;
+  for (int k = 0; k < 8; ++k) {
+    const int c = threadIdx.x + 128 * k;
     const int row = c >> 5, dc = c & 31;
     int slot = a.slot0 + min(r0 + row, a.n_rows - 1);
     while (slot >= a.cap) slot -= a.cap;
@@ -1510,7 +1519,7 @@ __global__ __launch_bounds__(256) void k_ring_project(ProjArgs a) {
   half8 wa[4][4];
   if constexpr (PACKED) {
     const half8* wp = (const half8*)a.wk +
-                      ((((int64_t)layer * n_hp + hp) * a.n_ds + ds) * 4 + wave) * 1024;
+                      ((((int64_t)layer * n_hp + hp) * a.n_ds + ds) * 4 + pw) * 1024;
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk)
 #pragma unroll
@@ -1519,7 +1528,7 @@ __global__ __launch_bounds__(256) void k_ring_project(ProjArgs a) {
     const bool is_v = hp >= a.n_head_kv;
     const int head = is_v ? hp - a.n_head_kv : hp;
     const uint16_t* wrow = (is_v ? a.wv : a.wk) +
-                           ((int64_t)layer * a.kv_row + head * kHeadDim + 32 * wave + (lane & 31)) *
+                           ((int64_t)layer * a.kv_row + head * kHeadDim + 32 * pw + (lane & 31)) *
                                a.d_model +
                            d0 + 32 * (lane >> 5);
 #pragma unroll
@@ -1530,8 +1539,8 @@ __global__ __launch_bounds__(256) void k_ring_project(ProjArgs a) {
   // every weight load is issued before the wait for the features
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int c = threadIdx.x + 256 * k;
+  for (int k = 0; k < 8; ++k) {
+    const int c = threadIdx.x + 128 * k;
     f_lds[(c >> 5) * kRowStride + (c & 31)] = fv[k];
   }
   lds_barrier();
@@ -1548,7 +1557,7 @@ __global__ __launch_bounds__(256) void k_ring_project(ProjArgs a) {
   if (n < a.n_rows) {
     float* dst = a.scratch +
                  (((int64_t)layer * a.n_ds + ds) * kProjRows + n) * 2 * a.kv_row +
-                 hp * kHeadDim + 32 * wave + 4 * (lane >> 5);
+                 hp * kHeadDim + 32 * pw + 4 * (lane >> 5);
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       *(float4*)(dst + 8 * q) = make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2],
@@ -1718,17 +1727,19 @@ hipError_t launch_merge(const MergeArgs& args, hipStream_t s, hipEvent_t t0, hip
 hipError_t launch_project(const ProjArgs& args, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
   if (args.n_rows <= 0) return hipSuccess;
   ProjArgs a = args;
-  const uint32_t n_rt = (a.n_rows + 31) / 32, n_hp = 2 * a.n_head_kv;
-  const uint64_t grid = (uint64_t)a.n_layer * n_hp * a.n_ds * n_rt;
+  // work-groups of two waves, one per half head part (1280 for 5 layers
+  // of 8 KV heads and 8 slices: five per compute unit)
+  const uint32_t n_rt = (a.n_rows + 31) / 32, n_hh = 4 * a.n_head_kv;
+  const uint64_t grid = (uint64_t)a.n_layer * n_hh * a.n_ds * n_rt;
   // every quotient exact: dividend times divisor at most 2^32
   if (grid * n_rt > (uint64_t(1) << 32) || grid > (uint64_t(1) << 31)) return hipErrorInvalidValue;
   a.rcp_n_rt = recip32(n_rt);
   a.rcp_n_ds = recip32(a.n_ds);
-  a.rcp_n_hp = recip32(n_hp);
+  a.rcp_n_hh = recip32(n_hh);
   if (a.packed)
-    hipExtLaunchKernelGGL(k_ring_project<true>, dim3((unsigned)grid), dim3(256), 0, s, t0, t1, 0, a);
+    hipExtLaunchKernelGGL(k_ring_project<true>, dim3((unsigned)grid), dim3(128), 0, s, t0, t1, 0, a);
   else
-    hipExtLaunchKernelGGL(k_ring_project<false>, dim3((unsigned)grid), dim3(256), 0, s, t0, t1, 0, a);
+    hipExtLaunchKernelGGL(k_ring_project<false>, dim3((unsigned)grid), dim3(128), 0, s, t0, t1, 0, a);
   return hipGetLastError();
 }
 
