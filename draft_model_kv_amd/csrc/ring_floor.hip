@@ -8,8 +8,8 @@
 //   kind 0  empty kernel (launch and drain only)
 //   kind 1  every visible K and V tile loaded once (16-byte loads per lane,
 //           the attention's fragment order) and folded by xor
-//   kind 2  kind 1, then the work-group's 16 KiB fp32 split partial and its
-//           (max, sum) pairs stored where the attention stores them
+//   kind 2  kind 1, then the work-group's 8 KiB F16 split partial and its
+//           fp32 (max, sum) pairs stored where the attention stores them
 //   kind 3  kind 2 with an in-kernel cross-split merge by the last arriver:
 //           partials stored with device-scope coherence (sc1, write-through),
 //           the stores waited for, one atomic ticket per work-group on a
@@ -43,6 +43,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ inline f32x16 floor_mfma(half8 a, half8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
@@ -172,19 +174,21 @@ __global__ __launch_bounds__(256) void k_ring_floor(FloorArgs a) {
       if (lane == 0) a.out[blockIdx.x * 4 + wave] = (float)(w & 0xFFFFu);
       return;
     } else {
-      // the split partial: 32 rows x 128 dims fp32 where the attention puts
-      // the partial of (unit, split, row block), and its (max, sum) pairs
+      // the split partial: 32 rows x 128 dims F16 where the attention puts
+      // the partial of (unit, split, row block), and its fp32 (max, sum) pairs
       const f32x4 v = {(float)(x.x & 0xFFu), (float)(x.y & 0xFFu), (float)(x.z & 0xFFu), 1.0f};
       const int64_t prow = ((int64_t)(unit * a.n_split + split) * a.n_rb + rb) * 32;
       const uint32_t pbytes = (uint32_t)a.part_bytes;
       const __amdgpu_buffer_rsrc_t pr = floor_rsrc(a.part_acc, pbytes);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint32_t off = (uint32_t)((prow * kHeadDim + (i * 256 + threadIdx.x) * 4) * 4);
+        const half4 h = {(_Float16)(v.x + i), (_Float16)(v.y + i), (_Float16)(v.z + i),
+                         (_Float16)(v.w + i)};
+        const uint32_t off = (uint32_t)((prow * kHeadDim + (i * 256 + threadIdx.x) * 4) * 2);
         if constexpr (KIND == 2)
-          *(f32x4*)(a.part_acc + prow * kHeadDim + (i * 256 + threadIdx.x) * 4) = v + (float)i;
+          *(half4*)(a.part_acc + prow * kHeadDim + (i * 256 + threadIdx.x) * 4) = h;
         else
-          __builtin_amdgcn_raw_buffer_store_b128(v + (float)i, pr, off, 0, kPolicySc1);
+          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, h), pr, off, 0, kPolicySc1);
       }
       if (threadIdx.x < 32) *(float2*)(a.part_ml + (prow + threadIdx.x) * 2) = make_float2(v.x, 1.0f);
       if constexpr (KIND == 2) return;
@@ -200,10 +204,12 @@ __global__ __launch_bounds__(256) void k_ring_floor(FloorArgs a) {
       const int64_t base_row = ((int64_t)unit * a.n_split * a.n_rb + rb) * 32;  // split 0
       const int64_t split_f4 = (int64_t)a.n_rb * 32 * kHeadDim / 4;            // between splits
       float* outp = a.out + ((int64_t)unit * a.n_rb + rb) * 32 * kHeadDim;
-      // float4 idx of split t's partial (sc1 load; past the buffer: zero)
+      // group idx of four values of split t's partial, as fp32 (sc1 load;
+      // past the buffer: zero)
       auto load_f4 = [&](int t, int idx) {
-        const uint32_t off = (uint32_t)(((base_row * kHeadDim / 4) + t * split_f4 + idx) * 16);
-        return __builtin_amdgcn_raw_buffer_load_b128(pr, off, 0, kPolicySc1);
+        const uint32_t off = (uint32_t)(((base_row * kHeadDim / 4) + t * split_f4 + idx) * 8);
+        const half4 h = __builtin_bit_cast(half4, __builtin_amdgcn_raw_buffer_load_b64(pr, off, 0, kPolicySc1));
+        return f32x4{(float)h.x, (float)h.y, (float)h.z, (float)h.w};
       };
       // sum over splits t = t_first, t_first + t_step, ... < n_split of float4
       // idx: eight loads in flight at a time, issued before any is added

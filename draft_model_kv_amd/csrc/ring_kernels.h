@@ -146,8 +146,9 @@ struct AttnArgs {
   const uint16_t* k_noise;   // [n_seq][q_len][kv_row]
   const uint16_t* v_noise;
   float* out;                // [n_seq][q_len][n_head][128]
-  float* part_acc;           // [n_seq * n_head_kv][n_split][mpad][128]
-  float* part_ml;            // [n_seq * n_head_kv][n_split][mpad][2]
+  uint16_t* part_acc;        // [n_seq * n_head_kv][n_split][mpad][128] F16: each split's
+                             // output normalised by its sum (fragment order)
+  float* part_ml;            // [n_seq * n_head_kv][n_split][mpad][2] its (max, sum)
   int64_t seq_stride;        // halves between sequences in kring / vring
   int64_t layer_offset;      // halves from a sequence's base to this layer
   int64_t head_stride;       // halves between KV heads (n_tiles * 4096)
@@ -186,7 +187,7 @@ struct FusedAttnArgs {
 };
 
 struct MergeArgs {
-  const float* part_acc;
+  const uint16_t* part_acc;  // F16 normalised split outputs (see AttnArgs)
   const float* part_ml;
   float* out;
   int32_t n_units, n_split, n_head, n_head_kv, group, q_len, m, mpad;
@@ -202,7 +203,7 @@ struct FloorArgs {
   const uint16_t* kring;
   const uint16_t* vring;
   int64_t seq_stride, layer_offset, head_stride;
-  float* part_acc;           // the ring's split partials, [unit][split][n_rb * 32][128]
+  uint16_t* part_acc;        // the ring's split partials, [unit][split][n_rb * 32][128] F16
   float* part_ml;            // [unit][split][n_rb * 32][2]
   int64_t part_bytes;        // bytes of part_acc (below 2^31 for kinds 3 and 4)
   float* out;                // profiling buffer, [unit * n_rb][32 * 128] fp32

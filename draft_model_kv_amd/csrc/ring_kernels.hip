@@ -30,6 +30,8 @@ constexpr float kNegInf = -__builtin_inff();
 // through a generic pointer become flat loads, and a flat load in flight
 // makes the compiler wait for every other load before the next use of any.
 typedef const __attribute__((address_space(1))) uint16_t gcu16;
+typedef __attribute__((address_space(1))) uint16_t gu16;
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 
 // 2^x with the hardware instruction: about 1 ulp for normal results; results
 // below 2^-126 flush to zero and 2^-inf = 0.  Softmax weights that small
@@ -744,12 +746,14 @@ __device__ inline __amdgpu_buffer_rsrc_t dev_rsrc(const void* p, uint32_t bytes)
 typedef __attribute__((address_space(1))) float gfloat;
 typedef __attribute__((address_space(1))) f32x2 gf32x2;
 typedef __attribute__((address_space(1))) f32x4 gf32x4;
+typedef __attribute__((address_space(1))) half4 ghalf4;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // What the store of a work-group's result needs: its output rows (one split)
 // or its partial slot, and the query geometry.
 struct EpilogueArgs {
   gfloat* out_unit;
-  gfloat* pacc;
+  gu16* pacc;
   gfloat* pml;
   bool one_split;
   bool coherent;  // the partial is stored with device-scope coherence for the
@@ -838,24 +842,31 @@ __device__ __forceinline__ void merge_store(const EpilogueArgs& a, unsigned char
                                            v[jj].w * inv};
       }
     } else {
-      // partial in fragment order [mb][block][jj][lane] float4: each store
-      // instruction writes 1 KB contiguous.
+      // partial in fragment order [mb][block][jj][lane], four F16 per lane:
+      // the work-group's output normalised by its sum (zeros where no key
+      // of this split is visible to the query, lt = 0), and (max, sum) in
+      // fp32; each store instruction writes 512 B contiguous.
+      const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+      half4 hv[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        hv[jj] = half4{(_Float16)(v[jj].x * inv), (_Float16)(v[jj].y * inv),
+                       (_Float16)(v[jj].z * inv), (_Float16)(v[jj].w * inv)};
       if (a.coherent) {
-        const __amdgpu_buffer_rsrc_t ra = dev_rsrc((const float*)a.pacc, MB * 32 * kHeadDim * 4);
+        const __amdgpu_buffer_rsrc_t ra = dev_rsrc((const uint16_t*)a.pacc, MB * 32 * kHeadDim * 2);
         const __amdgpu_buffer_rsrc_t rm = dev_rsrc((const float*)a.pml, MB * 32 * 2 * 4);
         if (W == 0 && hl == 0 && n < a.m)
           __builtin_amdgcn_raw_buffer_store_b64(f32x2{mx, lt}, rm, nl * 8, 0, kScDevice);
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj)
-          __builtin_amdgcn_raw_buffer_store_b128(f32x4{v[jj].x, v[jj].y, v[jj].z, v[jj].w}, ra,
-                                                 (((mb * 4 + W) * 4 + jj) * 64 + lane) * 16, 0,
-                                                 kScDevice);
+          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, hv[jj]), ra,
+                                                (((mb * 4 + W) * 4 + jj) * 64 + lane) * 8, 0,
+                                                kScDevice);
       } else {
         if (W == 0 && hl == 0 && n < a.m) *(gf32x2*)(a.pml + nl * 2) = f32x2{mx, lt};
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj)
-          *(gf32x4*)(a.pacc + (((mb * 4 + W) * 4 + jj) * 64 + lane) * 4) =
-              f32x4{v[jj].x, v[jj].y, v[jj].z, v[jj].w};
+          *(ghalf4*)(a.pacc + (((mb * 4 + W) * 4 + jj) * 64 + lane) * 4) = hv[jj];
       }
     }
   }
@@ -867,11 +878,12 @@ __device__ __forceinline__ void merge_store(const EpilogueArgs& a, unsigned char
 // once those stores are complete it draws a ticket from the counter of its
 // (sequence x KV head, row block), and the work-group that draws the last
 // one resets the counter and merges every split's partial into the output
-// as k_ring_merge does: M = max_t m_t, out = sum_t 2^(m_t - M) acc_t /
-// sum_t 2^(m_t - M) l_t (a split without a visible key has m = -inf, l = 0).
-// Thread x holds float4 f = 256 i + x of the work-group's partial, i <
-// 4 MB, in its fragment order [mb][block][jj][lane]; KB splits' loads are
-// in flight at a time and merged online.
+// as k_ring_merge does: M = max_t m_t, a_t = 2^(m_t - M) l_t, out =
+// sum_t a_t o_t / sum_t a_t for the normalised split outputs o_t (a split
+// without a visible key has m = -inf, l = 0).  Thread x holds group f =
+// 256 i + x of four values of the work-group's partial, i < 4 MB, in its
+// fragment order [mb][block][jj][lane]; KB splits' loads are in flight at
+// a time and merged online.
 template <int MB>
 __device__ __forceinline__ void last_arriver_merge(const AttnArgs& a, const EpilogueArgs& ep, int unit,
                                                    int rb) {
@@ -894,7 +906,7 @@ __device__ __forceinline__ void last_arriver_merge(const AttnArgs& a, const Epil
   const int64_t row00 = (int64_t)unit * a.n_split * split_rows + rb * MP;
   const uint32_t span = (uint32_t)keep_sgpr((a.n_split - 1) * split_rows + MP);
   const __amdgpu_buffer_rsrc_t ra = dev_rsrc(
-      (const float*)keep_sgpr((uint64_t)(a.part_acc + row00 * kHeadDim)), span * kHeadDim * 4);
+      (const uint16_t*)keep_sgpr((uint64_t)(a.part_acc + row00 * kHeadDim)), span * kHeadDim * 2);
   const __amdgpu_buffer_rsrc_t rm = dev_rsrc(
       (const float*)keep_sgpr((uint64_t)(a.part_ml + row00 * 2)), span * 2 * 4);
   const int x = threadIdx.x, ln = x & 63, col = ln & 31;
@@ -906,7 +918,7 @@ __device__ __forceinline__ void last_arriver_merge(const AttnArgs& a, const Epil
   for (int i = 0; i < NF; ++i) O[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int tb = 0; tb < a.n_split; tb += KB) {
     f32x2 ml[KB][MB];
-    f32x4 v[KB][NF];
+    half4 v[KB][NF];
 #pragma unroll
     for (int u = 0; u < KB; ++u) {
       const uint32_t t = (uint32_t)min(tb + u, a.n_split - 1);
@@ -916,8 +928,8 @@ __device__ __forceinline__ void last_arriver_merge(const AttnArgs& a, const Epil
             rm, (t * split_rows + mb * 32 + col) * 8, 0, kScDevice);
 #pragma unroll
       for (int i = 0; i < NF; ++i)
-        v[u][i] = __builtin_amdgcn_raw_buffer_load_b128(
-            ra, (t * split_rows * kHeadDim + (i * 256 + x) * 4) * 4, 0, kScDevice);
+        v[u][i] = __builtin_bit_cast(half4, __builtin_amdgcn_raw_buffer_load_b64(
+            ra, (t * split_rows * kHeadDim + (i * 256 + x) * 4) * 2, 0, kScDevice));
     }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -933,10 +945,13 @@ __device__ __forceinline__ void last_arriver_merge(const AttnArgs& a, const Epil
 #pragma unroll
       for (int u = 0; u < KB; ++u) {
         const float e = exp2_hw(ml[u][mb].x - mx);
-        const float w = (tb + u < a.n_split && ml[u][mb].x != kNegInf) ? e : 0.0f;
-        L[mb] += w * ml[u][mb].y;
+        const float w = (tb + u < a.n_split && ml[u][mb].x != kNegInf) ? e * ml[u][mb].y : 0.0f;
+        L[mb] += w;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) O[4 * mb + k] += w * v[u][4 * mb + k];
+        for (int k = 0; k < 4; ++k) {
+          const half4 h = v[u][4 * mb + k];
+          O[4 * mb + k] += w * f32x4{(float)h.x, (float)h.y, (float)h.z, (float)h.w};
+        }
       }
       M[mb] = mx;
     }
@@ -1017,9 +1032,9 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
   uint64_t out_unit = (uint64_t)(a.out + ((int64_t)seq * a.q_len * a.n_head + g * a.group) * kHeadDim);
   // partial rows [row0, row0 + MP) of the split's n_rb * MP
   const int64_t prow = ((int64_t)unit * a.n_split + split) * (MP * a.n_rb) + row0;
-  uint64_t pacc = (uint64_t)(a.part_acc + prow * kHeadDim);
+  uint64_t pacc = (uint64_t)(a.part_acc + prow * kHeadDim);  // F16
   uint64_t pml = (uint64_t)(a.part_ml + prow * 2);
-  const EpilogueArgs ep{(gfloat*)keep_sgpr(out_unit), (gfloat*)keep_sgpr(pacc),
+  const EpilogueArgs ep{(gfloat*)keep_sgpr(out_unit), (gu16*)keep_sgpr(pacc),
                         (gfloat*)keep_sgpr(pml), keep_sgpr(a.n_split == 1) != 0,
                         !SHORT && keep_sgpr(a.n_split > 1 && a.tickets != nullptr) != 0,
                         keep_sgpr(a.m), keep_sgpr(a.group), keep_sgpr(a.n_head),
@@ -1359,13 +1374,14 @@ __global__ __launch_bounds__(NW * 64, SHORT ? 2 : 1) void k_ring_attn_fused(Fuse
 }
 
 // ---------------------------------------------------------------------------
-// Cross-split merge: out = sum_t acc_t 2^(m_t - M) / sum_t l_t 2^(m_t - M),
-// M = max_t m_t.  The partial accumulators are in the attention's fragment
-// order [unit][split][mb][block b][jj][lane] float4, lane = query col + 32 hl
+// Cross-split merge: out = sum_t a_t o_t / sum_t a_t with a_t = l_t
+// 2^(m_t - M), M = max_t m_t, for the splits' outputs o_t normalised by their
+// sums l_t (stored F16).  The partials are in the attention's fragment order
+// [unit][split][mb][block b][jj][lane] of four F16, lane = query col + 32 hl
 // holding dims 32 b + 8 jj + 4 hl + 0..3.  One work-group per (unit, mb, b,
-// jj): wave w merges splits w, w + 4, ... (each split's float4 of a lane is
-// one contiguous 1 KB row of the wave and the merge is lane-local, every
-// load of the wave in flight together), then wave 0 combines the four
+// jj): wave w merges splits w, w + 4, ... (each split's four values of a
+// lane are one contiguous 512 B row of the wave and the merge is lane-local,
+// every load of the wave in flight together), then wave 0 combines the four
 // partial merges through LDS and writes the output.
 // ---------------------------------------------------------------------------
 template <int KMAX>
@@ -1393,15 +1409,15 @@ __global__ __launch_bounds__(256) void k_ring_merge(MergeArgs a) {
   const int n = mb * 32 + col;
   const int64_t ml_step = (int64_t)a.mpad * 2, acc_step = (int64_t)a.mpad * kHeadDim;
   const float* ml = a.part_ml + (int64_t)unit * a.n_split * ml_step + n * 2;
-  const float* acc = a.part_acc + (int64_t)unit * a.n_split * acc_step + (f * 64 + lane) * 4;
+  const uint16_t* acc = a.part_acc + (int64_t)unit * a.n_split * acc_step + (f * 64 + lane) * 4;
 
   float2 mlv[KMAX];
-  float4 u[KMAX];
+  half4 u[KMAX];
 #pragma unroll
   for (int k = 0; k < KMAX; ++k) {
     const int t = min(wave + 4 * k, a.n_split - 1);
     mlv[k] = *(const float2*)(ml + t * ml_step);
-    u[k] = *(const float4*)(acc + t * acc_step);
+    u[k] = *(const half4*)(acc + t * acc_step);
   }
   // Take every load as one batch: the reductions below start from a value
   // that the empty asm statements make depend on every loaded register, so
@@ -1409,8 +1425,7 @@ __global__ __launch_bounds__(256) void k_ring_merge(MergeArgs a) {
   float mx = kNegInf;
 #pragma unroll
   for (int k = 0; k < KMAX; ++k)
-    asm volatile("" : "+v"(mx) : "v"(mlv[k].x), "v"(mlv[k].y), "v"(u[k].x), "v"(u[k].y),
-                 "v"(u[k].z), "v"(u[k].w));
+    asm volatile("" : "+v"(mx) : "v"(mlv[k].x), "v"(mlv[k].y), "v"(__builtin_bit_cast(u32x2, u[k])));
 #pragma unroll
   for (int k = 0; k < KMAX; ++k)
     if (wave + 4 * k < a.n_split) mx = fmaxf(mx, mlv[k].x);
@@ -1419,10 +1434,12 @@ __global__ __launch_bounds__(256) void k_ring_merge(MergeArgs a) {
   float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
   for (int k = 0; k < KMAX; ++k) {
+    // a split's output is stored normalised: its weight is 2^(m - mx) l
     const float e = exp2_hw(mlv[k].x - mx);
-    const float w = (wave + 4 * k < a.n_split && mlv[k].x != kNegInf) ? e : 0.0f;
-    L += w * mlv[k].y;
-    O.x += w * u[k].x; O.y += w * u[k].y; O.z += w * u[k].z; O.w += w * u[k].w;
+    const float w = (wave + 4 * k < a.n_split && mlv[k].x != kNegInf) ? e * mlv[k].y : 0.0f;
+    L += w;
+    O.x += w * (float)u[k].x; O.y += w * (float)u[k].y;
+    O.z += w * (float)u[k].z; O.w += w * (float)u[k].w;
   }
   sM[wave][lane] = mx;
   sL[wave][lane] = L;

@@ -156,7 +156,7 @@ void geometry_of(const ring_config& c, ring_geometry* g, Layout* L) {
   L->off_ropeq = take((size_t)c.n_seq * c.q_len * 64 * 2 * 4);
   L->off_freq = take(64 * 8);
   const size_t n_part = L->n_split > 1 ? (size_t)c.n_seq * c.n_head_kv * L->n_split * L->mpad : 0;
-  L->off_pacc = take(n_part * kHeadDim * 4);
+  L->off_pacc = take(n_part * kHeadDim * 2);
   L->off_pml = take(n_part * 2 * 4);
   L->off_ticket = take(L->n_split > 1 ? (size_t)c.n_seq * c.n_head_kv * L->n_rb * 4 : 0);
   L->n_ds = c.d_model / kProjSlice;
@@ -218,7 +218,7 @@ struct ring {
   double* rope_noise = nullptr;
   float* rope_q = nullptr;
   double* inv_freq = nullptr;
-  float* part_acc = nullptr;
+  uint16_t* part_acc = nullptr;
   float* part_ml = nullptr;
   // ticket counters of the in-launch cross-split merge (zero between
   // launches), or nullptr; used only with RING_ATTN_MERGE=kernel
@@ -429,7 +429,7 @@ int ring_init(const ring_config* cfg, void* workspace, size_t workspace_bytes, v
   if (cfg->swa_window > 0) r->mask_swa = reinterpret_cast<uint16_t*>(r->ws + r->L.off_mask_swa);
   r->rope_q = reinterpret_cast<float*>(r->ws + r->L.off_ropeq);
   r->inv_freq = reinterpret_cast<double*>(r->ws + r->L.off_freq);
-  r->part_acc = reinterpret_cast<float*>(r->ws + r->L.off_pacc);
+  r->part_acc = reinterpret_cast<uint16_t*>(r->ws + r->L.off_pacc);
   r->part_ml = reinterpret_cast<float*>(r->ws + r->L.off_pml);
   if (r->L.n_split > 1) r->tickets = reinterpret_cast<uint32_t*>(r->ws + r->L.off_ticket);
   {
@@ -929,11 +929,11 @@ int check_attn(const ring* r, int32_t layer, const void* q, const void* k_noise,
   return RING_OK;
 }
 
-// Bytes of the split partials (accumulators, then (max, sum) pairs 256-byte
+// Bytes of the split partials (F16 normalised outputs, then (max, sum) pairs 256-byte
 // aligned) of a launch with n_split splits.
 size_t partial_bytes(const ring* r, int32_t n_split, size_t* ml_offset) {
   const size_t rows = (size_t)r->cfg.n_seq * r->cfg.n_head_kv * n_split * r->L.mpad;
-  const size_t acc = (size_t)align_up((int64_t)(rows * kHeadDim * 4), 256);
+  const size_t acc = (size_t)align_up((int64_t)(rows * kHeadDim * 2), 256);
   if (ml_offset) *ml_offset = acc;
   return acc + rows * 2 * 4;
 }
@@ -941,7 +941,7 @@ size_t partial_bytes(const ring* r, int32_t n_split, size_t* ml_offset) {
 // The attention launches of a checked call, split partials in part_acc /
 // part_ml (sized for the launch's splits).
 int attn_launch(ring* r, int32_t layer, const void* q, const void* k_noise, const void* v_noise,
-                float* out, void* stream, float* part_acc, float* part_ml) {
+                float* out, void* stream, uint16_t* part_acc, float* part_ml) {
   if (int e = use_device(r)) return e;
   hipStream_t s = static_cast<hipStream_t>(stream);
   r->last_stream = s;
@@ -1056,7 +1056,7 @@ int ring_attn_noalloc(ring_t* r, int32_t layer, const void* q, const void* k_noi
                 need, kStaticScratchBytes, r->cfg.n_seq, r->cfg.n_head_kv, n_split);
   uint8_t* base = static_cast<uint8_t*>(static_scratch(r->device));
   if (!base) return fail(RING_EDEVICE, "static scratch of device %d is not resolved", r->device);
-  return attn_launch(r, layer, q, k_noise, v_noise, out, stream, reinterpret_cast<float*>(base),
+  return attn_launch(r, layer, q, k_noise, v_noise, out, stream, reinterpret_cast<uint16_t*>(base),
                      reinterpret_cast<float*>(base + ml_off));
 }
 
@@ -1089,7 +1089,7 @@ int ring_profile_floor(ring_t* r, int32_t layer, int32_t kind, void* stream) {
   AttnArgs a;
   const int32_t n_split = attn_geometry(r, layer, &a, nullptr);
   const size_t part_bytes =
-      (size_t)r->cfg.n_seq * r->cfg.n_head_kv * r->L.n_split * r->L.mpad * kHeadDim * 4;
+      (size_t)r->cfg.n_seq * r->cfg.n_head_kv * r->L.n_split * r->L.mpad * kHeadDim * 2;
   const bool with_partials = kind == RING_FLOOR_PARTIALS || kind == RING_FLOOR_LAST_ARRIVER ||
                              kind == RING_FLOOR_BARRIER || kind == RING_FLOOR_TWO_LAUNCH;
   if (with_partials && n_split < 2)

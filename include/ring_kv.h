@@ -303,14 +303,15 @@ int ring_attn(ring_t* r, int32_t layer, const void* q, const void* k_noise,
 /* ring_attn for callers that cannot allocate device memory (code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
  * same arguments, checks, kernels and results as ring_attn, but the split
- * partials of the attention (fp32 accumulators and (max, sum) pairs, for a
- * launch with more than one split) go to a static array of 16 MiB in the
+ * partials of the attention (each split's output normalised by its softmax
+ * sum in F16, and fp32 (max, sum) pairs, for a launch with more than one
+ * split) go to a static array of 16 MiB in the
  * library's device code instead of the ring's workspace.  The call allocates
  * and frees nothing; ring_init resolves the array's address once per device.
  * Every call on one GPU shares that GPU's array: two calls whose work
  * overlaps on the device (different streams, not ordered) race on it, so
  * order them on one stream.  Launches whose partials need more than 16 MiB
- * (n_seq x n_head_kv x splits x 32 or 64 query rows x 520 B) are refused.
+ * (n_seq x n_head_kv x splits x 32 or 64 query rows x 264 B) are refused.
  * Errors: as ring_attn, and RING_EINVAL when the partials exceed the array. */
 int ring_attn_noalloc(ring_t* r, int32_t layer, const void* q, const void* k_noise,
                       const void* v_noise, float* out, void* stream);
@@ -382,9 +383,9 @@ int ring_profile_read(ring_t* r, int32_t kernel, int32_t* n_launches, double* to
  *   RING_FLOOR_EMPTY         a kernel that returns at once (launch + drain)
  *   RING_FLOOR_READ          every visible K and V tile loaded once with the
  *                            attention's 16-byte loads, folded by xor
- *   RING_FLOOR_PARTIALS      RING_FLOOR_READ plus the 16 KiB fp32 split
- *                            partial (and its max/sum pairs) each work-group
- *                            of the attention stores
+ *   RING_FLOOR_PARTIALS      RING_FLOOR_READ plus the 8 KiB F16 split
+ *                            partial (and its fp32 max/sum pairs) each
+ *                            work-group of the attention stores
  *   RING_FLOOR_TWO_LAUNCH    RING_FLOOR_PARTIALS, then the ring's own merge
  *                            launch over those partials: the data movement
  *                            of ring_attn's two launches (timed as two

@@ -2,7 +2,7 @@
 against ring_attn, through the C ABI (needs the GPU).
 
 Two calls in a row share the static array: first a 4096-slot ring (32
-splits, 4.3 MB of partials), then a smaller 512-slot ring (4 splits): the
+splits, 2.2 MB of partials), then a smaller 512-slot ring (4 splits): the
 second must not see the first's leftovers.  Each is compared with ring_attn
 on the same ring state (same kernels, so bit for bit) and with the CPU oracle
 within the attention tolerance; a deferred (fused) step through
@@ -92,7 +92,7 @@ def test_noalloc_fused_step_against_oracle():
 
 
 def test_noalloc_refuses_partials_beyond_the_array():
-    """8 sequences x 8 KV heads x 64 splits x 32 rows x 520 B = 68 MB > 16 MiB."""
+    """8 sequences x 8 KV heads x 64 splits x 32 rows x 264 B = 34.6 MB > 16 MiB."""
     from draft_model_kv_amd import RingError
     from draft_model_kv_amd.ring import RING_EINVAL
     d = _ring(8192, seed=903, n_seq=8, n_split=64)
