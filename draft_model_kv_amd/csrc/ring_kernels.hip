@@ -514,12 +514,13 @@ struct FusedCtx {
 //   1. loads for the query build, for the wave's extra key row (a noise row,
 //      or in a fused launch one of the step's new rows) and for its first
 //      ring tile;
-//   2. the work-group rotates/scales/splits the queries into LDS; one barrier;
-//   3. a wave that owns an extra row rotates it (fp64, one rounding to F16),
-//      stores it to its ring row and folds it into its online softmax
-//      (dot products on the vector unit, P V on the matrix core) while its
-//      ring tile is still in flight (a fused launch's tile pass hides the
-//      new slots, which it attends this way);
+//   2. the work-group rotates/scales/splits the queries into LDS, and a wave
+//      that owns an extra row rotates it (fp64, one rounding to F16), stores
+//      it to its ring row and stages it in LDS; one barrier;
+//   3. that wave folds the row into its online softmax (dot products on the
+//      vector unit, P V on the matrix core) while its ring tile is still in
+//      flight (a fused launch's tile pass hides the new slots, which it
+//      attends this way);
 //   4. each wave streams its ring tiles;
 //   5. waves merge through LDS; the work-group writes its output or partial.
 // Every global load of the fast path is issued unconditionally from an
@@ -609,16 +610,14 @@ __device__ __forceinline__ void load_noise_row(const AttnArgs& a, const FusedCtx
 
 // Rotate extra row r at its position (fp64, one rounding to F16), store it
 // to its ring row (noise row r: row cap + r; new row j: slot (start + j) %
-// cap), and fold it into the wave's running softmax as one more key.  S = Q k
-// on the vector unit (dot products of the hi and lo query fragments with the
-// F16 key); the P V update is one matrix op per 32-dim block with the row as
-// slot 0 of a V fragment.
-template <int MB, bool FUSED, bool QL>
-__device__ __forceinline__ void attend_noise_row(
-    const AttnArgs& a, const FusedCtx& fx, const NoiseRow<MB>& nr, int r, uint16_t* kh,
-    uint16_t* vh, uint16_t* rowk, uint16_t* rowv, int lane, int hl, int col, const QFrag<MB, QL>& q,
-    const half8* q_lds, float (&m_run)[MB], float (&l_run)[MB], f32x16 (&o)[MB][4],
-    bool store_row, bool store_slot_pos) {
+// cap) and stage it in the wave's own LDS row buffer.  It needs neither the
+// queries nor the tiles, so a wave does it while its tile is in flight,
+// before the work-group's query barrier.
+template <int MB, bool FUSED>
+__device__ __forceinline__ void stage_extra_row(const AttnArgs& a, const FusedCtx& fx,
+                                                const NoiseRow<MB>& nr, int r, uint16_t* kh,
+                                                uint16_t* vh, uint16_t* rowk, uint16_t* rowv,
+                                                int lane, bool store_row, bool store_slot_pos) {
   double2 cs = nr.cs;
   int slot = a.cap + r;  // ring row of this layer and head
   if constexpr (FUSED) {
@@ -652,6 +651,18 @@ __device__ __forceinline__ void attend_noise_row(
   rowk[lane + 64] = ky;
   rowv[lane] = nr.vx;
   rowv[lane + 64] = nr.vy;
+}
+
+// Fold the staged extra row into the wave's running softmax as one more
+// key.  S = Q k on the vector unit (dot products of the hi and lo query
+// fragments with the F16 key); the P V update is one matrix op per 32-dim
+// block with the row as slot 0 of a V fragment.
+template <int MB, bool QL>
+__device__ __forceinline__ void attend_extra_row(const NoiseRow<MB>& nr, const uint16_t* rowk,
+                                                 const uint16_t* rowv, int lane, int hl, int col,
+                                                 const QFrag<MB, QL>& q, const half8* q_lds,
+                                                 float (&m_run)[MB], float (&l_run)[MB],
+                                                 f32x16 (&o)[MB][4]) {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
@@ -1200,6 +1211,14 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
     q_lds[((mb * 2 + 1) * 8 + c) * 64 + ln] = xl;
     q_lds[((mb * 2 + 1) * 8 + c + 4) * 64 + ln] = yl;
   }
+  // ---- 2b. the wave's first extra key row, rotated, stored and staged
+  //      before the barrier (its loads were issued with the queries').
+  uint16_t* rowk = reinterpret_cast<uint16_t*>(lds + S::kQBytes) + wave * 2 * kHeadDim;
+  uint16_t* rowv = rowk + kHeadDim;
+  const bool store_rows = row0 == 0;  // one row block stores the rotated rows
+  const bool store_sp = store_rows && g == 0;  // and KV head 0 their slot_pos entries
+  if (rank < n_extra)
+    stage_extra_row<MB, FUSED>(a, fx, nr, rank, kh, vh, rowk, rowv, lane, store_rows, store_sp);
   lds_barrier();
 
   QFrag<MB, QL> qf;
@@ -1224,17 +1243,12 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
   }
 
   // ---- 3. extra key rows (noise rows, and a fused launch's new rows).
-  uint16_t* rowk = reinterpret_cast<uint16_t*>(lds + S::kQBytes) + wave * 2 * kHeadDim;
-  uint16_t* rowv = rowk + kHeadDim;
   if (rank < n_extra) {
-    const bool store_rows = row0 == 0;  // one row block stores the rotated rows
-    const bool store_sp = store_rows && g == 0;  // and KV head 0 their slot_pos entries
-    attend_noise_row<MB, FUSED, QL>(a, fx, nr, rank, kh, vh, rowk, rowv, lane, hl, col, qf, q_lds, m_run,
-                         l_run, o, store_rows, store_sp);
+    attend_extra_row<MB, QL>(nr, rowk, rowv, lane, hl, col, qf, q_lds, m_run, l_run, o);
     for (int r = rank + n_waves; r < n_extra; r += n_waves) {
       load_noise_row<MB, FUSED>(a, fx, seq, g, r, mask_seq, qrow, lane, nr);
-      attend_noise_row<MB, FUSED, QL>(a, fx, nr, r, kh, vh, rowk, rowv, lane, hl, col, qf, q_lds, m_run,
-                           l_run, o, store_rows, store_sp);
+      stage_extra_row<MB, FUSED>(a, fx, nr, r, kh, vh, rowk, rowv, lane, store_rows, store_sp);
+      attend_extra_row<MB, QL>(nr, rowk, rowv, lane, hl, col, qf, q_lds, m_run, l_run, o);
     }
   }
 
