@@ -955,7 +955,9 @@ def main() -> int:
     step_mode = "mirror" if mirror else "batch" if batched else "fused" if fused else "eager"
     begin = R.ring_begin_step_deferred if fused else R.ring_begin_step
     attn, optr = R.ring_attn, out.data_ptr()
-    mwrite, mbegin = R.ring_mirror_write, R.ring_begin_step_mirror
+    # the mirror step's feature write is deferred: the projection launch of
+    # the step carries it out (one launch fewer per step)
+    mwrite, mbegin = R.ring_mirror_write_deferred, R.ring_begin_step_mirror
     mbegin_reg = R.ring_begin_step_mirror_registered
     begin_batch = R.ring_begin_step_batch
     if batched:
@@ -1098,11 +1100,12 @@ def main() -> int:
     roofline = roof_attn
     if mirror:
         # the projection launch of a decode step reads every layer's wk and wv
-        # once and the new rows' features (n <= a_step rows of d_model F16)
+        # once and the new rows' features (n <= a_step rows of d_model F16),
+        # and writes those features into the mirror (the deferred write)
         seg_rows = [sum(n for _, _, _, _, n in steps_in[0][t // pool][0])
                     for t in range(args.warmup + args.steps, total)]
         proj_bytes = (2 * w.n_layer * w.kv_row * w.d_model * 2 +
-                      float(np.mean(seg_rows)) * w.d_model * 2)
+                      2 * float(np.mean(seg_rows)) * w.d_model * 2)
         proj_us = prof["k_ring_project"]["avg_us"]
         pa = proj_bytes / (proj_us * 1e-6) / 1e9
         roofline = {"kernel": "k_ring_project", "weights": args.proj, "bound": "hbm",

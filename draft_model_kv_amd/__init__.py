@@ -11,6 +11,7 @@ from .ring import (Ring, RingConfig, RingError, RingGeometry, RingKvWeights, Rin
                    ring_begin_step_deferred, ring_begin_step_mirror, ring_begin_step_mirror_registered,
                    ring_set_kv_weights,
                    ring_describe, ring_free, ring_init, ring_last_error, ring_mirror_write,
+                   ring_mirror_write_deferred,
                    ring_plan_from_state, ring_plan_step, ring_query_geometry, ring_read_mask,
                    ring_read_mask_swa, ring_read_rows, ring_read_slot_pos, ring_read_state,
                    ring_profile_enable, ring_profile_read, ring_profile_floor,
@@ -24,6 +25,7 @@ __all__ = ["Ring", "RingConfig", "RingError", "RingGeometry", "RingKvWeights", "
            "ring_begin_step_deferred",
            "ring_begin_step_mirror", "ring_begin_step_mirror_registered", "ring_set_kv_weights",
            "ring_describe", "ring_free", "ring_init", "ring_last_error", "ring_mirror_write",
+           "ring_mirror_write_deferred",
            "ring_plan_from_state", "ring_plan_step", "ring_query_geometry", "ring_read_mask",
            "ring_read_mask_swa", "ring_read_rows", "ring_read_slot_pos", "ring_read_state",
            "ring_profile_enable", "ring_profile_read", "ring_profile_floor",

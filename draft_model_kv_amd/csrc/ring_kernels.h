@@ -81,6 +81,12 @@ constexpr int kProjSlice = 256;
 constexpr int kProjMaxKvHeads = 16;   // KV heads a ring with a feature mirror may have
 struct ProjArgs {
   const uint16_t* mirror;    // this sequence's fused features [cap][d_model] F16, slot p % cap
+  // A deferred mirror write carried out by this launch, or nullptr: the
+  // features of its rows [n_rows][d_model] F16 (row i at position pos0 + i),
+  // read from here instead of the mirror and stored into the mirror
+  // (mirror_w, the same array) by the work-groups of layer 0, head part 0.
+  const uint16_t* feat;
+  uint16_t* mirror_w;
   const uint16_t* wk;        // [n_layer][kv_row][d_model] F16 (packed: the packed K and V weights)
   const uint16_t* wv;        // [n_layer][kv_row][d_model] F16 (packed: unused)
   int32_t packed;            // weights in the kernel's load order (pack_weights below)

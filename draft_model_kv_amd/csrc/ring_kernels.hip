@@ -1507,7 +1507,7 @@ __global__ __launch_bounds__(128) void k_ring_project(ProjArgs a) {
   constexpr int kRowStride = kProjSlice / 8 + 1;  // half8 per staged row (+1: no bank conflicts)
   __shared__ half8 f_lds[32 * kRowStride];
   // every argument fetched in one batch at entry (see attn_entry)
-  asm volatile("" ::"s"(a.mirror), "s"(a.wk), "s"(a.wv), "s"(a.scratch), "s"(a.slot0),
+  asm volatile("" ::"s"(a.mirror), "s"(a.feat), "s"(a.wk), "s"(a.wv), "s"(a.scratch), "s"(a.slot0),
                "s"(a.n_rows), "s"(a.cap), "s"(a.d_model), "s"(a.kv_row), "s"(a.n_head_kv),
                "s"(a.n_ds), "s"(a.rcp_n_rt), "s"(a.rcp_n_ds), "s"(a.rcp_n_hh));
   const int lane = threadIdx.x & 63;
@@ -1532,15 +1532,21 @@ __global__ __launch_bounds__(128) void k_ring_project(ProjArgs a) {
 
   // features of the tile's rows, first (loads return in issue order, and
   // the LDS staging needs them): 32 rows x 32 chunks of 16 B, 8 per thread;
-  // row i sits in mirror slot (slot0 + i) % cap (slot0 < cap, i < 64)
+  // row i sits in mirror slot (slot0 + i) % cap (slot0 < cap, i < 64), or,
+  // for a deferred mirror write, at row i of a.feat (the source picked
+  // without a branch, so that the loads issue together)
   half8 fv[8];
+  int fslot[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const int c = threadIdx.x + 128 * k;
     const int row = c >> 5, dc = c & 31;
-    int slot = a.slot0 + min(r0 + row, a.n_rows - 1);
+    const int i = min(r0 + row, a.n_rows - 1);
+    int slot = a.slot0 + i;
     while (slot >= a.cap) slot -= a.cap;
-    const uint16_t* src = a.mirror + (int64_t)slot * a.d_model + d0 + 8 * dc;
+    fslot[k] = slot;
+    const uint16_t* src = a.feat ? a.feat + (int64_t)i * a.d_model + d0 + 8 * dc
+                                 : a.mirror + (int64_t)slot * a.d_model + d0 + 8 * dc;
     fv[k] = *(const half8*)src;
   }
 
@@ -1573,6 +1579,16 @@ __global__ __launch_bounds__(128) void k_ring_project(ProjArgs a) {
   for (int k = 0; k < 8; ++k) {
     const int c = threadIdx.x + 128 * k;
     f_lds[(c >> 5) * kRowStride + (c & 31)] = fv[k];
+  }
+  // a deferred mirror write: the work-groups of layer 0, head part 0 (one
+  // per d-slice and row tile) store the rows' features into their slots
+  if (a.feat && layer == 0 && hh == 0) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int c = threadIdx.x + 128 * k;
+      if (r0 + (c >> 5) < a.n_rows)
+        *(half8*)(a.mirror_w + (int64_t)fslot[k] * a.d_model + d0 + 8 * (c & 31)) = fv[k];
+    }
   }
   lds_barrier();
 

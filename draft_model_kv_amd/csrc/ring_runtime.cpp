@@ -194,6 +194,14 @@ Plan plan_of(int64_t cap, int64_t a_step, int64_t committed, int64_t next_pos, i
 // A sequence's deferred fold-in step (ring_begin_step_deferred): its rows are
 // appended, layer by layer, by the next attention launch of each layer, and
 // the first such launch also rebuilds the index state.
+// A sequence's deferred mirror write (ring_mirror_write_deferred): the rows
+// of positions [pos0, pos0 + n) are still in the caller's buffer.
+struct MirrorPending {
+  bool active = false;
+  int64_t pos0 = 0, n = 0;
+  const uint16_t* features = nullptr;
+};
+
 struct Pending {
   bool active = false;
   const uint16_t* k = nullptr;  // [n_layer][n_new][kv_row] F16, not rotated
@@ -232,6 +240,8 @@ struct ring {
   bool weights_set = false;
   std::vector<int64_t> next_pos, held_lo, committed;
   std::vector<std::vector<int64_t>> mirror_pos;  // per sequence: position in each mirror slot, -1 empty
+                                                 // (a deferred write's rows included)
+  std::vector<MirrorPending> mirror_pending;      // per sequence
   std::vector<Pending> pending;                   // per sequence
   // per sequence: slot_pos is current but the masks and the noise RoPE table
   // still hold an earlier step's (a fused launch wrote the new rows' slot_pos
@@ -446,6 +456,7 @@ int ring_init(const ring_config* cfg, void* workspace, size_t workspace_bytes, v
     r->wpack = reinterpret_cast<uint16_t*>(r->ws + r->L.off_wpack);
     r->knorm = reinterpret_cast<float*>(r->ws + r->L.off_knorm);
     r->mirror_pos.assign(cfg->n_seq, std::vector<int64_t>(cfg->cap, -1));
+    r->mirror_pending.assign(cfg->n_seq, MirrorPending{});
   }
   r->pending.assign(cfg->n_seq, Pending{});
   r->index_owed.assign(cfg->n_seq, 0);
@@ -708,26 +719,33 @@ int ring_begin_step_deferred(ring_t* r, int32_t seq, int64_t committed, const vo
   return ok();
 }
 
-int ring_mirror_write(ring_t* r, int32_t seq, int64_t pos0, int64_t n, const void* features,
-                      void* stream) {
+namespace {
+int check_mirror_write(const ring* r, int32_t seq, int64_t pos0, int64_t n, const void* features) {
   if (!r) return fail(RING_EINVAL, "ring is NULL");
   if (!r->mirror) return fail(RING_ESTATE, "the ring has no feature mirror (d_model = 0)");
   if (seq < 0 || seq >= r->cfg.n_seq) return fail(RING_ERANGE, "seq %d out of range", seq);
   if (pos0 < 0 || n < 0 || pos0 + n + r->cfg.q_len > INT32_MAX)
     return fail(RING_ERANGE, "positions [%lld, %lld) out of range", (long long)pos0,
                 (long long)(pos0 + n));
-  if (n == 0) return ok();
-  if (!features) return fail(RING_EINVAL, "features is NULL");
-  if (int e = use_device(r)) return e;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  r->last_stream = s;
-  // Only the last cap rows can stay: earlier ones share their slots with later ones.
+  if (n > 0 && !features) return fail(RING_EINVAL, "features is NULL");
+  return RING_OK;
+}
+
+// Only the last cap rows of a write can stay: earlier ones share their slots
+// with later ones.  Returns the first position that stays.
+int64_t mirror_first_kept(const ring* r, int64_t pos0, int64_t n) {
+  return pos0 + std::max<int64_t>(0, n - r->cfg.cap);
+}
+
+// Copy the rows of positions [pos0, pos0 + n) (features row i = position
+// pos0 + i) into sequence seq's mirror, slot p % cap.
+int mirror_copy(ring* r, int32_t seq, int64_t pos0, int64_t n, const void* features,
+                hipStream_t s) {
   const int64_t cap = r->cfg.cap, d = r->cfg.d_model;
-  const int64_t skip = std::max<int64_t>(0, n - cap);
-  const int64_t first = pos0 + skip, m = n - skip;
+  const int64_t first = mirror_first_kept(r, pos0, n), m = pos0 + n - first;
   const int64_t s0 = first % cap;
   const int64_t piece1 = std::min<int64_t>(m, cap - s0);
-  const uint8_t* src = static_cast<const uint8_t*>(features) + skip * d * 2;
+  const uint8_t* src = static_cast<const uint8_t*>(features) + (first - pos0) * d * 2;
   uint16_t* base = r->mirror + (int64_t)seq * cap * d;
   hipError_t e = hipMemcpyAsync(base + s0 * d, src, (size_t)(piece1 * d * 2),
                                 hipMemcpyDeviceToDevice, s);
@@ -735,8 +753,55 @@ int ring_mirror_write(ring_t* r, int32_t seq, int64_t pos0, int64_t n, const voi
     e = hipMemcpyAsync(base, src + piece1 * d * 2, (size_t)((m - piece1) * d * 2),
                        hipMemcpyDeviceToDevice, s);
   if (e != hipSuccess) return fail(RING_EDEVICE, "mirror copy: %s", hipGetErrorString(e));
+  return RING_OK;
+}
+
+// Positions [first kept, pos0 + n) are held by the mirror (or will be, once
+// a deferred write lands).
+void mirror_record(ring* r, int32_t seq, int64_t pos0, int64_t n) {
   std::vector<int64_t>& mp = r->mirror_pos[seq];
-  for (int64_t p = first; p < pos0 + n; ++p) mp[p % cap] = p;
+  for (int64_t p = mirror_first_kept(r, pos0, n); p < pos0 + n; ++p) mp[p % r->cfg.cap] = p;
+}
+
+// A deferred mirror write of seq still owed, copied now on stream s.
+int flush_mirror(ring* r, int32_t seq, hipStream_t s) {
+  MirrorPending& m = r->mirror_pending[seq];
+  if (!m.active) return RING_OK;
+  const MirrorPending w = m;
+  if (int e = mirror_copy(r, seq, w.pos0, w.n, w.features, s)) return e;
+  m = MirrorPending{};
+  return RING_OK;
+}
+}  // namespace
+
+int ring_mirror_write(ring_t* r, int32_t seq, int64_t pos0, int64_t n, const void* features,
+                      void* stream) {
+  if (int e = check_mirror_write(r, seq, pos0, n, features)) return e;
+  if (n == 0) return ok();
+  if (int e = use_device(r)) return e;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  r->last_stream = s;
+  // an earlier deferred write lands first (a later write to its slots wins)
+  if (int e = flush_mirror(r, seq, s)) return e;
+  if (int e = mirror_copy(r, seq, pos0, n, features, s)) return e;
+  mirror_record(r, seq, pos0, n);
+  return ok();
+}
+
+int ring_mirror_write_deferred(ring_t* r, int32_t seq, int64_t pos0, int64_t n,
+                               const void* features, void* stream) {
+  if (int e = check_mirror_write(r, seq, pos0, n, features)) return e;
+  if (n == 0) return ok();
+  if (int e = use_device(r)) return e;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  r->last_stream = s;
+  if (int e = flush_mirror(r, seq, s)) return e;
+  MirrorPending& m = r->mirror_pending[seq];
+  m.active = true;
+  m.pos0 = pos0;
+  m.n = n;
+  m.features = static_cast<const uint16_t*>(features);
+  mirror_record(r, seq, pos0, n);
   return ok();
 }
 
@@ -798,6 +863,14 @@ int ring_begin_step_mirror(ring_t* r, int32_t seq, int64_t committed, const ring
   if (int e = flush_seq(r, seq)) return e;
   hipStream_t s = static_cast<hipStream_t>(stream);
   r->last_stream = s;
+  // A deferred mirror write of exactly this step's rows (one projection
+  // launch) is carried out by that launch; any other is copied first.
+  MirrorPending& mw = r->mirror_pending[seq];
+  const bool fuse_write = mw.active && p.n_new > 0 && p.n_new <= kProjRows &&
+                          mw.pos0 == p.start && mw.n == p.n_new;
+  if (!fuse_write) {
+    if (int e = flush_mirror(r, seq, s)) return e;
+  }
 
   StepArgs a = step_args(r, seq);
   a.start = p.start;
@@ -812,6 +885,10 @@ int ring_begin_step_mirror(ring_t* r, int32_t seq, int64_t committed, const ring
   a.n_ds = r->L.n_ds;
   ProjArgs pa{};
   pa.mirror = r->mirror + (int64_t)seq * r->cfg.cap * r->cfg.d_model;
+  if (fuse_write) {
+    pa.feat = mw.features;
+    pa.mirror_w = r->mirror + (int64_t)seq * r->cfg.cap * r->cfg.d_model;
+  }
   pa.wk = w ? static_cast<const uint16_t*>(w->wk) : r->wpack;
   pa.wv = w ? static_cast<const uint16_t*>(w->wv) : nullptr;
   pa.packed = w ? 0 : 1;
@@ -844,6 +921,7 @@ int ring_begin_step_mirror(ring_t* r, int32_t seq, int64_t committed, const ring
     if (int e = check_launch(launch_step(a, s, t0, t1), "append from features")) return e;
     row0 += n;
   } while (row0 < p.n_new);
+  if (fuse_write) mw = MirrorPending{};
   set_state(r, seq, committed, p);
   return ok();
 }

@@ -30,7 +30,7 @@ RING_MAX_SEQ = 64
 # Every function the header declares, in header order.
 EXPORTS = (
     "ring_query_geometry", "ring_init", "ring_plan_step", "ring_plan_from_state",
-    "ring_begin_step", "ring_begin_step_deferred", "ring_begin_step_batch", "ring_mirror_write", "ring_set_kv_weights", "ring_begin_step_mirror", "ring_attn", "ring_attn_noalloc",
+    "ring_begin_step", "ring_begin_step_deferred", "ring_begin_step_batch", "ring_mirror_write", "ring_mirror_write_deferred", "ring_set_kv_weights", "ring_begin_step_mirror", "ring_attn", "ring_attn_noalloc",
     "ring_free",
     "ring_last_error", "ring_describe",
     "ring_read_slot_pos", "ring_read_mask", "ring_read_mask_swa", "ring_read_rows",
@@ -105,6 +105,7 @@ def _load() -> ctypes.CDLL:
         "ring_begin_step_deferred": [P, I32, I64, P, P, I64, P],
         "ring_begin_step_batch": [P, I32, P, P, P, P, P, P],
         "ring_mirror_write": [P, I32, I64, I64, P, P],
+        "ring_mirror_write_deferred": [P, I32, I64, I64, P, P],
         "ring_set_kv_weights": [P, ctypes.POINTER(RingKvWeights), P],
         "ring_begin_step_mirror": [P, I32, I64, ctypes.POINTER(RingKvWeights), P],
         "ring_attn": [P, I32, P, P, P, P, P],
@@ -208,6 +209,12 @@ def ring_begin_step_batch(handle: int, seqs, committed, k_new, v_new, n_rows,
     a_n = (ctypes.c_int64 * max(n, 1))(*n_rows)
     _check(_lib.ring_begin_step_batch(handle, n, a_seq, a_com, a_k, a_v, a_n, stream or None),
            "ring_begin_step_batch")
+
+
+def ring_mirror_write_deferred(handle: int, seq: int, pos0: int, n: int, features: int,
+                               stream: int = 0) -> None:
+    _check(_lib.ring_mirror_write_deferred(handle, seq, pos0, n, features or None, stream or None),
+           "ring_mirror_write_deferred")
 
 
 def ring_mirror_write(handle: int, seq: int, pos0: int, n: int, features: int,
@@ -389,13 +396,16 @@ class Ring:
             ns.append(n)
         ring_begin_step_batch(self.handle, seqs, com, kp, vp, ns, self._stream())
 
-    def mirror_write(self, seq: int, pos0: int, features) -> None:
-        """features: F16 [n, d_model] of positions [pos0, pos0 + n)."""
+    def mirror_write(self, seq: int, pos0: int, features, deferred: bool = False) -> None:
+        """features: F16 [n, d_model] of positions [pos0, pos0 + n).  deferred:
+        ring_mirror_write_deferred (the tensor must stay alive and unchanged
+        until the next begin_step_mirror of the sequence)."""
         torch = self._torch
         n = features.shape[0]
-        ring_mirror_write(self.handle, seq, pos0, n,
-                          self._ptr(features, torch.float16, (n, self.cfg.d_model), "features"),
-                          self._stream())
+        fn = ring_mirror_write_deferred if deferred else ring_mirror_write
+        fn(self.handle, seq, pos0, n,
+           self._ptr(features, torch.float16, (n, self.cfg.d_model), "features"),
+           self._stream())
 
     def set_kv_weights(self, wk, wv, k_norm, eps: float) -> None:
         """Register the projection weights (shapes as for begin_step_mirror)."""

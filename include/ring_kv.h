@@ -250,6 +250,19 @@ typedef struct ring_kv_weights {
 int ring_mirror_write(ring_t* r, int32_t seq, int64_t pos0, int64_t n,
                       const void* features, void* stream);
 
+/* ring_mirror_write whose copy is left to the next projection of the
+ * sequence: the same checks and result, but the rows stay in the caller's
+ * buffer until then.  When the sequence's next ring_begin_step_mirror
+ * projects exactly positions [pos0, pos0 + n) in one launch (a decode step:
+ * n = n_new <= 64), that launch reads their features from `features` and
+ * also writes them into the mirror, so the step has one launch fewer; any
+ * other call that needs them first (another mirror write of the sequence,
+ * a begin_step_mirror of other rows) copies them as ring_mirror_write does,
+ * on its own stream.  `features` must stay valid and unchanged until that
+ * happens.  Errors: as ring_mirror_write.                                   */
+int ring_mirror_write_deferred(ring_t* r, int32_t seq, int64_t pos0, int64_t n,
+                               const void* features, void* stream);
+
 /* Register the projection weights of every layer once (the draft model's
  * wk / wv and k_norm are constant: the page's test log, item 4 of the list
  * of refuted hypotheses, names the projection as the shallow injection

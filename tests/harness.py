@@ -117,14 +117,15 @@ class Driver:
 
     def __init__(self, w: W.Workload, n_split: Optional[int] = None, device: str = "cuda:0",
                  row_blocks: Optional[bool] = None, registered_weights: bool = False,
-                 merge: Optional[str] = None):
+                 merge: Optional[str] = None, mirror_deferred: bool = False):
         """n_split: attention splits forced; row_blocks: False puts both
         32-row query blocks of a KV head in one work-group; merge: "kernel"
         merges the splits inside the attention launch where the library
         supports it, instead of in a launch of its own (the library reads
         these settings when the ring is created); registered_weights: rows from
         features go through the weights registered with ring_set_kv_weights
-        instead of the caller's."""
+        instead of the caller's; mirror_deferred: features written with
+        ring_mirror_write_deferred (kept alive until the next step)."""
         import torch
         from draft_model_kv_amd import Ring
         self.torch = torch
@@ -169,6 +170,8 @@ class Driver:
             self.kn_t = torch.from_numpy(self.kn).to(self.dev)
             self.orc_mirror = [ro.FeatureMirror(w.cap, w.d_model) for _ in range(w.n_seq)]
             self.registered = registered_weights
+            self.mirror_deferred = mirror_deferred
+            self._keep_feat = []
             if registered_weights:
                 self.ring.set_kv_weights(self.wk_t, self.wv_t, self.kn_t, self.eps)
             # (position, epoch) in each mirror slot, as written to both mirrors
@@ -211,7 +214,10 @@ class Driver:
             for e in np.unique(pe):
                 sel = pe == e
                 f[sel] = W.fused_features(w, seq, pos[sel], int(e))
-            self.ring.mirror_write(seq, a, self.torch.from_numpy(f).to(self.dev))
+            ft = self.torch.from_numpy(f).to(self.dev)
+            self.ring.mirror_write(seq, a, ft, deferred=self.mirror_deferred)
+            if self.mirror_deferred:
+                self._keep_feat.append(ft)
             self.orc_mirror[seq].write(pos, f)
             for p, e in zip(pos, pe):
                 held[int(p) % w.cap] = (int(p), int(e))
@@ -282,6 +288,10 @@ class Driver:
                                             self.eps)
             self.orc[seq].commit_features(op, self.orc_mirror[seq], list(self.wk), list(self.wv),
                                           list(self.kn), self.eps)
+            if self.mirror_deferred:
+                # the deferred rows are in the mirror once the stream has passed the step
+                self.torch.cuda.synchronize(self.dev)
+                self._keep_feat = []
             self.committed[seq] = committed
             return op
         k, v = self.rows(seq, pos)

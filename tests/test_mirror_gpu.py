@@ -53,6 +53,44 @@ def test_mirror_streams(commits):
     d.close()
 
 
+@pytest.mark.parametrize("commits", [
+    [40, 41, 47, 59, 64, 70, 90, 91],          # fold-ins: each write carried out by the projection
+    [200, 201, 209, 218],                      # a bulk (its write copied first), then folds
+    [50, 40, 45, 20, 64, 70],                  # rewinds: writes of other rows than the step's
+    [200, 150, 151, 300, 290, 291],
+    [5, 5, 6, 6],
+], ids=["fold_wrap", "bulk_chunks", "rewind_near", "rewind_far", "zero_rows"])
+def test_mirror_streams_deferred_writes(commits):
+    """ring_mirror_write_deferred: the step's features are written into the
+    mirror by the projection launch when it projects exactly those rows, else
+    copied before; the same parity as eager writes."""
+    d = Driver(small(seed=205), mirror_deferred=True)
+    run(d, commits)
+    d.close()
+
+
+def test_deferred_and_eager_mirror_writes_bit_for_bit():
+    """The same stream with deferred and with eager mirror writes (registered
+    weights): identical ring rows, attention outputs and mirror contents (the
+    next steps project from what the deferred writes left in the mirror)."""
+    w = small(d_model=512, seed=206, n_layer=2, cap=100, q_len=3, n_head=16, n_head_kv=4)
+    a = Driver(w, registered_weights=True)
+    b = Driver(w, registered_weights=True, mirror_deferred=True)
+    for t, c in enumerate([70, 71, 75, 76, 90, 140, 141, 150, 60, 61]):
+        a.step(0, c)
+        b.step(0, c)
+        for layer in range(w.n_layer):
+            ka, va = a.ring.rows(0, layer, 0, a.geo.cap)
+            kb, vb = b.ring.rows(0, layer, 0, b.geo.cap)
+            assert np.array_equal(ka.view(np.uint16), kb.view(np.uint16)), (t, layer)
+            assert np.array_equal(va.view(np.uint16), vb.view(np.uint16)), (t, layer)
+            assert np.array_equal(a.attn(layer, t)[0], b.attn(layer, t)[0]), (t, layer)
+        b.check_index(0)
+    b.check_attn(0, 200)
+    a.close()
+    b.close()
+
+
 @pytest.mark.parametrize("d_model", [512, 768, 2048])
 def test_mirror_feature_widths(d_model):
     """Several d-slices per row (2, 3 and 8 slices of 256 feature dims)."""
@@ -185,11 +223,13 @@ def test_registered_weights_needed_for_null():
     d.close()
 
 
-def test_mirror_stream_full_registered():
+@pytest.mark.parametrize("deferred", [False, True], ids=["eager_writes", "deferred_writes"])
+def test_mirror_stream_full_registered(deferred):
     """The full-size workload through registered weights: 4096-token prompt,
-    then 40 decode steps."""
+    then 40 decode steps (the bench's mirror step writes its features with
+    ring_mirror_write_deferred)."""
     w = W.WORKLOADS["mirror_stream"]
-    d = Driver(w, registered_weights=True)
+    d = Driver(w, registered_weights=True, mirror_deferred=deferred)
     stream = W.commit_stream(w, 0)[: 1 + 40]
     for t, c in enumerate(stream):
         d.step(0, c)
