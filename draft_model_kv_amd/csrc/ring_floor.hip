@@ -7,7 +7,7 @@
 // ring's visible window, but with a trivial consumer instead of the softmax:
 //   kind 0  empty kernel (launch and drain only)
 //   kind 1  every visible K and V tile loaded once (16-byte loads per lane,
-//           the attention's fragment order) and folded by xor
+//           the attention's fragment order and tile walk) and folded by xor
 //   kind 2  kind 1, then the work-group's 8 KiB F16 split partial and its
 //           fp32 (max, sum) pairs stored where the attention stores them
 //   kind 3  kind 2 with an in-kernel cross-split merge by the last arriver:
@@ -101,8 +101,14 @@ __global__ __launch_bounds__(256) void k_ring_floor(FloorArgs a) {
       qh[e] = (_Float16)(0.01f * (float)(lane + e));
       ql[e] = (_Float16)(1e-4f * (float)(lane - e));
     }
+    // the attention's tile walk: a start of its own per (unit, split) when
+    // its waves stream several tiles
+    const int n = t1 - t0;
+    const int rot = a.rotate && n > 0 ? ((unit * 5 + split * 3) * 4) % n : 0;
     for (int t = t0 + wave; t < t1; t += 4) {
-      int rt = first + t;
+      int j = t + rot;
+      if (j >= t1) j -= n;
+      int rt = first + j;
       if (rt >= a.ring_tiles) rt -= a.ring_tiles;
       const u32x4* kt = (const u32x4*)(kh + (int64_t)rt * kTileHalves);
       const u32x4* vt = (const u32x4*)(vh + (int64_t)rt * kTileHalves);

@@ -217,6 +217,7 @@ struct FloorArgs {
   uint32_t* err;             // bounded-wait timeouts
   uint32_t epoch;            // kind 4: launches of that kind since the counters were zeroed
   int32_t n_seq, n_head_kv, n_split, n_rb, ring_tiles;
+  int32_t rotate;            // the attention's tile walk starts per (unit, split): its waves stream several tiles
   uint64_t rcp_per_unit, rcp_n_rb, rcp_n_head_kv, rcp_n_split;
   int32_t vis_first[RING_MAX_SEQ_INTERNAL];
   int32_t vis_count[RING_MAX_SEQ_INTERNAL];

@@ -1221,6 +1221,11 @@ int ring_profile_floor(ring_t* r, int32_t layer, int32_t kind, void* stream) {
     f.vis_first[i] = a.vis_first[i];
     f.vis_count[i] = a.vis_count[i];
   }
+  {
+    AttnArgs sa = a;
+    sa.n_split = n_split;
+    f.rotate = attn_short_waves(sa) ? 0 : 1;
+  }
   hipEvent_t t0, t1;
   next_events(r, RING_KERNEL_FLOOR, &t0, &t1);
   const int fk = kind == RING_FLOOR_TWO_LAUNCH ? RING_FLOOR_PARTIALS : kind;
