@@ -35,6 +35,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -578,6 +579,37 @@ def summarize_floor(out_dir: str, khash: str) -> str:
     return p_
 
 
+def projection_segments(out_dir: str, run: str, decode_grid: int) -> dict:
+    """Durations of the projection dispatches in a mirror_stream kernel
+    trace: the decode-step launches (grid `decode_grid` threads, one per
+    step) cut at the bench's segments -- warm-up, timed steps and the
+    event-profiled steps cycle the pool's rings (cold weights), the last
+    segment runs ring 0 alone (its weights stay in the Infinity Cache) --
+    and the prefill's launches.  {name: (dispatches, median us, mean us)}."""
+    import statistics as stt
+    rows = sorted(_csv_rows(out_dir, run, "kernel_trace"), key=lambda r: int(r["Start_Timestamp"]))
+    proj = [r for r in rows if "k_ring_project" in r["Kernel_Name"]]
+    dur = lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3  # noqa: E731
+    dec = [dur(r) for r in proj if int(r["Grid_Size_X"]) == decode_grid]
+    pre = [dur(r) for r in proj if int(r["Grid_Size_X"]) != decode_grid]
+    out = {}
+    if pre:
+        out["prefill (64-row launches)"] = (len(pre), stt.median(pre), stt.mean(pre))
+    cmd = PROFILE_RUNS[run]
+    warm = int(re.search(r"--warmup (\d+)", cmd).group(1))
+    steps = int(re.search(r"--steps (\d+)", cmd).group(1))
+    cuts = (("decode steps: warm-up (pool cycled, cold)", 0, warm),
+            ("decode steps: timed (pool cycled, cold)", warm, warm + steps),
+            ("decode steps: event-profiled (pool cycled, cold)", warm + steps, warm + 2 * steps),
+            ("decode steps: ring 0 alone (its weights in the Infinity Cache)", warm + 2 * steps,
+             len(dec)))
+    for name, a, b in cuts:
+        v = dec[a:b]
+        if v:
+            out[name] = (len(v), stt.median(v), stt.mean(v))
+    return out
+
+
 def summarize_mirror(out_dir: str, khash: str, fetch_scale: float, write_scale: float):
     """Kernel trace and HBM traffic of the mirror_stream workload (rows from
     the feature mirror through the projection kernel)."""
@@ -602,18 +634,31 @@ def summarize_mirror(out_dir: str, khash: str, fetch_scale: float, write_scale: 
         short = next((k for k in KERNELS_MIRROR if k in name), None)
         if short and short not in trace:
             trace[short] = float(r["AverageNs"]) / 1e3
+    # decode-step projection launches: one 32-row tile (grid = layers x 4
+    # half head parts per KV head x d-slices work-groups of 128 threads, in
+    # threads); the prefill's 64-row launches have two
+    decode_grid = w.n_layer * 4 * w.n_head_kv * (w.d_model // 256) * 128
+    seg = projection_segments(out_dir, "prof_ktrace_mirror", decode_grid)
+    if seg:
+        lines += ["", "k_ring_project per dispatch in this trace (start to end timestamps), "
+                  "decode-step launches (one 32-row tile) in the order the bench runs them, "
+                  "and the prefill's 64-row launches apart:", "",
+                  "| launches | dispatches | median us | mean us |", "|---|---:|---:|---:|"]
+        for name, (n, med, mean) in seg.items():
+            lines.append(f"| {name} | {n} | {med:.2f} | {mean:.2f} |")
     if bl:
         ev = {k: v["avg_us"] for k, v in bl.get("kernels", {}).items()}
         lines += ["", f"The same bench without the profiler (`{PROFILE_RUNS['bench_plain_mirror']}`), "
                   "HIP events bound to the dispatches of its profiled segment: "
                   + ", ".join(f"{k} {v:.2f} us" for k, v in ev.items() if v)
                   + f"; {bl['value']:.0f} steps/s in its timed segment."]
+        if bl.get("floors"):
+            lines += ["", "Floors of the projection launch in the same bench run (ring_profile_floor "
+                      "kind RING_FLOOR_PROJ_READ: the projection's grid and weight loads with a "
+                      "trivial consumer, cycled over the pool's weight copies; ceiling_frac "
+                      f"{bl.get('ceiling_frac')}):", ""] + floor_table(bl["floors"])
     with open(os.path.join(prof, "k_ring_project_mirror_stream_kernel_trace.md"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
-    # decode-step projection launches: one 32-row tile (grid = layers x K/V
-    # heads x d-slices work-groups of 256 threads); the prefill's 64-row
-    # launches have two
-    decode_grid = w.n_layer * 2 * w.n_head_kv * (w.d_model // 256) * 256
     rows = {}
     for k, grid in (("k_ring_project", decode_grid), ("k_ring_project (prefill)", 2 * decode_grid)):
         f, nf = _kib_per_dispatch(out_dir, "pmc_fetch_mirror", "FETCH_SIZE",
@@ -700,6 +745,9 @@ def summarize_wide(out_dir: str, wl_name: str, khash: str, fetch_scale: float,
 
 FLOOR_KINDS = (("empty", 0), ("read", 1), ("partials", 2), ("two_launch", 5),
                ("last_arriver", 3), ("barrier", 4), ("matrix_math", 7), ("vector_math", 8))
+# the mirror step's projection launch: its grid with a trivial consumer of
+# the registered weights (every pool ring holds its own copy: cold)
+FLOOR_KINDS_MIRROR = (("empty", 0), ("proj_read", 9))
 
 
 def clock_warmup(dev, seconds: float, flush_mib: int) -> int:
@@ -722,7 +770,8 @@ def clock_warmup(dev, seconds: float, flush_mib: int) -> int:
     return n
 
 
-def floor_segment(rings, pool, launches, dev, R, attn_us, step_us, bytes_read, n_layer=1):
+def floor_segment(rings, pool, launches, dev, R, attn_us, step_us, bytes_read, n_layer=1,
+                  kinds=FLOOR_KINDS):
     """The ring_profile_floor kinds on layer 0, cycled over the pool (cold).
     Per launch: the device's back-to-back time (HIP events around a batch
     queued behind a RING_FLOOR_HOLD launch, so that the host's submission
@@ -731,7 +780,7 @@ def floor_segment(rings, pool, launches, dev, R, attn_us, step_us, bytes_read, n
     s = torch.cuda.current_stream(dev).cuda_stream
     fl = R.ring_profile_floor
     out = {"launches": launches, "layer": 0, "kv_bytes_read_per_launch": int(bytes_read)}
-    for name, kind in FLOOR_KINDS:
+    for name, kind in kinds:
         try:
             for t in range(min(pool, launches)):        # one launch per ring first
                 fl(rings[t % pool].handle, 0, kind, s)
@@ -1117,6 +1166,14 @@ def main() -> int:
     # algorithmic bytes (all layers) per step time
     step_bytes = per_call * w.n_layer
     floors, ceiling = None, None
+    if args.floor_launches and mirror:
+        floors, _ = floor_segment(rings, pool, args.floor_launches, dev, R, None, None,
+                                  2 * w.n_layer * w.kv_row * w.d_model * 2,
+                                  kinds=FLOOR_KINDS_MIRROR)
+        floors["weight_bytes_per_launch"] = floors.pop("kv_bytes_read_per_launch")
+        rd = floors.get("proj_read", {}).get("event_us")
+        if rd:
+            ceiling = {"proj_kernel": rd / proj_us}
     if args.floor_launches and not mirror:
         floors, ceiling = floor_segment(
             rings, pool, args.floor_launches, dev, R, attn_us, ms_per_step * 1e3,

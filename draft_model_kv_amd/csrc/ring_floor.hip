@@ -29,6 +29,10 @@
 //           fragments are stand-ins; the products are what is timed)
 //   kind 8  kind 1 plus the same 393,216 products per tile and wave on the
 //           vector unit (v_dot2_f32_f16), for the matrix-core A/B
+//   kind 9  the projection launch of a decode step instead (one 32-row tile):
+//           its grid of two-wave work-groups, each wave loading its 16 KiB of
+//           the packed weights as the projection does (16 loads of 1 KiB),
+//           folded by xor
 //   kind 6  one wave that sleeps for several milliseconds (a bounded loop of
 //           s_sleep): the host queues a batch of launches behind it, so that
 //           their back-to-back time on the device is not bounded by how fast
@@ -327,6 +331,44 @@ hipError_t launch_floor(const FloorArgs& args, int kind, hipStream_t s, hipEvent
     case 8: hipExtLaunchKernelGGL(k_ring_floor<8>, g, b, 0, s, t0, t1, 0, a); break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(128) void k_ring_floor_proj(ProjFloorArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // work-group -> (layer, half head part hh, d-slice), the projection's order
+  const uint32_t b1 = blockIdx.x;
+  const uint32_t b2 = quot32(b1, a.rcp_n_ds);
+  const int ds = (int)(b1 - b2 * a.n_ds);
+  const int n_hh = 4 * a.n_head_kv, n_hp = 2 * a.n_head_kv;
+  const int layer = (int)quot32(b2, a.rcp_n_hh);
+  const int hh = (int)(b2 - layer * n_hh);
+  const int pw = 2 * (hh & 1) + wave;
+  const u32x4* wp = (const u32x4*)a.wpack +
+                    ((((int64_t)layer * n_hp + (hh >> 1)) * a.n_ds + ds) * 4 + pw) * 1024;
+  u32x4 w[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) w[i] = wp[i * 64 + lane];
+  u32x4 x = w[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) x ^= w[i];
+  uint32_t v = x.x ^ x.y ^ x.z ^ x.w;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v ^= __shfl_xor(v, off);
+  if (lane == 0) a.out[blockIdx.x * 2 + wave] = (float)(v & 0xFFFFu);
+}
+
+hipError_t launch_floor_proj(const ProjFloorArgs& args, hipStream_t s, hipEvent_t t0,
+                             hipEvent_t t1) {
+  ProjFloorArgs a = args;
+  const uint32_t n_hh = 4 * a.n_head_kv;
+  const uint64_t grid = (uint64_t)a.n_layer * n_hh * a.n_ds;
+  if (a.n_ds < 1 || grid * a.n_ds > (uint64_t(1) << 32) || grid > (uint64_t(1) << 31))
+    return hipErrorInvalidValue;
+  a.rcp_n_ds = recip32(a.n_ds);
+  a.rcp_n_hh = recip32(n_hh);
+  hipExtLaunchKernelGGL(k_ring_floor_proj, dim3((unsigned)grid), dim3(128), 0, s, t0, t1, 0, a);
   return hipGetLastError();
 }
 

@@ -223,6 +223,15 @@ struct FloorArgs {
   int32_t vis_count[RING_MAX_SEQ_INTERNAL];
 };
 
+// Floor of the projection launch of a decode step (ring_profile_floor kind
+// 9): its grid for one 32-row tile and its weight loads, a trivial consumer.
+struct ProjFloorArgs {
+  const uint16_t* wpack;     // registered weights, packed (ProjArgs.wk with packed = 1)
+  float* out;                // one word per wave
+  int32_t n_layer, n_head_kv, n_ds;
+  uint64_t rcp_n_ds, rcp_n_hh;  // recip32 of n_ds and 4 n_head_kv (set by the launcher)
+};
+
 // t0 / t1: optional events bound to the dispatch (start and end of the
 // kernel itself), or nullptr.
 hipError_t launch_step(const StepArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
@@ -237,6 +246,7 @@ constexpr int kInKernelMergeMaxSplits = 16;
 hipError_t launch_attn_fused(const FusedAttnArgs& f, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
 hipError_t launch_project(const ProjArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
+hipError_t launch_floor_proj(const ProjFloorArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
 hipError_t launch_pack_weights(const PackArgs& a, hipStream_t s);
 hipError_t launch_fill_u16(uint16_t* p, uint16_t value, int64_t n, hipStream_t s);
 

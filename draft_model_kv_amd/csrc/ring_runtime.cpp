@@ -1145,15 +1145,20 @@ size_t floor_counter_bytes(const ring* r) {
   return (size_t)align_up((int64_t)r->cfg.n_seq * r->cfg.n_head_kv * r->L.n_rb * 4, 256);
 }
 size_t floor_out_bytes(const ring* r) {
-  return (size_t)r->cfg.n_seq * r->cfg.n_head_kv * r->L.n_rb * 32 * kHeadDim * 4;
+  // the attention floors' sums, or one word per wave of the projection floor
+  const size_t attn = (size_t)r->cfg.n_seq * r->cfg.n_head_kv * r->L.n_rb * 32 * kHeadDim * 4;
+  const size_t proj = (size_t)r->cfg.n_layer * 4 * r->cfg.n_head_kv * r->L.n_ds * 2 * 4;
+  return std::max(attn, proj);
 }
 }  // namespace
 
 int ring_profile_floor(ring_t* r, int32_t layer, int32_t kind, void* stream) {
   if (!r) return fail(RING_EINVAL, "ring is NULL");
   if (layer < 0 || layer >= r->cfg.n_layer) return fail(RING_ERANGE, "layer %d out of range", layer);
-  if (kind < RING_FLOOR_EMPTY || kind > RING_FLOOR_VECTOR_MATH)
+  if (kind < RING_FLOOR_EMPTY || kind > RING_FLOOR_PROJ_READ)
     return fail(RING_EINVAL, "floor kind %d out of range", kind);
+  if (kind == RING_FLOOR_PROJ_READ && !r->weights_set)
+    return fail(RING_ESTATE, "the projection floor reads registered weights (ring_set_kv_weights)");
   if (kind == RING_FLOOR_HOLD) {
     if (int e = use_device(r)) return e;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -1161,6 +1166,30 @@ int ring_profile_floor(ring_t* r, int32_t layer, int32_t kind, void* stream) {
     FloorArgs none{};
     return check_launch(launch_floor(none, kind, s, nullptr, nullptr), "floor hold launch")
                ? RING_EDEVICE : ok();
+  }
+  if (kind == RING_FLOOR_PROJ_READ) {
+    if (int e = use_device(r)) return e;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    r->last_stream = s;
+    if (!r->floor_buf) {
+      void* p = nullptr;
+      if (hipMalloc(&p, floor_counter_bytes(r) + 256 + floor_out_bytes(r)) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(RING_ENOMEM, "floor buffer allocation failed");
+      }
+      r->floor_buf = static_cast<uint8_t*>(p);
+      r->floor_last_kind = -1;
+    }
+    ProjFloorArgs f{};
+    f.wpack = r->wpack;
+    f.out = reinterpret_cast<float*>(r->floor_buf + floor_counter_bytes(r) + 256);
+    f.n_layer = r->cfg.n_layer;
+    f.n_head_kv = r->cfg.n_head_kv;
+    f.n_ds = r->L.n_ds;
+    hipEvent_t t0, t1;
+    next_events(r, RING_KERNEL_FLOOR, &t0, &t1);
+    if (int e = check_launch(launch_floor_proj(f, s, t0, t1), "projection floor launch")) return e;
+    return ok();
   }
   if (r->L.n_rb * 32 != r->L.mpad)
     return fail(RING_EINVAL, "floor launches need one work-group per 32-query block");

@@ -411,6 +411,15 @@ int ring_profile_read(ring_t* r, int32_t kernel, int32_t* n_launches, double* to
  *   RING_FLOOR_VECTOR_MATH   RING_FLOOR_READ plus the same 393,216 products
  *                            per tile and wave on the vector unit (v_dot2),
  *                            the other side of the matrix-core A/B
+ *   RING_FLOOR_PROJ_READ     the projection launch of ring_begin_step_mirror
+ *                            for one 32-row tile instead (page's notes on the
+ *                            port: the new rows' K/V come from the feature
+ *                            mirror through the draft's wk and wv): its grid
+ *                            of two-wave work-groups, each wave loading its
+ *                            16 KiB of the registered (packed) weights of
+ *                            every layer as the projection does, folded by
+ *                            xor; `layer` is only range-checked.  Needs
+ *                            ring_set_kv_weights first (else RING_ESTATE)
  *   RING_FLOOR_HOLD          one wave that sleeps for about 14 ms (a bounded
  *                            loop) and reads nothing: launches queued behind
  *                            it then run back to back on the device, however
@@ -443,6 +452,7 @@ int ring_profile_read(ring_t* r, int32_t kernel, int32_t* n_launches, double* to
 #define RING_FLOOR_HOLD          6
 #define RING_FLOOR_MATRIX_MATH   7
 #define RING_FLOOR_VECTOR_MATH   8
+#define RING_FLOOR_PROJ_READ     9
 int ring_profile_floor(ring_t* r, int32_t layer, int32_t kind, void* stream);
 
 /* Number of RING_FLOOR_BARRIER waits that ended by their poll limit rather

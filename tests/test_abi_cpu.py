@@ -28,6 +28,19 @@ def test_header_declares_the_binding_exports():
     assert header_functions() == sorted(rk.EXPORTS)
 
 
+def test_binding_constants_match_the_header():
+    """Every RING_* integer constant the header defines has the same value
+    in the Python binding (error codes, kernel kinds, floor kinds)."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    defs = dict(re.findall(r"^#define\s+(RING_\w+)\s+\(?(-?\d+)\)?\s*$", text, flags=re.M))
+    assert len(defs) >= 20
+    for name, value in defs.items():
+        if name == "RING_KV_H":
+            continue
+        assert hasattr(rk, name), name
+        assert getattr(rk, name) == int(value), name
+
+
 def test_library_exports_every_header_function():
     import ctypes
     lib = ctypes.CDLL(rk.LIB_PATH)

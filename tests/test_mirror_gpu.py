@@ -223,6 +223,27 @@ def test_registered_weights_needed_for_null():
     d.close()
 
 
+def test_projection_floor_kind():
+    """ring_profile_floor's projection kind (profiling only): refused until
+    weights are registered, then it runs between steps and the stream still
+    matches the oracle (it changes no state of the ring)."""
+    import torch
+    from draft_model_kv_amd import ring as rk
+    s = torch.cuda.current_stream().cuda_stream
+    d = Driver(small(seed=213))
+    with pytest.raises(rk.RingError) as e:
+        rk.ring_profile_floor(d.ring.handle, 0, rk.RING_FLOOR_PROJ_READ, s)
+    assert e.value.code == rk.RING_ESTATE
+    d.close()
+    d = Driver(small(seed=213, d_model=2048), registered_weights=True)
+    run(d, [40, 41])
+    for _ in range(3):
+        rk.ring_profile_floor(d.ring.handle, 0, rk.RING_FLOOR_PROJ_READ, s)
+    torch.cuda.synchronize()
+    run(d, [47, 59, 64])
+    d.close()
+
+
 @pytest.mark.parametrize("deferred", [False, True], ids=["eager_writes", "deferred_writes"])
 def test_mirror_stream_full_registered(deferred):
     """The full-size workload through registered weights: 4096-token prompt,
