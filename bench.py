@@ -1031,11 +1031,14 @@ def main() -> int:
             for layer, qp, knp, vnp in layers:
                 attn(h, layer, qp, knp, vnp, optr, s)
 
+    # clocks up and the Infinity Cache evicted, then the warm-up steps (they
+    # also warm the host's submission path: run before the clock warm-up,
+    # the first timed step took 31-40 us to submit instead of 8-11), then the
+    # timed steps: each cycles to the ring touched longest ago (pool x ring
+    # bytes >= 512 MB)
+    n_fills = clock_warmup(dev, args.warm_seconds, args.flush_mib)
     run(calls[:args.warmup])
     torch.cuda.synchronize(dev)
-    # clocks up and the Infinity Cache evicted, then the timed steps: each
-    # cycles to the ring touched longest ago (pool x ring bytes >= 512 MB)
-    n_fills = clock_warmup(dev, args.warm_seconds, args.flush_mib)
 
     if args.graph:
         print(json.dumps({"workload": args.workload, "step": step_mode, "ring_pool": pool,
