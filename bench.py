@@ -743,8 +743,9 @@ def summarize_wide(out_dir: str, wl_name: str, khash: str, fetch_scale: float,
     return path
 
 
-FLOOR_KINDS = (("empty", 0), ("read", 1), ("partials", 2), ("two_launch", 5),
-               ("last_arriver", 3), ("barrier", 4), ("matrix_math", 7), ("vector_math", 8))
+FLOOR_KINDS = (("empty", 0), ("read", 1), ("read_lockstep", 10), ("partials", 2),
+               ("two_launch", 5), ("last_arriver", 3), ("barrier", 4), ("matrix_math", 7),
+               ("vector_math", 8))
 # the mirror step's projection launch: its grid with a trivial consumer of
 # the registered weights (every pool ring holds its own copy: cold)
 FLOOR_KINDS_MIRROR = (("empty", 0), ("proj_read", 9))

@@ -19,7 +19,8 @@ from .ring import (Ring, RingConfig, RingError, RingGeometry, RingKvWeights, Rin
                    RING_KERNEL_MERGE, RING_KERNEL_PROJ, RING_KERNEL_FLOOR, RING_FLOOR_EMPTY,
                    RING_FLOOR_READ, RING_FLOOR_PARTIALS, RING_FLOOR_LAST_ARRIVER,
                    RING_FLOOR_BARRIER, RING_FLOOR_TWO_LAUNCH, RING_FLOOR_HOLD,
-                   RING_FLOOR_MATRIX_MATH, RING_FLOOR_VECTOR_MATH, RING_FLOOR_PROJ_READ)
+                   RING_FLOOR_MATRIX_MATH, RING_FLOOR_VECTOR_MATH, RING_FLOOR_PROJ_READ,
+                   RING_FLOOR_READ_LOCKSTEP)
 
 __all__ = ["Ring", "RingConfig", "RingError", "RingGeometry", "RingKvWeights", "RingPlan",
            "make_config", "ring_attn", "ring_attn_noalloc", "ring_begin_step", "ring_begin_step_batch",
@@ -34,4 +35,5 @@ __all__ = ["Ring", "RingConfig", "RingError", "RingGeometry", "RingKvWeights", "
            "RING_KERNEL_MERGE", "RING_KERNEL_PROJ", "RING_KERNEL_FLOOR", "RING_FLOOR_EMPTY",
            "RING_FLOOR_READ", "RING_FLOOR_PARTIALS", "RING_FLOOR_LAST_ARRIVER",
            "RING_FLOOR_BARRIER", "RING_FLOOR_TWO_LAUNCH", "RING_FLOOR_HOLD",
-           "RING_FLOOR_MATRIX_MATH", "RING_FLOOR_VECTOR_MATH", "RING_FLOOR_PROJ_READ"]
+           "RING_FLOOR_MATRIX_MATH", "RING_FLOOR_VECTOR_MATH", "RING_FLOOR_PROJ_READ",
+           "RING_FLOOR_READ_LOCKSTEP"]

@@ -1155,7 +1155,7 @@ size_t floor_out_bytes(const ring* r) {
 int ring_profile_floor(ring_t* r, int32_t layer, int32_t kind, void* stream) {
   if (!r) return fail(RING_EINVAL, "ring is NULL");
   if (layer < 0 || layer >= r->cfg.n_layer) return fail(RING_ERANGE, "layer %d out of range", layer);
-  if (kind < RING_FLOOR_EMPTY || kind > RING_FLOOR_PROJ_READ)
+  if (kind < RING_FLOOR_EMPTY || kind > RING_FLOOR_READ_LOCKSTEP)
     return fail(RING_EINVAL, "floor kind %d out of range", kind);
   if (kind == RING_FLOOR_PROJ_READ && !r->weights_set)
     return fail(RING_ESTATE, "the projection floor reads registered weights (ring_set_kv_weights)");
@@ -1253,11 +1253,13 @@ int ring_profile_floor(ring_t* r, int32_t layer, int32_t kind, void* stream) {
   {
     AttnArgs sa = a;
     sa.n_split = n_split;
-    f.rotate = attn_short_waves(sa) ? 0 : 1;
+    f.rotate = attn_short_waves(sa) || kind == RING_FLOOR_READ_LOCKSTEP ? 0 : 1;
   }
   hipEvent_t t0, t1;
   next_events(r, RING_KERNEL_FLOOR, &t0, &t1);
-  const int fk = kind == RING_FLOOR_TWO_LAUNCH ? RING_FLOOR_PARTIALS : kind;
+  const int fk = kind == RING_FLOOR_TWO_LAUNCH    ? RING_FLOOR_PARTIALS
+                 : kind == RING_FLOOR_READ_LOCKSTEP ? RING_FLOOR_READ
+                                                    : kind;
   if (int e = check_launch(launch_floor(f, fk, s, t0, t1), "floor launch")) return e;
   if (kind == RING_FLOOR_TWO_LAUNCH) {
     // the ring's own merge launch over those partials, into the floor buffer

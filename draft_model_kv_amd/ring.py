@@ -43,7 +43,8 @@ RING_KERNEL_FLOOR = 4
 # kinds of ring_profile_floor
 (RING_FLOOR_EMPTY, RING_FLOOR_READ, RING_FLOOR_PARTIALS, RING_FLOOR_LAST_ARRIVER,
  RING_FLOOR_BARRIER, RING_FLOOR_TWO_LAUNCH, RING_FLOOR_HOLD, RING_FLOOR_MATRIX_MATH,
- RING_FLOOR_VECTOR_MATH, RING_FLOOR_PROJ_READ) = 0, 1, 2, 3, 4, 5, 6, 7, 8, 9
+ RING_FLOOR_VECTOR_MATH, RING_FLOOR_PROJ_READ, RING_FLOOR_READ_LOCKSTEP) = (
+    0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10)
 
 
 class RingConfig(ctypes.Structure):

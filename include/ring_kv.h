@@ -420,6 +420,11 @@ int ring_profile_read(ring_t* r, int32_t kernel, int32_t* n_launches, double* to
  *                            every layer as the projection does, folded by
  *                            xor; `layer` is only range-checked.  Needs
  *                            ring_set_kv_weights first (else RING_ESTATE)
+ *   RING_FLOOR_READ_LOCKSTEP RING_FLOOR_READ with every work-group walking
+ *                            its split's tiles from the split's first one
+ *                            (the attention starts each walk at an offset of
+ *                            its own when its waves stream several tiles;
+ *                            this kind times the walk without it)
  *   RING_FLOOR_HOLD          one wave that sleeps for about 14 ms (a bounded
  *                            loop) and reads nothing: launches queued behind
  *                            it then run back to back on the device, however
@@ -453,6 +458,7 @@ int ring_profile_read(ring_t* r, int32_t kernel, int32_t* n_launches, double* to
 #define RING_FLOOR_MATRIX_MATH   7
 #define RING_FLOOR_VECTOR_MATH   8
 #define RING_FLOOR_PROJ_READ     9
+#define RING_FLOOR_READ_LOCKSTEP 10
 int ring_profile_floor(ring_t* r, int32_t layer, int32_t kind, void* stream);
 
 /* Number of RING_FLOOR_BARRIER waits that ended by their poll limit rather
