@@ -932,8 +932,8 @@ def main() -> int:
                     help="each ring's workspace: a torch tensor (default) or allocated by "
                          "ring_init itself")
     ap.add_argument("--warm-seconds", type=float, default=0.25,
-                    help="GPU clock warm-up before the timed steps (scratch writes that also "
-                         "evict the Infinity Cache)")
+                    help="GPU clock warm-up before the warm-up and timed steps (reads of a "
+                         "scratch buffer that also evict the rings from the Infinity Cache)")
     ap.add_argument("--flush-mib", type=int, default=512,
                     help="size of that scratch buffer (above the 256 MB Infinity Cache)")
     ap.add_argument("--floor-launches", type=int, default=400,
@@ -1208,9 +1208,10 @@ def main() -> int:
                    "n_layer": w.n_layer, "n_seq": w.n_seq, "kv_total": geo.kv_total,
                    "ring_pool": pool,
                    "infinity_cache": "cold" if pool * ring_bytes > (256 << 20) else "warm",
-                   "before_timing": f"{n_fills} writes of a {args.flush_mib} MiB scratch buffer "
-                                    f"over >= {args.warm_seconds} s (clocks up, Infinity Cache "
-                                    f"evicted); each timed step takes the ring touched longest ago",
+                   "before_timing": f"{n_fills} reads of a {args.flush_mib} MiB scratch buffer "
+                                    f"over >= {args.warm_seconds} s (clocks up, the Infinity Cache "
+                                    f"left holding its clean lines), then the {args.warmup} warm-up "
+                                    f"steps; each timed step takes the ring touched longest ago",
                    "ring": split_desc},
         "roofline": roofline,
         "ring_attn": {"kernels": "k_ring_attn_fused + k_ring_merge" if fused else
