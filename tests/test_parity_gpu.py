@@ -125,6 +125,19 @@ def test_merge_in_launch(n_split, n_head, row_blocks):
     d.close()
 
 
+@pytest.mark.parametrize("n_split", [3, 5])
+def test_tile_walk_start_ragged_splits(n_split):
+    """Waves that stream several tiles start their split's walk at an
+    offset of their own (a multiple of 4 tiles per unit and split, wrapping
+    inside the split): splits of 43/42 or 26/24 tiles, so the offset wraps
+    at ragged ends, on a full layer and a sliding-window layer whose window
+    wraps the ring end (the split's tiles themselves circular)."""
+    w = small(cap=4096, n_layer=2, swa_window=1000, swa_layers=0b10, seed=140 + n_split)
+    d = Driver(w, n_split=n_split)
+    run_steps(d, [4000, 4001, 4096, 4100, 4567, 5003, 8190, 8193])
+    d.close()
+
+
 @pytest.mark.parametrize("row_blocks", [True, False], ids=["row_blocks", "one_workgroup"])
 def test_long_noise_block_two_query_blocks(row_blocks):
     """q_len 16 with GQA 4 (m = 64): several rope-table passes, noise rows
