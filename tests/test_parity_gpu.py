@@ -125,6 +125,37 @@ def test_merge_in_launch(n_split, n_head, row_blocks):
     d.close()
 
 
+def test_floor_kinds_leave_the_ring_as_it_was():
+    """Every ring_profile_floor kind (profiling only) on both layers between
+    steps: the floors write only the split partials, which every attention
+    launch rewrites, and a buffer of their own, so the following steps still
+    match the oracle.  Bounded barrier waits all end by their tickets; the
+    projection kind needs registered weights; unknown kinds are refused."""
+    import torch
+    from draft_model_kv_amd import ring as rk
+    s = torch.cuda.current_stream().cuda_stream
+    d = Driver(small(cap=1024, n_layer=2, seed=150), n_split=4)
+    run_steps(d, [900, 901, 909])
+    kinds = (rk.RING_FLOOR_EMPTY, rk.RING_FLOOR_READ, rk.RING_FLOOR_READ_LOCKSTEP,
+             rk.RING_FLOOR_PARTIALS, rk.RING_FLOOR_TWO_LAUNCH, rk.RING_FLOOR_LAST_ARRIVER,
+             rk.RING_FLOOR_BARRIER, rk.RING_FLOOR_MATRIX_MATH, rk.RING_FLOOR_VECTOR_MATH)
+    for k in kinds:
+        for layer in range(2):
+            rk.ring_profile_floor(d.ring.handle, layer, k, s)
+    torch.cuda.synchronize()
+    assert rk.ring_profile_floor_timeouts(d.ring.handle) == 0
+    for kind, code in ((rk.RING_FLOOR_PROJ_READ, rk.RING_ESTATE), (11, rk.RING_EINVAL),
+                       (-1, rk.RING_EINVAL)):
+        with pytest.raises(rk.RingError) as e:
+            rk.ring_profile_floor(d.ring.handle, 0, kind, s)
+        assert e.value.code == code, kind
+    with pytest.raises(rk.RingError) as e:
+        rk.ring_profile_floor(d.ring.handle, 2, rk.RING_FLOOR_READ, s)
+    assert e.value.code == rk.RING_ERANGE
+    run_steps(d, [910, 925, 1030, 1031])
+    d.close()
+
+
 @pytest.mark.parametrize("n_split", [3, 5])
 def test_tile_walk_start_ragged_splits(n_split):
     """Waves that stream several tiles start their split's walk at an
