@@ -302,6 +302,24 @@ for _wl in WIDE_WORKLOADS:
                                            f"-d OUT/pmc_{_c}_{_wl} -o run -- python REPO/bench.py "
                                            f"--workload {_wl} --steps 16 --warmup 4 --no-cpu-baseline "
                                            "--floor-launches 0")
+# hardware counters of the decode stream's kernels and of the read floor
+# on the same grid, one pass per group (at most 8 SQ, 4 TCP, 4 TCC and 2 TA
+# counters per pass)
+COUNTER_PASSES = {
+    "pmc_sq_a": ("SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAIT_ANY",
+                 "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_VMEM", "SQ_ACTIVE_INST_VALU",
+                 "SQ_ACTIVE_INST_LDS"),
+    "pmc_sq_b": ("SQ_INSTS_VMEM_RD", "SQ_INSTS_SALU", "SQ_INSTS_VALU", "SQ_INSTS_LDS",
+                 "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_IFETCH", "SQ_ACTIVE_INST_SCA",
+                 "SQ_WAIT_INST_LDS"),
+    "pmc_tc_a": ("TCP_TCC_READ_REQ", "TCP_TCC_READ_REQ_LATENCY", "TCC_HIT", "TCC_MISS"),
+    "pmc_tc_b": ("TCP_PENDING_STALL_CYCLES", "TA_ADDR_STALLED_BY_TC_CYCLES",
+                 "TA_DATA_STALLED_BY_TC_CYCLES"),
+}
+for _run, _ctrs in COUNTER_PASSES.items():
+    PROFILE_RUNS[_run] = (f"rocprofv3 --pmc {' '.join(_ctrs)} --output-format csv -d OUT/{_run} "
+                          "-o run -- python REPO/bench.py --steps 64 --warmup 16 --no-cpu-baseline "
+                          "--floor-launches 64")
 CALIBRATE_COPY_MIB = 1024
 KERNELS = ("k_ring_attn", "k_ring_step", "k_ring_merge")
 KERNELS_MIRROR = ("k_ring_project", "k_ring_step", "k_ring_attn", "k_ring_merge")
@@ -491,6 +509,8 @@ def summarize_profiles(out_dir: str) -> int:
         written.append(summarize_floor(out_dir, khash))
     if os.path.exists(os.path.join(out_dir, "bench_graph.log")):
         written.append(summarize_graph(out_dir, khash))
+    if all(os.path.isdir(os.path.join(out_dir, r)) for r in COUNTER_PASSES):
+        written.append(summarize_counters(out_dir, khash))
     print(json.dumps({"written": written, "kernel_source_hash": khash}))
     return 0
 
@@ -512,6 +532,84 @@ def floor_table(fl: dict) -> list:
             ev = f"{v['event_us']:.2f}" if v.get("event_us") else "-"
             lines.append(f"| {k} | {v['b2b_us']:.2f} | {ev} |")
     return lines
+
+
+def summarize_counters(out_dir: str, khash: str) -> str:
+    """Hardware counters per dispatch of the decode stream's attention and
+    merge launches and of the read floors on the attention's grid
+    (COUNTER_PASSES), with the ratios they give: where the waves' cycles go."""
+    groups = (("k_ring_attn_fused (decode attention)", lambda n: "k_ring_attn_fused" in n),
+              ("k_ring_merge<8> (cross-split merge)", lambda n: "k_ring_merge" in n),
+              ("k_ring_floor<1> (read floor)", lambda n: "k_ring_floor<1>" in n),
+              ("k_ring_floor<2> (read + partials floor)", lambda n: "k_ring_floor<2>" in n))
+    vals = {g: {} for g, _ in groups}
+    counts = {g: 0 for g, _ in groups}
+    for run, ctrs in COUNTER_PASSES.items():
+        rows = _csv_rows(out_dir, run, "counter_collection")
+        for g, pick in groups:
+            per = {}
+            for r in rows:
+                if pick(r["Kernel_Name"]) and r["Counter_Name"] in ctrs:
+                    per.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            for c, v in per.items():
+                vals[g][c] = sum(v) / len(v)
+                counts[g] = max(counts[g], len(v))
+    lines = ["# Hardware counters: decode_stream (cap 4096, q_len 8, GQA 32/8 x 128, F16, 1 layer, "
+             "32-ring pool)", "", f"Kernel source hash: `{khash}`", "",
+             "Commands (cd /tmp; TMPDIR=/tmp), one counter group per run:", ""]
+    lines += [f"    {PROFILE_RUNS[r]}" for r in COUNTER_PASSES]
+    lines += ["", "Average per dispatch (SQ counters summed over the shader engines; cycle "
+              "counts of SQ_WAVE_CYCLES, SQ_WAIT_* and SQ_ACTIVE_INST_* in quad-cycles, "
+              "summed over waves).", "",
+              "| counter | " + " | ".join(g for g, _ in groups) + " |",
+              "|---|" + "---:|" * len(groups)]
+    for ctrs in COUNTER_PASSES.values():
+        for c in ctrs:
+            lines.append(f"| {c} | " + " | ".join(
+                f"{vals[g][c]:.4g}" if c in vals[g] else "-" for g, _ in groups) + " |")
+    lines += ["", "| derived | " + " | ".join(g for g, _ in groups) + " |",
+              "|---|" + "---:|" * len(groups)]
+
+    def ratio(g, a, b, scale=1.0):
+        v = vals[g]
+        return v[a] / v[b] * scale if v.get(a) is not None and v.get(b) else None
+
+    derived = (
+        ("waves", lambda g: vals[g].get("SQ_WAVES")),
+        ("cycles per wave (SQ_WAVE_CYCLES x 4 / SQ_WAVES)",
+         lambda g: ratio(g, "SQ_WAVE_CYCLES", "SQ_WAVES", 4.0)),
+        ("share of wave cycles waiting (SQ_WAIT_ANY / SQ_WAVE_CYCLES)",
+         lambda g: ratio(g, "SQ_WAIT_ANY", "SQ_WAVE_CYCLES")),
+        ("share waiting to issue (SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES)",
+         lambda g: ratio(g, "SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES")),
+        ("share issuing vector memory (SQ_ACTIVE_INST_VMEM / SQ_WAVE_CYCLES)",
+         lambda g: ratio(g, "SQ_ACTIVE_INST_VMEM", "SQ_WAVE_CYCLES")),
+        ("share issuing VALU (SQ_ACTIVE_INST_VALU / SQ_WAVE_CYCLES)",
+         lambda g: ratio(g, "SQ_ACTIVE_INST_VALU", "SQ_WAVE_CYCLES")),
+        ("vector memory reads per wave", lambda g: ratio(g, "SQ_INSTS_VMEM_RD", "SQ_WAVES")),
+        ("scalar ALU instructions per wave", lambda g: ratio(g, "SQ_INSTS_SALU", "SQ_WAVES")),
+        ("VALU instructions per wave", lambda g: ratio(g, "SQ_INSTS_VALU", "SQ_WAVES")),
+        ("LDS instructions per wave", lambda g: ratio(g, "SQ_INSTS_LDS", "SQ_WAVES")),
+        ("instruction fetches per wave", lambda g: ratio(g, "SQ_IFETCH", "SQ_WAVES")),
+        ("average L1 -> L2 read latency, cycles (TCP_TCC_READ_REQ_LATENCY / TCP_TCC_READ_REQ)",
+         lambda g: ratio(g, "TCP_TCC_READ_REQ_LATENCY", "TCP_TCC_READ_REQ")),
+        ("L2 hit rate (TCC_HIT / (TCC_HIT + TCC_MISS))",
+         lambda g: (vals[g]["TCC_HIT"] / (vals[g]["TCC_HIT"] + vals[g]["TCC_MISS"])
+                    if vals[g].get("TCC_HIT") is not None and vals[g].get("TCC_MISS") is not None
+                    and vals[g]["TCC_HIT"] + vals[g]["TCC_MISS"] > 0 else None)),
+    )
+    for name, f in derived:
+        cells = []
+        for g, _ in groups:
+            v = f(g)
+            cells.append("-" if v is None else (f"{v:.3f}" if v < 10 else f"{v:.4g}"))
+        lines.append(f"| {name} | " + " | ".join(cells) + " |")
+    lines += ["", "Dispatches averaged per group: " +
+              ", ".join(f"{g.split(' ')[0]} {counts[g]}" for g, _ in groups) + "."]
+    path = "profiles/k_ring_attn_decode_stream_counters.md"
+    with open(os.path.join(ROOT, path), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    return path
 
 
 def summarize_graph(out_dir: str, khash: str) -> str:
