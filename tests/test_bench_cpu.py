@@ -101,3 +101,35 @@ def test_bench_line_reader(tmp_path):
         {"metric": "m", "value": 1.0}) + "\ntrailing\n")
     assert bench._bench_line(str(tmp_path), "run") == {"metric": "m", "value": 1.0}
     assert bench._bench_line(str(tmp_path), "missing") is None
+
+
+def test_hardware_counter_summary(tmp_path, monkeypatch):
+    """The counter summary averages each counter per dispatch of each kernel
+    group and derives its ratios from those averages (wait share, cycles per
+    wave, L2 hit rate); counters a pass did not collect show as '-'."""
+    out = tmp_path / "out"
+    for run, ctrs in bench.COUNTER_PASSES.items():
+        rows = []
+        for k, kname in enumerate(("ringkv::k_ring_attn_fused<1, 4, 1, true>",
+                                   "ringkv::k_ring_floor<1>")):
+            for disp in range(2):
+                for c in ctrs:
+                    value = {"SQ_WAVES": 1024.0, "SQ_WAVE_CYCLES": 4000.0 + 1000 * k,
+                             "SQ_WAIT_ANY": 2000.0 + 2000 * disp, "TCC_HIT": 30.0,
+                             "TCC_MISS": 70.0}.get(c, 1.0)
+                    rows.append({"Kernel_Name": kname, "Grid_Size": 65536,
+                                 "Counter_Name": c, "Counter_Value": value})
+        _write_counter_csv(str(out / run / "x" / "run_counter_collection.csv"), rows)
+    (tmp_path / "profiles").mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    path = bench.summarize_counters(str(out), "hash0")
+    text = (tmp_path / path).read_text()
+    assert "Kernel source hash: `hash0`" in text
+    lines = {ln.split(" | ")[0].lstrip("| "): ln for ln in text.splitlines() if ln.startswith("| ")}
+    # attention: SQ_WAIT_ANY averages (2000 + 4000) / 2 over 4000 wave cycles
+    wait = lines["share of wave cycles waiting (SQ_WAIT_ANY / SQ_WAVE_CYCLES)"].split(" | ")
+    assert wait[1] == "0.750" and wait[3] == "0.600" and wait[2] == "-"
+    cyc = lines["cycles per wave (SQ_WAVE_CYCLES x 4 / SQ_WAVES)"].split(" | ")
+    assert cyc[1] == "15.62"
+    hit = lines["L2 hit rate (TCC_HIT / (TCC_HIT + TCC_MISS))"].split(" | ")
+    assert hit[1] == "0.300"
