@@ -3,11 +3,14 @@
 //
 // Each one runs on the attention's own grid: one work-group of four waves per
 // (sequence, KV head, split, row block), the same XCD-pinned work-group order
-// and the same tiles per wave (tile t0 + wave, t0 + wave + 4, ...) of the
-// ring's visible window, but with a trivial consumer instead of the softmax:
+// and the same tiles per wave (tile t0 + wave, t0 + wave + 4, ... of the
+// ring's visible window, the walk started at the attention's offset per
+// unit and split), but with a trivial consumer instead of the softmax:
 //   kind 0  empty kernel (launch and drain only)
 //   kind 1  every visible K and V tile loaded once (16-byte loads per lane,
-//           the attention's fragment order and tile walk) and folded by xor
+//           the attention's fragment order and tile walk) and folded by xor;
+//           with FloorArgs.rotate = 0 (the host's lockstep kind) every
+//           work-group walks its split's tiles from the first one
 //   kind 2  kind 1, then the work-group's 8 KiB F16 split partial and its
 //           fp32 (max, sum) pairs stored where the attention stores them
 //   kind 3  kind 2 with an in-kernel cross-split merge by the last arriver:
