@@ -869,6 +869,123 @@ def clock_warmup(dev, seconds: float, flush_mib: int) -> int:
     return n
 
 
+# Points of a wave's work at which the profiling build reads the clock
+# (ring_profile_stamps in include/ring_kv.h), per stamp region.
+STAMP_POINTS = {
+    "attn": ("entry", "work-group mapped", "first tile's loads issued",
+             "queries built, first extra rows staged (past the barrier)",
+             "extra key rows attended", "ring tiles attended",
+             "waves' blocks exchanged through LDS", "output or partial stored (issued)"),
+    "merge": ("entry", "work-group mapped", "partial loads issued", "partials in",
+              "past the LDS exchange", None, None, "output stored (issued)"),
+    "proj": ("entry", "work-group mapped", "feature and weight loads issued",
+             "features staged in LDS", "matrix-core products issued", None, None,
+             "slice sums stored (issued)"),
+}
+
+
+def stamps_segment(rings, pool, calls, first, n_steps, run, dev, R) -> dict:
+    """Per-wave timestamps (profiling build) of n_steps single steps, each on
+    the ring touched longest ago and queued behind a RING_FLOOR_HOLD launch
+    (a wave that sleeps about 14 ms), so that its launches dispatch back to
+    back as the timed steps' do rather than onto an idle device.  For each
+    kernel, per point: the median over steps of the median and of the latest
+    wave's time after the launch's first wave started (the merge's times count
+    from the attention's first wave), in microseconds; and where the
+    attention's work-groups ran (XCD and compute unit from each wave's
+    hardware registers)."""
+    import numpy as np
+    import torch
+    regions = (("attn", R.RING_STAMPS_ATTN), ("merge", R.RING_STAMPS_MERGE),
+               ("proj", R.RING_STAMPS_PROJ))
+    nw = R.RING_STAMP_WAVES
+    h0 = rings[0].handle
+    for _, reg in regions:
+        R.ring_profile_stamps(h0, reg, 0, True)
+    per = {name: {"med": [], "max": []} for name, _ in regions}
+    placement = {"waves": [], "xcd_is_block_mod_8": [], "cus": [], "max_waves_per_cu": []}
+    khz = 0
+    s = torch.cuda.current_stream(dev).cuda_stream
+    for t in range(first, first + n_steps):
+        R.ring_profile_floor(h0, 0, R.RING_FLOOR_HOLD, s)
+        run(calls[t:t + 1])
+        torch.cuda.synchronize(dev)
+        recs = {}
+        for name, reg in regions:
+            st, khz = R.ring_profile_stamps(h0, reg, nw, True)
+            recs[name] = st
+        us = 1000.0 / khz                       # microseconds per clock tick
+        a = recs["attn"]
+        valid_a = a[:, 0] != 0
+        t_first = int(a[valid_a, 0].min()) if valid_a.any() else 0
+        for name, st in recs.items():
+            valid = st[:, 0] != 0
+            if not valid.any():
+                continue
+            base = t_first if name == "merge" and t_first else int(st[valid, 0].min())
+            rel = (st[valid, :8].astype(np.int64) - base) * us
+            used = [p for p in range(8) if STAMP_POINTS[name][p]]
+            per[name]["med"].append([float(np.median(rel[:, p])) for p in used])
+            per[name]["max"].append([float(np.max(rel[:, p])) for p in used])
+        if valid_a.any():
+            idx = np.nonzero(valid_a)[0]
+            hw, xcc = a[idx, 8].astype(np.int64), a[idx, 9].astype(np.int64)
+            block = idx // 4
+            # HW_ID: cu_id bits 11:8, sh_id bit 12, se_id bits 15:13
+            cu = (xcc << 16) | (hw & 0xFF00)
+            u, cnt = np.unique(cu, return_counts=True)
+            placement["waves"].append(len(idx))
+            placement["xcd_is_block_mod_8"].append(float(np.mean(xcc == block % 8)))
+            placement["cus"].append(len(u))
+            placement["max_waves_per_cu"].append(int(cnt.max()))
+    out = {"steps": n_steps, "clock_khz": khz,
+           "what": "single steps, each queued behind a 14 ms hold launch"}
+    for name, _ in regions:
+        if not per[name]["med"]:
+            continue
+        pts = [p for p in STAMP_POINTS[name] if p]
+        med = np.median(np.array(per[name]["med"]), axis=0)
+        mx = np.median(np.array(per[name]["max"]), axis=0)
+        out[name] = {"points": pts, "median_wave_us": [round(float(x), 3) for x in med],
+                     "latest_wave_us": [round(float(x), 3) for x in mx]}
+    if placement["waves"]:
+        out["attn_placement"] = {
+            "waves": int(np.median(placement["waves"])),
+            "xcd_is_block_mod_8": float(np.min(placement["xcd_is_block_mod_8"])),
+            "compute_units": int(np.median(placement["cus"])),
+            "max_waves_per_cu": int(np.max(placement["max_waves_per_cu"]))}
+    return out
+
+
+def stamps_markdown(res: dict, cmd: str) -> str:
+    """The stamps mode's JSON as a short markdown summary."""
+    lines = [f"# Per-wave timestamps: {res['workload']} ({res['step']} step)", "",
+             f"Command: `{cmd}`", "",
+             f"Profiling build `libringkv_stamps.so` (`RINGKV_LIB=stamps`): {res['stamps']['steps']} "
+             f"single steps, each on the pool ring touched longest ago and queued behind a 14 ms "
+             f"hold launch (its launches dispatch back to back, as in the timed steps); clock "
+             f"{res['stamps']['clock_khz']} kHz.  Microseconds after the launch's "
+             f"first wave started (merge: after the attention's first wave); median over steps "
+             f"of the median wave and of the latest wave.  Kernel source hash: "
+             f"`{res['kernel_source_hash']}`.", ""]
+    for name in ("attn", "merge", "proj"):
+        r = res["stamps"].get(name)
+        if not r:
+            continue
+        lines += [f"## {name}", "", "| point | median wave | latest wave |", "|---|---:|---:|"]
+        lines += [f"| {p} | {a:.2f} | {b:.2f} |"
+                  for p, a, b in zip(r["points"], r["median_wave_us"], r["latest_wave_us"])]
+        lines.append("")
+    pl = res["stamps"].get("attn_placement")
+    if pl:
+        lines += ["## attention placement", "",
+                  f"{pl['waves']} waves on {pl['compute_units']} compute units (at most "
+                  f"{pl['max_waves_per_cu']} waves on one); fraction of waves whose XCC_ID equals "
+                  f"their work-group index mod 8: {pl['xcd_is_block_mod_8']:.3f} (lowest over the "
+                  f"steps).", ""]
+    return "\n".join(lines)
+
+
 def floor_segment(rings, pool, launches, dev, R, attn_us, step_us, bytes_read, n_layer=1,
                   kinds=FLOOR_KINDS):
     """The ring_profile_floor kinds on layer 0, cycled over the pool (cold).
@@ -1038,6 +1155,11 @@ def main() -> int:
                     help="launches per ring_profile_floor kind (0: no floor segment)")
     ap.add_argument("--floor", action="store_true",
                     help="only the floor segment (after the same warm-up), one JSON line")
+    ap.add_argument("--stamps", type=int, default=0, metavar="STEPS",
+                    help="profiling build (libringkv_stamps.so): per-wave timestamps of STEPS "
+                         "single steps after the warm-up, printed as JSON")
+    ap.add_argument("--stamps-md", default="", metavar="PATH",
+                    help="with --stamps: also write the markdown summary to PATH")
     ap.add_argument("--graph", action="store_true",
                     help="only the graph-replay comparison (after the same warm-up), one JSON "
                          "line: the step captured in HIP graphs and replayed, against plain "
@@ -1070,6 +1192,8 @@ def main() -> int:
         print(json.dumps({"calibrate_copy_bytes": n, "launches": 10}), flush=True)
         return 0
 
+    if args.stamps:
+        os.environ["RINGKV_LIB"] = "stamps"   # before the package loads its library
     import workload as W
     import draft_model_kv_amd as R
 
@@ -1089,10 +1213,12 @@ def main() -> int:
     # timed region); ring 0 alone then takes up to min(steps, 1000) more
     # steps for the cache-warm figure
     total = args.warmup + (0 if args.floor else 2 * args.steps)
+    if args.stamps:
+        total = args.warmup + args.stamps
     if args.graph:
         # plain steps, then one step per pool ring for the captured graphs
         total = args.warmup + GRAPH_PLAIN_STEPS + 8 * pool
-    warm_steps = min(args.steps, 1000) if pool > 1 and not args.floor else 0
+    warm_steps = min(args.steps, 1000) if pool > 1 and not (args.floor or args.stamps) else 0
     rings, calls, steps_in, committed, calls0 = prepare(w, pool, total, dev, warm_steps, args.proj,
                                                         args.workspace)
     s = torch.cuda.current_stream(dev).cuda_stream
@@ -1143,6 +1269,18 @@ def main() -> int:
         print(json.dumps({"workload": args.workload, "step": step_mode, "ring_pool": pool,
                           "graph": graph_segment(rings, pool, calls, args.warmup, run, dev, R)}),
               flush=True)
+        for r in rings:
+            r.close()
+        return 0
+
+    if args.stamps:
+        res = {"workload": args.workload, "step": step_mode, "ring_pool": pool,
+               "ring": rings[0].describe(), "kernel_source_hash": kernel_source_hash(),
+               "stamps": stamps_segment(rings, pool, calls, args.warmup, args.stamps, run, dev, R)}
+        print(json.dumps(res), flush=True)
+        if args.stamps_md:
+            with open(args.stamps_md, "w") as f:
+                f.write(stamps_markdown(res, "python bench.py " + " ".join(sys.argv[1:])))
         for r in rings:
             r.close()
         return 0

@@ -258,6 +258,20 @@ constexpr size_t kStaticScratchBytes = size_t(16) << 20;
 hipError_t resolve_static_scratch(int device);
 void* static_scratch(int device);
 hipError_t launch_floor(const FloorArgs& a, int kind, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
+
+// Per-wave timestamps (profiling build only: the library compiled with
+// RING_WAVE_STAMPS, libringkv_stamps.so).  Each wave of the attention, merge
+// and projection kernels records the device's constant-rate clock
+// (s_memrealtime) at fixed points of its work, and its hardware placement,
+// in region `kernel` of a static device array: kStampWords 64-bit words per
+// wave (kStampPhases stamps, HW_ID, XCC_ID), wave index = work-group index x
+// waves per work-group + wave.  In the product build the kernels record
+// nothing and stamps_address returns hipErrorNotSupported.
+constexpr int kStampRegions = 3;   // attention (plain and fused), merge, projection
+constexpr int kStampWaves = 8192;
+constexpr int kStampPhases = 8;
+constexpr int kStampWords = kStampPhases + 2;
+hipError_t stamps_address(void** ptr);
 // Work-groups of the floor kernel that fit the device at once (0 on error).
 int floor_resident_blocks();
 

@@ -33,6 +33,51 @@ typedef const __attribute__((address_space(1))) uint16_t gcu16;
 typedef __attribute__((address_space(1))) uint16_t gu16;
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 
+// Per-wave timestamps of the profiling build (RING_WAVE_STAMPS): stamp p is
+// the device clock when the wave passes point p of its work (the scheduler
+// keeps every instruction on its side of the point); flush stores the
+// stamps, HW_ID and XCC_ID of the wave with lane 0's vector stores.  In the
+// product build both are empty.
+#ifdef RING_WAVE_STAMPS
+__device__ uint64_t g_wave_stamps[kStampRegions * kStampWaves * kStampWords];
+struct WaveStamps {
+  uint64_t t[kStampPhases];
+  __device__ WaveStamps() {
+#pragma unroll
+    for (int p = 0; p < kStampPhases; ++p) t[p] = 0;
+    t[0] = __builtin_amdgcn_s_memrealtime();
+  }
+  __device__ inline void at(int p) {
+    __builtin_amdgcn_sched_barrier(0);
+    t[p] = __builtin_amdgcn_s_memrealtime();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __device__ inline void flush(int region, uint32_t wave_gid) {
+    at(kStampPhases - 1);
+    if (wave_gid >= (uint32_t)kStampWaves || (threadIdx.x & 63) != 0) return;
+    uint64_t* d = g_wave_stamps + ((size_t)region * kStampWaves + wave_gid) * kStampWords;
+#pragma unroll
+    for (int p = 0; p < kStampPhases; ++p) d[p] = t[p];
+    d[kStampPhases] = __builtin_amdgcn_s_getreg(4 | (31 << 11));       // HW_ID
+    d[kStampPhases + 1] = __builtin_amdgcn_s_getreg(20 | (3 << 11));   // XCC_ID, bits 3:0
+  }
+};
+#else
+struct WaveStamps {
+  __device__ inline void at(int) {}
+  __device__ inline void flush(int, uint32_t) {}
+};
+#endif
+
+hipError_t stamps_address(void** ptr) {
+#ifdef RING_WAVE_STAMPS
+  return hipGetSymbolAddress(ptr, HIP_SYMBOL(g_wave_stamps));
+#else
+  *ptr = nullptr;
+  return hipErrorNotSupported;
+#endif
+}
+
 // 2^x with the hardware instruction: about 1 ulp for normal results; results
 // below 2^-126 flush to zero and 2^-inf = 0.  Softmax weights that small
 // change no output at the precision that is kept.
@@ -378,6 +423,12 @@ __device__ inline void attend_tile(const half8 (&kc)[8], const half8 (&vc)[8],
                                    const QFrag<MB, QL>& q, const half8* q_lds, int lane,
                                    float (&m_run)[MB], float (&l_run)[MB],
                                    f32x16 (&o)[MB][4]) {
+  // Query fragments from LDS: the lane index passes through an empty asm
+  // statement at every tile, so the compiler cannot hoist the LDS reads out
+  // of the tile loop (held in registers, two query blocks' fragments take
+  // 128 VGPRs and push the accumulators to scratch).
+  int qln = lane;
+  if constexpr (QL) asm volatile("" : "+v"(qln));
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     f32x16 s = {};
@@ -385,8 +436,8 @@ __device__ inline void attend_tile(const half8 (&kc)[8], const half8 (&vc)[8],
     for (int c = 0; c < 8; ++c) {
       half8 qh, ql;
       if constexpr (QL) {
-        qh = q_lds[((mb * 2 + 0) * 8 + c) * 64 + lane];
-        ql = q_lds[((mb * 2 + 1) * 8 + c) * 64 + lane];
+        qh = q_lds[((mb * 2 + 0) * 8 + c) * 64 + qln];
+        ql = q_lds[((mb * 2 + 1) * 8 + c) * 64 + qln];
       } else {
         qh = q.hi[mb][c];
         ql = q.lo[mb][c];
@@ -777,7 +828,7 @@ template <int MB, int NW, int W, bool SHARE>
 __device__ __forceinline__ void merge_store(const EpilogueArgs& a, unsigned char* lds,
                                             float (*sm_m)[MB * 32], float (*sm_l)[MB * 32],
                                             const float (&m_run)[MB], const float (&l_run)[MB],
-                                            const f32x16 (&o)[MB][4], int lane) {
+                                            const f32x16 (&o)[MB][4], int lane, WaveStamps& st) {
   using S = AttnShape<MB, NW, false, SHARE>;
   const int hl = lane >> 5, col = lane & 31;
   // [mb][block][writer][jj][lane]
@@ -800,6 +851,7 @@ __device__ __forceinline__ void merge_store(const EpilogueArgs& a, unsigned char
     }
   }
   lds_barrier();
+  st.at(6);  // the waves' blocks exchanged through LDS
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     const int nl = mb * 32 + col;   // row within the work-group's block(s)
@@ -990,7 +1042,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
                                           const FusedLane& fl, double theta_lane, int unit,
                                           int split, int row0, int vis_first, int vis_count,
                                           unsigned char* lds, float (*sm_m)[MB * 32],
-                                          float (*sm_l)[MB * 32]) {
+                                          float (*sm_l)[MB * 32], WaveStamps& st) {
   constexpr bool QL = MB > 1 || SHORT;
   constexpr bool SHARE = SHORT;
   using S = AttnShape<MB, NW, FUSED, SHARE>;
@@ -1158,6 +1210,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
   uint32_t mw[MB][8];
   int4 spv[4];
   load_tile(ring_tile(min(tile, tile_last)), kc, vc, mw, spv);
+  st.at(2);  // the first tile's loads issued
   // ---- 2. queries: rotate at committed + i, scale by log2(e)/sqrt(d),
   //      split into hi + lo F16 (fragment order [mb][hi/lo][chunk][lane]);
   //      queries past q_len * group are zero.
@@ -1233,6 +1286,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
   if (rank < n_extra)
     stage_extra_row<MB, FUSED>(a, fx, nr, rank, kh, vh, rowk, rowv, lane, store_rows, store_sp);
   lds_barrier();
+  st.at(3);  // queries built, the first extra rows staged
 
   QFrag<MB, QL> qf;
   if constexpr (!QL) {
@@ -1264,6 +1318,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
       attend_extra_row<MB, QL>(nr, rowk, rowv, lane, hl, col, qf, q_lds, m_run, l_run, o);
     }
   }
+  st.at(4);  // extra key rows attended
 
   // Attend ring tile rt with its mask words (plain launch) or with the
   // visibility of its slots from their slot_pos (fused launch).
@@ -1283,7 +1338,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
   //      before the current tile is processed (two tiles in registers); two
   //      query blocks have no room for that.  (Two tiles ahead, through three
   //      rotating register buffers, measured slower on long waves.)
-  constexpr bool kPrefetch = MB == 1 && !SHORT;
+  constexpr bool kPrefetch = !SHORT;
   if constexpr (kPrefetch) {
     // every tile but the wave's last one: its successor is fetched first
     while (tile + NW < t1) {
@@ -1316,18 +1371,19 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedAttnArgs
       tile = next;
     }
   }
+  st.at(5);  // ring tiles attended
 
   // ---- 5./6. merge the waves and store: a copy of the code per wave, so
   //      that the wave's own accumulator block is picked at compile time.
   static_assert(NW == 4, "one 32-dim output block per wave");
   if (wave == 0)
-    merge_store<MB, NW, 0, SHARE>(ep, lds, sm_m, sm_l, m_run, l_run, o, lane);
+    merge_store<MB, NW, 0, SHARE>(ep, lds, sm_m, sm_l, m_run, l_run, o, lane, st);
   else if (wave == 1)
-    merge_store<MB, NW, 1, SHARE>(ep, lds, sm_m, sm_l, m_run, l_run, o, lane);
+    merge_store<MB, NW, 1, SHARE>(ep, lds, sm_m, sm_l, m_run, l_run, o, lane, st);
   else if (wave == 2)
-    merge_store<MB, NW, 2, SHARE>(ep, lds, sm_m, sm_l, m_run, l_run, o, lane);
+    merge_store<MB, NW, 2, SHARE>(ep, lds, sm_m, sm_l, m_run, l_run, o, lane, st);
   else
-    merge_store<MB, NW, 3, SHARE>(ep, lds, sm_m, sm_l, m_run, l_run, o, lane);
+    merge_store<MB, NW, 3, SHARE>(ep, lds, sm_m, sm_l, m_run, l_run, o, lane, st);
   if constexpr (!SHORT) {
     if (ep.coherent) last_arriver_merge<MB>(a, ep, unit, row0 / MP);
   }
@@ -1339,6 +1395,7 @@ __device__ __forceinline__ void attn_entry(const AttnArgs& a, const FusedAttnArg
   __shared__ __attribute__((aligned(16))) unsigned char lds[S::kTotalLds];
   __shared__ float sm_m[NW][S::MP];
   __shared__ float sm_l[NW][S::MP];
+  WaveStamps st;
   // Work-group -> (sequence, KV head, split).  Work-groups are handed to the
   // eight XCDs round-robin; keep every split of one (sequence, head) on one XCD.
   // Every argument the body reads is fetched here in one batch: left to
@@ -1382,9 +1439,11 @@ __device__ __forceinline__ void attn_entry(const AttnArgs& a, const FusedAttnArg
   const int seq = quot32(unit, a.rcp_n_head_kv);
   FusedLane fl{};
   if constexpr (FUSED) fl = fused_pick(fv, seq);
+  st.at(1);  // work-group mapped (kernel arguments in registers)
   attn_body<MB, NW, RP, FUSED, SHORT>(a, fa, fl, fv.theta, unit, split, rb * S::MP,
                                __builtin_amdgcn_readlane(firstv, seq),
-                               __builtin_amdgcn_readlane(countv, seq), lds, sm_m, sm_l);
+                               __builtin_amdgcn_readlane(countv, seq), lds, sm_m, sm_l, st);
+  st.flush(0, blockIdx.x * NW + (threadIdx.x >> 6));
 }
 
 template <int MB, int NW, int RP, bool SHORT>
@@ -1415,6 +1474,7 @@ template <int KMAX>
 __global__ __launch_bounds__(256) void k_ring_merge(MergeArgs a) {
   __shared__ float sM[4][64], sL[4][64];
   __shared__ float4 sO[4][64];
+  WaveStamps st;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // (unit, item) of this work-group; the items of a unit run on the XCD
@@ -1440,12 +1500,14 @@ __global__ __launch_bounds__(256) void k_ring_merge(MergeArgs a) {
 
   float2 mlv[KMAX];
   half4 u[KMAX];
+  st.at(1);  // work-group mapped
 #pragma unroll
   for (int k = 0; k < KMAX; ++k) {
     const int t = min(wave + 4 * k, a.n_split - 1);
     mlv[k] = *(const float2*)(ml + t * ml_step);
     u[k] = *(const half4*)(acc + t * acc_step);
   }
+  st.at(2);  // partial loads issued
   // Take every load as one batch: the reductions below start from a value
   // that the empty asm statements make depend on every loaded register, so
   // the scheduler cannot interleave them with the loads.
@@ -1453,6 +1515,7 @@ __global__ __launch_bounds__(256) void k_ring_merge(MergeArgs a) {
 #pragma unroll
   for (int k = 0; k < KMAX; ++k)
     asm volatile("" : "+v"(mx) : "v"(mlv[k].x), "v"(mlv[k].y), "v"(__builtin_bit_cast(u32x2, u[k])));
+  st.at(3);  // partials in
 #pragma unroll
   for (int k = 0; k < KMAX; ++k)
     if (wave + 4 * k < a.n_split) mx = fmaxf(mx, mlv[k].x);
@@ -1472,7 +1535,11 @@ __global__ __launch_bounds__(256) void k_ring_merge(MergeArgs a) {
   sL[wave][lane] = L;
   sO[wave][lane] = O;
   lds_barrier();
-  if (wave != 0) return;
+  st.at(4);  // the waves' sums exchanged through LDS
+  if (wave != 0) {
+    st.flush(1, blockIdx.x * 4 + wave);
+    return;
+  }
   float M = kNegInf;
 #pragma unroll
   for (int w = 0; w < 4; ++w) M = fmaxf(M, sM[w][lane]);
@@ -1496,6 +1563,7 @@ __global__ __launch_bounds__(256) void k_ring_merge(MergeArgs a) {
     float* dst = a.out + (((int64_t)seq * a.q_len + i) * a.n_head + g * a.group + hh) * kHeadDim;
     *(float4*)(dst + 32 * b + 8 * jj + 4 * hl) = Ot;
   }
+  st.flush(1, blockIdx.x * 4 + wave);
 }
 
 // ---------------------------------------------------------------------------
@@ -1519,6 +1587,7 @@ template <bool PACKED>
 __global__ __launch_bounds__(128) void k_ring_project(ProjArgs a) {
   constexpr int kRowStride = kProjSlice / 8 + 1;  // half8 per staged row (+1: no bank conflicts)
   __shared__ half8 f_lds[32 * kRowStride];
+  WaveStamps st;
   // every argument fetched in one batch at entry (see attn_entry)
   asm volatile("" ::"s"(a.mirror), "s"(a.feat), "s"(a.wk), "s"(a.wv), "s"(a.scratch), "s"(a.slot0),
                "s"(a.n_rows), "s"(a.cap), "s"(a.d_model), "s"(a.kv_row), "s"(a.n_head_kv),
@@ -1542,6 +1611,7 @@ __global__ __launch_bounds__(128) void k_ring_project(ProjArgs a) {
   const int pw = 2 * (hh & 1) + wave;  // the wave's 32 output dims of the head part
   const int r0 = rt * 32;
   const int d0 = ds * kProjSlice;
+  st.at(1);  // work-group mapped
 
   // features of the tile's rows, first (loads return in issue order, and
   // the LDS staging needs them): 32 rows x 32 chunks of 16 B, 8 per thread;
@@ -1588,6 +1658,7 @@ __global__ __launch_bounds__(128) void k_ring_project(ProjArgs a) {
   }
   // every weight load is issued before the wait for the features
   __builtin_amdgcn_sched_barrier(0);
+  st.at(2);  // feature and weight loads issued
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const int c = threadIdx.x + 128 * k;
@@ -1604,6 +1675,7 @@ __global__ __launch_bounds__(128) void k_ring_project(ProjArgs a) {
     }
   }
   lds_barrier();
+  st.at(3);  // features staged in LDS
 
   f32x16 acc = {};
   const half8* frow = f_lds + (lane & 31) * kRowStride + 4 * (lane >> 5);
@@ -1611,6 +1683,7 @@ __global__ __launch_bounds__(128) void k_ring_project(ProjArgs a) {
   for (int blk = 0; blk < 4; ++blk)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc = mfma32(wa[blk][j], frow[blk * 8 + j], acc);
+  st.at(4);  // matrix-core products issued
 
   // acc[r] = raw[out dim 8 (r / 4) + 4 (lane / 32) + r % 4][row lane % 32]
   const int n = r0 + (lane & 31);
@@ -1623,6 +1696,7 @@ __global__ __launch_bounds__(128) void k_ring_project(ProjArgs a) {
       *(float4*)(dst + 8 * q) = make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2],
                                             acc[4 * q + 3]);
   }
+  st.flush(2, blockIdx.x * 2 + wave);
 }
 
 // Weights into the projection's load order (PackArgs): one 16-byte chunk

@@ -1457,4 +1457,35 @@ int ring_profile_read(ring_t* r, int32_t kernel, int32_t* n_launches, double* to
   return ok();
 }
 
+static_assert(RING_STAMP_WAVES == kStampWaves && RING_STAMP_WORDS == kStampWords &&
+                  RING_STAMPS_PROJ + 1 == kStampRegions,
+              "stamp layout of the header and the kernels");
+
+int ring_profile_stamps(ring_t* r, int32_t region, uint64_t* host, int32_t max_waves,
+                        int32_t clear, int32_t* clock_khz) {
+  if (!r || region < 0 || region >= kStampRegions || max_waves < 0 ||
+      (max_waves > 0 && !host))
+    return fail(RING_EINVAL, "bad argument");
+  if (int e = use_device(r)) return e;
+  void* base = nullptr;
+  if (stamps_address(&base) != hipSuccess || !base)
+    return fail(RING_ESTATE, "library built without wave stamps (libringkv_stamps.so has them)");
+  if (hipDeviceSynchronize() != hipSuccess)
+    return fail(RING_EDEVICE, "device synchronisation failed");
+  const size_t words = (size_t)kStampWaves * kStampWords;
+  uint64_t* dev = reinterpret_cast<uint64_t*>(base) + (size_t)region * words;
+  const size_t n = (size_t)std::min(max_waves, kStampWaves) * kStampWords;
+  if (n && hipMemcpy(host, dev, n * 8, hipMemcpyDeviceToHost) != hipSuccess)
+    return fail(RING_EDEVICE, "stamp copy failed");
+  if (clear && (hipMemset(dev, 0, words * 8) != hipSuccess || hipDeviceSynchronize() != hipSuccess))
+    return fail(RING_EDEVICE, "stamp clear failed");
+  if (clock_khz) {
+    int khz = 0;
+    if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, r->device) != hipSuccess)
+      return fail(RING_EDEVICE, "clock rate query failed");
+    *clock_khz = khz;
+  }
+  return ok();
+}
+
 }  // extern "C"

@@ -17,7 +17,10 @@ from typing import Optional, Tuple
 
 import numpy as np
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libringkv.so")
+# RINGKV_LIB=stamps loads the profiling build with per-wave timestamps
+# (ring_profile_stamps) instead of the product library.
+LIB_NAME = "libringkv_stamps.so" if os.environ.get("RINGKV_LIB") == "stamps" else "libringkv.so"
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), LIB_NAME)
 
 RING_OK = 0
 RING_EINVAL = -1
@@ -36,7 +39,7 @@ EXPORTS = (
     "ring_read_slot_pos", "ring_read_mask", "ring_read_mask_swa", "ring_read_rows",
     "ring_read_state",
     "ring_profile_enable", "ring_profile_read", "ring_profile_floor",
-    "ring_profile_floor_timeouts",
+    "ring_profile_floor_timeouts", "ring_profile_stamps",
 )
 RING_KERNEL_STEP, RING_KERNEL_ATTN, RING_KERNEL_MERGE, RING_KERNEL_PROJ = 0, 1, 2, 3
 RING_KERNEL_FLOOR = 4
@@ -45,6 +48,9 @@ RING_KERNEL_FLOOR = 4
  RING_FLOOR_BARRIER, RING_FLOOR_TWO_LAUNCH, RING_FLOOR_HOLD, RING_FLOOR_MATRIX_MATH,
  RING_FLOOR_VECTOR_MATH, RING_FLOOR_PROJ_READ, RING_FLOOR_READ_LOCKSTEP) = (
     0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10)
+# regions of ring_profile_stamps and the layout of a wave's record
+RING_STAMPS_ATTN, RING_STAMPS_MERGE, RING_STAMPS_PROJ = 0, 1, 2
+RING_STAMP_WAVES, RING_STAMP_WORDS = 8192, 10
 
 
 class RingConfig(ctypes.Structure):
@@ -123,6 +129,7 @@ def _load() -> ctypes.CDLL:
         "ring_profile_read": [P, I32, ctypes.POINTER(I32), ctypes.POINTER(ctypes.c_double)],
         "ring_profile_floor": [P, I32, I32, P],
         "ring_profile_floor_timeouts": [P, ctypes.POINTER(ctypes.c_uint32)],
+        "ring_profile_stamps": [P, I32, P, I32, I32, ctypes.POINTER(I32)],
     }
     for name in EXPORTS:
         fn = getattr(lib, name)
@@ -319,6 +326,18 @@ def ring_profile_floor_timeouts(handle: int) -> int:
     n = ctypes.c_uint32()
     _check(_lib.ring_profile_floor_timeouts(handle, ctypes.byref(n)), "ring_profile_floor_timeouts")
     return n.value
+
+
+def ring_profile_stamps(handle: int, region: int, max_waves: int, clear: bool = True
+                        ) -> Tuple[np.ndarray, int]:
+    """Per-wave stamps of `region` (profiling build only): a uint64 array
+    [max_waves][RING_STAMP_WORDS] and the clock's rate in kHz."""
+    out = np.zeros((max_waves, RING_STAMP_WORDS), dtype=np.uint64)
+    khz = ctypes.c_int32()
+    _check(_lib.ring_profile_stamps(handle, region, out.ctypes.data if max_waves else None,
+                                    max_waves, int(clear), ctypes.byref(khz)),
+           "ring_profile_stamps")
+    return out, khz.value
 
 
 class Ring:

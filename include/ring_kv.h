@@ -465,6 +465,42 @@ int ring_profile_floor(ring_t* r, int32_t layer, int32_t kind, void* stream);
  * than by the last ticket (synchronous; 0 when no floor launch ran).        */
 int ring_profile_floor_timeouts(ring_t* r, uint32_t* timeouts);
 
+/* ---- Per-wave timestamps (profiling build only) ----
+ * The library built with RING_WAVE_STAMPS (libringkv_stamps.so, same sources)
+ * has every wave of the attention, merge and projection kernels read the
+ * device's constant-rate clock (s_memrealtime) at fixed points of its work
+ * and store the readings, with its hardware placement, in a static device
+ * array: per region, RING_STAMP_WAVES waves of RING_STAMP_WORDS uint64
+ * words, wave index = work-group index x waves per work-group + wave:
+ *   words 0..7  the clock at the wave's points (below), 8 HW_ID, 9 XCC_ID
+ *   RING_STAMPS_ATTN   (ring_attn's attention launch, plain or fused):
+ *                      0 entry, 1 work-group mapped, 2 first tile's loads
+ *                      issued, 3 queries built and first extra rows staged
+ *                      (past the barrier), 4 extra key rows attended, 5 ring
+ *                      tiles attended, 6 the waves' blocks exchanged through
+ *                      LDS, 7 output or partial stored (issued)
+ *   RING_STAMPS_MERGE  (its merge launch): 0 entry, 1 mapped, 2 loads
+ *                      issued, 3 partials in, 4 past the LDS exchange,
+ *                      5 and 6 unused (zero), 7 end
+ *   RING_STAMPS_PROJ   (ring_begin_step_mirror's projection): 0 entry,
+ *                      1 mapped, 2 feature and weight loads issued,
+ *                      3 features staged, 4 matrix-core products issued,
+ *                      5 and 6 unused, 7 slice sums stored (issued)
+ * Each launch overwrites the entries of its waves; words of waves that did
+ * not run keep what was there (zero after a clear).  This call waits for the
+ * device, copies the first min(max_waves, RING_STAMP_WAVES) waves of
+ * `region` to `host` (max_waves x RING_STAMP_WORDS uint64), then zeroes the
+ * region if `clear`; *clock_khz (if not NULL) gets the clock's rate.
+ * Errors: RING_EINVAL (region, max_waves, host NULL with max_waves > 0),
+ * RING_ESTATE (the product library, built without stamps), RING_EDEVICE. */
+#define RING_STAMPS_ATTN  0
+#define RING_STAMPS_MERGE 1
+#define RING_STAMPS_PROJ  2
+#define RING_STAMP_WAVES  8192
+#define RING_STAMP_WORDS  10
+int ring_profile_stamps(ring_t* r, int32_t region, uint64_t* host, int32_t max_waves,
+                        int32_t clear, int32_t* clock_khz);
+
 #ifdef __cplusplus
 }
 #endif

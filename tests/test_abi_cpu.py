@@ -48,6 +48,17 @@ def test_library_exports_every_header_function():
         assert hasattr(lib, name), name
 
 
+def test_stamps_build_exports_every_header_function():
+    """The profiling build (per-wave timestamps) is the same ABI."""
+    import ctypes
+    path = os.path.join(os.path.dirname(rk.LIB_PATH), "libringkv_stamps.so")
+    if not os.path.exists(path):
+        pytest.skip("libringkv_stamps.so not built")
+    lib = ctypes.CDLL(path)
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
 @pytest.mark.parametrize("cap,q_len,n_head,n_head_kv,n_layer",
                          [(4096, 8, 32, 8, 5), (64, 8, 32, 8, 1), (32768, 8, 64, 8, 1),
                           (1, 1, 8, 8, 1), (100, 3, 16, 4, 2), (23, 8, 32, 8, 1)])
