@@ -259,8 +259,12 @@ def test_sliding_window_single_noise_row():
     d.close()
 
 
-@pytest.mark.parametrize("n_split", [1, 2, 3, 7])
+@pytest.mark.parametrize("n_split", [1, 2, 3, 7, 13, 45, 64])
 def test_split_counts_agree(n_split):
+    """The merge launch's shapes (1, 2, 4 and 16 splits per merge wave; the
+    decode workloads' 32 splits take 8); at 45 and 64 splits of a 16-tile
+    ring most splits see no ring tile, and some merge waves see only splits
+    without a visible key."""
     w = small(cap=512, seed=106)
     d = Driver(w, n_split=n_split)
     run_steps(d, [700, 703, 708], check_rows=False)
