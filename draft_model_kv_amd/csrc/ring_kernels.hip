@@ -1625,8 +1625,10 @@ __global__ __launch_bounds__(128) void k_ring_project(ProjArgs a) {
     const int c = threadIdx.x + 128 * k;
     const int row = c >> 5, dc = c & 31;
     const int i = min(r0 + row, a.n_rows - 1);
+    // slot0 < cap and i < 64: one subtraction unless cap < 64
     int slot = a.slot0 + i;
-    while (slot >= a.cap) slot -= a.cap;
+    if (slot >= a.cap) slot -= a.cap;
+    if (slot >= a.cap) slot %= a.cap;
     fslot[k] = slot;
     const uint16_t* src = a.feat ? a.feat + (int64_t)i * a.d_model + d0 + 8 * dc
                                  : a.mirror + (int64_t)slot * a.d_model + d0 + 8 * dc;
@@ -1635,7 +1637,11 @@ __global__ __launch_bounds__(128) void k_ring_project(ProjArgs a) {
 
   // weights: row 32 w + lane % 32 of the head part, 4 blocks x 64 B (dims
   // 64 blk + 32 (lane / 32) + 8 j + e of the slice); packed weights hold the
-  // wave's 16 KiB in exactly this load order
+  // wave's 16 KiB in exactly this load order.  The loads are issued in the
+  // order the matrix ops use them (a scheduling barrier after each): loads
+  // return in issue order, so each op waits only for its own weights and
+  // the chain runs while the later ones arrive (left to itself the compiler
+  // issued the first op's weights fifteenth, and the chain waited for all).
   half8 wa[4][4];
   if constexpr (PACKED) {
     const half8* wp = (const half8*)a.wk +
@@ -1643,7 +1649,10 @@ __global__ __launch_bounds__(128) void k_ring_project(ProjArgs a) {
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) wa[blk][j] = wp[(blk * 4 + j) * 64 + lane];
+      for (int j = 0; j < 4; ++j) {
+        wa[blk][j] = wp[(blk * 4 + j) * 64 + lane];
+        __builtin_amdgcn_sched_barrier(0);
+      }
   } else {
     const bool is_v = hp >= a.n_head_kv;
     const int head = is_v ? hp - a.n_head_kv : hp;
@@ -1654,7 +1663,10 @@ __global__ __launch_bounds__(128) void k_ring_project(ProjArgs a) {
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) wa[blk][j] = *(const half8*)(wrow + blk * 64 + 8 * j);
+      for (int j = 0; j < 4; ++j) {
+        wa[blk][j] = *(const half8*)(wrow + blk * 64 + 8 * j);
+        __builtin_amdgcn_sched_barrier(0);
+      }
   }
   // every weight load is issued before the wait for the features
   __builtin_amdgcn_sched_barrier(0);
