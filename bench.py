@@ -844,6 +844,9 @@ def summarize_wide(out_dir: str, wl_name: str, khash: str, fetch_scale: float,
 FLOOR_KINDS = (("empty", 0), ("read", 1), ("read_lockstep", 10), ("partials", 2),
                ("two_launch", 5), ("last_arriver", 3), ("barrier", 4), ("matrix_math", 7),
                ("vector_math", 8))
+# rings with 64 queries per KV head (two 32-query blocks): also one read of
+# every tile for both blocks, eight waves sharing each tile through LDS
+FLOOR_KINDS_TWO_BLOCKS = FLOOR_KINDS + (("shared_tiles", 11),)
 # the mirror step's projection launch: its grid with a trivial consumer of
 # the registered weights (every pool ring holds its own copy: cold)
 FLOOR_KINDS_MIRROR = (("empty", 0), ("proj_read", 9))
@@ -1415,10 +1418,12 @@ def main() -> int:
         if rd:
             ceiling = {"proj_kernel": rd / proj_us}
     if args.floor_launches and not mirror:
+        two_blocks = w.q_len * (w.n_head // w.n_head_kv) > 32
         floors, ceiling = floor_segment(
             rings, pool, args.floor_launches, dev, R, attn_us, ms_per_step * 1e3,
             np.mean([sum(algorithmic_bytes(w, layer_window(c, 0), geo.kv_total)["kv"] for c in cs)
-                     for cs in seg]), w.n_layer)
+                     for cs in seg]), w.n_layer,
+            kinds=FLOOR_KINDS_TWO_BLOCKS if two_blocks else FLOOR_KINDS)
     for r in rings:
         r.close()
     line = {

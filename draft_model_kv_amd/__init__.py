@@ -20,7 +20,8 @@ from .ring import (Ring, RingConfig, RingError, RingGeometry, RingKvWeights, Rin
                    RING_FLOOR_READ, RING_FLOOR_PARTIALS, RING_FLOOR_LAST_ARRIVER,
                    RING_FLOOR_BARRIER, RING_FLOOR_TWO_LAUNCH, RING_FLOOR_HOLD,
                    RING_FLOOR_MATRIX_MATH, RING_FLOOR_VECTOR_MATH, RING_FLOOR_PROJ_READ,
-                   RING_FLOOR_READ_LOCKSTEP, ring_profile_stamps, RING_STAMPS_ATTN,
+                   RING_FLOOR_READ_LOCKSTEP, RING_FLOOR_SHARED_TILES, ring_profile_stamps,
+                   RING_STAMPS_ATTN,
                    RING_STAMPS_MERGE, RING_STAMPS_PROJ, RING_STAMP_WAVES, RING_STAMP_WORDS)
 
 __all__ = ["Ring", "RingConfig", "RingError", "RingGeometry", "RingKvWeights", "RingPlan",
@@ -37,5 +38,6 @@ __all__ = ["Ring", "RingConfig", "RingError", "RingGeometry", "RingKvWeights", "
            "RING_FLOOR_READ", "RING_FLOOR_PARTIALS", "RING_FLOOR_LAST_ARRIVER",
            "RING_FLOOR_BARRIER", "RING_FLOOR_TWO_LAUNCH", "RING_FLOOR_HOLD",
            "RING_FLOOR_MATRIX_MATH", "RING_FLOOR_VECTOR_MATH", "RING_FLOOR_PROJ_READ",
-           "RING_FLOOR_READ_LOCKSTEP", "ring_profile_stamps", "RING_STAMPS_ATTN",
+           "RING_FLOOR_READ_LOCKSTEP", "RING_FLOOR_SHARED_TILES", "ring_profile_stamps",
+           "RING_STAMPS_ATTN",
            "RING_STAMPS_MERGE", "RING_STAMPS_PROJ", "RING_STAMP_WAVES", "RING_STAMP_WORDS"]

@@ -302,6 +302,109 @@ __global__ __launch_bounds__(256) void k_ring_floor(FloorArgs a) {
   }
 }
 
+// kind 11: one read of every visible tile for both 32-query blocks of a KV
+// head.  A work-group of eight waves per (unit, split): wave w = 4 qb + p;
+// pair p (waves p and 4 + p) takes the split's tiles t0 + p, t0 + p + 4, ...
+// Wave p copies the tile's K and wave 4 + p its V into LDS with direct
+// global-to-LDS loads (1 KiB per instruction), two stages; after one barrier
+// per tile both waves read K and V from LDS and run the attention's 24
+// matrix ops on them (query fragments stand-ins), while the pair's next tile
+// is already on its way into the other stage.  Every wave of the
+// work-group passes the same number of barriers (the split's largest tile
+// count per pair).
+__global__ __launch_bounds__(512) void k_ring_floor_pair(FloorArgs a) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  typedef const __attribute__((address_space(1))) void gvoid;
+  __shared__ __attribute__((aligned(16))) u32x4 stage[2][4][2][512];  // 128 KiB
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int p = wave & 3, qb = wave >> 2;
+  const int n_units = a.n_seq * a.n_head_kv;
+  const int per_unit = a.n_split;
+  int unit, split;
+  if ((n_units & 7) == 0) {
+    const int xcd = blockIdx.x & 7, k = blockIdx.x >> 3;
+    const int q = quot32(k, a.rcp_per_unit);
+    unit = (q << 3) + xcd;
+    split = k - q * per_unit;
+  } else {
+    unit = quot32(blockIdx.x, a.rcp_per_unit);
+    split = blockIdx.x - unit * per_unit;
+  }
+  const int seq = quot32(unit, a.rcp_n_head_kv);
+  const int g = unit - seq * a.n_head_kv;
+  const int nvt = a.vis_count[seq];
+  const int first = a.vis_first[seq];
+  const int per = quot32(nvt + a.n_split - 1, a.rcp_n_split);
+  const int t0 = min(nvt, split * per);
+  const int t1 = min(nvt, t0 + per);
+  const int n = t1 - t0;
+  const int rot = a.rotate && n > 0 ? ((unit * 5 + split * 3) * 4) % n : 0;
+  const uint16_t* base = (qb == 0 ? a.kring : a.vring) + seq * a.seq_stride + a.layer_offset +
+                         g * a.head_stride;
+  auto ring_tile = [&](int k) {
+    int j = k + rot;
+    if (j >= t1) j -= n;
+    int rt = first + j;
+    return rt >= a.ring_tiles ? rt - a.ring_tiles : rt;
+  };
+  // this wave's half (K or V) of tile k into stage st
+  auto copy_in = [&](int k, int st) {
+    const uint16_t* src = base + (int64_t)ring_tile(k) * kTileHalves;
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      __builtin_amdgcn_global_load_lds((gvoid*)(src + c * 512 + lane * 8),
+                                       (lds_void*)&stage[st][p][qb][c * 64], 16, 0, 0);
+  };
+  const int trips = (n + 3) >> 2;
+  f32x16 acc[4] = {};
+  half8 qh, ql;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    qh[e] = (_Float16)(0.01f * (float)(lane + e));
+    ql[e] = (_Float16)(1e-4f * (float)(lane - e));
+  }
+  if (p < n) copy_in(t0 + p, 0);
+  for (int i = 0; i < trips; ++i) {
+    const int k = t0 + p + 4 * i;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (k + 4 < t1) copy_in(k + 4, (i + 1) & 1);
+    if (k < t1) {
+      const int st = i & 1;
+      half8 kc[8], vc[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        kc[c] = __builtin_bit_cast(half8, stage[st][p][0][c * 64 + lane]);
+        vc[c] = __builtin_bit_cast(half8, stage[st][p][1][c * 64 + lane]);
+      }
+      f32x16 sacc = {};
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        sacc = floor_mfma(kc[c], qh, sacc);
+        sacc = floor_mfma(kc[c], ql, sacc);
+      }
+      half8 p0, p1;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p0[e] = (_Float16)sacc[e];
+        p1[e] = (_Float16)sacc[8 + e];
+      }
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        acc[b] = floor_mfma(vc[2 * b], p0, acc[b]);
+        acc[b] = floor_mfma(vc[2 * b + 1], p1, acc[b]);
+      }
+    }
+  }
+  float r = 0.0f;
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) r += acc[b][j];
+  if (lane == 0) a.out[blockIdx.x * 8 + wave] = r;
+}
+
 // 4096 sleeps of 64 x 127 clocks each: about 14 ms at 2.4 GHz
 __global__ __launch_bounds__(64) void k_ring_floor_hold() {
   for (int i = 0; i < 4096; ++i) __builtin_amdgcn_s_sleep(127);
@@ -311,6 +414,21 @@ hipError_t launch_floor(const FloorArgs& args, int kind, hipStream_t s, hipEvent
                         hipEvent_t t1) {
   if (kind == 6) {
     hipExtLaunchKernelGGL(k_ring_floor_hold, dim3(1), dim3(64), 0, s, t0, t1, 0);
+    return hipGetLastError();
+  }
+  if (kind == 11) {
+    // one work-group of eight waves per (unit, split); a.n_split counts the
+    // splits of this grid, a.n_rb must be 1
+    FloorArgs a = args;
+    const uint64_t grid = (uint64_t)a.n_seq * a.n_head_kv * a.n_split;
+    if (a.n_split < 1 || a.n_rb != 1 || grid * a.n_split > (uint64_t(1) << 32) ||
+        (uint64_t)(a.ring_tiles + a.n_split) * a.n_split > (uint64_t(1) << 32))
+      return hipErrorInvalidValue;
+    a.rcp_per_unit = recip32((uint32_t)a.n_split);
+    a.rcp_n_rb = recip32(1);
+    a.rcp_n_head_kv = recip32(a.n_head_kv);
+    a.rcp_n_split = recip32(a.n_split);
+    hipExtLaunchKernelGGL(k_ring_floor_pair, dim3((unsigned)grid), dim3(512), 0, s, t0, t1, 0, a);
     return hipGetLastError();
   }
   FloorArgs a = args;

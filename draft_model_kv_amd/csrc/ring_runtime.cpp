@@ -1155,8 +1155,11 @@ size_t floor_out_bytes(const ring* r) {
 int ring_profile_floor(ring_t* r, int32_t layer, int32_t kind, void* stream) {
   if (!r) return fail(RING_EINVAL, "ring is NULL");
   if (layer < 0 || layer >= r->cfg.n_layer) return fail(RING_ERANGE, "layer %d out of range", layer);
-  if (kind < RING_FLOOR_EMPTY || kind > RING_FLOOR_READ_LOCKSTEP)
+  if (kind < RING_FLOOR_EMPTY || kind > RING_FLOOR_SHARED_TILES)
     return fail(RING_EINVAL, "floor kind %d out of range", kind);
+  if (kind == RING_FLOOR_SHARED_TILES && r->L.n_rb != 2)
+    return fail(RING_EINVAL, "the shared-tile floor needs a ring with two 32-query blocks per "
+                "KV head in work-groups of their own");
   if (kind == RING_FLOOR_PROJ_READ && !r->weights_set)
     return fail(RING_ESTATE, "the projection floor reads registered weights (ring_set_kv_weights)");
   if (kind == RING_FLOOR_HOLD) {
@@ -1245,6 +1248,12 @@ int ring_profile_floor(ring_t* r, int32_t layer, int32_t kind, void* stream) {
   f.n_head_kv = a.n_head_kv;
   f.n_split = n_split;
   f.n_rb = r->L.n_rb;
+  if (kind == RING_FLOOR_SHARED_TILES) {
+    // as many splits as the attention's grid has work-groups per head, each
+    // one work-group for both query blocks
+    f.n_split = n_split * r->L.n_rb;
+    f.n_rb = 1;
+  }
   f.ring_tiles = a.ring_tiles;
   for (int i = 0; i < RING_MAX_SEQ_INTERNAL; ++i) {
     f.vis_first[i] = a.vis_first[i];

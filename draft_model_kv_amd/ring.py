@@ -46,8 +46,8 @@ RING_KERNEL_FLOOR = 4
 # kinds of ring_profile_floor
 (RING_FLOOR_EMPTY, RING_FLOOR_READ, RING_FLOOR_PARTIALS, RING_FLOOR_LAST_ARRIVER,
  RING_FLOOR_BARRIER, RING_FLOOR_TWO_LAUNCH, RING_FLOOR_HOLD, RING_FLOOR_MATRIX_MATH,
- RING_FLOOR_VECTOR_MATH, RING_FLOOR_PROJ_READ, RING_FLOOR_READ_LOCKSTEP) = (
-    0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10)
+ RING_FLOOR_VECTOR_MATH, RING_FLOOR_PROJ_READ, RING_FLOOR_READ_LOCKSTEP,
+ RING_FLOOR_SHARED_TILES) = (0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11)
 # regions of ring_profile_stamps and the layout of a wave's record
 RING_STAMPS_ATTN, RING_STAMPS_MERGE, RING_STAMPS_PROJ = 0, 1, 2
 RING_STAMP_WAVES, RING_STAMP_WORDS = 8192, 10

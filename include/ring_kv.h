@@ -440,6 +440,17 @@ int ring_profile_read(ring_t* r, int32_t kernel, int32_t* n_launches, double* to
  *                            tickets of its head (at most 2^20 polls, then it
  *                            counts a timeout and goes on), then sums its
  *                            share of every split's partial
+ *   RING_FLOOR_SHARED_TILES  (rings with 64 queries per KV head, whose two
+ *                            32-query blocks the attention gives work-groups
+ *                            of their own, each reading every tile) one read
+ *                            of each visible tile for both blocks: a
+ *                            work-group of eight waves per (unit, split),
+ *                            with as many splits as the attention's grid has
+ *                            work-groups per head; each pair of waves copies
+ *                            its tile's K and V into LDS with direct
+ *                            global-to-LDS loads (two stages, one barrier per
+ *                            tile) and both run the attention's 24 matrix
+ *                            ops on them, one per query block
  * These launches read the ring but change none of its state or outputs (the
  * split partials are scratch; the sums go to a buffer of their own, which
  * the first floor launch allocates and ring_free releases).  Deferred steps
@@ -447,7 +458,8 @@ int ring_profile_read(ring_t* r, int32_t kernel, int32_t* n_launches, double* to
  * ring_profile_read time them as RING_KERNEL_FLOOR.
  * Errors: RING_ERANGE (layer), RING_EINVAL (kind; a launch with one split
  * for the kinds with partials; RING_FLOOR_BARRIER when the grid does not fit the
- * device at once), RING_ENOMEM, RING_EDEVICE.                               */
+ * device at once; RING_FLOOR_SHARED_TILES on a ring without two query-block
+ * work-groups per head), RING_ENOMEM, RING_EDEVICE.                         */
 #define RING_FLOOR_EMPTY        0
 #define RING_FLOOR_READ         1
 #define RING_FLOOR_PARTIALS     2
@@ -459,6 +471,7 @@ int ring_profile_read(ring_t* r, int32_t kernel, int32_t* n_launches, double* to
 #define RING_FLOOR_VECTOR_MATH   8
 #define RING_FLOOR_PROJ_READ     9
 #define RING_FLOOR_READ_LOCKSTEP 10
+#define RING_FLOOR_SHARED_TILES  11
 int ring_profile_floor(ring_t* r, int32_t layer, int32_t kind, void* stream);
 
 /* Number of RING_FLOOR_BARRIER waits that ended by their poll limit rather

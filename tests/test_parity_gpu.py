@@ -144,7 +144,8 @@ def test_floor_kinds_leave_the_ring_as_it_was():
             rk.ring_profile_floor(d.ring.handle, layer, k, s)
     torch.cuda.synchronize()
     assert rk.ring_profile_floor_timeouts(d.ring.handle) == 0
-    for kind, code in ((rk.RING_FLOOR_PROJ_READ, rk.RING_ESTATE), (11, rk.RING_EINVAL),
+    for kind, code in ((rk.RING_FLOOR_PROJ_READ, rk.RING_ESTATE),
+                       (rk.RING_FLOOR_SHARED_TILES, rk.RING_EINVAL), (12, rk.RING_EINVAL),
                        (-1, rk.RING_EINVAL)):
         with pytest.raises(rk.RingError) as e:
             rk.ring_profile_floor(d.ring.handle, 0, kind, s)
@@ -153,6 +154,23 @@ def test_floor_kinds_leave_the_ring_as_it_was():
         rk.ring_profile_floor(d.ring.handle, 2, rk.RING_FLOOR_READ, s)
     assert e.value.code == rk.RING_ERANGE
     run_steps(d, [910, 925, 1030, 1031])
+    d.close()
+
+
+def test_shared_tile_floor_leaves_the_ring_as_it_was():
+    """The shared-tile floor (64 queries per KV head: two query blocks, eight
+    waves per work-group sharing each tile through LDS) between steps of a
+    GQA-8 ring whose waves stream several tiles, a ragged split among them;
+    the following steps still match the oracle."""
+    import torch
+    from draft_model_kv_amd import ring as rk
+    s = torch.cuda.current_stream().cuda_stream
+    d = Driver(small(cap=2000, n_head=64, seed=151), n_split=3)
+    run_steps(d, [1900, 1903, 2100])
+    for _ in range(3):
+        rk.ring_profile_floor(d.ring.handle, 0, rk.RING_FLOOR_SHARED_TILES, s)
+    torch.cuda.synchronize()
+    run_steps(d, [2101, 2109, 2500])
     d.close()
 
 
