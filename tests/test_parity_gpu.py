@@ -231,6 +231,43 @@ def test_head_groupings(q_len, n_head, n_head_kv, deferred):
     d.close()
 
 
+@pytest.mark.parametrize("cap", [1, 5, 31])
+@pytest.mark.parametrize("deferred", [False, True], ids=["eager", "fused"])
+def test_degenerate_caps(cap, deferred):
+    """Rings smaller than one 32-slot tile and than the noise block (cap 1:
+    every step overwrites the one slot; cap 5 and 31: wraps inside every
+    fold-in), with rewinds and a bulk step."""
+    w = small(name="tiny_caps", cap=cap, seed=160 + cap)
+    d = Driver(w)
+    commits = [0, 1, 3, 4, 12, 13, 7, 9, 40, 41, 48, 30, 31]
+    for c in commits:
+        d.step(0, c, deferred=deferred)
+        d.check_attn_layers(c)
+        d.check_index(0)
+        d.check_rows(0, 0)
+    d.close()
+
+
+def test_largest_noise_block_and_sequence_count():
+    """q_len 32 with two query heads per KV head (64 queries, the most a KV
+    head takes), then 64 sequences (the most a ring holds) in one batched
+    append and one attention launch."""
+    w = small(cap=96, q_len=32, n_head=16, n_head_kv=8, seed=170)
+    d = Driver(w)
+    run_steps(d, [40, 41, 60, 97, 130, 131])
+    d.close()
+    w = small(cap=64, n_seq=64, seed=171)
+    d = Driver(w)
+    for t, base in enumerate([30, 31, 70, 75]):
+        for seq in range(w.n_seq):
+            d.step(seq, base + seq % 7 + (seq // 7) * t)
+        for seq in (0, 17, 63):
+            d.check_index(seq)
+            d.check_rows(seq, 0)
+        d.check_attn(0, t)
+    d.close()
+
+
 def test_multi_seq_multi_layer():
     w = small(cap=128, n_layer=2, n_seq=3, seed=105)
     d = Driver(w)
