@@ -887,17 +887,72 @@ STAMP_POINTS = {
 }
 
 
+def stamp_step_stats(recs: dict, khz: int) -> dict:
+    """One stamped step: recs[kernel] = that region's [waves][RING_STAMP_WORDS]
+    records (a wave that did not run has entry stamp 0).  Per kernel, per
+    point of STAMP_POINTS: the median and the latest wave's microseconds after
+    the launch's first wave started (the merge counts from the attention's
+    first wave); and where the attention's waves ran (four waves per
+    work-group: XCC_ID against the work-group index mod 8, compute units from
+    HW_ID's cu, sh and se fields)."""
+    import numpy as np
+    us = 1000.0 / khz                       # microseconds per clock tick
+    out = {}
+    a = recs.get("attn")
+    valid_a = a[:, 0] != 0 if a is not None else np.zeros(0, dtype=bool)
+    t_first = int(a[valid_a, 0].min()) if valid_a.any() else 0
+    for name, st in recs.items():
+        valid = st[:, 0] != 0
+        if not valid.any():
+            continue
+        base = t_first if name == "merge" and t_first else int(st[valid, 0].min())
+        rel = (st[valid, :8].astype(np.int64) - base) * us
+        used = [p for p in range(8) if STAMP_POINTS[name][p]]
+        out[name] = {"med": [float(np.median(rel[:, p])) for p in used],
+                     "max": [float(np.max(rel[:, p])) for p in used]}
+    if valid_a.any():
+        idx = np.nonzero(valid_a)[0]
+        hw, xcc = a[idx, 8].astype(np.int64), a[idx, 9].astype(np.int64)
+        block = idx // 4
+        # HW_ID: cu_id bits 11:8, sh_id bit 12, se_id bits 15:13
+        cu = (xcc << 16) | (hw & 0xFF00)
+        _, cnt = np.unique(cu, return_counts=True)
+        out["placement"] = {"waves": len(idx), "xcd_is_block_mod_8": float(np.mean(xcc == block % 8)),
+                            "cus": len(cnt), "max_waves_per_cu": int(cnt.max())}
+    return out
+
+
+def stamp_summary(steps: list, khz: int) -> dict:
+    """The stamped steps' statistics (stamp_step_stats each) summarised:
+    medians over steps of each point's median and latest wave."""
+    import numpy as np
+    out = {"steps": len(steps), "clock_khz": khz,
+           "what": "single steps, each queued behind a 14 ms hold launch"}
+    for name in ("attn", "merge", "proj"):
+        rows = [st[name] for st in steps if name in st]
+        if not rows:
+            continue
+        pts = [p for p in STAMP_POINTS[name] if p]
+        med = np.median(np.array([r["med"] for r in rows]), axis=0)
+        mx = np.median(np.array([r["max"] for r in rows]), axis=0)
+        out[name] = {"points": pts, "median_wave_us": [round(float(x), 3) for x in med],
+                     "latest_wave_us": [round(float(x), 3) for x in mx]}
+    pl = [st["placement"] for st in steps if "placement" in st]
+    if pl:
+        out["attn_placement"] = {
+            "waves": int(np.median([p["waves"] for p in pl])),
+            "xcd_is_block_mod_8": float(np.min([p["xcd_is_block_mod_8"] for p in pl])),
+            "compute_units": int(np.median([p["cus"] for p in pl])),
+            "max_waves_per_cu": int(np.max([p["max_waves_per_cu"] for p in pl]))}
+    return out
+
+
 def stamps_segment(rings, pool, calls, first, n_steps, run, dev, R) -> dict:
     """Per-wave timestamps (profiling build) of n_steps single steps, each on
     the ring touched longest ago and queued behind a RING_FLOOR_HOLD launch
     (a wave that sleeps about 14 ms), so that its launches dispatch back to
-    back as the timed steps' do rather than onto an idle device.  For each
-    kernel, per point: the median over steps of the median and of the latest
-    wave's time after the launch's first wave started (the merge's times count
-    from the attention's first wave), in microseconds; and where the
-    attention's work-groups ran (XCD and compute unit from each wave's
-    hardware registers)."""
-    import numpy as np
+    back as the timed steps' do rather than onto an idle device; summarised
+    by stamp_summary."""
     import torch
     regions = (("attn", R.RING_STAMPS_ATTN), ("merge", R.RING_STAMPS_MERGE),
                ("proj", R.RING_STAMPS_PROJ))
@@ -905,9 +960,7 @@ def stamps_segment(rings, pool, calls, first, n_steps, run, dev, R) -> dict:
     h0 = rings[0].handle
     for _, reg in regions:
         R.ring_profile_stamps(h0, reg, 0, True)
-    per = {name: {"med": [], "max": []} for name, _ in regions}
-    placement = {"waves": [], "xcd_is_block_mod_8": [], "cus": [], "max_waves_per_cu": []}
-    khz = 0
+    steps, khz = [], 0
     s = torch.cuda.current_stream(dev).cuda_stream
     for t in range(first, first + n_steps):
         R.ring_profile_floor(h0, 0, R.RING_FLOOR_HOLD, s)
@@ -915,49 +968,9 @@ def stamps_segment(rings, pool, calls, first, n_steps, run, dev, R) -> dict:
         torch.cuda.synchronize(dev)
         recs = {}
         for name, reg in regions:
-            st, khz = R.ring_profile_stamps(h0, reg, nw, True)
-            recs[name] = st
-        us = 1000.0 / khz                       # microseconds per clock tick
-        a = recs["attn"]
-        valid_a = a[:, 0] != 0
-        t_first = int(a[valid_a, 0].min()) if valid_a.any() else 0
-        for name, st in recs.items():
-            valid = st[:, 0] != 0
-            if not valid.any():
-                continue
-            base = t_first if name == "merge" and t_first else int(st[valid, 0].min())
-            rel = (st[valid, :8].astype(np.int64) - base) * us
-            used = [p for p in range(8) if STAMP_POINTS[name][p]]
-            per[name]["med"].append([float(np.median(rel[:, p])) for p in used])
-            per[name]["max"].append([float(np.max(rel[:, p])) for p in used])
-        if valid_a.any():
-            idx = np.nonzero(valid_a)[0]
-            hw, xcc = a[idx, 8].astype(np.int64), a[idx, 9].astype(np.int64)
-            block = idx // 4
-            # HW_ID: cu_id bits 11:8, sh_id bit 12, se_id bits 15:13
-            cu = (xcc << 16) | (hw & 0xFF00)
-            u, cnt = np.unique(cu, return_counts=True)
-            placement["waves"].append(len(idx))
-            placement["xcd_is_block_mod_8"].append(float(np.mean(xcc == block % 8)))
-            placement["cus"].append(len(u))
-            placement["max_waves_per_cu"].append(int(cnt.max()))
-    out = {"steps": n_steps, "clock_khz": khz,
-           "what": "single steps, each queued behind a 14 ms hold launch"}
-    for name, _ in regions:
-        if not per[name]["med"]:
-            continue
-        pts = [p for p in STAMP_POINTS[name] if p]
-        med = np.median(np.array(per[name]["med"]), axis=0)
-        mx = np.median(np.array(per[name]["max"]), axis=0)
-        out[name] = {"points": pts, "median_wave_us": [round(float(x), 3) for x in med],
-                     "latest_wave_us": [round(float(x), 3) for x in mx]}
-    if placement["waves"]:
-        out["attn_placement"] = {
-            "waves": int(np.median(placement["waves"])),
-            "xcd_is_block_mod_8": float(np.min(placement["xcd_is_block_mod_8"])),
-            "compute_units": int(np.median(placement["cus"])),
-            "max_waves_per_cu": int(np.max(placement["max_waves_per_cu"]))}
-    return out
+            recs[name], khz = R.ring_profile_stamps(h0, reg, nw, True)
+        steps.append(stamp_step_stats(recs, khz))
+    return stamp_summary(steps, khz)
 
 
 def stamps_markdown(res: dict, cmd: str) -> str:

@@ -133,3 +133,68 @@ def test_hardware_counter_summary(tmp_path, monkeypatch):
     assert cyc[1] == "15.62"
     hit = lines["L2 hit rate (TCC_HIT / (TCC_HIT + TCC_MISS))"].split(" | ")
     assert hit[1] == "0.300"
+
+
+def _stamp_records(n_waves, entry, points, hw=None, xcc=None):
+    """[waves][10] records: stamps entry + points[p] (ticks), HW_ID, XCC_ID."""
+    import numpy as np
+    r = np.zeros((8192, 10), dtype=np.uint64)
+    for w in range(n_waves):
+        for p, d in enumerate(points):
+            r[w, p] = entry[w] + d if d is not None else 0
+        r[w, 8] = 0 if hw is None else hw[w]
+        r[w, 9] = 0 if xcc is None else xcc[w]
+    return r
+
+
+def test_stamp_step_statistics():
+    """Per-wave stamps of one step (100 MHz clock: 10 ns per tick): the
+    attention's points count from its first wave's entry, the merge's from
+    the attention's first wave too; the median and the latest wave per point;
+    waves that did not run (entry 0) are left out; placement: XCC_ID against
+    work-group index mod 8, and compute units told apart by XCC and HW_ID's
+    cu/sh/se bits (not its wave and SIMD bits)."""
+    import numpy as np
+    khz = 100_000
+    # 8 waves = 2 work-groups of 4; entries 1000, 1010, ... ticks
+    entry = [1000 + 10 * w for w in range(8)]
+    pts = [0, 5, 20, 30, 40, 50, 60, 70]
+    # work-group 0 on XCD 0, work-group 1 on XCD 1; waves of a group on one
+    # compute unit (cu 3 / cu 5), different SIMD and wave ids
+    hw = [(3 << 8) | (w & 3) << 4 | w for w in range(4)] + [(5 << 8) | (w & 3) << 4 for w in range(4)]
+    xcc = [0] * 4 + [1] * 4
+    attn = _stamp_records(8, entry, pts, hw, xcc)
+    merge = _stamp_records(2, [1200, 1300], [0, 10, 20, 30, 40, None, None, 90])
+    st = bench.stamp_step_stats({"attn": attn, "merge": merge}, khz)
+    a = st["attn"]
+    # point p of wave w: 10 w + pts[p] ticks after the first entry; median
+    # over the 8 waves of 10 w is 35, the latest 70
+    assert np.allclose(a["med"], [0.01 * (35 + d) for d in pts])
+    assert np.allclose(a["max"], [0.01 * (70 + d) for d in pts])
+    # the merge's six points (5 and 6 unused), counted from the attention's
+    # first wave: its waves enter 200 and 300 ticks later
+    m = st["merge"]
+    used = (0, 10, 20, 30, 40, 90)
+    assert np.allclose(m["med"], [0.01 * (250 + d) for d in used])
+    assert np.allclose(m["max"], [0.01 * (300 + d) for d in used])
+    pl = st["placement"]
+    assert pl["waves"] == 8 and pl["cus"] == 2 and pl["max_waves_per_cu"] == 4
+    assert pl["xcd_is_block_mod_8"] == 1.0
+    # a work-group off its XCD shows in the fraction
+    attn2 = _stamp_records(8, entry, pts, hw, [0] * 4 + [2] * 4)
+    assert bench.stamp_step_stats({"attn": attn2}, khz)["placement"]["xcd_is_block_mod_8"] == 0.5
+
+
+def test_stamp_summary_takes_medians_over_steps():
+    import numpy as np
+    khz = 100_000
+    steps = []
+    for k in range(3):
+        a = _stamp_records(4, [0 + 1, 2, 3, 4], [0, 10 * (k + 1), 20, 30, 40, 50, 60, 70])
+        steps.append(bench.stamp_step_stats({"attn": a}, khz))
+    out = bench.stamp_summary(steps, khz)
+    assert out["steps"] == 3 and "merge" not in out
+    assert len(out["attn"]["points"]) == 8
+    # point 1 is 10 (k + 1) ticks after each wave's entry: median over steps 20
+    assert np.isclose(out["attn"]["median_wave_us"][1], 0.01 * (1.5 + 20))
+    assert out["attn_placement"]["waves"] == 4
