@@ -10,8 +10,9 @@ launch that appends the new rows, writes their slot_pos entries and attends,
 then the merge; the masks and noise RoPE table, which that launch does not
 read, are rebuilt only when a plain launch or a read needs them);
 --step eager gives it a launch of its own (ring_begin_step).  On a ring of
-several sequences (batched_seqs) a step is one ring_begin_step_batch over all
-of them, then one ring_attn per layer.
+several sequences (batched_seqs) a step is one ring_begin_step_deferred per
+sequence, then one ring_attn per layer (--step eager: one
+ring_begin_step_batch over all of them, then the ring_attn launches).
 Workload: the draft-window decode stream (cap 4096, q_len 8, 32 query / 8 KV
 heads x 128, F16), warmed by a 4096-token bulk prefill; synthetic seeded
 inputs, already resident in device memory when timing starts.
@@ -1148,13 +1149,15 @@ def main() -> int:
     ap.add_argument("--step", choices=("eager", "fused"), default="fused",
                     help="fused (default): ring_begin_step_deferred, the fold-in append and "
                          "index rebuild run inside the attention launch; eager: "
-                         "ring_begin_step's own append launch.  Rings of several sequences "
-                         "take ring_begin_step_batch, rows from features "
-                         "ring_begin_step_mirror, whatever this says")
-    ap.add_argument("--begin", choices=("auto", "per_seq"), default="auto",
-                    help="eager step of a ring with several sequences: auto takes one "
-                         "ring_begin_step_batch call for all of them (default), per_seq one "
-                         "ring_begin_step call per sequence")
+                         "ring_begin_step's own append launch (rings of several sequences: "
+                         "one ring_begin_step_batch call, see --begin); rows from features "
+                         "take ring_begin_step_mirror, whatever this says")
+    ap.add_argument("--begin", choices=("auto", "per_seq", "batch"), default="auto",
+                    help="ring with several sequences: auto takes one ring_begin_step_deferred "
+                         "call per sequence for the fused step (rings of up to 16 sequences) "
+                         "and one ring_begin_step_batch call for all of them otherwise; "
+                         "per_seq one begin call per sequence; batch one "
+                         "ring_begin_step_batch call")
     ap.add_argument("--proj", choices=("registered", "caller"), default="registered",
                     help="rows from features: weights registered once per ring "
                          "(ring_set_kv_weights, packed in the projection's load order; "
@@ -1240,7 +1243,8 @@ def main() -> int:
     s = torch.cuda.current_stream(dev).cuda_stream
     out = torch.empty((w.n_seq, w.q_len, w.n_head, w.head_dim), dtype=torch.float32, device=dev)
     mirror = w.d_model > 0
-    batched = not mirror and w.n_seq > 1 and args.begin == "auto"
+    batched = not mirror and w.n_seq > 1 and (
+        args.begin == "batch" or (args.begin == "auto" and (args.step == "eager" or w.n_seq > 16)))
     fused = args.step == "fused" and not mirror and not batched
     step_mode = "mirror" if mirror else "batch" if batched else "fused" if fused else "eager"
     begin = R.ring_begin_step_deferred if fused else R.ring_begin_step

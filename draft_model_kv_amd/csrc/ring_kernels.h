@@ -119,8 +119,9 @@ struct PackArgs {
 // launch of each layer (the fused launch): this layer's new rows, and the
 // window the attention sees.  Positions are below 2^31.  Per-sequence fields
 // are arrays of kFusedMaxSeq, so that a kernel fetches each with one
-// lane-indexed load.
-constexpr int kFusedMaxSeq = 8;
+// lane-indexed load (lane i holds sequence i % kFusedMaxSeq, a power of two
+// at most 64).
+constexpr int kFusedMaxSeq = 16;
 struct FusedSeqs {
   uint64_t k_new[kFusedMaxSeq];      // this layer's K rows [n_new][kv_row] F16, not rotated, or 0
   uint64_t v_new[kFusedMaxSeq];      // this layer's V rows

@@ -686,14 +686,13 @@ int ring_begin_step_deferred(ring_t* r, int32_t seq, int64_t committed, const vo
   if (committed < 0 || committed + r->cfg.q_len > INT32_MAX)
     return fail(RING_ERANGE, "committed %lld out of range", (long long)committed);
   const Plan p = plan_of(r->cfg.cap, r->geo.a_step, committed, r->next_pos[seq], r->held_lo[seq]);
-  // Bulk appends, rings beyond what one fused launch carries, and rings whose
-  // attention waves stream three or more tiles each append now: on those the
-  // append launch is a small part of the step, and the fused attention's own
-  // per-tile work (visibility from slot_pos, the new slots hidden) costs more
-  // than that launch (a 32768-slot window: 37 us fused against 31 us plain).
-  const int32_t ring_tiles = (r->cfg.cap + kTile - 1) / kTile;
-  const int32_t wave_tiles = ((ring_tiles + r->L.n_split - 1) / r->L.n_split + 3) / 4;
-  if (p.bulk || r->cfg.n_seq > kFusedMaxSeq || r->cfg.n_layer > 64 || wave_tiles >= 3)
+  // Bulk appends and rings beyond what one fused launch carries append now.
+  // (Rings whose attention waves stream several tiles are fused too: since
+  // the fused launch tests each slot's visibility with one window test on
+  // slot_pos, its tile pass costs what the plain one's does — a 32768-slot
+  // window 29.4-29.9 against 29.3 us — and the append launch it saves is
+  // the gain.)
+  if (p.bulk || r->cfg.n_seq > kFusedMaxSeq || r->cfg.n_layer > 64)
     return ring_begin_step(r, seq, committed, k_new, v_new, n_rows, stream);
   if (n_rows != p.n_new)
     return fail(RING_ESTATE, "n_rows %lld != planned n_new %lld (start %lld)", (long long)n_rows,

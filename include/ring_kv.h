@@ -189,9 +189,8 @@ int ring_begin_step(ring_t* r, int32_t seq, int64_t committed,
  * has not run) is appended by the ordinary append kernel on the ring's last
  * stream before any other call that needs it: a begin_step of the same
  * sequence and the ring_read_* inspection calls.  A bulk plan, and rings
- * with more than 8 sequences or 64 layers or whose attention streams three
- * or more 32-slot tiles per wave (cap above about 12 k slots at 32 splits),
- * append right away as ring_begin_step does.
+ * with more than 16 sequences or 64 layers, append right away as
+ * ring_begin_step does.
  * Errors: as ring_begin_step.                                               */
 int ring_begin_step_deferred(ring_t* r, int32_t seq, int64_t committed,
                              const void* k_new, const void* v_new, int64_t n_rows,

@@ -66,8 +66,8 @@ def test_fused_ragged_cap_short_block():
 ], ids=["ragged", "window_grows"])
 def test_deferred_on_wide_rings(cap, commits):
     """One split per KV head, so the waves stream three or more tiles: the
-    deferred steps append at once (there the plain attention is the faster
-    one), with the same results."""
+    fused launch's long-wave kernel appends and attends the new rows while
+    its waves walk several tiles each."""
     d = Driver(small(cap=cap, seed=306), n_split=1)
     run_fused(d, commits, rows=False)
     d.close()
@@ -126,10 +126,11 @@ def test_fused_multi_seq():
     d.close()
 
 
-@pytest.mark.parametrize("n_seq", [8, 9], ids=["eight_fused", "nine_append_at_once"])
+@pytest.mark.parametrize("n_seq", [16, 17], ids=["sixteen_fused", "seventeen_append_at_once"])
 def test_fused_sequence_limit(n_seq):
-    """Eight sequences fill every lane of a fused launch's per-sequence
-    fields; a ninth makes the deferred steps append at once.  Each sequence
+    """Sixteen sequences fill every per-sequence field of a fused launch
+    (lanes 0..15 of its lane-indexed loads); a seventeenth makes the deferred
+    steps append at once.  Each sequence
     starts at its own position, some below cap, some past a wrap."""
     w = small(cap=96, n_seq=n_seq, seed=310 + n_seq)
     d = Driver(w)
